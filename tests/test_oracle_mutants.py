@@ -1,0 +1,91 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by rewriting its source in a
+scratch namespace) and check that the pins catch every one of them."""
+import inspect
+import json
+import os
+import types
+
+import numpy as np
+import pytest
+
+from oracle import palu_oracle as O
+import tests.test_oracle_pins as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+MUTANTS = {
+    "rope_sign": ("apply_rope", "[c * x - s * y, s * x + c * y]", "[c * x + s * y, -s * x + c * y]"),
+    "rope_interleaved": ("apply_rope", "x, y = k[:, :half], k[:, half:]",
+                         "x, y = k[:, 0::2], k[:, 1::2]"),
+    "rope_freq_exponent": ("rope_angles", "-2.0 * i / head_dim", "-1.0 * i / head_dim"),
+    "rope_positions_from_1": ("decode_attention", "pos = np.arange(n)", "pos = np.arange(1, n + 1)"),
+    "no_scale": ("decode_attention", "out[b, h] = attend(to_f64(q[b, h]), Kj, Vj, scale)",
+                 "out[b, h] = attend(to_f64(q[b, h]), Kj, Vj, 1.0)"),
+    "gqa_modulo": ("decode_attention", "j = h // gqa", "j = h % (G * s)"),
+    "head_columns_strided": ("decode_attention", "Kj = apply_rope(Kg[:, jl * d:(jl + 1) * d]",
+                             "Kj = apply_rope(Kg[:, jl::s]"),
+    "value_uses_keys": ("decode_attention", "Vj = Vg[:, jl * d:(jl + 1) * d]",
+                        "Vj = Kg[:, jl * d:(jl + 1) * d]"),
+    "softmax_unnormalised": ("softmax", "return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
+    "reconstruct_transposed": ("reconstruct", "return to_f64(h) @ to_f64(b)",
+                               "return to_f64(h) @ to_f64(b)[::-1]"),
+    "project_wrong_side": ("latent_project", "return to_f64(x) @ to_f64(a)",
+                           "return (to_f64(a).T @ to_f64(x).T).T[::-1]"),
+    "append_truncates": ("append_rows_bf16", "return (keep + up.astype(np.uint64)).astype(np.uint16)",
+                         "return keep.astype(np.uint16)"),
+    "append_ties_up": ("append_rows_bf16", "(rest == 0x8000) & ((keep & np.uint64(1)) == 1)",
+                       "(rest == 0x8000)"),
+}
+
+PINS = [name for name in dir(P) if name.startswith("test_")]
+
+
+def _mutated_module(fn_name, old, new):
+    src = inspect.getsource(O)
+    fn_src = inspect.getsource(getattr(O, fn_name))
+    assert old in fn_src, (fn_name, old)
+    src = src.replace(fn_src, fn_src.replace(old, new))
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _run_pins(monkeypatch, mod):
+    with open(GOLDEN) as f:
+        golden = json.load(f)
+    monkeypatch.setattr(P, "O", mod)
+    failed = []
+    for name in PINS:
+        fn = getattr(P, name)
+        params = inspect.signature(fn).parameters
+        marks = getattr(fn, "pytestmark", [])
+        grids = [m for m in marks if m.name == "parametrize"]
+        calls = [{}]
+        for m in grids:
+            argnames = [a.strip() for a in (m.args[0].split(",") if isinstance(m.args[0], str) else m.args[0])]
+            new = []
+            for c in calls:
+                for v in m.args[1]:
+                    v = v if len(argnames) > 1 else (v,)
+                    new.append({**c, **dict(zip(argnames, v))})
+            calls = new
+        for kw in calls:
+            if "golden" in params:
+                kw = {**kw, "golden": golden}
+            try:
+                fn(**kw)
+            except (AssertionError, ValueError, IndexError):
+                failed.append(name)
+                break
+    return failed
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_mutant(mutant, monkeypatch):
+    mod = _mutated_module(*MUTANTS[mutant])
+    failed = _run_pins(monkeypatch, mod)
+    assert failed, f"no pin caught mutant {mutant}"
+
+
+def test_unmutated_oracle_passes_all_pins(monkeypatch):
+    assert _run_pins(monkeypatch, O) == []

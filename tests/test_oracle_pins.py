@@ -1,0 +1,394 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties the oracle to a closed form, a library routine, brute force on
+tiny inputs or an identity the pages state, so that a dropped term, a wrong
+sign, a wrong index or a transposed operand fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import palu_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _arr(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------- goldens ---
+
+def test_golden_two_token_softmax(golden):
+    c = golden["two_token_softmax"]
+    out = O.decode_attention(_arr(c["q"]), _arr(c["h_k"]), _arr(c["h_v"]), _arr(c["b_k"]),
+                             _arr(c["b_v"]), np.array(c["lens"]), rope_theta=c["rope_theta"])
+    np.testing.assert_allclose(out, _arr(c["out"]), rtol=0, atol=1e-12)
+
+
+def test_golden_project_then_reconstruct(golden):
+    c = golden["project_then_reconstruct"]
+    h = O.latent_project(_arr(c["x"]), _arr(c["a"]))
+    np.testing.assert_array_equal(h, _arr(c["h"]))
+    np.testing.assert_array_equal(O.reconstruct(h, _arr(c["b"])), _arr(c["y"]))
+
+
+def test_golden_rope_quarter_turn(golden):
+    c = golden["rope_quarter_turn"]
+    keys = np.tile(_arr(c["key"]), (len(c["positions"]), 1))
+    rot = O.apply_rope(keys, np.array(c["positions"]), c["theta"])
+    np.testing.assert_allclose(rot, _arr(c["rotated"]), rtol=0, atol=1e-12)
+
+
+def test_golden_property1_sign_convention(golden):
+    """The oracle's 2x2 rotation, read off by rotating unit vectors, reproduces the
+    printed products R C = C R of the CommVQ Property 1 proof (this fixes the sign)."""
+    c = golden["property1_product"]
+    d = 2                                      # one pair, omega_0 = 1: angle = position
+    C = np.array([[c["x"], c["y"]], [-c["y"], c["x"]]])
+    for ang, want in zip(c["angles"], c["products"]):
+        # positions are integers in the cache; use a fractional position to hit
+        # the printed angle exactly (the oracle accepts any real position)
+        e = np.eye(d)
+        cols = O.apply_rope(e, np.array([ang, ang]), theta=10000.0)  # rows = R e_i
+        R = cols.T                             # column i is R e_i
+        np.testing.assert_allclose(R @ C, _arr(want), atol=1e-12)
+        np.testing.assert_allclose(C @ R, _arr(want), atol=1e-12)
+
+
+def test_golden_gqa_single_token(golden):
+    c = golden["gqa_single_token"]
+    out = O.decode_attention(_arr(c["q"]), _arr(c["h_k"]), _arr(c["h_v"]), _arr(c["b_k"]),
+                             _arr(c["b_v"]), np.array(c["lens"]), rope_theta=c["rope_theta"])
+    np.testing.assert_array_equal(out, _arr(c["out"]))
+
+
+# ------------------------------------------------------------ brute force ---
+
+def _brute(q, h_k, h_v, b_k, b_v, lens, theta):
+    """Pure-Python loops with math.fsum; no numpy, no max subtraction."""
+    Bsz, Hq, d = len(q), len(q[0]), len(q[0][0])
+    G, r, Dg = len(b_k), len(b_k[0]), len(b_k[0][0])
+    s = Dg // d
+    gqa = Hq // (G * s)
+    half = d // 2
+    out = [[[0.0] * d for _ in range(Hq)] for _ in range(Bsz)]
+    for b in range(Bsz):
+        n = lens[b]
+        for h in range(Hq):
+            j = h // gqa
+            g, jl = j // s, j % s
+            keys, vals = [], []
+            for t in range(n):
+                kcol = [math.fsum(h_k[b][g][t][k] * b_k[g][k][jl * d + c] for k in range(r))
+                        for c in range(d)]
+                vcol = [math.fsum(h_v[b][g][t][k] * b_v[g][k][jl * d + c] for k in range(r))
+                        for c in range(d)]
+                if theta:
+                    rot = list(kcol)
+                    for i in range(half):
+                        ang = t * theta ** (-2.0 * i / d)
+                        x, y = kcol[i], kcol[i + half]
+                        rot[i] = x * math.cos(ang) - y * math.sin(ang)
+                        rot[i + half] = x * math.sin(ang) + y * math.cos(ang)
+                    kcol = rot
+                keys.append(kcol)
+                vals.append(vcol)
+            if n == 0:
+                continue
+            w = [math.exp(math.fsum(q[b][h][c] * keys[t][c] for c in range(d)) / math.sqrt(d))
+                 for t in range(n)]
+            tot = math.fsum(w)
+            for c in range(d):
+                out[b][h][c] = math.fsum(w[t] * vals[t][c] for t in range(n)) / tot
+    return out
+
+
+@pytest.mark.parametrize("theta", [0.0, 10000.0, 500000.0])
+@pytest.mark.parametrize("shape", [
+    # (B, Hq, Hkv, d, G, r, L)
+    (2, 4, 2, 8, 1, 4, 7),      # one group over both KV heads (joint), GQA 2
+    (1, 4, 4, 4, 2, 3, 6),      # MHA, two groups of two heads, odd rank
+    (2, 6, 2, 6, 2, 5, 5),      # GQA 3, groups of one head
+])
+def test_brute_force_tiny(shape, theta):
+    Bsz, Hq, Hkv, d, G, r, L = shape
+    s = Hkv // G
+    rng = np.random.default_rng(1234 + sum(shape))
+    q = rng.standard_normal((Bsz, Hq, d))
+    h_k = rng.standard_normal((Bsz, G, L, r))
+    h_v = rng.standard_normal((Bsz, G, L, r))
+    b_k = rng.standard_normal((G, r, s * d)) / math.sqrt(r)
+    b_v = rng.standard_normal((G, r, s * d)) / math.sqrt(r)
+    lens = np.array([L, L - 3][:Bsz])
+    want = _brute(q.tolist(), h_k.tolist(), h_v.tolist(), b_k.tolist(), b_v.tolist(),
+                  lens.tolist(), theta)
+    got = O.decode_attention(q, h_k, h_v, b_k, b_v, lens, rope_theta=theta)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_zero_and_one_length():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((3, 2, 4))
+    h_k = rng.standard_normal((3, 1, 5, 3))
+    h_v = rng.standard_normal((3, 1, 5, 3))
+    b_k = rng.standard_normal((1, 3, 8))
+    b_v = rng.standard_normal((1, 3, 8))
+    lens = np.array([0, 1, 5])
+    got = O.decode_attention(q, h_k, h_v, b_k, b_v, lens, rope_theta=10000.0)
+    want = _brute(q.tolist(), h_k.tolist(), h_v.tolist(), b_k.tolist(), b_v.tolist(),
+                  lens.tolist(), 10000.0)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-12, atol=1e-12)
+    assert np.all(got[0] == 0.0)
+
+
+# ------------------------------------------------------- library routines ---
+
+@pytest.mark.parametrize("Hq,Hkv,d,L", [(8, 8, 16, 33), (8, 2, 16, 40), (12, 3, 8, 17)])
+def test_identity_factors_reduce_to_sdpa(Hq, Hkv, d, L):
+    """r = D_g and B = I: Palu attention is ordinary (GQA) attention with K = H_k and
+    V = H_v; torch's fp64 scaled_dot_product_attention is the reference."""
+    G = Hkv
+    rng = np.random.default_rng(Hq * 100 + L)
+    q = rng.standard_normal((2, Hq, d))
+    h_k = rng.standard_normal((2, G, L, d))
+    h_v = rng.standard_normal((2, G, L, d))
+    eye = np.broadcast_to(np.eye(d), (G, d, d)).copy()
+    got = O.decode_attention(q, h_k, h_v, eye, eye, np.array([L, L]))
+    Q = torch.from_numpy(q)[:, :, None, :]                      # [B, Hq, 1, d]
+    K = torch.from_numpy(h_k).repeat_interleave(Hq // Hkv, dim=1)
+    V = torch.from_numpy(h_v).repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V)[:, :, 0, :].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_reconstructed_keys_have_rank_r():
+    """K_g = H B is at most rank r (the cache stores r numbers per token and group)."""
+    rng = np.random.default_rng(3)
+    for r in (3, 8):
+        H = rng.standard_normal((40, r))
+        B = rng.standard_normal((r, 32))
+        sv = np.linalg.svd(O.reconstruct(H, B), compute_uv=False)
+        assert np.all(sv[r:] < 1e-12 * sv[0])
+        assert sv[r - 1] > 1e-6 * sv[0]
+
+
+def test_projection_associativity():
+    """(x A) B = x (A B): caching the latent and reconstructing later equals the
+    full projection with W = A B (Palu response, answer to Q2)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 64))
+    A = rng.standard_normal((64, 16))
+    B = rng.standard_normal((16, 48))
+    lhs = O.reconstruct(O.latent_project(x, A), B)
+    rhs = x @ (A @ B)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-11)
+
+
+# -------------------------------------------------------------- invariants ---
+
+def _rand_case(rng, Bsz=2, Hq=8, Hkv=4, d=16, G=2, r=6, L=20):
+    s = Hkv // G
+    return dict(q=rng.standard_normal((Bsz, Hq, d)),
+                h_k=rng.standard_normal((Bsz, G, L, r)),
+                h_v=rng.standard_normal((Bsz, G, L, r)),
+                b_k=rng.standard_normal((G, r, s * d)) / math.sqrt(r),
+                b_v=rng.standard_normal((G, r, s * d)) / math.sqrt(r),
+                lens=np.array([L, L - 7][:Bsz]))
+
+
+def _absorbed(case, scale=None):
+    """No-RoPE attention with B_k moved onto the query, (q B_j^T) H_k^T, and B_v
+    applied after the weighted sum, (p H_v) B_v."""
+    q, h_k, h_v, b_k, b_v, lens = (case[k] for k in ("q", "h_k", "h_v", "b_k", "b_v", "lens"))
+    Bsz, Hq, d = q.shape
+    G, r, Dg = b_k.shape
+    s = Dg // d
+    gqa = Hq // (G * s)
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    out = np.zeros_like(q)
+    for b in range(Bsz):
+        n = lens[b]
+        for h in range(Hq):
+            j = h // gqa
+            g, jl = j // s, j % s
+            Bk = b_k[g][:, jl * d:(jl + 1) * d]
+            Bv = b_v[g][:, jl * d:(jl + 1) * d]
+            qt = Bk @ q[b, h]                      # q B_j^T, length r
+            z = h_k[b, g, :n] @ qt * scale
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            out[b, h] = (p @ h_v[b, g, :n]) @ Bv
+    return out
+
+
+def test_absorbed_equals_explicit_without_rope():
+    case = _rand_case(np.random.default_rng(11))
+    got = O.decode_attention(**case, rope_theta=0.0)
+    np.testing.assert_allclose(got, _absorbed(case), rtol=1e-12, atol=1e-12)
+
+
+def test_value_fold():
+    """(p H_v) B_v = p (H_v B_v)."""
+    rng = np.random.default_rng(2)
+    p = rng.random(30)
+    p /= p.sum()
+    H = rng.standard_normal((30, 7))
+    B = rng.standard_normal((7, 12))
+    np.testing.assert_allclose((p @ H) @ B, p @ O.reconstruct(H, B), rtol=1e-12, atol=1e-13)
+
+
+def test_softmax_rows_sum_to_one_and_shift_invariance():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((5, 33)) * 10
+    p = O.softmax(z)
+    assert np.all(p >= 0)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(O.softmax(z + 123.25), p, atol=1e-12)
+
+
+def test_single_token_returns_its_value():
+    case = _rand_case(np.random.default_rng(8))
+    case["lens"] = np.array([1, 1])
+    got = O.decode_attention(**case, rope_theta=500000.0)
+    Bsz, Hq, d = case["q"].shape
+    s = case["b_k"].shape[2] // d
+    gqa = Hq // (case["b_k"].shape[0] * s)
+    for b in range(Bsz):
+        for h in range(Hq):
+            j = h // gqa
+            g, jl = j // s, j % s
+            v0 = case["h_v"][b, g, 0] @ case["b_v"][g][:, jl * d:(jl + 1) * d]
+            np.testing.assert_allclose(got[b, h], v0, rtol=1e-13, atol=1e-13)
+
+
+def test_zero_keys_give_mean_of_values():
+    case = _rand_case(np.random.default_rng(9))
+    case["h_k"][:] = 0.0
+    got = O.decode_attention(**case, rope_theta=10000.0)
+    Bsz, Hq, d = case["q"].shape
+    s = case["b_k"].shape[2] // d
+    gqa = Hq // (case["b_k"].shape[0] * s)
+    for b in range(Bsz):
+        n = case["lens"][b]
+        for h in range(Hq):
+            j = h // gqa
+            g, jl = j // s, j % s
+            V = case["h_v"][b, g, :n] @ case["b_v"][g][:, jl * d:(jl + 1) * d]
+            np.testing.assert_allclose(got[b, h], V.mean(0), rtol=1e-12, atol=1e-12)
+
+
+def test_permutation_invariance_without_rope():
+    rng = np.random.default_rng(10)
+    case = _rand_case(rng)
+    case["lens"] = np.array([20, 20])
+    base = O.decode_attention(**case, rope_theta=0.0)
+    perm = rng.permutation(20)
+    case["h_k"] = case["h_k"][:, :, perm]
+    case["h_v"] = case["h_v"][:, :, perm]
+    np.testing.assert_allclose(O.decode_attention(**case, rope_theta=0.0), base,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rope_position_dependence():
+    """With RoPE the context order matters (the no-RoPE invariance above is not a
+    property of a path that silently skips the rotation)."""
+    rng = np.random.default_rng(12)
+    case = _rand_case(rng)
+    case["lens"] = np.array([20, 20])
+    base = O.decode_attention(**case, rope_theta=10000.0)
+    perm = rng.permutation(20)
+    case["h_k"] = case["h_k"][:, :, perm]
+    case["h_v"] = case["h_v"][:, :, perm]
+    assert np.max(np.abs(O.decode_attention(**case, rope_theta=10000.0) - base)) > 1e-3
+
+
+def test_rope_identity_at_zero_norm_and_relative_position():
+    rng = np.random.default_rng(13)
+    d, theta = 16, 10000.0
+    k = rng.standard_normal((1, d))
+    qv = rng.standard_normal((1, d))
+    np.testing.assert_allclose(O.apply_rope(k, np.array([0]), theta), k, atol=0)
+    for m, n in [(3, 11), (100, 7), (4096, 4000)]:
+        Rk = O.apply_rope(k, np.array([n]), theta)
+        Rq = O.apply_rope(qv, np.array([m]), theta)
+        np.testing.assert_allclose(np.linalg.norm(Rk), np.linalg.norm(k), rtol=1e-13)
+        lhs = (Rq @ Rk.T).item()
+        rhs = (qv @ O.apply_rope(k, np.array([n - m]), theta).T).item()
+        assert abs(lhs - rhs) < 1e-10
+
+
+def test_rope_frequency_schedule():
+    """At position 1 the pair (i, i + d/2) is turned by theta^(-2i/d)."""
+    d, theta = 8, 10000.0
+    for i in range(d // 2):
+        e = np.zeros((1, d))
+        e[0, i] = 1.0
+        rot = O.apply_rope(e, np.array([1]), theta)[0]
+        ang = math.atan2(rot[i + d // 2], rot[i])
+        assert abs(ang - theta ** (-2.0 * i / d)) < 1e-14
+        others = np.delete(rot, [i, i + d // 2])
+        assert np.all(others == 0)
+
+
+# ------------------------------------------------------------ split merge ---
+
+def test_split_merge_algebra():
+    """Partial softmax states (m, l, u) of any partition of the context merge to the
+    unsplit result: the algebra a split-context kernel relies on."""
+    rng = np.random.default_rng(14)
+    z = rng.standard_normal(97) * 3
+    H = rng.standard_normal((97, 5))
+    p = O.softmax(z)
+    want = p @ H
+    for cuts in ([0, 97], [0, 10, 97], [0, 1, 2, 50, 96, 97], list(range(0, 98, 13)) + [97]):
+        ms, ls, us = [], [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if b <= a:
+                continue
+            m = z[a:b].max()
+            e = np.exp(z[a:b] - m)
+            ms.append(m), ls.append(e.sum()), us.append(e @ H[a:b])
+        M = max(ms)
+        w = np.exp(np.array(ms) - M)
+        got = (w[:, None] * np.array(us)).sum(0) / (w * np.array(ls)).sum()
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------- append ---
+
+def test_append_rounding_is_fp32_then_bf16_nearest_even():
+    """append_rows_bf16 rounds through fp32 to bf16, ties to even: checked on
+    hand-picked fp32 bit patterns."""
+    cases = {
+        0x3F800000: 0x3F80,   # 1.0 exact
+        0x3F808000: 0x3F80,   # tie, even stays
+        0x3F818000: 0x3F82,   # tie, odd rounds up
+        0x3F808001: 0x3F81,   # above tie
+        0x3F807FFF: 0x3F80,   # below tie
+        0xBF818000: 0xBF82,   # negative tie, odd -> away from zero
+    }
+    for fbits, want in cases.items():
+        v = np.array([fbits], dtype=np.uint32).view(np.float32).astype(np.float64)
+        assert int(O.append_rows_bf16(v)[0]) == want, hex(fbits)
+
+
+def test_append_matches_projection():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((3, 32)).astype(np.float32)
+    A = rng.standard_normal((32, 12)).astype(np.float32)
+    h = O.latent_project(x, A)
+    np.testing.assert_allclose(h, x.astype(np.float64) @ A.astype(np.float64), rtol=1e-13)
+    bits = O.append_rows_bf16(h)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.abs(back - h) <= np.abs(h) * 2.0 ** -8)
