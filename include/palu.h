@@ -1,0 +1,149 @@
+/*
+ * palu.h - C ABI of libpalu: single-token decode attention over a low-rank
+ * (Palu-style) latent KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method, as the Palu author responses on OpenReview (paperhub page
+ * "LWMS4pk2vK") state it:
+ *   - answer to Q2 (ESPACE): at inference a down-projection h = x A is cached
+ *     and a reconstruction y = h B rebuilds the full vector;
+ *   - "Why Palu Requires Fewer Global Memory Access": per head group i the cache
+ *     holds H_i (L x r) in place of the key K_i (L x d_h); K_i = H_i B_i with
+ *     B_i (r x d_h); only q_i, H_i and B are read from global memory, and the
+ *     rebuilt keys stay on chip;
+ *   - "Quantitive Analysis": heads are decomposed per group (G-LRD); one group
+ *     over all heads is the joint form (J-LRD);
+ *   - clarification of W1: values are never rebuilt; B_v is applied after the
+ *     attention-weighted sum of value latents, and key reconstruction is needed
+ *     only because of the rotary embedding.
+ * Attention itself is softmax(q K^T / sqrt(d)) V (CurDKV author response,
+ * paperhub page "klmc4fwPLd", motivation of value-guided compression). The
+ * rotary embedding turns each pair of a key by the 2x2 rotation
+ * [[cos, -sin], [sin, cos]] (CommVQ author response, paperhub page
+ * "sbbyCB39HN", proof of Property 1); frequencies theta^(-2i/d) and the pairing
+ * (i, i + d/2) are this library's reading, the pages being silent on both.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are device pointers, owned by the caller, row-major
+ *     with the last index contiguous. The library never allocates, frees or
+ *     synchronises in these calls; it enqueues kernels on `stream`
+ *     (a hipStream_t; NULL is the null stream) and returns.
+ *   - Validation is done on the host before any HIP call; on an error nothing
+ *     is launched and palu_last_error() gives a one-line reason (thread-local).
+ *   - The library keeps no state between calls except that text and the
+ *     optional profiling records below; calls are re-entrant.
+ *   - Conditions only the device can see (a length above max_ctx, an append
+ *     position outside [0, max_ctx)) are not errors: lengths are clamped to
+ *     [0, max_ctx] and out-of-range append rows are skipped.
+ */
+#ifndef PALU_H
+#define PALU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum palu_status {
+  PALU_OK = 0,
+  PALU_ERR_NULL = 1,        /* a required pointer is NULL                           */
+  PALU_ERR_SHAPE = 2,       /* sizes inconsistent or out of the supported range    */
+  PALU_ERR_UNSUPPORTED = 3, /* dtype/mode/theta combination not provided           */
+  PALU_ERR_WORKSPACE = 4,   /* workspace smaller than palu_decode_attn_workspace   */
+  PALU_ERR_DEVICE = 5       /* a HIP call or kernel launch failed                   */
+} palu_status;
+
+typedef enum palu_dtype { PALU_F32 = 0, PALU_BF16 = 1 } palu_dtype;
+
+typedef enum palu_mode {
+  /* rebuild K = H_k B_k per tile on chip, rotate, score against q */
+  PALU_MODE_RECONSTRUCT = 0,
+  /* no rotary embedding: score q~ = q B_k^T against H_k directly */
+  PALU_MODE_ABSORBED = 1
+} palu_mode;
+
+/* Shapes: B = batch, Hq = query heads, Hkv = KV heads, d = head dim,
+ * G = head groups, s = Hkv / G heads per group, D_g = s * d, r = rank per
+ * group, L_cap = max_ctx. KV head j belongs to group j / s and uses columns
+ * (j % s) * d .. (j % s + 1) * d of its group's B; query head h reads KV head
+ * h / (Hq / Hkv). */
+typedef struct palu_attn_desc {
+  int32_t batch;        /* B   >= 1                                             */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads                          */
+  int32_t n_kv_heads;   /* Hkv, a multiple of n_groups                           */
+  int32_t head_dim;     /* d, even, 2..256                                       */
+  int32_t n_groups;     /* G >= 1                                                */
+  int32_t rank;         /* r, 1..512                                             */
+  int32_t max_ctx;      /* L_cap >= 1: rows per (b, g) and the cache's row stride */
+  int32_t dtype;        /* palu_dtype of q, h_k, h_v, b_k, b_v; out is fp32       */
+  int32_t mode;         /* palu_mode                                             */
+  int32_t split_tokens; /* tokens per context split; 0 picks one; else a multiple of 64 */
+  float scale;          /* softmax scale; <= 0 means 1/sqrt(d)                   */
+  double rope_theta;    /* RoPE base; 0 means none; must be 0 in ABSORBED mode   */
+} palu_attn_desc;
+
+/* Bytes of device workspace palu_decode_attn needs for this descriptor
+ * (split partials and, in ABSORBED mode, the absorbed queries). */
+palu_status palu_decode_attn_workspace(const palu_attn_desc* desc, size_t* bytes);
+
+/* Launch plan for this descriptor: number of context splits, tokens per split
+ * and the name of the main kernel (a static string). Any output may be NULL. */
+palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
+                                  int32_t* split_tokens, const char** kernel);
+
+/* out[b, h, :] = sum_t softmax_t(scale * <q[b,h], RoPE_t(K_j[t])>) * V_j[t]
+ * with K_j = h_k[b, g] B_k[g][:, cols(j)], V_j = h_v[b, g] B_v[g][:, cols(j)],
+ * t in [0, len[b]); V_j is never formed: the weighted sum runs over h_v rows and
+ * B_v is applied once per head afterwards.
+ *   q        [B, Hq, d]          dtype
+ *   h_k, h_v [B, G, L_cap, r]    dtype; rows >= len[b] are never read
+ *   b_k, b_v [G, r, D_g]         dtype
+ *   seq_lens [B] int32 on the device, or NULL for len[b] = L_cap
+ *   out      [B, Hq, d] fp32; a sequence of length 0 gives zeros
+ *   workspace, workspace_bytes: device scratch of at least the size reported by
+ *            palu_decode_attn_workspace; its contents are overwritten.
+ * Errors: NULL for a missing pointer (only seq_lens may be NULL), SHAPE,
+ * UNSUPPORTED (ABSORBED with rope_theta != 0, unknown dtype/mode, rope_theta < 0),
+ * WORKSPACE, DEVICE (launch failure). */
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,
+                             const void* h_v, const void* b_k, const void* b_v,
+                             const int32_t* seq_lens, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+typedef struct palu_append_desc {
+  int32_t batch;     /* B >= 1                                                    */
+  int32_t d_model;   /* width of x, 1..65536                                      */
+  int32_t n_groups;  /* G >= 1                                                    */
+  int32_t rank;      /* r, 1..512                                                 */
+  int32_t max_ctx;   /* L_cap: row stride of the cache                             */
+  int32_t dtype;     /* palu_dtype of x, a_k, a_v and the cache                    */
+} palu_append_desc;
+
+/* Cache write of one token per sequence (answer to Q2: h = x A):
+ *   h_k[b, g, pos[b], :] = x[b] . a_k[:, g*r:(g+1)*r], likewise h_v with a_v.
+ *   x [B, d_model]; a_k, a_v [d_model, G*r]; h_k, h_v [B, G, L_cap, r];
+ *   pos [B] int32 on the device. Products are summed in fp32; a bf16 cache
+ *   stores the sum rounded to the nearest bf16 (ties to even). Rows with pos
+ *   outside [0, L_cap) are left untouched. Errors: NULL, SHAPE, UNSUPPORTED,
+ *   DEVICE. */
+palu_status palu_latent_append(const palu_append_desc* desc, const void* x, const void* a_k,
+                               const void* a_v, void* h_k, void* h_v, const int32_t* pos,
+                               void* stream);
+
+/* Optional timing of the main decode kernel (the context-split kernel) with HIP
+ * events on the stream it is launched on. palu_profile_begin(n) arms n records
+ * (events are created here, once); each later palu_decode_attn call records one
+ * start/stop pair around that kernel until n are used. palu_profile_end waits
+ * for the recorded events, returns the summed milliseconds and the count,
+ * releases the events and disarms. Not thread-safe; for benchmarks. */
+palu_status palu_profile_begin(int32_t max_records);
+palu_status palu_profile_end(double* total_ms, int32_t* count);
+
+const char* palu_status_string(palu_status status);
+const char* palu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PALU_H */

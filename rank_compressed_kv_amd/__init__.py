@@ -1,0 +1,247 @@
+"""Python binding of libpalu: decode attention over a low-rank latent KV cache
+on MI355X (gfx950).
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices against the descriptor, then calls the C ABI of include/palu.h with
+raw device pointers and torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels. If libpalu.so is missing the
+calls raise; there is no fallback.
+
+Layouts (row-major): q [B, Hq, d]; h_k, h_v [B, G, L_cap, r]; b_k, b_v
+[G, r, s*d]; seq_lens [B] int32; out [B, Hq, d] float32; x [B, d_model];
+a_k, a_v [d_model, G*r]; pos [B] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
+           "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "library", "library_path",
+           "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+           "palu_latent_append", "palu_profile_begin", "palu_profile_end",
+           "attn_desc", "append_desc", "decode_attention", "latent_append",
+           "EXPORTED_SYMBOLS"]
+
+PALU_OK, PALU_ERR_NULL, PALU_ERR_SHAPE, PALU_ERR_UNSUPPORTED, PALU_ERR_WORKSPACE, \
+    PALU_ERR_DEVICE = range(6)
+PALU_F32, PALU_BF16 = 0, 1
+PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED = 0, 1
+
+EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+                    "palu_latent_append", "palu_profile_begin", "palu_profile_end",
+                    "palu_status_string", "palu_last_error")
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("PALU_LIBRARY", os.path.join(_DIR, "libpalu.so"))
+
+
+class PaluError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("rope_theta", ctypes.c_double)]
+
+
+class AppendDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libpalu.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libpalu.so not found at {path}: build it with "
+                           f"`python -m rank_compressed_kv_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)
+    lib.palu_decode_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
+    lib.palu_decode_attn_plan.argtypes = [ctypes.POINTER(AttnDesc), i32p, i32p,
+                                          ctypes.POINTER(ctypes.c_char_p)]
+    lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]
+    lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp]
+    lib.palu_profile_begin.argtypes = [ctypes.c_int32]
+    lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
+    for fn in ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+               "palu_latent_append", "palu_profile_begin", "palu_profile_end"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.palu_status_string.argtypes = [ctypes.c_int]
+    lib.palu_status_string.restype = ctypes.c_char_p
+    lib.palu_last_error.argtypes = []
+    lib.palu_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != PALU_OK:
+        lib = library()
+        detail = (lib.palu_last_error() or b"").decode() or lib.palu_status_string(status).decode()
+        raise PaluError(status, where, detail)
+
+
+# ------------------------------------------------------------------ raw ABI ---
+
+def palu_decode_attn_workspace(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().palu_decode_attn_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "palu_decode_attn_workspace")
+    return int(n.value)
+
+
+def palu_decode_attn_plan(desc: AttnDesc) -> Tuple[int, int, str]:
+    ns, st, name = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_char_p()
+    _check(library().palu_decode_attn_plan(ctypes.byref(desc), ctypes.byref(ns), ctypes.byref(st),
+                                           ctypes.byref(name)), "palu_decode_attn_plan")
+    return int(ns.value), int(st.value), name.value.decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PALU_F32
+    if t.dtype == torch.bfloat16:
+        return PALU_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_TORCH_DTYPE = {PALU_F32: torch.float32, PALU_BF16: torch.bfloat16}
+
+
+def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace,
+                     stream=None) -> None:
+    """Enqueue one decode step. All tensors are checked against desc first."""
+    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    G, r, L = desc.n_groups, desc.rank, desc.max_ctx
+    dg = (Hkv // G) * d
+    dt = _TORCH_DTYPE.get(desc.dtype)
+    if dt is None:
+        raise TypeError(f"unknown dtype code {desc.dtype}")
+    _need(q, "q", (B, Hq, d), dt)
+    _need(h_k, "h_k", (B, G, L, r), dt)
+    _need(h_v, "h_v", (B, G, L, r), dt)
+    _need(b_k, "b_k", (G, r, dg), dt)
+    _need(b_v, "b_v", (G, r, dg), dt)
+    _need(out, "out", (B, Hq, d), torch.float32)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", (B,), torch.int32)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().palu_decode_attn(
+        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), b_k.data_ptr(),
+        b_v.data_ptr(), None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
+
+
+def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, stream=None) -> None:
+    B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
+    dt = _TORCH_DTYPE.get(desc.dtype)
+    if dt is None:
+        raise TypeError(f"unknown dtype code {desc.dtype}")
+    _need(x, "x", (B, dm), dt)
+    _need(a_k, "a_k", (dm, G * r), dt)
+    _need(a_v, "a_v", (dm, G * r), dt)
+    _need(h_k, "h_k", (B, G, L, r), dt)
+    _need(h_v, "h_v", (B, G, L, r), dt)
+    _need(pos, "pos", (B,), torch.int32)
+    _check(library().palu_latent_append(
+        ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),
+        h_v.data_ptr(), pos.data_ptr(), _stream(stream)), "palu_latent_append")
+
+
+def palu_profile_begin(max_records: int) -> None:
+    _check(library().palu_profile_begin(int(max_records)), "palu_profile_begin")
+
+
+def palu_profile_end() -> Tuple[float, int]:
+    ms, n = ctypes.c_double(0), ctypes.c_int32(0)
+    _check(library().palu_profile_end(ctypes.byref(ms), ctypes.byref(n)), "palu_profile_end")
+    return float(ms.value), int(n.value)
+
+
+# ------------------------------------------------------------- convenience ---
+
+def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_groups: int,
+              rank: int, max_ctx: int, dtype: int, mode: str = "reconstruct",
+              rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0) -> AttnDesc:
+    modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED}
+    if mode not in modes:
+        raise ValueError(f"mode must be one of {sorted(modes)}")
+    return AttnDesc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
+                    n_groups=n_groups, rank=rank, max_ctx=max_ctx, dtype=dtype, mode=modes[mode],
+                    split_tokens=split_tokens, scale=scale, rope_theta=rope_theta)
+
+
+def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: int,
+                dtype: int) -> AppendDesc:
+    return AppendDesc(batch=batch, d_model=d_model, n_groups=n_groups, rank=rank,
+                      max_ctx=max_ctx, dtype=dtype)
+
+
+def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
+                     mode: str = "reconstruct", rope_theta: float = 0.0, scale: float = 0.0,
+                     split_tokens: int = 0, out=None, workspace=None, stream=None):
+    """Shapes are read from the tensors; n_kv_heads fixes the head layout.
+    Allocates out and the workspace with torch when they are not given."""
+    B, Hq, d = q.shape
+    _, G, L, r = h_k.shape
+    desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, n_groups=G,
+                     rank=r, max_ctx=L, dtype=_dt(q), mode=mode, rope_theta=rope_theta,
+                     scale=scale, split_tokens=split_tokens)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
+                                device=q.device)
+    palu_decode_attn(desc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace, stream)
+    return out
+
+
+def latent_append(x, a_k, a_v, h_k, h_v, pos, stream=None) -> None:
+    B, dm = x.shape
+    _, G, L, r = h_k.shape
+    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
+    palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, stream)

@@ -1,0 +1,274 @@
+// Host side of libpalu: descriptor validation (before any HIP call), launch
+// planning and dispatch onto the caller's stream. See include/palu.h.
+#include "palu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "palu_internal.h"
+
+namespace palu {
+
+size_t generic_split_smem(const DecodeParams& p, int absorbed);
+
+namespace {
+
+thread_local std::string g_error;
+
+palu_status fail(palu_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+palu_status fail(palu_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+palu_status ok() {
+  g_error.clear();
+  return PALU_OK;
+}
+
+constexpr int kSplitQuantum = 64;    // split sizes are multiples of this many tokens
+constexpr int kTargetWorkgroups = 1024;
+
+palu_status validate_attn(const palu_attn_desc* d) {
+  if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->n_groups < 1 || d->rank < 1 || d->max_ctx < 1)
+    return fail(PALU_ERR_SHAPE, "all sizes must be positive");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(PALU_ERR_SHAPE, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->n_kv_heads % d->n_groups)
+    return fail(PALU_ERR_SHAPE, "n_kv_heads (%d) is not a multiple of n_groups (%d)",
+                d->n_kv_heads, d->n_groups);
+  if (d->head_dim % 2 || d->head_dim > 2 * kMaxHalfDim)
+    return fail(PALU_ERR_SHAPE, "head_dim (%d) must be even and at most %d", d->head_dim,
+                2 * kMaxHalfDim);
+  if (d->rank > 512) return fail(PALU_ERR_SHAPE, "rank (%d) must be at most 512", d->rank);
+  if (d->split_tokens < 0 || d->split_tokens % kSplitQuantum)
+    return fail(PALU_ERR_SHAPE, "split_tokens (%d) must be 0 or a positive multiple of %d",
+                d->split_tokens, kSplitQuantum);
+  if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
+    return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->mode != PALU_MODE_RECONSTRUCT && d->mode != PALU_MODE_ABSORBED)
+    return fail(PALU_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
+  if (!(d->rope_theta >= 0.0) || std::isinf(d->rope_theta))
+    return fail(PALU_ERR_UNSUPPORTED, "rope_theta must be finite and >= 0");
+  if (d->mode == PALU_MODE_ABSORBED && d->rope_theta != 0.0)
+    return fail(PALU_ERR_UNSUPPORTED,
+                "ABSORBED mode needs rope_theta == 0: a rotated key cannot absorb B_k into q");
+  const double rows = double(d->batch) * d->n_groups * d->max_ctx;
+  if (rows * d->rank > 9.0e15) return fail(PALU_ERR_SHAPE, "cache too large");
+  return PALU_OK;
+}
+
+struct Plan {
+  int n_split;
+  int split_tokens;
+  SplitKernel kernel;
+};
+
+Plan make_plan(const palu_attn_desc* d) {
+  Plan pl{};
+  pl.kernel = SplitKernel::kGeneric;
+  int st = d->split_tokens;
+  if (st == 0) {
+    // about kTargetWorkgroups context splits over all (b, g) pairs
+    const double want = double(d->max_ctx) * d->batch * d->n_groups / kTargetWorkgroups;
+    st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
+    if (st < kSplitQuantum) st = kSplitQuantum;
+    if (st > 4096) st = 4096;
+  }
+  pl.split_tokens = st;
+  pl.n_split = (d->max_ctx + st - 1) / st;
+  return pl;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WorkspaceLayout {
+  size_t qt, ml, u, total;
+};
+
+WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
+  WorkspaceLayout w{};
+  const size_t heads = size_t(d->batch) * d->n_q_heads;
+  w.qt = 0;
+  const size_t qt_bytes = d->mode == PALU_MODE_ABSORBED ? align256(heads * d->rank * 4) : 0;
+  w.ml = w.qt + qt_bytes;
+  w.u = w.ml + align256(heads * pl.n_split * 2 * 4);
+  w.total = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
+  return w;
+}
+
+struct Profiler {
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+  bool armed = false;
+} g_prof;
+
+}  // namespace
+
+const char* split_kernel_name(SplitKernel k) {
+  switch (k) {
+    case SplitKernel::kGeneric: return "split_generic_kernel";
+  }
+  return "?";
+}
+
+}  // namespace palu
+
+using namespace palu;
+
+extern "C" {
+
+const char* palu_status_string(palu_status s) {
+  switch (s) {
+    case PALU_OK: return "ok";
+    case PALU_ERR_NULL: return "null pointer";
+    case PALU_ERR_SHAPE: return "bad shape";
+    case PALU_ERR_UNSUPPORTED: return "unsupported";
+    case PALU_ERR_WORKSPACE: return "workspace too small";
+    case PALU_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* palu_last_error(void) { return g_error.c_str(); }
+
+palu_status palu_decode_attn_workspace(const palu_attn_desc* desc, size_t* bytes) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
+  *bytes = layout(desc, make_plan(desc)).total;
+  return ok();
+}
+
+palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
+                                  int32_t* split_tokens, const char** kernel) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  const Plan pl = make_plan(desc);
+  if (n_split) *n_split = pl.n_split;
+  if (split_tokens) *split_tokens = pl.split_tokens;
+  if (kernel) *kernel = split_kernel_name(pl.kernel);
+  return ok();
+}
+
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,
+                             const void* h_v, const void* b_k, const void* b_v,
+                             const int32_t* seq_lens, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  if (!q || !h_k || !h_v || !b_k || !b_v || !out || !workspace)
+    return fail(PALU_ERR_NULL, "q, h_k, h_v, b_k, b_v, out and workspace must be non-NULL");
+  const Plan pl = make_plan(desc);
+  const WorkspaceLayout wl = layout(desc, pl);
+  if (workspace_bytes < wl.total)
+    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
+
+  DecodeParams p{};
+  p.q = q; p.h_k = h_k; p.h_v = h_v; p.b_k = b_k; p.b_v = b_v;
+  p.lens = seq_lens; p.out = out;
+  char* ws = static_cast<char*>(workspace);
+  p.qt = reinterpret_cast<float*>(ws + wl.qt);
+  p.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+  p.part_u = reinterpret_cast<float*>(ws + wl.u);
+  p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.d = desc->head_dim;
+  p.G = desc->n_groups; p.r = desc->rank; p.L = desc->max_ctx;
+  p.s = p.Hkv / p.G; p.gqa = p.Hq / p.Hkv; p.nq = p.Hq / p.G; p.Dg = p.s * p.d;
+  p.n_split = pl.n_split; p.split_tokens = pl.split_tokens;
+  const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
+  p.scale_log2 = float(scale * 1.4426950408889634);
+  p.rope = desc->rope_theta > 0.0 ? 1 : 0;
+  for (int i = 0; i < p.d / 2; ++i)
+    p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int absorbed = desc->mode == PALU_MODE_ABSORBED;
+  hipError_t e = hipSuccess;
+  if (absorbed) e = launch_absorb_q(p, desc->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
+
+  const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
+  if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
+  e = launch_split_generic(p, desc->dtype, absorbed, s);
+  if (timed) (void)hipEventRecord(g_prof.stop[g_prof.used++], s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
+
+  e = launch_merge(p, desc->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+palu_status palu_latent_append(const palu_append_desc* d, const void* x, const void* a_k,
+                               const void* a_v, void* h_k, void* h_v, const int32_t* pos,
+                               void* stream) {
+  if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
+  if (d->batch < 1 || d->d_model < 1 || d->n_groups < 1 || d->rank < 1 || d->max_ctx < 1)
+    return fail(PALU_ERR_SHAPE, "all sizes must be positive");
+  if (d->d_model > 65536 || d->rank > 512)
+    return fail(PALU_ERR_SHAPE, "d_model must be <= 65536 and rank <= 512");
+  if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
+    return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (!x || !a_k || !a_v || !h_k || !h_v || !pos)
+    return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v and pos must be non-NULL");
+  AppendParams p{};
+  p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
+  p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
+  hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+palu_status palu_profile_begin(int32_t max_records) {
+  if (max_records < 1 || max_records > 100000)
+    return fail(PALU_ERR_SHAPE, "max_records must be in 1..100000");
+  if (g_prof.armed) return fail(PALU_ERR_UNSUPPORTED, "profiling already armed");
+  g_prof.start.assign(max_records, nullptr);
+  g_prof.stop.assign(max_records, nullptr);
+  for (int i = 0; i < max_records; ++i) {
+    if (hipEventCreate(&g_prof.start[i]) != hipSuccess ||
+        hipEventCreate(&g_prof.stop[i]) != hipSuccess)
+      return fail(PALU_ERR_DEVICE, "hipEventCreate failed");
+  }
+  g_prof.used = 0;
+  g_prof.armed = true;
+  return ok();
+}
+
+palu_status palu_profile_end(double* total_ms, int32_t* count) {
+  if (!g_prof.armed) return fail(PALU_ERR_UNSUPPORTED, "profiling not armed");
+  double sum = 0.0;
+  palu_status st = PALU_OK;
+  for (int i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.stop[i]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.start[i], g_prof.stop[i]) != hipSuccess) {
+      st = fail(PALU_ERR_DEVICE, "event timing failed");
+      break;
+    }
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (count) *count = g_prof.used;
+  for (size_t i = 0; i < g_prof.start.size(); ++i) {
+    if (g_prof.start[i]) (void)hipEventDestroy(g_prof.start[i]);
+    if (g_prof.stop[i]) (void)hipEventDestroy(g_prof.stop[i]);
+  }
+  g_prof = Profiler{};
+  return st == PALU_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Small device helpers shared by the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace palu {
+
+// Storage element -> fp32. bf16 is held as raw 16-bit patterns: the value is
+// the fp32 number whose upper half is those bits, so widening is exact.
+__device__ __forceinline__ float load_f32(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_f32(const uint16_t* p, size_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, nearest with ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
+
+// cos and sin of the rotary angle at integer position t for a pair whose
+// frequency is omega_rev revolutions per position. The product and the
+// removal of whole turns are done in fp64 (exact enough for t up to 2^31), so
+// the fp32 sincos only sees an angle in [-pi, pi].
+__device__ __forceinline__ void rope_cos_sin(double omega_rev, int t, float& c, float& s) {
+  double rev = static_cast<double>(t) * omega_rev;
+  rev -= rint(rev);
+  const float ang = static_cast<float>(rev * 6.283185307179586476925);
+  sincosf(ang, &s, &c);
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int L) {
+  if (!lens) return L;
+  const int n = lens[b];
+  return n < 0 ? 0 : (n > L ? L : n);
+}
+
+}  // namespace palu

@@ -1,0 +1,58 @@
+// Internal interface between the host API (api.cpp) and the HIP kernels.
+// Not installed; callers use include/palu.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace palu {
+
+constexpr int kMaxHalfDim = 128;   // head_dim <= 256
+
+// Everything a decode launch needs, passed by value as the kernel argument.
+struct DecodeParams {
+  const void* q;        // [B, Hq, d]
+  const void* h_k;      // [B, G, L, r]
+  const void* h_v;      // [B, G, L, r]
+  const void* b_k;      // [G, r, Dg]
+  const void* b_v;      // [G, r, Dg]
+  const int32_t* lens;  // [B] or nullptr (all L)
+  float* out;           // [B, Hq, d]
+  float* qt;            // [B, Hq, r]     absorbed queries, pre-scaled to log2 units
+  float* part_ml;       // [B, Hq, n_split, 2]   running max (log2 units) and sum
+  float* part_u;        // [B, Hq, n_split, r]   unnormalised value-latent sums
+  int32_t B, Hq, Hkv, d, G, r, L;
+  int32_t s, gqa, nq, Dg;      // heads per group, q heads per kv head, q heads per group
+  int32_t n_split, split_tokens;
+  int32_t rope;                // 1 if rotary embedding is applied
+  float scale_log2;            // softmax scale * log2(e)
+  // omega_i / (2 pi) in fp64 for i < d/2: the pair turns by t * omega_rev[i]
+  // revolutions at position t
+  double omega_rev[kMaxHalfDim];
+};
+
+struct AppendParams {
+  const void* x;      // [B, dm]
+  const void* a_k;    // [dm, G*r]
+  const void* a_v;
+  void* h_k;          // [B, G, L, r]
+  void* h_v;
+  const int32_t* pos; // [B]
+  int32_t B, dm, G, r, L;
+};
+
+// Kernel variants of the context-split decode step.
+enum class SplitKernel {
+  kGeneric = 0,        // VALU, any dtype/shape in range
+};
+
+const char* split_kernel_name(SplitKernel k);
+
+// Launchers return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
+hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
+hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
+hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
+hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
+
+}  // namespace palu

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_compressed_kv_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "palu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.library_path()):
+        from rank_compressed_kv_amd import build
+        build.build()
+    return P.library()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(palu_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert set(declared) == set(P.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _desc(**kw):
+    base = dict(batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, n_groups=2, rank=256,
+                max_ctx=32768, dtype=P.PALU_BF16, mode="absorbed")
+    base.update(kw)
+    return P.attn_desc(**base)
+
+
+BAD = [
+    (dict(batch=0), P.PALU_ERR_SHAPE),
+    (dict(n_q_heads=30), P.PALU_ERR_SHAPE),
+    (dict(n_groups=3), P.PALU_ERR_SHAPE),
+    (dict(head_dim=127), P.PALU_ERR_SHAPE),
+    (dict(head_dim=258), P.PALU_ERR_SHAPE),
+    (dict(rank=513), P.PALU_ERR_SHAPE),
+    (dict(rank=0), P.PALU_ERR_SHAPE),
+    (dict(max_ctx=0), P.PALU_ERR_SHAPE),
+    (dict(split_tokens=100), P.PALU_ERR_SHAPE),
+    (dict(split_tokens=-64), P.PALU_ERR_SHAPE),
+    (dict(dtype=7), P.PALU_ERR_UNSUPPORTED),
+    (dict(rope_theta=5e5), P.PALU_ERR_UNSUPPORTED),          # absorbed + RoPE
+    (dict(mode="reconstruct", rope_theta=-1.0), P.PALU_ERR_UNSUPPORTED),
+    (dict(mode="reconstruct", rope_theta=float("nan")), P.PALU_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_descriptor_validation(lib, kw, status):
+    d = _desc(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.palu_decode_attn_workspace(ctypes.byref(d), ctypes.byref(n)) == status
+    assert lib.palu_last_error()
+    # the decode call itself rejects the same descriptor before touching the device
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake,
+                                fake, 1 << 40, None) == status
+
+
+def test_bad_mode(lib):
+    d = _desc()
+    d.mode = 5
+    assert lib.palu_decode_attn_plan(ctypes.byref(d), None, None, None) == P.PALU_ERR_UNSUPPORTED
+
+
+def test_null_pointers_and_workspace(lib):
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.palu_decode_attn(None, fake, fake, fake, fake, fake, None, fake, fake, 1 << 40,
+                                None) == P.PALU_ERR_NULL
+    for i in range(7):
+        ptrs = [fake] * 7
+        ptrs[i] = None
+        q, hk, hv, bk, bv, out, ws = ptrs
+        assert lib.palu_decode_attn(ctypes.byref(d), q, hk, hv, bk, bv, None, out, ws, 1 << 40,
+                                    None) == P.PALU_ERR_NULL
+    need = P.palu_decode_attn_workspace(d)
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake,
+                                need - 1, None) == P.PALU_ERR_WORKSPACE
+    assert b"needs" in lib.palu_last_error()
+
+
+def test_workspace_covers_partials_and_plan_covers_context(lib):
+    for mode in ("absorbed", "reconstruct"):
+        for st in (0, 64, 512, 4096):
+            d = _desc(mode=mode, split_tokens=st)
+            ns, tok, name = P.palu_decode_attn_plan(d)
+            assert tok % 64 == 0 and ns * tok >= d.max_ctx > (ns - 1) * tok
+            if st:
+                assert tok == st
+            heads = d.batch * d.n_q_heads
+            need = P.palu_decode_attn_workspace(d)
+            assert need >= heads * ns * (d.rank + 2) * 4
+            if mode == "absorbed":
+                assert need >= heads * ns * (d.rank + 2) * 4 + heads * d.rank * 4
+            assert isinstance(name, str) and name
+
+
+def test_append_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    good = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
+                         dtype=P.PALU_BF16)
+    bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
+           (dict(d_model=70000), P.PALU_ERR_SHAPE), (dict(dtype=3), P.PALU_ERR_UNSUPPORTED)]
+    for kw, status in bad:
+        d = P.AppendDesc(**{**{f: getattr(good, f) for f, _ in P.AppendDesc._fields_}, **kw})
+        assert lib.palu_latent_append(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
+                                      None) == status
+    assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, None, fake, fake,
+                                  None) == P.PALU_ERR_NULL
+    assert lib.palu_latent_append(None, fake, fake, fake, fake, fake, fake,
+                                  None) == P.PALU_ERR_NULL
+
+
+def test_profile_calls_validate(lib):
+    assert lib.palu_profile_end(None, None) == P.PALU_ERR_UNSUPPORTED
+    assert lib.palu_profile_begin(0) == P.PALU_ERR_SHAPE
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.palu_status_string(s)
+    assert lib.palu_status_string(42) == b"unknown status"
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    d = _desc(batch=1, max_ctx=64)
+    q = torch.zeros(1, 32, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        P.palu_decode_attn(d, q, q, q, q, q, None, q, q)

@@ -1,0 +1,142 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs, element by element, at sizes the oracle finishes in
+seconds; the bar is max |d| <= 2e-2 and relative L2 <= 5e-3 (fp32 workloads:
+1e-4 and 1e-5)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import palu_oracle as O
+from tests.parity_util import assert_close, dev, run_decode
+
+pytestmark = pytest.mark.gpu
+
+# reduced context so the oracle is quick; lengths chosen off the 64-token grid
+SMALL = {
+    1: W.CONFIGS[1],
+    2: W.CONFIGS[2].scaled(batch=2, max_ctx=1000),
+    3: W.CONFIGS[3].scaled(batch=2, max_ctx=1500),
+    4: W.CONFIGS[4].scaled(max_ctx=3000),
+    5: W.CONFIGS[5].scaled(batch=4, max_ctx=2048, ragged=(1, 2048)),
+}
+CASES = [(i, m) for i in SMALL for m in SMALL[i].modes]
+
+
+def _tol(cfg):
+    return dict(max_abs=1e-4, rel_l2=1e-5) if cfg.dtype == "f32" else {}
+
+
+def _oracle(cfg, t, theta, lens=None):
+    lens = t["lens"] if lens is None else lens
+    return O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], lens,
+                              rope_theta=theta)
+
+
+@pytest.mark.parametrize("idx,mode", CASES)
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_parity_reduced(idx, mode, split_tokens):
+    cfg = SMALL[idx]
+    t = W.generate(cfg)
+    print(f"[parity] cfg{idx} {cfg.name} mode={mode} split={split_tokens} lens={t['lens'].tolist()}",
+          flush=True)
+    got, theta = run_decode(cfg, t, mode, split_tokens=split_tokens)
+    want = _oracle(cfg, t, theta)
+    assert_close(got, want, what=f"cfg{idx}/{mode}", **_tol(cfg))
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_reconstruct_without_rope_equals_absorbed(idx):
+    """With theta = 0 the two key paths compute the same scores."""
+    cfg = SMALL[idx]
+    t = W.generate(cfg)
+    a, _ = run_decode(cfg, t, "absorbed")
+    b, _ = run_decode(cfg, t, "reconstruct", rope_theta=0.0)
+    assert_close(a, b, what="absorbed vs reconstruct", **_tol(cfg))
+
+
+@pytest.mark.parametrize("idx,mode", [(1, "absorbed"), (1, "reconstruct"), (3, "absorbed"),
+                                      (3, "reconstruct"), (5, "reconstruct")])
+def test_length_edges_and_poisoned_tail(idx, mode):
+    """Lengths 0, 1, around the split size and the capacity; rows past each length
+    are NaN, so any read beyond the context shows up."""
+    base = SMALL[idx]
+    L = 640
+    edge = [0, 1, 63, 64, 65, 129, 511, L]
+    cfg = base.scaled(batch=len(edge), max_ctx=L, ragged=None)
+    t = W.generate(cfg, lens=np.array(edge))
+    hk, hv = W.poison_tail(t["h_k"], t["lens"]), W.poison_tail(t["h_v"], t["lens"])
+    for st in (64, 128, 0):
+        print(f"[edges] cfg{idx} mode={mode} split={st}", flush=True)
+        got, theta = run_decode(cfg, t, mode, split_tokens=st, h_k=hk, h_v=hv)
+        want = _oracle(cfg, t, theta)
+        assert np.all(got[0] == 0.0)
+        assert_close(got, want, what=f"edges cfg{idx}/{mode}/split{st}", **_tol(cfg))
+
+
+def test_null_lens_means_full_capacity():
+    cfg = SMALL[3].scaled(max_ctx=300)
+    t = W.generate(cfg)
+    got, theta = run_decode(cfg, t, "reconstruct", lens=False)
+    want = _oracle(cfg, t, theta, lens=np.full(cfg.batch, cfg.max_ctx))
+    assert_close(got, want, what="lens=NULL")
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+def test_latent_append(idx):
+    """h[b, g, pos[b]] = x[b] A: bf16 rows agree with the oracle's fp32-then-bf16
+    rounding except where the exact value sits within the fp32 summation error
+    of a rounding midpoint; rows other than pos[b] are untouched."""
+    import torch
+    import rank_compressed_kv_amd as P
+    base = W.CONFIGS[idx]
+    cfg = base.scaled(batch=min(base.batch, 4), max_ctx=64, ragged=None)
+    t = W.generate(cfg, parts=("decode", "append"))
+    hk, hv = dev(t["h_k"]), dev(t["h_v"])
+    before_k = hk.clone()
+    P.latent_append(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv, dev(t["pos"]))
+    torch.cuda.synchronize()
+    G, r = cfg.n_groups, cfg.rank
+    for name, cache, a in (("k", hk, t["a_k"]), ("v", hv, t["a_v"])):
+        want64 = O.latent_project(t["x"], a)                  # [B, G*r]
+        c = cache.cpu()
+        for b, pos in enumerate(t["pos"]):
+            row = c[b, :, int(pos), :].reshape(-1)
+            if cfg.dtype == "bf16":
+                got_bits = row.view(torch.int16).numpy().view(np.uint16)
+                want_bits = O.append_rows_bf16(want64[b])
+                bad = got_bits != want_bits
+                if bad.any():
+                    # a differing row element must be the neighbouring bf16 value,
+                    # and the exact value must lie within the worst-case fp32
+                    # summation error (d_model * 2^-24 * sum |x_i a_i|) of the
+                    # midpoint between the two
+                    assert np.all(np.abs(got_bits[bad].astype(np.int32)
+                                         - want_bits[bad].astype(np.int32)) == 1), name
+                    g = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    wv = (want_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    mid = (g + wv) / 2
+                    bound = (np.sum(np.abs(O.to_f64(t["x"][b])[:, None] * O.to_f64(a)), 0)
+                             * cfg.d_model * 2.0 ** -24)
+                    assert np.all(np.abs(want64[b] - mid)[bad] <= bound[bad]), name
+                assert bad.mean() < 0.01
+            else:
+                np.testing.assert_allclose(row.numpy(), want64[b], rtol=1e-5, atol=1e-5)
+    # untouched rows
+    mask = torch.ones(cfg.batch, cfg.max_ctx, dtype=torch.bool)
+    for b, pos in enumerate(t["pos"]):
+        mask[b, int(pos)] = False
+    assert torch.equal(hk.cpu()[:, :, :, :].permute(0, 2, 1, 3)[mask],
+                       before_k.cpu().permute(0, 2, 1, 3)[mask])
+
+
+def test_append_out_of_range_rows_skipped():
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = W.CONFIGS[3].scaled(batch=2, max_ctx=16)
+    t = W.generate(cfg, parts=("decode", "append"))
+    hk, hv = dev(t["h_k"]), dev(t["h_v"])
+    before = (hk.clone(), hv.clone())
+    pos = torch.tensor([-1, 16], dtype=torch.int32, device="cuda")
+    P.latent_append(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(hk, before[0]) and torch.equal(hv, before[1])
