@@ -1,0 +1,269 @@
+"""Decode-step benchmark: latent-KV decode attention on one MI355X.
+
+A step is one pass of the hot path over the whole batch of one layer: the
+latent append of the new token (h = x A into row len-1 of both caches),
+then decode attention over the len rows (query absorption when applicable,
+the context-split kernel, the split merge with the B_v up-projection).
+
+Default workload: Llama-3-8B-shaped GQA (B=8, Hq=32, Hkv=8, d=128, 2 groups of
+4 KV heads at rank 256, 32768 tokens of context, bf16 latents), absorbed-key
+mode (no RoPE). The reconstruct+RoPE mode of the same shape is timed too and
+reported beside it. Inputs are seeded synthetic tensors resident in HBM before
+timing starts; several copies of the cache are rotated so that the 256 MB
+Infinity Cache cannot serve the latents.
+
+Prints ONE JSON line. Timing: W warm-up steps, then K steps between
+torch.cuda.synchronize() calls, timed with events on the launch stream. The
+main kernel is also timed alone with HIP events the library records around
+it (palu_profile_begin/end), which gives the roofline figure.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s + latent HBM GB/s (% peak), Llama-3-8B shape, 32K ctx"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 1.5 * 2 ** 30   # total size of the rotated cache copies
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--mode", default="absorbed", choices=["absorbed", "reconstruct"])
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip timing the other key mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="rough CPU time budget of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
+    """Returns dict with ms/step, kernel ms, and the output of the first step."""
+    theta = cfg.rope_theta if mode == "reconstruct" else 0.0
+    q, bk, bv = dev(torch, t["q"]), dev(torch, t["b_k"]), dev(torch, t["b_v"])
+    lens = dev(torch, t["lens"])
+    x, ak, av = dev(torch, t["x"]), dev(torch, t["a_k"]), dev(torch, t["a_v"])
+    pos = (lens - 1).to(torch.int32).contiguous()
+    hk0, hv0 = dev(torch, t["h_k"]), dev(torch, t["h_v"])
+    caches = [(hk0, hv0)] + [(hk0.clone(), hv0.clone()) for _ in range(n_copies - 1)]
+    desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
+                       max_ctx=cfg.max_ctx, dtype=P.PALU_BF16 if cfg.dtype == "bf16" else P.PALU_F32,
+                       mode=mode, rope_theta=theta, split_tokens=args.split_tokens)
+    adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=desc.dtype)
+    ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    n_split, split_tokens, kname = P.palu_decode_attn_plan(desc)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        hk, hv = caches[i % n_copies]
+        P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, stream)
+        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+
+    # the first step's output is kept for the sampled parity check; the append
+    # writes row len-1 of copy 0 (same bits as the generator's row replaced)
+    step(0)
+    torch.cuda.synchronize()
+    first_out = out.clone()
+    first_hk, first_hv = caches[0][0][:, :, :, :], caches[0][1]
+    for i in range(args.warmup):
+        step(i + 1)
+    torch.cuda.synchronize()
+    P.palu_profile_begin(args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms, kern_n = P.palu_profile_end()
+    total_ms = e0.elapsed_time(e1)
+    return dict(ms_per_step=total_ms / args.steps, kernel_ms=kern_ms / max(1, kern_n),
+                kernel=kname, n_split=n_split, split_tokens=split_tokens,
+                out=first_out.cpu().numpy(), hk_row=first_hk, hv_row=first_hv, pos=pos,
+                caches=caches)
+
+
+def sampled_parity(O, cfg, t, res, mode, pairs):
+    """Compare sampled (b, h) outputs of the first timed step with the oracle.
+    The oracle sees the cache after the step's append (row len-1 rewritten)."""
+    import torch
+    theta = cfg.rope_theta if mode == "reconstruct" else 0.0
+    hk = t["h_k"].copy()
+    hv = t["h_v"].copy()
+    hk_dev, hv_dev = res["caches"][0]
+    for b in range(cfg.batch):
+        p = int(t["lens"][b]) - 1
+        hk[b, :, p] = hk_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
+        hv[b, :, p] = hv_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.decode_attention(t["q"], hk, hv, t["b_k"], t["b_v"], t["lens"], rope_theta=theta,
+                              select=pairs)
+    got = res["out"].astype(np.float64)
+    idx = tuple(np.array(pairs).T)
+    d = got[idx] - want[idx]
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(want[idx]))
+
+
+def cpu_baseline(O, cfg, t, mode, budget_s):
+    """Time the oracle on the host cores on a bounded sample of the workload:
+    whole (b, g) pairs (all their query heads), as many as fit the budget."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    theta = cfg.rope_theta if mode == "reconstruct" else 0.0
+    heads_per_group = cfg.n_q_heads // cfg.n_groups
+    pairs_total = cfg.batch * cfg.n_groups
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b, g = divmod(done, cfg.n_groups)
+        sel = [(b, g * heads_per_group + i) for i in range(heads_per_group)]
+        O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"],
+                           rope_theta=theta, select=sel)
+        done += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or done == pairs_total:
+            break
+    frac = done / pairs_total
+    return {"value": frac / el, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {pairs_total} (batch, head-group) pairs of one step "
+                      f"({done * heads_per_group} of {cfg.batch * cfg.n_q_heads} query heads), "
+                      f"fp64 NumPy, {el:.1f} s; steps/s scaled by the sampled fraction"}
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch of the main kernel from committed counter runs, if any."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        return rec.get(kernel)
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import rank_compressed_kv_amd as P
+    import workloads as W
+    if not os.path.exists(P.library_path()):
+        from rank_compressed_kv_amd import build
+        build.build()
+    P.library()
+    torch.cuda.set_device(0)
+
+    cfg = W.CONFIGS[args.config]
+    t = W.generate(cfg, parts=("decode", "append"))
+    # the append writes row len-1, so the step attends over exactly len rows
+    lat_bytes = W.latent_bytes(cfg, t["lens"])
+    n_copies = max(1, int(math.ceil(ROTATE_BYTES / lat_bytes)))
+    print(f"[bench] cfg{args.config} {cfg.name}: latent bytes/step {lat_bytes}, "
+          f"{n_copies} cache copies", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    modes = [args.mode]
+    if not args.no_secondary:
+        modes += [m for m in cfg.modes if m != args.mode]
+    results = {}
+    for mode in modes:
+        res = time_mode(torch, P, W, cfg, t, mode, args, n_copies)
+        results[mode] = res
+        print(f"[bench] {mode}: {res['ms_per_step'] * 1e3:.1f} us/step, main kernel "
+              f"{res['kernel']} {res['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    from oracle import palu_oracle as O
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_q_heads))) for _ in range(4)]
+    parity = {}
+    for mode in modes:
+        parity[mode] = sampled_parity(O, cfg, t, results[mode], mode, pairs)
+    main_res = results[args.mode]
+    for r in results.values():
+        r.pop("caches")
+
+    ms = main_res["ms_per_step"]
+    steps_s = 1e3 / ms
+    gbs_step = lat_bytes / (ms * 1e-3) / 1e9
+    kern_gbs = lat_bytes / (main_res["kernel_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(main_res["kernel"])
+    line = {
+        "metric": METRIC,
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) bf16 latents, B ~ N(0,1/r)), no weights",
+        "config": {"workload": f"{cfg.name} {args.mode}: B={cfg.batch} Hq={cfg.n_q_heads} "
+                               f"Hkv={cfg.n_kv_heads} d={cfg.head_dim} G={cfg.n_groups} "
+                               f"r={cfg.rank} ctx={cfg.max_ctx}",
+                   "global_batch": cfg.batch, "seq_len": cfg.max_ctx, "parallelism": "none (1 GPU)",
+                   "mode": args.mode, "n_split": main_res["n_split"],
+                   "split_tokens": main_res["split_tokens"]},
+        "latent_GBps": round(gbs_step, 1),
+        "latent_pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": main_res["kernel"],
+                     "kernel_us": round(main_res["kernel_ms"] * 1e3, 2),
+                     "algorithmic_bytes": lat_bytes},
+        "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                      "kernel_us": round(r["kernel_ms"] * 1e3, 2), "kernel": r["kernel"],
+                      "latent_GBps_kernel": round(lat_bytes / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                      "sampled_parity_max_abs": parity[m][0],
+                      "sampled_parity_rel_l2": parity[m][1]}
+                  for m, r in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(O, cfg, t, args.mode, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

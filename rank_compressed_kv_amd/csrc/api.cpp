@@ -78,9 +78,21 @@ struct Plan {
   SplitKernel kernel;
 };
 
+// Shape fields of DecodeParams that kernel selection looks at.
+DecodeParams shape_params(const palu_attn_desc* d) {
+  DecodeParams p{};
+  p.B = d->batch; p.Hq = d->n_q_heads; p.Hkv = d->n_kv_heads; p.d = d->head_dim;
+  p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
+  p.s = p.Hkv / p.G; p.gqa = p.Hq / p.Hkv; p.nq = p.Hq / p.G; p.Dg = p.s * p.d;
+  return p;
+}
+
 Plan make_plan(const palu_attn_desc* d) {
   Plan pl{};
+  const DecodeParams sp = shape_params(d);
   pl.kernel = SplitKernel::kGeneric;
+  if (d->mode == PALU_MODE_ABSORBED && absorbed_mfma_supported(sp, d->dtype))
+    pl.kernel = SplitKernel::kAbsorbedMfma;
   int st = d->split_tokens;
   if (st == 0) {
     // about kTargetWorkgroups context splits over all (b, g) pairs
@@ -122,6 +134,7 @@ struct Profiler {
 const char* split_kernel_name(SplitKernel k) {
   switch (k) {
     case SplitKernel::kGeneric: return "split_generic_kernel";
+    case SplitKernel::kAbsorbedMfma: return "split_absorbed_mfma_kernel";
   }
   return "?";
 }
@@ -178,16 +191,13 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   if (workspace_bytes < wl.total)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
 
-  DecodeParams p{};
+  DecodeParams p = shape_params(desc);
   p.q = q; p.h_k = h_k; p.h_v = h_v; p.b_k = b_k; p.b_v = b_v;
   p.lens = seq_lens; p.out = out;
   char* ws = static_cast<char*>(workspace);
   p.qt = reinterpret_cast<float*>(ws + wl.qt);
   p.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   p.part_u = reinterpret_cast<float*>(ws + wl.u);
-  p.B = desc->batch; p.Hq = desc->n_q_heads; p.Hkv = desc->n_kv_heads; p.d = desc->head_dim;
-  p.G = desc->n_groups; p.r = desc->rank; p.L = desc->max_ctx;
-  p.s = p.Hkv / p.G; p.gqa = p.Hq / p.Hkv; p.nq = p.Hq / p.G; p.Dg = p.s * p.d;
   p.n_split = pl.n_split; p.split_tokens = pl.split_tokens;
   const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
   p.scale_log2 = float(scale * 1.4426950408889634);
@@ -203,7 +213,10 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
 
   const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
   if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
-  e = launch_split_generic(p, desc->dtype, absorbed, s);
+  switch (pl.kernel) {
+    case SplitKernel::kAbsorbedMfma: e = launch_split_absorbed_mfma(p, s); break;
+    default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
+  }
   if (timed) (void)hipEventRecord(g_prof.stop[g_prof.used++], s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
 

@@ -45,6 +45,7 @@ struct AppendParams {
 // Kernel variants of the context-split decode step.
 enum class SplitKernel {
   kGeneric = 0,        // VALU, any dtype/shape in range
+  kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {128, 256}, <= 16 q heads per group
 };
 
 const char* split_kernel_name(SplitKernel k);
@@ -52,6 +53,8 @@ const char* split_kernel_name(SplitKernel k);
 // Launchers return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
+bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
+hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 

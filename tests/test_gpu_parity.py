@@ -44,6 +44,19 @@ def test_parity_reduced(idx, mode, split_tokens):
     assert_close(got, want, what=f"cfg{idx}/{mode}", **_tol(cfg))
 
 
+@pytest.mark.parametrize("idx", [2, 4, 5])
+@pytest.mark.parametrize("split_tokens", [0, 64, 192])
+def test_parity_absorbed_other_shapes(idx, split_tokens):
+    """Absorbed keys (no RoPE) on the other head layouts: 4 query heads per group
+    (MHA), rank 128 with outlier channels, and one 32-head group at rank 512."""
+    cfg = SMALL[idx]
+    t = W.generate(cfg)
+    print(f"[absorbed] cfg{idx} split={split_tokens}", flush=True)
+    got, theta = run_decode(cfg, t, "absorbed", split_tokens=split_tokens)
+    assert theta == 0.0
+    assert_close(got, _oracle(cfg, t, 0.0), what=f"absorbed cfg{idx}")
+
+
 @pytest.mark.parametrize("idx", [1, 3])
 def test_reconstruct_without_rope_equals_absorbed(idx):
     """With theta = 0 the two key paths compute the same scores."""
