@@ -76,13 +76,14 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
                           rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=desc.dtype)
     ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(P.palu_latent_append_workspace(adesc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
     n_split, split_tokens, kname = P.palu_decode_attn_plan(desc)
     stream = torch.cuda.current_stream()
 
     def step(i):
         hk, hv = caches[i % n_copies]
-        P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, stream)
+        P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, aws, stream)
         P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
 
     # the first step's output is kept for the sampled parity check; the append

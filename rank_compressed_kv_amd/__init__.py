@@ -22,8 +22,8 @@ import torch
 __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "library", "library_path",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_latent_append", "palu_profile_begin", "palu_profile_end",
-           "attn_desc", "append_desc", "decode_attention", "latent_append",
+           "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+           "palu_profile_end", "attn_desc", "append_desc", "decode_attention", "latent_append",
            "EXPORTED_SYMBOLS"]
 
 PALU_OK, PALU_ERR_NULL, PALU_ERR_SHAPE, PALU_ERR_UNSUPPORTED, PALU_ERR_WORKSPACE, \
@@ -32,7 +32,8 @@ PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED = 0, 1
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-                    "palu_latent_append", "palu_profile_begin", "palu_profile_end",
+                    "palu_latent_append_workspace", "palu_latent_append",
+                    "palu_profile_begin", "palu_profile_end",
                     "palu_status_string", "palu_last_error")
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -82,11 +83,14 @@ def library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
-    lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp]
+    lib.palu_latent_append_workspace.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
+    lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp,
+                                       sz, vp]
     lib.palu_profile_begin.argtypes = [ctypes.c_int32]
     lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
     for fn in ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-               "palu_latent_append", "palu_profile_begin", "palu_profile_end"):
+               "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+               "palu_profile_end"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.palu_status_string.argtypes = [ctypes.c_int]
     lib.palu_status_string.restype = ctypes.c_char_p
@@ -176,7 +180,16 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
 
 
-def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, stream=None) -> None:
+def palu_latent_append_workspace(desc: AppendDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().palu_latent_append_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "palu_latent_append_workspace")
+    return int(n.value)
+
+
+def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, workspace,
+                       stream=None) -> None:
+    palu_latent_append_workspace(desc)   # the library validates the descriptor first
     B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
     dt = _TORCH_DTYPE.get(desc.dtype)
     if dt is None:
@@ -187,9 +200,13 @@ def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, stream=None
     _need(h_k, "h_k", (B, G, L, r), dt)
     _need(h_v, "h_v", (B, G, L, r), dt)
     _need(pos, "pos", (B,), torch.int32)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
     _check(library().palu_latent_append(
         ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),
-        h_v.data_ptr(), pos.data_ptr(), _stream(stream)), "palu_latent_append")
+        h_v.data_ptr(), pos.data_ptr(), workspace.data_ptr(), nbytes, _stream(stream)),
+        "palu_latent_append")
 
 
 def palu_profile_begin(max_records: int) -> None:
@@ -240,8 +257,12 @@ def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
     return out
 
 
-def latent_append(x, a_k, a_v, h_k, h_v, pos, stream=None) -> None:
+def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> None:
+    """Allocates the workspace with torch when it is not given."""
     B, dm = x.shape
     _, G, L, r = h_k.shape
     desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
-    palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, stream)
+    if workspace is None:
+        workspace = torch.empty(palu_latent_append_workspace(desc), dtype=torch.uint8,
+                                device=x.device)
+    palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, workspace, stream)

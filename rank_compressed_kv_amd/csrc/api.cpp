@@ -95,8 +95,12 @@ Plan make_plan(const palu_attn_desc* d) {
     pl.kernel = SplitKernel::kAbsorbedMfma;
   int st = d->split_tokens;
   if (st == 0) {
-    // about kTargetWorkgroups context splits over all (b, g) pairs
-    const double want = double(d->max_ctx) * d->batch * d->n_groups / kTargetWorkgroups;
+    // the generic kernel runs one workgroup per (split, head, batch); the MFMA
+    // kernel one per (split, group, batch) and fills a CU with one workgroup
+    const double units = pl.kernel == SplitKernel::kGeneric
+                             ? double(d->batch) * d->n_groups * 4.0
+                             : double(d->batch) * d->n_groups * kTargetWorkgroups / 256.0;
+    const double want = double(d->max_ctx) * units / kTargetWorkgroups;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
     if (st < kSplitQuantum) st = kSplitQuantum;
     if (st > 4096) st = 4096;
@@ -225,20 +229,42 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   return ok();
 }
 
-palu_status palu_latent_append(const palu_append_desc* d, const void* x, const void* a_k,
-                               const void* a_v, void* h_k, void* h_v, const int32_t* pos,
-                               void* stream) {
+namespace {
+palu_status validate_append(const palu_append_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
   if (d->batch < 1 || d->d_model < 1 || d->n_groups < 1 || d->rank < 1 || d->max_ctx < 1)
     return fail(PALU_ERR_SHAPE, "all sizes must be positive");
   if (d->d_model > 65536 || d->rank > 512)
     return fail(PALU_ERR_SHAPE, "d_model must be <= 65536 and rank <= 512");
+  if (double(d->n_groups) * d->rank > 65536.0)
+    return fail(PALU_ERR_SHAPE, "n_groups * rank must be <= 65536");
   if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
     return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
-  if (!x || !a_k || !a_v || !h_k || !h_v || !pos)
-    return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v and pos must be non-NULL");
+  return PALU_OK;
+}
+}  // namespace
+
+palu_status palu_latent_append_workspace(const palu_append_desc* d, size_t* bytes) {
+  palu_status st = validate_append(d);
+  if (st != PALU_OK) return st;
+  if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
+  return ok();
+}
+
+palu_status palu_latent_append(const palu_append_desc* d, const void* x, const void* a_k,
+                               const void* a_v, void* h_k, void* h_v, const int32_t* pos,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  palu_status st = validate_append(d);
+  if (st != PALU_OK) return st;
+  if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
+    return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
+  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
+  if (workspace_bytes < need)
+    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   AppendParams p{};
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
+  p.part = static_cast<float*>(workspace);
   p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
   hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));

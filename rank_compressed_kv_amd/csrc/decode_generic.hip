@@ -1,9 +1,7 @@
-// Plain VALU kernels of the decode step: query absorption, a context-split
-// attention kernel for any dtype and shape in range, and the split merge with
-// the value up-projection. The split kernel here handles one query head per
-// workgroup (the latents are re-read per head); the MFMA kernels in the other
-// files are the fast path for bf16, this one is the path for fp32 caches and
-// for shapes the fast kernels do not take.
+// Plain VALU context-split attention kernel for any dtype and shape in range.
+// It handles one query head per workgroup (the latents are re-read per head);
+// the MFMA kernels are the fast path for bf16, this one is the path for fp32
+// caches and for shapes the fast kernels do not take.
 //
 // Method (Palu author responses on OpenReview):
 //   K_j = H_k B_k[:, cols(j)]  ("Why Palu Requires Fewer Global Memory Access")
@@ -24,23 +22,6 @@ constexpr int kThreads = 256;
 constexpr int kTileTokens = 8;          // tokens per inner tile
 constexpr int kLanesPerToken = kThreads / kTileTokens;   // 32
 constexpr int kMaxRankPerThread = 2;    // rank <= 512
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int j = h / p.gqa, g = j / p.s, jl = j % p.s;
-  __shared__ float qs[2 * kMaxHalfDim];
-  const T* q = static_cast<const T*>(p.q) + (static_cast<size_t>(b) * p.Hq + h) * p.d;
-  for (int c = tid; c < p.d; c += kThreads) qs[c] = load_f32(q, c);
-  __syncthreads();
-  const T* bk = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
-  float* qt = p.qt + (static_cast<size_t>(b) * p.Hq + h) * p.r;
-  for (int k = tid; k < p.r; k += kThreads) {
-    float acc = 0.f;
-    for (int c = 0; c < p.d; ++c) acc = fmaf(qs[c], load_f32(bk, static_cast<size_t>(k) * p.Dg + c), acc);
-    qt[k] = acc * p.scale_log2;
-  }
-}
 
 template <typename T, bool kAbsorbed>
 __global__ __launch_bounds__(kThreads) void split_generic_kernel(DecodeParams p) {
@@ -154,69 +135,11 @@ __global__ __launch_bounds__(kThreads) void split_generic_kernel(DecodeParams p)
   }
 }
 
-// One workgroup per (head, batch): merge the live splits and apply B_v.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int n = clamp_len(p.lens, b, p.L);
-  const int ns = (n + p.split_tokens - 1) / p.split_tokens;
-  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
-  if (ns == 0) {
-    for (int c = tid; c < p.d; c += kThreads) out[c] = 0.f;
-    return;
-  }
-  const int j = h / p.gqa, g = j / p.s, jl = j % p.s;
-  const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
-  __shared__ float us[kMaxRankPerThread * kThreads];
-  __shared__ float red[kThreads];
-  // global max and weighted sum over splits: block reductions
-  float mloc = -INFINITY;
-  for (int sp = tid; sp < ns; sp += kThreads) mloc = fmaxf(mloc, p.part_ml[(base + sp) * 2]);
-  red[tid] = mloc;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float lloc = 0.f;
-  for (int sp = tid; sp < ns; sp += kThreads)
-    lloc += exp2f(p.part_ml[(base + sp) * 2] - M) * p.part_ml[(base + sp) * 2 + 1];
-  red[tid] = lloc;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  const float inv = 1.f / red[0];
-  for (int k = tid; k < p.r; k += kThreads) {
-    float acc = 0.f;
-    for (int sp = 0; sp < ns; ++sp)
-      acc = fmaf(exp2f(p.part_ml[(base + sp) * 2] - M), p.part_u[(base + sp) * p.r + k], acc);
-    us[k] = acc * inv;
-  }
-  __syncthreads();
-  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
-  for (int c = tid; c < p.d; c += kThreads) {
-    float acc = 0.f;
-    for (int k = 0; k < p.r; ++k) acc = fmaf(us[k], load_f32(Bv, static_cast<size_t>(k) * p.Dg + c), acc);
-    out[c] = acc;
-  }
-}
-
 }  // namespace
 
 size_t generic_split_smem(const DecodeParams& p, int absorbed) {
   const int dq = absorbed ? p.r : p.d;
   return sizeof(float) * (dq + 2 * kTileTokens * p.r + kTileTokens * p.d + kTileTokens);
-}
-
-hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
-  const dim3 grid(p.Hq, p.B);
-  if (dtype == 0) absorb_q_kernel<float><<<grid, kThreads, 0, st>>>(p);
-  else absorb_q_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
-  return hipGetLastError();
 }
 
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st) {
@@ -229,13 +152,6 @@ hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, 
     if (absorbed) split_generic_kernel<uint16_t, true><<<grid, kThreads, sm, st>>>(p);
     else split_generic_kernel<uint16_t, false><<<grid, kThreads, sm, st>>>(p);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st) {
-  const dim3 grid(p.Hq, p.B);
-  if (dtype == 0) merge_kernel<float><<<grid, kThreads, 0, st>>>(p);
-  else merge_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 

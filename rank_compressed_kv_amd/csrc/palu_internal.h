@@ -39,6 +39,7 @@ struct AppendParams {
   void* h_k;          // [B, G, L, r]
   void* h_v;
   const int32_t* pos; // [B]
+  float* part;        // [ceil(dm/128), B, 2*G*r] fp32 row-slice partial sums
   int32_t B, dm, G, r, L;
 };
 
@@ -56,6 +57,7 @@ hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, 
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
+size_t append_workspace_bytes(int B, int dm, int G, int r);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu

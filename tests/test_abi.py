@@ -115,14 +115,23 @@ def test_append_validation(lib):
                          dtype=P.PALU_BF16)
     bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
            (dict(d_model=70000), P.PALU_ERR_SHAPE), (dict(dtype=3), P.PALU_ERR_UNSUPPORTED)]
+    big = 1 << 40
     for kw, status in bad:
         d = P.AppendDesc(**{**{f: getattr(good, f) for f, _ in P.AppendDesc._fields_}, **kw})
         assert lib.palu_latent_append(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
-                                      None) == status
-    assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, None, fake, fake,
+                                      fake, big, None) == status
+        n = ctypes.c_size_t(0)
+        assert lib.palu_latent_append_workspace(ctypes.byref(d), ctypes.byref(n)) == status
+    for i in range(7):
+        ptrs = [fake] * 7
+        ptrs[i] = None
+        assert lib.palu_latent_append(ctypes.byref(good), *ptrs, big, None) == P.PALU_ERR_NULL
+    assert lib.palu_latent_append(None, fake, fake, fake, fake, fake, fake, fake, big,
                                   None) == P.PALU_ERR_NULL
-    assert lib.palu_latent_append(None, fake, fake, fake, fake, fake, fake,
-                                  None) == P.PALU_ERR_NULL
+    need = P.palu_latent_append_workspace(good)
+    assert need == 64 * 8 * 1024 * 4        # 64-row slices x batch x (k and v columns)
+    assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake,
+                                  need - 1, None) == P.PALU_ERR_WORKSPACE
 
 
 def test_profile_calls_validate(lib):
