@@ -121,7 +121,7 @@ typedef struct palu_append_desc {
 } palu_append_desc;
 
 /* Bytes of device workspace palu_latent_append needs for this descriptor
- * (fp32 partial sums over slices of 64 rows of d_model). */
+ * (fp32 partial sums over slices of 128 rows of d_model). */
 palu_status palu_latent_append_workspace(const palu_append_desc* desc, size_t* bytes);
 
 /* Cache write of one token per sequence (answer to Q2: h = x A):
@@ -129,9 +129,10 @@ palu_status palu_latent_append_workspace(const palu_append_desc* desc, size_t* b
  *   x [B, d_model]; a_k, a_v [d_model, G*r]; h_k, h_v [B, G, L_cap, r];
  *   pos [B] int32 on the device; workspace of at least the size reported by
  *   palu_latent_append_workspace (overwritten). Products are summed in fp32
- *   (per 64-row slice, then the slices in order); a bf16 cache stores the sum
+ *   (per 128-row slice, then the slices in order); a bf16 cache stores the sum
  *   rounded to the nearest bf16 (ties to even). Rows with pos outside
- *   [0, L_cap) are left untouched. Errors: NULL, SHAPE (also G*r > 65536),
+ *   [0, L_cap) are left untouched. Errors: NULL, SHAPE (also G*r > 65536 or
+ *   G*r not a multiple of 8),
  *   UNSUPPORTED, WORKSPACE, DEVICE. */
 palu_status palu_latent_append(const palu_append_desc* desc, const void* x, const void* a_k,
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,

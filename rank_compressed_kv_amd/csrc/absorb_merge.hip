@@ -1,18 +1,19 @@
-// The two small passes around the context-split kernel.
+// The two small passes around the context-split kernel. Both are latency
+// bound (a few MB of L2-resident data), so each thread issues all of its loads
+// at the start and the work costs about one memory round trip.
 //
 // absorb_q: for the absorbed-key mode, q~ = q B_k[g][:, cols(j)]^T for every
 //   query head (Palu author response on OpenReview, clarification of W1: only
 //   a rotary embedding forces the keys to be rebuilt; without it B_k can be
-//   applied to the query). One workgroup per (KV head, sequence) serves the
-//   KV head's query heads together, so each B_k row segment is read once per
-//   workgroup; q~ is stored in fp32, pre-multiplied by scale * log2(e).
+//   applied to the query). Workgroups over (KV head, sequence, slice of r);
+//   each thread loads its piece of a B_k row at once and the pieces of a row
+//   are added with lane shuffles; q~ is stored in fp32 pre-multiplied by
+//   scale * log2(e).
 //
 // merge: combine the per-split softmax states (m, l, u) of one query head,
 //   u* = sum_s 2^(m_s - M) u_s / sum_s 2^(m_s - M) l_s, then apply the value
 //   reconstruction once, out = u* B_v[g][:, cols(j)] (clarification of W1:
-//   values are never rebuilt, B_v acts after the weighted sum). Work is spread
-//   over thread phases (splits for u*, rows of B_v for out) so that many
-//   independent loads are in flight instead of one long dependent loop.
+//   values are never rebuilt, B_v acts after the weighted sum).
 #include <math.h>
 
 #include "device_util.h"
@@ -22,15 +23,36 @@ namespace palu {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWarps = kThreads / 64;
+constexpr int kAbsRows = 64;        // rows of r per absorb workgroup (general form)
 constexpr int kHeadChunk = 8;       // query heads absorbed per pass
-constexpr int kWeightChunk = 1024;  // split weights staged in LDS per pass
 
+// General form (any even d <= 256): thread = (row, quarter of d).
 template <typename T, bool kVec8>
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
   const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int g = j / p.s, jl = j % p.s;
+  const int kq = tid / 4, qtr = tid % 4;               // row in the slice, quarter of d
+  const int k = blockIdx.z * kAbsRows + kq;
+  const int dq = (p.d + 3) / 4;                        // columns per quarter
+  const int c0 = qtr * dq, c1 = min(p.d, c0 + dq);
   __shared__ float qs[kHeadChunk][2 * kMaxHalfDim];
-  const T* Bk = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
+  const T* row = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg +
+                 static_cast<size_t>(min(k, p.r - 1)) * p.Dg + jl * p.d;
+  // the quarter-row of B_k: at most 64 columns, loaded at once
+  float v[64];
+  if (kVec8 && dq % 8 == 0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (8 * u < dq) load8_f32(row + c0 + 8 * u, v + 8 * u);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * u + e] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 64; ++e) v[e] = c0 + e < c1 ? load_f32(row, c0 + e) : 0.f;
+  }
   for (int h0 = 0; h0 < p.gqa; h0 += kHeadChunk) {
     const int nh = min(kHeadChunk, p.gqa - h0);
     const int head0 = j * p.gqa + h0;
@@ -42,47 +64,79 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
                           : 0.f;
     }
     __syncthreads();
-    for (int k = tid; k < p.r; k += kThreads) {
-      float acc[kHeadChunk];
+    float acc[kHeadChunk];
 #pragma unroll
-      for (int hh = 0; hh < kHeadChunk; ++hh) acc[hh] = 0.f;
-      const T* row = Bk + static_cast<size_t>(k) * p.Dg;
-      if (kVec8) {
-        for (int c0 = 0; c0 < p.d; c0 += 64) {      // eight 16-byte loads in flight
-          float v[64];
+    for (int hh = 0; hh < kHeadChunk; ++hh) {
+      float a = 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if (c0 + 8 * u < p.d) load8_f32(row + c0 + 8 * u, v + 8 * u);
-            else
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[8 * u + e] = 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if (c0 + 8 * u >= p.d) break;
-#pragma unroll
-            for (int hh = 0; hh < kHeadChunk; ++hh)
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                acc[hh] = fmaf(qs[hh][c0 + 8 * u + e], v[8 * u + e], acc[hh]);
-          }
-        }
-      } else {
-        for (int c = 0; c < p.d; ++c) {
-          const float v = load_f32(row, c);
-#pragma unroll
-          for (int hh = 0; hh < kHeadChunk; ++hh) acc[hh] = fmaf(qs[hh][c], v, acc[hh]);
-        }
-      }
+      for (int e = 0; e < 64; ++e)
+        if (c0 + e < c1) a = fmaf(qs[hh][c0 + e], v[e], a);
+      a += __shfl_xor(a, 1);       // the four quarters of a row are adjacent lanes
+      a += __shfl_xor(a, 2);
+      acc[hh] = a;
+    }
+    if (qtr == 0 && k < p.r)
       for (int hh = 0; hh < nh; ++hh)
         p.qt[(static_cast<size_t>(b) * p.Hq + head0 + hh) * p.r + k] = acc[hh] * p.scale_log2;
+  }
+}
+
+// Fast form when d/8 is a power of two <= 32: thread = (row k, 8-column
+// chunk); one 16-byte load of B_k per thread, the chunks of a row are added
+// with lane shuffles. Workgroup (KV head, sequence, 256*8/d rows of r).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void absorb_q_vec_kernel(DecodeParams p) {
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int g = j / p.s, jl = j % p.s;
+  const int ncc = p.d / 8, rows = kThreads / ncc;
+  const int cc = tid % ncc, kr = tid / ncc;
+  const int k = blockIdx.z * rows + kr;
+  const T* row = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg +
+                 static_cast<size_t>(min(k, p.r - 1)) * p.Dg + jl * p.d;
+  float v[8];
+  load8_f32(row + 8 * cc, v);
+  __shared__ float qs[kHeadChunk][2 * kMaxHalfDim];
+  for (int h0 = 0; h0 < p.gqa; h0 += kHeadChunk) {
+    const int nh = min(kHeadChunk, p.gqa - h0);
+    const int head0 = j * p.gqa + h0;
+    __syncthreads();
+    for (int e = tid; e < nh * p.d; e += kThreads) {
+      const int hh = e / p.d, c = e % p.d;
+      qs[hh][c] = load_f32(static_cast<const T*>(p.q),
+                           (static_cast<size_t>(b) * p.Hq + head0 + hh) * p.d + c);
+    }
+    __syncthreads();
+    for (int hh = 0; hh < nh; ++hh) {
+      const float4 q0 = *reinterpret_cast<const float4*>(&qs[hh][8 * cc]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&qs[hh][8 * cc + 4]);
+      float a = q0.x * v[0];
+      a = fmaf(q0.y, v[1], a); a = fmaf(q0.z, v[2], a); a = fmaf(q0.w, v[3], a);
+      a = fmaf(q1.x, v[4], a); a = fmaf(q1.y, v[5], a); a = fmaf(q1.z, v[6], a);
+      a = fmaf(q1.w, v[7], a);
+      for (int off = 1; off < ncc; off <<= 1) a += __shfl_xor(a, off);
+      if (cc == 0 && k < p.r)
+        p.qt[(static_cast<size_t>(b) * p.Hq + head0 + hh) * p.r + k] = a * p.scale_log2;
     }
   }
+}
+
+constexpr int kBvRows = 16;        // B_v rows per thread kept in flight
+constexpr int kSplitBatch = 16;    // split partials per thread kept in flight
+constexpr int kSplitLDS = 1024;    // split weights staged in LDS per chunk
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, warp = tid >> 6;
   const int n = clamp_len(p.lens, b, p.L);
   const int ns = (n + p.split_tokens - 1) / p.split_tokens;
   float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
@@ -94,113 +148,142 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
   const float* ml = p.part_ml + base * 2;
   const float* pu = p.part_u + base * p.r;
+  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
 
-  __shared__ float red[kThreads];
-  __shared__ float wts[kWeightChunk];
+  __shared__ float wred[kWarps];
+  __shared__ float wts[kSplitLDS];
   __shared__ float us[2 * kThreads];   // r <= 512
+  __shared__ float red2[2048];
 
-  // M = max_s m_s
-  float mloc = -INFINITY;
-  for (int sp = tid; sp < ns; sp += kThreads) mloc = fmaxf(mloc, ml[sp * 2]);
-  red[tid] = mloc;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
+  // ---- 1. issue every independent load at once: the first B_v rows, this
+  //         thread's split state, the first split partials of its u* entries
+  const bool vec = p.d % 8 == 0;
+  const int ncc = vec ? p.d / 8 : 1, ngroups = kThreads / ncc;
+  const int cc = tid % ncc, rg = tid / ncc;
+  float bv[kBvRows][8];
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < kBvRows; ++i) {
+      const int k = rg + i * ngroups;
+      if (rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
+    }
   }
-  const float M = red[0];
-  __syncthreads();
-
-  // thread phases over splits for u*: phases = 256 / r (at least 1)
   const int phases = p.r >= kThreads ? 1 : kThreads / p.r;
   const int kq = p.r >= kThreads ? tid : tid % p.r;
   const int ph = p.r >= kThreads ? 0 : tid / p.r;
   const bool active = ph < phases;
+  const bool two = kq + kThreads < p.r;
+  float ua[kSplitBatch], ub[kSplitBatch];
+  auto load_u = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kSplitBatch; ++u) {
+      const int sp = s0 + ph + u * phases;
+      const bool ok = active && sp < ns;
+      const float* rowp = pu + static_cast<size_t>(ok ? sp : 0) * p.r;
+      ua[u] = ok ? rowp[kq] : 0.f;
+      ub[u] = ok && two ? rowp[kq + kThreads] : 0.f;
+    }
+  };
+  load_u(0);
+  const bool one_pass = ns <= kThreads;      // each thread holds one split's state
+  float my_m = -INFINITY, my_l = 0.f;
+  if (tid < ns) {
+    my_m = ml[tid * 2];
+    my_l = ml[tid * 2 + 1];
+  }
+
+  // ---- 2. M = max_s m_s (wave shuffles, one LDS step)
+  float mloc = my_m;
+  for (int sp = tid + kThreads; sp < ns; sp += kThreads) mloc = fmaxf(mloc, ml[sp * 2]);
+  mloc = wave_max(mloc);
+  if (lane == 0) wred[warp] = mloc;
+  __syncthreads();
+  float M = wred[0];
+#pragma unroll
+  for (int w = 1; w < kWarps; ++w) M = fmaxf(M, wred[w]);
+  __syncthreads();
+
+  // ---- 3. u* = sum_s w_s u_s / L, w_s = 2^(m_s - M), in chunks of kSplitLDS
   float u0 = 0.f, u1 = 0.f, lsum = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kWeightChunk) {
-    const int cnt = min(kWeightChunk, ns - s0);
-    __syncthreads();
+  for (int c0 = 0; c0 < ns; c0 += kSplitLDS) {
+    const int cnt = min(kSplitLDS, ns - c0);
+    if (c0 > 0) __syncthreads();
     for (int e = tid; e < cnt; e += kThreads) {
-      const float w = exp2f(ml[(s0 + e) * 2] - M);
+      const float m = one_pass ? my_m : ml[(c0 + e) * 2];
+      const float l = one_pass ? my_l : ml[(c0 + e) * 2 + 1];
+      const float w = exp2f(m - M);
       wts[e] = w;
-      lsum = fmaf(w, ml[(s0 + e) * 2 + 1], lsum);
+      lsum = fmaf(w, l, lsum);
     }
     __syncthreads();
-    if (active) {
-      const bool two = kq + kThreads < p.r;
-      for (int e0 = ph; e0 < cnt; e0 += 8 * phases) {   // eight splits' loads in flight
-        float w[8], a[8], b2[8];
+    for (int s0 = c0; s0 < c0 + cnt; s0 += kSplitBatch * phases) {
+      if (s0 > 0) load_u(s0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * phases;
-          const bool ok = e < cnt;
-          const float* row = pu + static_cast<size_t>(s0 + (ok ? e : 0)) * p.r;
-          w[u] = ok ? wts[e] : 0.f;
-          a[u] = ok ? row[kq] : 0.f;
-          b2[u] = ok && two ? row[kq + kThreads] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          u0 = fmaf(w[u], a[u], u0);
-          u1 = fmaf(w[u], b2[u], u1);
-        }
+      for (int u = 0; u < kSplitBatch; ++u) {
+        const int sp = s0 + ph + u * phases;
+        const float w = active && sp < c0 + cnt ? wts[sp - c0] : 0.f;
+        u0 = fmaf(w, ua[u], u0);
+        u1 = fmaf(w, ub[u], u1);
       }
     }
   }
-  // total weight: block sum of lsum
-  red[tid] = lsum;
+  lsum = wave_sum(lsum);
+  if (lane == 0) wred[warp] = lsum;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  const float inv = 1.f / red[0];
-  __syncthreads();
-  // reduce u over phases (phases > 1 only when r < 256)
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWarps; ++w) L += wred[w];
+  const float inv = 1.f / L;
+  // reduce u over the split phases (phases > 1 only when r < 256)
   if (phases == 1) {
     us[kq] = u0 * inv;
-    if (kq + kThreads < p.r) us[kq + kThreads] = u1 * inv;
-    __syncthreads();
+    if (two) us[kq + kThreads] = u1 * inv;
   } else {
-    red[tid] = active ? u0 : 0.f;
+    red2[tid] = active ? u0 : 0.f;
     __syncthreads();
     if (tid < p.r) {
       float a = 0.f;
-      for (int q = 0; q < phases; ++q) a += red[q * p.r + tid];
+      for (int q = 0; q < phases; ++q) a += red2[q * p.r + tid];
       us[tid] = a * inv;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // out = u* B_v[:, cols(j)]
-  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
-  if (p.d % 8 == 0) {
-    // thread = (row group, 8-column chunk); all of its rows' 16-byte loads go out
-    // together, then the row groups are added through LDS (groups * d == 2048)
-    __shared__ float red2[2048];
-    const int ncc = p.d / 8, ngroups = kThreads / ncc;
-    const int cc = tid % ncc, rg = tid / ncc;
+  // ---- 4. out = u* B_v[:, cols(j)]
+  if (vec) {
+    // thread = (row group, 8-column chunk); row groups added through LDS
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k0 = rg; k0 < p.r; k0 += 8 * ngroups) {
-      float v[8][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * ngroups;
-        if (k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, v[u]);
+    for (int i = 0; i < kBvRows; ++i) {
+      const int k = rg + i * ngroups;
+      const float w = rg < ngroups && k < p.r ? us[k] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, bv[i][e], acc[e]);
+    }
+    for (int k0 = rg + kBvRows * ngroups; k0 < p.r; k0 += kBvRows * ngroups) {
+#pragma unroll
+      for (int i = 0; i < kBvRows; ++i) {
+        const int k = k0 + i * ngroups;
+        if (rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
         else
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+          for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * ngroups;
-        const float w = k < p.r ? us[k] : 0.f;
+      for (int i = 0; i < kBvRows; ++i) {
+        const int k = k0 + i * ngroups;
+        const float w = rg < ngroups && k < p.r ? us[k] : 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, bv[i][e], acc[e]);
       }
     }
+    if (rg < ngroups) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red2[rg * p.d + 8 * cc + e] = acc[e];
+      for (int e = 0; e < 8; ++e) red2[rg * p.d + 8 * cc + e] = acc[e];
+    }
     __syncthreads();
     if (tid < p.d) {
       float a = 0.f;
@@ -219,11 +302,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 #pragma unroll 8
     for (int k = k0; k < k1; ++k) acc = fmaf(us[k], load_f32(Bv, static_cast<size_t>(k) * p.Dg + c), acc);
   }
-  red[tid] = acc;
+  red2[tid] = acc;
   __syncthreads();
   if (tid < p.d) {
     float a = 0.f;
-    for (int q = 0; q < kph; ++q) a += red[q * p.d + tid];
+    for (int q = 0; q < kph; ++q) a += red2[q * p.d + tid];
     out[tid] = a;
   }
 }
@@ -231,8 +314,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
-  const dim3 grid(p.Hkv, p.B);
-  const bool v8 = p.d % 8 == 0;
+  const int ncc = p.d / 8;
+  if (p.d % 8 == 0 && ncc <= 32 && (ncc & (ncc - 1)) == 0) {
+    const int rows = kThreads / ncc;
+    const dim3 grid(p.Hkv, p.B, (p.r + rows - 1) / rows);
+    if (dtype == 0) absorb_q_vec_kernel<float><<<grid, kThreads, 0, st>>>(p);
+    else absorb_q_vec_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
+    return hipGetLastError();
+  }
+  const dim3 grid(p.Hkv, p.B, (p.r + kAbsRows - 1) / kAbsRows);
+  const bool v8 = p.d % 32 == 0;     // quarters of d in whole 16-byte chunks
   if (dtype == 0) {
     if (v8) absorb_q_kernel<float, true><<<grid, kThreads, 0, st>>>(p);
     else absorb_q_kernel<float, false><<<grid, kThreads, 0, st>>>(p);

@@ -39,6 +39,7 @@ palu_status ok() {
 
 constexpr int kSplitQuantum = 64;    // split sizes are multiples of this many tokens
 constexpr int kTargetWorkgroups = 1024;
+constexpr int kAbsorbedWorkgroups = 256;   // one per CU on a 256-CU MI355X
 
 palu_status validate_attn(const palu_attn_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
@@ -95,12 +96,14 @@ Plan make_plan(const palu_attn_desc* d) {
     pl.kernel = SplitKernel::kAbsorbedMfma;
   int st = d->split_tokens;
   if (st == 0) {
-    // the generic kernel runs one workgroup per (split, head, batch); the MFMA
-    // kernel one per (split, group, batch) and fills a CU with one workgroup
-    const double units = pl.kernel == SplitKernel::kGeneric
-                             ? double(d->batch) * d->n_groups * 4.0
-                             : double(d->batch) * d->n_groups * kTargetWorkgroups / 256.0;
-    const double want = double(d->max_ctx) * units / kTargetWorkgroups;
+    // Aim at a fixed number of (split, b, g) units: 256 for the generic
+    // kernel, which launches one workgroup per query head of each unit, and
+    // one workgroup per CU (256 CUs, all resident at once) for the absorbed
+    // MFMA kernel, whose register use allows one wave per SIMD.
+    const double wg_target = pl.kernel == SplitKernel::kGeneric
+                                 ? double(kTargetWorkgroups) / 4.0
+                                 : double(kAbsorbedWorkgroups);
+    const double want = double(d->max_ctx) * d->batch * d->n_groups / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
     if (st < kSplitQuantum) st = kSplitQuantum;
     if (st > 4096) st = 4096;
@@ -236,8 +239,8 @@ palu_status validate_append(const palu_append_desc* d) {
     return fail(PALU_ERR_SHAPE, "all sizes must be positive");
   if (d->d_model > 65536 || d->rank > 512)
     return fail(PALU_ERR_SHAPE, "d_model must be <= 65536 and rank <= 512");
-  if (double(d->n_groups) * d->rank > 65536.0)
-    return fail(PALU_ERR_SHAPE, "n_groups * rank must be <= 65536");
+  if (double(d->n_groups) * d->rank > 65536.0 || (d->n_groups * d->rank) % 8)
+    return fail(PALU_ERR_SHAPE, "n_groups * rank must be a multiple of 8 and <= 65536");
   if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
     return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
   return PALU_OK;

@@ -8,27 +8,31 @@
 // value latents with the attention weights and applies B_v later (merge pass).
 //
 // One workgroup owns one (batch, group, context split) and all of the group's
-// query heads (up to 16), so every latent byte is read from HBM exactly once;
-// its four waves take the split's 16-token tiles round-robin (adjacent tiles
-// stream together, which measured ~13% faster than giving each wave a
-// contiguous quarter) and combine their softmax states in LDS at the end.
-// Per tile:
-//   scores  S^T[16 tok x 16 heads] = H_k[16 x r] * Q~^T        bf16 MFMA 16x16x32,
-//           q~ split as hi + lo bf16 (two MFMAs) so the query keeps ~16 bits,
-//           read from LDS;
+// query heads (up to 16), so every latent byte is read from HBM exactly once.
+// Its four waves take the split's 16-token tiles round-robin (adjacent tiles
+// stream together, which measured ~13% faster than contiguous quarters per
+// wave) and combine their softmax states in LDS at the end. Per tile:
+//   scores  S^T[16 tok x 16 heads] = H_k[16 x r] * Q~^T, bf16 MFMA 16x16x32,
+//           q~ split as hi + lo bf16 (two MFMAs, ~16 bits kept), read from LDS;
 //   softmax online, base 2, per head, with a lazy running max (the stored max
 //           moves only when a tile exceeds it by kLazy, so most tiles skip the
 //           rescale; the result is exact either way);
-//   values  U^T[r x 16 heads] += H_v^T[r x 16 tok] * P^T       fp32 MFMA 16x16x4:
-//           each lane feeds one bf16->fp32 latent per MFMA, so the value latents
-//           are used straight from their natural [token][r] rows, no transpose,
-//           and P stays in fp32.
-// Lane layouts (wave64): for 16x16x32 bf16, lane l holds A[l%16][k-slot(l/16)]
-// and B[k-slot(l/16)][l%16] (8 values each); for 16x16x4 fp32 one value each
-// with k = l/16; the result holds D[4*(l/16)+i][l%16], i < 4.
-// Loads: 16-byte global loads in the natural cache layout, two tiles in flight
-// per wave while a third is consumed (three register buffers). Rows past the split's end are clamped to its
-// last valid row and masked, so nothing outside [t0, len) is ever read.
+//   values  U^T[r x 16 heads] += H_v^T[r x 16 tok] * P^T, bf16 MFMA 16x16x16
+//           with P split as hi + lo bf16. The tile's value latents go through
+//           a wave-private LDS tile so each lane can gather one latent column
+//           over four tokens (the MFMA contracts over tokens); groups of
+//           four rows are offset by 32 bytes so those gathers hit distinct
+//           banks.
+// Lane layouts (wave64): 16x16x32 lane l holds A[l%16][k-slot l/16] and
+// B[k-slot l/16][l%16], eight bf16 each; 16x16x16 the same with four; the
+// result holds D[4*(l/16)+i][l%16]. A score tile leaves lane l with tokens
+// 4*(l/16)+i of head l%16, which is exactly the 16x16x16 k-slot of P^T, so the
+// weights never leave their lane.
+// Loads: 16-byte global loads; H_k in the MFMA operand pattern (row l%16),
+// H_v as contiguous 1 KiB per instruction; a ring of register buffers per wave
+// keeps the next tiles in flight while one is consumed. Rows past the split's end are
+// clamped to its last valid row and masked, so nothing outside [t0, len) is
+// ever read.
 #include <math.h>
 
 #include "device_util.h"
@@ -38,9 +42,18 @@ namespace palu {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazy = 8.0f;   // log2 units: p <= 2^8 between rescales
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kTile = 16;       // tokens per tile
+#ifndef ABS_NBUF
+#define ABS_NBUF 2      // register tile buffers per wave (measured best of 2..4)
+#endif
+#ifndef ABS_MINW
+#define ABS_MINW 1
+#endif
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -48,59 +61,95 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-template <int R>
-struct Tile {
-  uint4 k[R / 32];        // H_k row (lane%16): 8 latents at 32c + 8*(lane/16)
-  uint4 v[4][R / 128];    // H_v rows 4*(lane/16)+i: 8 latents at 128h + 8*(lane%16)
-};
-
-template <int R>
-__device__ __forceinline__ void load_tile(Tile<R>& tl, const uint16_t* Hk, const uint16_t* Hv,
-                                          int tok0, int last, int ln, int kb) {
-  const int rk = min(tok0 + ln, last);
-#pragma unroll
-  for (int c = 0; c < R / 32; ++c)
-    tl.k[c] = *reinterpret_cast<const uint4*>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rv = min(tok0 + 4 * kb + i, last);
-#pragma unroll
-    for (int h = 0; h < R / 128; ++h)
-      tl.v[i][h] = *reinterpret_cast<const uint4*>(Hv + static_cast<size_t>(rv) * R + 128 * h + 8 * ln);
-  }
-}
-
-template <int R>
-struct State {
-  floatx4 acc[R / 128][8];   // U^T: r = 128h + 8*(4*(lane/16)+i) + j, head lane%16
-  float m;                   // stored running max (log2 units) of head lane%16
-  float l;                   // this lane's share of the running sum
-};
-
-// Absorbed queries in LDS as the MFMA B operand: [hi|lo][head][k] bf16, rows
-// padded by 8 elements so the 16 heads' 16-byte reads spread over the banks.
+// q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] bf16; rows padded
+// by 8 elements so the 16 heads' 16-byte reads spread over the banks.
 template <int R>
 struct QTile {
   static constexpr int kStride = R + 8;
   uint16_t v[2][16][kStride];
 };
 
+// byte offset of (row, column byte) in a wave's value tile [16][R] bf16: each
+// group of four rows is shifted by 32 bytes, so the four lane groups of a
+// gather (rows 4*kb..4*kb+3, same columns) hit different banks while every
+// address stays one per-lane base plus an immediate
 template <int R>
-__device__ __forceinline__ void compute_tile(State<R>& st, const Tile<R>& tl, const QTile<R>& qs,
-                                             int tok0, int t1, int ln, int kb) {
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ int vtile_off(int row, int cb) {
+  return row * (2 * R) + (row >> 2) * 32 + cb;
+}
+template <int R>
+constexpr int kVTileBytes = kTile * R * 2 + 3 * 32;
+
+template <int R>
+struct Tile {
+  uint4 k[R / 32];     // H_k row tok0 + lane%16: 8 latents at 32c + 8*(lane/16)
+  uint4 v[R / 32];     // H_v: 16 rows x R contiguous, 1 KiB per entry across the wave
+};
+
+template <int R>
+__device__ __forceinline__ void load_k(Tile<R>& tl, const uint16_t* Hk, int tok0, int last, int lane) {
+  const int rk = min(tok0 + (lane & 15), last);
+#pragma unroll
+  for (int c = 0; c < R / 32; ++c)
+    tl.k[c] = *reinterpret_cast<const uint4*>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * (lane >> 4));
+}
+
+template <int R>
+__device__ __forceinline__ void load_v(Tile<R>& tl, const uint16_t* Hv, int tok0, int last, int lane) {
+#pragma unroll
+  for (int q = 0; q < R / 32; ++q) {
+    const int flat = q * 1024 + lane * 16;              // byte within the tile's 16 rows
+    const int rv = min(tok0 + flat / (2 * R), last);
+    tl.v[q] = *reinterpret_cast<const uint4*>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
+  }
+}
+
+template <int R>
+struct State {
+  floatx4 acc[R / 16];   // U^T: r = 16*rb + 4*(lane/16) + i, head lane%16
+  float m;               // stored running max (log2 units) of head lane%16
+  float l;               // this lane's share of the running sum
+};
+
+// stage a tile's value latents in this wave's LDS tile (swizzled columns)
+template <int R>
+__device__ __forceinline__ void stage_v(const Tile<R>& tl, char* vt, int lane) {
+#pragma unroll
+  for (int q = 0; q < R / 32; ++q) {
+    const int flat = q * 1024 + lane * 16;
+    *reinterpret_cast<uint4*>(vt + vtile_off<R>(flat / (2 * R), flat % (2 * R))) = tl.v[q];
+  }
+}
+
+// scores of a tile (log2 units), masked past t1
+template <int R>
+__device__ __forceinline__ floatx4 scores(const Tile<R>& tl, const QTile<R>& qs, int tok0, int t1,
+                                          int lane) {
+  const int ln = lane & 15, kb = lane >> 4;
+  // four independent accumulators (hi/lo x even/odd chunk) keep the MFMA
+  // dependency chains short; they are added at the end
+  floatx4 acc4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < R / 32; ++c) {
     const bf16x8 a = as_bf16x8(tl.k[c]);
     const bf16x8 qh = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[0][ln][32 * c + 8 * kb]));
     const bf16x8 ql = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[1][ln][32 * c + 8 * kb]));
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh, s, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql, s, 0, 0, 0);
+    acc4[2 * (c & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh, acc4[2 * (c & 1)], 0, 0, 0);
+    acc4[2 * (c & 1) + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql, acc4[2 * (c & 1) + 1], 0, 0, 0);
   }
-  // s[i]: score of token tok0 + 4*kb + i for head lane%16
+  floatx4 s = (acc4[0] + acc4[2]) + (acc4[1] + acc4[3]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (tok0 + 4 * kb + i >= t1) s[i] = -INFINITY;
+  return s;
+}
+
+// online softmax update and the value product from the staged LDS tile
+template <int R>
+__device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const char* vt, int lane) {
+  const int ln = lane & 15, kb = lane >> 4;
   float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -110,34 +159,45 @@ __device__ __forceinline__ void compute_tile(State<R>& st, const Tile<R>& tl, co
     st.m = mn;
     st.l *= alpha;
 #pragma unroll
-    for (int h = 0; h < R / 128; ++h)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st.acc[h][j] *= alpha;
+    for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= alpha;
   }
-  float p[4];
+  // P^T operand: k-slot e of lane group kb is token 4*kb + e; hi + lo bf16
+  short4v ph, pl;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = exp2f(s[i] - st.m);
-    st.l += p[i];
+  for (int e = 0; e < 4; ++e) {
+    const float p = exp2f(s[e] - st.m);
+    st.l += p;
+    const float hi = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
+    ph[e] = static_cast<short>(__float_as_uint(hi) >> 16);
+    pl[e] = static_cast<short>(f32_to_bf16_rne(p - hi));
   }
+  // values: gather H_v^T[16*rb + ln][tokens 4*kb .. 4*kb+3] from the LDS tile
+  const char* vb = vt + vtile_off<R>(4 * kb, 2 * ln);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int rb = 0; rb < R / 16; ++rb) {
+    short4v a;
 #pragma unroll
-    for (int h = 0; h < R / 128; ++h) {
-      const uint32_t w[4] = {tl.v[i][h].x, tl.v[i][h].y, tl.v[i][h].z, tl.v[i][h].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float a = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
-        st.acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[i], st.acc[h][j], 0, 0, 0);
-      }
-    }
+    for (int e = 0; e < 4; ++e)
+      a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
+    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, st.acc[rb], 0, 0, 0);
+    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, st.acc[rb], 0, 0, 0);
   }
 }
 
-constexpr int kWaves = 4;   // waves per workgroup; tiles are dealt round-robin
-
 template <int R>
-__global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(DecodeParams p) {
+struct Smem {
+  QTile<R> q;
+  union {
+    char vt[kWaves][kVTileBytes<R>];                 // per-wave value tiles (streaming)
+    struct {                                         // softmax states (final merge)
+      float acc[kWaves - 1][4 * (R / 16)][64];
+      float m[kWaves - 1][64], l[kWaves - 1][64];
+    } x;
+  } u;
+};
+
+template <int R, int kBuf, int kMinWaves>
+__global__ __launch_bounds__(64 * kWaves, kMinWaves) void split_absorbed_mfma_kernel(DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
@@ -147,14 +207,14 @@ __global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(Decode
   const int t1 = min(n, s0 + p.split_tokens);
   const int last = t1 - 1;
 
+  __shared__ Smem<R> sm;
   // absorbed queries of the group's heads, split hi/lo bf16 (padding heads are 0)
-  __shared__ QTile<R> qs;
   for (int e = threadIdx.x; e < 16 * R; e += 64 * kWaves) {
     const int hd = e / R, k = e % R;
     const float x = hd < p.nq ? p.qt[(static_cast<size_t>(b) * p.Hq + g * p.nq + hd) * R + k] : 0.f;
     const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
-    qs.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
-    qs.v[1][hd][k] = f32_to_bf16_rne(x - hi);
+    sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
+    sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
   }
   __syncthreads();
 
@@ -166,49 +226,51 @@ __global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(Decode
   st.m = -INFINITY;
   st.l = 0.f;
 #pragma unroll
-  for (int h = 0; h < R / 128; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // tiles of 16 tokens dealt round-robin: wave w takes tiles w, w+4, ..., so the
-  // four waves stream adjacent 8 KiB blocks together. Three register buffers:
-  // two tiles in flight while one is consumed; loads past the end read the last
-  // valid row again (cached, never out of range).
-  const int ntiles = (t1 - s0 + 15) / 16;
-  const int mine = (ntiles - wave + kWaves - 1) / kWaves;  // may be 0
+  // 16-token tiles dealt round-robin: wave w takes tiles w, w+4, ...; each
+  // register buffer is refilled as soon as its part is consumed (values right
+  // after staging, keys right after the score MFMAs); loads past the end read
+  // the last valid row again (cached, never out of range)
+  const int ntiles = (t1 - s0 + kTile - 1) / kTile;
+  const int mine = (ntiles - wave + kWaves - 1) / kWaves;   // may be 0
   if (mine > 0) {
-    const int step = 16 * kWaves;
-    const int first = s0 + 16 * wave;
-    Tile<R> ta, tb, tc;
-    load_tile<R>(ta, Hk, Hv, first, last, ln, kb);
-    load_tile<R>(tb, Hk, Hv, first + step, last, ln, kb);
-    for (int it = 0; it < mine; it += 3) {
-      load_tile<R>(tc, Hk, Hv, first + step * (it + 2), last, ln, kb);
-      compute_tile<R>(st, ta, qs, first + step * it, t1, ln, kb);
-      if (it + 1 >= mine) break;
-      load_tile<R>(ta, Hk, Hv, first + step * (it + 3), last, ln, kb);
-      compute_tile<R>(st, tb, qs, first + step * (it + 1), t1, ln, kb);
-      if (it + 2 >= mine) break;
-      load_tile<R>(tb, Hk, Hv, first + step * (it + 4), last, ln, kb);
-      compute_tile<R>(st, tc, qs, first + step * (it + 2), t1, ln, kb);
+    char* vt = sm.u.vt[wave];
+    const int step = kTile * kWaves;
+    const int first = s0 + kTile * wave;
+    // ring of kBuf register buffers: kBuf - 1 tiles in flight while one is
+    // consumed (indices are static after unrolling)
+    Tile<R> buf[kBuf];
+#pragma unroll
+    for (int j = 0; j < kBuf - 1; ++j) {
+      load_k<R>(buf[j], Hk, first + step * j, last, lane);
+      load_v<R>(buf[j], Hv, first + step * j, last, lane);
+    }
+    for (int it = 0; it < mine; it += kBuf) {
+#pragma unroll
+      for (int u = 0; u < kBuf; ++u) {
+        if (it + u >= mine) break;
+        Tile<R>& nx = buf[(u + kBuf - 1) % kBuf];
+        load_k<R>(nx, Hk, first + step * (it + u + kBuf - 1), last, lane);
+        load_v<R>(nx, Hv, first + step * (it + u + kBuf - 1), last, lane);
+        stage_v<R>(buf[u], vt, lane);
+        const floatx4 s = scores<R>(buf[u], sm.q, first + step * (it + u), t1, lane);
+        softmax_values<R>(st, s, vt, lane);
+      }
     }
   }
 
-  // merge the waves' states in LDS: waves 1..3 publish, wave 0 combines.
-  // Layout [wave][value][lane] keeps consecutive lanes on consecutive banks.
-  constexpr int kVals = 4 * 8 * (R / 128);
-  __shared__ float xacc[kWaves - 1][kVals][64];
-  __shared__ float xm[kWaves - 1][64], xl[kWaves - 1][64];
+  // merge the waves' states in LDS (the value tiles' space, after a barrier):
+  // waves 1..3 publish, wave 0 combines. [wave][value][lane] keeps
+  // consecutive lanes on consecutive banks.
+  __syncthreads();
   if (wave > 0) {
-    int v = 0;
 #pragma unroll
-    for (int h = 0; h < R / 128; ++h)
+    for (int rb = 0; rb < R / 16; ++rb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xacc[wave - 1][v++][lane] = st.acc[h][j][i];
-    xm[wave - 1][lane] = st.m;
-    xl[wave - 1][lane] = st.l;
+      for (int i = 0; i < 4; ++i) sm.u.x.acc[wave - 1][4 * rb + i][lane] = st.acc[rb][i];
+    sm.u.x.m[wave - 1][lane] = st.m;
+    sm.u.x.l[wave - 1][lane] = st.l;
   }
   __syncthreads();
   if (wave > 0) return;
@@ -216,7 +278,7 @@ __global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(Decode
   float M = st.m;
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w) {
-    mw[w] = xm[w][lane];
+    mw[w] = sm.u.x.m[w][lane];
     M = fmaxf(M, mw[w]);
   }
   const float a0 = exp2f(st.m - M);   // wave 0 always has a tile: M is finite
@@ -225,21 +287,18 @@ __global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(Decode
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w) {
     wgt[w] = exp2f(mw[w] - M);         // 0 for a wave that saw no token
-    l += wgt[w] * xl[w][lane];
+    l += wgt[w] * sm.u.x.l[w][lane];
   }
-  {
-    int v = 0;
 #pragma unroll
-    for (int h = 0; h < R / 128; ++h)
+  for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= a0;
+  // one wave's state at a time keeps the LDS reads in flight bounded
+#pragma unroll 1
+  for (int w = 0; w < kWaves - 1; ++w) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+    for (int rb = 0; rb < R / 16; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i, ++v) {
-          float a = st.acc[h][j][i] * a0;
-#pragma unroll
-          for (int w = 0; w < kWaves - 1; ++w) a = fmaf(wgt[w], xacc[w][v][lane], a);
-          st.acc[h][j][i] = a;
-        }
+      for (int i = 0; i < 4; ++i)
+        st.acc[rb][i] = fmaf(wgt[w], sm.u.x.acc[w][4 * rb + i][lane], st.acc[rb][i]);
   }
 
   // head totals: sum the four lane groups' shares
@@ -254,15 +313,9 @@ __global__ __launch_bounds__(64 * kWaves) void split_absorbed_mfma_kernel(Decode
   }
   float* u = p.part_u + slot * R;
 #pragma unroll
-  for (int h = 0; h < R / 128; ++h)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 128 * h + 8 * (4 * kb + i);
-      float4 lo4 = {st.acc[h][0][i], st.acc[h][1][i], st.acc[h][2][i], st.acc[h][3][i]};
-      float4 hi4 = {st.acc[h][4][i], st.acc[h][5][i], st.acc[h][6][i], st.acc[h][7][i]};
-      *reinterpret_cast<float4*>(u + r0) = lo4;
-      *reinterpret_cast<float4*>(u + r0 + 4) = hi4;
-    }
+  for (int rb = 0; rb < R / 16; ++rb)
+    *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) =
+        float4{st.acc[rb][0], st.acc[rb][1], st.acc[rb][2], st.acc[rb][3]};
 }
 
 }  // namespace
@@ -273,8 +326,8 @@ bool absorbed_mfma_supported(const DecodeParams& p, int dtype) {
 
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {
   const dim3 grid(p.n_split, p.G, p.B);
-  if (p.r == 128) split_absorbed_mfma_kernel<128><<<grid, 64 * kWaves, 0, st>>>(p);
-  else if (p.r == 256) split_absorbed_mfma_kernel<256><<<grid, 64 * kWaves, 0, st>>>(p);
+  if (p.r == 128) split_absorbed_mfma_kernel<128, ABS_NBUF, ABS_MINW><<<grid, 64 * kWaves, 0, st>>>(p);
+  else if (p.r == 256) split_absorbed_mfma_kernel<256, ABS_NBUF, ABS_MINW><<<grid, 64 * kWaves, 0, st>>>(p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -114,6 +114,7 @@ def test_append_validation(lib):
     good = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
                          dtype=P.PALU_BF16)
     bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
+           (dict(n_groups=1, rank=12), P.PALU_ERR_SHAPE),
            (dict(d_model=70000), P.PALU_ERR_SHAPE), (dict(dtype=3), P.PALU_ERR_UNSUPPORTED)]
     big = 1 << 40
     for kw, status in bad:
@@ -129,7 +130,7 @@ def test_append_validation(lib):
     assert lib.palu_latent_append(None, fake, fake, fake, fake, fake, fake, fake, big,
                                   None) == P.PALU_ERR_NULL
     need = P.palu_latent_append_workspace(good)
-    assert need == 64 * 8 * 1024 * 4        # 64-row slices x batch x (k and v columns)
+    assert need == 32 * 8 * 1024 * 4        # 128-row slices x batch x (k and v columns)
     assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake,
                                   need - 1, None) == P.PALU_ERR_WORKSPACE
 
