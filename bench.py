@@ -160,14 +160,23 @@ def cpu_baseline(O, cfg, t, mode, budget_s):
 
 
 def load_traffic(kernel: str):
-    """HBM bytes per launch of the main kernel from committed counter runs, if any."""
+    """HBM bytes (read + write) per launch of the main kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a 1 GiB copy measured in
+    the same runs). None when there is no record for the kernel or when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             rec = json.load(f)
-        return rec.get(kernel)
+        src = os.path.join(ROOT, rec["source"])
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        k = rec["kernels"].get(kernel)
+        return None if k is None else round(k["bytes"])
     except Exception:
         return None
 
