@@ -94,6 +94,8 @@ Plan make_plan(const palu_attn_desc* d) {
   pl.kernel = SplitKernel::kGeneric;
   if (d->mode == PALU_MODE_ABSORBED && absorbed_mfma_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kAbsorbedMfma;
+  if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_mfma_supported(sp, d->dtype))
+    pl.kernel = SplitKernel::kReconstructMfma;
   int st = d->split_tokens;
   if (st == 0) {
     // Aim at a fixed number of (split, b, g) units: 256 for the generic
@@ -116,17 +118,22 @@ Plan make_plan(const palu_attn_desc* d) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t qt, ml, u, total;
+  size_t qt, ml, u, bkt, total;
 };
 
 WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   WorkspaceLayout w{};
   const size_t heads = size_t(d->batch) * d->n_q_heads;
+  const size_t elem = d->dtype == PALU_BF16 ? 2 : 4;
   w.qt = 0;
   const size_t qt_bytes = d->mode == PALU_MODE_ABSORBED ? align256(heads * d->rank * 4) : 0;
   w.ml = w.qt + qt_bytes;
   w.u = w.ml + align256(heads * pl.n_split * 2 * 4);
-  w.total = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
+  w.bkt = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
+  const size_t bkt_bytes = pl.kernel == SplitKernel::kReconstructMfma
+                               ? align256(size_t(d->n_kv_heads) * d->head_dim * d->rank * elem)
+                               : 0;
+  w.total = w.bkt + bkt_bytes;
   return w;
 }
 
@@ -142,6 +149,7 @@ const char* split_kernel_name(SplitKernel k) {
   switch (k) {
     case SplitKernel::kGeneric: return "split_generic_kernel";
     case SplitKernel::kAbsorbedMfma: return "split_absorbed_mfma_kernel";
+    case SplitKernel::kReconstructMfma: return "split_reconstruct_mfma_kernel";
   }
   return "?";
 }
@@ -205,6 +213,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   p.qt = reinterpret_cast<float*>(ws + wl.qt);
   p.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   p.part_u = reinterpret_cast<float*>(ws + wl.u);
+  p.bkt = ws + wl.bkt;
   p.n_split = pl.n_split; p.split_tokens = pl.split_tokens;
   const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
   p.scale_log2 = float(scale * 1.4426950408889634);
@@ -217,11 +226,14 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   hipError_t e = hipSuccess;
   if (absorbed) e = launch_absorb_q(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
+  if (pl.kernel == SplitKernel::kReconstructMfma) e = launch_transpose_bk(p, desc->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
 
   const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
   if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
   switch (pl.kernel) {
     case SplitKernel::kAbsorbedMfma: e = launch_split_absorbed_mfma(p, s); break;
+    case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
   if (timed) (void)hipEventRecord(g_prof.stop[g_prof.used++], s);

@@ -22,6 +22,7 @@ struct DecodeParams {
   float* qt;            // [B, Hq, r]     absorbed queries, pre-scaled to log2 units
   float* part_ml;       // [B, Hq, n_split, 2]   running max (log2 units) and sum
   float* part_u;        // [B, Hq, n_split, r]   unnormalised value-latent sums
+  void* bkt;            // [G, Dg, r]  B_k transposed (reconstruct MFMA kernel)
   int32_t B, Hq, Hkv, d, G, r, L;
   int32_t s, gqa, nq, Dg;      // heads per group, q heads per kv head, q heads per group
   int32_t n_split, split_tokens;
@@ -47,6 +48,8 @@ struct AppendParams {
 enum class SplitKernel {
   kGeneric = 0,        // VALU, any dtype/shape in range
   kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {128, 256}, <= 16 q heads per group
+  kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, 4 KV heads per group,
+                         // <= 4 q heads per KV head, r in {128, 256}
 };
 
 const char* split_kernel_name(SplitKernel k);
@@ -56,6 +59,9 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
+bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);
+hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
+hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 size_t append_workspace_bytes(int B, int dm, int G, int r);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
