@@ -11,30 +11,29 @@
 //
 // Shape served: head_dim 128, four KV heads per group, at most four query heads
 // per KV head, rank 128 or 256. One workgroup owns one (batch, group, context
-// split); its four waves are the group's four KV heads and walk the split's
-// 16-token tiles together:
-//   keys     K^T[128 cols x 16 tok] = B_k^T[cols x r] * H_k^T[r x tok] per 16-col
-//            block, bf16 MFMA 16x16x32. Each wave holds its head's B_k^T (read
-//            once, from a transposed copy in the workspace) in registers for
-//            the whole split; H_k comes from the tile in LDS.
-//   rotate   the result leaves lane l with columns 16*cb + 4*(l/16) + i of
-//            token l%16, so the pair (f, f+64) sits in one lane (blocks cb and
-//            cb+4). cos/sin of t*omega_f advance by one exact complex product per
-//            tile (t grows by 16) and are recomputed from the angle every
-//            kAnchor tiles.
-//   scores   that layout is the A operand of a 16x16x16 MFMA (k = the 16
-//            columns of a block), so S^T[tok x q heads] = K_rot * Q^T chains on
-//            the matrix cores; keys are split into hi + lo bf16 (two MFMAs,
-//            ~16 bits kept), q is exact bf16, the scale is applied to the fp32
-//            result.
-//   softmax  online, base 2, per query head in the wave that owns its KV head.
-//   values   P and the rescale factors go through LDS; wave w then adds
+// split) and walks its 16-token tiles; its eight waves are (KV head, half):
+// a wave owns the 16-column blocks {2h, 2h+1, 2h+4, 2h+5} of its head, so the
+// rotary pair (f, f + 64) never leaves a wave, and its slice of B_k^T (r x 64
+// columns, read once from a transposed copy in the workspace) stays in
+// registers for the whole split. Per tile:
+//   keys     K^T[16 cols x 16 tok] = B_k^T[cols x r] * H_k^T[r x tok] per block,
+//            bf16 MFMA 16x16x32, H_k from the tile in LDS. Lane l ends up with
+//            columns 16*cb + 4*(l/16) + i of token l%16.
+//   rotate   in place; cos/sin of t*omega_f advance by one exact complex
+//            product per tile (t grows by 16) and are recomputed from the angle
+//            every kAnchor tiles.
+//   scores   that layout is the A operand of a 16x16x16 MFMA (k = the block's
+//            16 columns): S^T[tok x q heads] = K_rot * Q^T with keys split hi +
+//            lo bf16 (two MFMAs, ~16 bits kept) and exact bf16 q; the two
+//            halves of a head add their partial scores through LDS.
+//   softmax  online, base 2, by the first wave of each head.
+//   values   P and the rescale factors go through LDS; wave w adds
 //            H_v^T[r slice w] * P^T for all query heads of the group (bf16 MFMA
 //            16x16x16, P split hi + lo), gathering value columns from the tile
 //            in LDS (four-row groups offset by 32 B: conflict-free).
-// Loads: each thread moves 64 B of a tile (16 B loads) into registers two
-// tiles ahead and writes them to a ring of three LDS tile buffers; rows past
-// the split's end are clamped to its last valid row and masked.
+// Loads: 16-byte pieces of each tile are moved into kStages register stages
+// (kStages tiles in flight) and then into a ring of three LDS tile buffers;
+// rows past the split's end are clamped to its last valid row and masked.
 #include <math.h>
 
 #include "device_util.h"
@@ -44,13 +43,15 @@ namespace palu {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        // = KV heads per group
+constexpr int kHeads = 4;        // KV heads per group
+constexpr int kWaves = 2 * kHeads;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kD = 128;          // head dim
-constexpr int kBlocks = kD / 16; // 16-column blocks per head
 constexpr int kNB = 3;           // LDS tile buffers
 constexpr int kAnchor = 32;      // tiles between exact cos/sin evaluations
 
@@ -60,7 +61,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-// K tile: rows padded by 16 B so 16 lanes reading 16 B of 16 rows hit distinct banks
+// fp32 -> bf16 (hardware round to nearest even), as MFMA operand bits
+__device__ __forceinline__ short4v to_bf16x4(float a, float b, float c, float d) {
+  const bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  return __builtin_bit_cast(short4v, v);
+}
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
+}
+
+// K tile: rows padded by 16 B so the 16 rows of an operand read hit distinct banks
 template <int R>
 constexpr int kKStride = 2 * R + 16;
 // V tile: groups of four rows offset by 32 B (conflict-free column gathers)
@@ -75,52 +85,26 @@ template <int R>
 struct Smem {
   char k[kNB][kTile * kKStride<R>];
   char v[kNB][kVBytes<R>];
+  float4 spart[kWaves][64];   // partial scores of each wave (its lanes' float4)
   float pt[16][kTile];        // P of the group's query heads for the current tile
   float alpha[16];            // rescale factor of each query head for this tile
+  float rstep[64][2];         // cos, sin of 16 * omega_f
 };
 
-// one tile of H_k and H_v: 16 rows x R bf16 each = 32*R bytes; every thread of
-// the workgroup moves 32*R / 256 bytes, i.e. R/128 16-byte pieces of each
+// A tile is 16 rows x R bf16 per matrix = 2R pieces of 16 B; threads below 2R
+// move one piece of H_k and one of H_v. Byte offset of a thread's piece within
+// a row-major tile of 16 rows:
 template <int R>
-struct Stage {
-  uint4 k[R / 128];
-  uint4 v[R / 128];
-};
+__device__ __forceinline__ int piece_row(int tid) { return (tid * 16) / (2 * R); }
+template <int R>
+__device__ __forceinline__ int piece_col(int tid) { return (tid * 16) % (2 * R); }
 
 template <int R>
-__device__ __forceinline__ void load_stage(Stage<R>& sg, const uint16_t* Hk, const uint16_t* Hv,
-                                           int tok0, int last, int tid) {
-#pragma unroll
-  for (int q = 0; q < R / 128; ++q) {
-    const int flat = (q * 256 + tid) * 16;               // byte in the tile's 16 rows
-    const int row = min(tok0 + flat / (2 * R), last);
-    const int cb = flat % (2 * R);
-    sg.k[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Hk + static_cast<size_t>(row) * R) + cb);
-    sg.v[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Hv + static_cast<size_t>(row) * R) + cb);
-  }
-}
-
-template <int R>
-__device__ __forceinline__ void store_stage(const Stage<R>& sg, char* kt, char* vt, int tid) {
-#pragma unroll
-  for (int q = 0; q < R / 128; ++q) {
-    const int flat = (q * 256 + tid) * 16;
-    const int row = flat / (2 * R), cb = flat % (2 * R);
-    *reinterpret_cast<uint4*>(kt + row * kKStride<R> + cb) = sg.k[q];
-    *reinterpret_cast<uint4*>(vt + vtile_off<R>(row, cb)) = sg.v[q];
-  }
-}
-
-__device__ __forceinline__ short bf16_bits_rne(float x) {
-  return static_cast<short>(f32_to_bf16_rne(x));
-}
-
-template <int R>
-__global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, kb = lane >> 4;
-  const int jl = wave;                                   // this wave's KV head in the group
+  const int jl = wave >> 1, half = wave & 1;             // KV head in the group, column half
   const int n = clamp_len(p.lens, b, p.L);
   const int s0 = split * p.split_tokens;
   if (s0 >= n) return;                                   // whole workgroup
@@ -131,121 +115,114 @@ __global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(Dec
 
   __shared__ Smem<R> sm;
 
+  // owned 16-column blocks: cbs(j) = 2*half + j (j < 2) and their +64 partners
+  auto cbs = [half](int j) { return 2 * half + (j & 1) + 4 * (j >> 1); };
+
   // ---- operands held for the whole split -----------------------------------
-  // B_k^T rows (this head's 128 columns) as the A operand: lane (ln, kb) of
-  // block cb, chunk c holds column 16cb + ln, latents 32c + 8kb .. +8
+  // B_k^T as the A operand: lane (ln, kb) of block j, chunk c holds column
+  // 16*cbs(j) + ln, latents 32c + 8kb .. +8
   const uint16_t* Bt = static_cast<const uint16_t*>(p.bkt) +
                        (static_cast<size_t>(g) * p.Dg + jl * kD) * R;
-  uint4 bk[kBlocks][R / 32];
+  uint4 bk[4][R / 32];
 #pragma unroll
-  for (int cb = 0; cb < kBlocks; ++cb)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int c = 0; c < R / 32; ++c)
-      bk[cb][c] = *reinterpret_cast<const uint4*>(Bt + static_cast<size_t>(16 * cb + ln) * R + 32 * c + 8 * kb);
+      bk[j][c] = *reinterpret_cast<const uint4*>(Bt + static_cast<size_t>(16 * cbs(j) + ln) * R + 32 * c + 8 * kb);
   // q of this KV head's query heads as the score B operand: lane (ln = head
-  // slot, kb) of block cb holds columns 16cb + 4kb .. +4 (exact bf16)
-  short4v qb[kBlocks];
+  // slot, kb) of block j holds columns 16*cbs(j) + 4kb .. +4 (exact bf16)
+  short4v qb[4];
   {
     const bool valid = ln < gqa;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                            (static_cast<size_t>(b) * p.Hq + g * nq + jl * gqa + (valid ? ln : 0)) * kD;
 #pragma unroll
-    for (int cb = 0; cb < kBlocks; ++cb)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qb[cb][e] = valid ? static_cast<short>(qrow[16 * cb + 4 * kb + e]) : 0;
+      for (int e = 0; e < 4; ++e) qb[j][e] = valid ? static_cast<short>(qrow[16 * cbs(j) + 4 * kb + e]) : 0;
   }
-  // rotation state: this lane's token is tok0 + ln; its frequencies are
-  // f = 16*cb + 4*kb + i for cb < 4, i < 4
-  float cs[4][4], sn[4][4], cstep[4][4], sstep[4][4];
+  // rotation state for this lane's token (tok0 + ln) and its frequencies
+  // f = 16*cbs(j) + 4*kb + i, j < 2
   const bool rope = p.rope != 0;
+  float cs[2][4], sn[2][4];
   auto anchor = [&](int tok) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (rope) rope_cos_sin(p.omega_rev[16 * cb + 4 * kb + i], tok + ln, cs[cb][i], sn[cb][i]);
-        else { cs[cb][i] = 1.f; sn[cb][i] = 0.f; }
+        if (rope) rope_cos_sin(p.omega_rev[16 * cbs(j) + 4 * kb + i], tok + ln, cs[j][i], sn[j][i]);
+        else { cs[j][i] = 1.f; sn[j][i] = 0.f; }
       }
   };
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (rope) rope_cos_sin(p.omega_rev[16 * cb + 4 * kb + i], kTile, cstep[cb][i], sstep[cb][i]);
-      else { cstep[cb][i] = 1.f; sstep[cb][i] = 0.f; }
-    }
+  if (tid < 64) {   // per-tile rotation steps, one shared table
+    float c = 1.f, sv = 0.f;
+    if (rope) rope_cos_sin(p.omega_rev[tid], kTile, c, sv);
+    sm.rstep[tid][0] = c;
+    sm.rstep[tid][1] = sv;
+  }
 
   // ---- softmax state of the owned query heads (lane ln = head slot) ---------
   float m = -INFINITY, l = 0.f;
   // value-latent sums for all query heads over this wave's r slice:
-  // acc[rb] holds r = wave*R/4 + 16*rb + 4*kb + i for query head ln
-  floatx4 acc[R / 64];
+  // acc[rb] holds r = wave*R/8 + 16*rb + 4*kb + i for query head ln
+  constexpr int kRB = R / (16 * kWaves);
+  floatx4 acc[kRB];
 #pragma unroll
-  for (int rb = 0; rb < R / 64; ++rb) acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < kRB; ++rb) acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
   const uint16_t* Hk = static_cast<const uint16_t*>(p.h_k) + row0 * R;
   const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
   const int ntiles = (t1 - s0 + kTile - 1) / kTile;
 
-  // prologue: tile 0 into LDS, tile 1 staged in registers
-  Stage<R> sg;
-  load_stage<R>(sg, Hk, Hv, s0, last, tid);
-  store_stage<R>(sg, sm.k[0], sm.v[0], tid);
-  load_stage<R>(sg, Hk, Hv, s0 + kTile, last, tid);
-
-  for (int it = 0; it < ntiles; ++it) {
+  auto process = [&](int it) {
     const int tok0 = s0 + it * kTile;
-    // tile it+1 to LDS (its buffer held tile it-2, finished by everyone), then
-    // fetch tile it+2 into the staging registers
-    store_stage<R>(sg, sm.k[(it + 1) % kNB], sm.v[(it + 1) % kNB], tid);
-    load_stage<R>(sg, Hk, Hv, tok0 + 2 * kTile, last, tid);
-    __syncthreads();
     const char* kt = sm.k[it % kNB];
     const char* vt = sm.v[it % kNB];
-
-    // keys of this head: K^T[16cb + 4kb + i][token ln]
-    floatx4 kk[kBlocks];
+    // keys of the owned blocks: K^T[16*cbs(j) + 4kb + i][token ln]
+    floatx4 kk[4];
 #pragma unroll
-    for (int cb = 0; cb < kBlocks; ++cb) kk[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) kk[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < R / 32; ++c) {
       const bf16x8 h = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
 #pragma unroll
-      for (int cb = 0; cb < kBlocks; ++cb)
-        kk[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bk[cb][c]), h, kk[cb], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        kk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bk[j][c]), h, kk[j], 0, 0, 0);
     }
     // rotate the pairs (f, f + 64) and advance cos/sin by 16 positions
     if (it % kAnchor == 0) anchor(tok0);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = kk[cb][i], y = kk[cb + 4][i];
-        const float c = cs[cb][i], s = sn[cb][i];
-        kk[cb][i] = x * c - y * s;
-        kk[cb + 4][i] = x * s + y * c;
-        cs[cb][i] = c * cstep[cb][i] - s * sstep[cb][i];
-        sn[cb][i] = s * cstep[cb][i] + c * sstep[cb][i];
+        const float x = kk[j][i], y = kk[j + 2][i];
+        const float c = cs[j][i], s = sn[j][i];
+        kk[j][i] = x * c - y * s;
+        kk[j + 2][i] = x * s + y * c;
+        const int f = 16 * cbs(j) + 4 * kb + i;
+        const float cst = sm.rstep[f][0], sst = sm.rstep[f][1];
+        cs[j][i] = c * cst - s * sst;
+        sn[j][i] = s * cst + c * sst;
       }
-    // scores S^T[token 4kb+i][head slot ln] = K_rot . q over the 8 blocks
+    // partial scores S^T[token 4kb+i][head slot ln] over the owned blocks
     floatx4 sc = {0.f, 0.f, 0.f, 0.f}, sc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < kBlocks; ++cb) {
-      short4v ah, al;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const short hb = bf16_bits_rne(kk[cb][i]);
-        ah[i] = hb;
-        al[i] = bf16_bits_rne(kk[cb][i] - __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(hb)) << 16));
-      }
-      sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[cb], sc, 0, 0, 0);
-      sc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[cb], sc2, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const bf16x4 hb = {(__bf16)kk[j][0], (__bf16)kk[j][1], (__bf16)kk[j][2], (__bf16)kk[j][3]};
+      const short4v ah = __builtin_bit_cast(short4v, hb);
+      const short4v al = to_bf16x4(kk[j][0] - bf16_to_f32(hb[0]), kk[j][1] - bf16_to_f32(hb[1]),
+                                   kk[j][2] - bf16_to_f32(hb[2]), kk[j][3] - bf16_to_f32(hb[3]));
+      sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], sc, 0, 0, 0);
+      sc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[j], sc2, 0, 0, 0);
     }
     sc += sc2;
-    // online softmax for the owned heads (lanes ln < gqa carry real heads)
-    float pv[4];
-    {
+    sm.spart[wave][lane] = float4{sc[0], sc[1], sc[2], sc[3]};
+    __syncthreads();
+    // softmax of the owned heads by the first wave of each KV head
+    if (half == 0) {
+      const float4 o = sm.spart[wave + 1][lane];
+      sc[0] += o.x; sc[1] += o.y; sc[2] += o.z; sc[3] += o.w;
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -259,6 +236,7 @@ __global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(Dec
       const float alpha = exp2f(m - mn);
       m = mn;
       l *= alpha;
+      float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pv[i] = exp2f(sc[i] - mn);
@@ -276,17 +254,13 @@ __global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(Dec
       const bool hv = ln < nq;
       const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
       const float al = hv ? sm.alpha[ln] : 1.f;
-      short4v ph, pl;
-      const float pa[4] = {pp.x, pp.y, pp.z, pp.w};
+      const bf16x4 hb = {(__bf16)pp.x, (__bf16)pp.y, (__bf16)pp.z, (__bf16)pp.w};
+      const short4v ph = __builtin_bit_cast(short4v, hb);
+      const short4v pl = to_bf16x4(pp.x - bf16_to_f32(hb[0]), pp.y - bf16_to_f32(hb[1]),
+                                   pp.z - bf16_to_f32(hb[2]), pp.w - bf16_to_f32(hb[3]));
+      const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / kWaves) + ln));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float hi = __uint_as_float(__float_as_uint(pa[e]) & 0xffff0000u);
-        ph[e] = static_cast<short>(__float_as_uint(hi) >> 16);
-        pl[e] = bf16_bits_rne(pa[e] - hi);
-      }
-      const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / 4) + ln));
-#pragma unroll
-      for (int rb = 0; rb < R / 64; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         short4v a;
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
@@ -295,12 +269,52 @@ __global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(Dec
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[rb], 0, 0, 0);
       }
     }
+  };
+
+  // Loads: each thread below 2R moves one 16-byte piece of H_k and of H_v per
+  // tile; two tiles wait in registers (stages a and b) while one is in LDS.
+  const bool mover = tid < 2 * R;
+  const int prow = piece_row<R>(tid), pcol = piece_col<R>(tid);
+  const char* gk = reinterpret_cast<const char*>(Hk) + pcol;
+  const char* gv = reinterpret_cast<const char*>(Hv) + pcol;
+  const int ko = prow * kKStride<R> + pcol, vo = vtile_off<R>(prow, pcol);
+  auto fetch = [&](int tok0, uint4& k, uint4& v) {
+    if (mover) {
+      const size_t row = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R);
+      k = *reinterpret_cast<const uint4*>(gk + row);
+      v = *reinterpret_cast<const uint4*>(gv + row);
+    }
+  };
+  auto put = [&](int buf, const uint4& k, const uint4& v) {
+    if (mover) {
+      *reinterpret_cast<uint4*>(sm.k[buf] + ko) = k;
+      *reinterpret_cast<uint4*>(sm.v[buf] + vo) = v;
+    }
+  };
+  uint4 ka, va, kb2, vb2;
+  fetch(s0, ka, va);
+  put(0, ka, va);
+  fetch(s0 + kTile, ka, va);
+  fetch(s0 + 2 * kTile, kb2, vb2);
+  for (int it = 0; it < ntiles; it += 2) {
+    // stage a holds tile it+1: to LDS (its buffer held tile it-2, finished by
+    // everyone), then fetch tile it+3 into it
+    put((it + 1) % kNB, ka, va);
+    fetch(s0 + (it + 3) * kTile, ka, va);
+    __syncthreads();
+    process(it);
+    if (it + 1 < ntiles) {
+      put((it + 2) % kNB, kb2, vb2);
+      fetch(s0 + (it + 4) * kTile, kb2, vb2);
+      __syncthreads();
+      process(it + 1);
+    }
   }
 
   // ---- partials: this wave's r slice for every query head; (m, l) by owners
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (ln < gqa && kb == 0) {
+  if (half == 0 && ln < gqa && kb == 0) {
     const int head = g * nq + jl * gqa + ln;
     const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
     p.part_ml[slot * 2] = m;
@@ -309,9 +323,9 @@ __global__ __launch_bounds__(64 * kWaves) void split_reconstruct_mfma_kernel(Dec
   if (ln < nq) {
     const int head = g * nq + ln;
     const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
-    float* u = p.part_u + slot * R + wave * (R / 4);
+    float* u = p.part_u + slot * R + wave * (R / kWaves);
 #pragma unroll
-    for (int rb = 0; rb < R / 64; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
       *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) = float4{acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]};
   }
 }
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(256) void transpose_bk_kernel(DecodeParams p) {
 }  // namespace
 
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && p.d == kD && p.s == kWaves && p.gqa <= 4 && (p.r == 128 || p.r == 256);
+  return dtype == 1 && p.d == kD && p.s == kHeads && p.gqa <= 4 && (p.r == 128 || p.r == 256);
 }
 
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st) {
@@ -351,8 +365,8 @@ hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st)
 
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st) {
   const dim3 grid(p.n_split, p.G, p.B);
-  if (p.r == 128) split_reconstruct_mfma_kernel<128><<<grid, 64 * kWaves, 0, st>>>(p);
-  else if (p.r == 256) split_reconstruct_mfma_kernel<256><<<grid, 64 * kWaves, 0, st>>>(p);
+  if (p.r == 128) split_reconstruct_mfma_kernel<128><<<grid, kThreads, 0, st>>>(p);
+  else if (p.r == 256) split_reconstruct_mfma_kernel<256><<<grid, kThreads, 0, st>>>(p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
