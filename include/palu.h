@@ -120,20 +120,25 @@ typedef struct palu_append_desc {
   int32_t dtype;     /* palu_dtype of x, a_k, a_v and the cache                    */
 } palu_append_desc;
 
-/* Bytes of device workspace palu_latent_append needs for this descriptor
- * (fp32 partial sums over slices of 128 rows of d_model). */
+/* Bytes of device workspace palu_latent_append needs for this descriptor:
+ * arrival counters (one int32 per 128 columns of [a_k | a_v], padded to 256
+ * bytes) followed by fp32 partial sums over slices of 128 rows of d_model. */
 palu_status palu_latent_append_workspace(const palu_append_desc* desc, size_t* bytes);
 
 /* Cache write of one token per sequence (answer to Q2: h = x A):
  *   h_k[b, g, pos[b], :] = x[b] . a_k[:, g*r:(g+1)*r], likewise h_v with a_v.
  *   x [B, d_model]; a_k, a_v [d_model, G*r]; h_k, h_v [B, G, L_cap, r];
- *   pos [B] int32 on the device; workspace of at least the size reported by
- *   palu_latent_append_workspace (overwritten). Products are summed in fp32
- *   (per 128-row slice, then the slices in order); a bf16 cache stores the sum
- *   rounded to the nearest bf16 (ties to even). Rows with pos outside
- *   [0, L_cap) are left untouched. Errors: NULL, SHAPE (also G*r > 65536 or
- *   G*r not a multiple of 8),
- *   UNSUPPORTED, WORKSPACE, DEVICE. */
+ *   pos [B] int32 on the device; workspace: 16-byte aligned device memory of
+ *   at least the size reported by palu_latent_append_workspace whose counter
+ *   area (its first bytes, see above) is zero before the first call, e.g.
+ *   allocated zeroed; every call that completes leaves it zero again and
+ *   overwrites the rest. Calls that share a workspace must not overlap in
+ *   time (same stream, or ordered by events). Products are summed in fp32
+ *   (per 128-row slice in a fixed order, then the slices in order); a bf16
+ *   cache stores the sum rounded to the nearest bf16 (ties to even). Rows with
+ *   pos outside [0, L_cap) are left untouched. Errors: NULL, SHAPE (also
+ *   G*r > 65536 or G*r not a multiple of 8), UNSUPPORTED, WORKSPACE (too small
+ *   or misaligned), DEVICE. */
 palu_status palu_latent_append(const palu_append_desc* desc, const void* x, const void* a_k,
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,
                                void* workspace, size_t workspace_bytes, void* stream);

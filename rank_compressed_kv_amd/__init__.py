@@ -263,6 +263,6 @@ def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> No
     _, G, L, r = h_k.shape
     desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
     if workspace is None:
-        workspace = torch.empty(palu_latent_append_workspace(desc), dtype=torch.uint8,
+        workspace = torch.zeros(palu_latent_append_workspace(desc), dtype=torch.uint8,
                                 device=x.device)
     palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, workspace, stream)

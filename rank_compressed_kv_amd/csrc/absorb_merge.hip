@@ -311,6 +311,109 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   }
 }
 
+// Merge for up to kFastSplits splits, d/8 a power of two <= 32, r <= 512:
+// every wave reduces the split states itself (lane s holds split s), so the
+// only workgroup barriers are the two around the B_v product, and every load
+// (split states, partials of the first 16 splits, the first 16 B_v rows of the
+// thread) is issued before any arithmetic.
+constexpr int kFastSplits = 64;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int j = h / p.gqa, g = j / p.s, jl = j % p.s;
+  const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
+  const float* ml = p.part_ml + base * 2;
+  const float* pu = p.part_u + base * p.r;
+  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
+  const int ncc = p.d / 8, ngroups = kThreads / ncc;
+  const int cc = tid % ncc, rg = tid / ncc;
+  const int nrow = (p.r + ngroups - 1) / ngroups;      // B_v rows of this thread
+
+  // Loads do not wait for the sequence length: the first 16 splits' states
+  // and partials (all inside the workspace) are requested together with the
+  // length and B_v, and entries of splits >= ns are discarded afterwards.
+  float bv[16][8];
+  auto load_bv = [&](int i0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = rg + ngroups * (i0 + i);
+      if (k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
+    }
+  };
+  // thread t holds u entries t and t + 256 of 16 splits at a time
+  float ua[16], ub[16];
+  auto load_u = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int sp = min(s0 + u, p.n_split - 1);
+      const float* row = pu + static_cast<size_t>(sp) * p.r;
+      ua[u] = tid < p.r ? row[tid] : 0.f;
+      ub[u] = tid + kThreads < p.r ? row[tid + kThreads] : 0.f;
+    }
+  };
+  const int n = clamp_len(p.lens, b, p.L);
+  const float ms_raw = lane < p.n_split ? ml[2 * lane] : 0.f;
+  const float ls_raw = lane < p.n_split ? ml[2 * lane + 1] : 0.f;
+  load_u(0);
+  load_bv(0);
+  const int ns = (n + p.split_tokens - 1) / p.split_tokens;
+  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
+  if (ns == 0) {
+    for (int c = tid; c < p.d; c += kThreads) out[c] = 0.f;
+    return;
+  }
+  const float ms = lane < ns ? ms_raw : -INFINITY;
+  const float ls = lane < ns ? ls_raw : 0.f;
+
+  // split weights 2^(m_s - M) and L = sum_s w_s l_s, in every wave
+  const float M = wave_max(ms);
+  const float w = lane < ns ? exp2f(ms - M) : 0.f;
+  const float L = wave_sum(w * ls);
+  float u0 = 0.f, u1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    if (s0 > 0) load_u(s0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (s0 + u < ns) {              // uniform; later splits hold stale data
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
+        u0 = fmaf(ws, ua[u], u0);
+        u1 = fmaf(ws, ub[u], u1);
+      }
+    }
+  }
+  __shared__ float us[2 * kThreads];
+  __shared__ float red[2048];
+  const float inv = 1.f / L;
+  if (tid < p.r) us[tid] = u0 * inv;
+  if (tid + kThreads < p.r) us[tid + kThreads] = u1 * inv;
+  __syncthreads();
+
+  // out = u* B_v[:, cols(j)]: thread (row group, 8-column chunk), groups added in LDS
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nrow; i0 += 16) {
+    if (i0 > 0) load_bv(i0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = rg + ngroups * (i0 + i);
+      const float wv = k < p.r ? us[k] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv, bv[i][e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg * p.d + 8 * cc + e] = acc[e];
+  __syncthreads();
+  if (tid < p.d) {
+    float a = 0.f;
+    for (int q = 0; q < ngroups; ++q) a += red[q * p.d + tid];
+    out[tid] = a;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
@@ -336,6 +439,13 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
 
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st) {
   const dim3 grid(p.Hq, p.B);
+  const int ncc = p.d / 8;
+  if (p.d % 8 == 0 && ncc <= 32 && (ncc & (ncc - 1)) == 0 && p.r <= 2 * kThreads &&
+      p.n_split <= kFastSplits) {
+    if (dtype == 0) merge_fast_kernel<float><<<grid, kThreads, 0, st>>>(p);
+    else merge_fast_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
+    return hipGetLastError();
+  }
   if (dtype == 0) merge_kernel<float><<<grid, kThreads, 0, st>>>(p);
   else merge_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -277,10 +278,12 @@ palu_status palu_latent_append(const palu_append_desc* d, const void* x, const v
   const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   if (workspace_bytes < need)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PALU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   AppendParams p{};
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
-  p.part = static_cast<float*>(workspace);
   p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
+  append_bind_workspace(p, workspace);
   hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   return ok();
@@ -293,8 +296,10 @@ palu_status palu_profile_begin(int32_t max_records) {
   g_prof.start.assign(max_records, nullptr);
   g_prof.stop.assign(max_records, nullptr);
   for (int i = 0; i < max_records; ++i) {
-    if (hipEventCreate(&g_prof.start[i]) != hipSuccess ||
-        hipEventCreate(&g_prof.stop[i]) != hipSuccess)
+    // timing-only events: no system-scope fence (no cache write-back and
+    // invalidation around the timed kernel)
+    if (hipEventCreateWithFlags(&g_prof.start[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&g_prof.stop[i], hipEventDisableSystemFence) != hipSuccess)
       return fail(PALU_ERR_DEVICE, "hipEventCreate failed");
   }
   g_prof.used = 0;

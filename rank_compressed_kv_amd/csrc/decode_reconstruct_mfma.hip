@@ -43,7 +43,6 @@ namespace palu {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -61,13 +60,25 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-// fp32 -> bf16 (hardware round to nearest even), as MFMA operand bits
-__device__ __forceinline__ short4v to_bf16x4(float a, float b, float c, float d) {
-  const bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-  return __builtin_bit_cast(short4v, v);
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a ~ hi + lo with hi = bf16(a) and lo = bf16(a - hi) (round to nearest even,
+// one packed conversion per pair): about 16 significant bits in two bf16 terms.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+  const float ah = __uint_as_float(hi << 16), bh = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a - ah, b - bh}, bf16x2));
 }
-__device__ __forceinline__ float bf16_to_f32(__bf16 x) {
-  return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
+__device__ __forceinline__ void split_bf16x4(floatx4 v, short4v& hi, short4v& lo) {
+  uint32_t h0, h1, l0, l1;
+  split_bf16x2(v[0], v[1], h0, l0);
+  split_bf16x2(v[2], v[3], h1, l1);
+  hi = __builtin_bit_cast(short4v, uint2{h0, h1});
+  lo = __builtin_bit_cast(short4v, uint2{l0, l1});
+}
+__device__ __forceinline__ float lane_xor(float x, int addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
 }
 
 // K tile: rows padded by 16 B so the 16 rows of an operand read hit distinct banks
@@ -88,7 +99,9 @@ struct Smem {
   float4 spart[kWaves][64];   // partial scores of each wave (its lanes' float4)
   float pt[16][kTile];        // P of the group's query heads for the current tile
   float alpha[16];            // rescale factor of each query head for this tile
-  float rstep[64][2];         // cos, sin of 16 * omega_f
+  // cos, sin of t * omega_f for the 16 tokens t of the current tile, f < 64:
+  // rtab[f / 4][t - tok0][f % 4] (a lane's four frequencies are 32 contiguous B)
+  float2 rtab[16][kTile][4];
 };
 
 // A tile is 16 rows x R bf16 per matrix = 2R pieces of 16 B; threads below 2R
@@ -141,25 +154,36 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
 #pragma unroll
       for (int e = 0; e < 4; ++e) qb[j][e] = valid ? static_cast<short>(qrow[16 * cbs(j) + 4 * kb + e]) : 0;
   }
-  // rotation state for this lane's token (tok0 + ln) and its frequencies
-  // f = 16*cbs(j) + 4*kb + i, j < 2
+  // rotation table: thread (gt = tid % 16, fa = tid / 16) keeps cos/sin of
+  // (tok0 + gt) * omega for f = fa and fa + 32 and writes them for each tile;
+  // every kAnchor tiles they are evaluated from the angle, in between they
+  // advance by one exact complex product with the 16-position step.
   const bool rope = p.rope != 0;
-  float cs[2][4], sn[2][4];
-  auto anchor = [&](int tok) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (rope) rope_cos_sin(p.omega_rev[16 * cbs(j) + 4 * kb + i], tok + ln, cs[j][i], sn[j][i]);
-        else { cs[j][i] = 1.f; sn[j][i] = 0.f; }
-      }
-  };
-  if (tid < 64) {   // per-tile rotation steps, one shared table
-    float c = 1.f, sv = 0.f;
-    if (rope) rope_cos_sin(p.omega_rev[tid], kTile, c, sv);
-    sm.rstep[tid][0] = c;
-    sm.rstep[tid][1] = sv;
+  const int gt = tid & 15, fa = tid >> 4, fb = fa + 32;
+  float ca = 1.f, sa = 0.f, cb = 1.f, sb = 0.f;
+  float stca = 1.f, stsa = 0.f, stcb = 1.f, stsb = 0.f;
+  if (rope) {
+    rope_cos_sin(p.omega_rev[fa], kTile, stca, stsa);
+    rope_cos_sin(p.omega_rev[fb], kTile, stcb, stsb);
   }
+  auto rope_exact = [&](int tok0) {
+    if (rope) {
+      rope_cos_sin(p.omega_rev[fa], tok0 + gt, ca, sa);
+      rope_cos_sin(p.omega_rev[fb], tok0 + gt, cb, sb);
+    }
+  };
+  auto rope_advance = [&]() {
+    const float c1 = ca * stca - sa * stsa, s1 = sa * stca + ca * stsa;
+    const float c2 = cb * stcb - sb * stsb, s2 = sb * stcb + cb * stsb;
+    ca = c1; sa = s1; cb = c2; sb = s2;
+  };
+  auto rope_write = [&]() {
+    sm.rtab[fa >> 2][gt][fa & 3] = float2{ca, sa};
+    sm.rtab[fb >> 2][gt][fb & 3] = float2{cb, sb};
+  };
+  rope_exact(s0);
+  rope_write();
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // bpermute addresses
 
   // ---- softmax state of the owned query heads (lane ln = head slot) ---------
   float m = -INFINITY, l = 0.f;
@@ -190,58 +214,58 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
       for (int j = 0; j < 4; ++j)
         kk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bk[j][c]), h, kk[j], 0, 0, 0);
     }
-    // rotate the pairs (f, f + 64) and advance cos/sin by 16 positions
-    if (it % kAnchor == 0) anchor(tok0);
+    // rotate the pairs (f, f + 64): f = 16*cbs(j) + 4kb + i, token ln
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[4 * cbs(j) + kb][ln][0]);
+      const float4 r01 = rt[0];
+      const float4 r23 = rt[1];
+      const float c4[4] = {r01.x, r01.z, r23.x, r23.z}, s4[4] = {r01.y, r01.w, r23.y, r23.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = kk[j][i], y = kk[j + 2][i];
-        const float c = cs[j][i], s = sn[j][i];
-        kk[j][i] = x * c - y * s;
-        kk[j + 2][i] = x * s + y * c;
-        const int f = 16 * cbs(j) + 4 * kb + i;
-        const float cst = sm.rstep[f][0], sst = sm.rstep[f][1];
-        cs[j][i] = c * cst - s * sst;
-        sn[j][i] = s * cst + c * sst;
+        kk[j][i] = x * c4[i] - y * s4[i];
+        kk[j + 2][i] = x * s4[i] + y * c4[i];
       }
+    }
     // partial scores S^T[token 4kb+i][head slot ln] over the owned blocks
     floatx4 sc = {0.f, 0.f, 0.f, 0.f}, sc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x4 hb = {(__bf16)kk[j][0], (__bf16)kk[j][1], (__bf16)kk[j][2], (__bf16)kk[j][3]};
-      const short4v ah = __builtin_bit_cast(short4v, hb);
-      const short4v al = to_bf16x4(kk[j][0] - bf16_to_f32(hb[0]), kk[j][1] - bf16_to_f32(hb[1]),
-                                   kk[j][2] - bf16_to_f32(hb[2]), kk[j][3] - bf16_to_f32(hb[3]));
+      short4v ah, al;
+      split_bf16x4(kk[j], ah, al);
       sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], sc, 0, 0, 0);
       sc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[j], sc2, 0, 0, 0);
     }
     sc += sc2;
     sm.spart[wave][lane] = float4{sc[0], sc[1], sc[2], sc[3]};
     __syncthreads();
+    // every wave has rotated this tile: the table can take the next one
+    if (it + 1 < ntiles) {
+      if ((it + 1) % kAnchor == 0) rope_exact(tok0 + kTile);
+      else if (rope) rope_advance();
+      rope_write();
+    }
     // softmax of the owned heads by the first wave of each KV head
     if (half == 0) {
       const float4 o = sm.spart[wave + 1][lane];
       sc[0] += o.x; sc[1] += o.y; sc[2] += o.z; sc[3] += o.w;
-      float mx = -INFINITY;
+      sc *= p.scale_log2;
+      if (tok0 + kTile > t1) {                           // last tile of the split
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] *= p.scale_log2;
-        if (tok0 + 4 * kb + i >= t1) sc[i] = -INFINITY;
-        mx = fmaxf(mx, sc[i]);
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 4 * kb + i >= t1) sc[i] = -INFINITY;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = fmaxf(mx, lane_xor(mx, x16));
+      mx = fmaxf(mx, lane_xor(mx, x32));
       const float mn = fmaxf(m, mx);
-      const float alpha = exp2f(m - mn);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
       m = mn;
-      l *= alpha;
       float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = exp2f(sc[i] - mn);
-        l += pv[i];
-      }
+      for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - mn);
+      l = l * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
       if (ln < gqa) {
         const int hg = jl * gqa + ln;                    // query head within the group
         *reinterpret_cast<float4*>(&sm.pt[hg][4 * kb]) = float4{pv[0], pv[1], pv[2], pv[3]};
@@ -254,10 +278,8 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
       const bool hv = ln < nq;
       const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
       const float al = hv ? sm.alpha[ln] : 1.f;
-      const bf16x4 hb = {(__bf16)pp.x, (__bf16)pp.y, (__bf16)pp.z, (__bf16)pp.w};
-      const short4v ph = __builtin_bit_cast(short4v, hb);
-      const short4v pl = to_bf16x4(pp.x - bf16_to_f32(hb[0]), pp.y - bf16_to_f32(hb[1]),
-                                   pp.z - bf16_to_f32(hb[2]), pp.w - bf16_to_f32(hb[3]));
+      short4v ph, pl;
+      split_bf16x4(floatx4{pp.x, pp.y, pp.z, pp.w}, ph, pl);
       const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / kWaves) + ln));
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {

@@ -2,18 +2,19 @@
 // answer to Q2 on ESPACE: the down-projection output is what is cached).
 //
 // x [B, d_model] times A [d_model, G*r] is a skinny product whose cost is
-// reading A once (4 MiB per matrix at d_model 4096, G*r 512 in bf16). To read A
-// once with the whole chip and every load of a thread in flight together, the
-// d_model sum is split:
-//   pass 1: workgroup (128-column block of [A_k | A_v], 128-row slice): thread
-//           (8-column chunk, row group) issues its eight 16-byte loads at once,
-//           accumulates x[b, row] * A[row, col] for every sequence, and the
-//           row groups are added (lane shuffles, then LDS) into one fp32
-//           partial per (slice, sequence, column) in the workspace;
-//   pass 2: one thread per (sequence, column) adds the slice partials in a
-//           fixed order, rounds (bf16: nearest, ties to even) and writes row
-//           pos[b] of the cache.
-// Both passes sum in fp32.
+// reading A once (4 MiB per matrix at d_model 4096, G*r 512 in bf16) and whose
+// time is one memory latency if every load of the chip is in flight together.
+// One launch does all of it, split over d_model:
+//   every workgroup owns a 128-column block of [A_k | A_v] and a 128-row
+//   slice; thread (8-column chunk, row group of 8 rows) issues its eight
+//   16-byte loads at once and accumulates x[b, row] * A[row, col] for every
+//   sequence. The 16 row groups are added in LDS in a fixed order and the
+//   workgroup stores one fp32 partial per (slice, sequence, column) in the
+//   workspace, then counts itself in the column block's arrival counter;
+//   the last workgroup of a column block adds the slice partials in slice
+//   order, rounds (bf16: nearest, ties to even), writes row pos[b] of the
+//   cache and puts the counter back to zero for the next call.
+// The result does not depend on which workgroup arrives last.
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -25,20 +26,42 @@ constexpr int kRows = 128;          // d_model rows per slice
 constexpr int kCols = 128;          // columns per block (16 chunks of 8)
 constexpr int kRowGroups = 16;      // threads per column chunk; 8 rows each
 constexpr int kBatchChunk = 8;      // sequences accumulated per pass
+constexpr size_t kCounterAlign = 256;
+
+// LDS slot of the 4-column quarter (chunk cc, half hf) of a block: the two
+// halves of a chunk are 16 slots apart so a wave's 16-byte writes spread over
+// all banks; slot q holds columns col_of_slot(q) .. +4.
+__device__ __forceinline__ int col_of_slot(int q) { return q < 16 ? 8 * q : 8 * (q - 16) + 4; }
+
+// Hand-off of the partials between workgroups on different XCDs, whose L2
+// caches are not coherent with each other:
+//   writer: device-scope stores (written through past its L2), then
+//           s_waitcnt vmcnt(0) (acknowledged, i.e. performed at device scope)
+//           before the workgroup barrier and the counter increment, so no
+//           cache-wide L2 write-back is needed;
+//   reader: the last arriver's device-scope acquire fence invalidates its own
+//           caches, after which ordinary 16-byte loads see every partial.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void append_partial_kernel(AppendParams p) {
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   const int width = p.G * p.r;                 // columns of one matrix
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int cc = tid % 16, rg = tid / 16;      // 8-column chunk, row group
-  const int col0 = blockIdx.x * kCols + 8 * cc;  // in [0, 2*width)
-  const int i0 = blockIdx.y * kRows;
+  const int cb0 = blockIdx.x * kCols;
+  const int col0 = cb0 + 8 * cc;               // in [0, 2*width)
+  const int slice = blockIdx.y, nslices = gridDim.y;
+  const int i0 = slice * kRows;
   const int rows = min(kRows, p.dm - i0);
   const bool active = col0 < 2 * width;
   const bool is_v = col0 >= width;
   const int c = is_v ? col0 - width : col0;
   const T* A = static_cast<const T*>(is_v ? p.a_v : p.a_k);
   const T* x = static_cast<const T*>(p.x);
+  const size_t prow = 2 * static_cast<size_t>(width);   // floats per (slice, sequence)
 
   // all of this thread's A rows (rg + 16 i) first, 16 bytes each
   float a[8][8];
@@ -51,7 +74,10 @@ __global__ __launch_bounds__(kThreads) void append_partial_kernel(AppendParams p
       for (int e = 0; e < 8; ++e) a[i][e] = 0.f;
   }
   __shared__ float xs[kBatchChunk][kRows];
-  __shared__ float red[kThreads / 64][kBatchChunk][kCols];
+  __shared__ float4 red[kRowGroups][kBatchChunk][kCols / 4];
+  __shared__ int is_last;
+  const int fb = tid / 32, fq = tid % 32;      // reader: sequence in chunk, slot
+  const int fcol = cb0 + col_of_slot(fq);
   for (int b0 = 0; b0 < p.B; b0 += kBatchChunk) {
     const int nb = min(kBatchChunk, p.B - b0);
     __syncthreads();
@@ -60,93 +86,103 @@ __global__ __launch_bounds__(kThreads) void append_partial_kernel(AppendParams p
       xs[bb][i] = bb < nb && i < rows ? load_f32(x, static_cast<size_t>(b0 + bb) * p.dm + i0 + i) : 0.f;
     }
     __syncthreads();
-    float acc[kBatchChunk][8];
 #pragma unroll
     for (int bb = 0; bb < kBatchChunk; ++bb) {
+      float acc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[bb][e] = 0.f;
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float xv = xs[bb][rg + kRowGroups * i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(xv, a[i][e], acc[bb][e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv, a[i][e], acc[e]);
       }
-    }
-    // add the four row groups of this wave (lanes cc, cc+16, cc+32, cc+48),
-    // then the four waves through LDS
-#pragma unroll
-    for (int bb = 0; bb < kBatchChunk; ++bb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[bb][e];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[bb][e] = v;
-      }
-    if (lane < 16) {
-#pragma unroll
-      for (int bb = 0; bb < kBatchChunk; ++bb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave][bb][8 * cc + e] = acc[bb][e];
+      red[rg][bb][cc] = float4{acc[0], acc[1], acc[2], acc[3]};
+      red[rg][bb][cc + 16] = float4{acc[4], acc[5], acc[6], acc[7]};
     }
     __syncthreads();
-    for (int e = tid; e < nb * kCols; e += kThreads) {
-      const int bb = e / kCols, cl = e % kCols;
-      const int col = blockIdx.x * kCols + cl;
-      if (col < 2 * width) {
-        const float v = (red[0][bb][cl] + red[1][bb][cl]) + (red[2][bb][cl] + red[3][bb][cl]);
-        p.part[(static_cast<size_t>(blockIdx.y) * p.B + b0 + bb) * 2 * width + col] = v;
+    // row groups added in order; one 16-byte partial per thread
+    float4 s = red[0][fb][fq];
+#pragma unroll
+    for (int k = 1; k < kRowGroups; ++k) {
+      const float4 v = red[k][fb][fq];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (fb < nb && fcol < 2 * width) {
+      float* dst = p.part + (static_cast<size_t>(slice) * p.B + b0 + fb) * prow + fcol;
+      store_coherent(dst + 0, s.x);
+      store_coherent(dst + 1, s.y);
+      store_coherent(dst + 2, s.z);
+      store_coherent(dst + 3, s.w);
+    }
+  }
+
+  // arrival: every thread's partial stores are complete (device-coherent)
+  // before the workgroup is counted; the last one reads them coherently.
+  wait_stores_complete();
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == nslices - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  if (fcol < 2 * width) {
+    const size_t sstride = static_cast<size_t>(p.B) * prow;
+    for (int b = fb; b < p.B; b += kThreads / 32) {
+      const int pos = p.pos[b];
+      if (pos < 0 || pos >= p.L) continue;
+      const float* src = p.part + static_cast<size_t>(b) * prow + fcol;
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < nslices; s0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = s0 + u < nslices ? *reinterpret_cast<const float4*>(src + (s0 + u) * sstride)
+                                  : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {   // slices added in order
+          acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        }
+      }
+      const float r4[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = fcol + e;
+        const bool v = col >= width;
+        const int cl = v ? col - width : col;
+        const int g = cl / p.r, k = cl % p.r;
+        T* h = static_cast<T*>(v ? p.h_v : p.h_k);
+        store_elem(h, ((static_cast<size_t>(b) * p.G + g) * p.L + pos) * p.r + k, r4[e]);
       }
     }
   }
+  if (tid == 0) __hip_atomic_store(&p.counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void append_finish_kernel(AppendParams p) {
-  const int width = p.G * p.r;
-  const int col = blockIdx.x * kThreads + threadIdx.x;
-  const int b = blockIdx.y;
-  if (col >= 2 * width) return;
-  const int pos = p.pos[b];
-  if (pos < 0 || pos >= p.L) return;
-  const int nks = (p.dm + kRows - 1) / kRows;
-  const size_t stride = static_cast<size_t>(p.B) * 2 * width;
-  const float* src = p.part + static_cast<size_t>(b) * 2 * width + col;
-  float acc = 0.f;
-  for (int k0 = 0; k0 < nks; k0 += 32) {
-    float v[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) v[u] = k0 + u < nks ? src[(k0 + u) * stride] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) acc += v[u];   // slices added in order
-  }
-  const bool is_v = col >= width;
-  const int c = is_v ? col - width : col;
-  const int g = c / p.r, k = c % p.r;
-  T* h = static_cast<T*>(is_v ? p.h_v : p.h_k);
-  store_elem(h, ((static_cast<size_t>(b) * p.G + g) * p.L + pos) * p.r + k, acc);
+size_t counter_bytes(int G, int r) {
+  const size_t blocks = (2 * static_cast<size_t>(G) * r + kCols - 1) / kCols;
+  return (blocks * sizeof(int32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
 }
 
 }  // namespace
 
 size_t append_workspace_bytes(int B, int dm, int G, int r) {
   const size_t nks = (dm + kRows - 1) / kRows;
-  return nks * B * 2 * size_t(G) * r * sizeof(float);
+  return counter_bytes(G, r) + nks * B * 2 * size_t(G) * r * sizeof(float);
 }
 
-bool append_shape_supported(int G, int r) { return (G * r) % 8 == 0; }
+void append_bind_workspace(AppendParams& p, void* workspace) {
+  p.counters = static_cast<int32_t*>(workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p.G, p.r));
+}
 
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
   const int cols = 2 * p.G * p.r;
-  const dim3 g1((cols + kCols - 1) / kCols, (p.dm + kRows - 1) / kRows);
-  const dim3 g2((cols + kThreads - 1) / kThreads, p.B);
-  if (dtype == 0) {
-    append_partial_kernel<float><<<g1, kThreads, 0, st>>>(p);
-    append_finish_kernel<float><<<g2, kThreads, 0, st>>>(p);
-  } else {
-    append_partial_kernel<uint16_t><<<g1, kThreads, 0, st>>>(p);
-    append_finish_kernel<uint16_t><<<g2, kThreads, 0, st>>>(p);
-  }
+  const dim3 grid((cols + kCols - 1) / kCols, (p.dm + kRows - 1) / kRows);
+  if (dtype == 0) append_kernel<float><<<grid, kThreads, 0, st>>>(p);
+  else append_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct AppendParams {
   void* h_k;          // [B, G, L, r]
   void* h_v;
   const int32_t* pos; // [B]
+  int32_t* counters;  // one arrival counter per 128-column block; zero between calls
   float* part;        // [ceil(dm/128), B, 2*G*r] fp32 row-slice partial sums
   int32_t B, dm, G, r, L;
 };
@@ -64,6 +65,7 @@ hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st)
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 size_t append_workspace_bytes(int B, int dm, int G, int r);
+void append_bind_workspace(AppendParams& p, void* workspace);   // sets counters, part
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu

@@ -130,9 +130,14 @@ def test_append_validation(lib):
     assert lib.palu_latent_append(None, fake, fake, fake, fake, fake, fake, fake, big,
                                   None) == P.PALU_ERR_NULL
     need = P.palu_latent_append_workspace(good)
-    assert need == 32 * 8 * 1024 * 4        # 128-row slices x batch x (k and v columns)
+    # 256 bytes of arrival counters (8 column blocks of 128), then the partials
+    # of 128-row slices x batch x (k and v columns)
+    assert need == 256 + 32 * 8 * 1024 * 4
     assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake,
                                   need - 1, None) == P.PALU_ERR_WORKSPACE
+    misaligned = ctypes.c_void_p(0x1008)
+    assert lib.palu_latent_append(ctypes.byref(good), fake, fake, fake, fake, fake, fake,
+                                  misaligned, need, None) == P.PALU_ERR_WORKSPACE
 
 
 def test_profile_calls_validate(lib):

@@ -86,6 +86,17 @@ def test_length_edges_and_poisoned_tail(idx, mode):
         assert_close(got, want, what=f"edges cfg{idx}/{mode}/split{st}", **_tol(cfg))
 
 
+@pytest.mark.parametrize("mode", ["absorbed", "reconstruct"])
+def test_more_than_64_splits(mode):
+    """79 splits of 64 tokens: the merge that stages split states through LDS
+    (the fast merge keeps at most 64 split states in one wave)."""
+    cfg = W.CONFIGS[4].scaled(max_ctx=5000)
+    t = W.generate(cfg)
+    print(f"[many splits] cfg4 mode={mode}", flush=True)
+    got, theta = run_decode(cfg, t, mode, split_tokens=64)
+    assert_close(got, _oracle(cfg, t, theta), what=f"79 splits/{mode}")
+
+
 def test_null_lens_means_full_capacity():
     cfg = SMALL[3].scaled(max_ctx=300)
     t = W.generate(cfg)
@@ -140,6 +151,31 @@ def test_latent_append(idx):
         mask[b, int(pos)] = False
     assert torch.equal(hk.cpu()[:, :, :, :].permute(0, 2, 1, 3)[mask],
                        before_k.cpu().permute(0, 2, 1, 3)[mask])
+
+
+def test_append_workspace_reuse():
+    """The arrival counters return to zero after every call, so one workspace
+    serves call after call (batch sizes and positions changing) with results
+    bit-identical to calls on a fresh workspace."""
+    import torch
+    import rank_compressed_kv_amd as P
+    ws = None
+    for i, batch in enumerate((4, 2, 4)):
+        cfg = W.CONFIGS[3].scaled(batch=batch, max_ctx=16, seed=100 + i)
+        t = W.generate(cfg, parts=("decode", "append"))
+        x, ak, av, pos = dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), dev(t["pos"])
+        hk, hv = dev(t["h_k"]), dev(t["h_v"])
+        hk2, hv2 = hk.clone(), hv.clone()
+        desc = P.append_desc(batch=batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
+                             rank=cfg.rank, max_ctx=16, dtype=P.PALU_BF16)
+        if ws is None:
+            ws = torch.zeros(P.palu_latent_append_workspace(desc), dtype=torch.uint8,
+                             device="cuda")
+        P.palu_latent_append(desc, x, ak, av, hk, hv, pos, ws)
+        P.latent_append(x, ak, av, hk2, hv2, pos)          # fresh zeroed workspace
+        torch.cuda.synchronize()
+        assert torch.equal(hk, hk2) and torch.equal(hv, hv2)
+        assert int(ws[:256].count_nonzero()) == 0
 
 
 def test_append_out_of_range_rows_skipped():
