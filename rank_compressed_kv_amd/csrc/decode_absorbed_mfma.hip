@@ -46,14 +46,15 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazy = 8.0f;   // log2 units: p <= 2^8 between rescales
-constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTile = 16;       // tokens per tile
-#ifndef ABS_NBUF
-#define ABS_NBUF 2      // register tile buffers per wave (measured best of 2..4)
+#ifndef ABS_WAVES
+#define ABS_WAVES 4     // waves per workgroup (one per SIMD; measured better than 8)
 #endif
-#ifndef ABS_MINW
-#define ABS_MINW 1
+#ifndef ABS_INFLIGHT
+#define ABS_INFLIGHT 1  // tiles in flight per wave
 #endif
+constexpr int kWaves = ABS_WAVES;
+constexpr int kInFlight = ABS_INFLIGHT;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -79,30 +80,12 @@ __device__ __forceinline__ int vtile_off(int row, int cb) {
 }
 template <int R>
 constexpr int kVTileBytes = kTile * R * 2 + 3 * 32;
-
+// key tile rows padded by 16 bytes: the 16 rows of an operand read start on
+// different banks
 template <int R>
-struct Tile {
-  uint4 k[R / 32];     // H_k row tok0 + lane%16: 8 latents at 32c + 8*(lane/16)
-  uint4 v[R / 32];     // H_v: 16 rows x R contiguous, 1 KiB per entry across the wave
-};
-
+constexpr int kKStride = 2 * R + 16;
 template <int R>
-__device__ __forceinline__ void load_k(Tile<R>& tl, const uint16_t* Hk, int tok0, int last, int lane) {
-  const int rk = min(tok0 + (lane & 15), last);
-#pragma unroll
-  for (int c = 0; c < R / 32; ++c)
-    tl.k[c] = *reinterpret_cast<const uint4*>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * (lane >> 4));
-}
-
-template <int R>
-__device__ __forceinline__ void load_v(Tile<R>& tl, const uint16_t* Hv, int tok0, int last, int lane) {
-#pragma unroll
-  for (int q = 0; q < R / 32; ++q) {
-    const int flat = q * 1024 + lane * 16;              // byte within the tile's 16 rows
-    const int rv = min(tok0 + flat / (2 * R), last);
-    tl.v[q] = *reinterpret_cast<const uint4*>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
-  }
-}
+constexpr int kKTileBytes = kTile * kKStride<R>;
 
 template <int R>
 struct State {
@@ -111,19 +94,9 @@ struct State {
   float l;               // this lane's share of the running sum
 };
 
-// stage a tile's value latents in this wave's LDS tile (swizzled columns)
-template <int R>
-__device__ __forceinline__ void stage_v(const Tile<R>& tl, char* vt, int lane) {
-#pragma unroll
-  for (int q = 0; q < R / 32; ++q) {
-    const int flat = q * 1024 + lane * 16;
-    *reinterpret_cast<uint4*>(vt + vtile_off<R>(flat / (2 * R), flat % (2 * R))) = tl.v[q];
-  }
-}
-
 // scores of a tile (log2 units), masked past t1
 template <int R>
-__device__ __forceinline__ floatx4 scores(const Tile<R>& tl, const QTile<R>& qs, int tok0, int t1,
+__device__ __forceinline__ floatx4 scores(const char* kt, const QTile<R>& qs, int tok0, int t1,
                                           int lane) {
   const int ln = lane & 15, kb = lane >> 4;
   // four independent accumulators (hi/lo x even/odd chunk) keep the MFMA
@@ -133,7 +106,7 @@ __device__ __forceinline__ floatx4 scores(const Tile<R>& tl, const QTile<R>& qs,
   for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < R / 32; ++c) {
-    const bf16x8 a = as_bf16x8(tl.k[c]);
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
     const bf16x8 qh = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[0][ln][32 * c + 8 * kb]));
     const bf16x8 ql = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[1][ln][32 * c + 8 * kb]));
     acc4[2 * (c & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh, acc4[2 * (c & 1)], 0, 0, 0);
@@ -188,16 +161,46 @@ template <int R>
 struct Smem {
   QTile<R> q;
   union {
-    char vt[kWaves][kVTileBytes<R>];                 // per-wave value tiles (streaming)
+    struct {                                         // per-wave tiles (streaming)
+      char kt[kWaves][kKTileBytes<R>];
+      char vt[kWaves][kVTileBytes<R>];
+    } t;
     struct {                                         // softmax states (final merge)
-      float acc[kWaves - 1][4 * (R / 16)][64];
-      float m[kWaves - 1][64], l[kWaves - 1][64];
+      float acc[kWaves / 2][4 * (R / 16)][64];
+      float m[kWaves / 2][64], l[kWaves / 2][64];
     } x;
   } u;
 };
 
-template <int R, int kBuf, int kMinWaves>
-__global__ __launch_bounds__(64 * kWaves, kMinWaves) void split_absorbed_mfma_kernel(DecodeParams p) {
+// st <- st (+) the state another wave published in slot w; a side that saw no
+// token has m = -inf and weight 0
+template <int R>
+__device__ __forceinline__ void combine(State<R>& st, const Smem<R>& sm, int w, int lane) {
+  const float mo = sm.u.x.m[w][lane];
+  const float M = fmaxf(st.m, mo);
+  const float a = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
+  const float c = mo == -INFINITY ? 0.f : exp2f(mo - M);
+  st.m = M;
+  st.l = st.l * a + sm.u.x.l[w][lane] * c;
+#pragma unroll
+  for (int rb = 0; rb < R / 16; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st.acc[rb][i] = st.acc[rb][i] * a + sm.u.x.acc[w][4 * rb + i][lane] * c;
+}
+
+template <int R>
+__device__ __forceinline__ void publish(const State<R>& st, Smem<R>& sm, int w, int lane) {
+#pragma unroll
+  for (int rb = 0; rb < R / 16; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.u.x.acc[w][4 * rb + i][lane] = st.acc[rb][i];
+  sm.u.x.m[w][lane] = st.m;
+  sm.u.x.l[w][lane] = st.l;
+}
+
+template <int R>
+__global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
@@ -235,71 +238,83 @@ __global__ __launch_bounds__(64 * kWaves, kMinWaves) void split_absorbed_mfma_ke
   const int ntiles = (t1 - s0 + kTile - 1) / kTile;
   const int mine = (ntiles - wave + kWaves - 1) / kWaves;   // may be 0
   if (mine > 0) {
-    char* vt = sm.u.vt[wave];
+    char* kt = sm.u.t.kt[wave];
+    char* vt = sm.u.t.vt[wave];
     const int step = kTile * kWaves;
     const int first = s0 + kTile * wave;
-    // ring of kBuf register buffers: kBuf - 1 tiles in flight while one is
-    // consumed (indices are static after unrolling)
-    Tile<R> buf[kBuf];
+    // kInFlight tiles in registers (vector types: arrays of uint4 here ended
+    // up in scratch memory) while the previous one, copied into the wave's
+    // LDS tiles, is consumed
+    typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
+    auto fetch = [&](u32v& nkv, u32v& nvv, int tok0) {
+      const int rk = min(tok0 + ln, last);
 #pragma unroll
-    for (int j = 0; j < kBuf - 1; ++j) {
-      load_k<R>(buf[j], Hk, first + step * j, last, lane);
-      load_v<R>(buf[j], Hv, first + step * j, last, lane);
-    }
-    for (int it = 0; it < mine; it += kBuf) {
+      for (int c = 0; c < R / 32; ++c) {
+        const uint4 t = load_stream16(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
+        nkv[4 * c] = t.x; nkv[4 * c + 1] = t.y; nkv[4 * c + 2] = t.z; nkv[4 * c + 3] = t.w;
+      }
 #pragma unroll
-      for (int u = 0; u < kBuf; ++u) {
-        if (it + u >= mine) break;
-        Tile<R>& nx = buf[(u + kBuf - 1) % kBuf];
-        load_k<R>(nx, Hk, first + step * (it + u + kBuf - 1), last, lane);
-        load_v<R>(nx, Hv, first + step * (it + u + kBuf - 1), last, lane);
-        stage_v<R>(buf[u], vt, lane);
-        const floatx4 s = scores<R>(buf[u], sm.q, first + step * (it + u), t1, lane);
-        softmax_values<R>(st, s, vt, lane);
+      for (int q = 0; q < R / 32; ++q) {
+        const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
+        const int rv = min(tok0 + flat / (2 * R), last);
+        const uint4 t = load_stream16(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
+        nvv[4 * q] = t.x; nvv[4 * q + 1] = t.y; nvv[4 * q + 2] = t.z; nvv[4 * q + 3] = t.w;
+      }
+    };
+    auto stage = [&](const u32v& nkv, const u32v& nvv) {
+#pragma unroll
+      for (int c = 0; c < R / 32; ++c)
+        *reinterpret_cast<uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)) =
+            uint4{nkv[4 * c], nkv[4 * c + 1], nkv[4 * c + 2], nkv[4 * c + 3]};
+#pragma unroll
+      for (int q = 0; q < R / 32; ++q) {
+        const int flat = q * 1024 + lane * 16;
+        *reinterpret_cast<uint4*>(vt + vtile_off<R>(flat / (2 * R), flat % (2 * R))) =
+            uint4{nvv[4 * q], nvv[4 * q + 1], nvv[4 * q + 2], nvv[4 * q + 3]};
+      }
+    };
+    auto consume = [&](int j) {
+      const floatx4 s = scores<R>(kt, sm.q, first + step * j, t1, lane);
+      softmax_values<R>(st, s, vt, lane);
+    };
+    u32v ka, va;
+    fetch(ka, va, first);
+    if constexpr (kInFlight == 1) {
+      for (int j = 0; j < mine; ++j) {
+        stage(ka, va);
+        fetch(ka, va, first + step * (j + 1));
+        consume(j);
+      }
+    } else {
+      u32v kb2, vb2;
+      fetch(kb2, vb2, first + step);
+      for (int j = 0; j < mine; j += 2) {
+        stage(ka, va);
+        fetch(ka, va, first + step * (j + 2));
+        consume(j);
+        if (j + 1 < mine) {
+          stage(kb2, vb2);
+          fetch(kb2, vb2, first + step * (j + 3));
+          consume(j + 1);
+        }
       }
     }
   }
 
-  // merge the waves' states in LDS (the value tiles' space, after a barrier):
-  // waves 1..3 publish, wave 0 combines. [wave][value][lane] keeps
+  // merge the waves' states in LDS (the value tiles' space, after a barrier),
+  // halving the number of live states each round: waves [h, 2h) publish,
+  // waves [0, h) fold in the state of wave + h. [slot][value][lane] keeps
   // consecutive lanes on consecutive banks.
-  __syncthreads();
-  if (wave > 0) {
 #pragma unroll
-    for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.u.x.acc[wave - 1][4 * rb + i][lane] = st.acc[rb][i];
-    sm.u.x.m[wave - 1][lane] = st.m;
-    sm.u.x.l[wave - 1][lane] = st.l;
+  for (int h = kWaves / 2; h >= 1; h /= 2) {
+    __syncthreads();
+    if (wave >= h && wave < 2 * h) publish<R>(st, sm, wave - h, lane);
+    __syncthreads();
+    if (wave < h) combine<R>(st, sm, wave, lane);
   }
-  __syncthreads();
   if (wave > 0) return;
-  float mw[kWaves - 1];
-  float M = st.m;
-#pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    mw[w] = sm.u.x.m[w][lane];
-    M = fmaxf(M, mw[w]);
-  }
-  const float a0 = exp2f(st.m - M);   // wave 0 always has a tile: M is finite
-  float wgt[kWaves - 1];
-  float l = st.l * a0;
-#pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    wgt[w] = exp2f(mw[w] - M);         // 0 for a wave that saw no token
-    l += wgt[w] * sm.u.x.l[w][lane];
-  }
-#pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= a0;
-  // one wave's state at a time keeps the LDS reads in flight bounded
-#pragma unroll 1
-  for (int w = 0; w < kWaves - 1; ++w) {
-#pragma unroll
-    for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.acc[rb][i] = fmaf(wgt[w], sm.u.x.acc[w][4 * rb + i][lane], st.acc[rb][i]);
-  }
+  const float M = st.m;
+  float l = st.l;
 
   // head totals: sum the four lane groups' shares
   l += __shfl_xor(l, 16);
@@ -326,8 +341,8 @@ bool absorbed_mfma_supported(const DecodeParams& p, int dtype) {
 
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {
   const dim3 grid(p.n_split, p.G, p.B);
-  if (p.r == 128) split_absorbed_mfma_kernel<128, ABS_NBUF, ABS_MINW><<<grid, 64 * kWaves, 0, st>>>(p);
-  else if (p.r == 256) split_absorbed_mfma_kernel<256, ABS_NBUF, ABS_MINW><<<grid, 64 * kWaves, 0, st>>>(p);
+  if (p.r == 128) split_absorbed_mfma_kernel<128><<<grid, 64 * kWaves, 0, st>>>(p);
+  else if (p.r == 256) split_absorbed_mfma_kernel<256><<<grid, 64 * kWaves, 0, st>>>(p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

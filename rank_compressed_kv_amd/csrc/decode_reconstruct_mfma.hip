@@ -303,8 +303,8 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
   auto fetch = [&](int tok0, uint4& k, uint4& v) {
     if (mover) {
       const size_t row = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R);
-      k = *reinterpret_cast<const uint4*>(gk + row);
-      v = *reinterpret_cast<const uint4*>(gv + row);
+      k = load_stream16(gk + row);
+      v = load_stream16(gv + row);
     }
   };
   auto put = [&](int buf, const uint4& k, const uint4& v) {
