@@ -187,10 +187,12 @@ def load_traffic(kernel: str):
     try:
         with open(path) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, rec["source"])
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None
+        h = hashlib.sha256()
+        for rel in rec["sources"]:          # the kernel file and the headers it uses
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
         k = rec["kernels"].get(kernel)
         return None if k is None else round(k["bytes"])
     except Exception:

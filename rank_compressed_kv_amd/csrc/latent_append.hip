@@ -41,8 +41,11 @@ __device__ __forceinline__ int col_of_slot(int q) { return q < 16 ? 8 * q : 8 * 
 //           cache-wide L2 write-back is needed;
 //   reader: the last arriver's device-scope acquire fence invalidates its own
 //           caches, after which ordinary 16-byte loads see every partial.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t bits = static_cast<uint64_t>(__float_as_uint(a)) |
+                        (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -110,10 +113,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
     }
     if (fb < nb && fcol < 2 * width) {
       float* dst = p.part + (static_cast<size_t>(slice) * p.B + b0 + fb) * prow + fcol;
-      store_coherent(dst + 0, s.x);
-      store_coherent(dst + 1, s.y);
-      store_coherent(dst + 2, s.z);
-      store_coherent(dst + 3, s.w);
+      store_coherent2(dst, s.x, s.y);
+      store_coherent2(dst + 2, s.z, s.w);
     }
   }
 
