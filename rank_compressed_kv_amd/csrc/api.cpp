@@ -106,7 +106,11 @@ Plan make_plan(const palu_attn_desc* d) {
     const double wg_target = pl.kernel == SplitKernel::kGeneric
                                  ? double(kTargetWorkgroups) / 4.0
                                  : double(kAbsorbedWorkgroups);
-    const double want = double(d->max_ctx) * d->batch * d->n_groups / wg_target;
+    // the reconstruct MFMA kernel launches one workgroup per slice of KV heads
+    const int slices = pl.kernel == SplitKernel::kReconstructMfma
+                           ? sp.s / reconstruct_heads_per_wg(sp.r, sp.s)
+                           : 1;
+    const double want = double(d->max_ctx) * d->batch * d->n_groups * slices / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
     if (st < kSplitQuantum) st = kSplitQuantum;
     if (st > 4096) st = 4096;

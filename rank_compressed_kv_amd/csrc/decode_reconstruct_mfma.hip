@@ -9,31 +9,44 @@
 // CommVQ response (proof of Property 1). Values stay in latent space: the
 // weighted sum runs over h_v rows and B_v is applied in the merge pass.
 //
-// Shape served: head_dim 128, four KV heads per group, at most four query heads
-// per KV head, rank 128 or 256. One workgroup owns one (batch, group, context
-// split) and walks its 16-token tiles; its eight waves are (KV head, half):
-// a wave owns the 16-column blocks {2h, 2h+1, 2h+4, 2h+5} of its head, so the
-// rotary pair (f, f + 64) never leaves a wave, and its slice of B_k^T (r x 64
-// columns, read once from a transposed copy in the workspace) stays in
-// registers for the whole split. Per tile:
+// Shapes served: head_dim 128, at most four query heads per KV head, rank 32,
+// 64, 128, 256 or 512, any number of KV heads per group (the head slice is the
+// largest of 4, 2, 1 heads that divides it and leaves every wave a 16-row block
+// of value latents).
+// A workgroup owns one (batch, group, context split, slice of HW KV heads) and
+// walks its 16-token tiles. A KV head's 128 columns are 8 blocks of 16; the
+// rotary pair (f, f + 64) joins block c with block c + 4. Each wave owns kP
+// such block pairs of one head (2 kP blocks), so rotation never leaves a wave,
+// and its slice of B_k^T (32 kP columns x r, read once from a transposed copy
+// in the workspace) stays in registers for the whole split:
+//   rank <= 256: kP = 2, two waves per head, up to four heads (eight waves),
+//                two heads at rank 64 and one at rank 32;
+//   rank 512:    kP = 1, four waves per head, up to two heads (eight waves).
+// When the slice is smaller than the group, the workgroups of one context
+// split that differ only in their head slice get launch ids 8 apart, which
+// places them on the same XCD at about the same time, so the latent tiles they
+// all read are shared through that XCD's L2 (those loads use ordinary caching;
+// a split read by one workgroup streams with non-temporal loads).
+// Per tile:
 //   keys     K^T[16 cols x 16 tok] = B_k^T[cols x r] * H_k^T[r x tok] per block,
 //            bf16 MFMA 16x16x32, H_k from the tile in LDS. Lane l ends up with
 //            columns 16*cb + 4*(l/16) + i of token l%16.
-//   rotate   in place; cos/sin of t*omega_f advance by one exact complex
-//            product per tile (t grows by 16) and are recomputed from the angle
-//            every kAnchor tiles.
+//   rotate   in place with cos/sin of t*omega_f from a table in LDS that all
+//            waves share; the table advances by one exact complex product per
+//            tile (t grows by 16) and is recomputed from the angle every
+//            kAnchor tiles.
 //   scores   that layout is the A operand of a 16x16x16 MFMA (k = the block's
 //            16 columns): S^T[tok x q heads] = K_rot * Q^T with keys split hi +
-//            lo bf16 (two MFMAs, ~16 bits kept) and exact bf16 q; the two
-//            halves of a head add their partial scores through LDS.
+//            lo bf16 (two MFMAs, ~16 bits kept) and exact bf16 q; the waves of
+//            a head add their partial scores through LDS.
 //   softmax  online, base 2, by the first wave of each head.
 //   values   P and the rescale factors go through LDS; wave w adds
-//            H_v^T[r slice w] * P^T for all query heads of the group (bf16 MFMA
+//            H_v^T[r slice w] * P^T for all query heads of the slice (bf16 MFMA
 //            16x16x16, P split hi + lo), gathering value columns from the tile
 //            in LDS (four-row groups offset by 32 B: conflict-free).
-// Loads: 16-byte pieces of each tile are moved into kStages register stages
-// (kStages tiles in flight) and then into a ring of three LDS tile buffers;
-// rows past the split's end are clamped to its last valid row and masked.
+// Loads: 16-byte pieces of each tile go through two register stages (two tiles
+// in flight) into a ring of three LDS tile buffers; rows past the split's end
+// are clamped to its last valid row and masked.
 #include <math.h>
 
 #include "device_util.h"
@@ -45,13 +58,12 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kHeads = 4;        // KV heads per group
-constexpr int kWaves = 2 * kHeads;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kD = 128;          // head dim
-constexpr int kNB = 3;           // LDS tile buffers
+constexpr int kNBuf = 3;         // LDS tile buffers
 constexpr int kAnchor = 32;      // tiles between exact cos/sin evaluations
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -59,9 +71,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   __builtin_memcpy(&r, &v, sizeof(r));
   return r;
 }
-
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // a ~ hi + lo with hi = bf16(a) and lo = bf16(a - hi) (round to nearest even,
 // one packed conversion per pair): about 16 significant bits in two bf16 terms.
@@ -92,94 +101,148 @@ __device__ __forceinline__ int vtile_off(int row, int cb) {
 template <int R>
 constexpr int kVBytes = kTile * 2 * R + 3 * 32;
 
-template <int R>
+template <int R, int kP, int HW>
+struct Shape {
+  static constexpr int kNB = 2 * kP;             // column blocks per wave
+  static constexpr int kWPH = 4 / kP;            // waves per KV head
+  static constexpr int kWaves = HW * kWPH;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRB = R / (16 * kWaves);  // 16-row value blocks per wave
+  static constexpr int kPieces = (2 * R + kThreads - 1) / kThreads;  // 16-B pieces per matrix
+  static constexpr int kRE = 1024 / kThreads;    // rotation-table entries per thread
+  static_assert(kRB >= 1 && kRB * 16 * kWaves == R, "rank must split evenly over the waves");
+};
+
+template <int R, int kWaves>
 struct Smem {
-  char k[kNB][kTile * kKStride<R>];
-  char v[kNB][kVBytes<R>];
+  char k[kNBuf][kTile * kKStride<R>];
+  char v[kNBuf][kVBytes<R>];
   float4 spart[kWaves][64];   // partial scores of each wave (its lanes' float4)
-  float pt[16][kTile];        // P of the group's query heads for the current tile
+  float pt[16][kTile];        // P of the slice's query heads for the current tile
   float alpha[16];            // rescale factor of each query head for this tile
   // cos, sin of t * omega_f for the 16 tokens t of the current tile, f < 64:
   // rtab[f / 4][t - tok0][f % 4] (a lane's four frequencies are 32 contiguous B)
   float2 rtab[16][kTile][4];
 };
 
-// A tile is 16 rows x R bf16 per matrix = 2R pieces of 16 B; threads below 2R
-// move one piece of H_k and one of H_v. Byte offset of a thread's piece within
-// a row-major tile of 16 rows:
-template <int R>
-__device__ __forceinline__ int piece_row(int tid) { return (tid * 16) / (2 * R); }
-template <int R>
-__device__ __forceinline__ int piece_col(int tid) { return (tid * 16) % (2 * R); }
+// Which (context split, batch, group, head slice) a workgroup owns. With a
+// single head slice, blockIdx is (split, g, b); otherwise the units are
+// numbered u = split + n_split*(g + G*b), padded to a multiple of 8, and the
+// nslice workgroups of unit u get linear ids 8 apart.
+struct Unit {
+  int split, g, b, hs;
+  bool live;
+};
+__device__ __forceinline__ Unit unit_of(const DecodeParams& p, int nslice) {
+  Unit u{};
+  if (nslice == 1) {
+    u.split = blockIdx.x; u.g = blockIdx.y; u.b = blockIdx.z; u.hs = 0; u.live = true;
+    return u;
+  }
+  const int id = blockIdx.x;
+  const int lo = id & 7, hi = id >> 3;
+  u.hs = hi % nslice;
+  const int unit = (hi / nslice) * 8 + lo;
+  u.live = unit < p.n_split * p.G * p.B;
+  u.split = unit % p.n_split;
+  const int rest = unit / p.n_split;
+  u.g = rest % p.G;
+  u.b = rest / p.G;
+  return u;
+}
 
-template <int R>
-__global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(DecodeParams p) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+template <bool kShared>
+__device__ __forceinline__ uint4 load_tile16(const void* ptr) {
+  if constexpr (kShared) return *static_cast<const uint4*>(ptr);
+  else return load_stream16(ptr);
+}
+
+template <int R, int kP, int HW, bool kShared>
+__global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruct_mfma_kernel(
+    DecodeParams p) {
+  using S = Shape<R, kP, HW>;
+  constexpr int kNB = S::kNB, kWPH = S::kWPH, kWaves = S::kWaves, kThreads = S::kThreads;
+  constexpr int kRB = S::kRB, kPieces = S::kPieces, kRE = S::kRE;
+  const int nslice = p.s / HW;
+  const Unit un = unit_of(p, nslice);
+  if (!un.live) return;
+  const int split = un.split, g = un.g, b = un.b, hs = un.hs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, kb = lane >> 4;
-  const int jl = wave >> 1, half = wave & 1;             // KV head in the group, column half
+  const int jl = wave / kWPH, part = wave % kWPH;        // KV head in the slice, column part
   const int n = clamp_len(p.lens, b, p.L);
   const int s0 = split * p.split_tokens;
   if (s0 >= n) return;                                   // whole workgroup
   const int t1 = min(n, s0 + p.split_tokens);
   const int last = t1 - 1;
   const int gqa = p.gqa;                                 // query heads per KV head (<= 4)
-  const int nq = p.nq;                                   // query heads of the group (<= 16)
+  const int nqs = HW * gqa;                              // query heads of the slice (<= 16)
+  const int head0 = g * p.nq + hs * nqs;                 // first query head of the slice
+  const int kvh = hs * HW + jl;                          // KV head within the group
 
-  __shared__ Smem<R> sm;
+  __shared__ Smem<R, kWaves> sm;
 
-  // owned 16-column blocks: cbs(j) = 2*half + j (j < 2) and their +64 partners
-  auto cbs = [half](int j) { return 2 * half + (j & 1) + 4 * (j >> 1); };
+  // owned 16-column blocks: pair i (< kP) joins block part*kP + i and its +4 partner
+  auto cbs = [part](int j) { return part * kP + (j % kP) + 4 * (j / kP); };
 
   // ---- operands held for the whole split -----------------------------------
   // B_k^T as the A operand: lane (ln, kb) of block j, chunk c holds column
   // 16*cbs(j) + ln, latents 32c + 8kb .. +8
   const uint16_t* Bt = static_cast<const uint16_t*>(p.bkt) +
-                       (static_cast<size_t>(g) * p.Dg + jl * kD) * R;
-  uint4 bk[4][R / 32];
+                       (static_cast<size_t>(g) * p.Dg + kvh * kD) * R;
+  uint4 bk[kNB][R / 32];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < kNB; ++j)
 #pragma unroll
     for (int c = 0; c < R / 32; ++c)
       bk[j][c] = *reinterpret_cast<const uint4*>(Bt + static_cast<size_t>(16 * cbs(j) + ln) * R + 32 * c + 8 * kb);
   // q of this KV head's query heads as the score B operand: lane (ln = head
   // slot, kb) of block j holds columns 16*cbs(j) + 4kb .. +4 (exact bf16)
-  short4v qb[4];
+  short4v qb[kNB];
   {
     const bool valid = ln < gqa;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           (static_cast<size_t>(b) * p.Hq + g * nq + jl * gqa + (valid ? ln : 0)) * kD;
+                           (static_cast<size_t>(b) * p.Hq + head0 + jl * gqa + (valid ? ln : 0)) * kD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) qb[j][e] = valid ? static_cast<short>(qrow[16 * cbs(j) + 4 * kb + e]) : 0;
   }
-  // rotation table: thread (gt = tid % 16, fa = tid / 16) keeps cos/sin of
-  // (tok0 + gt) * omega for f = fa and fa + 32 and writes them for each tile;
-  // every kAnchor tiles they are evaluated from the angle, in between they
-  // advance by one exact complex product with the 16-position step.
+
+  // rotation table: thread entry e is (token gt = idx % 16, frequency
+  // f = idx / 16) with idx = tid + e * kThreads; it keeps cos/sin of
+  // (tok0 + gt) * omega_f and writes them for each tile; every kAnchor tiles
+  // they are evaluated from the angle, in between they advance by one exact
+  // complex product with the 16-position step.
   const bool rope = p.rope != 0;
-  const int gt = tid & 15, fa = tid >> 4, fb = fa + 32;
-  float ca = 1.f, sa = 0.f, cb = 1.f, sb = 0.f;
-  float stca = 1.f, stsa = 0.f, stcb = 1.f, stsb = 0.f;
-  if (rope) {
-    rope_cos_sin(p.omega_rev[fa], kTile, stca, stsa);
-    rope_cos_sin(p.omega_rev[fb], kTile, stcb, stsb);
+  float rc[kRE], rs[kRE], stc[kRE], sts[kRE];
+#pragma unroll
+  for (int e = 0; e < kRE; ++e) {
+    rc[e] = 1.f; rs[e] = 0.f; stc[e] = 1.f; sts[e] = 0.f;
+    if (rope) rope_cos_sin(p.omega_rev[(tid + e * kThreads) >> 4], kTile, stc[e], sts[e]);
   }
   auto rope_exact = [&](int tok0) {
     if (rope) {
-      rope_cos_sin(p.omega_rev[fa], tok0 + gt, ca, sa);
-      rope_cos_sin(p.omega_rev[fb], tok0 + gt, cb, sb);
+#pragma unroll
+      for (int e = 0; e < kRE; ++e) {
+        const int idx = tid + e * kThreads;
+        rope_cos_sin(p.omega_rev[idx >> 4], tok0 + (idx & 15), rc[e], rs[e]);
+      }
     }
   };
   auto rope_advance = [&]() {
-    const float c1 = ca * stca - sa * stsa, s1 = sa * stca + ca * stsa;
-    const float c2 = cb * stcb - sb * stsb, s2 = sb * stcb + cb * stsb;
-    ca = c1; sa = s1; cb = c2; sb = s2;
+#pragma unroll
+    for (int e = 0; e < kRE; ++e) {
+      const float c1 = rc[e] * stc[e] - rs[e] * sts[e], s1 = rs[e] * stc[e] + rc[e] * sts[e];
+      rc[e] = c1; rs[e] = s1;
+    }
   };
   auto rope_write = [&]() {
-    sm.rtab[fa >> 2][gt][fa & 3] = float2{ca, sa};
-    sm.rtab[fb >> 2][gt][fb & 3] = float2{cb, sb};
+#pragma unroll
+    for (int e = 0; e < kRE; ++e) {
+      const int idx = tid + e * kThreads, f = idx >> 4;
+      sm.rtab[f >> 2][idx & 15][f & 3] = float2{rc[e], rs[e]};
+    }
   };
   rope_exact(s0);
   rope_write();
@@ -187,9 +250,8 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
 
   // ---- softmax state of the owned query heads (lane ln = head slot) ---------
   float m = -INFINITY, l = 0.f;
-  // value-latent sums for all query heads over this wave's r slice:
-  // acc[rb] holds r = wave*R/8 + 16*rb + 4*kb + i for query head ln
-  constexpr int kRB = R / (16 * kWaves);
+  // value-latent sums for all query heads of the slice over this wave's r
+  // slice: acc[rb] holds r = wave*R/kWaves + 16*rb + 4*kb + i for head slot ln
   floatx4 acc[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -201,37 +263,37 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
 
   auto process = [&](int it) {
     const int tok0 = s0 + it * kTile;
-    const char* kt = sm.k[it % kNB];
-    const char* vt = sm.v[it % kNB];
+    const char* kt = sm.k[it % kNBuf];
+    const char* vt = sm.v[it % kNBuf];
     // keys of the owned blocks: K^T[16*cbs(j) + 4kb + i][token ln]
-    floatx4 kk[4];
+    floatx4 kk[kNB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kk[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kNB; ++j) kk[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < R / 32; ++c) {
       const bf16x8 h = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kNB; ++j)
         kk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bk[j][c]), h, kk[j], 0, 0, 0);
     }
-    // rotate the pairs (f, f + 64): f = 16*cbs(j) + 4kb + i, token ln
+    // rotate the pairs (f, f + 64): f = 16*cbs(i) + 4kb + e, token ln
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[4 * cbs(j) + kb][ln][0]);
+    for (int i = 0; i < kP; ++i) {
+      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[4 * cbs(i) + kb][ln][0]);
       const float4 r01 = rt[0];
       const float4 r23 = rt[1];
       const float c4[4] = {r01.x, r01.z, r23.x, r23.z}, s4[4] = {r01.y, r01.w, r23.y, r23.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = kk[j][i], y = kk[j + 2][i];
-        kk[j][i] = x * c4[i] - y * s4[i];
-        kk[j + 2][i] = x * s4[i] + y * c4[i];
+      for (int e = 0; e < 4; ++e) {
+        const float x = kk[i][e], y = kk[i + kP][e];
+        kk[i][e] = x * c4[e] - y * s4[e];
+        kk[i + kP][e] = x * s4[e] + y * c4[e];
       }
     }
     // partial scores S^T[token 4kb+i][head slot ln] over the owned blocks
     floatx4 sc = {0.f, 0.f, 0.f, 0.f}, sc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kNB; ++j) {
       short4v ah, al;
       split_bf16x4(kk[j], ah, al);
       sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], sc, 0, 0, 0);
@@ -247,9 +309,12 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
       rope_write();
     }
     // softmax of the owned heads by the first wave of each KV head
-    if (half == 0) {
-      const float4 o = sm.spart[wave + 1][lane];
-      sc[0] += o.x; sc[1] += o.y; sc[2] += o.z; sc[3] += o.w;
+    if (part == 0) {
+#pragma unroll
+      for (int w = 1; w < kWPH; ++w) {
+        const float4 o = sm.spart[wave + w][lane];
+        sc[0] += o.x; sc[1] += o.y; sc[2] += o.z; sc[3] += o.w;
+      }
       sc *= p.scale_log2;
       if (tok0 + kTile > t1) {                           // last tile of the split
 #pragma unroll
@@ -267,15 +332,15 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
       for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - mn);
       l = l * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
       if (ln < gqa) {
-        const int hg = jl * gqa + ln;                    // query head within the group
+        const int hg = jl * gqa + ln;                    // query head within the slice
         *reinterpret_cast<float4*>(&sm.pt[hg][4 * kb]) = float4{pv[0], pv[1], pv[2], pv[3]};
         if (kb == 0) sm.alpha[hg] = alpha;
       }
     }
     __syncthreads();
-    // values: this wave's r slice for all query heads of the group
+    // values: this wave's r slice for all query heads of the slice
     {
-      const bool hv = ln < nq;
+      const bool hv = ln < nqs;
       const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
       const float al = hv ? sm.alpha[ln] : 1.f;
       short4v ph, pl;
@@ -293,27 +358,39 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
     }
   };
 
-  // Loads: each thread below 2R moves one 16-byte piece of H_k and of H_v per
-  // tile; two tiles wait in registers (stages a and b) while one is in LDS.
-  const bool mover = tid < 2 * R;
-  const int prow = piece_row<R>(tid), pcol = piece_col<R>(tid);
-  const char* gk = reinterpret_cast<const char*>(Hk) + pcol;
-  const char* gv = reinterpret_cast<const char*>(Hv) + pcol;
-  const int ko = prow * kKStride<R> + pcol, vo = vtile_off<R>(prow, pcol);
-  auto fetch = [&](int tok0, uint4& k, uint4& v) {
-    if (mover) {
-      const size_t row = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R);
-      k = load_stream16(gk + row);
-      v = load_stream16(gv + row);
+  // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
+  // the tile (byte 16*that in a row-major tile of 16 rows), if below 2R; two
+  // tiles wait in registers (stages a and b, vector types so they stay in
+  // registers) while one is in LDS.
+  typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
+  auto fetch = [&](int tok0, u32v& k, u32v& v) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int pc = tid + i * kThreads;
+      if (pc < 2 * R) {
+        const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
+        const size_t row = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R) + pcol;
+        const uint4 a = load_tile16<kShared>(reinterpret_cast<const char*>(Hk) + row);
+        const uint4 c = load_tile16<kShared>(reinterpret_cast<const char*>(Hv) + row);
+        k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
+        v[4 * i] = c.x; v[4 * i + 1] = c.y; v[4 * i + 2] = c.z; v[4 * i + 3] = c.w;
+      }
     }
   };
-  auto put = [&](int buf, const uint4& k, const uint4& v) {
-    if (mover) {
-      *reinterpret_cast<uint4*>(sm.k[buf] + ko) = k;
-      *reinterpret_cast<uint4*>(sm.v[buf] + vo) = v;
+  auto put = [&](int buf, const u32v& k, const u32v& v) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int pc = tid + i * kThreads;
+      if (pc < 2 * R) {
+        const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
+        *reinterpret_cast<uint4*>(sm.k[buf] + prow * kKStride<R> + pcol) =
+            uint4{k[4 * i], k[4 * i + 1], k[4 * i + 2], k[4 * i + 3]};
+        *reinterpret_cast<uint4*>(sm.v[buf] + vtile_off<R>(prow, pcol)) =
+            uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      }
     }
   };
-  uint4 ka, va, kb2, vb2;
+  u32v ka, va, kb2, vb2;
   fetch(s0, ka, va);
   put(0, ka, va);
   fetch(s0 + kTile, ka, va);
@@ -321,12 +398,12 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
   for (int it = 0; it < ntiles; it += 2) {
     // stage a holds tile it+1: to LDS (its buffer held tile it-2, finished by
     // everyone), then fetch tile it+3 into it
-    put((it + 1) % kNB, ka, va);
+    put((it + 1) % kNBuf, ka, va);
     fetch(s0 + (it + 3) * kTile, ka, va);
     __syncthreads();
     process(it);
     if (it + 1 < ntiles) {
-      put((it + 2) % kNB, kb2, vb2);
+      put((it + 2) % kNBuf, kb2, vb2);
       fetch(s0 + (it + 4) * kTile, kb2, vb2);
       __syncthreads();
       process(it + 1);
@@ -336,14 +413,14 @@ __global__ __launch_bounds__(kThreads) void split_reconstruct_mfma_kernel(Decode
   // ---- partials: this wave's r slice for every query head; (m, l) by owners
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (half == 0 && ln < gqa && kb == 0) {
-    const int head = g * nq + jl * gqa + ln;
+  if (part == 0 && ln < gqa && kb == 0) {
+    const int head = head0 + jl * gqa + ln;
     const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
     p.part_ml[slot * 2] = m;
     p.part_ml[slot * 2 + 1] = l;
   }
-  if (ln < nq) {
-    const int head = g * nq + ln;
+  if (ln < nqs) {
+    const int head = head0 + ln;
     const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
     float* u = p.part_u + slot * R + wave * (R / kWaves);
 #pragma unroll
@@ -372,10 +449,35 @@ __global__ __launch_bounds__(256) void transpose_bk_kernel(DecodeParams p) {
   }
 }
 
+template <int R, int kP, int HW>
+hipError_t launch_shape(const DecodeParams& p, hipStream_t st) {
+  using S = Shape<R, kP, HW>;
+  const int nslice = p.s / HW;
+  if (nslice == 1) {
+    const dim3 grid(p.n_split, p.G, p.B);
+    split_reconstruct_mfma_kernel<R, kP, HW, false><<<grid, S::kThreads, 0, st>>>(p);
+  } else {
+    const long units = static_cast<long>(p.n_split) * p.G * p.B;
+    const long ids = (units + 7) / 8 * 8 * nslice;
+    if (ids > 0x7fffffffL) return hipErrorInvalidValue;
+    split_reconstruct_mfma_kernel<R, kP, HW, true>
+        <<<dim3(static_cast<unsigned>(ids)), S::kThreads, 0, st>>>(p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
+int reconstruct_heads_per_wg(int r, int s) {
+  // every wave needs at least one 16-row block of value latents: r >= 16 * waves
+  if (r == 512 || r == 64) return s % 2 == 0 ? 2 : 1;
+  if (r == 128 || r == 256) return s % 4 == 0 ? 4 : (s % 2 == 0 ? 2 : 1);
+  if (r == 32) return 1;
+  return 0;
+}
+
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && p.d == kD && p.s == kHeads && p.gqa <= 4 && (p.r == 128 || p.r == 256);
+  return dtype == 1 && p.d == kD && p.gqa <= 4 && reconstruct_heads_per_wg(p.r, p.s) > 0;
 }
 
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st) {
@@ -386,11 +488,20 @@ hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st)
 }
 
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st) {
-  const dim3 grid(p.n_split, p.G, p.B);
-  if (p.r == 128) split_reconstruct_mfma_kernel<128><<<grid, kThreads, 0, st>>>(p);
-  else if (p.r == 256) split_reconstruct_mfma_kernel<256><<<grid, kThreads, 0, st>>>(p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  switch (p.r * 8 + reconstruct_heads_per_wg(p.r, p.s)) {
+    case 128 * 8 + 4: return launch_shape<128, 2, 4>(p, st);
+    case 128 * 8 + 2: return launch_shape<128, 2, 2>(p, st);
+    case 128 * 8 + 1: return launch_shape<128, 2, 1>(p, st);
+    case 256 * 8 + 4: return launch_shape<256, 2, 4>(p, st);
+    case 256 * 8 + 2: return launch_shape<256, 2, 2>(p, st);
+    case 256 * 8 + 1: return launch_shape<256, 2, 1>(p, st);
+    case 512 * 8 + 2: return launch_shape<512, 1, 2>(p, st);
+    case 512 * 8 + 1: return launch_shape<512, 1, 1>(p, st);
+    case 64 * 8 + 2: return launch_shape<64, 2, 2>(p, st);
+    case 64 * 8 + 1: return launch_shape<64, 2, 1>(p, st);
+    case 32 * 8 + 1: return launch_shape<32, 2, 1>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace palu

@@ -49,8 +49,8 @@ struct AppendParams {
 enum class SplitKernel {
   kGeneric = 0,        // VALU, any dtype/shape in range
   kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {128, 256}, <= 16 q heads per group
-  kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, 4 KV heads per group,
-                         // <= 4 q heads per KV head, r in {128, 256}
+  kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
+                         // head, r in {128, 256, 512}
 };
 
 const char* split_kernel_name(SplitKernel k);
@@ -61,6 +61,7 @@ hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, 
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);
+int reconstruct_heads_per_wg(int r, int s);   // KV heads per workgroup (0: not served)
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);

@@ -86,6 +86,26 @@ def test_length_edges_and_poisoned_tail(idx, mode):
         assert_close(got, want, what=f"edges cfg{idx}/{mode}/split{st}", **_tol(cfg))
 
 
+# (KV heads per group s, rank r): the granularities at 75% key compression
+# (M-LRD s=1 r=32 ... J-LRD s=8 r=256) and rank 512 with 2, 4 and 8 heads
+GROUPINGS = [(1, 32), (2, 64), (4, 128), (8, 256), (1, 128), (2, 256), (2, 512), (4, 512),
+             (8, 512)]
+
+
+@pytest.mark.parametrize("s,r", GROUPINGS)
+def test_reconstruct_head_groupings(s, r):
+    """Rebuilt and rotated keys for every head grouping the MFMA kernel serves:
+    one, two or four KV heads per workgroup, and groups whose heads are spread
+    over several workgroups of the same context split."""
+    cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r, batch=2, max_ctx=700, seed=40 + s)
+    t = W.generate(cfg)
+    print(f"[grouping] s={s} r={r}", flush=True)
+    for st in (0, 128):
+        got, theta = run_decode(cfg, t, "reconstruct", split_tokens=st)
+        assert theta > 0
+        assert_close(got, _oracle(cfg, t, theta), what=f"s={s} r={r} split={st}")
+
+
 @pytest.mark.parametrize("mode", ["absorbed", "reconstruct"])
 def test_more_than_64_splits(mode):
     """79 splits of 64 tokens: the merge that stages split states through LDS
