@@ -174,3 +174,32 @@ def decode_attention(q: np.ndarray, h_k: np.ndarray, h_v: np.ndarray, b_k: np.nd
                 Vj = Vg[:, jl * d:(jl + 1) * d]
                 out[b, h] = attend(to_f64(q[b, h]), Kj, Vj, scale)
     return out
+
+
+def full_rank_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, lens: np.ndarray, *,
+                        scale: Optional[float] = None,
+                        select: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """The uncompressed baseline the pages measure against ("Why Palu Requires
+    Fewer Global Memory Access": the baseline reads the full key K_i and forms
+    q_i K_i^T): ordinary decode attention over full keys and values.
+
+    q [B, Hq, d]; k, v [B, Hkv, L_cap, d] (keys already position-encoded);
+    lens [B]. Query head h reads KV head h // (Hq / Hkv). Returns fp64
+    [B, Hq, d]; with select only those (b, h) rows are computed (rest NaN).
+    """
+    Bsz, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    gqa = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    out = np.full((Bsz, Hq, d), np.nan)
+    wanted = None if select is None else {(int(b), int(h)) for b, h in select}
+    for b in range(Bsz):
+        n = int(lens[b])
+        for h in range(Hq):
+            if wanted is not None and (b, h) not in wanted:
+                continue
+            j = h // gqa
+            out[b, h] = attend(to_f64(q[b, h]), to_f64(k[b, j, :n]), to_f64(v[b, j, :n]), scale)
+    return out

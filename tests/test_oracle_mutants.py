@@ -26,6 +26,11 @@ MUTANTS = {
                              "Kj = apply_rope(Kg[:, jl::s]"),
     "value_uses_keys": ("decode_attention", "Vj = Vg[:, jl * d:(jl + 1) * d]",
                         "Vj = Kg[:, jl * d:(jl + 1) * d]"),
+    "full_rank_gqa_modulo": ("full_rank_attention", "j = h // gqa", "j = h % Hkv"),
+    "full_rank_value_uses_keys": ("full_rank_attention", "to_f64(k[b, j, :n]), to_f64(v[b, j, :n])",
+                                  "to_f64(k[b, j, :n]), to_f64(k[b, j, :n])"),
+    "full_rank_len_off_by_one": ("full_rank_attention", "n = int(lens[b])",
+                                 "n = max(0, int(lens[b]) - 1)"),
     "softmax_unnormalised": ("softmax", "return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "reconstruct_transposed": ("reconstruct", "return to_f64(h) @ to_f64(b)",
                                "return to_f64(h) @ to_f64(b)[::-1]"),

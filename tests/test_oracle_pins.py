@@ -172,6 +172,41 @@ def test_identity_factors_reduce_to_sdpa(Hq, Hkv, d, L):
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,L", [(8, 8, 16, 33), (8, 2, 16, 40), (12, 3, 8, 17)])
+def test_full_rank_baseline_is_sdpa(Hq, Hkv, d, L):
+    """The uncompressed baseline is ordinary GQA decode attention: torch's fp64
+    scaled_dot_product_attention over the first len rows is the reference."""
+    rng = np.random.default_rng(Hq * 7 + L)
+    q = rng.standard_normal((2, Hq, d))
+    k = rng.standard_normal((2, Hkv, L, d))
+    v = rng.standard_normal((2, Hkv, L, d))
+    lens = np.array([L, L // 2])
+    got = O.full_rank_attention(q, k, v, lens)
+    for b in range(2):
+        n = int(lens[b])
+        Q = torch.from_numpy(q[b:b + 1])[:, :, None, :]
+        K = torch.from_numpy(k[b:b + 1, :, :n]).repeat_interleave(Hq // Hkv, dim=1)
+        V = torch.from_numpy(v[b:b + 1, :, :n]).repeat_interleave(Hq // Hkv, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V)[0, :, 0, :].numpy()
+        np.testing.assert_allclose(got[b], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_full_rank_baseline_edges():
+    """Length 0 gives zeros, length 1 returns that token's value row, and the
+    latent path with identity factors (r = d, one group per KV head) agrees."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 4, 8))
+    k = rng.standard_normal((3, 2, 6, 8))
+    v = rng.standard_normal((3, 2, 6, 8))
+    lens = np.array([0, 1, 6])
+    got = O.full_rank_attention(q, k, v, lens)
+    assert np.all(got[0] == 0.0)
+    np.testing.assert_allclose(got[1], v[1, [0, 0, 1, 1], 0, :], rtol=0, atol=1e-15)
+    eye = np.broadcast_to(np.eye(8), (2, 8, 8)).copy()
+    np.testing.assert_allclose(got, O.decode_attention(q, k, v, eye, eye, lens), rtol=1e-12,
+                               atol=1e-13)
+
+
 def test_reconstructed_keys_have_rank_r():
     """K_g = H B is at most rank r (the cache stores r numbers per token and group)."""
     rng = np.random.default_rng(3)
