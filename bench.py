@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the second timed loop with events around the main kernel")
+    ap.add_argument("--no-full-rank", action="store_true",
+                    help="skip the uncompressed baseline (full bf16 K and V)")
     return ap.parse_args()
 
 
@@ -110,6 +112,15 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     e1.record(stream)
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
+    # timed loop 1b: the decode call alone (no cache write), the quantity the
+    # pages compare with the uncompressed baseline
+    e0.record(stream)
+    for i in range(args.steps):
+        hk, hv = caches[i % n_copies]
+        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = e0.elapsed_time(e1)
     # timed loop 2: the same steps with HIP events recorded by the library
     # around the main kernel on its launch stream (the roofline figure); the
     # event packets add a few microseconds between kernels, so this loop does
@@ -122,9 +133,55 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
         torch.cuda.synchronize()
         kern_ms, kern_n = P.palu_profile_end()
     return dict(ms_per_step=total_ms / args.steps, kernel_ms=kern_ms / max(1, kern_n),
+                decode_ms=decode_ms / args.steps,
                 kernel=kname, n_split=n_split, split_tokens=split_tokens,
                 out=first_out.cpu().numpy(), hk_row=first_hk, hv_row=first_hv, pos=pos,
                 caches=caches)
+
+
+def time_full_rank(torch, P, W, cfg, t, args):
+    """The uncompressed baseline at the same shape: full bf16 K and V
+    [B, Hkv, L, d], keys cached rotated, one decode call per step."""
+    tf = W.generate(cfg, parts=("full",))
+    q, lens = dev(torch, t["q"]), dev(torch, t["lens"])
+    k0, v0 = dev(torch, tf["k_full"]), dev(torch, tf["v_full"])
+    kv_bytes = 2 * k0.numel() * k0.element_size()
+    n_copies = max(1, int(math.ceil(ROTATE_BYTES / kv_bytes)))
+    caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_copies - 1)]
+    desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, n_groups=cfg.n_kv_heads, rank=cfg.head_dim,
+                       max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, mode="full_rank",
+                       split_tokens=0)
+    ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        k, v = caches[i % n_copies]
+        P.palu_decode_attn(desc, q, k, v, None, None, lens, out, ws, stream)
+
+    call(0)
+    torch.cuda.synchronize()
+    first = out.clone()
+    for i in range(args.warmup):
+        call(i + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    P.palu_profile_begin(args.steps)
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    kern_ms, kern_n = P.palu_profile_end()
+    bytes_ = 2 * int(np.sum(t["lens"], dtype=np.int64)) * cfg.n_kv_heads * cfg.head_dim * 2
+    del caches
+    return dict(ms=ms, kernel_ms=kern_ms / max(1, kern_n), bytes=bytes_, out=first.cpu().numpy(),
+                k=tf["k_full"], v=tf["v_full"])
 
 
 def sampled_parity(O, cfg, t, res, mode, pairs):
@@ -249,6 +306,22 @@ def main():
     main_res = results[args.mode]
     for r in results.values():
         r.pop("caches")
+    full = None
+    if not args.no_full_rank and cfg.dtype == "bf16":
+        fr = time_full_rank(torch, P, W, cfg, t, args)
+        want = O.full_rank_attention(t["q"], fr["k"], fr["v"], t["lens"], select=pairs)
+        idx = tuple(np.array(pairs).T)
+        dd = fr["out"].astype(np.float64)[idx] - want[idx]
+        dec_ms = results["absorbed"]["decode_ms"] if "absorbed" in results else None
+        full = {"us_per_call": round(fr["ms"] * 1e3, 2),
+                "kernel_us": _r(fr["kernel_ms"] * 1e3, 2),
+                "kv_bytes": fr["bytes"],
+                "GBps_kernel": _r(fr["bytes"] / (fr["kernel_ms"] * 1e-3) / 1e9, 1),
+                "sampled_parity_max_abs": float(np.abs(dd).max()),
+                "palu_absorbed_speedup_decode_call": (round(fr["ms"] / dec_ms, 3)
+                                                      if dec_ms else None)}
+        print(f"[bench] full-rank baseline: {fr['ms'] * 1e3:.1f} us/call, kernel "
+              f"{fr['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     ms = main_res["ms_per_step"]
     steps_s = 1e3 / ms
@@ -281,7 +354,9 @@ def main():
                      "traffic": traffic, "kernel": main_res["kernel"],
                      "kernel_us": _r(main_res["kernel_ms"] * 1e3, 2),
                      "algorithmic_bytes": lat_bytes},
+        "full_rank_baseline": full,
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                      "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
                       "kernel_us": _r(r["kernel_ms"] * 1e3, 2), "kernel": r["kernel"],
                       "latent_GBps_kernel": _r(lat_bytes / (r["kernel_ms"] * 1e-3) / 1e9, 1),
                       "sampled_parity_max_abs": parity[m][0],

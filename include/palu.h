@@ -60,7 +60,13 @@ typedef enum palu_mode {
   /* rebuild K = H_k B_k per tile on chip, rotate, score against q */
   PALU_MODE_RECONSTRUCT = 0,
   /* no rotary embedding: score q~ = q B_k^T against H_k directly */
-  PALU_MODE_ABSORBED = 1
+  PALU_MODE_ABSORBED = 1,
+  /* the uncompressed baseline every speedup of the method is measured
+   * against ("Why Palu Requires Fewer Global Memory Access": the full K_i is
+   * read): h_k, h_v hold the full keys and values, one "group" per KV head,
+   * rank = head_dim, no B matrices (b_k, b_v are ignored and may be NULL);
+   * keys are cached already rotated, so rope_theta must be 0 */
+  PALU_MODE_FULL_RANK = 2
 } palu_mode;
 
 /* Shapes: B = batch, Hq = query heads, Hkv = KV heads, d = head dim,
@@ -103,9 +109,13 @@ palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
  *   out      [B, Hq, d] fp32; a sequence of length 0 gives zeros
  *   workspace, workspace_bytes: device scratch of at least the size reported by
  *            palu_decode_attn_workspace; its contents are overwritten.
- * Errors: NULL for a missing pointer (only seq_lens may be NULL), SHAPE,
- * UNSUPPORTED (ABSORBED with rope_theta != 0, unknown dtype/mode, rope_theta < 0),
- * WORKSPACE, DEVICE (launch failure). */
+ * FULL_RANK mode: out[b, h, :] = sum_t softmax_t(scale * <q[b,h], h_k[b,j,t]>)
+ * h_v[b,j,t] with j = h / (Hq / Hkv); needs n_groups == n_kv_heads and
+ * rank == head_dim; b_k and b_v are not read.
+ * Errors: NULL for a missing pointer (only seq_lens may be NULL, and b_k, b_v
+ * in FULL_RANK mode), SHAPE (also FULL_RANK with n_groups != n_kv_heads or
+ * rank != head_dim), UNSUPPORTED (ABSORBED or FULL_RANK with rope_theta != 0,
+ * unknown dtype/mode, rope_theta < 0), WORKSPACE, DEVICE (launch failure). */
 palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,
                              const void* h_v, const void* b_k, const void* b_v,
                              const int32_t* seq_lens, float* out, void* workspace,

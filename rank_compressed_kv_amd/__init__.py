@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
-           "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "library", "library_path",
+           "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
+           "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
            "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
            "palu_profile_end", "attn_desc", "append_desc", "decode_attention", "latent_append",
@@ -29,7 +30,7 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
 PALU_OK, PALU_ERR_NULL, PALU_ERR_SHAPE, PALU_ERR_UNSUPPORTED, PALU_ERR_WORKSPACE, \
     PALU_ERR_DEVICE = range(6)
 PALU_F32, PALU_BF16 = 0, 1
-PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED = 0, 1
+PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
                     "palu_latent_append_workspace", "palu_latent_append",
@@ -166,8 +167,11 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
     _need(q, "q", (B, Hq, d), dt)
     _need(h_k, "h_k", (B, G, L, r), dt)
     _need(h_v, "h_v", (B, G, L, r), dt)
-    _need(b_k, "b_k", (G, r, dg), dt)
-    _need(b_v, "b_v", (G, r, dg), dt)
+    full = desc.mode == PALU_MODE_FULL_RANK
+    if not full or b_k is not None:
+        _need(b_k, "b_k", (G, r, dg), dt)
+    if not full or b_v is not None:
+        _need(b_v, "b_v", (G, r, dg), dt)
     _need(out, "out", (B, Hq, d), torch.float32)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", (B,), torch.int32)
@@ -175,8 +179,9 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
     _check(library().palu_decode_attn(
-        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), b_k.data_ptr(),
-        b_v.data_ptr(), None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(),
+        None if b_k is None else b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
+        None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
 
 
@@ -224,7 +229,8 @@ def palu_profile_end() -> Tuple[float, int]:
 def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_groups: int,
               rank: int, max_ctx: int, dtype: int, mode: str = "reconstruct",
               rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0) -> AttnDesc:
-    modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED}
+    modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED,
+             "full_rank": PALU_MODE_FULL_RANK}
     if mode not in modes:
         raise ValueError(f"mode must be one of {sorted(modes)}")
     return AttnDesc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
@@ -254,6 +260,24 @@ def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
         workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
                                 device=q.device)
     palu_decode_attn(desc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace, stream)
+    return out
+
+
+def full_rank_attention(q, k, v, seq_lens=None, *, scale: float = 0.0, split_tokens: int = 0,
+                        out=None, workspace=None, stream=None):
+    """The uncompressed baseline: k, v [B, Hkv, L, d] hold the full (already
+    rotated) keys and values. Allocates out and the workspace when not given."""
+    B, Hq, d = q.shape
+    _, Hkv, L, dk = k.shape
+    desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_groups=Hkv,
+                     rank=dk, max_ctx=L, dtype=_dt(q), mode="full_rank", scale=scale,
+                     split_tokens=split_tokens)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
+                                device=q.device)
+    palu_decode_attn(desc, q, k, v, None, None, seq_lens, out, workspace, stream)
     return out
 
 

@@ -120,6 +120,15 @@ __global__ __launch_bounds__(kThreads) void absorb_q_vec_kernel(DecodeParams p) 
   }
 }
 
+// q~ = q (the uncompressed baseline: keys are the cached rows themselves),
+// pre-multiplied by scale * log2(e) like the absorbed queries
+template <typename T>
+__global__ __launch_bounds__(kThreads) void prescale_q_kernel(DecodeParams p) {
+  const size_t n = static_cast<size_t>(p.B) * p.Hq * p.d;
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) p.qt[i] = load_f32(static_cast<const T*>(p.q), i) * p.scale_log2;
+}
+
 constexpr int kBvRows = 16;        // B_v rows per thread kept in flight
 constexpr int kSplitBatch = 16;    // split partials per thread kept in flight
 constexpr int kSplitLDS = 1024;    // split weights staged in LDS per chunk
@@ -148,7 +157,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
   const float* ml = p.part_ml + base * 2;
   const float* pu = p.part_u + base * p.r;
-  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
+  const bool full = p.full_rank != 0;                  // no B_v: out = u*
+  const T* Bv = full ? nullptr
+                     : static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
 
   __shared__ float wred[kWarps];
   __shared__ float wts[kSplitLDS];
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kBvRows; ++i) {
       const int k = rg + i * ngroups;
-      if (rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
+      if (!full && rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
       else
 #pragma unroll
         for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
@@ -251,6 +262,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
+  if (full) {                                          // r == d
+    for (int c = tid; c < p.d; c += kThreads) out[c] = us[c];
+    return;
+  }
 
   // ---- 4. out = u* B_v[:, cols(j)]
   if (vec) {
@@ -325,7 +340,9 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
   const float* ml = p.part_ml + base * 2;
   const float* pu = p.part_u + base * p.r;
-  const T* Bv = static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
+  const bool full = p.full_rank != 0;                  // no B_v: out = u*
+  const T* Bv = full ? nullptr
+                     : static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
   const int ncc = p.d / 8, ngroups = kThreads / ncc;
   const int cc = tid % ncc, rg = tid / ncc;
   const int nrow = (p.r + ngroups - 1) / ngroups;      // B_v rows of this thread
@@ -359,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   const float ms_raw = lane < p.n_split ? ml[2 * lane] : 0.f;
   const float ls_raw = lane < p.n_split ? ml[2 * lane + 1] : 0.f;
   load_u(0);
-  load_bv(0);
+  if (!full) load_bv(0);
   const int ns = (n + p.split_tokens - 1) / p.split_tokens;
   float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
   if (ns == 0) {
@@ -388,6 +405,11 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   __shared__ float us[2 * kThreads];
   __shared__ float red[2048];
   const float inv = 1.f / L;
+  if (full) {                                          // r == d
+    if (tid < p.r) out[tid] = u0 * inv;
+    if (tid + kThreads < p.r) out[tid + kThreads] = u1 * inv;
+    return;
+  }
   if (tid < p.r) us[tid] = u0 * inv;
   if (tid + kThreads < p.r) us[tid + kThreads] = u1 * inv;
   __syncthreads();
@@ -434,6 +456,14 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
     if (v8) absorb_q_kernel<uint16_t, true><<<grid, kThreads, 0, st>>>(p);
     else absorb_q_kernel<uint16_t, false><<<grid, kThreads, 0, st>>>(p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st) {
+  const size_t n = static_cast<size_t>(p.B) * p.Hq * p.d;
+  const dim3 grid(static_cast<unsigned>((n + kThreads - 1) / kThreads));
+  if (dtype == 0) prescale_q_kernel<float><<<grid, kThreads, 0, st>>>(p);
+  else prescale_q_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -62,13 +62,20 @@ palu_status validate_attn(const palu_attn_desc* d) {
                 d->split_tokens, kSplitQuantum);
   if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
     return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
-  if (d->mode != PALU_MODE_RECONSTRUCT && d->mode != PALU_MODE_ABSORBED)
+  if (d->mode != PALU_MODE_RECONSTRUCT && d->mode != PALU_MODE_ABSORBED &&
+      d->mode != PALU_MODE_FULL_RANK)
     return fail(PALU_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
   if (!(d->rope_theta >= 0.0) || std::isinf(d->rope_theta))
     return fail(PALU_ERR_UNSUPPORTED, "rope_theta must be finite and >= 0");
   if (d->mode == PALU_MODE_ABSORBED && d->rope_theta != 0.0)
     return fail(PALU_ERR_UNSUPPORTED,
                 "ABSORBED mode needs rope_theta == 0: a rotated key cannot absorb B_k into q");
+  if (d->mode == PALU_MODE_FULL_RANK) {
+    if (d->rope_theta != 0.0)
+      return fail(PALU_ERR_UNSUPPORTED, "FULL_RANK mode needs rope_theta == 0 (keys cached rotated)");
+    if (d->n_groups != d->n_kv_heads || d->rank != d->head_dim)
+      return fail(PALU_ERR_SHAPE, "FULL_RANK mode needs n_groups == n_kv_heads and rank == head_dim");
+  }
   const double rows = double(d->batch) * d->n_groups * d->max_ctx;
   if (rows * d->rank > 9.0e15) return fail(PALU_ERR_SHAPE, "cache too large");
   return PALU_OK;
@@ -93,7 +100,7 @@ Plan make_plan(const palu_attn_desc* d) {
   Plan pl{};
   const DecodeParams sp = shape_params(d);
   pl.kernel = SplitKernel::kGeneric;
-  if (d->mode == PALU_MODE_ABSORBED && absorbed_mfma_supported(sp, d->dtype))
+  if (d->mode != PALU_MODE_RECONSTRUCT && absorbed_mfma_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kAbsorbedMfma;
   if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_mfma_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kReconstructMfma;
@@ -131,7 +138,7 @@ WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   const size_t heads = size_t(d->batch) * d->n_q_heads;
   const size_t elem = d->dtype == PALU_BF16 ? 2 : 4;
   w.qt = 0;
-  const size_t qt_bytes = d->mode == PALU_MODE_ABSORBED ? align256(heads * d->rank * 4) : 0;
+  const size_t qt_bytes = d->mode != PALU_MODE_RECONSTRUCT ? align256(heads * d->rank * 4) : 0;
   w.ml = w.qt + qt_bytes;
   w.u = w.ml + align256(heads * pl.n_split * 2 * 4);
   w.bkt = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
@@ -204,8 +211,10 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              size_t workspace_bytes, void* stream) {
   palu_status st = validate_attn(desc);
   if (st != PALU_OK) return st;
-  if (!q || !h_k || !h_v || !b_k || !b_v || !out || !workspace)
-    return fail(PALU_ERR_NULL, "q, h_k, h_v, b_k, b_v, out and workspace must be non-NULL");
+  const bool full = desc->mode == PALU_MODE_FULL_RANK;
+  if (!q || !h_k || !h_v || (!full && (!b_k || !b_v)) || !out || !workspace)
+    return fail(PALU_ERR_NULL, full ? "q, h_k, h_v, out and workspace must be non-NULL"
+                                    : "q, h_k, h_v, b_k, b_v, out and workspace must be non-NULL");
   const Plan pl = make_plan(desc);
   const WorkspaceLayout wl = layout(desc, pl);
   if (workspace_bytes < wl.total)
@@ -223,13 +232,15 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
   p.scale_log2 = float(scale * 1.4426950408889634);
   p.rope = desc->rope_theta > 0.0 ? 1 : 0;
+  p.full_rank = full ? 1 : 0;
   for (int i = 0; i < p.d / 2; ++i)
     p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int absorbed = desc->mode == PALU_MODE_ABSORBED;
+  const int absorbed = desc->mode != PALU_MODE_RECONSTRUCT;   // scores against q~
   hipError_t e = hipSuccess;
-  if (absorbed) e = launch_absorb_q(p, desc->dtype, s);
+  if (full) e = launch_prescale_q(p, desc->dtype, s);
+  else if (absorbed) e = launch_absorb_q(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
   if (pl.kernel == SplitKernel::kReconstructMfma) e = launch_transpose_bk(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));

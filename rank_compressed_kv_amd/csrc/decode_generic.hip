@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kThreads) void split_generic_kernel(DecodeParams p)
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
   const T* Hk = static_cast<const T*>(p.h_k) + row0 * r;
   const T* Hv = static_cast<const T*>(p.h_v) + row0 * r;
-  const T* Bk = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * r * p.Dg + jl * d;
+  const T* Bk = kAbsorbed ? nullptr
+                          : static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * r * p.Dg + jl * d;
 
   float m = -INFINITY, l = 0.f;
   float u[kMaxRankPerThread];

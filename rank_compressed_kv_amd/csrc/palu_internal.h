@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t s, gqa, nq, Dg;      // heads per group, q heads per kv head, q heads per group
   int32_t n_split, split_tokens;
   int32_t rope;                // 1 if rotary embedding is applied
+  int32_t full_rank;           // 1: h_k, h_v are full K, V; no B_k, B_v
   float scale_log2;            // softmax scale * log2(e)
   // omega_i / (2 pi) in fp64 for i < d/2: the pair turns by t * omega_rev[i]
   // revolutions at position t
@@ -57,6 +58,7 @@ const char* split_kernel_name(SplitKernel k);
 
 // Launchers return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
+hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);

@@ -55,7 +55,28 @@ BAD = [
     (dict(rope_theta=5e5), P.PALU_ERR_UNSUPPORTED),          # absorbed + RoPE
     (dict(mode="reconstruct", rope_theta=-1.0), P.PALU_ERR_UNSUPPORTED),
     (dict(mode="reconstruct", rope_theta=float("nan")), P.PALU_ERR_UNSUPPORTED),
+    # the uncompressed baseline: one group per KV head, rank = head_dim, no RoPE
+    (dict(mode="full_rank", n_groups=8, rank=128, rope_theta=5e5), P.PALU_ERR_UNSUPPORTED),
+    (dict(mode="full_rank", n_groups=2, rank=128), P.PALU_ERR_SHAPE),
+    (dict(mode="full_rank", n_groups=8, rank=256), P.PALU_ERR_SHAPE),
 ]
+
+
+def test_full_rank_mode_needs_no_factors(lib):
+    """FULL_RANK accepts NULL b_k, b_v (it never reads them) but not a NULL cache."""
+    d = _desc(mode="full_rank", n_groups=8, rank=128)
+    n = ctypes.c_size_t(0)
+    assert lib.palu_decode_attn_workspace(ctypes.byref(d), ctypes.byref(n)) == P.PALU_OK
+    heads = 8 * 32
+    assert n.value >= heads * 128 * 4          # the pre-scaled queries
+    _, _, kname = P.palu_decode_attn_plan(d)
+    assert kname == "split_absorbed_mfma_kernel"
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, None, fake, None, None, None, fake,
+                                fake, 1 << 40, None) == P.PALU_ERR_NULL
+    # too small a workspace is caught before anything is launched
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake,
+                                fake, 16, None) == P.PALU_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw,status", BAD)

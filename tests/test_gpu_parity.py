@@ -117,6 +117,40 @@ def test_more_than_64_splits(mode):
     assert_close(got, _oracle(cfg, t, theta), what=f"79 splits/{mode}")
 
 
+def _run_full(cfg, t, split_tokens=0, lens=None):
+    import torch
+    import rank_compressed_kv_amd as P
+    ln = dev(t["lens"] if lens is None else lens)
+    out = P.full_rank_attention(dev(t["q"]), dev(t["k_full"]), dev(t["v_full"]), ln,
+                                split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 5])
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_full_rank_baseline(idx, split_tokens):
+    """The uncompressed baseline (full bf16 K and V, keys cached rotated) on the
+    MHA, GQA and ragged shapes: ordinary decode attention."""
+    cfg = SMALL[idx]
+    t = W.generate(cfg, parts=("decode", "full"))
+    print(f"[full rank] cfg{idx} split={split_tokens}", flush=True)
+    got = _run_full(cfg, t, split_tokens)
+    want = O.full_rank_attention(t["q"], t["k_full"], t["v_full"], t["lens"])
+    assert_close(got, want, what=f"full rank cfg{idx}")
+
+
+def test_full_rank_length_edges():
+    cfg = SMALL[3].scaled(batch=8, max_ctx=640, ragged=None)
+    edge = np.array([0, 1, 63, 64, 65, 129, 511, 640])
+    t = W.generate(cfg, parts=("decode", "full"), lens=edge)
+    for st in (64, 0):
+        got = _run_full(cfg, t, st)
+        assert np.all(got[0] == 0.0)
+        want = O.full_rank_attention(t["q"], t["k_full"], t["v_full"], edge)
+        assert_close(got, want, what=f"full rank edges split={st}")
+
+
 def test_null_lens_means_full_capacity():
     cfg = SMALL[3].scaled(max_ctx=300)
     t = W.generate(cfg)

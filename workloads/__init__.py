@@ -40,7 +40,7 @@ __all__ = ["Config", "CONFIGS", "generate", "f32_to_bf16_bits", "bf16_bits_to_f3
 # child-stream index of every tensor: fixed, so adding a tensor never changes
 # the bits of another
 _STREAM = {"q": 0, "h_k": 1, "h_v": 2, "b_k": 3, "b_v": 4, "lens": 5,
-           "outlier": 6, "x": 7, "a_k": 8, "a_v": 9, "pos": 10}
+           "outlier": 6, "x": 7, "a_k": 8, "a_v": 9, "pos": 10, "k_full": 11, "v_full": 12}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -150,7 +150,9 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
              lens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Draw one workload.
 
-    parts: "decode" -> q, h_k, h_v, b_k, b_v, lens; "append" -> x, a_k, a_v, pos.
+    parts: "decode" -> q, h_k, h_v, b_k, b_v, lens; "append" -> x, a_k, a_v, pos;
+    "full" -> k_full, v_full [B, Hkv, L_cap, d] (the uncompressed baseline's
+    cache, same q and lens as "decode", which it needs).
     lens overrides the drawn lengths (edge-case tests). Values are fp32 arrays or
     uint16 bf16 bits, per cfg.dtype; lens and pos are int32.
     """
@@ -185,6 +187,10 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
         if lens.shape != (B,) or lens.min(initial=0) < 0 or lens.max(initial=0) > L:
             raise ValueError("lens must be [B] with 0 <= len <= max_ctx")
         out["lens"] = lens
+    if "full" in parts:
+        Hkv = cfg.n_kv_heads
+        for name in ("k_full", "v_full"):
+            out[name] = _store(_normal(seed, name, (B, Hkv, L, d)), cfg.dtype)
     if "append" in parts:
         dm = cfg.d_model
         out["x"] = _store(_normal(seed, "x", (B, dm)), cfg.dtype)
