@@ -46,7 +46,9 @@
 //            in LDS (four-row groups offset by 32 B: conflict-free).
 // Loads: 16-byte pieces of each tile go through two register stages (two tiles
 // in flight) into a ring of three LDS tile buffers; rows past the split's end
-// are clamped to its last valid row and masked.
+// are clamped to its last valid row and masked. Two workgroup barriers per
+// tile: one after the partial scores, one after the softmax (which also
+// covers the copy of a later tile into LDS).
 #include <math.h>
 
 #include "device_util.h"
@@ -261,10 +263,12 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
   const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
   const int ntiles = (t1 - s0 + kTile - 1) / kTile;
 
-  auto process = [&](int it) {
-    const int tok0 = s0 + it * kTile;
+  // Phase A of tile it (needs the K tile and the rotation table of tile it):
+  // rebuild the owned key blocks, rotate them and store this wave's partial
+  // scores.
+  floatx4 sc;
+  auto keys_scores = [&](int it) {
     const char* kt = sm.k[it % kNBuf];
-    const char* vt = sm.v[it % kNBuf];
     // keys of the owned blocks: K^T[16*cbs(j) + 4kb + i][token ln]
     floatx4 kk[kNB];
 #pragma unroll
@@ -291,24 +295,28 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
       }
     }
     // partial scores S^T[token 4kb+i][head slot ln] over the owned blocks
-    floatx4 sc = {0.f, 0.f, 0.f, 0.f}, sc2 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
       short4v ah, al;
       split_bf16x4(kk[j], ah, al);
-      sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], sc, 0, 0, 0);
-      sc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[j], sc2, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[j], s2, 0, 0, 0);
     }
-    sc += sc2;
+    sc = s1 + s2;
     sm.spart[wave][lane] = float4{sc[0], sc[1], sc[2], sc[3]};
-    __syncthreads();
-    // every wave has rotated this tile: the table can take the next one
+  };
+  // Phase B of tile it (after every wave's partial scores are in LDS): the
+  // rotation table moves to tile it+1, and the first wave of each KV head
+  // runs the online softmax of its query heads and publishes P and the
+  // rescale factors.
+  auto softmax_tile = [&](int it) {
+    const int tok0 = s0 + it * kTile;
     if (it + 1 < ntiles) {
       if ((it + 1) % kAnchor == 0) rope_exact(tok0 + kTile);
       else if (rope) rope_advance();
       rope_write();
     }
-    // softmax of the owned heads by the first wave of each KV head
     if (part == 0) {
 #pragma unroll
       for (int w = 1; w < kWPH; ++w) {
@@ -337,31 +345,32 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
         if (kb == 0) sm.alpha[hg] = alpha;
       }
     }
-    __syncthreads();
-    // values: this wave's r slice for all query heads of the slice
-    {
-      const bool hv = ln < nqs;
-      const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
-      const float al = hv ? sm.alpha[ln] : 1.f;
-      short4v ph, pl;
-      split_bf16x4(floatx4{pp.x, pp.y, pp.z, pp.w}, ph, pl);
-      const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / kWaves) + ln));
+  };
+  // Phase C of tile it (after P is in LDS): this wave's r slice of the value
+  // sums for all query heads of the slice.
+  auto values_tile = [&](int it) {
+    const char* vt = sm.v[it % kNBuf];
+    const bool hv = ln < nqs;
+    const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
+    const float al = hv ? sm.alpha[ln] : 1.f;
+    short4v ph, pl;
+    split_bf16x4(floatx4{pp.x, pp.y, pp.z, pp.w}, ph, pl);
+    const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / kWaves) + ln));
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        short4v a;
+    for (int rb = 0; rb < kRB; ++rb) {
+      short4v a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
-        acc[rb] *= al;
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, acc[rb], 0, 0, 0);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[rb], 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
+      acc[rb] *= al;
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, acc[rb], 0, 0, 0);
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[rb], 0, 0, 0);
     }
   };
 
   // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
-  // the tile (byte 16*that in a row-major tile of 16 rows), if below 2R; two
+  // the tile (byte 16*that in a row-major tile of 16 rows), if below 2R. Two
   // tiles wait in registers (stages a and b, vector types so they stay in
-  // registers) while one is in LDS.
+  // registers) and two ahead of the one being consumed are in LDS.
   typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
   auto fetch = [&](int tok0, u32v& k, u32v& v) {
 #pragma unroll
@@ -390,24 +399,39 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
       }
     }
   };
+
+  // Two barriers per tile. Iteration it: [after B1(it)] softmax of tile it and
+  // the copy of tile it+2 into LDS (its buffer last held tile it-1, whose
+  // values every wave finished before B1(it)); B2(it); the values of tile it
+  // and the keys and scores of tile it+1, back to back so the scheduler can
+  // interleave their MFMAs and VALU work; B1(it+1).
   u32v ka, va, kb2, vb2;
   fetch(s0, ka, va);
   put(0, ka, va);
   fetch(s0 + kTile, ka, va);
-  fetch(s0 + 2 * kTile, kb2, vb2);
+  put(1, ka, va);
+  fetch(s0 + 2 * kTile, ka, va);
+  fetch(s0 + 3 * kTile, kb2, vb2);
+  __syncthreads();
+  keys_scores(0);
+  __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
-    // stage a holds tile it+1: to LDS (its buffer held tile it-2, finished by
-    // everyone), then fetch tile it+3 into it
-    put((it + 1) % kNBuf, ka, va);
-    fetch(s0 + (it + 3) * kTile, ka, va);
+    softmax_tile(it);
+    put((it + 2) % kNBuf, ka, va);
+    fetch(s0 + (it + 4) * kTile, ka, va);
     __syncthreads();
-    process(it);
-    if (it + 1 < ntiles) {
-      put((it + 2) % kNBuf, kb2, vb2);
-      fetch(s0 + (it + 4) * kTile, kb2, vb2);
-      __syncthreads();
-      process(it + 1);
-    }
+    values_tile(it);
+    if (it + 1 >= ntiles) break;
+    keys_scores(it + 1);
+    __syncthreads();
+    softmax_tile(it + 1);
+    put((it + 3) % kNBuf, kb2, vb2);
+    fetch(s0 + (it + 5) * kTile, kb2, vb2);
+    __syncthreads();
+    values_tile(it + 1);
+    if (it + 2 >= ntiles) break;
+    keys_scores(it + 2);
+    __syncthreads();
   }
 
   // ---- partials: this wave's r slice for every query head; (m, l) by owners
