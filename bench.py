@@ -55,6 +55,9 @@ def parse():
                     help="skip the second timed loop with events around the main kernel")
     ap.add_argument("--no-full-rank", action="store_true",
                     help="skip the uncompressed baseline (full bf16 K and V)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the head-grouping sweep (s = 1, 2, 4, 8 KV heads per "
+                         "group at 75%% key compression) and add it to the JSON line")
     return ap.parse_args()
 
 
@@ -184,6 +187,67 @@ def time_full_rank(torch, P, W, cfg, t, args):
                 k=tf["k_full"], v=tf["v_full"])
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
+
+
+def granularity_sweep(torch, P, W, cfg, args):
+    """Decode-call time per head grouping at 75% key compression (r = D_g / 4):
+    M-LRD s = 1 ... J-LRD s = Hkv, same total latent bytes; key-rebuild FLOPs
+    grow with s. Both key modes; the reconstruct mode carries RoPE."""
+    rows = []
+    for s in (1, 2, 4, 8):
+        if cfg.n_kv_heads % s:
+            continue
+        c = cfg.scaled(n_groups=cfg.n_kv_heads // s, rank=s * cfg.head_dim // 4, seed=60 + s)
+        t = W.generate(c)
+        lat_bytes = W.latent_bytes(c, t["lens"])
+        tokens = int(np.sum(t["lens"], dtype=np.int64))
+        flops = 2.0 * tokens * c.n_groups * c.rank * c.group_dim      # key rebuild
+        q, bk, bv, lens = (dev(torch, t[k]) for k in ("q", "b_k", "b_v", "lens"))
+        hk, hv = dev(torch, t["h_k"]), dev(torch, t["h_v"])
+        del t
+        row = {"s": s, "groups": c.n_groups, "rank": c.rank, "latent_bytes": lat_bytes,
+               "rebuild_gflop": round(flops / 1e9, 2),
+               "rebuild_flop_per_byte": round(flops / lat_bytes, 1)}
+        for mode in ("absorbed", "reconstruct"):
+            theta = c.rope_theta if mode == "reconstruct" else 0.0
+            desc = P.attn_desc(batch=c.batch, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+                               head_dim=c.head_dim, n_groups=c.n_groups, rank=c.rank,
+                               max_ctx=c.max_ctx, dtype=P.PALU_BF16, mode=mode, rope_theta=theta)
+            ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+            out = torch.empty(c.batch, c.n_q_heads, c.head_dim, dtype=torch.float32, device="cuda")
+            _, _, kname = P.palu_decode_attn_plan(desc)
+            stream = torch.cuda.current_stream()
+            for _ in range(3):
+                P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+            torch.cuda.synchronize()
+            n = max(5, args.steps // 4)
+            P.palu_profile_begin(n)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            kms, kn = P.palu_profile_end()
+            kus = kms / max(1, kn) * 1e3
+            call_us = e0.elapsed_time(e1) / n * 1e3
+            entry = {"kernel": kname, "call_us": round(call_us, 2), "kernel_us": round(kus, 2),
+                     "latent_GBps_kernel": round(lat_bytes / (kus * 1e-6) / 1e9, 1)}
+            if mode == "reconstruct":
+                tf = flops / (kus * 1e-6) / 1e12
+                entry["rebuild_TFLOPs"] = round(tf, 1)
+                ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+                entry["roofline_bound"] = "mfma" if flops / lat_bytes > ridge else "hbm"
+            row[mode] = entry
+        rows.append(row)
+        print(f"[sweep] s={s} r={c.rank}: absorbed {row['absorbed']['kernel_us']} us, "
+              f"reconstruct {row['reconstruct']['kernel_us']} us", file=sys.stderr, flush=True)
+        del q, bk, bv, lens, hk, hv
+        torch.cuda.empty_cache()
+    return rows
+
+
 def sampled_parity(O, cfg, t, res, mode, pairs):
     """Compare sampled (b, h) outputs of the first timed step with the oracle.
     The oracle sees the cache after the step's append (row len-1 rewritten)."""
@@ -194,8 +258,12 @@ def sampled_parity(O, cfg, t, res, mode, pairs):
     hk_dev, hv_dev = res["caches"][0]
     for b in range(cfg.batch):
         p = int(t["lens"][b]) - 1
-        hk[b, :, p] = hk_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
-        hv[b, :, p] = hv_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
+        if cfg.dtype == "bf16":
+            hk[b, :, p] = hk_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
+            hv[b, :, p] = hv_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            hk[b, :, p] = hk_dev[b, :, p].cpu().numpy()
+            hv[b, :, p] = hv_dev[b, :, p].cpu().numpy()
     want = O.decode_attention(t["q"], hk, hv, t["b_k"], t["b_v"], t["lens"], rope_theta=theta,
                               select=pairs)
     got = res["out"].astype(np.float64)
@@ -275,7 +343,9 @@ def main():
     t = W.generate(cfg, parts=("decode", "append"))
     # the append writes row len-1, so the step attends over exactly len rows
     lat_bytes = W.latent_bytes(cfg, t["lens"])
-    n_copies = max(1, int(math.ceil(ROTATE_BYTES / lat_bytes)))
+    # enough copies to defeat the 256 MB Infinity Cache (at most 16: a tiny
+    # workload is launch-bound whatever the cache holds)
+    n_copies = min(16, max(1, int(math.ceil(ROTATE_BYTES / lat_bytes))))
     print(f"[bench] cfg{args.config} {cfg.name}: latent bytes/step {lat_bytes}, "
           f"{n_copies} cache copies", file=sys.stderr, flush=True)
 
@@ -363,6 +433,8 @@ def main():
                       "sampled_parity_rel_l2": parity[m][1]}
                   for m, r in results.items()},
     }
+    if args.sweep:
+        line["granularity_sweep"] = granularity_sweep(torch, P, W, cfg, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(O, cfg, t, args.mode, args.cpu_seconds)
     print(json.dumps(line), flush=True)

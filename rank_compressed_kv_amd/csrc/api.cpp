@@ -41,6 +41,7 @@ palu_status ok() {
 constexpr int kSplitQuantum = 64;    // split sizes are multiples of this many tokens
 constexpr int kTargetWorkgroups = 1024;
 constexpr int kAbsorbedWorkgroups = 256;   // one per CU on a 256-CU MI355X
+constexpr int kTargetWaves = 2048;         // reconstruct kernel: eight per CU
 
 palu_status validate_attn(const palu_attn_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
@@ -110,13 +111,16 @@ Plan make_plan(const palu_attn_desc* d) {
     // kernel, which launches one workgroup per query head of each unit, and
     // one workgroup per CU (256 CUs, all resident at once) for the absorbed
     // MFMA kernel, whose register use allows one wave per SIMD.
-    const double wg_target = pl.kernel == SplitKernel::kGeneric
-                                 ? double(kTargetWorkgroups) / 4.0
-                                 : double(kAbsorbedWorkgroups);
-    // the reconstruct MFMA kernel launches one workgroup per slice of KV heads
-    const int slices = pl.kernel == SplitKernel::kReconstructMfma
-                           ? sp.s / reconstruct_heads_per_wg(sp.r, sp.s)
-                           : 1;
+    double wg_target = pl.kernel == SplitKernel::kGeneric ? double(kTargetWorkgroups) / 4.0
+                                                          : double(kAbsorbedWorkgroups);
+    // the reconstruct MFMA kernel launches one workgroup per slice of KV heads,
+    // and aims at about 2048 waves on the chip whatever its workgroup size
+    int slices = 1;
+    if (pl.kernel == SplitKernel::kAbsorbedMfma) slices = absorbed_head_slices(sp.nq);
+    if (pl.kernel == SplitKernel::kReconstructMfma) {
+      slices = sp.s / reconstruct_heads_per_wg(sp.r, sp.s);
+      wg_target = double(kTargetWaves) / reconstruct_waves_per_wg(sp.r, sp.s);
+    }
     const double want = double(d->max_ctx) * d->batch * d->n_groups * slices / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
     if (st < kSplitQuantum) st = kSplitQuantum;

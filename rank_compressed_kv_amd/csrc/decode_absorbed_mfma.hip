@@ -199,9 +199,16 @@ __device__ __forceinline__ void publish(const State<R>& st, Smem<R>& sm, int w, 
   sm.u.x.l[w][lane] = st.l;
 }
 
-template <int R>
+template <int R, bool kShared>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(DecodeParams p) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // query heads of a group beyond 16 go to further head slices (workgroups
+  // that read the same latents, shared through one XCD's L2)
+  const int nslice = (p.nq + 15) / 16;
+  const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
+  if (!un.live) return;
+  const int split = un.split, g = un.g, b = un.b;
+  const int hq0 = un.hs * 16;                            // first query head of the slice
+  const int nqs = min(16, p.nq - hq0);                   // its query heads
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
   const int n = clamp_len(p.lens, b, p.L);
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   // absorbed queries of the group's heads, split hi/lo bf16 (padding heads are 0)
   for (int e = threadIdx.x; e < 16 * R; e += 64 * kWaves) {
     const int hd = e / R, k = e % R;
-    const float x = hd < p.nq ? p.qt[(static_cast<size_t>(b) * p.Hq + g * p.nq + hd) * R + k] : 0.f;
+    const float x = hd < nqs ? p.qt[(static_cast<size_t>(b) * p.Hq + g * p.nq + hq0 + hd) * R + k] : 0.f;
     const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
     sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
     sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
@@ -250,14 +257,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
       const int rk = min(tok0 + ln, last);
 #pragma unroll
       for (int c = 0; c < R / 32; ++c) {
-        const uint4 t = load_stream16(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
+        const uint4 t = load_tile16<kShared>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
         nkv[4 * c] = t.x; nkv[4 * c + 1] = t.y; nkv[4 * c + 2] = t.z; nkv[4 * c + 3] = t.w;
       }
 #pragma unroll
       for (int q = 0; q < R / 32; ++q) {
         const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
         const int rv = min(tok0 + flat / (2 * R), last);
-        const uint4 t = load_stream16(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
+        const uint4 t = load_tile16<kShared>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
         nvv[4 * q] = t.x; nvv[4 * q + 1] = t.y; nvv[4 * q + 2] = t.z; nvv[4 * q + 3] = t.w;
       }
     };
@@ -319,8 +326,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   // head totals: sum the four lane groups' shares
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (ln >= p.nq) return;
-  const int head = g * p.nq + ln;
+  if (ln >= nqs) return;
+  const int head = g * p.nq + hq0 + ln;
   const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
   if (kb == 0) {
     p.part_ml[slot * 2] = M;
@@ -336,15 +343,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
 }  // namespace
 
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && (p.r == 128 || p.r == 256) && p.nq <= 16;
+  return dtype == 1 && (p.r == 32 || p.r == 64 || p.r == 128 || p.r == 256);
+}
+
+int absorbed_head_slices(int nq) { return (nq + 15) / 16; }
+
+template <int R>
+hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
+  const int nslice = absorbed_head_slices(p.nq);
+  if (nslice == 1) {
+    split_absorbed_mfma_kernel<R, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+  } else {
+    const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
+    if (ids == 0) return hipErrorInvalidValue;
+    split_absorbed_mfma_kernel<R, true>
+        <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {
-  const dim3 grid(p.n_split, p.G, p.B);
-  if (p.r == 128) split_absorbed_mfma_kernel<128><<<grid, 64 * kWaves, 0, st>>>(p);
-  else if (p.r == 256) split_absorbed_mfma_kernel<256><<<grid, 64 * kWaves, 0, st>>>(p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  switch (p.r) {
+    case 32: return launch_rank<32>(p, st);
+    case 64: return launch_rank<64>(p, st);
+    case 128: return launch_rank<128>(p, st);
+    case 256: return launch_rank<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace palu

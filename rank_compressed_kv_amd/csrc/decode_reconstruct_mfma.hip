@@ -127,38 +127,6 @@ struct Smem {
   float2 rtab[16][kTile][4];
 };
 
-// Which (context split, batch, group, head slice) a workgroup owns. With a
-// single head slice, blockIdx is (split, g, b); otherwise the units are
-// numbered u = split + n_split*(g + G*b), padded to a multiple of 8, and the
-// nslice workgroups of unit u get linear ids 8 apart.
-struct Unit {
-  int split, g, b, hs;
-  bool live;
-};
-__device__ __forceinline__ Unit unit_of(const DecodeParams& p, int nslice) {
-  Unit u{};
-  if (nslice == 1) {
-    u.split = blockIdx.x; u.g = blockIdx.y; u.b = blockIdx.z; u.hs = 0; u.live = true;
-    return u;
-  }
-  const int id = blockIdx.x;
-  const int lo = id & 7, hi = id >> 3;
-  u.hs = hi % nslice;
-  const int unit = (hi / nslice) * 8 + lo;
-  u.live = unit < p.n_split * p.G * p.B;
-  u.split = unit % p.n_split;
-  const int rest = unit / p.n_split;
-  u.g = rest % p.G;
-  u.b = rest / p.G;
-  return u;
-}
-
-template <bool kShared>
-__device__ __forceinline__ uint4 load_tile16(const void* ptr) {
-  if constexpr (kShared) return *static_cast<const uint4*>(ptr);
-  else return load_stream16(ptr);
-}
-
 template <int R, int kP, int HW, bool kShared>
 __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruct_mfma_kernel(
     DecodeParams p) {
@@ -166,7 +134,7 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
   constexpr int kNB = S::kNB, kWPH = S::kWPH, kWaves = S::kWaves, kThreads = S::kThreads;
   constexpr int kRB = S::kRB, kPieces = S::kPieces, kRE = S::kRE;
   const int nslice = p.s / HW;
-  const Unit un = unit_of(p, nslice);
+  const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
   if (!un.live) return;
   const int split = un.split, g = un.g, b = un.b, hs = un.hs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -481,9 +449,8 @@ hipError_t launch_shape(const DecodeParams& p, hipStream_t st) {
     const dim3 grid(p.n_split, p.G, p.B);
     split_reconstruct_mfma_kernel<R, kP, HW, false><<<grid, S::kThreads, 0, st>>>(p);
   } else {
-    const long units = static_cast<long>(p.n_split) * p.G * p.B;
-    const long ids = (units + 7) / 8 * 8 * nslice;
-    if (ids > 0x7fffffffL) return hipErrorInvalidValue;
+    const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
+    if (ids == 0) return hipErrorInvalidValue;
     split_reconstruct_mfma_kernel<R, kP, HW, true>
         <<<dim3(static_cast<unsigned>(ids)), S::kThreads, 0, st>>>(p);
   }
@@ -498,6 +465,11 @@ int reconstruct_heads_per_wg(int r, int s) {
   if (r == 128 || r == 256) return s % 4 == 0 ? 4 : (s % 2 == 0 ? 2 : 1);
   if (r == 32) return 1;
   return 0;
+}
+
+int reconstruct_waves_per_wg(int r, int s) {
+  const int hw = reconstruct_heads_per_wg(r, s);
+  return (r == 512 ? 4 : 2) * hw;
 }
 
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype) {

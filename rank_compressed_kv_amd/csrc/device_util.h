@@ -63,4 +63,47 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int L) {
   return n < 0 ? 0 : (n > L ? L : n);
 }
 
+// Which (context split, batch, group, head slice) a workgroup of a
+// context-split kernel owns. With one head slice, blockIdx is (split, g, b).
+// With several, the launch is one-dimensional: units u = split + n_split*(g +
+// G*b) are padded to a multiple of 8 and the nslice workgroups of unit u get
+// linear ids 8 apart, which puts them on the same XCD (workgroups are dealt
+// to the 8 XCDs round-robin) at about the same time, so the latent tiles they
+// all read are shared through that XCD's L2.
+struct SplitUnit {
+  int split, g, b, hs;
+  bool live;
+};
+__device__ __forceinline__ SplitUnit split_unit(int n_split, int G, int B, int nslice) {
+  SplitUnit u{};
+  if (nslice == 1) {
+    u.split = blockIdx.x; u.g = blockIdx.y; u.b = blockIdx.z; u.hs = 0; u.live = true;
+    return u;
+  }
+  const int id = blockIdx.x;
+  const int lo = id & 7, hi = id >> 3;
+  u.hs = hi % nslice;
+  const int unit = (hi / nslice) * 8 + lo;
+  u.live = unit < n_split * G * B;
+  u.split = unit % n_split;
+  const int rest = unit / n_split;
+  u.g = rest % G;
+  u.b = rest / G;
+  return u;
+}
+// number of one-dimensional workgroup ids for nslice > 1 (0 if too many)
+inline long split_unit_ids(int n_split, int G, int B, int nslice) {
+  const long units = static_cast<long>(n_split) * G * B;
+  const long ids = (units + 7) / 8 * 8 * nslice;
+  return ids > 0x7fffffffL ? 0 : ids;
+}
+
+// a 16-byte piece of a latent tile: ordinary (L2-cached) when several
+// workgroups read the same tile, non-temporal otherwise
+template <bool kShared>
+__device__ __forceinline__ uint4 load_tile16(const void* ptr) {
+  if constexpr (kShared) return *static_cast<const uint4*>(ptr);
+  else return load_stream16(ptr);
+}
+
 }  // namespace palu

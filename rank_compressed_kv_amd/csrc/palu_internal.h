@@ -49,7 +49,7 @@ struct AppendParams {
 // Kernel variants of the context-split decode step.
 enum class SplitKernel {
   kGeneric = 0,        // VALU, any dtype/shape in range
-  kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {128, 256}, <= 16 q heads per group
+  kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {32, 64, 128, 256}
   kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
                          // head, r in {128, 256, 512}
 };
@@ -61,9 +61,11 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
+int absorbed_head_slices(int nq);   // workgroups per (split, b, g): 16 query heads each
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);
 int reconstruct_heads_per_wg(int r, int s);   // KV heads per workgroup (0: not served)
+int reconstruct_waves_per_wg(int r, int s);
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);

@@ -106,6 +106,18 @@ def test_reconstruct_head_groupings(s, r):
         assert_close(got, _oracle(cfg, t, theta), what=f"s={s} r={r} split={st}")
 
 
+@pytest.mark.parametrize("s,r", [(1, 32), (2, 64), (4, 128), (8, 256)])
+def test_absorbed_head_groupings(s, r):
+    """Absorbed keys for every head grouping at 75% compression: ranks 32-256 on
+    the MFMA kernel, and 32 query heads per group (two head slices that share
+    the latent tiles)."""
+    cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r, batch=2, max_ctx=700, seed=50 + s)
+    t = W.generate(cfg)
+    for st in (0, 128):
+        got, theta = run_decode(cfg, t, "absorbed", split_tokens=st)
+        assert_close(got, _oracle(cfg, t, 0.0), what=f"absorbed s={s} r={r} split={st}")
+
+
 @pytest.mark.parametrize("mode", ["absorbed", "reconstruct"])
 def test_more_than_64_splits(mode):
     """79 splits of 64 tokens: the merge that stages split states through LDS
