@@ -203,3 +203,39 @@ def full_rank_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, lens: np.nd
             j = h // gqa
             out[b, h] = attend(to_f64(q[b, h]), to_f64(k[b, j, :n]), to_f64(v[b, j, :n]), scale)
     return out
+
+
+def decode_value_latents(q: np.ndarray, h_k: np.ndarray, h_v: np.ndarray, b_k: np.ndarray,
+                         lens: np.ndarray, group_dim: int, *, rope_theta: float = 0.0,
+                         scale: Optional[float] = None) -> np.ndarray:
+    """The attention-weighted sum of value latents, u*[b, h] = sum_t p_t h_v[b, g, t]
+    (Palu author response, clarification of W1: the value reconstruction matrix
+    acts after this sum, so it can be fused with the output projection: the
+    result times B_v[g][:, cols(j)] is the attention output of decode_attention).
+
+    q [B, Hq, d]; h_k, h_v [B, G, L_cap, r]; b_k [G, r, D_g]; group_dim = D_g.
+    The weights p_t come from the same rebuilt (and rotated) keys as in
+    decode_attention. Returns fp64 [B, Hq, r]; length 0 gives zeros.
+    """
+    Bsz, Hq, d = q.shape
+    G, r, Dg = b_k.shape
+    if Dg != group_dim:
+        raise ValueError("b_k does not match group_dim")
+    s, gqa, _ = head_layout(Hq, G, r, Dg, d)
+    scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    out = np.zeros((Bsz, Hq, r))
+    bk_all = to_f64(b_k)
+    for b in range(Bsz):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for g in range(G):
+            Kg = reconstruct(h_k[b, g, :n], bk_all[g])        # [n, D_g]
+            Hv = to_f64(h_v[b, g, :n])                        # [n, r]
+            pos = np.arange(n)
+            for h in range(g * s * gqa, (g + 1) * s * gqa):
+                jl = h // gqa - g * s
+                Kj = apply_rope(Kg[:, jl * d:(jl + 1) * d], pos, rope_theta)
+                p_t = softmax((Kj @ to_f64(q[b, h])) * scale)
+                out[b, h] = p_t @ Hv
+    return out

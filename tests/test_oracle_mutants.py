@@ -31,6 +31,9 @@ MUTANTS = {
                                   "to_f64(k[b, j, :n]), to_f64(k[b, j, :n])"),
     "full_rank_len_off_by_one": ("full_rank_attention", "n = int(lens[b])",
                                  "n = max(0, int(lens[b]) - 1)"),
+    "latents_value_uses_keys": ("decode_value_latents", "Hv = to_f64(h_v[b, g, :n])",
+                                "Hv = to_f64(h_k[b, g, :n])"),
+    "latents_gqa_modulo": ("decode_value_latents", "jl = h // gqa - g * s", "jl = h % s"),
     "softmax_unnormalised": ("softmax", "return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "reconstruct_transposed": ("reconstruct", "return to_f64(h) @ to_f64(b)",
                                "return to_f64(h) @ to_f64(b)[::-1]"),

@@ -283,6 +283,42 @@ def test_value_fold():
     np.testing.assert_allclose((p @ H) @ B, p @ O.reconstruct(H, B), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("theta", [0.0, 1e4])
+def test_value_latents_times_bv_is_the_output(theta):
+    """u* B_v[g][:, cols(j)] reproduces the attention output head by head
+    (GQA, two groups of two KV heads), with and without RoPE."""
+    rng = np.random.default_rng(31)
+    B, Hq, d, G, r, L = 2, 8, 8, 2, 5, 9
+    Dg = 2 * d
+    q = rng.standard_normal((B, Hq, d))
+    h_k = rng.standard_normal((B, G, L, r))
+    h_v = rng.standard_normal((B, G, L, r))
+    b_k = rng.standard_normal((G, r, Dg))
+    b_v = rng.standard_normal((G, r, Dg))
+    lens = np.array([L, 4])
+    u = O.decode_value_latents(q, h_k, h_v, b_k, lens, Dg, rope_theta=theta)
+    want = O.decode_attention(q, h_k, h_v, b_k, b_v, lens, rope_theta=theta)
+    for h in range(Hq):
+        g, jl = (h // 2) // 2, (h // 2) % 2
+        got = u[:, h] @ b_v[g][:, jl * d:(jl + 1) * d]
+        np.testing.assert_allclose(got, want[:, h], rtol=1e-11, atol=1e-12)
+
+
+def test_value_latents_closed_forms():
+    """One token: u* is that token's value latent row; equal value rows: u* is
+    that row whatever the weights; length 0: zeros."""
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((3, 2, 4))
+    h_k = rng.standard_normal((3, 1, 5, 3))
+    h_v = rng.standard_normal((3, 1, 5, 3))
+    h_v[2, 0, :] = np.array([0.5, -1.25, 2.0])
+    b_k = rng.standard_normal((1, 3, 8))
+    u = O.decode_value_latents(q, h_k, h_v, b_k, np.array([1, 0, 5]), 8, rope_theta=100.0)
+    np.testing.assert_allclose(u[0], np.tile(h_v[0, 0, 0], (2, 1)), rtol=0, atol=1e-15)
+    assert np.all(u[1] == 0.0)
+    np.testing.assert_allclose(u[2], np.tile([0.5, -1.25, 2.0], (2, 1)), rtol=0, atol=1e-14)
+
+
 def test_softmax_rows_sum_to_one_and_shift_invariance():
     rng = np.random.default_rng(4)
     z = rng.standard_normal((5, 33)) * 10
