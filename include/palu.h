@@ -87,6 +87,12 @@ typedef struct palu_attn_desc {
   int32_t split_tokens; /* tokens per context split; 0 picks one; else a multiple of 64 */
   float scale;          /* softmax scale; <= 0 means 1/sqrt(d)                   */
   double rope_theta;    /* RoPE base; 0 means none; must be 0 in ABSORBED mode   */
+  int32_t latent_out;   /* 0: out [B, Hq, d] = u* B_v[g][:, cols(j)];
+                           1: out [B, Hq, r] = u*, the attention-weighted sum of
+                           value latents, and b_v is not read (may be NULL): the
+                           caller applies B_v, e.g. fused with its output
+                           projection (Palu author response, clarification of W1:
+                           B_v acts after the weighted sum). FULL_RANK ignores it. */
 } palu_attn_desc;
 
 /* Bytes of device workspace palu_decode_attn needs for this descriptor
@@ -106,14 +112,15 @@ palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
  *   h_k, h_v [B, G, L_cap, r]    dtype; rows >= len[b] are never read
  *   b_k, b_v [G, r, D_g]         dtype
  *   seq_lens [B] int32 on the device, or NULL for len[b] = L_cap
- *   out      [B, Hq, d] fp32; a sequence of length 0 gives zeros
+ *   out      [B, Hq, d] fp32 ([B, Hq, r] with latent_out); a sequence of length
+ *            0 gives zeros
  *   workspace, workspace_bytes: device scratch of at least the size reported by
  *            palu_decode_attn_workspace; its contents are overwritten.
  * FULL_RANK mode: out[b, h, :] = sum_t softmax_t(scale * <q[b,h], h_k[b,j,t]>)
  * h_v[b,j,t] with j = h / (Hq / Hkv); needs n_groups == n_kv_heads and
  * rank == head_dim; b_k and b_v are not read.
  * Errors: NULL for a missing pointer (only seq_lens may be NULL, and b_k, b_v
- * in FULL_RANK mode), SHAPE (also FULL_RANK with n_groups != n_kv_heads or
+ * in FULL_RANK mode or with latent_out), SHAPE (also FULL_RANK with n_groups != n_kv_heads or
  * rank != head_dim), UNSUPPORTED (ABSORBED or FULL_RANK with rope_theta != 0,
  * unknown dtype/mode, rope_theta < 0), WORKSPACE, DEVICE (launch failure). */
 palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,

@@ -56,7 +56,8 @@ class AttnDesc(ctypes.Structure):
                 ("n_groups", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("rope_theta", ctypes.c_double)]
+                ("scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("latent_out", ctypes.c_int32)]
 
 
 class AppendDesc(ctypes.Structure):
@@ -168,11 +169,12 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
     _need(h_k, "h_k", (B, G, L, r), dt)
     _need(h_v, "h_v", (B, G, L, r), dt)
     full = desc.mode == PALU_MODE_FULL_RANK
+    latent = not full and bool(desc.latent_out)
     if not full or b_k is not None:
         _need(b_k, "b_k", (G, r, dg), dt)
-    if not full or b_v is not None:
+    if not (full or latent) or b_v is not None:
         _need(b_v, "b_v", (G, r, dg), dt)
-    _need(out, "out", (B, Hq, d), torch.float32)
+    _need(out, "out", (B, Hq, r if latent else d), torch.float32)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", (B,), torch.int32)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
@@ -228,14 +230,16 @@ def palu_profile_end() -> Tuple[float, int]:
 
 def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_groups: int,
               rank: int, max_ctx: int, dtype: int, mode: str = "reconstruct",
-              rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0) -> AttnDesc:
+              rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0,
+              latent_out: bool = False) -> AttnDesc:
     modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED,
              "full_rank": PALU_MODE_FULL_RANK}
     if mode not in modes:
         raise ValueError(f"mode must be one of {sorted(modes)}")
     return AttnDesc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                     n_groups=n_groups, rank=rank, max_ctx=max_ctx, dtype=dtype, mode=modes[mode],
-                    split_tokens=split_tokens, scale=scale, rope_theta=rope_theta)
+                    split_tokens=split_tokens, scale=scale, rope_theta=rope_theta,
+                    latent_out=1 if latent_out else 0)
 
 
 def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: int,
@@ -246,16 +250,19 @@ def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: 
 
 def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
                      mode: str = "reconstruct", rope_theta: float = 0.0, scale: float = 0.0,
-                     split_tokens: int = 0, out=None, workspace=None, stream=None):
+                     split_tokens: int = 0, latent_out: bool = False, out=None,
+                     workspace=None, stream=None):
     """Shapes are read from the tensors; n_kv_heads fixes the head layout.
+    With latent_out the result is u* [B, Hq, r] and b_v may be None.
     Allocates out and the workspace with torch when they are not given."""
     B, Hq, d = q.shape
     _, G, L, r = h_k.shape
     desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, n_groups=G,
                      rank=r, max_ctx=L, dtype=_dt(q), mode=mode, rope_theta=rope_theta,
-                     scale=scale, split_tokens=split_tokens)
+                     scale=scale, split_tokens=split_tokens, latent_out=latent_out)
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, r if latent_out else d), dtype=torch.float32,
+                          device=q.device)
     if workspace is None:
         workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
                                 device=q.device)

@@ -148,16 +148,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const int lane = tid & 63, warp = tid >> 6;
   const int n = clamp_len(p.lens, b, p.L);
   const int ns = (n + p.split_tokens - 1) / p.split_tokens;
-  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
+  const bool full = p.full_rank != 0 || p.latent_out != 0;   // no B_v: out = u*
+  const int ow = full ? p.r : p.d;                            // output width
+  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * ow;
   if (ns == 0) {
-    for (int c = tid; c < p.d; c += kThreads) out[c] = 0.f;
+    for (int c = tid; c < ow; c += kThreads) out[c] = 0.f;
     return;
   }
   const int j = h / p.gqa, g = j / p.s, jl = j % p.s;
   const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
   const float* ml = p.part_ml + base * 2;
   const float* pu = p.part_u + base * p.r;
-  const bool full = p.full_rank != 0;                  // no B_v: out = u*
   const T* Bv = full ? nullptr
                      : static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
 
@@ -262,8 +263,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (full) {                                          // r == d
-    for (int c = tid; c < p.d; c += kThreads) out[c] = us[c];
+  if (full) {
+    for (int c = tid; c < p.r; c += kThreads) out[c] = us[c];
     return;
   }
 
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   const size_t base = (static_cast<size_t>(b) * p.Hq + h) * p.n_split;
   const float* ml = p.part_ml + base * 2;
   const float* pu = p.part_u + base * p.r;
-  const bool full = p.full_rank != 0;                  // no B_v: out = u*
+  const bool full = p.full_rank != 0 || p.latent_out != 0;   // no B_v: out = u*
   const T* Bv = full ? nullptr
                      : static_cast<const T*>(p.b_v) + static_cast<size_t>(g) * p.r * p.Dg + jl * p.d;
   const int ncc = p.d / 8, ngroups = kThreads / ncc;
@@ -378,9 +379,10 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   load_u(0);
   if (!full) load_bv(0);
   const int ns = (n + p.split_tokens - 1) / p.split_tokens;
-  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * p.d;
+  const int ow = full ? p.r : p.d;                            // output width
+  float* out = p.out + (static_cast<size_t>(b) * p.Hq + h) * ow;
   if (ns == 0) {
-    for (int c = tid; c < p.d; c += kThreads) out[c] = 0.f;
+    for (int c = tid; c < ow; c += kThreads) out[c] = 0.f;
     return;
   }
   const float ms = lane < ns ? ms_raw : -INFINITY;
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   __shared__ float us[2 * kThreads];
   __shared__ float red[2048];
   const float inv = 1.f / L;
-  if (full) {                                          // r == d
+  if (full) {
     if (tid < p.r) out[tid] = u0 * inv;
     if (tid + kThreads < p.r) out[tid + kThreads] = u1 * inv;
     return;

@@ -216,9 +216,10 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   palu_status st = validate_attn(desc);
   if (st != PALU_OK) return st;
   const bool full = desc->mode == PALU_MODE_FULL_RANK;
-  if (!q || !h_k || !h_v || (!full && (!b_k || !b_v)) || !out || !workspace)
-    return fail(PALU_ERR_NULL, full ? "q, h_k, h_v, out and workspace must be non-NULL"
-                                    : "q, h_k, h_v, b_k, b_v, out and workspace must be non-NULL");
+  const bool latent = !full && desc->latent_out != 0;
+  if (!q || !h_k || !h_v || (!full && !b_k) || (!full && !latent && !b_v) || !out || !workspace)
+    return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
+                               "must be non-NULL");
   const Plan pl = make_plan(desc);
   const WorkspaceLayout wl = layout(desc, pl);
   if (workspace_bytes < wl.total)
@@ -237,6 +238,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   p.scale_log2 = float(scale * 1.4426950408889634);
   p.rope = desc->rope_theta > 0.0 ? 1 : 0;
   p.full_rank = full ? 1 : 0;
+  p.latent_out = latent ? 1 : 0;
   for (int i = 0; i < p.d / 2; ++i)
     p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
 

@@ -28,6 +28,7 @@ struct DecodeParams {
   int32_t n_split, split_tokens;
   int32_t rope;                // 1 if rotary embedding is applied
   int32_t full_rank;           // 1: h_k, h_v are full K, V; no B_k, B_v
+  int32_t latent_out;          // 1: out [B, Hq, r] holds u* (B_v left to the caller)
   float scale_log2;            // softmax scale * log2(e)
   // omega_i / (2 pi) in fp64 for i < d/2: the pair turns by t * omega_rev[i]
   // revolutions at position t

@@ -62,6 +62,20 @@ BAD = [
 ]
 
 
+def test_latent_output_needs_no_bv(lib):
+    """latent_out: b_v may be NULL (the check moves on to the workspace); without
+    it a NULL b_v is an error. b_k stays required."""
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc(latent_out=True)
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, None, None, fake,
+                                fake, 16, None) == P.PALU_ERR_WORKSPACE
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake,
+                                fake, 1 << 40, None) == P.PALU_ERR_NULL
+    d = _desc()
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, None, None, fake,
+                                fake, 1 << 40, None) == P.PALU_ERR_NULL
+
+
 def test_full_rank_mode_needs_no_factors(lib):
     """FULL_RANK accepts NULL b_k, b_v (it never reads them) but not a NULL cache."""
     d = _desc(mode="full_rank", n_groups=8, rank=128)

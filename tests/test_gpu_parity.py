@@ -163,6 +163,28 @@ def test_full_rank_length_edges():
         assert_close(got, want, what=f"full rank edges split={st}")
 
 
+@pytest.mark.parametrize("idx,mode", [(3, "absorbed"), (3, "reconstruct"), (2, "reconstruct"),
+                                      (5, "reconstruct"), (4, "absorbed")])
+def test_latent_output_without_bv(idx, mode):
+    """latent_out: the call returns the weighted value latents u* [B, Hq, r] and
+    never reads B_v (passed as None), for the caller to fuse B_v with W_o."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = SMALL[idx]
+    t = W.generate(cfg)
+    theta = cfg.rope_theta if mode == "reconstruct" else 0.0
+    print(f"[latent out] cfg{idx} mode={mode}", flush=True)
+    for st in (0, 64):
+        got = P.decode_attention(dev(t["q"]), dev(t["h_k"]), dev(t["h_v"]), dev(t["b_k"]), None,
+                                 dev(t["lens"]), n_kv_heads=cfg.n_kv_heads, mode=mode,
+                                 rope_theta=theta, split_tokens=st, latent_out=True)
+        torch.cuda.synchronize()
+        want = O.decode_value_latents(t["q"], t["h_k"], t["h_v"], t["b_k"], t["lens"],
+                                      cfg.group_dim, rope_theta=theta)
+        assert got.shape == (cfg.batch, cfg.n_q_heads, cfg.rank)
+        assert_close(got.cpu().numpy().astype(np.float64), want, what=f"u* cfg{idx}/{mode}")
+
+
 def test_null_lens_means_full_capacity():
     cfg = SMALL[3].scaled(max_ctx=300)
     t = W.generate(cfg)
