@@ -172,15 +172,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const bool vec = p.d % 8 == 0;
   const int ncc = vec ? p.d / 8 : 1, ngroups = kThreads / ncc;
   const int cc = tid % ncc, rg = tid / ncc;
-  float bv[kBvRows][8];
-  if (vec) {
+  // B_v rows as raw bits, rows past r (or threads past the row groups) read a
+  // valid row whose weight is 0
+  Raw8<T> bv[kBvRows];
+  if (vec && !full) {
 #pragma unroll
     for (int i = 0; i < kBvRows; ++i) {
-      const int k = rg + i * ngroups;
-      if (!full && rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
+      const int k = min(min(rg, ngroups - 1) + i * ngroups, p.r - 1);
+      bv[i].load(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc);
     }
   }
   const int phases = p.r >= kThreads ? 1 : kThreads / p.r;
@@ -282,11 +281,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     for (int k0 = rg + kBvRows * ngroups; k0 < p.r; k0 += kBvRows * ngroups) {
 #pragma unroll
       for (int i = 0; i < kBvRows; ++i) {
-        const int k = k0 + i * ngroups;
-        if (rg < ngroups && k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
+        const int k = min(k0 + i * ngroups, p.r - 1);
+        bv[i].load(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc);
       }
 #pragma unroll
       for (int i = 0; i < kBvRows; ++i) {
@@ -351,15 +347,12 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
   // Loads do not wait for the sequence length: the first 16 splits' states
   // and partials (all inside the workspace) are requested together with the
   // length and B_v, and entries of splits >= ns are discarded afterwards.
-  float bv[16][8];
-  auto load_bv = [&](int i0) {
+  Raw8<T> bv[16];
+  auto load_bv = [&](int i0) {   // rows past r read row r-1 (finite, weight 0)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int k = rg + ngroups * (i0 + i);
-      if (k < p.r) load8_f32(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc, bv[i]);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bv[i][e] = 0.f;
+      const int k = min(rg + ngroups * (i0 + i), p.r - 1);
+      bv[i].load(Bv + static_cast<size_t>(k) * p.Dg + 8 * cc);
     }
   };
   // thread t holds u entries t and t + 256 of 16 splits at a time

@@ -24,6 +24,36 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
+// Eight consecutive elements kept as raw bits: loaded with no branch around
+// them (callers clamp the address instead of skipping the load), so that many
+// loads stay in flight together, and widened to fp32 only where they are used.
+// (A load whose widening sits in the same conditional block as the load makes
+// the compiler wait for it before the next one.)
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const float4& h = e < 4 ? a : b;
+    const int k = e & 3;
+    return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+  }
+};
+
 // Eight consecutive elements widened to fp32 (16-byte aligned addresses).
 __device__ __forceinline__ void load8_f32(const uint16_t* p, float* v) {
   const uint4 w = *reinterpret_cast<const uint4*>(p);

@@ -66,16 +66,30 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   const T* x = static_cast<const T*>(p.x);
   const size_t prow = 2 * static_cast<size_t>(width);   // floats per (slice, sequence)
 
-  // all of this thread's A rows (rg + 16 i) first, 16 bytes each
-  float a[8][8];
+  // all of this thread's A rows (rg + 16 i) first, 16 bytes each, with no
+  // branch around the loads: rows past the slice read its last row and
+  // columns past the block read column 0 (finite values; the matching x
+  // entries are 0 and the results for such columns are never stored)
+  Raw8<T> a[8];
+  const int ca = active ? c : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = rg + kRowGroups * i;
-    if (active && row < rows) load8_f32(A + static_cast<size_t>(i0 + row) * width + c, a[i]);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[i][e] = 0.f;
+    const int row = min(rg + kRowGroups * i, rows - 1);
+    a[i].load(A + static_cast<size_t>(i0 + row) * width + ca);
   }
+  // x entries of the first sequence chunk: four per thread, issued right
+  // after the A loads so both are in flight together
+  constexpr int kPer = kBatchChunk * kRows / kThreads;
+  float xv[kPer];
+  auto load_x = [&](int b0, int nb) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads, bb = e / kRows, i = e % kRows;
+      const int bc = min(bb, nb - 1), ic = min(i, rows - 1);
+      xv[u] = load_f32(x, static_cast<size_t>(b0 + bc) * p.dm + i0 + ic);
+    }
+  };
+  load_x(0, min(kBatchChunk, p.B));
   __shared__ float xs[kBatchChunk][kRows];
   __shared__ float4 red[kRowGroups][kBatchChunk][kCols / 4];
   __shared__ int is_last;
@@ -84,9 +98,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   for (int b0 = 0; b0 < p.B; b0 += kBatchChunk) {
     const int nb = min(kBatchChunk, p.B - b0);
     __syncthreads();
-    for (int e = tid; e < kBatchChunk * kRows; e += kThreads) {
-      const int bb = e / kRows, i = e % kRows;
-      xs[bb][i] = bb < nb && i < rows ? load_f32(x, static_cast<size_t>(b0 + bb) * p.dm + i0 + i) : 0.f;
+    {
+      if (b0 > 0) load_x(b0, nb);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kThreads, bb = e / kRows, i = e % kRows;
+        xs[bb][i] = bb < nb && i < rows ? xv[u] : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -135,16 +153,18 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
       const int pos = p.pos[b];
       if (pos < 0 || pos >= p.L) continue;
       const float* src = p.part + static_cast<size_t>(b) * prow + fcol;
+      // up to 32 slices (d_model 4096) in flight at once, then added in order
       float4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < nslices; s0 += 8) {
-        float4 v[8];
+      for (int s0 = 0; s0 < nslices; s0 += 32) {
+        float4 v[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = s0 + u < nslices ? *reinterpret_cast<const float4*>(src + (s0 + u) * sstride)
-                                  : float4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 32; ++u)
+          v[u] = *reinterpret_cast<const float4*>(src + min(s0 + u, nslices - 1) * sstride);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {   // slices added in order
-          acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        for (int u = 0; u < 32; ++u) {
+          if (s0 + u < nslices) {
+            acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+          }
         }
       }
       const float r4[4] = {acc.x, acc.y, acc.z, acc.w};
