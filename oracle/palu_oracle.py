@@ -75,6 +75,39 @@ def append_rows_bf16(h64: np.ndarray) -> np.ndarray:
     return (keep + up.astype(np.uint64)).astype(np.uint16)
 
 
+def quantize_rows_i8(h32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token int8 quantisation of latent rows (the pages list per-token
+    quantisation of the low-rank latents as the follow-on lever; reading of
+    this build: symmetric, one scale per cached row of r latents).
+
+    With fp32 arithmetic throughout (the kernel's precision, so that both sides
+    take the same integer decisions): amax = max |h|, scale = amax / 127,
+    inv = 127 / amax (each a correctly rounded fp32 division), code =
+    round-to-nearest-even(h * inv) clamped to [-127, 127]. A row of zeros gets
+    scale 0 and codes 0. Returns (int8 codes [..., r], fp32 scales [...]).
+    """
+    h = np.asarray(h32, dtype=np.float32)
+    amax = np.max(np.abs(h), axis=-1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1.0)).astype(np.float32)
+    scale = np.where(nz, safe / np.float32(127.0), np.float32(0.0)).astype(np.float32)
+    inv = np.where(nz, np.float32(127.0) / safe, np.float32(0.0)).astype(np.float32)
+    prod = (h * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def dequantize_rows_i8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """h = code * scale, exactly, in fp64."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def append_rows_i8(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantised cache write: the latent row as the kernel forms it (the fp32
+    sum, here the exact value rounded once to fp32), then quantize_rows_i8."""
+    return quantize_rows_i8(np.asarray(h64, dtype=np.float64).astype(np.float32))
+
+
 # --------------------------------------------------------- reconstruction ---
 
 def reconstruct(h: np.ndarray, b: np.ndarray) -> np.ndarray:

@@ -34,6 +34,12 @@ MUTANTS = {
     "latents_value_uses_keys": ("decode_value_latents", "Hv = to_f64(h_v[b, g, :n])",
                                 "Hv = to_f64(h_k[b, g, :n])"),
     "latents_gqa_modulo": ("decode_value_latents", "jl = h // gqa - g * s", "jl = h % s"),
+    "quant_floor": ("quantize_rows_i8", "np.clip(np.rint(prod)", "np.clip(np.floor(prod)"),
+    "quant_128_steps": ("quantize_rows_i8", "np.float32(127.0) / safe", "np.float32(128.0) / safe"),
+    "quant_ties_away": ("quantize_rows_i8", "np.clip(np.rint(prod)",
+                        "np.clip(np.sign(prod) * np.floor(np.abs(prod) + 0.5)"),
+    "quant_column_amax": ("quantize_rows_i8", "amax = np.max(np.abs(h), axis=-1)",
+                          "amax = np.broadcast_to(np.max(np.abs(h)), h.shape[:-1])"),
     "softmax_unnormalised": ("softmax", "return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "reconstruct_transposed": ("reconstruct", "return to_f64(h) @ to_f64(b)",
                                "return to_f64(h) @ to_f64(b)[::-1]"),

@@ -29,6 +29,15 @@ def _arr(x):
 
 # --------------------------------------------------------------- goldens ---
 
+def test_golden_quantize_rows_i8(golden):
+    """Hand-derived codes: amax 2 gives inv 63.5; -63.5 and 0.5 are ties and go
+    to the even neighbour; a zero row has scale 0."""
+    c = golden["quantize_rows_i8"]
+    codes, scales = O.quantize_rows_i8(np.array(c["h"], dtype=np.float32))
+    np.testing.assert_array_equal(codes, np.array(c["codes"], dtype=np.int8))
+    np.testing.assert_allclose(scales * 127.0, c["scales_times_127"], rtol=1e-7, atol=0)
+
+
 def test_golden_two_token_softmax(golden):
     c = golden["two_token_softmax"]
     out = O.decode_attention(_arr(c["q"]), _arr(c["h_k"]), _arr(c["h_v"]), _arr(c["b_k"]),
@@ -317,6 +326,28 @@ def test_value_latents_closed_forms():
     np.testing.assert_allclose(u[0], np.tile(h_v[0, 0, 0], (2, 1)), rtol=0, atol=1e-15)
     assert np.all(u[1] == 0.0)
     np.testing.assert_allclose(u[2], np.tile([0.5, -1.25, 2.0], (2, 1)), rtol=0, atol=1e-14)
+
+
+def test_quantize_round_trip_and_symmetry():
+    """Each code is within half a step of h / scale (dequantised error at most
+    half a scale), the largest magnitude of a row maps to +-127, codes are odd
+    under negation, and a row scaled by 2^k keeps its codes."""
+    rng = np.random.default_rng(41)
+    h = rng.standard_normal((64, 96)).astype(np.float32)
+    h[5] *= 300.0
+    h[9, 3] = 40.0                                   # an outlier in one row
+    codes, scales = O.quantize_rows_i8(h)
+    deq = O.dequantize_rows_i8(codes, scales)
+    assert np.all(np.abs(deq - h) <= scales[:, None] * (0.5 + 1e-5))
+    rows = np.arange(64)
+    top = np.argmax(np.abs(h), axis=1)
+    np.testing.assert_array_equal(np.abs(codes[rows, top]), 127)
+    c2, s2 = O.quantize_rows_i8(-h)
+    np.testing.assert_array_equal(c2, -codes)
+    np.testing.assert_array_equal(s2, scales)
+    c3, s3 = O.quantize_rows_i8(h * np.float32(8.0))
+    np.testing.assert_array_equal(c3, codes)
+    np.testing.assert_array_equal(s3, scales * np.float32(8.0))
 
 
 def test_softmax_rows_sum_to_one_and_shift_invariance():

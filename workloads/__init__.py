@@ -40,7 +40,8 @@ __all__ = ["Config", "CONFIGS", "generate", "f32_to_bf16_bits", "bf16_bits_to_f3
 # child-stream index of every tensor: fixed, so adding a tensor never changes
 # the bits of another
 _STREAM = {"q": 0, "h_k": 1, "h_v": 2, "b_k": 3, "b_v": 4, "lens": 5,
-           "outlier": 6, "x": 7, "a_k": 8, "a_v": 9, "pos": 10, "k_full": 11, "v_full": 12}
+           "outlier": 6, "x": 7, "a_k": 8, "a_v": 9, "pos": 10, "k_full": 11, "v_full": 12,
+           "k_i8": 13, "v_i8": 14, "sk": 15, "sv": 16}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,7 +153,9 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
 
     parts: "decode" -> q, h_k, h_v, b_k, b_v, lens; "append" -> x, a_k, a_v, pos;
     "full" -> k_full, v_full [B, Hkv, L_cap, d] (the uncompressed baseline's
-    cache, same q and lens as "decode", which it needs).
+    cache, same q and lens as "decode", which it needs); "i8" -> k_i8, v_i8
+    int8 [B, G, L_cap, r] (codes uniform in [-127, 127]) and sk, sv fp32
+    [B, G, L_cap] (scales uniform in [0.005, 0.025)): an int8 latent cache.
     lens overrides the drawn lengths (edge-case tests). Values are fp32 arrays or
     uint16 bf16 bits, per cfg.dtype; lens and pos are int32.
     """
@@ -191,6 +194,12 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
         Hkv = cfg.n_kv_heads
         for name in ("k_full", "v_full"):
             out[name] = _store(_normal(seed, name, (B, Hkv, L, d)), cfg.dtype)
+    if "i8" in parts:
+        for name in ("k_i8", "v_i8"):
+            out[name] = _rng(seed, name).integers(-127, 128, size=(B, G, L, r)).astype(np.int8)
+        for name in ("sk", "sv"):
+            u = _rng(seed, name).random(size=(B, G, L), dtype=np.float32)
+            out[name] = (np.float32(0.005) + np.float32(0.02) * u).astype(np.float32)
     if "append" in parts:
         dm = cfg.d_model
         out["x"] = _store(_normal(seed, "x", (B, dm)), cfg.dtype)
