@@ -128,6 +128,25 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              const int32_t* seq_lens, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* palu_decode_attn over an int8 latent cache with one scale per cached row:
+ * latent row t of (b, g) is h[t, k] = codes[t, k] * scales[t] (per-token
+ * quantisation of the latents combined with the low-rank cache, Palu author
+ * response to reviewer Fsn9 on W1/W2; "Avg. Bits" with a scale shared by a
+ * group of elements, answer to Q4). Same result as palu_decode_attn on the
+ * dequantised cache, up to rounding.
+ *   h_k, h_v [B, G, L_cap, r]    int8 codes; rows >= len[b] are never read
+ *   s_k, s_v [B, G, L_cap]       fp32 scales, finite and >= 0
+ *   q, b_k, b_v, seq_lens, out, workspace as in palu_decode_attn (the
+ *            workspace size is palu_decode_attn_workspace's for desc)
+ * Provided for mode ABSORBED, dtype BF16 and rank 64, 128 or 256
+ * (latent_out allowed); anything else is UNSUPPORTED. Errors as in
+ * palu_decode_attn, and NULL for a missing s_k or s_v. */
+palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const int8_t* h_k,
+                                const int8_t* h_v, const float* s_k, const float* s_v,
+                                const void* b_k, const void* b_v, const int32_t* seq_lens,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 typedef struct palu_append_desc {
   int32_t batch;     /* B >= 1                                                    */
   int32_t d_model;   /* width of x, 1..65536                                      */

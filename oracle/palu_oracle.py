@@ -77,8 +77,8 @@ def append_rows_bf16(h64: np.ndarray) -> np.ndarray:
 
 def quantize_rows_i8(h32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Per-token int8 quantisation of latent rows (the pages list per-token
-    quantisation of the low-rank latents as the follow-on lever; reading of
-    this build: symmetric, one scale per cached row of r latents).
+    quantisation of the low-rank latents as the follow-on lever; reading taken
+    here: symmetric, one scale per cached row of r latents).
 
     With fp32 arithmetic throughout (the kernel's precision, so that both sides
     take the same integer decisions): amax = max |h|, scale = amax / 127,

@@ -7,7 +7,8 @@ raw device pointers and torch's current HIP stream. Every step of the
 computation runs in the library's HIP kernels. If libpalu.so is missing the
 calls raise; there is no fallback.
 
-Layouts (row-major): q [B, Hq, d]; h_k, h_v [B, G, L_cap, r]; b_k, b_v
+Layouts (row-major): q [B, Hq, d]; h_k, h_v [B, G, L_cap, r] (int8 caches
+with row scales s_k, s_v [B, G, L_cap] float32); b_k, b_v
 [G, r, s*d]; seq_lens [B] int32; out [B, Hq, d] float32; x [B, d_model];
 a_k, a_v [d_model, G*r]; pos [B] int32.
 """
@@ -23,7 +24,7 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+           "palu_decode_attn_i8", "decode_attention_i8", "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
            "palu_profile_end", "attn_desc", "append_desc", "decode_attention", "latent_append",
            "EXPORTED_SYMBOLS"]
 
@@ -33,6 +34,7 @@ PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+                    "palu_decode_attn_i8",
                     "palu_latent_append_workspace", "palu_latent_append",
                     "palu_profile_begin", "palu_profile_end",
                     "palu_status_string", "palu_last_error")
@@ -85,13 +87,15 @@ def library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
+    lib.palu_decode_attn_i8.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
     lib.palu_latent_append_workspace.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
     lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
     lib.palu_profile_begin.argtypes = [ctypes.c_int32]
     lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
     for fn in ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-               "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+               "palu_decode_attn_i8", "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
                "palu_profile_end"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.palu_status_string.argtypes = [ctypes.c_int]
@@ -187,6 +191,39 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
 
 
+def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
+                        workspace, stream=None) -> None:
+    """Enqueue one decode step over an int8 latent cache: h_k, h_v [B, G, L, r]
+    int8 codes, s_k, s_v [B, G, L] float32 row scales."""
+    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    G, r, L = desc.n_groups, desc.rank, desc.max_ctx
+    dg = (Hkv // G) * d
+    dt = _TORCH_DTYPE.get(desc.dtype)
+    if dt is None:
+        raise TypeError(f"unknown dtype code {desc.dtype}")
+    latent = bool(desc.latent_out)
+    _need(q, "q", (B, Hq, d), dt)
+    _need(h_k, "h_k", (B, G, L, r), torch.int8)
+    _need(h_v, "h_v", (B, G, L, r), torch.int8)
+    _need(s_k, "s_k", (B, G, L), torch.float32)
+    _need(s_v, "s_v", (B, G, L), torch.float32)
+    _need(b_k, "b_k", (G, r, dg), dt)
+    if not latent or b_v is not None:
+        _need(b_v, "b_v", (G, r, dg), dt)
+    _need(out, "out", (B, Hq, r if latent else d), torch.float32)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", (B,), torch.int32)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().palu_decode_attn_i8(
+        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), s_k.data_ptr(),
+        s_v.data_ptr(), b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
+        None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn_i8")
+
+
 def palu_latent_append_workspace(desc: AppendDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(library().palu_latent_append_workspace(ctypes.byref(desc), ctypes.byref(n)),
@@ -267,6 +304,26 @@ def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
         workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
                                 device=q.device)
     palu_decode_attn(desc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace, stream)
+    return out
+
+
+def decode_attention_i8(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
+                        scale: float = 0.0, split_tokens: int = 0, latent_out: bool = False,
+                        out=None, workspace=None, stream=None):
+    """Absorbed-mode decode over int8 latents (codes h_k, h_v with row scales
+    s_k, s_v). Allocates out and the workspace with torch when not given."""
+    B, Hq, d = q.shape
+    _, G, L, r = h_k.shape
+    desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, n_groups=G,
+                     rank=r, max_ctx=L, dtype=_dt(q), mode="absorbed", scale=scale,
+                     split_tokens=split_tokens, latent_out=latent_out)
+    if out is None:
+        out = torch.empty((B, Hq, r if latent_out else d), dtype=torch.float32,
+                          device=q.device)
+    if workspace is None:
+        workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
+                                device=q.device)
+    palu_decode_attn_i8(desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace, stream)
     return out
 
 

@@ -209,18 +209,23 @@ palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
   return ok();
 }
 
-palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,
-                             const void* h_v, const void* b_k, const void* b_v,
-                             const int32_t* seq_lens, float* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  palu_status st = validate_attn(desc);
-  if (st != PALU_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// both decode entry points; s_k, s_v non-NULL selects int8 latents
+palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, const void* h_v,
+                   const float* s_k, const float* s_v, const void* b_k, const void* b_v,
+                   const int32_t* seq_lens, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   const bool full = desc->mode == PALU_MODE_FULL_RANK;
   const bool latent = !full && desc->latent_out != 0;
   if (!q || !h_k || !h_v || (!full && !b_k) || (!full && !latent && !b_v) || !out || !workspace)
     return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
                                "must be non-NULL");
   const Plan pl = make_plan(desc);
+  if (s_k && pl.kernel != SplitKernel::kAbsorbedMfma)
+    return fail(PALU_ERR_UNSUPPORTED, "int8 latents need the absorbed MFMA kernel");
   const WorkspaceLayout wl = layout(desc, pl);
   if (workspace_bytes < wl.total)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
@@ -239,6 +244,8 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   p.rope = desc->rope_theta > 0.0 ? 1 : 0;
   p.full_rank = full ? 1 : 0;
   p.latent_out = latent ? 1 : 0;
+  p.latent_i8 = s_k ? 1 : 0;
+  p.s_k = s_k; p.s_v = s_v;
   for (int i = 0; i < p.d / 2; ++i)
     p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
 
@@ -264,6 +271,37 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   e = launch_merge(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const void* h_k,
+                             const void* h_v, const void* b_k, const void* b_v,
+                             const int32_t* seq_lens, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  return decode(desc, q, h_k, h_v, nullptr, nullptr, b_k, b_v, seq_lens, out, workspace,
+                workspace_bytes, stream);
+}
+
+palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const int8_t* h_k,
+                                const int8_t* h_v, const float* s_k, const float* s_v,
+                                const void* b_k, const void* b_v, const int32_t* seq_lens,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  if (desc->mode != PALU_MODE_ABSORBED || desc->dtype != PALU_BF16 ||
+      !absorbed_i8_supported(shape_params(desc), desc->dtype))
+    return fail(PALU_ERR_UNSUPPORTED,
+                "int8 latents need mode ABSORBED, dtype BF16 and rank 64, 128 or 256 "
+                "(got mode %d, dtype %d, rank %d)", desc->mode, desc->dtype, desc->rank);
+  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  return decode(desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace,
+                workspace_bytes, stream);
 }
 
 namespace {

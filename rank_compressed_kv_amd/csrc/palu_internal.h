@@ -29,6 +29,9 @@ struct DecodeParams {
   int32_t rope;                // 1 if rotary embedding is applied
   int32_t full_rank;           // 1: h_k, h_v are full K, V; no B_k, B_v
   int32_t latent_out;          // 1: out [B, Hq, r] holds u* (B_v left to the caller)
+  int32_t latent_i8;           // 1: h_k, h_v are int8 codes with row scales s_k, s_v
+  const float* s_k;            // [B, G, L] (int8 latents)
+  const float* s_v;
   float scale_log2;            // softmax scale * log2(e)
   // omega_i / (2 pi) in fp64 for i < d/2: the pair turns by t * omega_rev[i]
   // revolutions at position t
@@ -62,6 +65,7 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
+bool absorbed_i8_supported(const DecodeParams& p, int dtype);   // int8 latents
 int absorbed_head_slices(int nq);   // workgroups per (split, b, g): 16 query heads each
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);

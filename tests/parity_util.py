@@ -15,8 +15,8 @@ def dev(a: np.ndarray) -> torch.Tensor:
     """Seeded host array -> device tensor with the same bits (uint16 = bf16)."""
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    if a.dtype == np.int32:
-        return torch.from_numpy(a).cuda()
+    if a.dtype in (np.int32, np.int8):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 

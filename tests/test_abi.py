@@ -23,7 +23,7 @@ def lib():
 def _header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(palu_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(palu_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -91,6 +91,41 @@ def test_full_rank_mode_needs_no_factors(lib):
     # too small a workspace is caught before anything is launched
     assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake,
                                 fake, 16, None) == P.PALU_ERR_WORKSPACE
+
+
+def _i8(lib, d, *ptrs, nbytes=1 << 40):
+    fake = ctypes.c_void_p(0x1000)
+    q, hk, hv, sk, sv, bk, bv, out, ws = [fake if p is True else p for p in ptrs]
+    return lib.palu_decode_attn_i8(ctypes.byref(d), q, hk, hv, sk, sv, bk, bv, None, out, ws,
+                                   nbytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(mode="reconstruct", rope_theta=5e5),
+                                dict(mode="full_rank", n_groups=8, rank=128),
+                                dict(dtype=P.PALU_F32), dict(rank=32), dict(rank=512),
+                                dict(rank=96)])
+def test_int8_decode_unsupported_combinations(lib, kw):
+    """int8 latents are provided for ABSORBED, BF16, rank 64/128/256 only."""
+    assert _i8(lib, _desc(**kw), *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
+    assert b"int8" in lib.palu_last_error()
+
+
+def test_int8_decode_validation(lib):
+    """Descriptor errors come first, then missing pointers, then the workspace
+    (same size as palu_decode_attn's)."""
+    assert _i8(lib, _desc(batch=0), *([True] * 9)) == P.PALU_ERR_SHAPE
+    d = _desc(rank=128)
+    for i in range(9):                       # every pointer is needed here
+        ptrs = [True] * 9
+        ptrs[i] = None
+        assert _i8(lib, d, *ptrs, nbytes=16) == P.PALU_ERR_NULL, i
+    # latent_out: b_v may be NULL
+    d = _desc(rank=128, latent_out=True)
+    ptrs = [True] * 9
+    ptrs[6] = None
+    assert _i8(lib, d, *ptrs, nbytes=16) == P.PALU_ERR_WORKSPACE
+    need = P.palu_decode_attn_workspace(d)
+    assert _i8(lib, d, *([True] * 9), nbytes=need - 1) == P.PALU_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw,status", BAD)
