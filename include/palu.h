@@ -153,7 +153,7 @@ typedef struct palu_append_desc {
   int32_t n_groups;  /* G >= 1                                                    */
   int32_t rank;      /* r, 1..512                                                 */
   int32_t max_ctx;   /* L_cap: row stride of the cache                             */
-  int32_t dtype;     /* palu_dtype of x, a_k, a_v and the cache                    */
+  int32_t dtype;     /* palu_dtype of x, a_k, a_v and (except the int8 calls) the cache */
 } palu_append_desc;
 
 /* Bytes of device workspace palu_latent_append needs for this descriptor:
@@ -178,6 +178,30 @@ palu_status palu_latent_append_workspace(const palu_append_desc* desc, size_t* b
 palu_status palu_latent_append(const palu_append_desc* desc, const void* x, const void* a_k,
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace palu_latent_append_i8 needs: the counters of
+ * palu_latent_append, a second counter area (one int32 per (matrix, group)
+ * row segment, padded to 256 bytes), the same partial sums, and the finished
+ * fp32 rows [B, 2*G*r]. The whole counter area must be zero before the first
+ * call, as for palu_latent_append. */
+palu_status palu_latent_append_i8_workspace(const palu_append_desc* desc, size_t* bytes);
+
+/* Quantised cache write of one token per sequence for the int8 cache that
+ * palu_decode_attn_i8 reads (per-token quantisation, Palu author response to
+ * reviewer Fsn9 on W1/W2): the fp32 row h = x[b] . a[:, g*r:(g+1)*r], formed as
+ * in palu_latent_append, is stored as
+ *   s[b, g, pos[b]] = amax / 127, h_8[b, g, pos[b], k] = round(h[k] * 127 / amax)
+ * with amax = max_k |h[k]|, correctly rounded fp32 divisions, round to nearest
+ * (ties to even) of the fp32 product, codes clamped to [-127, 127]; a row of
+ * zeros stores scale 0 and codes 0.
+ *   x, a_k, a_v, pos as in palu_latent_append (desc->dtype is theirs);
+ *   h_k, h_v [B, G, L_cap, r] int8, 4-byte aligned; s_k, s_v [B, G, L_cap] fp32.
+ * Needs r a multiple of 4 (SHAPE otherwise). Workspace rules, overlap rules
+ * and errors as in palu_latent_append. */
+palu_status palu_latent_append_i8(const palu_append_desc* desc, const void* x, const void* a_k,
+                                  const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
+                                  float* s_v, const int32_t* pos, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Optional timing of the main decode kernel (the context-split kernel) with HIP
  * events on the stream it is launched on. palu_profile_begin(n) arms n records

@@ -24,7 +24,8 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_decode_attn_i8", "decode_attention_i8", "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+           "palu_decode_attn_i8", "decode_attention_i8", "palu_latent_append_workspace",
+           "palu_latent_append_i8_workspace", "palu_latent_append_i8", "latent_append_i8", "palu_latent_append", "palu_profile_begin",
            "palu_profile_end", "attn_desc", "append_desc", "decode_attention", "latent_append",
            "EXPORTED_SYMBOLS"]
 
@@ -36,6 +37,7 @@ PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
                     "palu_decode_attn_i8",
                     "palu_latent_append_workspace", "palu_latent_append",
+                    "palu_latent_append_i8_workspace", "palu_latent_append_i8",
                     "palu_profile_begin", "palu_profile_end",
                     "palu_status_string", "palu_last_error")
 
@@ -92,10 +94,15 @@ def library() -> ctypes.CDLL:
     lib.palu_latent_append_workspace.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
     lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
+    lib.palu_latent_append_i8_workspace.argtypes = [ctypes.POINTER(AppendDesc),
+                                                    ctypes.POINTER(sz)]
+    lib.palu_latent_append_i8.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, sz, vp]
     lib.palu_profile_begin.argtypes = [ctypes.c_int32]
     lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
     for fn in ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-               "palu_decode_attn_i8", "palu_latent_append_workspace", "palu_latent_append", "palu_profile_begin",
+               "palu_decode_attn_i8", "palu_latent_append_workspace",
+               "palu_latent_append_i8_workspace", "palu_latent_append_i8", "palu_latent_append", "palu_profile_begin",
                "palu_profile_end"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.palu_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +260,38 @@ def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, workspace,
         "palu_latent_append")
 
 
+def palu_latent_append_i8_workspace(desc: AppendDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().palu_latent_append_i8_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "palu_latent_append_i8_workspace")
+    return int(n.value)
+
+
+def palu_latent_append_i8(desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace,
+                          stream=None) -> None:
+    """Quantised cache write: h_k, h_v [B, G, L, r] int8, s_k, s_v [B, G, L] float32."""
+    palu_latent_append_i8_workspace(desc)   # the library validates the descriptor first
+    B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
+    dt = _TORCH_DTYPE.get(desc.dtype)
+    if dt is None:
+        raise TypeError(f"unknown dtype code {desc.dtype}")
+    _need(x, "x", (B, dm), dt)
+    _need(a_k, "a_k", (dm, G * r), dt)
+    _need(a_v, "a_v", (dm, G * r), dt)
+    _need(h_k, "h_k", (B, G, L, r), torch.int8)
+    _need(h_v, "h_v", (B, G, L, r), torch.int8)
+    _need(s_k, "s_k", (B, G, L), torch.float32)
+    _need(s_v, "s_v", (B, G, L), torch.float32)
+    _need(pos, "pos", (B,), torch.int32)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().palu_latent_append_i8(
+        ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),
+        h_v.data_ptr(), s_k.data_ptr(), s_v.data_ptr(), pos.data_ptr(), workspace.data_ptr(),
+        nbytes, _stream(stream)), "palu_latent_append_i8")
+
+
 def palu_profile_begin(max_records: int) -> None:
     _check(library().palu_profile_begin(int(max_records)), "palu_profile_begin")
 
@@ -354,3 +393,15 @@ def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> No
         workspace = torch.zeros(palu_latent_append_workspace(desc), dtype=torch.uint8,
                                 device=x.device)
     palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, workspace, stream)
+
+
+def latent_append_i8(x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace=None, stream=None) -> None:
+    """Quantised cache write into an int8 cache. Allocates the (zeroed)
+    workspace with torch when it is not given."""
+    B, dm = x.shape
+    _, G, L, r = h_k.shape
+    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
+    if workspace is None:
+        workspace = torch.zeros(palu_latent_append_i8_workspace(desc), dtype=torch.uint8,
+                                device=x.device)
+    palu_latent_append_i8(desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream)

@@ -1,6 +1,9 @@
 // Host side of libpalu: descriptor validation (before any HIP call), launch
 // planning and dispatch onto the caller's stream. See include/palu.h.
+// the library is built with hidden visibility; only the C ABI is exported
+#pragma GCC visibility push(default)
 #include "palu.h"
+#pragma GCC visibility pop
 
 #include <hip/hip_runtime.h>
 
@@ -304,6 +307,8 @@ palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const
                 workspace_bytes, stream);
 }
 
+}  // extern "C"
+
 namespace {
 palu_status validate_append(const palu_append_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
@@ -317,13 +322,47 @@ palu_status validate_append(const palu_append_desc* d) {
     return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
   return PALU_OK;
 }
+
+palu_status validate_append_i8(const palu_append_desc* d) {
+  palu_status st = validate_append(d);
+  if (st != PALU_OK) return st;
+  if (d->rank % 4) return fail(PALU_ERR_SHAPE, "int8 cache needs rank %% 4 == 0 (got %d)", d->rank);
+  return PALU_OK;
+}
+
+// both append entry points; s_k non-NULL selects the int8 cache
+palu_status append(const palu_append_desc* d, const void* x, const void* a_k, const void* a_v,
+                   void* h_k, void* h_v, float* s_k, float* s_v, const int32_t* pos,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const bool quant = s_k != nullptr;
+  if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
+    return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
+  if (quant && (reinterpret_cast<uintptr_t>(h_k) % 4 || reinterpret_cast<uintptr_t>(h_v) % 4))
+    return fail(PALU_ERR_SHAPE, "int8 caches must be 4-byte aligned");
+  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, quant);
+  if (workspace_bytes < need)
+    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PALU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  AppendParams p{};
+  p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
+  p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
+  p.quant = quant ? 1 : 0;
+  p.s_k = s_k; p.s_v = s_v;
+  append_bind_workspace(p, workspace);
+  hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
 }  // namespace
+
+extern "C" {
 
 palu_status palu_latent_append_workspace(const palu_append_desc* d, size_t* bytes) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
-  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, false);
   return ok();
 }
 
@@ -332,20 +371,26 @@ palu_status palu_latent_append(const palu_append_desc* d, const void* x, const v
                                void* workspace, size_t workspace_bytes, void* stream) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
-  if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
-    return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
-  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
-  if (workspace_bytes < need)
-    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 16)
-    return fail(PALU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  AppendParams p{};
-  p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
-  p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
-  append_bind_workspace(p, workspace);
-  hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  return append(d, x, a_k, a_v, h_k, h_v, nullptr, nullptr, pos, workspace, workspace_bytes,
+                stream);
+}
+
+palu_status palu_latent_append_i8_workspace(const palu_append_desc* d, size_t* bytes) {
+  palu_status st = validate_append_i8(d);
+  if (st != PALU_OK) return st;
+  if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, true);
   return ok();
+}
+
+palu_status palu_latent_append_i8(const palu_append_desc* d, const void* x, const void* a_k,
+                                  const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
+                                  float* s_v, const int32_t* pos, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  palu_status st = validate_append_i8(d);
+  if (st != PALU_OK) return st;
+  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  return append(d, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
 }
 
 palu_status palu_profile_begin(int32_t max_records) {

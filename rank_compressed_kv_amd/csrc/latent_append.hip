@@ -15,6 +15,15 @@
 //   order, rounds (bf16: nearest, ties to even), writes row pos[b] of the
 //   cache and puts the counter back to zero for the next call.
 // The result does not depend on which workgroup arrives last.
+//
+// int8 cache (per-token quantisation of the latents, Palu author response to
+// reviewer Fsn9 on W1/W2): each cached row of r latents is stored as int8
+// codes with one fp32 scale, amax / 127, codes round(h * 127 / amax) (nearest,
+// ties to even; all in fp32). A row can span several column blocks, so the
+// column blocks' last arrivers hand the finished fp32 rows over once more:
+// they store them in the workspace and count themselves in the arrival
+// counter of each (matrix, group) row segment they cover; the last one of a
+// segment quantises it for every sequence and resets that counter.
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -49,7 +58,46 @@ __device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
 }
 __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T>
+// quantise the finished fp32 rows of segment j (matrix j / G, group j % G) of
+// every sequence into the int8 cache: one wave per sequence, four consecutive
+// latents per lane (r % 4 == 0)
+__device__ void quantize_segment(const AppendParams& p, int j, int wave, int lane) {
+  const int width = p.G * p.r;
+  const bool is_v = j >= p.G;
+  const int g = is_v ? j - p.G : j;
+  int8_t* h = static_cast<int8_t*>(is_v ? p.h_v : p.h_k);
+  float* sc = is_v ? p.s_v : p.s_k;
+  const int nq = p.r / 4;                              // float4 per row, <= 128
+  for (int b = wave; b < p.B; b += kThreads / 64) {
+    const int pos = p.pos[b];
+    if (pos < 0 || pos >= p.L) continue;
+    const float* src = p.rows + static_cast<size_t>(b) * 2 * width + static_cast<size_t>(j) * p.r;
+    float4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    if (lane < nq) v0 = *reinterpret_cast<const float4*>(src + 4 * lane);
+    if (lane + 64 < nq) v1 = *reinterpret_cast<const float4*>(src + 4 * (lane + 64));
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+    // correctly rounded fp32 divisions (the HIP default)
+    const float scale = amax > 0.f ? amax / 127.f : 0.f;
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    auto code = [&](float x) {
+      const float c = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+      return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
+    };
+    auto pack = [&](float4 v) {
+      return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
+    };
+    const size_t row = (static_cast<size_t>(b) * p.G + g) * p.L + pos;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(h + row * p.r);
+    if (lane < nq) dst[lane] = pack(v0);
+    if (lane + 64 < nq) dst[lane + 64] = pack(v1);
+    if (lane == 0) sc[row] = scale;
+  }
+}
+
+template <typename T, bool kQuant>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   const int width = p.G * p.r;                 // columns of one matrix
   const int tid = threadIdx.x;
@@ -167,43 +215,89 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
           }
         }
       }
-      const float r4[4] = {acc.x, acc.y, acc.z, acc.w};
+      if constexpr (kQuant) {
+        float* dst = p.rows + static_cast<size_t>(b) * prow + fcol;
+        store_coherent2(dst, acc.x, acc.y);
+        store_coherent2(dst + 2, acc.z, acc.w);
+      } else {
+        const float r4[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int col = fcol + e;
-        const bool v = col >= width;
-        const int cl = v ? col - width : col;
-        const int g = cl / p.r, k = cl % p.r;
-        T* h = static_cast<T*>(v ? p.h_v : p.h_k);
-        store_elem(h, ((static_cast<size_t>(b) * p.G + g) * p.L + pos) * p.r + k, r4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int col = fcol + e;
+          const bool v = col >= width;
+          const int cl = v ? col - width : col;
+          const int g = cl / p.r, k = cl % p.r;
+          T* h = static_cast<T*>(v ? p.h_v : p.h_k);
+          store_elem(h, ((static_cast<size_t>(b) * p.G + g) * p.L + pos) * p.r + k, r4[e]);
+        }
       }
     }
   }
   if (tid == 0) __hip_atomic_store(&p.counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (kQuant) {
+    // second hand-off: row segments j = column / r (matrix j / G, group j % G)
+    // overlapping this block; the rows are complete at device scope before
+    // the segment counters count this block
+    __shared__ int seg_last[kCols + 1];
+    const int j0 = cb0 / p.r, j1 = (min(cb0 + kCols, 2 * width) - 1) / p.r;
+    wait_stores_complete();
+    __syncthreads();
+    for (int j = j0 + tid; j <= j1; j += kThreads) {
+      const int blocks = ((j + 1) * p.r - 1) / kCols - (j * p.r) / kCols + 1;
+      seg_last[j - j0] = __hip_atomic_fetch_add(&p.seg_counters[j], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == blocks - 1;
+    }
+    __syncthreads();
+    bool any = false;
+    for (int j = j0; j <= j1; ++j) any |= seg_last[j - j0] != 0;
+    if (!any) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int j = j0; j <= j1; ++j) {
+      if (!seg_last[j - j0]) continue;
+      quantize_segment(p, j, tid / 64, tid % 64);
+      if (tid == 0)
+        __hip_atomic_store(&p.seg_counters[j], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
-size_t counter_bytes(int G, int r) {
+size_t align_counters(size_t n) {
+  return (n * sizeof(int32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+}
+// counter area: one per column block, then (int8 cache) one per row segment
+size_t counter_bytes(int G, int r, bool quant) {
   const size_t blocks = (2 * static_cast<size_t>(G) * r + kCols - 1) / kCols;
-  return (blocks * sizeof(int32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+  return align_counters(blocks) + (quant ? align_counters(2 * static_cast<size_t>(G)) : 0);
 }
 
 }  // namespace
 
-size_t append_workspace_bytes(int B, int dm, int G, int r) {
+size_t append_workspace_bytes(int B, int dm, int G, int r, bool quant) {
   const size_t nks = (dm + kRows - 1) / kRows;
-  return counter_bytes(G, r) + nks * B * 2 * size_t(G) * r * sizeof(float);
+  const size_t row = 2 * size_t(G) * r * sizeof(float);
+  return counter_bytes(G, r, quant) + nks * B * row + (quant ? B * row : 0);
 }
 
 void append_bind_workspace(AppendParams& p, void* workspace) {
-  p.counters = static_cast<int32_t*>(workspace);
-  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p.G, p.r));
+  char* w = static_cast<char*>(workspace);
+  const size_t blocks = (2 * static_cast<size_t>(p.G) * p.r + kCols - 1) / kCols;
+  p.counters = reinterpret_cast<int32_t*>(w);
+  p.seg_counters = p.quant ? reinterpret_cast<int32_t*>(w + align_counters(blocks)) : nullptr;
+  p.part = reinterpret_cast<float*>(w + counter_bytes(p.G, p.r, p.quant != 0));
+  const size_t nks = (p.dm + kRows - 1) / kRows;
+  p.rows = p.quant ? p.part + nks * p.B * 2 * size_t(p.G) * p.r : nullptr;
 }
 
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
   const int cols = 2 * p.G * p.r;
   const dim3 grid((cols + kCols - 1) / kCols, (p.dm + kRows - 1) / kRows);
-  if (dtype == 0) append_kernel<float><<<grid, kThreads, 0, st>>>(p);
-  else append_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
+  if (p.quant) {
+    if (dtype == 0) append_kernel<float, true><<<grid, kThreads, 0, st>>>(p);
+    else append_kernel<uint16_t, true><<<grid, kThreads, 0, st>>>(p);
+  } else {
+    if (dtype == 0) append_kernel<float, false><<<grid, kThreads, 0, st>>>(p);
+    else append_kernel<uint16_t, false><<<grid, kThreads, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 

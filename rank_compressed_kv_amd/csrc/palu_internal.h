@@ -48,6 +48,12 @@ struct AppendParams {
   int32_t* counters;  // one arrival counter per 128-column block; zero between calls
   float* part;        // [ceil(dm/128), B, 2*G*r] fp32 row-slice partial sums
   int32_t B, dm, G, r, L;
+  // int8 cache (h_k, h_v int8 codes): per-row scales and the second hand-off
+  int32_t quant;
+  float* s_k;         // [B, G, L]
+  float* s_v;
+  int32_t* seg_counters;  // one per (matrix, group) row segment; zero between calls
+  float* rows;        // [B, 2*G*r] fp32 finished latent rows
 };
 
 // Kernel variants of the context-split decode step.
@@ -74,8 +80,9 @@ int reconstruct_waves_per_wg(int r, int s);
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
-size_t append_workspace_bytes(int B, int dm, int G, int r);
-void append_bind_workspace(AppendParams& p, void* workspace);   // sets counters, part
+size_t append_workspace_bytes(int B, int dm, int G, int r, bool quant);
+// sets counters, part (and, with p.quant, seg_counters and rows)
+void append_bind_workspace(AppendParams& p, void* workspace);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu

@@ -210,6 +210,53 @@ def test_append_validation(lib):
                                   misaligned, need, None) == P.PALU_ERR_WORKSPACE
 
 
+def test_append_i8_validation(lib):
+    """The quantised cache write: the append checks, rank % 4, NULL scales,
+    4-byte aligned caches, and a workspace with a second counter area and the
+    finished rows."""
+    fake = ctypes.c_void_p(0x1000)
+    good = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
+                         dtype=P.PALU_BF16)
+    big = 1 << 40
+
+    def call(d, *ptrs, nbytes=big):
+        ptrs = [fake if p is True else p for p in ptrs]
+        return lib.palu_latent_append_i8(ctypes.byref(d), *ptrs, nbytes, None)
+
+    bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
+           (dict(n_groups=4, rank=6), P.PALU_ERR_SHAPE),        # G*r % 8 == 0, r % 4 != 0
+           (dict(dtype=3), P.PALU_ERR_UNSUPPORTED)]
+    for kw, status in bad:
+        d = P.AppendDesc(**{**{f: getattr(good, f) for f, _ in P.AppendDesc._fields_}, **kw})
+        assert call(d, *([True] * 9)) == status
+        n = ctypes.c_size_t(0)
+        assert lib.palu_latent_append_i8_workspace(ctypes.byref(d), ctypes.byref(n)) == status
+    for i in range(9):
+        ptrs = [True] * 9
+        ptrs[i] = None
+        assert call(good, *ptrs) == P.PALU_ERR_NULL, i
+    need = P.palu_latent_append_i8_workspace(good)
+    # column-block counters (256 B), row-segment counters (256 B), the
+    # partials, then the finished fp32 rows [B, 2*G*r]
+    assert need == 256 + 256 + 32 * 8 * 1024 * 4 + 8 * 1024 * 4
+    assert call(good, *([True] * 9), nbytes=need - 1) == P.PALU_ERR_WORKSPACE
+    odd = ctypes.c_void_p(0x1002)
+    assert call(good, True, True, True, odd, True, True, True, True, True) == P.PALU_ERR_SHAPE
+    assert call(good, *([True] * 8), ctypes.c_void_p(0x1008)) == P.PALU_ERR_WORKSPACE
+
+
+def test_only_the_c_abi_is_exported(lib):
+    """Every function the library exports is one the header declares."""
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"]}
+    assert funcs == set(_header_functions())
+
+
 def test_profile_calls_validate(lib):
     assert lib.palu_profile_end(None, None) == P.PALU_ERR_UNSUPPORTED
     assert lib.palu_profile_begin(0) == P.PALU_ERR_SHAPE

@@ -127,3 +127,144 @@ def test_int8_matches_bf16_path_on_exact_cache():
     torch.cuda.synchronize()
     assert_close(a, b.cpu().numpy().astype(np.float64), max_abs=2e-3, rel_l2=5e-4,
                  what="int8 vs bf16 path")
+
+
+# ------------------------------------------------------ quantised cache write ---
+
+APPEND = {
+    "r256_g2": W.CONFIGS[3].scaled(batch=4, max_ctx=64, ragged=None),       # a row spans 2 blocks
+    "r256_g8": W.CONFIGS[2].scaled(batch=3, max_ctx=32, ragged=None),
+    "r128": W.CONFIGS[4].scaled(max_ctx=48, ragged=None),                   # one block per row
+    "r64": W.CONFIGS[3].scaled(n_groups=4, rank=64, batch=2, max_ctx=32, seed=81),
+    "r96": W.CONFIGS[3].scaled(n_groups=4, rank=96, batch=2, max_ctx=32, seed=82),  # straddles
+    "r32_f32": W.CONFIGS[1].scaled(batch=3, max_ctx=16, ragged=None),       # fp32 inputs
+}
+
+
+def _code_bounds(e, E, amax_lo, amax_hi):
+    """Range of codes rint(S * fl(127 / A)) over every fp32 sum S within E of
+    the exact value e and every row maximum A in [amax_lo, amax_hi] (rounding
+    is monotone, so the corners bound it); returns (lo, hi) codes."""
+    eps = 2.0 ** -23
+    inv_lo = 127.0 / amax_hi * (1 - eps)
+    inv_hi = 127.0 / amax_lo * (1 + eps) if amax_lo > 0 else np.inf
+    corners = np.stack([(e - E) * inv_lo, (e - E) * inv_hi, (e + E) * inv_lo, (e + E) * inv_hi])
+    with np.errstate(invalid="ignore"):
+        lo = np.nanmin(corners, 0) * (1 - np.sign(np.nanmin(corners, 0)) * eps)
+        hi = np.nanmax(corners, 0) * (1 + np.sign(np.nanmax(corners, 0)) * eps)
+    return np.clip(np.rint(lo), -127, 127), np.clip(np.rint(hi), -127, 127)
+
+
+@pytest.mark.parametrize("name", sorted(APPEND))
+def test_int8_append(name):
+    """h = x A quantised per row: the codes and scales equal the oracle's
+    (quantisation of the exact row rounded to fp32) except where the exact
+    value sits within the fp32 summation error of a decision boundary, and
+    there they lie between the decisions at exact -/+ that error; rows other
+    than pos[b] are untouched; a zero x row stores scale 0 and codes 0."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = APPEND[name]
+    t = W.generate(cfg, parts=("decode", "append", "i8"))
+    x = t["x"].copy()
+    x[0] = 0                                         # all-zero latent row for b = 0
+    hk, hv = dev(t["k_i8"]), dev(t["v_i8"])
+    sk, sv = dev(t["sk"]), dev(t["sv"])
+    before = [c.clone() for c in (hk, hv, sk, sv)]
+    print(f"[int8 append] {name} pos={t['pos'].tolist()}", flush=True)
+    P.latent_append_i8(dev(x), dev(t["a_k"]), dev(t["a_v"]), hk, hv, sk, sv, dev(t["pos"]))
+    torch.cuda.synchronize()
+    G, r, dm = cfg.n_groups, cfg.rank, cfg.d_model
+    mism = tot = 0
+    for codes_d, scales_d, a in ((hk, sk, t["a_k"]), (hv, sv, t["a_v"])):
+        codes, scales = codes_d.cpu().numpy(), scales_d.cpu().numpy()
+        h64 = O.latent_project(x, a).reshape(cfg.batch, G, r)
+        # bound on |fp32 sum - exact| for any summation order
+        E = (np.abs(O.to_f64(x))[:, :, None] * np.abs(O.to_f64(a))[None]).sum(1)
+        E = E.reshape(cfg.batch, G, r) * dm * 2.0 ** -24
+        for b, pos in enumerate(t["pos"]):
+            wc, ws = O.append_rows_i8(h64[b])            # [G, r], [G]
+            gc, gs = codes[b, :, pos, :].astype(np.int64), scales[b, :, pos]
+            if b == 0:
+                assert np.all(gc == 0) and np.all(gs == 0.0)
+                continue
+            mism += int(np.sum(gc != wc))
+            tot += gc.size
+            for g in range(G):
+                e, eb = h64[b, g], E[b, g]
+                amax_lo = max(float(np.max(np.abs(e) - eb)), 0.0)
+                amax_hi = float(np.max(np.abs(e) + eb))
+                assert amax_lo / 127 * (1 - 2.0 ** -23) <= gs[g] <= amax_hi / 127 * (1 + 2.0 ** -23)
+                if np.all(gc[g] == wc[g]) and gs[g] == ws[g]:
+                    continue
+                lo, hi = _code_bounds(e, eb, amax_lo, amax_hi)
+                assert np.all((gc[g] >= lo) & (gc[g] <= hi)), (b, g)
+                assert np.max(np.abs(gc[g] - wc[g])) <= 1
+    assert mism <= 0.01 * tot
+    # every other row is untouched
+    for got, old in zip((hk, hv, sk, sv), before):
+        g, o = got.cpu().clone(), old.cpu().clone()
+        for b, pos in enumerate(t["pos"]):
+            g[b, :, int(pos)] = 0
+            o[b, :, int(pos)] = 0
+        assert torch.equal(g, o)
+
+
+def test_int8_append_workspace_reuse_and_skipped_rows():
+    """Both counter areas return to zero after every call, so one workspace
+    serves call after call with results identical to a fresh one; positions
+    outside [0, L) are skipped."""
+    import torch
+    import rank_compressed_kv_amd as P
+    ws = None
+    for i, batch in enumerate((4, 2, 4)):
+        cfg = W.CONFIGS[3].scaled(batch=batch, max_ctx=16, seed=110 + i)
+        t = W.generate(cfg, parts=("decode", "append", "i8"))
+        pos = t["pos"].copy()
+        pos[-1] = [-1, 16, 5][i]
+        x, ak, av, dpos = dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), dev(pos)
+        bufs = [dev(t[k]) for k in ("k_i8", "v_i8", "sk", "sv")]
+        fresh = [b.clone() for b in bufs]
+        orig = [b.clone() for b in bufs]
+        desc = P.append_desc(batch=batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
+                             rank=cfg.rank, max_ctx=16, dtype=P.PALU_BF16)
+        if ws is None:
+            ws = torch.zeros(P.palu_latent_append_i8_workspace(desc), dtype=torch.uint8,
+                             device="cuda")
+        P.palu_latent_append_i8(desc, x, ak, av, *bufs, dpos, ws)
+        P.latent_append_i8(x, ak, av, *fresh, dpos)
+        torch.cuda.synchronize()
+        for a, b in zip(bufs, fresh):
+            assert torch.equal(a, b)
+        assert int(ws[:512].count_nonzero()) == 0
+        if not 0 <= pos[-1] < 16:
+            for a, o in zip(bufs, orig):
+                assert torch.equal(a[-1], o[-1])
+
+
+def test_int8_append_then_decode():
+    """A token written by the quantised append is read back by the int8 decode
+    like any other row: attention over the updated cache matches the oracle on
+    the cache with the oracle's own quantised rows at pos (a code one step off
+    near a rounding boundary moves the output far less than the tolerance)."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = W.CONFIGS[3].scaled(batch=2, max_ctx=300, ragged=None, seed=90)
+    t = W.generate(cfg, parts=("decode", "append", "i8"))
+    pos = np.array([299, 150], dtype=np.int32)
+    lens = pos + 1
+    bufs = [dev(t[k]) for k in ("k_i8", "v_i8", "sk", "sv")]
+    P.latent_append_i8(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), *bufs, dev(pos))
+    out = P.decode_attention_i8(dev(t["q"]), *bufs, dev(t["b_k"]), dev(t["b_v"]), dev(lens),
+                                n_kv_heads=cfg.n_kv_heads)
+    torch.cuda.synchronize()
+    G, r = cfg.n_groups, cfg.rank
+    caches = {}
+    for key, codes, scales, a in (("k", "k_i8", "sk", "a_k"), ("v", "v_i8", "sv", "a_v")):
+        c, sc = t[codes].copy(), t[scales].copy()
+        h64 = O.latent_project(t["x"], t[a]).reshape(cfg.batch, G, r)
+        for b, p_ in enumerate(pos):
+            c[b, :, p_], sc[b, :, p_] = O.append_rows_i8(h64[b])
+        caches[key] = O.dequantize_rows_i8(c, sc)
+    want = O.decode_attention(t["q"], caches["k"], caches["v"], t["b_k"], t["b_v"], lens)
+    assert_close(out.cpu().numpy().astype(np.float64), want, what="append then decode")
