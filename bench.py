@@ -55,6 +55,8 @@ def parse():
                     help="skip the second timed loop with events around the main kernel")
     ap.add_argument("--no-full-rank", action="store_true",
                     help="skip the uncompressed baseline (full bf16 K and V)")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the int8-latent absorbed step")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the head-grouping sweep (s = 1, 2, 4, 8 KV heads per "
                          "group at 75%% key compression) and add it to the JSON line")
@@ -98,12 +100,11 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
         P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, aws, stream)
         P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
 
-    # the first step's output is kept for the sampled parity check; the append
-    # writes row len-1 of copy 0 (same bits as the generator's row replaced)
+    # the first step's output is kept for the sampled parity check (the append
+    # has written row len-1 of copy 0)
     step(0)
     torch.cuda.synchronize()
     first_out = out.clone()
-    first_hk, first_hv = caches[0][0][:, :, :, :], caches[0][1]
     for i in range(args.warmup):
         step(i + 1)
     torch.cuda.synchronize()
@@ -138,8 +139,68 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     return dict(ms_per_step=total_ms / args.steps, kernel_ms=kern_ms / max(1, kern_n),
                 decode_ms=decode_ms / args.steps,
                 kernel=kname, n_split=n_split, split_tokens=split_tokens,
-                out=first_out.cpu().numpy(), hk_row=first_hk, hv_row=first_hv, pos=pos,
-                caches=caches)
+                out=first_out.cpu().numpy())
+
+
+def time_int8(torch, P, W, cfg, t, args):
+    """The absorbed step over an int8 latent cache (codes plus one fp32 scale
+    per row): quantised append, then decode. Same shape, same timing loops."""
+    ti = W.generate(cfg, parts=("i8",))
+    q, bk, bv = dev(torch, t["q"]), dev(torch, t["b_k"]), dev(torch, t["b_v"])
+    lens = dev(torch, t["lens"])
+    x, ak, av = dev(torch, t["x"]), dev(torch, t["a_k"]), dev(torch, t["a_v"])
+    pos = (lens - 1).to(torch.int32).contiguous()
+    from rank_compressed_kv_amd.layout import pack_i8_cache
+    bufs0 = [dev(torch, pack_i8_cache(ti["k_i8"], "k")), dev(torch, pack_i8_cache(ti["v_i8"], "v")),
+             dev(torch, ti["sk"]), dev(torch, ti["sv"])]
+    per_copy = sum(b.numel() * b.element_size() for b in bufs0)
+    n_copies = min(16, max(1, int(math.ceil(ROTATE_BYTES / per_copy))))
+    caches = [bufs0] + [[b.clone() for b in bufs0] for _ in range(n_copies - 1)]
+    desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
+                       max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, mode="absorbed",
+                       split_tokens=args.split_tokens)
+    adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=P.PALU_BF16)
+    ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    aws = torch.zeros(P.palu_latent_append_i8_workspace(adesc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def decode(i):
+        hk, hv, sk, sv = caches[i % n_copies]
+        P.palu_decode_attn_i8(desc, q, hk, hv, sk, sv, bk, bv, lens, out, ws, stream)
+
+    def step(i):
+        hk, hv, sk, sv = caches[i % n_copies]
+        P.palu_latent_append_i8(adesc, x, ak, av, hk, hv, sk, sv, pos, aws, stream)
+        decode(i)
+
+    step(0)
+    torch.cuda.synchronize()
+    first = out.clone()
+    for i in range(args.warmup):
+        step(i + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("step", step), ("decode", decode)):
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    kern_ms, kern_n = float("nan"), 0
+    if not args.no_kernel_events:
+        P.palu_profile_begin(args.steps)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        kern_ms, kern_n = P.palu_profile_end()
+    del caches
+    return dict(ms_per_step=res["step"], decode_ms=res["decode"],
+                kernel_ms=kern_ms / max(1, kern_n), out=first.cpu().numpy(), ti=ti)
 
 
 def time_full_rank(torch, P, W, cfg, t, args):
@@ -268,22 +329,37 @@ def granularity_sweep(torch, P, W, cfg, args):
     return rows
 
 
+def oracle_appended(O, cfg, t, caches):
+    """The caches as the oracle has them after one step's append: row len-1 of
+    each sequence replaced by the oracle's own cache write of x A (bf16: the
+    exact row rounded to fp32, then to bf16; int8: its quantisation)."""
+    B, G, r = cfg.batch, cfg.n_groups, cfg.rank
+    out = []
+    for cache, a in zip(caches, ("a_k", "a_v")):
+        h64 = O.latent_project(t["x"], t[a]).reshape(B, G, r)
+        if isinstance(cache, tuple):                    # (int8 codes, scales)
+            codes, scales = cache[0].copy(), cache[1].copy()
+            for b in range(B):
+                p = int(t["lens"][b]) - 1
+                if p >= 0:
+                    codes[b, :, p], scales[b, :, p] = O.append_rows_i8(h64[b])
+            out.append((codes, scales))
+            continue
+        c = cache.copy()
+        for b in range(B):
+            p = int(t["lens"][b]) - 1
+            if p >= 0:
+                c[b, :, p] = (O.append_rows_bf16(h64[b]) if cfg.dtype == "bf16"
+                              else h64[b].astype(np.float32))
+        out.append(c)
+    return out
+
+
 def sampled_parity(O, cfg, t, res, mode, pairs):
-    """Compare sampled (b, h) outputs of the first timed step with the oracle.
-    The oracle sees the cache after the step's append (row len-1 rewritten)."""
-    import torch
+    """Compare sampled (b, h) outputs of the first timed step with the oracle
+    on the cache after its own append of the step's token."""
     theta = cfg.rope_theta if mode == "reconstruct" else 0.0
-    hk = t["h_k"].copy()
-    hv = t["h_v"].copy()
-    hk_dev, hv_dev = res["caches"][0]
-    for b in range(cfg.batch):
-        p = int(t["lens"][b]) - 1
-        if cfg.dtype == "bf16":
-            hk[b, :, p] = hk_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
-            hv[b, :, p] = hv_dev[b, :, p].view(torch.int16).cpu().numpy().view(np.uint16)
-        else:
-            hk[b, :, p] = hk_dev[b, :, p].cpu().numpy()
-            hv[b, :, p] = hv_dev[b, :, p].cpu().numpy()
+    hk, hv = oracle_appended(O, cfg, t, (t["h_k"], t["h_v"]))
     want = O.decode_attention(t["q"], hk, hv, t["b_k"], t["b_v"], t["lens"], rope_theta=theta,
                               select=pairs)
     got = res["out"].astype(np.float64)
@@ -394,8 +470,6 @@ def main():
     for mode in modes:
         parity[mode] = sampled_parity(O, cfg, t, results[mode], mode, pairs)
     main_res = results[args.mode]
-    for r in results.values():
-        r.pop("caches")
     full = None
     if not args.no_full_rank and cfg.dtype == "bf16":
         fr = time_full_rank(torch, P, W, cfg, t, args)
@@ -412,6 +486,36 @@ def main():
                                                       if dec_ms else None)}
         print(f"[bench] full-rank baseline: {fr['ms'] * 1e3:.1f} us/call, kernel "
               f"{fr['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    int8 = None
+    if not args.no_int8 and cfg.dtype == "bf16" and "absorbed" in results and \
+            cfg.rank in (64, 128, 256):
+        ri = time_int8(torch, P, W, cfg, t, args)
+        ti = ri.pop("ti")
+        (ck, sk), (cv, sv) = oracle_appended(O, cfg, t, ((ti["k_i8"], ti["sk"]),
+                                                          (ti["v_i8"], ti["sv"])))
+        # the oracle dequantises only the sampled sequences
+        dmax, num, den = 0.0, 0.0, 0.0
+        for b, h in pairs:
+            w = O.decode_attention(t["q"][b:b + 1], O.dequantize_rows_i8(ck[b:b + 1], sk[b:b + 1]),
+                                   O.dequantize_rows_i8(cv[b:b + 1], sv[b:b + 1]), t["b_k"],
+                                   t["b_v"], t["lens"][b:b + 1], select=[(0, h)])[0, h]
+            dd = ri["out"][b, h].astype(np.float64) - w
+            dmax, num, den = max(dmax, float(np.abs(dd).max())), num + float(dd @ dd), den + float(w @ w)
+        i8_bytes = int(np.sum(t["lens"], dtype=np.int64)) * cfg.n_groups * (2 * cfg.rank + 8)
+        kus = ri["kernel_ms"] * 1e3
+        int8 = {"us_per_step": round(ri["ms_per_step"] * 1e3, 2),
+                "us_per_decode_call": round(ri["decode_ms"] * 1e3, 2),
+                "kernel_us": _r(kus, 2),
+                "algorithmic_bytes": i8_bytes,
+                "GBps_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9, 1),
+                "frac_hbm_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "step_speedup_vs_bf16": round(results["absorbed"]["ms_per_step"]
+                                              / ri["ms_per_step"], 3),
+                "sampled_parity_max_abs": dmax,
+                "sampled_parity_rel_l2": math.sqrt(num / den) if den > 0 else None}
+        print(f"[bench] int8 absorbed: {ri['ms_per_step'] * 1e3:.1f} us/step, kernel "
+              f"{kus:.1f} us", file=sys.stderr, flush=True)
 
     ms = main_res["ms_per_step"]
     steps_s = 1e3 / ms
@@ -441,6 +545,7 @@ def main():
         "latent_pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "roofline": roofline(cfg, t, args.mode, main_res, lat_bytes, kern_gbs, traffic),
         "full_rank_baseline": full,
+        "int8_latents": int8,
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                       "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
                       "kernel_us": _r(r["kernel_ms"] * 1e3, 2), "kernel": r["kernel"],

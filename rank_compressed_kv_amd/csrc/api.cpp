@@ -264,7 +264,9 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
   if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
   switch (pl.kernel) {
-    case SplitKernel::kAbsorbedMfma: e = launch_split_absorbed_mfma(p, s); break;
+    case SplitKernel::kAbsorbedMfma:
+      e = p.latent_i8 ? launch_split_absorbed_i8(p, s) : launch_split_absorbed_mfma(p, s);
+      break;
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
@@ -298,11 +300,18 @@ palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const
   palu_status st = validate_attn(desc);
   if (st != PALU_OK) return st;
   if (desc->mode != PALU_MODE_ABSORBED || desc->dtype != PALU_BF16 ||
-      !absorbed_i8_supported(shape_params(desc), desc->dtype))
+      (desc->rank != 64 && desc->rank != 128 && desc->rank != 256))
     return fail(PALU_ERR_UNSUPPORTED,
                 "int8 latents need mode ABSORBED, dtype BF16 and rank 64, 128 or 256 "
                 "(got mode %d, dtype %d, rank %d)", desc->mode, desc->dtype, desc->rank);
+  if (desc->max_ctx % 32)
+    return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", desc->max_ctx);
+  if (!absorbed_i8_supported(shape_params(desc), desc->dtype))
+    return fail(PALU_ERR_UNSUPPORTED, "int8 latents: combination not provided");
   if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(h_k) | reinterpret_cast<uintptr_t>(h_v) |
+       reinterpret_cast<uintptr_t>(s_k) | reinterpret_cast<uintptr_t>(s_v)) % 16)
+    return fail(PALU_ERR_SHAPE, "int8 caches and scales must be 16-byte aligned");
   return decode(desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace,
                 workspace_bytes, stream);
 }
@@ -326,7 +335,10 @@ palu_status validate_append(const palu_append_desc* d) {
 palu_status validate_append_i8(const palu_append_desc* d) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
-  if (d->rank % 4) return fail(PALU_ERR_SHAPE, "int8 cache needs rank %% 4 == 0 (got %d)", d->rank);
+  if (d->rank != 64 && d->rank != 128 && d->rank != 256)
+    return fail(PALU_ERR_UNSUPPORTED, "int8 cache needs rank 64, 128 or 256 (got %d)", d->rank);
+  if (d->max_ctx % 32)
+    return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", d->max_ctx);
   return PALU_OK;
 }
 

@@ -1,0 +1,354 @@
+// Context-split decode kernel for the absorbed-key mode over an int8 latent
+// cache (per-token quantisation of the latents, Palu author response to
+// reviewer Fsn9 on W1/W2: codes with one fp32 scale per cached row, h = code *
+// scale), on the gfx950 matrix cores.
+//
+// The scores and the value sum are those of the bf16 kernel (absorbed keys:
+// q~ = q B_k^T scored against the key latents, value latents summed with the
+// weights, B_v applied in the merge); what differs is the cache and the data
+// path:
+//   - the int8 cache is stored in 32-token blocks whose byte order is that of
+//     the MFMA operands (see i8_cache_layout below), so every 16-byte load of
+//     a lane holds exactly the operand bytes that lane needs: no LDS staging,
+//     no gathers, fully coalesced 1 KiB per load instruction;
+//   - codes are widened to fp16 in registers (exact for |code| <= 127) and
+//     multiplied on fp16 MFMAs, 16x16x32 for the scores (16 tokens x 16 heads
+//     over 32 latents) and for the values (r x 16 heads over 32 tokens);
+//   - a block's key scales multiply its scores, its value scales fold into the
+//     weights (p_t s_t; the running sum l keeps p_t). q~ (hi + lo in fp16) is
+//     divided per head by a power of two near its largest entry and the value
+//     scales by the split's largest one, so fp16 operands stay in range
+//     whatever the magnitudes; both are undone in fp32.
+// One workgroup owns one (batch, group, context split) and 16 query heads;
+// its four waves take the split's 32-token blocks round-robin, each with the
+// next block's loads in flight (two register sets, alternating) while the
+// current one is multiplied, and combine their softmax states in LDS at the
+// end. Blocks are read whole: rows past the length inside the last block are
+// masked (their codes are finite whatever they hold; their scales are
+// replaced by 0 before use), and no byte outside the cache is touched.
+#include <math.h>
+
+#include "device_util.h"
+#include "palu_internal.h"
+
+namespace palu {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;        // one per SIMD
+constexpr int kBlock = 32;       // tokens per cache block and per wave step
+constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
+
+// x ~ hi + lo in two fp16 (nearest even each): the MFMA operand bits
+__device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
+  const _Float16 h = static_cast<_Float16>(x);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x - static_cast<float>(h)));
+}
+
+// four int8 codes -> four fp16 values, exactly: with u = code + 128 (the byte
+// XOR 0x80), the fp16 with bits 0x64uu is 1024 + u; one byte permute per pair
+// of codes and one packed fp16 subtraction of 1152 give the codes
+__device__ __forceinline__ uint2 i8x4_to_f16x4(uint32_t w) {
+  const uint32_t x = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+  const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  const half2v a = __builtin_bit_cast(half2v, lo) - bias;
+  const half2v c = __builtin_bit_cast(half2v, hi) - bias;
+  return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+}
+// eight codes (two words) -> one 8 x fp16 MFMA operand
+__device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
+  const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
+  return uint4{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] fp16 bits; rows
+// padded by 8 elements so the 16 heads' 16-byte reads spread over the banks
+template <int R>
+struct Smem {
+  uint16_t q[2][16][R + 8];
+  float qc[16];              // power of two each head's q~ was divided by
+  float svmax[kWaves];       // each wave's largest value scale
+  float acc[kWaves / 2][4 * (R / 16)][64];   // softmax states (final merge)
+  float m[kWaves / 2][64], l[kWaves / 2][64];
+};
+
+template <int R>
+struct State {
+  floatx4 acc[R / 16];   // U^T: r = 16*rb + 4*(lane/16) + i, head lane%16
+  float m;               // stored running max (log2 units) of head lane%16
+  float l;               // this lane's share of the running sum
+};
+
+// One cache block in registers: R/32 16-byte words of each matrix (word i of
+// lane l is bytes [1024 i + 16 l, +16) of the block) and the key and value
+// scales of the lane's eight tokens 4*(l/16) + i and 16 + 4*(l/16) + i.
+template <int R>
+struct Block {
+  typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
+  u32v k, v;
+  floatx4 sk0, sk1, sv0, sv1;
+};
+
+template <int R, bool kShared>
+__global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(DecodeParams p) {
+  const int nslice = (p.nq + 15) / 16;
+  const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
+  if (!un.live) return;
+  const int split = un.split, g = un.g, b = un.b;
+  const int hq0 = un.hs * 16;                            // first query head of the slice
+  const int nqs = min(16, p.nq - hq0);                   // its query heads
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ln = lane & 15, kb = lane >> 4;
+  const int n = clamp_len(p.lens, b, p.L);
+  const int s0 = split * p.split_tokens;                 // a multiple of 64
+  if (s0 >= n) return;                                   // whole workgroup
+  const int t1 = min(n, s0 + p.split_tokens);
+
+  __shared__ Smem<R> sm;
+  const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
+  const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
+  {
+    // the split's largest value scale (scales are >= 0)
+    float smax = 0.f;
+    for (int t = s0 + static_cast<int>(threadIdx.x); t < t1; t += 64 * kWaves)
+      smax = fmaxf(smax, p.s_v[row0 + t]);
+    // one wave per head: q~ / 2^e with 2^e <= max |q~_h| < 2^(e+1), hi + lo
+    for (int hd = wave; hd < 16; hd += kWaves) {
+      float x[R / 64];
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < R / 64; ++j) {
+        x[j] = hd < nqs ? qrow[hd * R + lane + 64 * j] : 0.f;
+        amax = fmaxf(amax, fabsf(x[j]));
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
+      const float c = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
+      const float inv = 1.f / c;                     // exact: c is a power of two
+#pragma unroll
+      for (int j = 0; j < R / 64; ++j)
+        split_f16(x[j] * inv, sm.q[0][hd][lane + 64 * j], sm.q[1][hd][lane + 64 * j]);
+      if (lane == 0) sm.qc[hd] = c;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
+    if (lane == 0) sm.svmax[wave] = smax;
+  }
+  __syncthreads();
+  // scores are multiplied by qc * s_k, value weights by s_v / vref and the
+  // partial sums by vref
+  const float qc = sm.qc[ln];
+  float vref = sm.svmax[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) vref = fmaxf(vref, sm.svmax[w]);
+  if (!(vref > 0.f && vref < INFINITY)) vref = 1.f;
+  const float vinv = 1.f / vref;
+
+  State<R> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * R;
+  const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * R;
+  const int nblk = (t1 - s0 + kBlock - 1) / kBlock;
+  const int mine = (nblk - wave + kWaves - 1) / kWaves;   // blocks of this wave, may be 0
+  auto tok_of = [&](int j) { return s0 + kBlock * (wave + kWaves * j); };
+
+  auto fetch = [&](Block<R>& x, int t0) {
+    const size_t base = static_cast<size_t>(t0) * R + lane * 16;   // t0 % 32 == 0
+#pragma unroll
+    for (int i = 0; i < R / 32; ++i) {
+      const uint4 a = load_tile16<kShared>(Hk + base + i * 1024);
+      const uint4 c = load_tile16<kShared>(Hv + base + i * 1024);
+      x.k[4 * i] = a.x; x.k[4 * i + 1] = a.y; x.k[4 * i + 2] = a.z; x.k[4 * i + 3] = a.w;
+      x.v[4 * i] = c.x; x.v[4 * i + 1] = c.y; x.v[4 * i + 2] = c.z; x.v[4 * i + 3] = c.w;
+    }
+    const size_t srow = row0 + t0 + 4 * kb;              // 16-byte aligned
+    const float4 a0 = *reinterpret_cast<const float4*>(p.s_k + srow);
+    const float4 a1 = *reinterpret_cast<const float4*>(p.s_k + srow + 16);
+    const float4 c0 = *reinterpret_cast<const float4*>(p.s_v + srow);
+    const float4 c1 = *reinterpret_cast<const float4*>(p.s_v + srow + 16);
+    x.sk0 = floatx4{a0.x, a0.y, a0.z, a0.w};
+    x.sk1 = floatx4{a1.x, a1.y, a1.z, a1.w};
+    x.sv0 = floatx4{c0.x, c0.y, c0.z, c0.w};
+    x.sv1 = floatx4{c1.x, c1.y, c1.z, c1.w};
+  };
+
+  auto compute = [&](const Block<R>& x, int t0) {
+    // q~ is read from LDS again for every block: held in registers across the
+    // loop it would take 128 of them at r = 256 (a compiler-only barrier keeps
+    // the reads inside)
+    asm volatile("" ::: "memory");
+    // scores of the two 16-token halves: S^T[16 tok x 16 heads], key chunk c
+    // of half h in word h*R/64 + c/2, bytes 8*(c%2) .. +8
+    floatx4 sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      floatx4 acc4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < R / 32; ++c) {
+        const int w = 4 * (h * (R / 64) + c / 2) + 2 * (c % 2);
+        const uint4 a = widen8(x.k[w], x.k[w + 1]);
+        const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[0][ln][32 * c + 8 * kb]);
+        const uint4 ql = *reinterpret_cast<const uint4*>(&sm.q[1][ln][32 * c + 8 * kb]);
+        acc4[2 * (c & 1)] = mfma(a, qh, acc4[2 * (c & 1)]);
+        acc4[2 * (c & 1) + 1] = mfma(a, ql, acc4[2 * (c & 1) + 1]);
+      }
+      sc[h] = (acc4[0] + acc4[2]) + (acc4[1] + acc4[3]);
+    }
+    sc[0] *= x.sk0 * qc;
+    sc[1] *= x.sk1 * qc;
+    floatx4 sv[2] = {x.sv0 * vinv, x.sv1 * vinv};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + 16 * h + 4 * kb + i >= t1) {
+          sc[h][i] = -INFINITY;
+          sv[h][i] = 0.f;
+        }
+    // online softmax over the block's 32 tokens of head ln
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > st.m + kLazy)) {
+      const float mn = fmaxf(st.m, mx);
+      const float alpha = exp2f(st.m - mn);
+      st.m = mn;
+      st.l *= alpha;
+#pragma unroll
+      for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= alpha;
+    }
+    // P^T operand: k-slot 8*kb + j is token 4*kb + j (j < 4) or 16 + 4*kb + j - 4
+    uint16_t ph[8], pl[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = exp2f(sc[h][i] - st.m);
+        st.l += pe;
+        split_f16(pe * sv[h][i], ph[4 * h + i], pl[4 * h + i]);
+      }
+    const uint4 bh = {ph[0] | (uint32_t(ph[1]) << 16), ph[2] | (uint32_t(ph[3]) << 16),
+                      ph[4] | (uint32_t(ph[5]) << 16), ph[6] | (uint32_t(ph[7]) << 16)};
+    const uint4 bl = {pl[0] | (uint32_t(pl[1]) << 16), pl[2] | (uint32_t(pl[3]) << 16),
+                      pl[4] | (uint32_t(pl[5]) << 16), pl[6] | (uint32_t(pl[7]) << 16)};
+    // values: U^T[16 rb .. +16, heads] += H_v^T[., 32 tokens] P^T; latent rows
+    // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
+#pragma unroll
+    for (int rb = 0; rb < R / 16; ++rb) {
+      const int w = 4 * (rb / 2) + 2 * (rb % 2);
+      const uint4 a = widen8(x.v[w], x.v[w + 1]);
+      st.acc[rb] = mfma(a, bh, st.acc[rb]);
+      st.acc[rb] = mfma(a, bl, st.acc[rb]);
+    }
+  };
+
+  if (mine > 0) {
+    Block<R> xa, xb;
+    fetch(xa, tok_of(0));
+    for (int j = 0; j < mine; j += 2) {
+      if (j + 1 < mine) fetch(xb, tok_of(j + 1));
+      compute(xa, tok_of(j));
+      if (j + 1 < mine) {
+        if (j + 2 < mine) fetch(xa, tok_of(j + 2));
+        compute(xb, tok_of(j + 1));
+      }
+    }
+  }
+
+  // merge the waves' states in LDS, halving the number of live states each
+  // round: waves [h, 2h) publish, waves [0, h) fold in the state of wave + h;
+  // a side that saw no token has m = -inf and weight 0
+#pragma unroll
+  for (int h = kWaves / 2; h >= 1; h /= 2) {
+    __syncthreads();
+    if (wave >= h && wave < 2 * h) {
+      const int w = wave - h;
+#pragma unroll
+      for (int rb = 0; rb < R / 16; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.acc[w][4 * rb + i][lane] = st.acc[rb][i];
+      sm.m[w][lane] = st.m;
+      sm.l[w][lane] = st.l;
+    }
+    __syncthreads();
+    if (wave < h) {
+      const float mo = sm.m[wave][lane];
+      const float M = fmaxf(st.m, mo);
+      const float a = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
+      const float c = mo == -INFINITY ? 0.f : exp2f(mo - M);
+      st.m = M;
+      st.l = st.l * a + sm.l[wave][lane] * c;
+#pragma unroll
+      for (int rb = 0; rb < R / 16; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st.acc[rb][i] = st.acc[rb][i] * a + sm.acc[wave][4 * rb + i][lane] * c;
+    }
+  }
+  if (wave > 0) return;
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (ln >= nqs) return;
+  const int head = g * p.nq + hq0 + ln;
+  const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
+  if (kb == 0) {
+    p.part_ml[slot * 2] = st.m;
+    p.part_ml[slot * 2 + 1] = l;
+  }
+  float* u = p.part_u + slot * R;
+#pragma unroll
+  for (int rb = 0; rb < R / 16; ++rb) {
+    const floatx4 v = st.acc[rb] * vref;
+    *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) = float4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+template <int R>
+hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
+  const int nslice = absorbed_head_slices(p.nq);
+  if (nslice == 1) {
+    split_absorbed_i8_kernel<R, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+  } else {
+    const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
+    if (ids == 0) return hipErrorInvalidValue;
+    split_absorbed_i8_kernel<R, true><<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool absorbed_i8_supported(const DecodeParams& p, int dtype) {
+  return dtype == 1 && (p.r == 64 || p.r == 128 || p.r == 256) && p.L % kBlock == 0;
+}
+
+hipError_t launch_split_absorbed_i8(const DecodeParams& p, hipStream_t st) {
+  switch (p.r) {
+    case 64: return launch_rank<64>(p, st);
+    case 128: return launch_rank<128>(p, st);
+    case 256: return launch_rank<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace palu

@@ -1,45 +1,38 @@
-// Context-split decode kernel for the absorbed-key mode on the gfx950 matrix
-// cores: bf16 latents, or int8 latents with one scale per cached row.
+// Context-split decode kernel for the absorbed-key mode, bf16 latents, on the
+// gfx950 matrix cores.
 //
 // Method (Palu author response on OpenReview, "Why Palu Requires Fewer Global
 // Memory Access" and the clarification of W1): without a rotary embedding the
 // reconstruction matrix of the keys moves onto the query, q~ = q B_k^T, so the
 // score of token t is <q~, h_k[t]> and no key is rebuilt; the value path sums
 // value latents with the attention weights and applies B_v later (merge pass).
-// The same kernel serves the uncompressed baseline (q~ = q, full K and V).
 //
-// One workgroup owns one (batch, group, context split) and 16 query heads of
-// the group (groups with more heads get further head slices, whose workgroups
-// read the same latents through one XCD's L2), so every latent byte is read
-// from HBM once. Its four waves take the split's 16-token tiles round-robin
-// (adjacent tiles stream together) and combine their softmax states in LDS at
-// the end. Per tile:
-//   scores  S^T[16 tok x 16 heads] = H_k[16 x r] * Q~^T, MFMA 16x16x32, q~
-//           split as hi + lo (two MFMAs, ~16 bits kept), read from LDS;
+// One workgroup owns one (batch, group, context split) and all of the group's
+// query heads (up to 16), so every latent byte is read from HBM exactly once.
+// Its four waves take the split's 16-token tiles round-robin (adjacent tiles
+// stream together, which measured ~13% faster than contiguous quarters per
+// wave) and combine their softmax states in LDS at the end. Per tile:
+//   scores  S^T[16 tok x 16 heads] = H_k[16 x r] * Q~^T, bf16 MFMA 16x16x32,
+//           q~ split as hi + lo bf16 (two MFMAs, ~16 bits kept), read from LDS;
 //   softmax online, base 2, per head, with a lazy running max (the stored max
 //           moves only when a tile exceeds it by kLazy, so most tiles skip the
 //           rescale; the result is exact either way);
-//   values  U^T[r x 16 heads] += H_v^T[r x 16 tok] * P^T, MFMA 16x16x16 with P
-//           split as hi + lo. The value latents are gathered from a
-//           wave-private LDS tile so each lane can take one latent column over
-//           four tokens (the MFMA contracts over tokens); groups of four rows
-//           are offset by 32 bytes so those gathers hit distinct banks.
-// bf16 latents use bf16 MFMAs. int8 latents (code times the row's scale) are
-// widened to fp16 (exact for |code| <= 127) as they are copied into the LDS
-// tiles and use fp16 MFMAs: a tile's key scales multiply its scores, its value
-// scales fold into the weights (p_t s_t), and the running sum l keeps p_t.
-// To keep fp16 operands in range whatever the magnitudes, each head's q~ is
-// divided by a power of two near its largest entry (undone on the scores)
-// and the value scales by the split's largest one (undone on the partials).
+//   values  U^T[r x 16 heads] += H_v^T[r x 16 tok] * P^T, bf16 MFMA 16x16x16
+//           with P split as hi + lo bf16. The tile's value latents go through
+//           a wave-private LDS tile so each lane can gather one latent column
+//           over four tokens (the MFMA contracts over tokens); groups of
+//           four rows are offset by 32 bytes so those gathers hit distinct
+//           banks.
 // Lane layouts (wave64): 16x16x32 lane l holds A[l%16][k-slot l/16] and
-// B[k-slot l/16][l%16], eight 16-bit values each; 16x16x16 the same with four;
-// the result holds D[4*(l/16)+i][l%16]. A score tile leaves lane l with tokens
+// B[k-slot l/16][l%16], eight bf16 each; 16x16x16 the same with four; the
+// result holds D[4*(l/16)+i][l%16]. A score tile leaves lane l with tokens
 // 4*(l/16)+i of head l%16, which is exactly the 16x16x16 k-slot of P^T, so the
 // weights never leave their lane.
-// Loads: 16-byte non-temporal loads (the latents are read once) of the next
-// tile into registers while the current one, already in LDS, is consumed.
-// Rows past the split's end are clamped to its last valid row and masked, so
-// nothing outside [t0, len) is ever read.
+// Loads: 16-byte global loads; H_k in the MFMA operand pattern (row l%16),
+// H_v as contiguous 1 KiB per instruction; a ring of register buffers per wave
+// keeps the next tiles in flight while one is consumed. Rows past the split's end are
+// clamped to its last valid row and masked, so nothing outside [t0, len) is
+// ever read.
 #include <math.h>
 
 #include "device_util.h"
@@ -49,9 +42,6 @@ namespace palu {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -60,55 +50,19 @@ constexpr int kTile = 16;       // tokens per tile
 #ifndef ABS_WAVES
 #define ABS_WAVES 4     // waves per workgroup (one per SIMD; measured better than 8)
 #endif
+#ifndef ABS_INFLIGHT
+#define ABS_INFLIGHT 1  // tiles in flight per wave
+#endif
 constexpr int kWaves = ABS_WAVES;
+constexpr int kInFlight = ABS_INFLIGHT;
 
-// x ~ hi + lo in two 16-bit floats (fp16 or bf16, nearest even each): the
-// MFMA operand bits of both terms
-template <bool kF16>
-__device__ __forceinline__ void split16(float x, uint16_t& hi, uint16_t& lo) {
-  if constexpr (kF16) {
-    const _Float16 h = static_cast<_Float16>(x);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x - static_cast<float>(h)));
-  } else {
-    const __bf16 h = static_cast<__bf16>(x);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x - static_cast<float>(h)));
-  }
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, sizeof(r));
+  return r;
 }
 
-// four int8 codes -> four fp16 values, exactly: with u = code + 128 (the byte
-// XOR 0x80), the fp16 with bits 0x64uu is 1024 + u; one byte permute per pair
-// of codes and one packed fp16 subtraction of 1152 give the codes
-__device__ __forceinline__ uint2 i8x4_to_f16x4(uint32_t w) {
-  const uint32_t x = w ^ 0x80808080u;
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
-  const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
-  const half2v a = __builtin_bit_cast(half2v, lo) - bias;
-  const half2v c = __builtin_bit_cast(half2v, hi) - bias;
-  return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
-}
-
-template <bool kF16>
-__device__ __forceinline__ floatx4 mfma32(uint4 a, uint4 b, floatx4 c) {
-  if constexpr (kF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
-                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-template <bool kF16>
-__device__ __forceinline__ floatx4 mfma16(short4v a, short4v b, floatx4 c) {
-  if constexpr (kF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4, a),
-                                                 __builtin_bit_cast(half4, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-// q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] 16-bit; rows padded
+// q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] bf16; rows padded
 // by 8 elements so the 16 heads' 16-byte reads spread over the banks.
 template <int R>
 struct QTile {
@@ -116,8 +70,8 @@ struct QTile {
   uint16_t v[2][16][kStride];
 };
 
-// byte offset of (row, column byte) in a wave's value tile [16][R] (16-bit):
-// each group of four rows is shifted by 32 bytes, so the four lane groups of a
+// byte offset of (row, column byte) in a wave's value tile [16][R] bf16: each
+// group of four rows is shifted by 32 bytes, so the four lane groups of a
 // gather (rows 4*kb..4*kb+3, same columns) hit different banks while every
 // address stays one per-lane base plus an immediate
 template <int R>
@@ -140,10 +94,10 @@ struct State {
   float l;               // this lane's share of the running sum
 };
 
-// scores of a tile (log2 units; int8: times the key scales), masked past t1
-template <int R, bool kF16>
+// scores of a tile (log2 units), masked past t1
+template <int R>
 __device__ __forceinline__ floatx4 scores(const char* kt, const QTile<R>& qs, int tok0, int t1,
-                                          int lane, floatx4 sk) {
+                                          int lane) {
   const int ln = lane & 15, kb = lane >> 4;
   // four independent accumulators (hi/lo x even/odd chunk) keep the MFMA
   // dependency chains short; they are added at the end
@@ -152,25 +106,22 @@ __device__ __forceinline__ floatx4 scores(const char* kt, const QTile<R>& qs, in
   for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < R / 32; ++c) {
-    const uint4 a = *reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb));
-    const uint4 qh = *reinterpret_cast<const uint4*>(&qs.v[0][ln][32 * c + 8 * kb]);
-    const uint4 ql = *reinterpret_cast<const uint4*>(&qs.v[1][ln][32 * c + 8 * kb]);
-    acc4[2 * (c & 1)] = mfma32<kF16>(a, qh, acc4[2 * (c & 1)]);
-    acc4[2 * (c & 1) + 1] = mfma32<kF16>(a, ql, acc4[2 * (c & 1) + 1]);
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
+    const bf16x8 qh = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[0][ln][32 * c + 8 * kb]));
+    const bf16x8 ql = as_bf16x8(*reinterpret_cast<const uint4*>(&qs.v[1][ln][32 * c + 8 * kb]));
+    acc4[2 * (c & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh, acc4[2 * (c & 1)], 0, 0, 0);
+    acc4[2 * (c & 1) + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql, acc4[2 * (c & 1) + 1], 0, 0, 0);
   }
   floatx4 s = (acc4[0] + acc4[2]) + (acc4[1] + acc4[3]);
-  if constexpr (kF16) s *= sk;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (tok0 + 4 * kb + i >= t1) s[i] = -INFINITY;
   return s;
 }
 
-// online softmax update and the value product from the staged LDS tile; sv
-// (int8 latents) holds the value scales of the lane's four tokens
-template <int R, bool kF16>
-__device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const char* vt, int lane,
-                                               floatx4 sv) {
+// online softmax update and the value product from the staged LDS tile
+template <int R>
+__device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const char* vt, int lane) {
   const int ln = lane & 15, kb = lane >> 4;
   float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -183,16 +134,15 @@ __device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const ch
 #pragma unroll
     for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= alpha;
   }
-  // P^T operand: k-slot e of lane group kb is token 4*kb + e; hi + lo
+  // P^T operand: k-slot e of lane group kb is token 4*kb + e; hi + lo bf16
   short4v ph, pl;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float pe = exp2f(s[e] - st.m);
-    st.l += pe;
-    uint16_t h, lo;
-    split16<kF16>(kF16 ? pe * sv[e] : pe, h, lo);
-    ph[e] = static_cast<short>(h);
-    pl[e] = static_cast<short>(lo);
+    const float p = exp2f(s[e] - st.m);
+    st.l += p;
+    const float hi = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
+    ph[e] = static_cast<short>(__float_as_uint(hi) >> 16);
+    pl[e] = static_cast<short>(f32_to_bf16_rne(p - hi));
   }
   // values: gather H_v^T[16*rb + ln][tokens 4*kb .. 4*kb+3] from the LDS tile
   const char* vb = vt + vtile_off<R>(4 * kb, 2 * ln);
@@ -202,16 +152,14 @@ __device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const ch
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
-    st.acc[rb] = mfma16<kF16>(a, ph, st.acc[rb]);
-    st.acc[rb] = mfma16<kF16>(a, pl, st.acc[rb]);
+    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, st.acc[rb], 0, 0, 0);
+    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, st.acc[rb], 0, 0, 0);
   }
 }
 
 template <int R>
 struct Smem {
   QTile<R> q;
-  float qc[16];              // int8: power of two each head's q~ was divided by
-  float svmax[kWaves];       // int8: each wave's largest value scale
   union {
     struct {                                         // per-wave tiles (streaming)
       char kt[kWaves][kKTileBytes<R>];
@@ -251,24 +199,7 @@ __device__ __forceinline__ void publish(const State<R>& st, Smem<R>& sm, int w, 
   sm.u.x.l[w][lane] = st.l;
 }
 
-// The next tile of a wave in registers (vector types: arrays of uint4 here
-// ended up in scratch memory). bf16: the key rows in the score operand
-// pattern (row lane%16) and the value rows contiguous, 1 KiB per instruction.
-// int8: both contiguous, 16 codes per lane and instruction, plus the key and
-// value scales of the lane's four tokens 4*(lane/16) .. +3.
-template <int R, bool kI8>
-struct Pending {
-  typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
-  u32v k, v;
-};
-template <int R>
-struct Pending<R, true> {
-  typedef uint32_t u32v __attribute__((ext_vector_type(R / 16)));
-  u32v k, v;
-  floatx4 sk, sv;
-};
-
-template <int R, bool kShared, bool kI8>
+template <int R, bool kShared>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(DecodeParams p) {
   // query heads of a group beyond 16 go to further head slices (workgroups
   // that read the same latents, shared through one XCD's L2)
@@ -287,55 +218,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   const int last = t1 - 1;
 
   __shared__ Smem<R> sm;
-  const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
-  const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
-  // absorbed queries of the slice's heads, split hi/lo (padding heads are 0)
-  if constexpr (kI8) {
-    // the split's largest value scale (scales are >= 0)
-    float smax = 0.f;
-    for (int t = s0 + static_cast<int>(threadIdx.x); t < t1; t += 64 * kWaves)
-      smax = fmaxf(smax, p.s_v[row0 + t]);
-    // one wave per head: scale by a power of two 2^e <= max |q~_h| < 2^(e+1)
-    for (int hd = wave; hd < 16; hd += kWaves) {
-      float x[R / 64];
-      float amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < R / 64; ++j) {
-        x[j] = hd < nqs ? qrow[hd * R + lane + 64 * j] : 0.f;
-        amax = fmaxf(amax, fabsf(x[j]));
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
-      const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
-      const float c = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
-      const float inv = 1.f / c;                     // exact: c is a power of two
-#pragma unroll
-      for (int j = 0; j < R / 64; ++j)
-        split16<true>(x[j] * inv, sm.q.v[0][hd][lane + 64 * j], sm.q.v[1][hd][lane + 64 * j]);
-      if (lane == 0) sm.qc[hd] = c;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
-    if (lane == 0) sm.svmax[wave] = smax;
-  } else {
-    for (int e = threadIdx.x; e < 16 * R; e += 64 * kWaves) {
-      const int hd = e / R, k = e % R;
-      const float x = hd < nqs ? qrow[hd * R + k] : 0.f;
-      split16<false>(x, sm.q.v[0][hd][k], sm.q.v[1][hd][k]);
-    }
+  // absorbed queries of the group's heads, split hi/lo bf16 (padding heads are 0)
+  for (int e = threadIdx.x; e < 16 * R; e += 64 * kWaves) {
+    const int hd = e / R, k = e % R;
+    const float x = hd < nqs ? p.qt[(static_cast<size_t>(b) * p.Hq + g * p.nq + hq0 + hd) * R + k] : 0.f;
+    const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+    sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
+    sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
   }
   __syncthreads();
-  // int8: scores are multiplied by qc * s_k, value weights by s_v / vref, and
-  // the partial sums by vref
-  float qc = 1.f, vref = 1.f;
-  if constexpr (kI8) {
-    qc = sm.qc[ln];
-    float m = sm.svmax[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, sm.svmax[w]);
-    if (m > 0.f && m < INFINITY) vref = m;
-  }
-  const float vinv = 1.f / vref;
+
+  const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
+  const uint16_t* Hk = static_cast<const uint16_t*>(p.h_k) + row0 * R;
+  const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
 
   State<R> st;
   st.m = -INFINITY;
@@ -343,8 +238,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // 16-token tiles dealt round-robin: wave w takes tiles w, w+4, ...; loads
-  // past the end read the last valid row again (never out of range)
+  // 16-token tiles dealt round-robin: wave w takes tiles w, w+4, ...; each
+  // register buffer is refilled as soon as its part is consumed (values right
+  // after staging, keys right after the score MFMAs); loads past the end read
+  // the last valid row again (cached, never out of range)
   const int ntiles = (t1 - s0 + kTile - 1) / kTile;
   const int mine = (ntiles - wave + kWaves - 1) / kWaves;   // may be 0
   if (mine > 0) {
@@ -352,85 +249,62 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
     char* vt = sm.u.t.vt[wave];
     const int step = kTile * kWaves;
     const int first = s0 + kTile * wave;
-    Pending<R, kI8> nx;
-    auto fetch = [&](int tok0) {
-      if constexpr (kI8) {
-        const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * R;
-        const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * R;
+    // kInFlight tiles in registers (vector types: arrays of uint4 here ended
+    // up in scratch memory) while the previous one, copied into the wave's
+    // LDS tiles, is consumed
+    typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
+    auto fetch = [&](u32v& nkv, u32v& nvv, int tok0) {
+      const int rk = min(tok0 + ln, last);
 #pragma unroll
-        for (int q = 0; q < R / 64; ++q) {
-          const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
-          const size_t off = static_cast<size_t>(min(tok0 + flat / R, last)) * R + flat % R;
-          const uint4 a = load_tile16<kShared>(Hk + off);
-          const uint4 c = load_tile16<kShared>(Hv + off);
-          nx.k[4 * q] = a.x; nx.k[4 * q + 1] = a.y; nx.k[4 * q + 2] = a.z; nx.k[4 * q + 3] = a.w;
-          nx.v[4 * q] = c.x; nx.v[4 * q + 1] = c.y; nx.v[4 * q + 2] = c.z; nx.v[4 * q + 3] = c.w;
-        }
+      for (int c = 0; c < R / 32; ++c) {
+        const uint4 t = load_tile16<kShared>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
+        nkv[4 * c] = t.x; nkv[4 * c + 1] = t.y; nkv[4 * c + 2] = t.z; nkv[4 * c + 3] = t.w;
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const size_t t = row0 + min(tok0 + 4 * kb + i, last);
-          nx.sk[i] = p.s_k[t];
-          nx.sv[i] = p.s_v[t];
-        }
-      } else {
-        const uint16_t* Hk = static_cast<const uint16_t*>(p.h_k) + row0 * R;
-        const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
-        const int rk = min(tok0 + ln, last);
-#pragma unroll
-        for (int c = 0; c < R / 32; ++c) {
-          const uint4 t = load_tile16<kShared>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
-          nx.k[4 * c] = t.x; nx.k[4 * c + 1] = t.y; nx.k[4 * c + 2] = t.z; nx.k[4 * c + 3] = t.w;
-        }
-#pragma unroll
-        for (int q = 0; q < R / 32; ++q) {
-          const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
-          const int rv = min(tok0 + flat / (2 * R), last);
-          const uint4 t = load_tile16<kShared>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
-          nx.v[4 * q] = t.x; nx.v[4 * q + 1] = t.y; nx.v[4 * q + 2] = t.z; nx.v[4 * q + 3] = t.w;
-        }
+      for (int q = 0; q < R / 32; ++q) {
+        const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
+        const int rv = min(tok0 + flat / (2 * R), last);
+        const uint4 t = load_tile16<kShared>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
+        nvv[4 * q] = t.x; nvv[4 * q + 1] = t.y; nvv[4 * q + 2] = t.z; nvv[4 * q + 3] = t.w;
       }
     };
-    // copy the pending tile into the wave's LDS tiles (int8: widened to fp16)
-    // and keep its scales for the consumer
-    floatx4 sk = {1.f, 1.f, 1.f, 1.f}, sv = {1.f, 1.f, 1.f, 1.f};
-    auto stage = [&]() {
-      if constexpr (kI8) {
+    auto stage = [&](const u32v& nkv, const u32v& nvv) {
 #pragma unroll
-        for (int q = 0; q < R / 64; ++q) {
-          const int flat = q * 1024 + lane * 16;
-          const int row = flat / R, col = flat % R;       // 16 codes -> 32 bytes
-          const uint2 k0 = i8x4_to_f16x4(nx.k[4 * q]), k1 = i8x4_to_f16x4(nx.k[4 * q + 1]);
-          const uint2 k2 = i8x4_to_f16x4(nx.k[4 * q + 2]), k3 = i8x4_to_f16x4(nx.k[4 * q + 3]);
-          char* kd = kt + row * kKStride<R> + 2 * col;
-          *reinterpret_cast<uint4*>(kd) = uint4{k0.x, k0.y, k1.x, k1.y};
-          *reinterpret_cast<uint4*>(kd + 16) = uint4{k2.x, k2.y, k3.x, k3.y};
-          const uint2 v0 = i8x4_to_f16x4(nx.v[4 * q]), v1 = i8x4_to_f16x4(nx.v[4 * q + 1]);
-          const uint2 v2 = i8x4_to_f16x4(nx.v[4 * q + 2]), v3 = i8x4_to_f16x4(nx.v[4 * q + 3]);
-          char* vd = vt + vtile_off<R>(row, 2 * col);
-          *reinterpret_cast<uint4*>(vd) = uint4{v0.x, v0.y, v1.x, v1.y};
-          *reinterpret_cast<uint4*>(vd + 16) = uint4{v2.x, v2.y, v3.x, v3.y};
-        }
-        sk = nx.sk * qc;
-        sv = nx.sv * vinv;
-      } else {
+      for (int c = 0; c < R / 32; ++c)
+        *reinterpret_cast<uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)) =
+            uint4{nkv[4 * c], nkv[4 * c + 1], nkv[4 * c + 2], nkv[4 * c + 3]};
 #pragma unroll
-        for (int c = 0; c < R / 32; ++c)
-          *reinterpret_cast<uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)) =
-              uint4{nx.k[4 * c], nx.k[4 * c + 1], nx.k[4 * c + 2], nx.k[4 * c + 3]};
-#pragma unroll
-        for (int q = 0; q < R / 32; ++q) {
-          const int flat = q * 1024 + lane * 16;
-          *reinterpret_cast<uint4*>(vt + vtile_off<R>(flat / (2 * R), flat % (2 * R))) =
-              uint4{nx.v[4 * q], nx.v[4 * q + 1], nx.v[4 * q + 2], nx.v[4 * q + 3]};
-        }
+      for (int q = 0; q < R / 32; ++q) {
+        const int flat = q * 1024 + lane * 16;
+        *reinterpret_cast<uint4*>(vt + vtile_off<R>(flat / (2 * R), flat % (2 * R))) =
+            uint4{nvv[4 * q], nvv[4 * q + 1], nvv[4 * q + 2], nvv[4 * q + 3]};
       }
     };
-    fetch(first);
-    for (int j = 0; j < mine; ++j) {
-      stage();
-      fetch(first + step * (j + 1));
-      const floatx4 s = scores<R, kI8>(kt, sm.q, first + step * j, t1, lane, sk);
-      softmax_values<R, kI8>(st, s, vt, lane, sv);
+    auto consume = [&](int j) {
+      const floatx4 s = scores<R>(kt, sm.q, first + step * j, t1, lane);
+      softmax_values<R>(st, s, vt, lane);
+    };
+    u32v ka, va;
+    fetch(ka, va, first);
+    if constexpr (kInFlight == 1) {
+      for (int j = 0; j < mine; ++j) {
+        stage(ka, va);
+        fetch(ka, va, first + step * (j + 1));
+        consume(j);
+      }
+    } else {
+      u32v kb2, vb2;
+      fetch(kb2, vb2, first + step);
+      for (int j = 0; j < mine; j += 2) {
+        stage(ka, va);
+        fetch(ka, va, first + step * (j + 2));
+        consume(j);
+        if (j + 1 < mine) {
+          stage(kb2, vb2);
+          fetch(kb2, vb2, first + step * (j + 3));
+          consume(j + 1);
+        }
+      }
     }
   }
 
@@ -461,25 +335,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   }
   float* u = p.part_u + slot * R;
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb) {
-    if constexpr (kI8) st.acc[rb] *= vref;
+  for (int rb = 0; rb < R / 16; ++rb)
     *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) =
         float4{st.acc[rb][0], st.acc[rb][1], st.acc[rb][2], st.acc[rb][3]};
-  }
-}
-
-template <int R, bool kI8>
-hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
-  const int nslice = absorbed_head_slices(p.nq);
-  if (nslice == 1) {
-    split_absorbed_mfma_kernel<R, false, kI8><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
-  } else {
-    const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
-    if (ids == 0) return hipErrorInvalidValue;
-    split_absorbed_mfma_kernel<R, true, kI8>
-        <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -488,26 +346,28 @@ bool absorbed_mfma_supported(const DecodeParams& p, int dtype) {
   return dtype == 1 && (p.r == 32 || p.r == 64 || p.r == 128 || p.r == 256);
 }
 
-bool absorbed_i8_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && (p.r == 64 || p.r == 128 || p.r == 256);
-}
-
 int absorbed_head_slices(int nq) { return (nq + 15) / 16; }
 
-hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {
-  if (p.latent_i8) {
-    switch (p.r) {
-      case 64: return launch_rank<64, true>(p, st);
-      case 128: return launch_rank<128, true>(p, st);
-      case 256: return launch_rank<256, true>(p, st);
-      default: return hipErrorInvalidValue;
-    }
+template <int R>
+hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
+  const int nslice = absorbed_head_slices(p.nq);
+  if (nslice == 1) {
+    split_absorbed_mfma_kernel<R, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+  } else {
+    const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
+    if (ids == 0) return hipErrorInvalidValue;
+    split_absorbed_mfma_kernel<R, true>
+        <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {
   switch (p.r) {
-    case 32: return launch_rank<32, false>(p, st);
-    case 64: return launch_rank<64, false>(p, st);
-    case 128: return launch_rank<128, false>(p, st);
-    case 256: return launch_rank<256, false>(p, st);
+    case 32: return launch_rank<32>(p, st);
+    case 64: return launch_rank<64>(p, st);
+    case 128: return launch_rank<128>(p, st);
+    case 256: return launch_rank<256>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

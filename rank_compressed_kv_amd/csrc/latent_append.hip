@@ -58,9 +58,27 @@ __device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
 }
 __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Byte offset of latent k of token t inside one (b, g) slab of the int8 cache.
+// The slab is a run of 32-token blocks of 32 r bytes each, ordered as the
+// decode kernel's MFMA operands so that 16-byte word i of lane l of a block is
+// bytes [1024 i + 16 l, +16) (lane l = 16 kb + ln):
+//   keys:   half h = (t%32)/16 of the block holds 16 tokens, ln = t%16; the
+//           16 bytes of (word, kb, ln) are latents 32c + 8kb + j, c = 2 word' +
+//           byte/8 (word' the word within the half), j = byte%8;
+//   values: the 16 bytes of (word, kb, ln) are latent 16 rb + ln, rb = 2 word +
+//           byte/8, of the tokens 4kb + j (j = byte%8 < 4) and 16 + 4kb + j - 4.
+__device__ __forceinline__ size_t i8_key_offset(int t, int k, int r) {
+  return static_cast<size_t>(t / 32) * 32 * r + ((t % 32) / 16) * 16 * r + (k / 64) * 1024 +
+         ((k % 32) / 8) * 256 + (t % 16) * 16 + ((k / 32) % 2) * 8 + k % 8;
+}
+__device__ __forceinline__ size_t i8_value_offset(int t, int k, int r) {
+  return static_cast<size_t>(t / 32) * 32 * r + (k / 32) * 1024 + ((t % 16) / 4) * 256 +
+         (k % 16) * 16 + ((k / 16) % 2) * 8 + ((t % 32) / 16) * 4 + t % 4;
+}
+
 // quantise the finished fp32 rows of segment j (matrix j / G, group j % G) of
 // every sequence into the int8 cache: one wave per sequence, four consecutive
-// latents per lane (r % 4 == 0)
+// latents per lane (r in {64, 128, 256})
 __device__ void quantize_segment(const AppendParams& p, int j, int wave, int lane) {
   const int width = p.G * p.r;
   const bool is_v = j >= p.G;
@@ -90,9 +108,21 @@ __device__ void quantize_segment(const AppendParams& p, int j, int wave, int lan
       return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
     };
     const size_t row = (static_cast<size_t>(b) * p.G + g) * p.L + pos;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(h + row * p.r);
-    if (lane < nq) dst[lane] = pack(v0);
-    if (lane + 64 < nq) dst[lane + 64] = pack(v1);
+    int8_t* slab = h + (row - pos) * p.r;
+    // keys: four consecutive latents are four consecutive bytes; values: 16
+    // bytes apart
+    auto put = [&](int k, float4 v) {
+      if (!is_v) {
+        *reinterpret_cast<uint32_t*>(slab + i8_key_offset(pos, k, p.r)) = pack(v);
+      } else {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          slab[i8_value_offset(pos, k + i, p.r)] = static_cast<int8_t>(static_cast<uint8_t>(code(e[i])));
+      }
+    };
+    if (lane < nq) put(4 * lane, v0);
+    if (lane + 64 < nq) put(4 * (lane + 64), v1);
     if (lane == 0) sc[row] = scale;
   }
 }

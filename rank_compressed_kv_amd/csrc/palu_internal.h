@@ -71,7 +71,9 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
-bool absorbed_i8_supported(const DecodeParams& p, int dtype);   // int8 latents
+// int8 latents (tiled cache): bf16 q and B, r in {64, 128, 256}, L % 32 == 0
+bool absorbed_i8_supported(const DecodeParams& p, int dtype);
+hipError_t launch_split_absorbed_i8(const DecodeParams& p, hipStream_t st);
 int absorbed_head_slices(int nq);   // workgroups per (split, b, g): 16 query heads each
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);

@@ -111,9 +111,16 @@ def test_int8_decode_unsupported_combinations(lib, kw):
 
 
 def test_int8_decode_validation(lib):
-    """Descriptor errors come first, then missing pointers, then the workspace
-    (same size as palu_decode_attn's)."""
+    """Descriptor errors come first (the tiled int8 cache needs max_ctx % 32
+    == 0), then missing pointers, 16-byte alignment, then the workspace (same
+    size as palu_decode_attn's)."""
     assert _i8(lib, _desc(batch=0), *([True] * 9)) == P.PALU_ERR_SHAPE
+    assert _i8(lib, _desc(max_ctx=1000), *([True] * 9)) == P.PALU_ERR_SHAPE
+    odd = ctypes.c_void_p(0x1008)
+    for i in (1, 2, 3, 4):                   # h_k, h_v, s_k, s_v
+        ptrs = [True] * 9
+        ptrs[i] = odd
+        assert _i8(lib, _desc(), *ptrs) == P.PALU_ERR_SHAPE, i
     d = _desc(rank=128)
     for i in range(9):                       # every pointer is needed here
         ptrs = [True] * 9
@@ -224,7 +231,9 @@ def test_append_i8_validation(lib):
         return lib.palu_latent_append_i8(ctypes.byref(d), *ptrs, nbytes, None)
 
     bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
-           (dict(n_groups=4, rank=6), P.PALU_ERR_SHAPE),        # G*r % 8 == 0, r % 4 != 0
+           (dict(n_groups=4, rank=6), P.PALU_ERR_UNSUPPORTED),  # the tiled cache: r 64/128/256
+           (dict(n_groups=4, rank=96), P.PALU_ERR_UNSUPPORTED),
+           (dict(max_ctx=1000), P.PALU_ERR_SHAPE),              # whole 32-token blocks
            (dict(dtype=3), P.PALU_ERR_UNSUPPORTED)]
     for kw, status in bad:
         d = P.AppendDesc(**{**{f: getattr(good, f) for f, _ in P.AppendDesc._fields_}, **kw})
