@@ -20,10 +20,12 @@
 //     scales by the split's largest one, so fp16 operands stay in range
 //     whatever the magnitudes; both are undone in fp32.
 // One workgroup owns one (batch, group, context split) and 16 query heads;
-// its four waves take the split's 32-token blocks round-robin, each with the
-// next block's loads in flight (two register sets, alternating) while the
-// current one is multiplied, and combine their softmax states in LDS at the
-// end. Blocks are read whole: rows past the length inside the last block are
+// its four waves take the split's 32-token blocks round-robin and combine
+// their softmax states in LDS at the end. A wave holds one block in
+// registers and refills each half as soon as it is consumed (the key words
+// and scales right after the score MFMAs, the value words and scales right
+// after the value MFMAs), so about one block per wave is always in flight
+// without a second register set. Blocks are read whole: rows past the length inside the last block are
 // masked (their codes are finite whatever they hold; their scales are
 // replaced by 0 before use), and no byte outside the cache is touched.
 #include <math.h>
@@ -38,7 +40,17 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        // one per SIMD
+#ifndef I8_WAVES
+#define I8_WAVES 4
+#endif
+constexpr int kWaves = I8_WAVES;        // one per SIMD
+#ifndef I8_REFILL
+#define I8_REFILL 0
+#endif
+constexpr bool kRefill = I8_REFILL;   // 1: halves refilled with the block two ahead when consumed
+#ifndef I8_NT
+#define I8_NT 1
+#endif
 constexpr int kBlock = 32;       // tokens per cache block and per wave step
 constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
 
@@ -117,20 +129,94 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 
   __shared__ Smem<R> sm;
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
-  const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
+  const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * R;
+  const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * R;
+  const int nblk = (t1 - s0 + kBlock - 1) / kBlock;
+  const int mine = (nblk - wave + kWaves - 1) / kWaves;   // blocks of this wave, may be 0
+  auto tok_of = [&](int j) { return s0 + kBlock * (wave + kWaves * j); };
+
+  // one matrix's R/32 words of the block at t0 (t0 % 32 == 0) and the
+  // scales of the lane's eight tokens (16-byte aligned: L % 32 == 0)
+  auto fetch_half = [&](typename Block<R>::u32v& w, floatx4& s0v, floatx4& s1v,
+                        const int8_t* H, const float* S, int t0) {
+    const size_t base = static_cast<size_t>(t0) * R + lane * 16;
+#pragma unroll
+    for (int i = 0; i < R / 32; ++i) {
+      const uint4 a = load_tile16<kShared || !I8_NT>(H + base + i * 1024);
+      w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
+    }
+    const size_t srow = row0 + t0 + 4 * kb;
+    const float4 a0 = *reinterpret_cast<const float4*>(S + srow);
+    const float4 a1 = *reinterpret_cast<const float4*>(S + srow + 16);
+    s0v = floatx4{a0.x, a0.y, a0.z, a0.w};
+    s1v = floatx4{a1.x, a1.y, a1.z, a1.w};
+  };
+  auto fetch = [&](Block<R>& x, int t0) {
+    fetch_half(x.k, x.sk0, x.sk1, Hk, p.s_k, t0);
+    fetch_half(x.v, x.sv0, x.sv1, Hv, p.s_v, t0);
+  };
+  Block<R> xa, xb;
+
   {
-    // the split's largest value scale (scales are >= 0)
+    // every load of this prologue is issued before the first is used: the
+    // split's value scales (4096 tokens per round, indexes clamped to the
+    // split) and the q~ entries of this wave's heads
+    constexpr int kS = 4096 / (64 * kWaves);
+    float svx[kS];
+    auto load_scales = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < kS; ++u)
+        svx[u] = p.s_v[row0 + min(base + static_cast<int>(threadIdx.x) + u * 64 * kWaves, t1 - 1)];
+    };
+    load_scales(s0);
+    constexpr int kH = 16 / kWaves;
+    const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
+    float qx[kH][R / 64];
+#pragma unroll
+    for (int i = 0; i < kH; ++i)
+#pragma unroll
+      for (int j = 0; j < R / 64; ++j)
+        qx[i][j] = qrow[min(wave + kWaves * i, nqs - 1) * R + lane + 64 * j];
+    // splits longer than 4096 tokens (not planned by the library; a caller
+    // may ask for them) take further rounds of scale loads here, before any
+    // block is requested
     float smax = 0.f;
-    for (int t = s0 + static_cast<int>(threadIdx.x); t < t1; t += 64 * kWaves)
-      smax = fmaxf(smax, p.s_v[row0 + t]);
+    if (t1 - s0 > 4096) {
+      for (int base = s0;;) {
+#pragma unroll
+        for (int u = 0; u < kS; ++u) smax = fmaxf(smax, svx[u]);
+        base += 4096;
+        if (base >= t1) break;
+        load_scales(base);
+      }
+    }
+    // then the first blocks' loads: issued after the prologue's own loads (a
+    // compiler-only barrier keeps that order), so that waiting for those
+    // (memory counters drain in issue order) leaves the blocks in flight
+    // through the prologue. The requests are unconditional (a wave without
+    // blocks reads the split's first block, unused): after a conditional
+    // request the compiler could no longer count them and drained them all.
+    asm volatile("" ::: "memory");
+    fetch(xa, mine > 0 ? tok_of(0) : s0);
+    if (kRefill) fetch(xb, mine > 1 ? tok_of(1) : s0);
+    // the split's largest value scale (scales are >= 0; clamped duplicates
+    // do not change a maximum)
+    if (t1 - s0 <= 4096) {
+#pragma unroll
+      for (int u = 0; u < kS; ++u) smax = fmaxf(smax, svx[u]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
+    if (lane == 0) sm.svmax[wave] = smax;
     // one wave per head: q~ / 2^e with 2^e <= max |q~_h| < 2^(e+1), hi + lo
-    for (int hd = wave; hd < 16; hd += kWaves) {
-      float x[R / 64];
+#pragma unroll
+    for (int i = 0; i < kH; ++i) {
+      const int hd = wave + kWaves * i;
       float amax = 0.f;
 #pragma unroll
       for (int j = 0; j < R / 64; ++j) {
-        x[j] = hd < nqs ? qrow[hd * R + lane + 64 * j] : 0.f;
-        amax = fmaxf(amax, fabsf(x[j]));
+        if (hd >= nqs) qx[i][j] = 0.f;                 // padding heads are 0
+        amax = fmaxf(amax, fabsf(qx[i][j]));
       }
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -139,14 +225,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
       const float inv = 1.f / c;                     // exact: c is a power of two
 #pragma unroll
       for (int j = 0; j < R / 64; ++j)
-        split_f16(x[j] * inv, sm.q[0][hd][lane + 64 * j], sm.q[1][hd][lane + 64 * j]);
+        split_f16(qx[i][j] * inv, sm.q[0][hd][lane + 64 * j], sm.q[1][hd][lane + 64 * j]);
       if (lane == 0) sm.qc[hd] = c;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
-    if (lane == 0) sm.svmax[wave] = smax;
   }
-  __syncthreads();
+  barrier_lds();            // the first tiles stay in flight
   // scores are multiplied by qc * s_k, value weights by s_v / vref and the
   // partial sums by vref
   const float qc = sm.qc[ln];
@@ -162,33 +245,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * R;
-  const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * R;
-  const int nblk = (t1 - s0 + kBlock - 1) / kBlock;
-  const int mine = (nblk - wave + kWaves - 1) / kWaves;   // blocks of this wave, may be 0
-  auto tok_of = [&](int j) { return s0 + kBlock * (wave + kWaves * j); };
-
-  auto fetch = [&](Block<R>& x, int t0) {
-    const size_t base = static_cast<size_t>(t0) * R + lane * 16;   // t0 % 32 == 0
-#pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const uint4 a = load_tile16<kShared>(Hk + base + i * 1024);
-      const uint4 c = load_tile16<kShared>(Hv + base + i * 1024);
-      x.k[4 * i] = a.x; x.k[4 * i + 1] = a.y; x.k[4 * i + 2] = a.z; x.k[4 * i + 3] = a.w;
-      x.v[4 * i] = c.x; x.v[4 * i + 1] = c.y; x.v[4 * i + 2] = c.z; x.v[4 * i + 3] = c.w;
-    }
-    const size_t srow = row0 + t0 + 4 * kb;              // 16-byte aligned
-    const float4 a0 = *reinterpret_cast<const float4*>(p.s_k + srow);
-    const float4 a1 = *reinterpret_cast<const float4*>(p.s_k + srow + 16);
-    const float4 c0 = *reinterpret_cast<const float4*>(p.s_v + srow);
-    const float4 c1 = *reinterpret_cast<const float4*>(p.s_v + srow + 16);
-    x.sk0 = floatx4{a0.x, a0.y, a0.z, a0.w};
-    x.sk1 = floatx4{a1.x, a1.y, a1.z, a1.w};
-    x.sv0 = floatx4{c0.x, c0.y, c0.z, c0.w};
-    x.sv1 = floatx4{c1.x, c1.y, c1.z, c1.w};
-  };
-
-  auto compute = [&](const Block<R>& x, int t0) {
+  auto compute = [&](Block<R>& x, int t0, bool more, int tnext) {
     // q~ is read from LDS again for every block: held in registers across the
     // loop it would take 128 of them at r = 256 (a compiler-only barrier keeps
     // the reads inside)
@@ -214,6 +271,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     }
     sc[0] *= x.sk0 * qc;
     sc[1] *= x.sk1 * qc;
+    // the key words and scales are consumed: refill them with the next block
+    if (kRefill && more) fetch_half(x.k, x.sk0, x.sk1, Hk, p.s_k, tnext);
     floatx4 sv[2] = {x.sv0 * vinv, x.sv1 * vinv};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -259,17 +318,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
       st.acc[rb] = mfma(a, bh, st.acc[rb]);
       st.acc[rb] = mfma(a, bl, st.acc[rb]);
     }
+    if (kRefill && more) fetch_half(x.v, x.sv0, x.sv1, Hv, p.s_v, tnext);
   };
-
+  // the hot loops fetch unconditionally (a fetch under a branch made the
+  // compiler wait for the current block before issuing the next one); the
+  // last blocks are peeled off
   if (mine > 0) {
-    Block<R> xa, xb;
-    fetch(xa, tok_of(0));
-    for (int j = 0; j < mine; j += 2) {
-      if (j + 1 < mine) fetch(xb, tok_of(j + 1));
-      compute(xa, tok_of(j));
+    int j = 0;
+    if constexpr (kRefill) {
+      // two register sets, each half refilled with the block two ahead as
+      // soon as it is consumed: about 1.5 blocks per wave stay in flight
+      for (; j + 3 < mine; j += 2) {
+        compute(xa, tok_of(j), true, tok_of(j + 2));
+        compute(xb, tok_of(j + 1), true, tok_of(j + 3));
+      }
+      compute(xa, tok_of(j), j + 2 < mine, tok_of(j + 2));
+      if (j + 1 < mine) compute(xb, tok_of(j + 1), false, 0);
+      if (j + 2 < mine) compute(xa, tok_of(j + 2), false, 0);
+    } else {
+      // two register sets: the next block is requested before the current
+      // one is multiplied
+      for (; j + 2 < mine; j += 2) {
+        fetch(xb, tok_of(j + 1));
+        compute(xa, tok_of(j), false, 0);
+        fetch(xa, tok_of(j + 2));
+        compute(xb, tok_of(j + 1), false, 0);
+      }
       if (j + 1 < mine) {
-        if (j + 2 < mine) fetch(xa, tok_of(j + 2));
-        compute(xb, tok_of(j + 1));
+        fetch(xb, tok_of(j + 1));
+        compute(xa, tok_of(j), false, 0);
+        compute(xb, tok_of(j + 1), false, 0);
+      } else {
+        compute(xa, tok_of(j), false, 0);
       }
     }
   }

@@ -50,11 +50,8 @@ constexpr int kTile = 16;       // tokens per tile
 #ifndef ABS_WAVES
 #define ABS_WAVES 4     // waves per workgroup (one per SIMD; measured better than 8)
 #endif
-#ifndef ABS_INFLIGHT
-#define ABS_INFLIGHT 1  // tiles in flight per wave
-#endif
+
 constexpr int kWaves = ABS_WAVES;
-constexpr int kInFlight = ABS_INFLIGHT;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -218,19 +215,61 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   const int last = t1 - 1;
 
   __shared__ Smem<R> sm;
-  // absorbed queries of the group's heads, split hi/lo bf16 (padding heads are 0)
-  for (int e = threadIdx.x; e < 16 * R; e += 64 * kWaves) {
-    const int hd = e / R, k = e % R;
-    const float x = hd < nqs ? p.qt[(static_cast<size_t>(b) * p.Hq + g * p.nq + hq0 + hd) * R + k] : 0.f;
-    const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
-    sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
-    sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
-  }
-  __syncthreads();
-
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
   const uint16_t* Hk = static_cast<const uint16_t*>(p.h_k) + row0 * R;
   const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
+
+  // 16-token tiles dealt round-robin: wave w takes tiles w, w+4, ...; the
+  // registers of a tile are refilled with the next one as soon as the tile
+  // is copied into the wave's LDS tiles; loads past the end read the last
+  // valid row again (cached, never out of range)
+  const int ntiles = (t1 - s0 + kTile - 1) / kTile;
+  const int mine = (ntiles - wave + kWaves - 1) / kWaves;   // may be 0
+  const int step = kTile * kWaves;
+  const int first = s0 + kTile * wave;
+  // one tile in registers (vector types: arrays of uint4 here ended up in
+  // scratch memory)
+  typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
+  auto fetch = [&](u32v& nkv, u32v& nvv, int tok0) {
+    const int rk = min(tok0 + ln, last);
+#pragma unroll
+    for (int c = 0; c < R / 32; ++c) {
+      const uint4 t = load_tile16<kShared>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
+      nkv[4 * c] = t.x; nkv[4 * c + 1] = t.y; nkv[4 * c + 2] = t.z; nkv[4 * c + 3] = t.w;
+    }
+#pragma unroll
+    for (int q = 0; q < R / 32; ++q) {
+      const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
+      const int rv = min(tok0 + flat / (2 * R), last);
+      const uint4 t = load_tile16<kShared>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
+      nvv[4 * q] = t.x; nvv[4 * q + 1] = t.y; nvv[4 * q + 2] = t.z; nvv[4 * q + 3] = t.w;
+    }
+  };
+  // the first tile's loads go out before anything waits
+  u32v ka, va;
+  if (mine > 0) fetch(ka, va, first);
+
+  // absorbed queries of the group's heads, split hi/lo bf16 (padding heads
+  // are 0): all of a thread's loads are issued before the first is used
+  {
+    constexpr int kQ = 16 * R / (64 * kWaves);
+    const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
+    float qx[kQ];
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
+      qx[u] = qrow[min(hd, nqs - 1) * R + k];
+    }
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
+      const float x = hd < nqs ? qx[u] : 0.f;
+      const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+      sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
+      sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
+    }
+  }
+  barrier_lds();            // the first tiles stay in flight
 
   State<R> st;
   st.m = -INFINITY;
@@ -238,36 +277,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // 16-token tiles dealt round-robin: wave w takes tiles w, w+4, ...; each
-  // register buffer is refilled as soon as its part is consumed (values right
-  // after staging, keys right after the score MFMAs); loads past the end read
-  // the last valid row again (cached, never out of range)
-  const int ntiles = (t1 - s0 + kTile - 1) / kTile;
-  const int mine = (ntiles - wave + kWaves - 1) / kWaves;   // may be 0
   if (mine > 0) {
     char* kt = sm.u.t.kt[wave];
     char* vt = sm.u.t.vt[wave];
-    const int step = kTile * kWaves;
-    const int first = s0 + kTile * wave;
-    // kInFlight tiles in registers (vector types: arrays of uint4 here ended
-    // up in scratch memory) while the previous one, copied into the wave's
-    // LDS tiles, is consumed
-    typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
-    auto fetch = [&](u32v& nkv, u32v& nvv, int tok0) {
-      const int rk = min(tok0 + ln, last);
-#pragma unroll
-      for (int c = 0; c < R / 32; ++c) {
-        const uint4 t = load_tile16<kShared>(Hk + static_cast<size_t>(rk) * R + 32 * c + 8 * kb);
-        nkv[4 * c] = t.x; nkv[4 * c + 1] = t.y; nkv[4 * c + 2] = t.z; nkv[4 * c + 3] = t.w;
-      }
-#pragma unroll
-      for (int q = 0; q < R / 32; ++q) {
-        const int flat = q * 1024 + lane * 16;          // byte within the tile's 16 rows
-        const int rv = min(tok0 + flat / (2 * R), last);
-        const uint4 t = load_tile16<kShared>(Hv + static_cast<size_t>(rv) * R + (flat % (2 * R)) / 2);
-        nvv[4 * q] = t.x; nvv[4 * q + 1] = t.y; nvv[4 * q + 2] = t.z; nvv[4 * q + 3] = t.w;
-      }
-    };
     auto stage = [&](const u32v& nkv, const u32v& nvv) {
 #pragma unroll
       for (int c = 0; c < R / 32; ++c)
@@ -280,31 +292,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
             uint4{nvv[4 * q], nvv[4 * q + 1], nvv[4 * q + 2], nvv[4 * q + 3]};
       }
     };
-    auto consume = [&](int j) {
+    for (int j = 0; j < mine; ++j) {
+      stage(ka, va);
+      fetch(ka, va, first + step * (j + 1));
       const floatx4 s = scores<R>(kt, sm.q, first + step * j, t1, lane);
       softmax_values<R>(st, s, vt, lane);
-    };
-    u32v ka, va;
-    fetch(ka, va, first);
-    if constexpr (kInFlight == 1) {
-      for (int j = 0; j < mine; ++j) {
-        stage(ka, va);
-        fetch(ka, va, first + step * (j + 1));
-        consume(j);
-      }
-    } else {
-      u32v kb2, vb2;
-      fetch(kb2, vb2, first + step);
-      for (int j = 0; j < mine; j += 2) {
-        stage(ka, va);
-        fetch(ka, va, first + step * (j + 2));
-        consume(j);
-        if (j + 1 < mine) {
-          stage(kb2, vb2);
-          fetch(kb2, vb2, first + step * (j + 3));
-          consume(j + 1);
-        }
-      }
     }
   }
 

@@ -136,4 +136,13 @@ __device__ __forceinline__ uint4 load_tile16(const void* ptr) {
   else return load_stream16(ptr);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads issued before
+// it stay in flight (__syncthreads also orders global memory, which makes
+// every wave wait for all of its outstanding loads first).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace palu
