@@ -42,8 +42,11 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["to_f64", "latent_project", "append_rows_bf16", "reconstruct", "rope_angles",
-           "apply_rope", "softmax", "attend", "decode_attention", "head_layout"]
+__all__ = ["to_f64", "latent_project", "append_rows_bf16", "quantize_rows_i8",
+           "dequantize_rows_i8", "append_rows_i8", "hadamard", "append_rows_i8_hadamard",
+           "dequantize_rows_i8_hadamard", "reconstruct", "rope_angles", "apply_rope", "softmax",
+           "attend", "decode_attention", "full_rank_attention", "decode_value_latents",
+           "head_layout"]
 
 
 # ---------------------------------------------------------------- inputs ---
@@ -106,6 +109,45 @@ def append_rows_i8(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantised cache write: the latent row as the kernel forms it (the fp32
     sum, here the exact value rounded once to fp32), then quantize_rows_i8."""
     return quantize_rows_i8(np.asarray(h64, dtype=np.float64).astype(np.float32))
+
+
+# -------------------------------------------- Hadamard-rotated int8 cache ---
+#
+# The Palu author responses name fusing a Hadamard transform as one of the
+# quantisation-friendly enhancements of the latent cache (answer to Q2,
+# ESPACE; the reply on LASER lists the same enhancements), next to per-token
+# quantisation of the latents (reply to reviewer Fsn9 on W1/W2). Reading
+# taken here (the pages give neither the matrix nor where it is applied): each latent row h (length r, a power
+# of two) is rotated by the Sylvester Hadamard matrix H_r before per-token
+# quantisation, h'' = h H_r, so that an outlier channel is spread over all r
+# codes; since H_r H_r = r I, the row is recovered as h = h'' H_r / r. The
+# rotation is orthogonal up to the factor r, so attention over the recovered
+# rows is attention over the original ones, up to quantisation.
+
+def hadamard(r: int) -> np.ndarray:
+    """Sylvester's Hadamard matrix of order r (a power of two), entries +-1:
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    if r < 1 or r & (r - 1):
+        raise ValueError("r must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < r:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def append_rows_i8_hadamard(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantised cache write of rotated rows: h'' = h H_r formed exactly and
+    rounded once to fp32 (the kernel's precision for the integer decisions),
+    then quantize_rows_i8. Returns (codes of h'', scales of h'')."""
+    h = np.asarray(h64, dtype=np.float64)
+    rot = h @ hadamard(h.shape[-1])
+    return quantize_rows_i8(rot.astype(np.float32))
+
+
+def dequantize_rows_i8_hadamard(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Latent rows of a rotated int8 cache: (code * scale) H_r / r, in fp64."""
+    r = codes.shape[-1]
+    return dequantize_rows_i8(codes, scales) @ hadamard(r) / r
 
 
 # --------------------------------------------------------- reconstruction ---

@@ -40,6 +40,11 @@ MUTANTS = {
                         "np.clip(np.sign(prod) * np.floor(np.abs(prod) + 0.5)"),
     "quant_column_amax": ("quantize_rows_i8", "amax = np.max(np.abs(h), axis=-1)",
                           "amax = np.broadcast_to(np.max(np.abs(h)), h.shape[:-1])"),
+    "hadamard_block_sign": ("hadamard", "h = np.block([[h, h], [h, -h]])",
+                            "h = np.block([[h, h], [-h, h]])"),
+    "hadamard_no_rescale": ("dequantize_rows_i8_hadamard", "@ hadamard(r) / r", "@ hadamard(r)"),
+    "hadamard_quantise_first": ("append_rows_i8_hadamard", "rot = h @ hadamard(h.shape[-1])",
+                                "rot = h"),
     "softmax_unnormalised": ("softmax", "return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "reconstruct_transposed": ("reconstruct", "return to_f64(h) @ to_f64(b)",
                                "return to_f64(h) @ to_f64(b)[::-1]"),

@@ -350,6 +350,52 @@ def test_quantize_round_trip_and_symmetry():
     np.testing.assert_array_equal(s3, scales * np.float32(8.0))
 
 
+@pytest.mark.parametrize("r", [1, 2, 4, 64, 256])
+def test_hadamard_is_sylvester(r):
+    """Entry (i, j) of Sylvester's matrix is (-1)^popcount(i & j) (closed form,
+    by induction on the block construction); hence symmetric and H H = r I."""
+    H = O.hadamard(r)
+    i, j = np.meshgrid(np.arange(r), np.arange(r), indexing="ij")
+    pop = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    np.testing.assert_array_equal(H, (-1.0) ** pop)
+    np.testing.assert_array_equal(H @ H, r * np.eye(r))
+    with pytest.raises(ValueError):
+        O.hadamard(96)
+
+
+def test_hadamard_quantisation_of_a_spike():
+    """A row with one nonzero latent c at index k rotates to c times row k of
+    H (all entries +-c): every code is +-127 with the sign of H[k], the scale
+    is |c|/127, and the recovered row is the spike again."""
+    r, k, c = 64, 5, np.float32(-3.0)
+    h = np.zeros((1, r))
+    h[0, k] = c
+    codes, scales = O.append_rows_i8_hadamard(h)
+    np.testing.assert_array_equal(codes[0], (127 * np.sign(c) * O.hadamard(r)[k]).astype(np.int8))
+    assert scales[0] == np.float32(3.0) / np.float32(127.0)
+    back = O.dequantize_rows_i8_hadamard(codes, scales)
+    np.testing.assert_allclose(back[0], h[0], atol=1e-6)
+
+
+def test_hadamard_round_trip_bound_and_outliers():
+    """Rotated rows come back within half a scale step per element (the
+    rotation error e H / r has max norm at most |e|_1 / r <= max |e|); on rows
+    with an outlier channel the rotated int8 cache loses less than the plain
+    one, which is what the transform is for."""
+    rng = np.random.default_rng(43)
+    h = rng.standard_normal((200, 128))
+    h[:, 7] *= 20.0                                  # one outlier channel
+    codes, scales = O.append_rows_i8_hadamard(h)
+    back = O.dequantize_rows_i8_hadamard(codes, scales)
+    rot32 = (h @ O.hadamard(128)).astype(np.float32).astype(np.float64) @ O.hadamard(128) / 128
+    assert np.all(np.abs(back - rot32) <= scales[:, None] * (0.5 + 1e-5))
+    pc, ps = O.append_rows_i8(h)
+    plain = O.dequantize_rows_i8(pc, ps)
+    err_rot = np.linalg.norm(back - h) / np.linalg.norm(h)
+    err_plain = np.linalg.norm(plain - h) / np.linalg.norm(h)
+    assert err_rot < 0.5 * err_plain
+
+
 def test_softmax_rows_sum_to_one_and_shift_invariance():
     rng = np.random.default_rng(4)
     z = rng.standard_normal((5, 33)) * 10
