@@ -93,6 +93,8 @@ typedef struct palu_attn_desc {
                            caller applies B_v, e.g. fused with its output
                            projection (Palu author response, clarification of W1:
                            B_v acts after the weighted sum). FULL_RANK ignores it. */
+  int32_t hadamard;     /* palu_decode_attn_i8 only (0 elsewhere): 1 if the int8 cache
+                           holds Hadamard-rotated rows (see palu_latent_append_i8) */
 } palu_attn_desc;
 
 /* Bytes of device workspace palu_decode_attn needs for this descriptor
@@ -128,19 +130,36 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              const int32_t* seq_lens, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* palu_decode_attn over an int8 latent cache with one scale per cached row:
- * latent row t of (b, g) is h[t, k] = codes[t, k] * scales[t] (per-token
- * quantisation of the latents combined with the low-rank cache, Palu author
- * response to reviewer Fsn9 on W1/W2; "Avg. Bits" with a scale shared by a
- * group of elements, answer to Q4). Same result as palu_decode_attn on the
- * dequantised cache, up to rounding.
- *   h_k, h_v [B, G, L_cap, r]    int8 codes; rows >= len[b] are never read
- *   s_k, s_v [B, G, L_cap]       fp32 scales, finite and >= 0
+/* The int8 latent cache (per-token quantisation of the latents combined with
+ * the low-rank cache, Palu author response to reviewer Fsn9 on W1/W2; "Avg.
+ * Bits" with a scale shared by a group of elements, answer to Q4):
+ *   codes h_k, h_v: B*G slabs of L_cap*r bytes; s_k, s_v [B, G, L_cap] fp32.
+ *   Latent k of token t of slab (b, g) is codes * scale, the code byte of
+ *   (t, k) sitting at this offset inside its slab (L_cap % 32 == 0, r in
+ *   {64, 128, 256}; the order of the decode kernel's matrix-core operands):
+ *     keys:   32r*(t/32) + 16r*((t%32)/16) + 1024*(k/64) + 256*((k%32)/8)
+ *             + 16*(t%16) + 8*((k/32)%2) + k%8
+ *     values: 32r*(t/32) + 1024*(k/32) + 256*((t%16)/4) + 16*(k%16)
+ *             + 8*((k/16)%2) + 4*((t%32)/16) + t%4
+ *   Each 32-token block is a permutation of its own 32 r bytes.
+ *   With hadamard = 1 a row holds the codes of h'' = h H_r (H_r Sylvester's
+ *   Hadamard matrix of order r, entries +-1; the author responses list fusing
+ *   a Hadamard transform among the quantisation-friendly enhancements, answer
+ *   to Q2) and the latent row is h = (codes * scale) H_r / r.
+ *
+ * palu_decode_attn over such a cache: same result as palu_decode_attn on the
+ * dequantised latents, up to rounding.
+ *   h_k, h_v, s_k, s_v  as above, 16-byte aligned; rows >= len[b] may be read
+ *            when they share a 32-token block with row len[b]-1, but never
+ *            change the result (whatever their bytes hold)
  *   q, b_k, b_v, seq_lens, out, workspace as in palu_decode_attn (the
  *            workspace size is palu_decode_attn_workspace's for desc)
+ *   desc->hadamard: 1 for a rotated cache (the kernel rotates q~ and the
+ *            value sums back; B_k and B_v are the unrotated ones)
  * Provided for mode ABSORBED, dtype BF16 and rank 64, 128 or 256
  * (latent_out allowed); anything else is UNSUPPORTED. Errors as in
- * palu_decode_attn, and NULL for a missing s_k or s_v. */
+ * palu_decode_attn, NULL for a missing s_k or s_v, SHAPE for L_cap % 32 != 0
+ * or a misaligned cache or scale pointer. */
 palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const int8_t* h_k,
                                 const int8_t* h_v, const float* s_k, const float* s_v,
                                 const void* b_k, const void* b_v, const int32_t* seq_lens,
@@ -154,6 +173,8 @@ typedef struct palu_append_desc {
   int32_t rank;      /* r, 1..512                                                 */
   int32_t max_ctx;   /* L_cap: row stride of the cache                             */
   int32_t dtype;     /* palu_dtype of x, a_k, a_v and (except the int8 calls) the cache */
+  int32_t hadamard;  /* palu_latent_append_i8 only (0 elsewhere): 1 rotates each row by
+                        the Hadamard matrix before quantising */
 } palu_append_desc;
 
 /* Bytes of device workspace palu_latent_append needs for this descriptor:
@@ -186,18 +207,19 @@ palu_status palu_latent_append(const palu_append_desc* desc, const void* x, cons
  * call, as for palu_latent_append. */
 palu_status palu_latent_append_i8_workspace(const palu_append_desc* desc, size_t* bytes);
 
-/* Quantised cache write of one token per sequence for the int8 cache that
- * palu_decode_attn_i8 reads (per-token quantisation, Palu author response to
- * reviewer Fsn9 on W1/W2): the fp32 row h = x[b] . a[:, g*r:(g+1)*r], formed as
- * in palu_latent_append, is stored as
- *   s[b, g, pos[b]] = amax / 127, h_8[b, g, pos[b], k] = round(h[k] * 127 / amax)
+/* Quantised cache write of one token per sequence into the int8 cache that
+ * palu_decode_attn_i8 reads (layout above): the fp32 row h = x[b] .
+ * a[:, g*r:(g+1)*r], formed as in palu_latent_append (with desc->hadamard = 1
+ * then rotated in fp32, h'' = h H_r), is stored as
+ *   s[b, g, pos[b]] = amax / 127, code of latent k = round(h[k] * 127 / amax)
  * with amax = max_k |h[k]|, correctly rounded fp32 divisions, round to nearest
  * (ties to even) of the fp32 product, codes clamped to [-127, 127]; a row of
  * zeros stores scale 0 and codes 0.
  *   x, a_k, a_v, pos as in palu_latent_append (desc->dtype is theirs);
- *   h_k, h_v [B, G, L_cap, r] int8, 4-byte aligned; s_k, s_v [B, G, L_cap] fp32.
- * Needs r a multiple of 4 (SHAPE otherwise). Workspace rules, overlap rules
- * and errors as in palu_latent_append. */
+ *   h_k, h_v int8 slabs, 4-byte aligned; s_k, s_v [B, G, L_cap] fp32.
+ * Needs r in {64, 128, 256} (UNSUPPORTED otherwise) and L_cap % 32 == 0
+ * (SHAPE). Workspace rules, overlap rules and errors as in
+ * palu_latent_append. */
 palu_status palu_latent_append_i8(const palu_append_desc* desc, const void* x, const void* a_k,
                                   const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
                                   float* s_v, const int32_t* pos, void* workspace,

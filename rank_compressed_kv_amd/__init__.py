@@ -61,13 +61,14 @@ class AttnDesc(ctypes.Structure):
                 ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
-                ("latent_out", ctypes.c_int32)]
+                ("latent_out", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
 
 
 class AppendDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_groups", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("hadamard", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -307,7 +308,7 @@ def palu_profile_end() -> Tuple[float, int]:
 def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_groups: int,
               rank: int, max_ctx: int, dtype: int, mode: str = "reconstruct",
               rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0,
-              latent_out: bool = False) -> AttnDesc:
+              latent_out: bool = False, hadamard: bool = False) -> AttnDesc:
     modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED,
              "full_rank": PALU_MODE_FULL_RANK}
     if mode not in modes:
@@ -315,13 +316,13 @@ def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_g
     return AttnDesc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                     n_groups=n_groups, rank=rank, max_ctx=max_ctx, dtype=dtype, mode=modes[mode],
                     split_tokens=split_tokens, scale=scale, rope_theta=rope_theta,
-                    latent_out=1 if latent_out else 0)
+                    latent_out=1 if latent_out else 0, hadamard=1 if hadamard else 0)
 
 
 def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: int,
-                dtype: int) -> AppendDesc:
+                dtype: int, hadamard: bool = False) -> AppendDesc:
     return AppendDesc(batch=batch, d_model=d_model, n_groups=n_groups, rank=rank,
-                      max_ctx=max_ctx, dtype=dtype)
+                      max_ctx=max_ctx, dtype=dtype, hadamard=1 if hadamard else 0)
 
 
 def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
@@ -348,14 +349,14 @@ def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
 
 def decode_attention_i8(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
                         scale: float = 0.0, split_tokens: int = 0, latent_out: bool = False,
-                        out=None, workspace=None, stream=None):
+                        hadamard: bool = False, out=None, workspace=None, stream=None):
     """Absorbed-mode decode over int8 latents (codes h_k, h_v with row scales
     s_k, s_v). Allocates out and the workspace with torch when not given."""
     B, Hq, d = q.shape
     _, G, L, r = h_k.shape
     desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, n_groups=G,
                      rank=r, max_ctx=L, dtype=_dt(q), mode="absorbed", scale=scale,
-                     split_tokens=split_tokens, latent_out=latent_out)
+                     split_tokens=split_tokens, latent_out=latent_out, hadamard=hadamard)
     if out is None:
         out = torch.empty((B, Hq, r if latent_out else d), dtype=torch.float32,
                           device=q.device)
@@ -395,12 +396,15 @@ def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> No
     palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, workspace, stream)
 
 
-def latent_append_i8(x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace=None, stream=None) -> None:
-    """Quantised cache write into an int8 cache. Allocates the (zeroed)
-    workspace with torch when it is not given."""
+def latent_append_i8(x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace=None, stream=None, *,
+                     hadamard: bool = False) -> None:
+    """Quantised cache write into an int8 cache (rows rotated by the Hadamard
+    matrix first with hadamard=True). Allocates the (zeroed) workspace with
+    torch when it is not given."""
     B, dm = x.shape
     _, G, L, r = h_k.shape
-    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
+    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x),
+                       hadamard=hadamard)
     if workspace is None:
         workspace = torch.zeros(palu_latent_append_i8_workspace(desc), dtype=torch.uint8,
                                 device=x.device)

@@ -248,6 +248,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   p.full_rank = full ? 1 : 0;
   p.latent_out = latent ? 1 : 0;
   p.latent_i8 = s_k ? 1 : 0;
+  p.hadamard = desc->hadamard;
   p.s_k = s_k; p.s_v = s_v;
   for (int i = 0; i < p.d / 2; ++i)
     p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
@@ -288,6 +289,8 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              size_t workspace_bytes, void* stream) {
   palu_status st = validate_attn(desc);
   if (st != PALU_OK) return st;
+  if (desc->hadamard)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 cache only");
   return decode(desc, q, h_k, h_v, nullptr, nullptr, b_k, b_v, seq_lens, out, workspace,
                 workspace_bytes, stream);
 }
@@ -306,6 +309,8 @@ palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const
                 "(got mode %d, dtype %d, rank %d)", desc->mode, desc->dtype, desc->rank);
   if (desc->max_ctx % 32)
     return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", desc->max_ctx);
+  if (desc->hadamard != 0 && desc->hadamard != 1)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard must be 0 or 1 (got %d)", desc->hadamard);
   if (!absorbed_i8_supported(shape_params(desc), desc->dtype))
     return fail(PALU_ERR_UNSUPPORTED, "int8 latents: combination not provided");
   if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
@@ -339,6 +344,8 @@ palu_status validate_append_i8(const palu_append_desc* d) {
     return fail(PALU_ERR_UNSUPPORTED, "int8 cache needs rank 64, 128 or 256 (got %d)", d->rank);
   if (d->max_ctx % 32)
     return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", d->max_ctx);
+  if (d->hadamard != 0 && d->hadamard != 1)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard must be 0 or 1 (got %d)", d->hadamard);
   return PALU_OK;
 }
 
@@ -360,6 +367,7 @@ palu_status append(const palu_append_desc* d, const void* x, const void* a_k, co
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
   p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
   p.quant = quant ? 1 : 0;
+  p.hadamard = d->hadamard;
   p.s_k = s_k; p.s_v = s_v;
   append_bind_workspace(p, workspace);
   hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
@@ -383,6 +391,8 @@ palu_status palu_latent_append(const palu_append_desc* d, const void* x, const v
                                void* workspace, size_t workspace_bytes, void* stream) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
+  if (d->hadamard)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 cache only");
   return append(d, x, a_k, a_v, h_k, h_v, nullptr, nullptr, pos, workspace, workspace_bytes,
                 stream);
 }

@@ -8,7 +8,7 @@
 // weights, B_v applied in the merge); what differs is the cache and the data
 // path:
 //   - the int8 cache is stored in 32-token blocks whose byte order is that of
-//     the MFMA operands (see i8_cache_layout below), so every 16-byte load of
+//     the MFMA operands (the append kernel writes it), so every 16-byte load of
 //     a lane holds exactly the operand bytes that lane needs: no LDS staging,
 //     no gathers, fully coalesced 1 KiB per load instruction;
 //   - codes are widened to fp16 in registers (exact for |code| <= 127) and
@@ -21,13 +21,15 @@
 //     whatever the magnitudes; both are undone in fp32.
 // One workgroup owns one (batch, group, context split) and 16 query heads;
 // its four waves take the split's 32-token blocks round-robin and combine
-// their softmax states in LDS at the end. A wave holds one block in
-// registers and refills each half as soon as it is consumed (the key words
-// and scales right after the score MFMAs, the value words and scales right
-// after the value MFMAs), so about one block per wave is always in flight
-// without a second register set. Blocks are read whole: rows past the length inside the last block are
-// masked (their codes are finite whatever they hold; their scales are
-// replaced by 0 before use), and no byte outside the cache is touched.
+// their softmax states in LDS at the end. A wave holds two blocks in
+// registers: the next one is requested before the current one is multiplied
+// (non-temporal loads: the cache is read once). Blocks are read whole: rows
+// past the length inside the last block are masked (their codes are finite
+// whatever they hold; their scales are replaced by 0 before use), and no byte
+// outside the cache is touched.
+// A rotated cache (Hadamard rows, see the append) is read the same way: q~ is
+// rotated in the prologue and each split's value sum rotated back before it
+// is written, so the merge and B_k, B_v are those of the plain cache.
 #include <math.h>
 
 #include "device_util.h"
@@ -40,17 +42,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-#ifndef I8_WAVES
-#define I8_WAVES 4
-#endif
-constexpr int kWaves = I8_WAVES;        // one per SIMD
-#ifndef I8_REFILL
-#define I8_REFILL 0
-#endif
-constexpr bool kRefill = I8_REFILL;   // 1: halves refilled with the block two ahead when consumed
-#ifndef I8_NT
-#define I8_NT 1
-#endif
+constexpr int kWaves = 4;        // one per SIMD
 constexpr int kBlock = 32;       // tokens per cache block and per wave step
 constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
 
@@ -82,6 +74,14 @@ __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
                                                 __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// Walsh-Hadamard butterflies for a rotated cache (Sylvester's H_r, H_r H_r =
+// r I): the pair (x_i, x_i+m) becomes (x_i + x_i+m, x_i - x_i+m), over every
+// bit m of the index. The index bits sit in lanes (shuffles) or in registers.
+__device__ __forceinline__ float bfly_lane(float x, int lane, int m) {
+  const float o = __shfl_xor(x, m);
+  return (lane & m) ? o - x : x + o;
 }
 
 // q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] fp16 bits; rows
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     const size_t base = static_cast<size_t>(t0) * R + lane * 16;
 #pragma unroll
     for (int i = 0; i < R / 32; ++i) {
-      const uint4 a = load_tile16<kShared || !I8_NT>(H + base + i * 1024);
+      const uint4 a = load_tile16<kShared>(H + base + i * 1024);
       w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
     }
     const size_t srow = row0 + t0 + 4 * kb;
@@ -198,7 +198,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     // request the compiler could no longer count them and drained them all.
     asm volatile("" ::: "memory");
     fetch(xa, mine > 0 ? tok_of(0) : s0);
-    if (kRefill) fetch(xb, mine > 1 ? tok_of(1) : s0);
     // the split's largest value scale (scales are >= 0; clamped duplicates
     // do not change a maximum)
     if (t1 - s0 <= 4096) {
@@ -212,12 +211,31 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 #pragma unroll
     for (int i = 0; i < kH; ++i) {
       const int hd = wave + kWaves * i;
+      if (hd >= nqs) {
+#pragma unroll
+        for (int j = 0; j < R / 64; ++j) qx[i][j] = 0.f;   // padding heads are 0
+      }
+      if (p.hadamard) {
+        // rotated cache: score <q~, h> = <q~ H_r / r, h''>; latent lane + 64 j
+#pragma unroll
+        for (int m = 1; m < 64; m *= 2)
+#pragma unroll
+          for (int j = 0; j < R / 64; ++j) qx[i][j] = bfly_lane(qx[i][j], lane, m);
+#pragma unroll
+        for (int m = 1; m < R / 64; m *= 2)
+#pragma unroll
+          for (int j = 0; j < R / 64; ++j)
+            if (!(j & m)) {
+              const float a = qx[i][j], c = qx[i][j + m];
+              qx[i][j] = a + c;
+              qx[i][j + m] = a - c;
+            }
+#pragma unroll
+        for (int j = 0; j < R / 64; ++j) qx[i][j] *= 1.f / R;   // exact: R = 2^k
+      }
       float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < R / 64; ++j) {
-        if (hd >= nqs) qx[i][j] = 0.f;                 // padding heads are 0
-        amax = fmaxf(amax, fabsf(qx[i][j]));
-      }
+      for (int j = 0; j < R / 64; ++j) amax = fmaxf(amax, fabsf(qx[i][j]));
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
       const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](Block<R>& x, int t0, bool more, int tnext) {
+  auto compute = [&](const Block<R>& x, int t0) {
     // q~ is read from LDS again for every block: held in registers across the
     // loop it would take 128 of them at r = 256 (a compiler-only barrier keeps
     // the reads inside)
@@ -271,8 +289,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     }
     sc[0] *= x.sk0 * qc;
     sc[1] *= x.sk1 * qc;
-    // the key words and scales are consumed: refill them with the next block
-    if (kRefill && more) fetch_half(x.k, x.sk0, x.sk1, Hk, p.s_k, tnext);
     floatx4 sv[2] = {x.sv0 * vinv, x.sv1 * vinv};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -318,39 +334,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
       st.acc[rb] = mfma(a, bh, st.acc[rb]);
       st.acc[rb] = mfma(a, bl, st.acc[rb]);
     }
-    if (kRefill && more) fetch_half(x.v, x.sv0, x.sv1, Hv, p.s_v, tnext);
   };
   // the hot loops fetch unconditionally (a fetch under a branch made the
   // compiler wait for the current block before issuing the next one); the
   // last blocks are peeled off
   if (mine > 0) {
+    // two register sets: the next block is requested before the current one
+    // is multiplied
     int j = 0;
-    if constexpr (kRefill) {
-      // two register sets, each half refilled with the block two ahead as
-      // soon as it is consumed: about 1.5 blocks per wave stay in flight
-      for (; j + 3 < mine; j += 2) {
-        compute(xa, tok_of(j), true, tok_of(j + 2));
-        compute(xb, tok_of(j + 1), true, tok_of(j + 3));
-      }
-      compute(xa, tok_of(j), j + 2 < mine, tok_of(j + 2));
-      if (j + 1 < mine) compute(xb, tok_of(j + 1), false, 0);
-      if (j + 2 < mine) compute(xa, tok_of(j + 2), false, 0);
+    for (; j + 2 < mine; j += 2) {
+      fetch(xb, tok_of(j + 1));
+      compute(xa, tok_of(j));
+      fetch(xa, tok_of(j + 2));
+      compute(xb, tok_of(j + 1));
+    }
+    if (j + 1 < mine) {
+      fetch(xb, tok_of(j + 1));
+      compute(xa, tok_of(j));
+      compute(xb, tok_of(j + 1));
     } else {
-      // two register sets: the next block is requested before the current
-      // one is multiplied
-      for (; j + 2 < mine; j += 2) {
-        fetch(xb, tok_of(j + 1));
-        compute(xa, tok_of(j), false, 0);
-        fetch(xa, tok_of(j + 2));
-        compute(xb, tok_of(j + 1), false, 0);
-      }
-      if (j + 1 < mine) {
-        fetch(xb, tok_of(j + 1));
-        compute(xa, tok_of(j), false, 0);
-        compute(xb, tok_of(j + 1), false, 0);
-      } else {
-        compute(xa, tok_of(j), false, 0);
-      }
+      compute(xa, tok_of(j));
     }
   }
 
@@ -388,6 +391,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  float uscale = vref;
+  if (p.hadamard) {
+    // rotated cache: u = u'' H_r / r; latent 16 rb + 4 kb + i of the lane's
+    // head: bits 0-1 in the vector, 2-3 in lane bits 4-5, the rest in rb
+#pragma unroll
+    for (int rb = 0; rb < R / 16; ++rb) {
+      floatx4& a = st.acc[rb];
+      const float x0 = a[0] + a[1], x1 = a[0] - a[1], x2 = a[2] + a[3], x3 = a[2] - a[3];
+      a = floatx4{x0 + x2, x1 + x3, x0 - x2, x1 - x3};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = bfly_lane(a[e], lane, 16);
+        a[e] = bfly_lane(a[e], lane, 32);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < R / 16; m *= 2)
+#pragma unroll
+      for (int rb = 0; rb < R / 16; ++rb)
+        if (!(rb & m)) {
+          const floatx4 a = st.acc[rb], c = st.acc[rb + m];
+          st.acc[rb] = a + c;
+          st.acc[rb + m] = a - c;
+        }
+    uscale *= 1.f / R;                                   // exact: R = 2^k
+  }
   if (ln >= nqs) return;
   const int head = g * p.nq + hq0 + ln;
   const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
@@ -398,7 +427,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
   float* u = p.part_u + slot * R;
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) {
-    const floatx4 v = st.acc[rb] * vref;
+    const floatx4 v = st.acc[rb] * uscale;
     *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) = float4{v[0], v[1], v[2], v[3]};
   }
 }

@@ -24,6 +24,9 @@
 // they store them in the workspace and count themselves in the arrival
 // counter of each (matrix, group) row segment they cover; the last one of a
 // segment quantises it for every sequence and resets that counter.
+// With the Hadamard option (a quantisation-friendly enhancement the author
+// responses name, answer to Q2) each fp32 row is first rotated by Sylvester's
+// H_r, h'' = h H_r, which spreads an outlier latent over all r codes.
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -76,25 +79,40 @@ __device__ __forceinline__ size_t i8_value_offset(int t, int k, int r) {
          (k % 16) * 16 + ((k / 16) % 2) * 8 + ((t % 32) / 16) * 4 + t % 4;
 }
 
+// h H_r for the row a wave holds, four consecutive latents 4 lane + e per lane
+// (lanes >= nq hold zeros): butterflies (x_i, x_i+m) -> (x_i + x_i+m,
+// x_i - x_i+m) over the two index bits inside the lane, then over lane bits
+__device__ __forceinline__ float4 hadamard_row(float4 v, int lane, int nq) {
+  const float a = v.x + v.y, b = v.x - v.y, c = v.z + v.w, d = v.z - v.w;
+  v = float4{a + c, b + d, a - c, b - d};
+  for (int m = 1; m < nq; m *= 2) {                    // wave-uniform bound
+    const float4 o = {__shfl_xor(v.x, m), __shfl_xor(v.y, m), __shfl_xor(v.z, m),
+                      __shfl_xor(v.w, m)};
+    const bool up = (lane & m) != 0;
+    v = up ? float4{o.x - v.x, o.y - v.y, o.z - v.z, o.w - v.w}
+           : float4{v.x + o.x, v.y + o.y, v.z + o.z, v.w + o.w};
+  }
+  return v;
+}
+
 // quantise the finished fp32 rows of segment j (matrix j / G, group j % G) of
 // every sequence into the int8 cache: one wave per sequence, four consecutive
-// latents per lane (r in {64, 128, 256})
+// latents per lane (r in {64, 128, 256}, so nq <= 64)
 __device__ void quantize_segment(const AppendParams& p, int j, int wave, int lane) {
   const int width = p.G * p.r;
   const bool is_v = j >= p.G;
   const int g = is_v ? j - p.G : j;
   int8_t* h = static_cast<int8_t*>(is_v ? p.h_v : p.h_k);
   float* sc = is_v ? p.s_v : p.s_k;
-  const int nq = p.r / 4;                              // float4 per row, <= 128
+  const int nq = p.r / 4;                              // float4 per row, <= 64
   for (int b = wave; b < p.B; b += kThreads / 64) {
     const int pos = p.pos[b];
     if (pos < 0 || pos >= p.L) continue;
     const float* src = p.rows + static_cast<size_t>(b) * 2 * width + static_cast<size_t>(j) * p.r;
-    float4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    float4 v0 = {0.f, 0.f, 0.f, 0.f};
     if (lane < nq) v0 = *reinterpret_cast<const float4*>(src + 4 * lane);
-    if (lane + 64 < nq) v1 = *reinterpret_cast<const float4*>(src + 4 * (lane + 64));
-    float amax = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+    if (p.hadamard) v0 = hadamard_row(v0, lane, nq);
+    float amax = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
 #pragma unroll
     for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
     // correctly rounded fp32 divisions (the HIP default)
@@ -122,7 +140,6 @@ __device__ void quantize_segment(const AppendParams& p, int j, int wave, int lan
       }
     };
     if (lane < nq) put(4 * lane, v0);
-    if (lane + 64 < nq) put(4 * (lane + 64), v1);
     if (lane == 0) sc[row] = scale;
   }
 }

@@ -30,6 +30,7 @@ struct DecodeParams {
   int32_t full_rank;           // 1: h_k, h_v are full K, V; no B_k, B_v
   int32_t latent_out;          // 1: out [B, Hq, r] holds u* (B_v left to the caller)
   int32_t latent_i8;           // 1: h_k, h_v are int8 codes with row scales s_k, s_v
+  int32_t hadamard;            // 1: the int8 rows are Hadamard-rotated
   const float* s_k;            // [B, G, L] (int8 latents)
   const float* s_v;
   float scale_log2;            // softmax scale * log2(e)
@@ -50,6 +51,7 @@ struct AppendParams {
   int32_t B, dm, G, r, L;
   // int8 cache (h_k, h_v int8 codes): per-row scales and the second hand-off
   int32_t quant;
+  int32_t hadamard;   // 1: rows rotated by the Hadamard matrix before quantising
   float* s_k;         // [B, G, L]
   float* s_v;
   int32_t* seg_counters;  // one per (matrix, group) row segment; zero between calls

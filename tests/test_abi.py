@@ -254,6 +254,28 @@ def test_append_i8_validation(lib):
     assert call(good, *([True] * 8), ctypes.c_void_p(0x1008)) == P.PALU_ERR_WORKSPACE
 
 
+def test_hadamard_flag_is_for_int8_only(lib):
+    """The rotated-cache flag is refused by the bf16 calls, accepted by the
+    int8 ones (which then fail on the fake workspace size), and must be 0/1."""
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc(rank=128, hadamard=True)
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake,
+                                fake, 1 << 40, None) == P.PALU_ERR_UNSUPPORTED
+    assert b"int8" in lib.palu_last_error()
+    assert _i8(lib, d, *([True] * 9), nbytes=16) == P.PALU_ERR_WORKSPACE
+    d.hadamard = 2
+    assert _i8(lib, d, *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
+    a = P.append_desc(batch=2, d_model=256, n_groups=2, rank=64, max_ctx=64,
+                      dtype=P.PALU_BF16, hadamard=True)
+    assert lib.palu_latent_append(ctypes.byref(a), fake, fake, fake, fake, fake, fake, fake,
+                                  1 << 40, None) == P.PALU_ERR_UNSUPPORTED
+    assert lib.palu_latent_append_i8(ctypes.byref(a), *([fake] * 9), 16,
+                                     None) == P.PALU_ERR_WORKSPACE
+    a.hadamard = -1
+    assert lib.palu_latent_append_i8(ctypes.byref(a), *([fake] * 9), 1 << 40,
+                                     None) == P.PALU_ERR_UNSUPPORTED
+
+
 def test_only_the_c_abi_is_exported(lib):
     """Every function the library exports is one the header declares."""
     import shutil

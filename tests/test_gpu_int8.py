@@ -276,3 +276,118 @@ def test_int8_append_then_decode():
         caches[key] = O.dequantize_rows_i8(c, sc)
     want = O.decode_attention(t["q"], caches["k"], caches["v"], t["b_k"], t["b_v"], lens)
     assert_close(out.cpu().numpy().astype(np.float64), want, what="append then decode")
+
+
+# --------------------------------------------------- Hadamard-rotated rows ---
+
+def _want_rot(t, **kw):
+    hk = O.dequantize_rows_i8_hadamard(t["k_i8"], t["sk"])
+    hv = O.dequantize_rows_i8_hadamard(t["v_i8"], t["sv"])
+    return O.decode_attention(t["q"], hk, hv, t["b_k"], t["b_v"], t["lens"], **kw)
+
+
+@pytest.mark.parametrize("idx", [3, 4, 64])
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_int8_hadamard_decode_parity(idx, split_tokens):
+    """A rotated cache (rows h'' = h H_r): the kernel rotates q~ and the value
+    sums back; compared with the oracle on the rows (codes*scale) H_r / r."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = SMALL[idx]
+    t = W.generate(cfg, parts=("decode", "i8"))
+    print(f"[int8 hadamard] cfg{idx} split={split_tokens}", flush=True)
+    got = P.decode_attention_i8(dev(t["q"]), _cache(t, "k"), _cache(t, "v"), dev(t["sk"]),
+                                dev(t["sv"]), dev(t["b_k"]), dev(t["b_v"]), dev(t["lens"]),
+                                n_kv_heads=cfg.n_kv_heads, split_tokens=split_tokens,
+                                hadamard=True)
+    torch.cuda.synchronize()
+    assert_close(got.cpu().numpy().astype(np.float64), _want_rot(t), what=f"rot cfg{idx}")
+
+
+def test_int8_hadamard_latent_output():
+    """latent_out on a rotated cache returns u* in the unrotated latent space."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = SMALL[4]
+    t = W.generate(cfg, parts=("decode", "i8"))
+    hk = O.dequantize_rows_i8_hadamard(t["k_i8"], t["sk"])
+    hv = O.dequantize_rows_i8_hadamard(t["v_i8"], t["sv"])
+    want = O.decode_value_latents(t["q"], hk, hv, t["b_k"], t["lens"], cfg.group_dim)
+    got = P.decode_attention_i8(dev(t["q"]), _cache(t, "k"), _cache(t, "v"), dev(t["sk"]),
+                                dev(t["sv"]), dev(t["b_k"]), None, dev(t["lens"]),
+                                n_kv_heads=cfg.n_kv_heads, latent_out=True, hadamard=True)
+    torch.cuda.synchronize()
+    assert_close(got.cpu().numpy().astype(np.float64), want, what="rot u*")
+
+
+@pytest.mark.parametrize("name", ["r256_g2", "r128", "r64", "r64_f32"])
+def test_int8_hadamard_append(name):
+    """Rotated quantised cache write: codes and scales of h H_r agree with the
+    oracle's except within the fp32 error bound of a decision boundary (the
+    sum's bound carried through the rotation, plus the rotation's own
+    rounding), and never by more than one step."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = APPEND[name]
+    t = W.generate(cfg, parts=("decode", "append", "i8"))
+    hk, hv = _cache(t, "k"), _cache(t, "v")
+    sk, sv = dev(t["sk"]), dev(t["sv"])
+    print(f"[int8 hadamard append] {name}", flush=True)
+    P.latent_append_i8(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv, sk, sv, dev(t["pos"]),
+                       hadamard=True)
+    torch.cuda.synchronize()
+    G, r, dm = cfg.n_groups, cfg.rank, cfg.d_model
+    H = O.hadamard(r)
+    mism = tot = 0
+    for kind, codes_d, scales_d, a in (("k", hk, sk, t["a_k"]), ("v", hv, sv, t["a_v"])):
+        codes, scales = unpack_i8_cache(codes_d.cpu().numpy(), kind), scales_d.cpu().numpy()
+        h64 = O.latent_project(t["x"], a).reshape(cfg.batch, G, r)
+        E = (np.abs(O.to_f64(t["x"]))[:, :, None] * np.abs(O.to_f64(a))[None]).sum(1)
+        E = E.reshape(cfg.batch, G, r) * dm * 2.0 ** -24
+        for b, pos in enumerate(t["pos"]):
+            wc, ws = O.append_rows_i8_hadamard(h64[b])
+            gc, gs = codes[b, :, pos, :].astype(np.int64), scales[b, :, pos]
+            mism += int(np.sum(gc != wc))
+            tot += gc.size
+            for g in range(G):
+                e = h64[b, g] @ H
+                eb = 1.5 * (E[b, g].sum() + np.log2(r) * 2.0 ** -24 *
+                            np.sum(np.abs(h64[b, g]) + E[b, g]))
+                amax_lo = max(float(np.max(np.abs(e)) - eb), 0.0)
+                amax_hi = float(np.max(np.abs(e)) + eb)
+                assert amax_lo / 127 * (1 - 2.0 ** -23) <= gs[g] <= amax_hi / 127 * (1 + 2.0 ** -23)
+                if np.all(gc[g] == wc[g]):
+                    continue
+                lo, hi = _code_bounds(e, eb, amax_lo, amax_hi)
+                assert np.all((gc[g] >= lo) & (gc[g] <= hi)), (b, g)
+                assert np.max(np.abs(gc[g] - wc[g])) <= 1
+    assert mism <= 0.01 * tot
+
+
+def test_int8_hadamard_helps_on_outlier_channels():
+    """Latents with outlier channels (20x on 1% of the channels, as in the
+    131K workload), quantised per token with and without the rotation: the
+    int8 decode on the rotated cache lands closer to attention over the
+    unquantised latents."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = W.CONFIGS[4].scaled(batch=2, max_ctx=1024, ragged=None, seed=91)
+    t = W.generate(cfg)
+    h = {kind: O.to_f64(t[f"h_{kind}"]) for kind in "kv"}
+    exact = O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"])
+    errs = {}
+    for rot in (False, True):
+        cache, scales = {}, {}
+        for kind in "kv":
+            c, s = (O.append_rows_i8_hadamard if rot else O.append_rows_i8)(h[kind])
+            cache[kind] = dev(pack_i8_cache(c, kind))
+            scales[kind] = dev(s)
+        got = P.decode_attention_i8(dev(t["q"]), cache["k"], cache["v"], scales["k"],
+                                    scales["v"], dev(t["b_k"]), dev(t["b_v"]), dev(t["lens"]),
+                                    n_kv_heads=cfg.n_kv_heads, hadamard=rot)
+        torch.cuda.synchronize()
+        d = got.cpu().numpy().astype(np.float64) - exact
+        errs[rot] = np.linalg.norm(d) / np.linalg.norm(exact)
+    print(f"[int8 outliers] rel L2 error plain {errs[False]:.3e} rotated {errs[True]:.3e}",
+          flush=True)
+    assert errs[True] < 0.7 * errs[False]
