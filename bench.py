@@ -142,9 +142,10 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
                 out=first_out.cpu().numpy())
 
 
-def time_int8(torch, P, W, cfg, t, args):
+def time_int8(torch, P, W, cfg, t, args, rot=False):
     """The absorbed step over an int8 latent cache (codes plus one fp32 scale
-    per row): quantised append, then decode. Same shape, same timing loops."""
+    per row; rows Hadamard-rotated with rot): quantised append, then decode.
+    Same shape, same timing loops."""
     ti = W.generate(cfg, parts=("i8",))
     q, bk, bv = dev(torch, t["q"]), dev(torch, t["b_k"]), dev(torch, t["b_v"])
     lens = dev(torch, t["lens"])
@@ -159,9 +160,9 @@ def time_int8(torch, P, W, cfg, t, args):
     desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                        head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
                        max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, mode="absorbed",
-                       split_tokens=args.split_tokens)
+                       split_tokens=args.split_tokens, hadamard=rot)
     adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
-                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=P.PALU_BF16)
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, hadamard=rot)
     ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
     aws = torch.zeros(P.palu_latent_append_i8_workspace(adesc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
@@ -329,10 +330,11 @@ def granularity_sweep(torch, P, W, cfg, args):
     return rows
 
 
-def oracle_appended(O, cfg, t, caches):
+def oracle_appended(O, cfg, t, caches, rot=False):
     """The caches as the oracle has them after one step's append: row len-1 of
     each sequence replaced by the oracle's own cache write of x A (bf16: the
-    exact row rounded to fp32, then to bf16; int8: its quantisation)."""
+    exact row rounded to fp32, then to bf16; int8: its quantisation, of the
+    Hadamard-rotated row with rot)."""
     B, G, r = cfg.batch, cfg.n_groups, cfg.rank
     out = []
     for cache, a in zip(caches, ("a_k", "a_v")):
@@ -342,7 +344,8 @@ def oracle_appended(O, cfg, t, caches):
             for b in range(B):
                 p = int(t["lens"][b]) - 1
                 if p >= 0:
-                    codes[b, :, p], scales[b, :, p] = O.append_rows_i8(h64[b])
+                    codes[b, :, p], scales[b, :, p] = (O.append_rows_i8_hadamard if rot
+                                                       else O.append_rows_i8)(h64[b])
             out.append((codes, scales))
             continue
         c = cache.copy()
@@ -489,33 +492,38 @@ def main():
 
     int8 = None
     if not args.no_int8 and cfg.dtype == "bf16" and "absorbed" in results and \
-            cfg.rank in (64, 128, 256):
-        ri = time_int8(torch, P, W, cfg, t, args)
-        ti = ri.pop("ti")
-        (ck, sk), (cv, sv) = oracle_appended(O, cfg, t, ((ti["k_i8"], ti["sk"]),
-                                                          (ti["v_i8"], ti["sv"])))
-        # the oracle dequantises only the sampled sequences
-        dmax, num, den = 0.0, 0.0, 0.0
-        for b, h in pairs:
-            w = O.decode_attention(t["q"][b:b + 1], O.dequantize_rows_i8(ck[b:b + 1], sk[b:b + 1]),
-                                   O.dequantize_rows_i8(cv[b:b + 1], sv[b:b + 1]), t["b_k"],
-                                   t["b_v"], t["lens"][b:b + 1], select=[(0, h)])[0, h]
-            dd = ri["out"][b, h].astype(np.float64) - w
-            dmax, num, den = max(dmax, float(np.abs(dd).max())), num + float(dd @ dd), den + float(w @ w)
+            cfg.rank in (64, 128, 256) and cfg.max_ctx % 32 == 0:
         i8_bytes = int(np.sum(t["lens"], dtype=np.int64)) * cfg.n_groups * (2 * cfg.rank + 8)
-        kus = ri["kernel_ms"] * 1e3
-        int8 = {"us_per_step": round(ri["ms_per_step"] * 1e3, 2),
+        int8 = {"algorithmic_bytes": i8_bytes}
+        for rot in (False, True):
+            ri = time_int8(torch, P, W, cfg, t, args, rot)
+            ti = ri.pop("ti")
+            (ck, sk), (cv, sv) = oracle_appended(O, cfg, t, ((ti["k_i8"], ti["sk"]),
+                                                              (ti["v_i8"], ti["sv"])), rot)
+            deq = O.dequantize_rows_i8_hadamard if rot else O.dequantize_rows_i8
+            # the oracle dequantises only the sampled sequences
+            dmax, num, den = 0.0, 0.0, 0.0
+            for b, h in pairs:
+                w = O.decode_attention(t["q"][b:b + 1], deq(ck[b:b + 1], sk[b:b + 1]),
+                                       deq(cv[b:b + 1], sv[b:b + 1]), t["b_k"], t["b_v"],
+                                       t["lens"][b:b + 1], select=[(0, h)])[0, h]
+                dd = ri["out"][b, h].astype(np.float64) - w
+                dmax = max(dmax, float(np.abs(dd).max()))
+                num, den = num + float(dd @ dd), den + float(w @ w)
+            kus = ri["kernel_ms"] * 1e3
+            int8["hadamard" if rot else "plain"] = {
+                "us_per_step": round(ri["ms_per_step"] * 1e3, 2),
                 "us_per_decode_call": round(ri["decode_ms"] * 1e3, 2),
                 "kernel_us": _r(kus, 2),
-                "algorithmic_bytes": i8_bytes,
                 "GBps_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9, 1),
                 "frac_hbm_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "step_speedup_vs_bf16": round(results["absorbed"]["ms_per_step"]
                                               / ri["ms_per_step"], 3),
                 "sampled_parity_max_abs": dmax,
                 "sampled_parity_rel_l2": math.sqrt(num / den) if den > 0 else None}
-        print(f"[bench] int8 absorbed: {ri['ms_per_step'] * 1e3:.1f} us/step, kernel "
-              f"{kus:.1f} us", file=sys.stderr, flush=True)
+            print(f"[bench] int8 absorbed{' hadamard' if rot else ''}: "
+                  f"{ri['ms_per_step'] * 1e3:.1f} us/step, kernel {kus:.1f} us",
+                  file=sys.stderr, flush=True)
 
     ms = main_res["ms_per_step"]
     steps_s = 1e3 / ms
