@@ -37,18 +37,20 @@
 //            kAnchor tiles.
 //   scores   that layout is the A operand of a 16x16x16 MFMA (k = the block's
 //            16 columns): S^T[tok x q heads] = K_rot * Q^T with keys split hi +
-//            lo bf16 (two MFMAs, ~16 bits kept) and exact bf16 q; the waves of
-//            a head add their partial scores through LDS.
-//   softmax  online, base 2, by the first wave of each head.
-//   values   P and the rescale factors go through LDS; wave w adds
-//            H_v^T[r slice w] * P^T for all query heads of the slice (bf16 MFMA
-//            16x16x16, P split hi + lo), gathering value columns from the tile
-//            in LDS (four-row groups offset by 32 B: conflict-free).
+//            lo bf16 (two MFMAs, ~16 bits kept) and exact bf16 q; each wave
+//            stores its partial scores in LDS.
+//   softmax  online, base 2, run by every wave for all query heads of the
+//            slice (lane ln adds the partial scores of query head ln's KV
+//            head), so the weights and rescale factors stay in registers.
+//   values   wave w adds H_v^T[r slice w] * P^T for all query heads of the
+//            slice (bf16 MFMA 16x16x16, P split hi + lo), gathering value
+//            columns from the tile in LDS (four-row groups offset by 32 B:
+//            conflict-free).
 // Loads: 16-byte pieces of each tile go through two register stages (two tiles
 // in flight) into a ring of three LDS tile buffers; rows past the split's end
-// are clamped to its last valid row and masked. Two workgroup barriers per
-// tile: one after the partial scores, one after the softmax (which also
-// covers the copy of a later tile into LDS).
+// are clamped to its last valid row and masked. One workgroup barrier per
+// tile, after the partial scores (the partial scores and the rotation table
+// are double-buffered); it orders LDS only, so the loads stay in flight.
 #include <math.h>
 
 #include "device_util.h"
@@ -119,12 +121,10 @@ template <int R, int kWaves>
 struct Smem {
   char k[kNBuf][kTile * kKStride<R>];
   char v[kNBuf][kVBytes<R>];
-  float4 spart[kWaves][64];   // partial scores of each wave (its lanes' float4)
-  float pt[16][kTile];        // P of the slice's query heads for the current tile
-  float alpha[16];            // rescale factor of each query head for this tile
-  // cos, sin of t * omega_f for the 16 tokens t of the current tile, f < 64:
-  // rtab[f / 4][t - tok0][f % 4] (a lane's four frequencies are 32 contiguous B)
-  float2 rtab[16][kTile][4];
+  float4 spart[2][kWaves][64];   // partial scores of each wave (its lanes' float4), two tiles
+  // cos, sin of t * omega_f for the 16 tokens t of a tile, f < 64, two tiles:
+  // rtab[buf][f / 4][t - tok0][f % 4] (a lane's four frequencies are 32 contiguous B)
+  float2 rtab[2][16][kTile][4];
 };
 
 template <int R, int kP, int HW, bool kShared>
@@ -207,18 +207,22 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
       rc[e] = c1; rs[e] = s1;
     }
   };
-  auto rope_write = [&]() {
+  auto rope_write = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < kRE; ++e) {
       const int idx = tid + e * kThreads, f = idx >> 4;
-      sm.rtab[f >> 2][idx & 15][f & 3] = float2{rc[e], rs[e]};
+      sm.rtab[buf][f >> 2][idx & 15][f & 3] = float2{rc[e], rs[e]};
     }
   };
+  // the tables of tiles 0 and 1; the thread state then stands at tile 1
   rope_exact(s0);
-  rope_write();
+  rope_write(0);
+  if (rope) rope_advance();
+  rope_write(1);
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // bpermute addresses
 
-  // ---- softmax state of the owned query heads (lane ln = head slot) ---------
+  // ---- softmax state: every wave keeps it for all query heads of the slice
+  // (lane ln = query head ln of the slice), so the weights never go through LDS
   float m = -INFINITY, l = 0.f;
   // value-latent sums for all query heads of the slice over this wave's r
   // slice: acc[rb] holds r = wave*R/kWaves + 16*rb + 4*kb + i for head slot ln
@@ -231,10 +235,9 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
   const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
   const int ntiles = (t1 - s0 + kTile - 1) / kTile;
 
-  // Phase A of tile it (needs the K tile and the rotation table of tile it):
-  // rebuild the owned key blocks, rotate them and store this wave's partial
-  // scores.
-  floatx4 sc;
+  // Keys and scores of tile it (needs the K tile and the rotation table of
+  // tile it): rebuild the owned key blocks, rotate them and store this wave's
+  // partial scores.
   auto keys_scores = [&](int it) {
     const char* kt = sm.k[it % kNBuf];
     // keys of the owned blocks: K^T[16*cbs(j) + 4kb + i][token ln]
@@ -251,7 +254,7 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
     // rotate the pairs (f, f + 64): f = 16*cbs(i) + 4kb + e, token ln
 #pragma unroll
     for (int i = 0; i < kP; ++i) {
-      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[4 * cbs(i) + kb][ln][0]);
+      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[it & 1][4 * cbs(i) + kb][ln][0]);
       const float4 r01 = rt[0];
       const float4 r23 = rt[1];
       const float c4[4] = {r01.x, r01.z, r23.x, r23.z}, s4[4] = {r01.y, r01.w, r23.y, r23.w};
@@ -271,68 +274,62 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
       s1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[j], s1, 0, 0, 0);
       s2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[j], s2, 0, 0, 0);
     }
-    sc = s1 + s2;
-    sm.spart[wave][lane] = float4{sc[0], sc[1], sc[2], sc[3]};
+    const floatx4 sc = s1 + s2;
+    sm.spart[it & 1][wave][lane] = float4{sc[0], sc[1], sc[2], sc[3]};
   };
-  // Phase B of tile it (after every wave's partial scores are in LDS): the
-  // rotation table moves to tile it+1, and the first wave of each KV head
-  // runs the online softmax of its query heads and publishes P and the
-  // rescale factors.
-  auto softmax_tile = [&](int it) {
+  // Softmax and values of tile it (after every wave's partial scores are in
+  // LDS). Every wave runs the online softmax of all query heads of the slice,
+  // lane ln for query head ln (KV head ln / gqa, whose waves' partial scores
+  // it adds), and multiplies its own r slice of the value sums; the weights
+  // stay in the lane that computed them.
+  auto softmax_values = [&](int it) {
     const int tok0 = s0 + it * kTile;
-    if (it + 1 < ntiles) {
-      if ((it + 1) % kAnchor == 0) rope_exact(tok0 + kTile);
-      else if (rope) rope_advance();
-      rope_write();
-    }
-    if (part == 0) {
+    const bool hv = ln < nqs;
+    floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+    if (hv) {
+      const int jh = ln / gqa, slot = ln - jh * gqa;
 #pragma unroll
-      for (int w = 1; w < kWPH; ++w) {
-        const float4 o = sm.spart[wave + w][lane];
+      for (int w = 0; w < kWPH; ++w) {
+        const float4 o = sm.spart[it & 1][jh * kWPH + w][slot + 16 * kb];
         sc[0] += o.x; sc[1] += o.y; sc[2] += o.z; sc[3] += o.w;
       }
-      sc *= p.scale_log2;
-      if (tok0 + kTile > t1) {                           // last tile of the split
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tok0 + 4 * kb + i >= t1) sc[i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mx = fmaxf(mx, lane_xor(mx, x16));
-      mx = fmaxf(mx, lane_xor(mx, x32));
-      const float mn = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - mn);
-      l = l * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
-      if (ln < gqa) {
-        const int hg = jl * gqa + ln;                    // query head within the slice
-        *reinterpret_cast<float4*>(&sm.pt[hg][4 * kb]) = float4{pv[0], pv[1], pv[2], pv[3]};
-        if (kb == 0) sm.alpha[hg] = alpha;
-      }
     }
-  };
-  // Phase C of tile it (after P is in LDS): this wave's r slice of the value
-  // sums for all query heads of the slice.
-  auto values_tile = [&](int it) {
-    const char* vt = sm.v[it % kNBuf];
-    const bool hv = ln < nqs;
-    const float4 pp = hv ? *reinterpret_cast<const float4*>(&sm.pt[ln][4 * kb]) : float4{0.f, 0.f, 0.f, 0.f};
-    const float al = hv ? sm.alpha[ln] : 1.f;
+    sc *= p.scale_log2;
+    if (tok0 + kTile > t1) {                             // last tile of the split
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tok0 + 4 * kb + i >= t1) sc[i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, lane_xor(mx, x16));
+    mx = fmaxf(mx, lane_xor(mx, x32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    floatx4 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - mn);
+    l = l * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
     short4v ph, pl;
-    split_bf16x4(floatx4{pp.x, pp.y, pp.z, pp.w}, ph, pl);
+    split_bf16x4(pv, ph, pl);
+    const char* vt = sm.v[it % kNBuf];
     const char* vb = vt + vtile_off<R>(4 * kb, 2 * (wave * (R / kWaves) + ln));
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       short4v a;
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
-      acc[rb] *= al;
+      acc[rb] *= alpha;
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, acc[rb], 0, 0, 0);
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[rb], 0, 0, 0);
     }
+  };
+  // the rotation table of tile nt into buffer nt & 1 (the thread state moves
+  // from tile nt - 1 to nt)
+  auto rope_next = [&](int nt) {
+    if (nt % kAnchor == 0) rope_exact(s0 + nt * kTile);
+    else if (rope) rope_advance();
+    rope_write(nt & 1);
   };
 
   // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
@@ -368,11 +365,16 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
     }
   };
 
-  // Two barriers per tile. Iteration it: [after B1(it)] softmax of tile it and
-  // the copy of tile it+2 into LDS (its buffer last held tile it-1, whose
-  // values every wave finished before B1(it)); B2(it); the values of tile it
-  // and the keys and scores of tile it+1, back to back so the scheduler can
-  // interleave their MFMAs and VALU work; B1(it+1).
+  // One barrier per tile. Iteration it (after the barrier that follows the
+  // partial scores of tile it): the softmax and values of tile it; the copy
+  // of tile it+2 into LDS (its buffer last held tile it-1, finished before
+  // that barrier) and the request of tile it+4 into the same register stage;
+  // the rotation table of tile it+2 (its buffer last served tile it); the
+  // keys and partial scores of tile it+1 (their buffer last served tile
+  // it-1); the barrier. Two register stages alternate, so each request has
+  // two iterations to arrive; the barrier orders LDS only, so requests stay
+  // in flight across it; the requests are unconditional (rows past the split
+  // clamp to its last one).
   u32v ka, va, kb2, vb2;
   fetch(s0, ka, va);
   put(0, ka, va);
@@ -380,33 +382,28 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
   put(1, ka, va);
   fetch(s0 + 2 * kTile, ka, va);
   fetch(s0 + 3 * kTile, kb2, vb2);
-  __syncthreads();
+  barrier_lds();
   keys_scores(0);
-  __syncthreads();
+  barrier_lds();
+  auto iteration = [&](int it, u32v& k, u32v& v) {
+    softmax_values(it);
+    put((it + 2) % kNBuf, k, v);
+    fetch(s0 + (it + 4) * kTile, k, v);
+    if (it + 2 < ntiles) rope_next(it + 2);
+    if (it + 1 < ntiles) keys_scores(it + 1);
+    barrier_lds();
+  };
   for (int it = 0; it < ntiles; it += 2) {
-    softmax_tile(it);
-    put((it + 2) % kNBuf, ka, va);
-    fetch(s0 + (it + 4) * kTile, ka, va);
-    __syncthreads();
-    values_tile(it);
+    iteration(it, ka, va);
     if (it + 1 >= ntiles) break;
-    keys_scores(it + 1);
-    __syncthreads();
-    softmax_tile(it + 1);
-    put((it + 3) % kNBuf, kb2, vb2);
-    fetch(s0 + (it + 5) * kTile, kb2, vb2);
-    __syncthreads();
-    values_tile(it + 1);
-    if (it + 2 >= ntiles) break;
-    keys_scores(it + 2);
-    __syncthreads();
+    iteration(it + 1, kb2, vb2);
   }
 
-  // ---- partials: this wave's r slice for every query head; (m, l) by owners
+  // ---- partials: this wave's r slice for every query head; (m, l) by wave 0
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (part == 0 && ln < gqa && kb == 0) {
-    const int head = head0 + jl * gqa + ln;
+  if (wave == 0 && ln < nqs && kb == 0) {
+    const int head = head0 + ln;
     const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
     p.part_ml[slot * 2] = m;
     p.part_ml[slot * 2 + 1] = l;
