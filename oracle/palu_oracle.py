@@ -43,7 +43,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["to_f64", "latent_project", "append_rows_bf16", "quantize_rows_i8",
-           "dequantize_rows_i8", "append_rows_i8", "hadamard", "append_rows_i8_hadamard",
+           "dequantize_rows_i8", "append_rows_i8", "quantize_rows_i4", "append_rows_i4",
+           "hadamard", "append_rows_i8_hadamard", "append_rows_i4_hadamard",
            "dequantize_rows_i8_hadamard", "reconstruct", "rope_angles", "apply_rope", "softmax",
            "attend", "decode_attention", "full_rank_attention", "decode_value_latents",
            "head_layout"]
@@ -111,6 +112,28 @@ def append_rows_i8(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return quantize_rows_i8(np.asarray(h64, dtype=np.float64).astype(np.float32))
 
 
+def quantize_rows_i4(h32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token int4 quantisation of latent rows (the other width the
+    follow-on lever names; reading taken here: symmetric, 15 levels): in fp32,
+    amax = max |h|, scale = amax / 7, inv = 7 / amax (correctly rounded),
+    code = round-to-nearest-even(h * inv) clamped to [-7, 7]; a row of zeros
+    gets scale 0 and codes 0. Returns (int8 codes in [-7, 7], fp32 scales)."""
+    h = np.asarray(h32, dtype=np.float32)
+    amax = np.max(np.abs(h), axis=-1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1.0)).astype(np.float32)
+    scale = np.where(nz, safe / np.float32(7.0), np.float32(0.0)).astype(np.float32)
+    inv = np.where(nz, np.float32(7.0) / safe, np.float32(0.0)).astype(np.float32)
+    prod = (h * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(prod), -7, 7).astype(np.int8)
+    return codes, scale
+
+
+def append_rows_i4(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """int4 cache write: the exact row rounded once to fp32, then quantize_rows_i4."""
+    return quantize_rows_i4(np.asarray(h64, dtype=np.float64).astype(np.float32))
+
+
 # -------------------------------------------- Hadamard-rotated int8 cache ---
 #
 # The Palu author responses name fusing a Hadamard transform as one of the
@@ -145,9 +168,16 @@ def append_rows_i8_hadamard(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def dequantize_rows_i8_hadamard(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Latent rows of a rotated int8 cache: (code * scale) H_r / r, in fp64."""
+    """Latent rows of a rotated int8 (or int4) cache: (code * scale) H_r / r, in fp64."""
     r = codes.shape[-1]
     return dequantize_rows_i8(codes, scales) @ hadamard(r) / r
+
+
+def append_rows_i4_hadamard(h64: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Rotated int4 cache write: h H_r formed exactly, rounded once to fp32,
+    then quantize_rows_i4."""
+    h = np.asarray(h64, dtype=np.float64)
+    return quantize_rows_i4((h @ hadamard(h.shape[-1])).astype(np.float32))
 
 
 # --------------------------------------------------------- reconstruction ---

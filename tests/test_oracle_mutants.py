@@ -40,6 +40,11 @@ MUTANTS = {
                         "np.clip(np.sign(prod) * np.floor(np.abs(prod) + 0.5)"),
     "quant_column_amax": ("quantize_rows_i8", "amax = np.max(np.abs(h), axis=-1)",
                           "amax = np.broadcast_to(np.max(np.abs(h)), h.shape[:-1])"),
+    "quant4_8_steps": ("quantize_rows_i4", "np.float32(7.0) / safe", "np.float32(8.0) / safe"),
+    "quant4_floor": ("quantize_rows_i4", "np.clip(np.rint(prod), -7, 7)",
+                     "np.clip(np.floor(prod), -7, 7)"),
+    "quant4_clamp_8": ("quantize_rows_i4", "np.clip(np.rint(prod), -7, 7)",
+                       "np.clip(np.rint(prod * np.float32(1.1)), -8, 7)"),
     "hadamard_block_sign": ("hadamard", "h = np.block([[h, h], [h, -h]])",
                             "h = np.block([[h, h], [-h, h]])"),
     "hadamard_no_rescale": ("dequantize_rows_i8_hadamard", "@ hadamard(r) / r", "@ hadamard(r)"),

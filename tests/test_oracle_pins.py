@@ -350,6 +350,37 @@ def test_quantize_round_trip_and_symmetry():
     np.testing.assert_array_equal(s3, scales * np.float32(8.0))
 
 
+def test_golden_quantize_rows_i4():
+    """Hand-derived int4 codes: amax 3.5 -> scale 0.5, codes h / 0.5 rounded
+    to nearest even (1.25 -> 2.5 -> 2, 0.75 -> 1.5 -> 2, -0.25 -> -0.5 -> 0),
+    clamped to +-7; a zero row stores scale 0."""
+    h = np.array([[3.5, 1.25, 0.75, -0.25, -3.5, 0.0, 1.0, -2.75],
+                  [0.0] * 8], dtype=np.float32)
+    codes, scales = O.quantize_rows_i4(h)
+    np.testing.assert_array_equal(codes[0], [7, 2, 2, 0, -7, 0, 2, -6])
+    np.testing.assert_array_equal(codes[1], [0] * 8)
+    assert scales[0] == np.float32(0.5) and scales[1] == 0.0
+
+
+def test_quantize_i4_round_trip_and_symmetry():
+    """Codes within half a step (dequantised error at most half a scale), the
+    row maximum maps to +-7, odd under negation, invariant under 2^k scaling."""
+    rng = np.random.default_rng(47)
+    h = rng.standard_normal((64, 64)).astype(np.float32)
+    h[3] *= 100.0
+    codes, scales = O.quantize_rows_i4(h)
+    deq = O.dequantize_rows_i8(codes, scales)
+    assert np.all(np.abs(deq - h) <= scales[:, None] * (0.5 + 1e-5))
+    top = np.argmax(np.abs(h), axis=1)
+    np.testing.assert_array_equal(np.abs(codes[np.arange(64), top]), 7)
+    c2, _ = O.quantize_rows_i4(-h)
+    np.testing.assert_array_equal(c2, -codes)
+    c3, s3 = O.quantize_rows_i4(h * np.float32(4.0))
+    np.testing.assert_array_equal(c3, codes)
+    np.testing.assert_array_equal(s3, scales * np.float32(4.0))
+    assert codes.min() >= -7 and codes.max() <= 7
+
+
 @pytest.mark.parametrize("r", [1, 2, 4, 64, 256])
 def test_hadamard_is_sylvester(r):
     """Entry (i, j) of Sylvester's matrix is (-1)^popcount(i & j) (closed form,
