@@ -93,8 +93,9 @@ typedef struct palu_attn_desc {
                            caller applies B_v, e.g. fused with its output
                            projection (Palu author response, clarification of W1:
                            B_v acts after the weighted sum). FULL_RANK ignores it. */
-  int32_t hadamard;     /* palu_decode_attn_i8 only (0 elsewhere): 1 if the int8 cache
-                           holds Hadamard-rotated rows (see palu_latent_append_i8) */
+  int32_t hadamard;     /* palu_decode_attn_i8 / _i4 only (0 elsewhere): 1 if the
+                           quantised cache holds Hadamard-rotated rows (see
+                           palu_latent_append_i8) */
 } palu_attn_desc;
 
 /* Bytes of device workspace palu_decode_attn needs for this descriptor
@@ -166,15 +167,40 @@ palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* The int4 latent cache: the same per-token scheme at 4 bits (the author
+ * responses fix no code width for quantised latents; 4 bits halves the int8
+ * cache again), codes in [-7, 7] stored as the nibble code + 8.
+ *   codes h_k, h_v: B*G slabs of L_cap*r/2 bytes; s_k, s_v [B, G, L_cap] fp32.
+ *   Latent k of token t of slab (b, g) is code * scale; with
+ *     keys:   u = (r/32)*((t%32)/16) + k/32, l = 16*((k%32)/8) + t%16,
+ *             e = (k%8)/4 + 2*(k%2), n = (k/2)%2
+ *     values: u = k/16, l = 16*((t%16)/4) + k%16,
+ *             e = (t%32)/16 + 2*(t%2), n = (t%4)/2
+ *   its nibble is the high (n = 1) or low (n = 0) half of the byte at
+ *     16r*(t/32) + 1024*(u/4) + 16*l + 4*(u%4) + e
+ *   inside its slab (L_cap % 32 == 0, r in {64, 128, 256}): 32-bit unit u of
+ *   lane l of the decode kernel's matrix-core operand, whose element 2m sits
+ *   in nibble m and 2m+1 in nibble m+4. Each 32-token block is a permutation
+ *   of its own 16 r bytes' nibbles. hadamard as for the int8 cache.
+ *
+ * palu_decode_attn over such a cache, as palu_decode_attn_i8 (same rules,
+ * restrictions and errors, the int4 slabs in place of the int8 ones). */
+palu_status palu_decode_attn_i4(const palu_attn_desc* desc, const void* q, const uint8_t* h_k,
+                                const uint8_t* h_v, const float* s_k, const float* s_v,
+                                const void* b_k, const void* b_v, const int32_t* seq_lens,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 typedef struct palu_append_desc {
   int32_t batch;     /* B >= 1                                                    */
   int32_t d_model;   /* width of x, 1..65536                                      */
   int32_t n_groups;  /* G >= 1                                                    */
   int32_t rank;      /* r, 1..512                                                 */
   int32_t max_ctx;   /* L_cap: row stride of the cache                             */
-  int32_t dtype;     /* palu_dtype of x, a_k, a_v and (except the int8 calls) the cache */
-  int32_t hadamard;  /* palu_latent_append_i8 only (0 elsewhere): 1 rotates each row by
-                        the Hadamard matrix before quantising */
+  int32_t dtype;     /* palu_dtype of x, a_k, a_v and (except the int8 / int4 calls)
+                        the cache */
+  int32_t hadamard;  /* palu_latent_append_i8 / _i4 only (0 elsewhere): 1 rotates each
+                        row by the Hadamard matrix before quantising */
 } palu_append_desc;
 
 /* Bytes of device workspace palu_latent_append needs for this descriptor:
@@ -222,6 +248,22 @@ palu_status palu_latent_append_i8_workspace(const palu_append_desc* desc, size_t
  * palu_latent_append. */
 palu_status palu_latent_append_i8(const palu_append_desc* desc, const void* x, const void* a_k,
                                   const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
+                                  float* s_v, const int32_t* pos, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace palu_latent_append_i4 needs (the same areas as
+ * for palu_latent_append_i8, under the same zero-counter rule). */
+palu_status palu_latent_append_i4_workspace(const palu_append_desc* desc, size_t* bytes);
+
+/* Quantised cache write of one token per sequence into the int4 cache that
+ * palu_decode_attn_i4 reads (layout above), as palu_latent_append_i8 with 7
+ * in place of 127: s = amax / 7, code = round(h[k] * 7 / amax) clamped to
+ * [-7, 7]. A value byte also holds the code of another token of the same
+ * block (t xor 2), which is kept: the call reads and rewrites that byte, so
+ * calls that write either token must not overlap. h_k, h_v 4-byte aligned.
+ * Restrictions, workspace rules and errors as in palu_latent_append_i8. */
+palu_status palu_latent_append_i4(const palu_append_desc* desc, const void* x, const void* a_k,
+                                  const void* a_v, uint8_t* h_k, uint8_t* h_v, float* s_k,
                                   float* s_v, const int32_t* pos, void* workspace,
                                   size_t workspace_bytes, void* stream);
 

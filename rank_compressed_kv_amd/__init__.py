@@ -24,7 +24,9 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_decode_attn_i8", "decode_attention_i8", "palu_latent_append_workspace",
+           "palu_decode_attn_i8", "decode_attention_i8", "palu_decode_attn_i4",
+           "decode_attention_i4", "palu_latent_append_workspace",
+           "palu_latent_append_i4_workspace", "palu_latent_append_i4", "latent_append_i4",
            "palu_latent_append_i8_workspace", "palu_latent_append_i8", "latent_append_i8", "palu_latent_append", "palu_profile_begin",
            "palu_profile_end", "attn_desc", "append_desc", "decode_attention", "latent_append",
            "EXPORTED_SYMBOLS"]
@@ -35,9 +37,10 @@ PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-                    "palu_decode_attn_i8",
+                    "palu_decode_attn_i8", "palu_decode_attn_i4",
                     "palu_latent_append_workspace", "palu_latent_append",
                     "palu_latent_append_i8_workspace", "palu_latent_append_i8",
+                    "palu_latent_append_i4_workspace", "palu_latent_append_i4",
                     "palu_profile_begin", "palu_profile_end",
                     "palu_status_string", "palu_last_error")
 
@@ -90,21 +93,22 @@ def library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
-    lib.palu_decode_attn_i8.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, sz, vp]
+    for fn in ("palu_decode_attn_i8", "palu_decode_attn_i4"):
+        getattr(lib, fn).argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, sz, vp]
     lib.palu_latent_append_workspace.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
     lib.palu_latent_append.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
-    lib.palu_latent_append_i8_workspace.argtypes = [ctypes.POINTER(AppendDesc),
-                                                    ctypes.POINTER(sz)]
-    lib.palu_latent_append_i8.argtypes = [ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp,
-                                          vp, vp, vp, sz, vp]
+    for b in ("i8", "i4"):
+        getattr(lib, f"palu_latent_append_{b}_workspace").argtypes = [
+            ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
+        getattr(lib, f"palu_latent_append_{b}").argtypes = [
+            ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.palu_profile_begin.argtypes = [ctypes.c_int32]
     lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
-    for fn in ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-               "palu_decode_attn_i8", "palu_latent_append_workspace",
-               "palu_latent_append_i8_workspace", "palu_latent_append_i8", "palu_latent_append", "palu_profile_begin",
-               "palu_profile_end"):
+    for fn in EXPORTED_SYMBOLS:
+        if fn in ("palu_status_string", "palu_last_error"):
+            continue
         getattr(lib, fn).restype = ctypes.c_int
     lib.palu_status_string.argtypes = [ctypes.c_int]
     lib.palu_status_string.restype = ctypes.c_char_p
@@ -199,10 +203,8 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
 
 
-def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
-                        workspace, stream=None) -> None:
-    """Enqueue one decode step over an int8 latent cache: h_k, h_v [B, G, L, r]
-    int8 codes, s_k, s_v [B, G, L] float32 row scales."""
+def _decode_quant(bits: int, desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
+                  workspace, stream) -> None:
     palu_decode_attn_plan(desc)          # the library validates the descriptor first
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r, L = desc.n_groups, desc.rank, desc.max_ctx
@@ -211,9 +213,11 @@ def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_len
     if dt is None:
         raise TypeError(f"unknown dtype code {desc.dtype}")
     latent = bool(desc.latent_out)
+    cache = (B, G, L, r) if bits == 8 else (B, G, L, r // 2)
+    ctype = torch.int8 if bits == 8 else torch.uint8
     _need(q, "q", (B, Hq, d), dt)
-    _need(h_k, "h_k", (B, G, L, r), torch.int8)
-    _need(h_v, "h_v", (B, G, L, r), torch.int8)
+    _need(h_k, "h_k", cache, ctype)
+    _need(h_v, "h_v", cache, ctype)
     _need(s_k, "s_k", (B, G, L), torch.float32)
     _need(s_v, "s_v", (B, G, L), torch.float32)
     _need(b_k, "b_k", (G, r, dg), dt)
@@ -225,11 +229,26 @@ def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_len
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(library().palu_decode_attn_i8(
+    name = f"palu_decode_attn_i{bits}"
+    _check(getattr(library(), name)(
         ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), s_k.data_ptr(),
         s_v.data_ptr(), b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
         None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
-        workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn_i8")
+        workspace.data_ptr(), nbytes, _stream(stream)), name)
+
+
+def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
+                        workspace, stream=None) -> None:
+    """Enqueue one decode step over an int8 latent cache: h_k, h_v [B, G, L, r]
+    int8 codes, s_k, s_v [B, G, L] float32 row scales."""
+    _decode_quant(8, desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace, stream)
+
+
+def palu_decode_attn_i4(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
+                        workspace, stream=None) -> None:
+    """Enqueue one decode step over an int4 latent cache: h_k, h_v [B, G, L, r/2]
+    uint8 (two biased 4-bit codes a byte), s_k, s_v [B, G, L] float32."""
+    _decode_quant(4, desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace, stream)
 
 
 def palu_latent_append_workspace(desc: AppendDesc) -> int:
@@ -268,29 +287,52 @@ def palu_latent_append_i8_workspace(desc: AppendDesc) -> int:
     return int(n.value)
 
 
-def palu_latent_append_i8(desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace,
-                          stream=None) -> None:
-    """Quantised cache write: h_k, h_v [B, G, L, r] int8, s_k, s_v [B, G, L] float32."""
-    palu_latent_append_i8_workspace(desc)   # the library validates the descriptor first
+def palu_latent_append_i4_workspace(desc: AppendDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().palu_latent_append_i4_workspace(ctypes.byref(desc), ctypes.byref(n)),
+           "palu_latent_append_i4_workspace")
+    return int(n.value)
+
+
+def _append_quant(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
+                  workspace, stream) -> None:
+    # the library validates the descriptor first
+    (palu_latent_append_i8_workspace if bits == 8 else palu_latent_append_i4_workspace)(desc)
     B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
     dt = _TORCH_DTYPE.get(desc.dtype)
     if dt is None:
         raise TypeError(f"unknown dtype code {desc.dtype}")
+    cache = (B, G, L, r) if bits == 8 else (B, G, L, r // 2)
+    ctype = torch.int8 if bits == 8 else torch.uint8
     _need(x, "x", (B, dm), dt)
     _need(a_k, "a_k", (dm, G * r), dt)
     _need(a_v, "a_v", (dm, G * r), dt)
-    _need(h_k, "h_k", (B, G, L, r), torch.int8)
-    _need(h_v, "h_v", (B, G, L, r), torch.int8)
+    _need(h_k, "h_k", cache, ctype)
+    _need(h_v, "h_v", cache, ctype)
     _need(s_k, "s_k", (B, G, L), torch.float32)
     _need(s_v, "s_v", (B, G, L), torch.float32)
     _need(pos, "pos", (B,), torch.int32)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(library().palu_latent_append_i8(
+    name = f"palu_latent_append_i{bits}"
+    _check(getattr(library(), name)(
         ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),
         h_v.data_ptr(), s_k.data_ptr(), s_v.data_ptr(), pos.data_ptr(), workspace.data_ptr(),
-        nbytes, _stream(stream)), "palu_latent_append_i8")
+        nbytes, _stream(stream)), name)
+
+
+def palu_latent_append_i8(desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace,
+                          stream=None) -> None:
+    """Quantised cache write: h_k, h_v [B, G, L, r] int8, s_k, s_v [B, G, L] float32."""
+    _append_quant(8, desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream)
+
+
+def palu_latent_append_i4(desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace,
+                          stream=None) -> None:
+    """Quantised cache write: h_k, h_v [B, G, L, r/2] uint8 (4-bit codes), s_k, s_v
+    [B, G, L] float32."""
+    _append_quant(4, desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream)
 
 
 def palu_profile_begin(max_records: int) -> None:
@@ -347,13 +389,11 @@ def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
     return out
 
 
-def decode_attention_i8(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
-                        scale: float = 0.0, split_tokens: int = 0, latent_out: bool = False,
-                        hadamard: bool = False, out=None, workspace=None, stream=None):
-    """Absorbed-mode decode over int8 latents (codes h_k, h_v with row scales
-    s_k, s_v). Allocates out and the workspace with torch when not given."""
+def _decode_attention_quant(bits, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, n_kv_heads,
+                            scale, split_tokens, latent_out, hadamard, out, workspace, stream):
     B, Hq, d = q.shape
-    _, G, L, r = h_k.shape
+    _, G, L, rr = h_k.shape
+    r = rr if bits == 8 else 2 * rr
     desc = attn_desc(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, n_groups=G,
                      rank=r, max_ctx=L, dtype=_dt(q), mode="absorbed", scale=scale,
                      split_tokens=split_tokens, latent_out=latent_out, hadamard=hadamard)
@@ -363,8 +403,29 @@ def decode_attention_i8(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_
     if workspace is None:
         workspace = torch.empty(palu_decode_attn_workspace(desc), dtype=torch.uint8,
                                 device=q.device)
-    palu_decode_attn_i8(desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace, stream)
+    _decode_quant(bits, desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace, stream)
     return out
+
+
+def decode_attention_i8(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
+                        scale: float = 0.0, split_tokens: int = 0, latent_out: bool = False,
+                        hadamard: bool = False, out=None, workspace=None, stream=None):
+    """Absorbed-mode decode over int8 latents (codes h_k, h_v with row scales
+    s_k, s_v). Allocates out and the workspace with torch when not given."""
+    return _decode_attention_quant(8, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, n_kv_heads,
+                                   scale, split_tokens, latent_out, hadamard, out, workspace,
+                                   stream)
+
+
+def decode_attention_i4(q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
+                        scale: float = 0.0, split_tokens: int = 0, latent_out: bool = False,
+                        hadamard: bool = False, out=None, workspace=None, stream=None):
+    """Absorbed-mode decode over int4 latents (h_k, h_v [B, G, L, r/2] uint8 in
+    the tiled nibble order, row scales s_k, s_v). Allocates out and the
+    workspace with torch when not given."""
+    return _decode_attention_quant(4, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, n_kv_heads,
+                                   scale, split_tokens, latent_out, hadamard, out, workspace,
+                                   stream)
 
 
 def full_rank_attention(q, k, v, seq_lens=None, *, scale: float = 0.0, split_tokens: int = 0,
@@ -396,16 +457,30 @@ def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> No
     palu_latent_append(desc, x, a_k, a_v, h_k, h_v, pos, workspace, stream)
 
 
+def _latent_append_quant(bits, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream,
+                         hadamard) -> None:
+    B, dm = x.shape
+    _, G, L, rr = h_k.shape
+    r = rr if bits == 8 else 2 * rr
+    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x),
+                       hadamard=hadamard)
+    if workspace is None:
+        need = (palu_latent_append_i8_workspace if bits == 8
+                else palu_latent_append_i4_workspace)(desc)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    _append_quant(bits, desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream)
+
+
 def latent_append_i8(x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace=None, stream=None, *,
                      hadamard: bool = False) -> None:
     """Quantised cache write into an int8 cache (rows rotated by the Hadamard
     matrix first with hadamard=True). Allocates the (zeroed) workspace with
     torch when it is not given."""
-    B, dm = x.shape
-    _, G, L, r = h_k.shape
-    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x),
-                       hadamard=hadamard)
-    if workspace is None:
-        workspace = torch.zeros(palu_latent_append_i8_workspace(desc), dtype=torch.uint8,
-                                device=x.device)
-    palu_latent_append_i8(desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream)
+    _latent_append_quant(8, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream, hadamard)
+
+
+def latent_append_i4(x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace=None, stream=None, *,
+                     hadamard: bool = False) -> None:
+    """Quantised cache write into an int4 cache (h_k, h_v [B, G, L, r/2] uint8).
+    Allocates the (zeroed) workspace with torch when it is not given."""
+    _latent_append_quant(4, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, stream, hadamard)

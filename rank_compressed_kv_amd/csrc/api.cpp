@@ -218,8 +218,8 @@ namespace {
 
 // both decode entry points; s_k, s_v non-NULL selects int8 latents
 palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, const void* h_v,
-                   const float* s_k, const float* s_v, const void* b_k, const void* b_v,
-                   const int32_t* seq_lens, float* out, void* workspace,
+                   const float* s_k, const float* s_v, int qbits, const void* b_k,
+                   const void* b_v, const int32_t* seq_lens, float* out, void* workspace,
                    size_t workspace_bytes, void* stream) {
   const bool full = desc->mode == PALU_MODE_FULL_RANK;
   const bool latent = !full && desc->latent_out != 0;
@@ -227,8 +227,8 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
     return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
                                "must be non-NULL");
   const Plan pl = make_plan(desc);
-  if (s_k && pl.kernel != SplitKernel::kAbsorbedMfma)
-    return fail(PALU_ERR_UNSUPPORTED, "int8 latents need the absorbed MFMA kernel");
+  if (qbits && pl.kernel != SplitKernel::kAbsorbedMfma)
+    return fail(PALU_ERR_UNSUPPORTED, "quantised latents need the absorbed MFMA kernel");
   const WorkspaceLayout wl = layout(desc, pl);
   if (workspace_bytes < wl.total)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
@@ -247,7 +247,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   p.rope = desc->rope_theta > 0.0 ? 1 : 0;
   p.full_rank = full ? 1 : 0;
   p.latent_out = latent ? 1 : 0;
-  p.latent_i8 = s_k ? 1 : 0;
+  p.qbits = qbits;
   p.hadamard = desc->hadamard;
   p.s_k = s_k; p.s_v = s_v;
   for (int i = 0; i < p.d / 2; ++i)
@@ -266,7 +266,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
   switch (pl.kernel) {
     case SplitKernel::kAbsorbedMfma:
-      e = p.latent_i8 ? launch_split_absorbed_i8(p, s) : launch_split_absorbed_mfma(p, s);
+      e = p.qbits ? launch_split_absorbed_quant(p, s) : launch_split_absorbed_mfma(p, s);
       break;
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
@@ -277,6 +277,33 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   e = launch_merge(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// both quantised decode entry points: bits 8 (int8) or 4 (int4)
+palu_status decode_quant(const palu_attn_desc* desc, int bits, const void* q, const void* h_k,
+                         const void* h_v, const float* s_k, const float* s_v, const void* b_k,
+                         const void* b_v, const int32_t* seq_lens, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  if (desc->mode != PALU_MODE_ABSORBED || desc->dtype != PALU_BF16 ||
+      (desc->rank != 64 && desc->rank != 128 && desc->rank != 256))
+    return fail(PALU_ERR_UNSUPPORTED,
+                "int%d latents need mode ABSORBED, dtype BF16 and rank 64, 128 or 256 "
+                "(got mode %d, dtype %d, rank %d)", bits, desc->mode, desc->dtype, desc->rank);
+  if (desc->max_ctx % 32)
+    return fail(PALU_ERR_SHAPE, "int%d cache needs max_ctx %% 32 == 0 (got %d)", bits,
+                desc->max_ctx);
+  if (desc->hadamard != 0 && desc->hadamard != 1)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard must be 0 or 1 (got %d)", desc->hadamard);
+  if (!absorbed_quant_supported(shape_params(desc), desc->dtype))
+    return fail(PALU_ERR_UNSUPPORTED, "int%d latents: combination not provided", bits);
+  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(h_k) | reinterpret_cast<uintptr_t>(h_v) |
+       reinterpret_cast<uintptr_t>(s_k) | reinterpret_cast<uintptr_t>(s_v)) % 16)
+    return fail(PALU_ERR_SHAPE, "int%d caches and scales must be 16-byte aligned", bits);
+  return decode(desc, q, h_k, h_v, s_k, s_v, bits, b_k, b_v, seq_lens, out, workspace,
+                workspace_bytes, stream);
 }
 
 }  // namespace
@@ -290,8 +317,8 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
   palu_status st = validate_attn(desc);
   if (st != PALU_OK) return st;
   if (desc->hadamard)
-    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 cache only");
-  return decode(desc, q, h_k, h_v, nullptr, nullptr, b_k, b_v, seq_lens, out, workspace,
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
+  return decode(desc, q, h_k, h_v, nullptr, nullptr, 0, b_k, b_v, seq_lens, out, workspace,
                 workspace_bytes, stream);
 }
 
@@ -300,25 +327,17 @@ palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const
                                 const void* b_k, const void* b_v, const int32_t* seq_lens,
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  palu_status st = validate_attn(desc);
-  if (st != PALU_OK) return st;
-  if (desc->mode != PALU_MODE_ABSORBED || desc->dtype != PALU_BF16 ||
-      (desc->rank != 64 && desc->rank != 128 && desc->rank != 256))
-    return fail(PALU_ERR_UNSUPPORTED,
-                "int8 latents need mode ABSORBED, dtype BF16 and rank 64, 128 or 256 "
-                "(got mode %d, dtype %d, rank %d)", desc->mode, desc->dtype, desc->rank);
-  if (desc->max_ctx % 32)
-    return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", desc->max_ctx);
-  if (desc->hadamard != 0 && desc->hadamard != 1)
-    return fail(PALU_ERR_UNSUPPORTED, "hadamard must be 0 or 1 (got %d)", desc->hadamard);
-  if (!absorbed_i8_supported(shape_params(desc), desc->dtype))
-    return fail(PALU_ERR_UNSUPPORTED, "int8 latents: combination not provided");
-  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
-  if ((reinterpret_cast<uintptr_t>(h_k) | reinterpret_cast<uintptr_t>(h_v) |
-       reinterpret_cast<uintptr_t>(s_k) | reinterpret_cast<uintptr_t>(s_v)) % 16)
-    return fail(PALU_ERR_SHAPE, "int8 caches and scales must be 16-byte aligned");
-  return decode(desc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace,
-                workspace_bytes, stream);
+  return decode_quant(desc, 8, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace,
+                      workspace_bytes, stream);
+}
+
+palu_status palu_decode_attn_i4(const palu_attn_desc* desc, const void* q, const uint8_t* h_k,
+                                const uint8_t* h_v, const float* s_k, const float* s_v,
+                                const void* b_k, const void* b_v, const int32_t* seq_lens,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_quant(desc, 4, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -337,27 +356,29 @@ palu_status validate_append(const palu_append_desc* d) {
   return PALU_OK;
 }
 
-palu_status validate_append_i8(const palu_append_desc* d) {
+palu_status validate_append_quant(const palu_append_desc* d, int bits) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
   if (d->rank != 64 && d->rank != 128 && d->rank != 256)
-    return fail(PALU_ERR_UNSUPPORTED, "int8 cache needs rank 64, 128 or 256 (got %d)", d->rank);
+    return fail(PALU_ERR_UNSUPPORTED, "int%d cache needs rank 64, 128 or 256 (got %d)", bits,
+                d->rank);
   if (d->max_ctx % 32)
-    return fail(PALU_ERR_SHAPE, "int8 cache needs max_ctx %% 32 == 0 (got %d)", d->max_ctx);
+    return fail(PALU_ERR_SHAPE, "int%d cache needs max_ctx %% 32 == 0 (got %d)", bits,
+                d->max_ctx);
   if (d->hadamard != 0 && d->hadamard != 1)
     return fail(PALU_ERR_UNSUPPORTED, "hadamard must be 0 or 1 (got %d)", d->hadamard);
   return PALU_OK;
 }
 
-// both append entry points; s_k non-NULL selects the int8 cache
-palu_status append(const palu_append_desc* d, const void* x, const void* a_k, const void* a_v,
-                   void* h_k, void* h_v, float* s_k, float* s_v, const int32_t* pos,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  const bool quant = s_k != nullptr;
+// every append entry point; qbits 8 / 4: int8 / int4 cache with scales, 0: dtype
+palu_status append(const palu_append_desc* d, int qbits, const void* x, const void* a_k,
+                   const void* a_v, void* h_k, void* h_v, float* s_k, float* s_v,
+                   const int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool quant = qbits != 0;
   if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
     return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
   if (quant && (reinterpret_cast<uintptr_t>(h_k) % 4 || reinterpret_cast<uintptr_t>(h_v) % 4))
-    return fail(PALU_ERR_SHAPE, "int8 caches must be 4-byte aligned");
+    return fail(PALU_ERR_SHAPE, "int%d caches must be 4-byte aligned", qbits);
   const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, quant);
   if (workspace_bytes < need)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -366,7 +387,7 @@ palu_status append(const palu_append_desc* d, const void* x, const void* a_k, co
   AppendParams p{};
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
   p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
-  p.quant = quant ? 1 : 0;
+  p.quant = qbits;
   p.hadamard = d->hadamard;
   p.s_k = s_k; p.s_v = s_v;
   append_bind_workspace(p, workspace);
@@ -392,13 +413,13 @@ palu_status palu_latent_append(const palu_append_desc* d, const void* x, const v
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
   if (d->hadamard)
-    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 cache only");
-  return append(d, x, a_k, a_v, h_k, h_v, nullptr, nullptr, pos, workspace, workspace_bytes,
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
+  return append(d, 0, x, a_k, a_v, h_k, h_v, nullptr, nullptr, pos, workspace, workspace_bytes,
                 stream);
 }
 
 palu_status palu_latent_append_i8_workspace(const palu_append_desc* d, size_t* bytes) {
-  palu_status st = validate_append_i8(d);
+  palu_status st = validate_append_quant(d, 8);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
   *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, true);
@@ -409,10 +430,28 @@ palu_status palu_latent_append_i8(const palu_append_desc* d, const void* x, cons
                                   const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
                                   float* s_v, const int32_t* pos, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  palu_status st = validate_append_i8(d);
+  palu_status st = validate_append_quant(d, 8);
   if (st != PALU_OK) return st;
   if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
-  return append(d, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
+  return append(d, 8, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
+}
+
+palu_status palu_latent_append_i4_workspace(const palu_append_desc* d, size_t* bytes) {
+  palu_status st = validate_append_quant(d, 4);
+  if (st != PALU_OK) return st;
+  if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, true);
+  return ok();
+}
+
+palu_status palu_latent_append_i4(const palu_append_desc* d, const void* x, const void* a_k,
+                                  const void* a_v, uint8_t* h_k, uint8_t* h_v, float* s_k,
+                                  float* s_v, const int32_t* pos, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  palu_status st = validate_append_quant(d, 4);
+  if (st != PALU_OK) return st;
+  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  return append(d, 4, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
 }
 
 palu_status palu_profile_begin(int32_t max_records) {

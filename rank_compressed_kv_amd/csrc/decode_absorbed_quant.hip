@@ -1,17 +1,19 @@
-// Context-split decode kernel for the absorbed-key mode over an int8 latent
-// cache (per-token quantisation of the latents, Palu author response to
-// reviewer Fsn9 on W1/W2: codes with one fp32 scale per cached row, h = code *
-// scale), on the gfx950 matrix cores.
+// Context-split decode kernel for the absorbed-key mode over an int8 or int4
+// latent cache (per-token quantisation of the latents, Palu author response
+// to reviewer Fsn9 on W1/W2: codes with one fp32 scale per cached row, h =
+// code * scale), on the gfx950 matrix cores.
 //
 // The scores and the value sum are those of the bf16 kernel (absorbed keys:
 // q~ = q B_k^T scored against the key latents, value latents summed with the
 // weights, B_v applied in the merge); what differs is the cache and the data
 // path:
-//   - the int8 cache is stored in 32-token blocks whose byte order is that of
+//   - the quantised cache is stored in 32-token blocks whose byte order is that of
 //     the MFMA operands (the append kernel writes it), so every 16-byte load of
 //     a lane holds exactly the operand bytes that lane needs: no LDS staging,
 //     no gathers, fully coalesced 1 KiB per load instruction;
-//   - codes are widened to fp16 in registers (exact for |code| <= 127) and
+//   - codes are widened to fp16 in registers (exact for |code| <= 127; int4
+//     codes sit biased in nibbles ordered so that one shift and one and-or
+//     give a pair of operand elements) and
 //     multiplied on fp16 MFMAs, 16x16x32 for the scores (16 tokens x 16 heads
 //     over 32 latents) and for the values (r x 16 heads over 32 tokens);
 //   - a block's key scales multiply its scores, its value scales fold into the
@@ -70,6 +72,20 @@ __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
   const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
   return uint4{a.x, a.y, b.x, b.y};
 }
+// eight int4 codes, stored biased (u = code + 8) with operand element 2m in
+// nibble m and 2m+1 in nibble m+4 -> one 8 x fp16 MFMA operand, exactly: the
+// fp16 with bits 0x640u is 1024 + u, so one shift and one and-or per pair
+// and one packed subtraction of 1032 give the codes
+__device__ __forceinline__ uint4 widen4(uint32_t w) {
+  const half2v bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  uint32_t r[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t pr = ((w >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+    r[m] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr) - bias);
+  }
+  return uint4{r[0], r[1], r[2], r[3]};
+}
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
@@ -102,18 +118,20 @@ struct State {
   float l;               // this lane's share of the running sum
 };
 
-// One cache block in registers: R/32 16-byte words of each matrix (word i of
-// lane l is bytes [1024 i + 16 l, +16) of the block) and the key and value
-// scales of the lane's eight tokens 4*(l/16) + i and 16 + 4*(l/16) + i.
-template <int R>
+// One cache block in registers: R*kBits/256 16-byte words of each matrix
+// (word i of lane l is bytes [1024 i + 16 l, +16) of the block) and the key
+// and value scales of the lane's eight tokens 4*(l/16) + i and 16 + 4*(l/16)
+// + i.
+template <int R, int kBits>
 struct Block {
-  typedef uint32_t u32v __attribute__((ext_vector_type(R / 8)));
+  typedef uint32_t u32v __attribute__((ext_vector_type(R * kBits / 64)));
   u32v k, v;
   floatx4 sk0, sk1, sv0, sv1;
 };
 
-template <int R, bool kShared>
-__global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(DecodeParams p) {
+template <int R, bool kShared, int kBits>
+__global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(DecodeParams p) {
+  constexpr int kRowBytes = R * kBits / 8;               // bytes of a cached row
   const int nslice = (p.nq + 15) / 16;
   const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
   if (!un.live) return;
@@ -129,19 +147,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 
   __shared__ Smem<R> sm;
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
-  const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * R;
-  const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * R;
+  const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * kRowBytes;
+  const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * kRowBytes;
   const int nblk = (t1 - s0 + kBlock - 1) / kBlock;
   const int mine = (nblk - wave + kWaves - 1) / kWaves;   // blocks of this wave, may be 0
   auto tok_of = [&](int j) { return s0 + kBlock * (wave + kWaves * j); };
 
-  // one matrix's R/32 words of the block at t0 (t0 % 32 == 0) and the
-  // scales of the lane's eight tokens (16-byte aligned: L % 32 == 0)
-  auto fetch_half = [&](typename Block<R>::u32v& w, floatx4& s0v, floatx4& s1v,
+  // one matrix's words of the block at t0 (t0 % 32 == 0) and the scales of
+  // the lane's eight tokens (16-byte aligned: L % 32 == 0)
+  auto fetch_half = [&](typename Block<R, kBits>::u32v& w, floatx4& s0v, floatx4& s1v,
                         const int8_t* H, const float* S, int t0) {
-    const size_t base = static_cast<size_t>(t0) * R + lane * 16;
+    const size_t base = static_cast<size_t>(t0) * kRowBytes + lane * 16;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
+    for (int i = 0; i < R * kBits / 256; ++i) {
       const uint4 a = load_tile16<kShared>(H + base + i * 1024);
       w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
     }
@@ -151,11 +169,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     s0v = floatx4{a0.x, a0.y, a0.z, a0.w};
     s1v = floatx4{a1.x, a1.y, a1.z, a1.w};
   };
-  auto fetch = [&](Block<R>& x, int t0) {
+  auto fetch = [&](Block<R, kBits>& x, int t0) {
     fetch_half(x.k, x.sk0, x.sk1, Hk, p.s_k, t0);
     fetch_half(x.v, x.sv0, x.sv1, Hv, p.s_v, t0);
   };
-  Block<R> xa, xb;
+  Block<R, kBits> xa, xb;
 
   {
     // every load of this prologue is issued before the first is used: the
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Block<R>& x, int t0) {
+  auto compute = [&](const Block<R, kBits>& x, int t0) {
     // q~ is read from LDS again for every block: held in registers across the
     // loop it would take 128 of them at r = 256 (a compiler-only barrier keeps
     // the reads inside)
@@ -278,8 +296,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
       for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < R / 32; ++c) {
-        const int w = 4 * (h * (R / 64) + c / 2) + 2 * (c % 2);
-        const uint4 a = widen8(x.k[w], x.k[w + 1]);
+        // int8: word h*R/64 + c/2, bytes 8*(c%2) .. +8; int4: the lane's
+        // 32-bit unit h*R/32 + c
+        uint4 a;
+        if constexpr (kBits == 8) {
+          const int w = 4 * (h * (R / 64) + c / 2) + 2 * (c % 2);
+          a = widen8(x.k[w], x.k[w + 1]);
+        } else {
+          a = widen4(x.k[h * (R / 32) + c]);
+        }
         const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[0][ln][32 * c + 8 * kb]);
         const uint4 ql = *reinterpret_cast<const uint4*>(&sm.q[1][ln][32 * c + 8 * kb]);
         acc4[2 * (c & 1)] = mfma(a, qh, acc4[2 * (c & 1)]);
@@ -329,8 +354,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
     // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
 #pragma unroll
     for (int rb = 0; rb < R / 16; ++rb) {
-      const int w = 4 * (rb / 2) + 2 * (rb % 2);
-      const uint4 a = widen8(x.v[w], x.v[w + 1]);
+      uint4 a;
+      if constexpr (kBits == 8) {
+        const int w = 4 * (rb / 2) + 2 * (rb % 2);
+        a = widen8(x.v[w], x.v[w + 1]);
+      } else {
+        a = widen4(x.v[rb]);                             // the lane's unit rb
+      }
       st.acc[rb] = mfma(a, bh, st.acc[rb]);
       st.acc[rb] = mfma(a, bl, st.acc[rb]);
     }
@@ -432,30 +462,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_i8_kernel(Decod
   }
 }
 
-template <int R>
+template <int R, int kBits>
 hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
   const int nslice = absorbed_head_slices(p.nq);
   if (nslice == 1) {
-    split_absorbed_i8_kernel<R, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+    split_absorbed_int_kernel<R, false, kBits><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
   } else {
     const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
     if (ids == 0) return hipErrorInvalidValue;
-    split_absorbed_i8_kernel<R, true><<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
+    split_absorbed_int_kernel<R, true, kBits>
+        <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool absorbed_i8_supported(const DecodeParams& p, int dtype) {
+bool absorbed_quant_supported(const DecodeParams& p, int dtype) {
   return dtype == 1 && (p.r == 64 || p.r == 128 || p.r == 256) && p.L % kBlock == 0;
 }
 
-hipError_t launch_split_absorbed_i8(const DecodeParams& p, hipStream_t st) {
-  switch (p.r) {
-    case 64: return launch_rank<64>(p, st);
-    case 128: return launch_rank<128>(p, st);
-    case 256: return launch_rank<256>(p, st);
+hipError_t launch_split_absorbed_quant(const DecodeParams& p, hipStream_t st) {
+  switch (p.r * 16 + p.qbits) {
+    case 64 * 16 + 8: return launch_rank<64, 8>(p, st);
+    case 128 * 16 + 8: return launch_rank<128, 8>(p, st);
+    case 256 * 16 + 8: return launch_rank<256, 8>(p, st);
+    case 64 * 16 + 4: return launch_rank<64, 4>(p, st);
+    case 128 * 16 + 4: return launch_rank<128, 4>(p, st);
+    case 256 * 16 + 4: return launch_rank<256, 4>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

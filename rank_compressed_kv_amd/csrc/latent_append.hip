@@ -34,9 +34,10 @@ namespace palu {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 128;          // d_model rows per slice
+constexpr int kRows = 128;          // d_model rows per slice (256 and 512 measured slower)
 constexpr int kCols = 128;          // columns per block (16 chunks of 8)
-constexpr int kRowGroups = 16;      // threads per column chunk; 8 rows each
+constexpr int kRowGroups = 16;      // threads per column chunk
+constexpr int kRowsPerThread = kRows / kRowGroups;
 constexpr int kBatchChunk = 8;      // sequences accumulated per pass
 constexpr size_t kCounterAlign = 256;
 
@@ -79,6 +80,28 @@ __device__ __forceinline__ size_t i8_value_offset(int t, int k, int r) {
          (k % 16) * 16 + ((k / 16) % 2) * 8 + ((t % 32) / 16) * 4 + t % 4;
 }
 
+// int4 cache: byte of latent k of token t inside one (b, g) slab (32-token
+// blocks of 16 r bytes, word w of lane l at 1024 w + 16 l as for int8) and the
+// nibble it occupies (hi = 1: the high nibble). A lane's 32-bit unit holds its
+// eight operand elements, element 2m in nibble m and 2m+1 in nibble m+4; keys:
+// unit h*r/32 + c of half h and chunk c (elements: latents 32c + 8kb + j);
+// values: unit rb (elements: tokens 4kb + j and 16 + 4kb + j - 4 of latent
+// 16 rb + ln).
+__device__ __forceinline__ size_t i4_byte(int t, int unit, int j, int lane, int r, int& hi) {
+  const int pos = (j & 1) ? 4 + (j >> 1) : (j >> 1);   // nibble within the unit
+  const int bl = unit * 4 + pos / 2;                     // byte within the lane's r/4
+  hi = pos & 1;
+  return static_cast<size_t>(t / 32) * 16 * r + (bl / 16) * 1024 + lane * 16 + bl % 16;
+}
+__device__ __forceinline__ size_t i4_key_byte(int t, int k, int r, int& hi) {
+  const int unit = ((t % 32) / 16) * (r / 32) + k / 32;
+  return i4_byte(t, unit, k % 8, 16 * ((k % 32) / 8) + t % 16, r, hi);
+}
+__device__ __forceinline__ size_t i4_value_byte(int t, int k, int r, int& hi) {
+  const int tt = t % 32;
+  return i4_byte(t, k / 16, (tt / 16) * 4 + tt % 4, 16 * ((tt % 16) / 4) + k % 16, r, hi);
+}
+
 // h H_r for the row a wave holds, four consecutive latents 4 lane + e per lane
 // (lanes >= nq hold zeros): butterflies (x_i, x_i+m) -> (x_i + x_i+m,
 // x_i - x_i+m) over the two index bits inside the lane, then over lane bits
@@ -115,17 +138,47 @@ __device__ void quantize_segment(const AppendParams& p, int j, int wave, int lan
     float amax = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
 #pragma unroll
     for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
-    // correctly rounded fp32 divisions (the HIP default)
-    const float scale = amax > 0.f ? amax / 127.f : 0.f;
-    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    // correctly rounded fp32 divisions (the HIP default); int4: 15 levels
+    const float qmax = p.quant == 4 ? 7.f : 127.f;
+    const float scale = amax > 0.f ? amax / qmax : 0.f;
+    const float inv = amax > 0.f ? qmax / amax : 0.f;
     auto code = [&](float x) {
-      const float c = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+      const float c = fminf(fmaxf(rintf(x * inv), -qmax), qmax);
       return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
+    };
+    auto code4 = [&](float x) {                          // biased nibble code + 8
+      return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x * inv), -7.f), 7.f)) + 8);
     };
     auto pack = [&](float4 v) {
       return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
     };
     const size_t row = (static_cast<size_t>(b) * p.G + g) * p.L + pos;
+    if (p.quant == 4) {
+      // keys: the four latents 4 lane .. +3 fill two whole bytes; values: each
+      // byte also holds another token's code (not written by this call), so
+      // its other nibble is kept
+      uint8_t* slab4 = reinterpret_cast<uint8_t*>(h) + (row - pos) * (p.r / 2);
+      if (lane < nq) {
+        const int k0 = 4 * lane;
+        int hi;
+        if (!is_v) {
+          slab4[i4_key_byte(pos, k0, p.r, hi)] =
+              static_cast<uint8_t>(code4(v0.x) | (code4(v0.z) << 4));
+          slab4[i4_key_byte(pos, k0 + 1, p.r, hi)] =
+              static_cast<uint8_t>(code4(v0.y) | (code4(v0.w) << 4));
+        } else {
+          const float e[4] = {v0.x, v0.y, v0.z, v0.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint8_t* byte = slab4 + i4_value_byte(pos, k0 + i, p.r, hi);
+            const uint32_t u = code4(e[i]);
+            *byte = static_cast<uint8_t>(hi ? ((*byte & 0x0Fu) | (u << 4)) : ((*byte & 0xF0u) | u));
+          }
+        }
+      }
+      if (lane == 0) sc[row] = scale;
+      continue;
+    }
     int8_t* slab = h + (row - pos) * p.r;
     // keys: four consecutive latents are four consecutive bytes; values: 16
     // bytes apart
@@ -165,10 +218,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   // branch around the loads: rows past the slice read its last row and
   // columns past the block read column 0 (finite values; the matching x
   // entries are 0 and the results for such columns are never stored)
-  Raw8<T> a[8];
+  Raw8<T> a[kRowsPerThread];
   const int ca = active ? c : 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kRowsPerThread; ++i) {
     const int row = min(rg + kRowGroups * i, rows - 1);
     a[i].load(A + static_cast<size_t>(i0 + row) * width + ca);
   }
@@ -208,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kRowsPerThread; ++i) {
         const float xv = xs[bb][rg + kRowGroups * i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv, a[i][e], acc[e]);

@@ -29,8 +29,9 @@ struct DecodeParams {
   int32_t rope;                // 1 if rotary embedding is applied
   int32_t full_rank;           // 1: h_k, h_v are full K, V; no B_k, B_v
   int32_t latent_out;          // 1: out [B, Hq, r] holds u* (B_v left to the caller)
-  int32_t latent_i8;           // 1: h_k, h_v are int8 codes with row scales s_k, s_v
-  int32_t hadamard;            // 1: the int8 rows are Hadamard-rotated
+  int32_t qbits;               // 8 or 4: h_k, h_v hold int8 / int4 codes with row
+                               // scales s_k, s_v (tiled order); 0: dtype latents
+  int32_t hadamard;            // 1: the quantised rows are Hadamard-rotated
   const float* s_k;            // [B, G, L] (int8 latents)
   const float* s_v;
   float scale_log2;            // softmax scale * log2(e)
@@ -50,7 +51,7 @@ struct AppendParams {
   float* part;        // [ceil(dm/128), B, 2*G*r] fp32 row-slice partial sums
   int32_t B, dm, G, r, L;
   // int8 cache (h_k, h_v int8 codes): per-row scales and the second hand-off
-  int32_t quant;
+  int32_t quant;      // 0: dtype cache; 8 or 4: quantised cache of that width
   int32_t hadamard;   // 1: rows rotated by the Hadamard matrix before quantising
   float* s_k;         // [B, G, L]
   float* s_v;
@@ -73,9 +74,9 @@ hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
-// int8 latents (tiled cache): bf16 q and B, r in {64, 128, 256}, L % 32 == 0
-bool absorbed_i8_supported(const DecodeParams& p, int dtype);
-hipError_t launch_split_absorbed_i8(const DecodeParams& p, hipStream_t st);
+// int8 / int4 latents (tiled cache): bf16 q and B, r in {64, 128, 256}, L % 32 == 0
+bool absorbed_quant_supported(const DecodeParams& p, int dtype);
+hipError_t launch_split_absorbed_quant(const DecodeParams& p, hipStream_t st);
 int absorbed_head_slices(int nq);   // workgroups per (split, b, g): 16 query heads each
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);

@@ -15,7 +15,7 @@ def dev(a: np.ndarray) -> torch.Tensor:
     """Seeded host array -> device tensor with the same bits (uint16 = bf16)."""
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    if a.dtype in (np.int32, np.int8):
+    if a.dtype in (np.int32, np.int8, np.uint8):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
@@ -47,3 +47,17 @@ def assert_close(got, want, *, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):
     ma, rel = errors(got, want)
     assert ma <= max_abs and rel <= rel_l2, f"{what}: max|d|={ma:.3e} relL2={rel:.3e}"
     return ma, rel
+
+
+def code_bounds(e, E, amax_lo, amax_hi, qmax):
+    """Range of codes rint(S * fl(qmax / A)) over every fp32 sum S within E of
+    the exact value e and every row maximum A in [amax_lo, amax_hi] (rounding
+    is monotone, so the corners bound it); returns (lo, hi) codes."""
+    eps = 2.0 ** -23
+    inv_lo = qmax / amax_hi * (1 - eps)
+    inv_hi = qmax / amax_lo * (1 + eps) if amax_lo > 0 else np.inf
+    corners = np.stack([(e - E) * inv_lo, (e - E) * inv_hi, (e + E) * inv_lo, (e + E) * inv_hi])
+    with np.errstate(invalid="ignore"):
+        lo = np.nanmin(corners, 0) * (1 - np.sign(np.nanmin(corners, 0)) * eps)
+        hi = np.nanmax(corners, 0) * (1 + np.sign(np.nanmax(corners, 0)) * eps)
+    return np.clip(np.rint(lo), -qmax, qmax), np.clip(np.rint(hi), -qmax, qmax)

@@ -93,46 +93,49 @@ def test_full_rank_mode_needs_no_factors(lib):
                                 fake, 16, None) == P.PALU_ERR_WORKSPACE
 
 
-def _i8(lib, d, *ptrs, nbytes=1 << 40):
+def _quant(lib, bits, d, *ptrs, nbytes=1 << 40):
     fake = ctypes.c_void_p(0x1000)
     q, hk, hv, sk, sv, bk, bv, out, ws = [fake if p is True else p for p in ptrs]
-    return lib.palu_decode_attn_i8(ctypes.byref(d), q, hk, hv, sk, sv, bk, bv, None, out, ws,
-                                   nbytes, None)
+    fn = lib.palu_decode_attn_i8 if bits == 8 else lib.palu_decode_attn_i4
+    return fn(ctypes.byref(d), q, hk, hv, sk, sv, bk, bv, None, out, ws, nbytes, None)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("kw", [dict(mode="reconstruct", rope_theta=5e5),
                                 dict(mode="full_rank", n_groups=8, rank=128),
                                 dict(dtype=P.PALU_F32), dict(rank=32), dict(rank=512),
                                 dict(rank=96)])
-def test_int8_decode_unsupported_combinations(lib, kw):
-    """int8 latents are provided for ABSORBED, BF16, rank 64/128/256 only."""
-    assert _i8(lib, _desc(**kw), *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
-    assert b"int8" in lib.palu_last_error()
+def test_quant_decode_unsupported_combinations(lib, kw, bits):
+    """int8 / int4 latents are provided for ABSORBED, BF16, rank 64/128/256 only."""
+    assert _quant(lib, bits, _desc(**kw), *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
+    assert f"int{bits}".encode() in lib.palu_last_error()
 
 
-def test_int8_decode_validation(lib):
-    """Descriptor errors come first (the tiled int8 cache needs max_ctx % 32
-    == 0), then missing pointers, 16-byte alignment, then the workspace (same
-    size as palu_decode_attn's)."""
-    assert _i8(lib, _desc(batch=0), *([True] * 9)) == P.PALU_ERR_SHAPE
-    assert _i8(lib, _desc(max_ctx=1000), *([True] * 9)) == P.PALU_ERR_SHAPE
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quant_decode_validation(lib, bits):
+    """Descriptor errors come first (the tiled caches need max_ctx % 32 == 0),
+    then missing pointers, 16-byte alignment, then the workspace (same size as
+    palu_decode_attn's)."""
+
+    assert _quant(lib, bits, _desc(batch=0), *([True] * 9)) == P.PALU_ERR_SHAPE
+    assert _quant(lib, bits, _desc(max_ctx=1000), *([True] * 9)) == P.PALU_ERR_SHAPE
     odd = ctypes.c_void_p(0x1008)
     for i in (1, 2, 3, 4):                   # h_k, h_v, s_k, s_v
         ptrs = [True] * 9
         ptrs[i] = odd
-        assert _i8(lib, _desc(), *ptrs) == P.PALU_ERR_SHAPE, i
+        assert _quant(lib, bits, _desc(), *ptrs) == P.PALU_ERR_SHAPE, i
     d = _desc(rank=128)
     for i in range(9):                       # every pointer is needed here
         ptrs = [True] * 9
         ptrs[i] = None
-        assert _i8(lib, d, *ptrs, nbytes=16) == P.PALU_ERR_NULL, i
+        assert _quant(lib, bits, d, *ptrs, nbytes=16) == P.PALU_ERR_NULL, i
     # latent_out: b_v may be NULL
     d = _desc(rank=128, latent_out=True)
     ptrs = [True] * 9
     ptrs[6] = None
-    assert _i8(lib, d, *ptrs, nbytes=16) == P.PALU_ERR_WORKSPACE
+    assert _quant(lib, bits, d, *ptrs, nbytes=16) == P.PALU_ERR_WORKSPACE
     need = P.palu_decode_attn_workspace(d)
-    assert _i8(lib, d, *([True] * 9), nbytes=need - 1) == P.PALU_ERR_WORKSPACE
+    assert _quant(lib, bits, d, *([True] * 9), nbytes=need - 1) == P.PALU_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw,status", BAD)
@@ -217,10 +220,11 @@ def test_append_validation(lib):
                                   misaligned, need, None) == P.PALU_ERR_WORKSPACE
 
 
-def test_append_i8_validation(lib):
-    """The quantised cache write: the append checks, rank % 4, NULL scales,
-    4-byte aligned caches, and a workspace with a second counter area and the
-    finished rows."""
+@pytest.mark.parametrize("bits", [8, 4])
+def test_append_quant_validation(lib, bits):
+    """The quantised cache write: the append checks, rank 64/128/256, NULL
+    scales, 4-byte aligned caches, and a workspace with a second counter area
+    and the finished rows (the same for both widths)."""
     fake = ctypes.c_void_p(0x1000)
     good = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
                          dtype=P.PALU_BF16)
@@ -228,7 +232,13 @@ def test_append_i8_validation(lib):
 
     def call(d, *ptrs, nbytes=big):
         ptrs = [fake if p is True else p for p in ptrs]
-        return lib.palu_latent_append_i8(ctypes.byref(d), *ptrs, nbytes, None)
+        fn = lib.palu_latent_append_i8 if bits == 8 else lib.palu_latent_append_i4
+        return fn(ctypes.byref(d), *ptrs, nbytes, None)
+
+    def workspace_call(d, n):
+        fn = (lib.palu_latent_append_i8_workspace if bits == 8
+              else lib.palu_latent_append_i4_workspace)
+        return fn(ctypes.byref(d), ctypes.byref(n))
 
     bad = [(dict(batch=0), P.PALU_ERR_SHAPE), (dict(rank=600), P.PALU_ERR_SHAPE),
            (dict(n_groups=4, rank=6), P.PALU_ERR_UNSUPPORTED),  # the tiled cache: r 64/128/256
@@ -239,12 +249,13 @@ def test_append_i8_validation(lib):
         d = P.AppendDesc(**{**{f: getattr(good, f) for f, _ in P.AppendDesc._fields_}, **kw})
         assert call(d, *([True] * 9)) == status
         n = ctypes.c_size_t(0)
-        assert lib.palu_latent_append_i8_workspace(ctypes.byref(d), ctypes.byref(n)) == status
+        assert workspace_call(d, n) == status
     for i in range(9):
         ptrs = [True] * 9
         ptrs[i] = None
         assert call(good, *ptrs) == P.PALU_ERR_NULL, i
-    need = P.palu_latent_append_i8_workspace(good)
+    need = (P.palu_latent_append_i8_workspace if bits == 8
+            else P.palu_latent_append_i4_workspace)(good)
     # column-block counters (256 B), row-segment counters (256 B), the
     # partials, then the finished fp32 rows [B, 2*G*r]
     assert need == 256 + 256 + 32 * 8 * 1024 * 4 + 8 * 1024 * 4
@@ -254,26 +265,27 @@ def test_append_i8_validation(lib):
     assert call(good, *([True] * 8), ctypes.c_void_p(0x1008)) == P.PALU_ERR_WORKSPACE
 
 
-def test_hadamard_flag_is_for_int8_only(lib):
+@pytest.mark.parametrize("bits", [8, 4])
+def test_hadamard_flag_is_for_quantised_caches_only(lib, bits):
     """The rotated-cache flag is refused by the bf16 calls, accepted by the
-    int8 ones (which then fail on the fake workspace size), and must be 0/1."""
+    int8 and int4 ones (which then fail on the fake workspace size), and must
+    be 0/1."""
+    append_q = lib.palu_latent_append_i8 if bits == 8 else lib.palu_latent_append_i4
     fake = ctypes.c_void_p(0x1000)
     d = _desc(rank=128, hadamard=True)
     assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake,
                                 fake, 1 << 40, None) == P.PALU_ERR_UNSUPPORTED
     assert b"int8" in lib.palu_last_error()
-    assert _i8(lib, d, *([True] * 9), nbytes=16) == P.PALU_ERR_WORKSPACE
+    assert _quant(lib, bits, d, *([True] * 9), nbytes=16) == P.PALU_ERR_WORKSPACE
     d.hadamard = 2
-    assert _i8(lib, d, *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
+    assert _quant(lib, bits, d, *([True] * 9)) == P.PALU_ERR_UNSUPPORTED
     a = P.append_desc(batch=2, d_model=256, n_groups=2, rank=64, max_ctx=64,
                       dtype=P.PALU_BF16, hadamard=True)
     assert lib.palu_latent_append(ctypes.byref(a), fake, fake, fake, fake, fake, fake, fake,
                                   1 << 40, None) == P.PALU_ERR_UNSUPPORTED
-    assert lib.palu_latent_append_i8(ctypes.byref(a), *([fake] * 9), 16,
-                                     None) == P.PALU_ERR_WORKSPACE
+    assert append_q(ctypes.byref(a), *([fake] * 9), 16, None) == P.PALU_ERR_WORKSPACE
     a.hadamard = -1
-    assert lib.palu_latent_append_i8(ctypes.byref(a), *([fake] * 9), 1 << 40,
-                                     None) == P.PALU_ERR_UNSUPPORTED
+    assert append_q(ctypes.byref(a), *([fake] * 9), 1 << 40, None) == P.PALU_ERR_UNSUPPORTED
 
 
 def test_only_the_c_abi_is_exported(lib):

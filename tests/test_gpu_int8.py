@@ -9,7 +9,7 @@ import pytest
 import workloads as W
 from oracle import palu_oracle as O
 from rank_compressed_kv_amd.layout import pack_i8_cache, unpack_i8_cache
-from tests.parity_util import assert_close, dev
+from tests.parity_util import assert_close, code_bounds, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -147,17 +147,7 @@ APPEND = {
 
 
 def _code_bounds(e, E, amax_lo, amax_hi):
-    """Range of codes rint(S * fl(127 / A)) over every fp32 sum S within E of
-    the exact value e and every row maximum A in [amax_lo, amax_hi] (rounding
-    is monotone, so the corners bound it); returns (lo, hi) codes."""
-    eps = 2.0 ** -23
-    inv_lo = 127.0 / amax_hi * (1 - eps)
-    inv_hi = 127.0 / amax_lo * (1 + eps) if amax_lo > 0 else np.inf
-    corners = np.stack([(e - E) * inv_lo, (e - E) * inv_hi, (e + E) * inv_lo, (e + E) * inv_hi])
-    with np.errstate(invalid="ignore"):
-        lo = np.nanmin(corners, 0) * (1 - np.sign(np.nanmin(corners, 0)) * eps)
-        hi = np.nanmax(corners, 0) * (1 + np.sign(np.nanmax(corners, 0)) * eps)
-    return np.clip(np.rint(lo), -127, 127), np.clip(np.rint(hi), -127, 127)
+    return code_bounds(e, E, amax_lo, amax_hi, 127)
 
 
 @pytest.mark.parametrize("name", sorted(APPEND))

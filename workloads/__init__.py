@@ -41,7 +41,8 @@ __all__ = ["Config", "CONFIGS", "generate", "f32_to_bf16_bits", "bf16_bits_to_f3
 # the bits of another
 _STREAM = {"q": 0, "h_k": 1, "h_v": 2, "b_k": 3, "b_v": 4, "lens": 5,
            "outlier": 6, "x": 7, "a_k": 8, "a_v": 9, "pos": 10, "k_full": 11, "v_full": 12,
-           "k_i8": 13, "v_i8": 14, "sk": 15, "sv": 16}
+           "k_i8": 13, "v_i8": 14, "sk": 15, "sv": 16, "k_i4": 17, "v_i4": 18, "sk_i4": 19,
+           "sv_i4": 20}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -155,7 +156,10 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
     "full" -> k_full, v_full [B, Hkv, L_cap, d] (the uncompressed baseline's
     cache, same q and lens as "decode", which it needs); "i8" -> k_i8, v_i8
     int8 [B, G, L_cap, r] (codes uniform in [-127, 127]) and sk, sv fp32
-    [B, G, L_cap] (scales uniform in [0.005, 0.025)): an int8 latent cache.
+    [B, G, L_cap] (scales uniform in [0.005, 0.025)): an int8 latent cache;
+    "i4" -> k_i4, v_i4 int8 [B, G, L_cap, r] (codes uniform in [-7, 7]) and
+    sk_i4, sv_i4 (scales uniform in [0.1, 0.45)): an int4 latent cache, codes
+    in row order (both caches span latents up to about 3.2 in magnitude).
     lens overrides the drawn lengths (edge-case tests). Values are fp32 arrays or
     uint16 bf16 bits, per cfg.dtype; lens and pos are int32.
     """
@@ -200,6 +204,12 @@ def generate(cfg: Config, *, seed: Optional[int] = None, parts=("decode",),
         for name in ("sk", "sv"):
             u = _rng(seed, name).random(size=(B, G, L), dtype=np.float32)
             out[name] = (np.float32(0.005) + np.float32(0.02) * u).astype(np.float32)
+    if "i4" in parts:
+        for name in ("k_i4", "v_i4"):
+            out[name] = _rng(seed, name).integers(-7, 8, size=(B, G, L, r)).astype(np.int8)
+        for name in ("sk_i4", "sv_i4"):
+            u = _rng(seed, name).random(size=(B, G, L), dtype=np.float32)
+            out[name] = (np.float32(0.1) + np.float32(0.35) * u).astype(np.float32)
     if "append" in parts:
         dm = cfg.d_model
         out["x"] = _store(_normal(seed, "x", (B, dm)), cfg.dtype)
