@@ -55,8 +55,8 @@ def parse():
                     help="skip the second timed loop with events around the main kernel")
     ap.add_argument("--no-full-rank", action="store_true",
                     help="skip the uncompressed baseline (full bf16 K and V)")
-    ap.add_argument("--no-int8", action="store_true",
-                    help="skip the int8-latent absorbed step")
+    ap.add_argument("--no-quant", action="store_true",
+                    help="skip the int8- and int4-latent absorbed steps")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the head-grouping sweep (s = 1, 2, 4, 8 KV heads per "
                          "group at 75%% key compression) and add it to the JSON line")
@@ -142,18 +142,20 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
                 out=first_out.cpu().numpy())
 
 
-def time_int8(torch, P, W, cfg, t, args, rot=False):
-    """The absorbed step over an int8 latent cache (codes plus one fp32 scale
-    per row; rows Hadamard-rotated with rot): quantised append, then decode.
-    Same shape, same timing loops."""
-    ti = W.generate(cfg, parts=("i8",))
+def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
+    """The absorbed step over an int8 (bits 8) or int4 (bits 4) latent cache
+    (codes plus one fp32 scale per row; rows Hadamard-rotated with rot):
+    quantised append, then decode. Same shape, same timing loops."""
+    ti = W.generate(cfg, parts=(f"i{bits}",))
+    sfx = "" if bits == 8 else "_i4"
     q, bk, bv = dev(torch, t["q"]), dev(torch, t["b_k"]), dev(torch, t["b_v"])
     lens = dev(torch, t["lens"])
     x, ak, av = dev(torch, t["x"]), dev(torch, t["a_k"]), dev(torch, t["a_v"])
     pos = (lens - 1).to(torch.int32).contiguous()
-    from rank_compressed_kv_amd.layout import pack_i8_cache
-    bufs0 = [dev(torch, pack_i8_cache(ti["k_i8"], "k")), dev(torch, pack_i8_cache(ti["v_i8"], "v")),
-             dev(torch, ti["sk"]), dev(torch, ti["sv"])]
+    from rank_compressed_kv_amd.layout import pack_i4_cache, pack_i8_cache
+    pack = pack_i8_cache if bits == 8 else pack_i4_cache
+    bufs0 = [dev(torch, pack(ti[f"k_i{bits}"], "k")), dev(torch, pack(ti[f"v_i{bits}"], "v")),
+             dev(torch, ti["sk" + sfx]), dev(torch, ti["sv" + sfx])]
     per_copy = sum(b.numel() * b.element_size() for b in bufs0)
     n_copies = min(16, max(1, int(math.ceil(ROTATE_BYTES / per_copy))))
     caches = [bufs0] + [[b.clone() for b in bufs0] for _ in range(n_copies - 1)]
@@ -164,17 +166,21 @@ def time_int8(torch, P, W, cfg, t, args, rot=False):
     adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
                           rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, hadamard=rot)
     ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
-    aws = torch.zeros(P.palu_latent_append_i8_workspace(adesc), dtype=torch.uint8, device="cuda")
+    append_ws = (P.palu_latent_append_i8_workspace if bits == 8
+                 else P.palu_latent_append_i4_workspace)
+    decode_fn = P.palu_decode_attn_i8 if bits == 8 else P.palu_decode_attn_i4
+    append_fn = P.palu_latent_append_i8 if bits == 8 else P.palu_latent_append_i4
+    aws = torch.zeros(append_ws(adesc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def decode(i):
         hk, hv, sk, sv = caches[i % n_copies]
-        P.palu_decode_attn_i8(desc, q, hk, hv, sk, sv, bk, bv, lens, out, ws, stream)
+        decode_fn(desc, q, hk, hv, sk, sv, bk, bv, lens, out, ws, stream)
 
     def step(i):
         hk, hv, sk, sv = caches[i % n_copies]
-        P.palu_latent_append_i8(adesc, x, ak, av, hk, hv, sk, sv, pos, aws, stream)
+        append_fn(adesc, x, ak, av, hk, hv, sk, sv, pos, aws, stream)
         decode(i)
 
     step(0)
@@ -330,22 +336,25 @@ def granularity_sweep(torch, P, W, cfg, args):
     return rows
 
 
-def oracle_appended(O, cfg, t, caches, rot=False):
+def oracle_appended(O, cfg, t, caches, rot=False, bits=8):
     """The caches as the oracle has them after one step's append: row len-1 of
     each sequence replaced by the oracle's own cache write of x A (bf16: the
-    exact row rounded to fp32, then to bf16; int8: its quantisation, of the
-    Hadamard-rotated row with rot)."""
+    exact row rounded to fp32, then to bf16; int8 / int4 (bits): its
+    quantisation, of the Hadamard-rotated row with rot)."""
+    if bits == 8:
+        quant = O.append_rows_i8_hadamard if rot else O.append_rows_i8
+    else:
+        quant = O.append_rows_i4_hadamard if rot else O.append_rows_i4
     B, G, r = cfg.batch, cfg.n_groups, cfg.rank
     out = []
     for cache, a in zip(caches, ("a_k", "a_v")):
         h64 = O.latent_project(t["x"], t[a]).reshape(B, G, r)
-        if isinstance(cache, tuple):                    # (int8 codes, scales)
+        if isinstance(cache, tuple):                    # (codes, scales)
             codes, scales = cache[0].copy(), cache[1].copy()
             for b in range(B):
                 p = int(t["lens"][b]) - 1
                 if p >= 0:
-                    codes[b, :, p], scales[b, :, p] = (O.append_rows_i8_hadamard if rot
-                                                       else O.append_rows_i8)(h64[b])
+                    codes[b, :, p], scales[b, :, p] = quant(h64[b])
             out.append((codes, scales))
             continue
         c = cache.copy()
@@ -399,10 +408,12 @@ def cpu_baseline(O, cfg, t, mode, budget_s):
                       f"fp64 NumPy, {el:.1f} s; steps/s scaled by the sampled fraction"}
 
 
-def load_traffic(kernel: str):
-    """HBM bytes (read + write) per launch of the main kernel, from the committed
+def load_traffic(kernel: str, args_suffix: str = ""):
+    """HBM bytes (read + write) per launch of a kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a 1 GiB copy measured in
-    the same runs). None when there is no record for the kernel or when the
+    the same runs). The records are keyed by kernel name with template
+    arguments: the one whose name is `kernel` and whose arguments end with
+    args_suffix is taken. None when there is no single such record or when the
     kernel's source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -417,8 +428,9 @@ def load_traffic(kernel: str):
                 h.update(f.read())
         if h.hexdigest() != rec["sources_sha256"]:
             return None
-        k = rec["kernels"].get(kernel)
-        return None if k is None else round(k["bytes"])
+        hits = [v for name, v in rec["kernels"].items()
+                if name.split("<")[0] == kernel and name.endswith(args_suffix)]
+        return round(hits[0]["bytes"]) if len(hits) == 1 else None
     except Exception:
         return None
 
@@ -490,40 +502,49 @@ def main():
         print(f"[bench] full-rank baseline: {fr['ms'] * 1e3:.1f} us/call, kernel "
               f"{fr['kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
-    int8 = None
-    if not args.no_int8 and cfg.dtype == "bf16" and "absorbed" in results and \
+    quant = None
+    if not args.no_quant and cfg.dtype == "bf16" and "absorbed" in results and \
             cfg.rank in (64, 128, 256) and cfg.max_ctx % 32 == 0:
-        i8_bytes = int(np.sum(t["lens"], dtype=np.int64)) * cfg.n_groups * (2 * cfg.rank + 8)
-        int8 = {"algorithmic_bytes": i8_bytes}
-        for rot in (False, True):
-            ri = time_int8(torch, P, W, cfg, t, args, rot)
-            ti = ri.pop("ti")
-            (ck, sk), (cv, sv) = oracle_appended(O, cfg, t, ((ti["k_i8"], ti["sk"]),
-                                                              (ti["v_i8"], ti["sv"])), rot)
-            deq = O.dequantize_rows_i8_hadamard if rot else O.dequantize_rows_i8
-            # the oracle dequantises only the sampled sequences
-            dmax, num, den = 0.0, 0.0, 0.0
-            for b, h in pairs:
-                w = O.decode_attention(t["q"][b:b + 1], deq(ck[b:b + 1], sk[b:b + 1]),
-                                       deq(cv[b:b + 1], sv[b:b + 1]), t["b_k"], t["b_v"],
-                                       t["lens"][b:b + 1], select=[(0, h)])[0, h]
-                dd = ri["out"][b, h].astype(np.float64) - w
-                dmax = max(dmax, float(np.abs(dd).max()))
-                num, den = num + float(dd @ dd), den + float(w @ w)
-            kus = ri["kernel_ms"] * 1e3
-            int8["hadamard" if rot else "plain"] = {
-                "us_per_step": round(ri["ms_per_step"] * 1e3, 2),
-                "us_per_decode_call": round(ri["decode_ms"] * 1e3, 2),
-                "kernel_us": _r(kus, 2),
-                "GBps_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9, 1),
-                "frac_hbm_kernel": _r(i8_bytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "step_speedup_vs_bf16": round(results["absorbed"]["ms_per_step"]
-                                              / ri["ms_per_step"], 3),
-                "sampled_parity_max_abs": dmax,
-                "sampled_parity_rel_l2": math.sqrt(num / den) if den > 0 else None}
-            print(f"[bench] int8 absorbed{' hadamard' if rot else ''}: "
-                  f"{ri['ms_per_step'] * 1e3:.1f} us/step, kernel {kus:.1f} us",
-                  file=sys.stderr, flush=True)
+        quant = {}
+        ntok = int(np.sum(t["lens"], dtype=np.int64))
+        for bits in (8, 4):
+            # codes of both matrices plus the two fp32 scales of every row
+            qbytes = ntok * cfg.n_groups * (2 * cfg.rank * bits // 8 + 8)
+            entry = {"algorithmic_bytes": qbytes}
+            sfx = "" if bits == 8 else "_i4"
+            for rot in (False, True):
+                ri = time_quant(torch, P, W, cfg, t, args, bits, rot)
+                ti = ri.pop("ti")
+                (ck, sk), (cv, sv) = oracle_appended(
+                    O, cfg, t, ((ti[f"k_i{bits}"], ti["sk" + sfx]),
+                                (ti[f"v_i{bits}"], ti["sv" + sfx])), rot, bits)
+                deq = O.dequantize_rows_i8_hadamard if rot else O.dequantize_rows_i8
+                # the oracle dequantises only the sampled sequences
+                dmax, num, den = 0.0, 0.0, 0.0
+                for b, h in pairs:
+                    w = O.decode_attention(t["q"][b:b + 1], deq(ck[b:b + 1], sk[b:b + 1]),
+                                           deq(cv[b:b + 1], sv[b:b + 1]), t["b_k"], t["b_v"],
+                                           t["lens"][b:b + 1], select=[(0, h)])[0, h]
+                    dd = ri["out"][b, h].astype(np.float64) - w
+                    dmax = max(dmax, float(np.abs(dd).max()))
+                    num, den = num + float(dd @ dd), den + float(w @ w)
+                kus = ri["kernel_ms"] * 1e3
+                entry["hadamard" if rot else "plain"] = {
+                    "us_per_step": round(ri["ms_per_step"] * 1e3, 2),
+                    "us_per_decode_call": round(ri["decode_ms"] * 1e3, 2),
+                    "kernel_us": _r(kus, 2),
+                    "GBps_kernel": _r(qbytes / (kus * 1e-6) / 1e9, 1),
+                    "frac_hbm_kernel": _r(qbytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "step_speedup_vs_bf16": round(results["absorbed"]["ms_per_step"]
+                                                  / ri["ms_per_step"], 3),
+                    "traffic": load_traffic("split_absorbed_int_kernel",
+                                            f", {bits}>") if not rot else None,
+                    "sampled_parity_max_abs": dmax,
+                    "sampled_parity_rel_l2": math.sqrt(num / den) if den > 0 else None}
+                print(f"[bench] int{bits} absorbed{' hadamard' if rot else ''}: "
+                      f"{ri['ms_per_step'] * 1e3:.1f} us/step, kernel {kus:.1f} us",
+                      file=sys.stderr, flush=True)
+            quant[f"int{bits}"] = entry
 
     ms = main_res["ms_per_step"]
     steps_s = 1e3 / ms
@@ -553,7 +574,7 @@ def main():
         "latent_pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "roofline": roofline(cfg, t, args.mode, main_res, lat_bytes, kern_gbs, traffic),
         "full_rank_baseline": full,
-        "int8_latents": int8,
+        "quantised_latents": quant,
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                       "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
                       "kernel_us": _r(r["kernel_ms"] * 1e3, 2), "kernel": r["kernel"],

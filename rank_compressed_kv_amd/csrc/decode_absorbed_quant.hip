@@ -34,6 +34,8 @@
 // is written, so the merge and B_k, B_v are those of the plain cache.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -72,19 +74,32 @@ __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
   const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
   return uint4{a.x, a.y, b.x, b.y};
 }
+// 0x64006400 in a register the compiler cannot see through: with both
+// operands in registers, mask-and-or pairs become single and-or instructions
+// (no literal operands there); computed once, outside the loops
+__device__ __forceinline__ uint32_t f16x2_1024_bits() {
+  uint32_t r;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
+  return r;
+}
 // eight int4 codes, stored biased (u = code + 8) with operand element 2m in
 // nibble m and 2m+1 in nibble m+4 -> one 8 x fp16 MFMA operand, exactly: the
-// fp16 with bits 0x640u is 1024 + u, so one shift and one and-or per pair
-// and one packed subtraction of 1032 give the codes
-__device__ __forceinline__ uint4 widen4(uint32_t w) {
+// fp16 with bits 0x640u is 1024 + u (pairs 0, 2: nibbles 0/4 of w and of
+// w >> 8), minus 1032; the one with bits 0x64u0 is 1024 + 16u (pairs 1, 3:
+// nibbles 1/5), times 1/16 minus 72 (one fused step, exact)
+__device__ __forceinline__ uint4 widen4(uint32_t w, uint32_t k1024) {
   const half2v bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-  uint32_t r[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t pr = ((w >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
-    r[m] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr) - bias);
-  }
-  return uint4{r[0], r[1], r[2], r[3]};
+  const half2v sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const half2v bias16 = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+  const uint32_t w8 = w >> 8;
+  const half2v p0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | k1024);
+  const half2v p1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | k1024);
+  const half2v p2 = __builtin_bit_cast(half2v, (w8 & 0x000F000Fu) | k1024);
+  const half2v p3 = __builtin_bit_cast(half2v, (w8 & 0x00F000F0u) | k1024);
+  return uint4{__builtin_bit_cast(uint32_t, p0 - bias),
+               __builtin_bit_cast(uint32_t, p1 * sixteenth + bias16),
+               __builtin_bit_cast(uint32_t, p2 - bias),
+               __builtin_bit_cast(uint32_t, p3 * sixteenth + bias16)};
 }
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
@@ -281,53 +296,57 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Block<R, kBits>& x, int t0) {
+  const uint32_t k1024 = f16x2_1024_bits();
+  // masked: the block may reach past the split's end (only a wave's last
+  // block can: every other block of a wave lies whole inside the split)
+  auto compute = [&](const Block<R, kBits>& x, int t0, auto masked) {
     // q~ is read from LDS again for every block: held in registers across the
     // loop it would take 128 of them at r = 256 (a compiler-only barrier keeps
     // the reads inside)
     asm volatile("" ::: "memory");
-    // scores of the two 16-token halves: S^T[16 tok x 16 heads], key chunk c
-    // of half h in word h*R/64 + c/2, bytes 8*(c%2) .. +8
-    floatx4 sc[2];
+    // scores of the two 16-token halves: S^T[16 tok x 16 heads] of half h
+    // (q~ hi and lo parts in separate accumulators: four independent chains)
+    floatx4 shi[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 slo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      floatx4 acc4[4];
+    for (int c = 0; c < R / 32; ++c) {
+      const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[0][ln][32 * c + 8 * kb]);
+      const uint4 ql = *reinterpret_cast<const uint4*>(&sm.q[1][ln][32 * c + 8 * kb]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc4[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < R / 32; ++c) {
-        // int8: word h*R/64 + c/2, bytes 8*(c%2) .. +8; int4: the lane's
-        // 32-bit unit h*R/32 + c
+      for (int h = 0; h < 2; ++h) {
+        // key chunk c of half h: int8 word h*R/64 + c/2, bytes 8*(c%2) .. +8;
+        // int4 the lane's 32-bit unit h*R/32 + c
         uint4 a;
         if constexpr (kBits == 8) {
           const int w = 4 * (h * (R / 64) + c / 2) + 2 * (c % 2);
           a = widen8(x.k[w], x.k[w + 1]);
         } else {
-          a = widen4(x.k[h * (R / 32) + c]);
+          a = widen4(x.k[h * (R / 32) + c], k1024);
         }
-        const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[0][ln][32 * c + 8 * kb]);
-        const uint4 ql = *reinterpret_cast<const uint4*>(&sm.q[1][ln][32 * c + 8 * kb]);
-        acc4[2 * (c & 1)] = mfma(a, qh, acc4[2 * (c & 1)]);
-        acc4[2 * (c & 1) + 1] = mfma(a, ql, acc4[2 * (c & 1) + 1]);
+        shi[h] = mfma(a, qh, shi[h]);
+        slo[h] = mfma(a, ql, slo[h]);
       }
-      sc[h] = (acc4[0] + acc4[2]) + (acc4[1] + acc4[3]);
     }
-    sc[0] *= x.sk0 * qc;
-    sc[1] *= x.sk1 * qc;
+    // scores in units of qc (the head's power-of-two divisor): qc is applied
+    // in the exponent
+    floatx4 sc[2] = {(shi[0] + slo[0]) * x.sk0, (shi[1] + slo[1]) * x.sk1};
     floatx4 sv[2] = {x.sv0 * vinv, x.sv1 * vinv};
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (t0 + 16 * h + 4 * kb + i >= t1) {
-          sc[h][i] = -INFINITY;
-          sv[h][i] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 16 * h + 4 * kb + i >= t1) {
+            sc[h][i] = -INFINITY;
+            sv[h][i] = 0.f;
+          }
+    }
     // online softmax over the block's 32 tokens of head ln
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx *= qc;                                            // qc > 0: the true maximum
     if (__any(mx > st.m + kLazy)) {
       const float mn = fmaxf(st.m, mx);
       const float alpha = exp2f(st.m - mn);
@@ -337,19 +356,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
       for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] *= alpha;
     }
     // P^T operand: k-slot 8*kb + j is token 4*kb + j (j < 4) or 16 + 4*kb + j - 4
-    uint16_t ph[8], pl[8];
+    // weights (v_exp_f32: arguments <= kLazy, results below 2^-126 flush to
+    // 0, far under the fp16 operands' resolution), each as hi + lo fp16
+    uint32_t ph[4], pl[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pe = exp2f(sc[h][i] - st.m);
-        st.l += pe;
-        split_f16(pe * sv[h][i], ph[4 * h + i], pl[4 * h + i]);
+      for (int i = 0; i < 4; i += 2) {
+        const float pe0 = __builtin_amdgcn_exp2f(fmaf(qc, sc[h][i], -st.m));
+        const float pe1 = __builtin_amdgcn_exp2f(fmaf(qc, sc[h][i + 1], -st.m));
+        st.l += pe0 + pe1;
+        const float x0 = pe0 * sv[h][i], x1 = pe1 * sv[h][i + 1];
+        const half2v hi = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+        const half2v lo = {static_cast<_Float16>(x0 - static_cast<float>(hi[0])),
+                           static_cast<_Float16>(x1 - static_cast<float>(hi[1]))};
+        ph[2 * h + i / 2] = __builtin_bit_cast(uint32_t, hi);
+        pl[2 * h + i / 2] = __builtin_bit_cast(uint32_t, lo);
       }
-    const uint4 bh = {ph[0] | (uint32_t(ph[1]) << 16), ph[2] | (uint32_t(ph[3]) << 16),
-                      ph[4] | (uint32_t(ph[5]) << 16), ph[6] | (uint32_t(ph[7]) << 16)};
-    const uint4 bl = {pl[0] | (uint32_t(pl[1]) << 16), pl[2] | (uint32_t(pl[3]) << 16),
-                      pl[4] | (uint32_t(pl[5]) << 16), pl[6] | (uint32_t(pl[7]) << 16)};
+    const uint4 bh = {ph[0], ph[1], ph[2], ph[3]};
+    const uint4 bl = {pl[0], pl[1], pl[2], pl[3]};
     // values: U^T[16 rb .. +16, heads] += H_v^T[., 32 tokens] P^T; latent rows
     // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
 #pragma unroll
@@ -359,7 +384,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
         const int w = 4 * (rb / 2) + 2 * (rb % 2);
         a = widen8(x.v[w], x.v[w + 1]);
       } else {
-        a = widen4(x.v[rb]);                             // the lane's unit rb
+        a = widen4(x.v[rb], k1024);                      // the lane's unit rb
       }
       st.acc[rb] = mfma(a, bh, st.acc[rb]);
       st.acc[rb] = mfma(a, bl, st.acc[rb]);
@@ -374,16 +399,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
     int j = 0;
     for (; j + 2 < mine; j += 2) {
       fetch(xb, tok_of(j + 1));
-      compute(xa, tok_of(j));
+      compute(xa, tok_of(j), std::false_type{});
       fetch(xa, tok_of(j + 2));
-      compute(xb, tok_of(j + 1));
+      compute(xb, tok_of(j + 1), std::false_type{});
     }
     if (j + 1 < mine) {
       fetch(xb, tok_of(j + 1));
-      compute(xa, tok_of(j));
-      compute(xb, tok_of(j + 1));
+      compute(xa, tok_of(j), std::false_type{});
+      compute(xb, tok_of(j + 1), std::true_type{});
     } else {
-      compute(xa, tok_of(j));
+      compute(xa, tok_of(j), std::true_type{});
     }
   }
 
