@@ -11,18 +11,19 @@
 //     the MFMA operands (the append kernel writes it), so every 16-byte load of
 //     a lane holds exactly the operand bytes that lane needs: no LDS staging,
 //     no gathers, fully coalesced 1 KiB per load instruction;
-//   - codes are widened to fp16 in registers (exact for |code| <= 127; int4
-//     codes sit biased in nibbles ordered so that one shift and one and-or
-//     give a pair of operand elements) and
-//     multiplied on fp16 MFMAs, 16x16x32 for the scores (16 tokens x 16 heads
-//     over 32 latents) and for the values (r x 16 heads over 32 tokens);
+//   - codes become fp16 operands in registers as exact subnormals (a byte
+//     permute or a nibble mask per pair of codes; value operands also lose
+//     their bias in one packed subtraction) and are multiplied on fp16 MFMAs,
+//     16x16x32 for the scores (16 tokens x 16 heads over 32 latents) and for
+//     the values (r x 16 heads over 32 tokens);
 //   - a block's key scales multiply its scores, its value scales fold into the
 //     weights (p_t s_t; the running sum l keeps p_t). q~ (hi + lo in fp16) is
 //     divided per head by a power of two near its largest entry and the value
 //     scales by the split's largest one, so fp16 operands stay in range
 //     whatever the magnitudes; both are undone in fp32.
 // One workgroup owns one (batch, group, context split) and 16 query heads;
-// its four waves take the split's 32-token blocks round-robin and combine
+// its waves (four for int8, eight for int4) take the split's 32-token
+// blocks round-robin and combine
 // their softmax states in LDS at the end. A wave holds two blocks in
 // registers: the next one is requested before the current one is multiplied
 // (non-temporal loads: the cache is read once). Blocks are read whole: rows
@@ -46,7 +47,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        // one per SIMD
+// waves per workgroup: an int4 wave fits in half a SIMD's registers, so two
+// waves per SIMD keep twice the blocks in flight (measured 39 -> 35 us at
+// Llama-3-8B, 32K context); an int8 wave needs a whole SIMD's registers
+template <int kBits>
+constexpr int kWavesFor = kBits == 4 ? 8 : 4;
 constexpr int kBlock = 32;       // tokens per cache block and per wave step
 constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
 
@@ -57,49 +62,53 @@ __device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
   lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x - static_cast<float>(h)));
 }
 
-// four int8 codes -> four fp16 values, exactly: with u = code + 128 (the byte
-// XOR 0x80), the fp16 with bits 0x64uu is 1024 + u; one byte permute per pair
-// of codes and one packed fp16 subtraction of 1152 give the codes
-__device__ __forceinline__ uint2 i8x4_to_f16x4(uint32_t w) {
+// Codes enter the matrix cores as fp16 subnormals: the fp16 with bits 0x00uu
+// is u * 2^-24 exactly, so a byte or a nibble moved into the low bits of a
+// 16-bit lane is already an operand. They are biased codes (u = code + 128
+// after flipping an int8 code's sign bit; u = code + 8 as an int4 cache
+// stores it). Key operands keep the bias, which leaves once per head and
+// token: the score accumulators start at -bias * sum_k q_k (a product of
+// bounded size per token). Value operands take it off exactly, in fp16,
+// before the product: a bias inside the weighted sum over thousands of tokens
+// would cancel against a sum thousands of times larger than the result, which
+// the matrix cores' accumulation does not carry accurately enough. The factor
+// 2^-24 goes into the head's exponent factor and the output scale.
+
+// four int8 codes -> two fp16 pairs u * 2^-24 (u = code + 128)
+__device__ __forceinline__ uint2 i8x4_operand(uint32_t w) {
   const uint32_t x = w ^ 0x80808080u;
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
-  const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
-  const half2v a = __builtin_bit_cast(half2v, lo) - bias;
-  const half2v c = __builtin_bit_cast(half2v, hi) - bias;
-  return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+  return uint2{__builtin_amdgcn_perm(0u, x, 0x0C010C00u), __builtin_amdgcn_perm(0u, x, 0x0C030C02u)};
 }
-// eight codes (two words) -> one 8 x fp16 MFMA operand
-__device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
-  const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
+// eight int4 codes (biased nibbles, operand element 2m in nibble m and 2m+1
+// in nibble m+4) -> fp16 pairs: pairs 0 and 2 (nibbles 0/4 of w and of w >>
+// 8) are u * 2^-24, pairs 1 and 3 (nibbles 1/5) 16u * 2^-24; the other
+// operand carries 1/16 at those positions (elements k % 8 in {2, 3, 6, 7})
+__device__ __forceinline__ uint4 i4x8_operand(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  return uint4{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+}
+__device__ __forceinline__ uint32_t sub_f16x2(uint32_t a, _Float16 b) {
+  const half2v bb = {b, b};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) - bb);
+}
+// key operands (biased): eight int8 codes from two words, or eight int4 codes
+__device__ __forceinline__ uint4 key_operand8(uint32_t w0, uint32_t w1) {
+  const uint2 a = i8x4_operand(w0), b = i8x4_operand(w1);
   return uint4{a.x, a.y, b.x, b.y};
 }
-// 0x64006400 in a register the compiler cannot see through: with both
-// operands in registers, mask-and-or pairs become single and-or instructions
-// (no literal operands there); computed once, outside the loops
-__device__ __forceinline__ uint32_t f16x2_1024_bits() {
-  uint32_t r;
-  asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
-  return r;
+__device__ __forceinline__ uint4 key_operand4(uint32_t w) { return i4x8_operand(w); }
+// value operands: the codes themselves (code * 2^-24, or 16 code * 2^-24 at
+// the scaled int4 positions), exact subnormal differences
+__device__ __forceinline__ uint4 value_operand8(uint32_t w0, uint32_t w1) {
+  const _Float16 b = static_cast<_Float16>(0x1p-17f);            // 128 * 2^-24
+  const uint4 a = key_operand8(w0, w1);
+  return uint4{sub_f16x2(a.x, b), sub_f16x2(a.y, b), sub_f16x2(a.z, b), sub_f16x2(a.w, b)};
 }
-// eight int4 codes, stored biased (u = code + 8) with operand element 2m in
-// nibble m and 2m+1 in nibble m+4 -> one 8 x fp16 MFMA operand, exactly: the
-// fp16 with bits 0x640u is 1024 + u (pairs 0, 2: nibbles 0/4 of w and of
-// w >> 8), minus 1032; the one with bits 0x64u0 is 1024 + 16u (pairs 1, 3:
-// nibbles 1/5), times 1/16 minus 72 (one fused step, exact)
-__device__ __forceinline__ uint4 widen4(uint32_t w, uint32_t k1024) {
-  const half2v bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-  const half2v sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-  const half2v bias16 = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-  const uint32_t w8 = w >> 8;
-  const half2v p0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | k1024);
-  const half2v p1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | k1024);
-  const half2v p2 = __builtin_bit_cast(half2v, (w8 & 0x000F000Fu) | k1024);
-  const half2v p3 = __builtin_bit_cast(half2v, (w8 & 0x00F000F0u) | k1024);
-  return uint4{__builtin_bit_cast(uint32_t, p0 - bias),
-               __builtin_bit_cast(uint32_t, p1 * sixteenth + bias16),
-               __builtin_bit_cast(uint32_t, p2 - bias),
-               __builtin_bit_cast(uint32_t, p3 * sixteenth + bias16)};
+__device__ __forceinline__ uint4 value_operand4(uint32_t w) {
+  const _Float16 b8 = static_cast<_Float16>(0x1p-21f);           // 8 * 2^-24
+  const _Float16 b128 = static_cast<_Float16>(0x1p-17f);         // 16 * 8 * 2^-24
+  const uint4 a = i4x8_operand(w);
+  return uint4{sub_f16x2(a.x, b8), sub_f16x2(a.y, b128), sub_f16x2(a.z, b8), sub_f16x2(a.w, b128)};
 }
 
 __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
@@ -117,10 +126,11 @@ __device__ __forceinline__ float bfly_lane(float x, int lane, int m) {
 
 // q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] fp16 bits; rows
 // padded by 8 elements so the 16 heads' 16-byte reads spread over the banks
-template <int R>
+template <int R, int kWaves>
 struct Smem {
   uint16_t q[2][16][R + 8];
   float qc[16];              // power of two each head's q~ was divided by
+  float qbias[16];           // -bias * sum_k q_k * 2^-24: the score accumulators' start
   float svmax[kWaves];       // each wave's largest value scale
   float acc[kWaves / 2][4 * (R / 16)][64];   // softmax states (final merge)
   float m[kWaves / 2][64], l[kWaves / 2][64];
@@ -145,7 +155,8 @@ struct Block {
 };
 
 template <int R, bool kShared, int kBits>
-__global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_kernel(DecodeParams p) {
+  constexpr int kWaves = kWavesFor<kBits>;
   constexpr int kRowBytes = R * kBits / 8;               // bytes of a cached row
   const int nslice = (p.nq + 15) / 16;
   const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
   if (s0 >= n) return;                                   // whole workgroup
   const int t1 = min(n, s0 + p.split_tokens);
 
-  __shared__ Smem<R> sm;
+  __shared__ Smem<R, kWaves> sm;
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
   const int8_t* Hk = static_cast<const int8_t*>(p.h_k) + row0 * kRowBytes;
   const int8_t* Hv = static_cast<const int8_t*>(p.h_v) + row0 * kRowBytes;
@@ -274,29 +285,50 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
       const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
       const float c = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
       const float inv = 1.f / c;                     // exact: c is a power of two
+      // int4: latents k % 8 in {2, 3, 6, 7} (k = lane + 64 j) meet operands
+      // scaled by 16, so their q~ is divided by 16 (exact)
+      const bool by16 = kBits == 4 && ((lane >> 1) & 1);
+      const float ks = by16 ? 0.0625f : 1.f;
+      float qsum = 0.f;                              // sum_k of what the products see
 #pragma unroll
-      for (int j = 0; j < R / 64; ++j)
-        split_f16(qx[i][j] * inv, sm.q[0][hd][lane + 64 * j], sm.q[1][hd][lane + 64 * j]);
-      if (lane == 0) sm.qc[hd] = c;
+      for (int j = 0; j < R / 64; ++j) {
+        uint16_t hb, lb;
+        split_f16(qx[i][j] * inv * ks, hb, lb);
+        sm.q[0][hd][lane + 64 * j] = hb;
+        sm.q[1][hd][lane + 64 * j] = lb;
+        qsum += (static_cast<float>(__builtin_bit_cast(_Float16, hb)) +
+                 static_cast<float>(__builtin_bit_cast(_Float16, lb))) * (by16 ? 16.f : 1.f);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o /= 2) qsum += __shfl_xor(qsum, o);
+      if (lane == 0) {
+        sm.qc[hd] = c;
+        sm.qbias[hd] = -(kBits == 8 ? 128.f : 8.f) * qsum * 0x1p-24f;
+      }
     }
   }
   barrier_lds();            // the first tiles stay in flight
   // scores are multiplied by qc * s_k, value weights by s_v / vref and the
   // partial sums by vref
-  const float qc = sm.qc[ln];
+  const float qc = sm.qc[ln] * 0x1p24f;                 // the operands' 2^-24 too
+  const float qb = sm.qbias[ln];
   float vref = sm.svmax[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) vref = fmaxf(vref, sm.svmax[w]);
   if (!(vref > 0.f && vref < INFINITY)) vref = 1.f;
   const float vinv = 1.f / vref;
+  // value weights of the tokens whose int4 operand elements carry 16 u (k-slot
+  // elements 2, 3, 6, 7: the lane's tokens i = 2, 3 of each half) divided by 16
+  const floatx4 vinvv = kBits == 4 ? floatx4{vinv, vinv, vinv * 0.0625f, vinv * 0.0625f}
+                                   : floatx4{vinv, vinv, vinv, vinv};
 
   State<R> st;
   st.m = -INFINITY;
   st.l = 0.f;
+
 #pragma unroll
   for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t k1024 = f16x2_1024_bits();
   // masked: the block may reach past the split's end (only a wave's last
   // block can: every other block of a wave lies whole inside the split)
   auto compute = [&](const Block<R, kBits>& x, int t0, auto masked) {
@@ -306,7 +338,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
     asm volatile("" ::: "memory");
     // scores of the two 16-token halves: S^T[16 tok x 16 heads] of half h
     // (q~ hi and lo parts in separate accumulators: four independent chains)
-    floatx4 shi[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 shi[2] = {{qb, qb, qb, qb}, {qb, qb, qb, qb}};
     floatx4 slo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int c = 0; c < R / 32; ++c) {
@@ -319,18 +351,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
         uint4 a;
         if constexpr (kBits == 8) {
           const int w = 4 * (h * (R / 64) + c / 2) + 2 * (c % 2);
-          a = widen8(x.k[w], x.k[w + 1]);
+          a = key_operand8(x.k[w], x.k[w + 1]);
         } else {
-          a = widen4(x.k[h * (R / 32) + c], k1024);
+          a = key_operand4(x.k[h * (R / 32) + c]);
         }
         shi[h] = mfma(a, qh, shi[h]);
         slo[h] = mfma(a, ql, slo[h]);
       }
     }
-    // scores in units of qc (the head's power-of-two divisor): qc is applied
-    // in the exponent
+    // scores in units of qc * 2^-24 (qc the head's power-of-two divisor),
+    // bias already out: that factor is applied in the exponent
     floatx4 sc[2] = {(shi[0] + slo[0]) * x.sk0, (shi[1] + slo[1]) * x.sk1};
-    floatx4 sv[2] = {x.sv0 * vinv, x.sv1 * vinv};
+    floatx4 sv[2] = {x.sv0 * vinvv, x.sv1 * vinvv};
     if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -377,17 +409,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
     const uint4 bl = {pl[0], pl[1], pl[2], pl[3]};
     // values: U^T[16 rb .. +16, heads] += H_v^T[., 32 tokens] P^T; latent rows
     // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
+    // (four row blocks at a time, hi parts first: an MFMA never waits on the
+    // one just before it)
 #pragma unroll
-    for (int rb = 0; rb < R / 16; ++rb) {
-      uint4 a;
-      if constexpr (kBits == 8) {
-        const int w = 4 * (rb / 2) + 2 * (rb % 2);
-        a = widen8(x.v[w], x.v[w + 1]);
-      } else {
-        a = widen4(x.v[rb], k1024);                      // the lane's unit rb
+    for (int rb0 = 0; rb0 < R / 16; rb0 += 4) {
+      uint4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rb = rb0 + u;
+        if constexpr (kBits == 8) {
+          const int w = 4 * (rb / 2) + 2 * (rb % 2);
+          a[u] = value_operand8(x.v[w], x.v[w + 1]);
+        } else {
+          a[u] = value_operand4(x.v[rb]);                // the lane's unit rb
+        }
       }
-      st.acc[rb] = mfma(a, bh, st.acc[rb]);
-      st.acc[rb] = mfma(a, bl, st.acc[rb]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st.acc[rb0 + u] = mfma(a[u], bh, st.acc[rb0 + u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st.acc[rb0 + u] = mfma(a[u], bl, st.acc[rb0 + u]);
     }
   };
   // the hot loops fetch unconditionally (a fetch under a branch made the
@@ -446,7 +486,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_int_kernel(Deco
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  float uscale = vref;
+  float uscale = vref * 0x1p24f;                       // the operands' 2^-24
   if (p.hadamard) {
     // rotated cache: u = u'' H_r / r; latent 16 rb + 4 kb + i of the lane's
     // head: bits 0-1 in the vector, 2-3 in lane bits 4-5, the rest in rb
@@ -491,12 +531,13 @@ template <int R, int kBits>
 hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
   const int nslice = absorbed_head_slices(p.nq);
   if (nslice == 1) {
-    split_absorbed_int_kernel<R, false, kBits><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+    split_absorbed_int_kernel<R, false, kBits>
+        <<<dim3(p.n_split, p.G, p.B), 64 * kWavesFor<kBits>, 0, st>>>(p);
   } else {
     const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
     if (ids == 0) return hipErrorInvalidValue;
     split_absorbed_int_kernel<R, true, kBits>
-        <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
+        <<<dim3(static_cast<unsigned>(ids)), 64 * kWavesFor<kBits>, 0, st>>>(p);
   }
   return hipGetLastError();
 }

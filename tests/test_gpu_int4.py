@@ -133,8 +133,9 @@ def test_int4_latent_output():
 @pytest.mark.parametrize("idx", [3, 64])
 def test_int4_matches_int8_on_the_same_codes(idx):
     """Codes in [-7, 7] are also int8 codes: the int8 decode on them (same
-    scales) runs the same fp16 operands through the same arithmetic, so the
-    two agree to rounding noise at most."""
+    scales) computes the same attention; the two differ only in the rounding
+    of the score accumulators, whose bias term (128 or 8 times the sum of q~)
+    is taken back in fp32."""
     import torch
     import rank_compressed_kv_amd as P
     cfg = SMALL[idx]
@@ -147,7 +148,7 @@ def test_int4_matches_int8_on_the_same_codes(idx):
     torch.cuda.synchronize()
     b = b.cpu().numpy().astype(np.float64)
     print(f"[int4 vs int8] cfg{idx} max|d|={np.max(np.abs(a - b)):.3e}", flush=True)
-    assert_close(a, b, max_abs=1e-5, rel_l2=1e-6, what="int4 vs int8")
+    assert_close(a, b, max_abs=2e-4, rel_l2=2e-5, what="int4 vs int8")
 
 
 @pytest.mark.parametrize("idx", [3, 4, 64])
