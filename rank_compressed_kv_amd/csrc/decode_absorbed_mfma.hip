@@ -142,15 +142,24 @@ __device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const ch
     pl[e] = static_cast<short>(f32_to_bf16_rne(p - hi));
   }
   // values: gather H_v^T[16*rb + ln][tokens 4*kb .. 4*kb+3] from the LDS tile
+  // (four row blocks at a time, hi parts first: an MFMA never waits on the one
+  // just before it)
+  constexpr int kU = R / 16 < 4 ? R / 16 : 4;            // R / 16 is a multiple
   const char* vb = vt + vtile_off<R>(4 * kb, 2 * ln);
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb) {
-    short4v a;
+  for (int rb0 = 0; rb0 < R / 16; rb0 += kU) {
+    short4v a[kU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      a[e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * rb);
-    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, st.acc[rb], 0, 0, 0);
-    st.acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, st.acc[rb], 0, 0, 0);
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[u][e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * (rb0 + u));
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      st.acc[rb0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[u], ph, st.acc[rb0 + u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      st.acc[rb0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[u], pl, st.acc[rb0 + u], 0, 0, 0);
   }
 }
 

@@ -411,6 +411,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
     // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
     // (four row blocks at a time, hi parts first: an MFMA never waits on the
     // one just before it)
+    static_assert(R % 64 == 0, "row blocks come in fours");
 #pragma unroll
     for (int rb0 = 0; rb0 < R / 16; rb0 += 4) {
       uint4 a[4];
