@@ -226,11 +226,9 @@ palu_status palu_latent_append(const palu_append_desc* desc, const void* x, cons
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace palu_latent_append_i8 needs: the counters of
- * palu_latent_append, a second counter area (one int32 per (matrix, group)
- * row segment, padded to 256 bytes), the same partial sums, and the finished
- * fp32 rows [B, 2*G*r]. The whole counter area must be zero before the first
- * call, as for palu_latent_append. */
+/* Bytes of device workspace palu_latent_append_i8 needs: the same areas as
+ * palu_latent_append's (counters, then partial sums), under the same rule:
+ * the counter area is zero before the first call. */
 palu_status palu_latent_append_i8_workspace(const palu_append_desc* desc, size_t* bytes);
 
 /* Quantised cache write of one token per sequence into the int8 cache that

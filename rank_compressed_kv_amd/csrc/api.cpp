@@ -379,7 +379,7 @@ palu_status append(const palu_append_desc* d, int qbits, const void* x, const vo
     return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
   if (quant && (reinterpret_cast<uintptr_t>(h_k) % 4 || reinterpret_cast<uintptr_t>(h_v) % 4))
     return fail(PALU_ERR_SHAPE, "int%d caches must be 4-byte aligned", qbits);
-  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, quant);
+  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   if (workspace_bytes < need)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 16)
@@ -403,7 +403,7 @@ palu_status palu_latent_append_workspace(const palu_append_desc* d, size_t* byte
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
-  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, false);
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   return ok();
 }
 
@@ -422,7 +422,7 @@ palu_status palu_latent_append_i8_workspace(const palu_append_desc* d, size_t* b
   palu_status st = validate_append_quant(d, 8);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
-  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, true);
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   return ok();
 }
 
@@ -440,7 +440,7 @@ palu_status palu_latent_append_i4_workspace(const palu_append_desc* d, size_t* b
   palu_status st = validate_append_quant(d, 4);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
-  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank, true);
+  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   return ok();
 }
 

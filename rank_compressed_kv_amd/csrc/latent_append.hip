@@ -5,25 +5,25 @@
 // reading A once (4 MiB per matrix at d_model 4096, G*r 512 in bf16) and whose
 // time is one memory latency if every load of the chip is in flight together.
 // One launch does all of it, split over d_model:
-//   every workgroup owns a 128-column block of [A_k | A_v] and a 128-row
-//   slice; thread (8-column chunk, row group of 8 rows) issues its eight
-//   16-byte loads at once and accumulates x[b, row] * A[row, col] for every
-//   sequence. The 16 row groups are added in LDS in a fixed order and the
-//   workgroup stores one fp32 partial per (slice, sequence, column) in the
-//   workspace, then counts itself in the column block's arrival counter;
+//   every workgroup owns a block of columns of [A_k | A_v] (128 columns and
+//   four waves for a dtype cache, 256 and eight for a quantised one) and a
+//   128-row slice; thread (8-column chunk, row group of 8 rows) issues its
+//   eight 16-byte loads at once and accumulates x[b, row] * A[row, col] for
+//   every sequence. The 16 row groups are added in LDS in a fixed order and
+//   the workgroup stores one fp32 partial per (slice, sequence, column) in
+//   the workspace, then counts itself in the column block's arrival counter;
 //   the last workgroup of a column block adds the slice partials in slice
 //   order, rounds (bf16: nearest, ties to even), writes row pos[b] of the
 //   cache and puts the counter back to zero for the next call.
 // The result does not depend on which workgroup arrives last.
 //
-// int8 cache (per-token quantisation of the latents, Palu author response to
-// reviewer Fsn9 on W1/W2): each cached row of r latents is stored as int8
-// codes with one fp32 scale, amax / 127, codes round(h * 127 / amax) (nearest,
-// ties to even; all in fp32). A row can span several column blocks, so the
-// column blocks' last arrivers hand the finished fp32 rows over once more:
-// they store them in the workspace and count themselves in the arrival
-// counter of each (matrix, group) row segment they cover; the last one of a
-// segment quantises it for every sequence and resets that counter.
+// Quantised caches (per-token quantisation of the latents, Palu author
+// response to reviewer Fsn9 on W1/W2): each cached row of r latents is stored
+// as int8 codes with one fp32 scale, amax / 127, codes round(h * 127 / amax)
+// (nearest, ties to even; all in fp32), or as int4 codes with amax / 7. A
+// row (r in {64, 128, 256} columns, aligned to r) never crosses a 256-column
+// block, so the block's last arriver holds whole rows: it stages them in LDS
+// and quantises them there, one wave per (sequence, row).
 // With the Hadamard option (a quantisation-friendly enhancement the author
 // responses name, answer to Q2) each fp32 row is first rotated by Sylvester's
 // H_r, h'' = h H_r, which spreads an outlier latent over all r codes.
@@ -33,18 +33,31 @@
 namespace palu {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;          // d_model rows per slice (256 and 512 measured slower)
-constexpr int kCols = 128;          // columns per block (16 chunks of 8)
-constexpr int kRowGroups = 16;      // threads per column chunk
-constexpr int kRowsPerThread = kRows / kRowGroups;
-constexpr int kBatchChunk = 8;      // sequences accumulated per pass
+constexpr int kRows = 128;          // d_model rows per slice
+constexpr int kMinCols = 128;       // the narrower column block (counter area size)
 constexpr size_t kCounterAlign = 256;
 
-// LDS slot of the 4-column quarter (chunk cc, half hf) of a block: the two
-// halves of a chunk are 16 slots apart so a wave's 16-byte writes spread over
-// all banks; slot q holds columns col_of_slot(q) .. +4.
-__device__ __forceinline__ int col_of_slot(int q) { return q < 16 ? 8 * q : 8 * (q - 16) + 4; }
+// Tiling of the two forms. dtype caches: 128-column blocks of four waves
+// (measured 10.8 us against 11.6 us for the wider form at Llama-3-8B);
+// quantised caches: 256-column blocks of eight waves, so that a block holds
+// whole quantised rows (12.7 us against 14.4 us with a second hand-off).
+template <bool kQuant>
+struct Tiling {
+  static constexpr int kThreads = kQuant ? 512 : 256;
+  static constexpr int kCols = kQuant ? 256 : kMinCols;
+  static constexpr int kChunks = kCols / 8;                   // 8-column chunks
+  static constexpr int kRowGroups = kThreads / kChunks;       // threads per chunk
+  static constexpr int kRowsPerThread = kRows / kRowGroups;
+  static constexpr int kBatchChunk = kQuant ? 4 : 8;          // sequences per LDS round
+  static constexpr int kXPer = kBatchChunk * kRows / kThreads;   // x entries per thread
+  static constexpr int kReaders = kThreads / (2 * kChunks);   // sequences per final round
+  // LDS slot of the 4-column quarter (chunk cc, half hf) of a block: the two
+  // halves of a chunk are kChunks slots apart so a wave's 16-byte writes
+  // spread over all banks; slot q holds columns col_of_slot(q) .. +4.
+  static __device__ __forceinline__ int col_of_slot(int q) {
+    return q < kChunks ? 8 * q : 8 * (q - kChunks) + 4;
+  }
+};
 
 // Hand-off of the partials between workgroups on different XCDs, whose L2
 // caches are not coherent with each other:
@@ -118,90 +131,86 @@ __device__ __forceinline__ float4 hadamard_row(float4 v, int lane, int nq) {
   return v;
 }
 
-// quantise the finished fp32 rows of segment j (matrix j / G, group j % G) of
-// every sequence into the int8 cache: one wave per sequence, four consecutive
-// latents per lane (r in {64, 128, 256}, so nq <= 64)
-__device__ void quantize_segment(const AppendParams& p, int j, int wave, int lane) {
-  const int width = p.G * p.r;
+// quantise one finished fp32 row (segment j = matrix j / G, group j % G of
+// sequence b, four consecutive latents per lane: r in {64, 128, 256}, so nq
+// <= 64) into the cache at pos: one wave
+__device__ void quantize_row(const AppendParams& p, float4 v0, int j, int b, int pos, int lane) {
   const bool is_v = j >= p.G;
   const int g = is_v ? j - p.G : j;
   int8_t* h = static_cast<int8_t*>(is_v ? p.h_v : p.h_k);
   float* sc = is_v ? p.s_v : p.s_k;
   const int nq = p.r / 4;                              // float4 per row, <= 64
-  for (int b = wave; b < p.B; b += kThreads / 64) {
-    const int pos = p.pos[b];
-    if (pos < 0 || pos >= p.L) continue;
-    const float* src = p.rows + static_cast<size_t>(b) * 2 * width + static_cast<size_t>(j) * p.r;
-    float4 v0 = {0.f, 0.f, 0.f, 0.f};
-    if (lane < nq) v0 = *reinterpret_cast<const float4*>(src + 4 * lane);
-    if (p.hadamard) v0 = hadamard_row(v0, lane, nq);
-    float amax = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
+  if (lane >= nq) v0 = float4{0.f, 0.f, 0.f, 0.f};
+  if (p.hadamard) v0 = hadamard_row(v0, lane, nq);
+  float amax = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
 #pragma unroll
-    for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
-    // correctly rounded fp32 divisions (the HIP default); int4: 15 levels
-    const float qmax = p.quant == 4 ? 7.f : 127.f;
-    const float scale = amax > 0.f ? amax / qmax : 0.f;
-    const float inv = amax > 0.f ? qmax / amax : 0.f;
-    auto code = [&](float x) {
-      const float c = fminf(fmaxf(rintf(x * inv), -qmax), qmax);
-      return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
-    };
-    auto code4 = [&](float x) {                          // biased nibble code + 8
-      return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x * inv), -7.f), 7.f)) + 8);
-    };
-    auto pack = [&](float4 v) {
-      return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
-    };
-    const size_t row = (static_cast<size_t>(b) * p.G + g) * p.L + pos;
-    if (p.quant == 4) {
-      // keys: the four latents 4 lane .. +3 fill two whole bytes; values: each
-      // byte also holds another token's code (not written by this call), so
-      // its other nibble is kept
-      uint8_t* slab4 = reinterpret_cast<uint8_t*>(h) + (row - pos) * (p.r / 2);
-      if (lane < nq) {
-        const int k0 = 4 * lane;
-        int hi;
-        if (!is_v) {
-          slab4[i4_key_byte(pos, k0, p.r, hi)] =
-              static_cast<uint8_t>(code4(v0.x) | (code4(v0.z) << 4));
-          slab4[i4_key_byte(pos, k0 + 1, p.r, hi)] =
-              static_cast<uint8_t>(code4(v0.y) | (code4(v0.w) << 4));
-        } else {
-          const float e[4] = {v0.x, v0.y, v0.z, v0.w};
+  for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // correctly rounded fp32 divisions (the HIP default); int4: 15 levels
+  const float qmax = p.quant == 4 ? 7.f : 127.f;
+  const float scale = amax > 0.f ? amax / qmax : 0.f;
+  const float inv = amax > 0.f ? qmax / amax : 0.f;
+  auto code = [&](float x) {
+    const float c = fminf(fmaxf(rintf(x * inv), -qmax), qmax);
+    return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
+  };
+  auto code4 = [&](float x) {                          // biased nibble code + 8
+    return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x * inv), -7.f), 7.f)) + 8);
+  };
+  auto pack = [&](float4 v) {
+    return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
+  };
+  const size_t row = (static_cast<size_t>(b) * p.G + g) * p.L + pos;
+  if (p.quant == 4) {
+    // keys: the four latents 4 lane .. +3 fill two whole bytes; values: each
+    // byte also holds another token's code (not written by this call), so
+    // its other nibble is kept
+    uint8_t* slab4 = reinterpret_cast<uint8_t*>(h) + (row - pos) * (p.r / 2);
+    if (lane < nq) {
+      const int k0 = 4 * lane;
+      int hi;
+      if (!is_v) {
+        slab4[i4_key_byte(pos, k0, p.r, hi)] =
+            static_cast<uint8_t>(code4(v0.x) | (code4(v0.z) << 4));
+        slab4[i4_key_byte(pos, k0 + 1, p.r, hi)] =
+            static_cast<uint8_t>(code4(v0.y) | (code4(v0.w) << 4));
+      } else {
+        const float e[4] = {v0.x, v0.y, v0.z, v0.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint8_t* byte = slab4 + i4_value_byte(pos, k0 + i, p.r, hi);
-            const uint32_t u = code4(e[i]);
-            *byte = static_cast<uint8_t>(hi ? ((*byte & 0x0Fu) | (u << 4)) : ((*byte & 0xF0u) | u));
-          }
+        for (int i = 0; i < 4; ++i) {
+          uint8_t* byte = slab4 + i4_value_byte(pos, k0 + i, p.r, hi);
+          const uint32_t u = code4(e[i]);
+          *byte = static_cast<uint8_t>(hi ? ((*byte & 0x0Fu) | (u << 4)) : ((*byte & 0xF0u) | u));
         }
       }
-      if (lane == 0) sc[row] = scale;
-      continue;
     }
+  } else {
     int8_t* slab = h + (row - pos) * p.r;
     // keys: four consecutive latents are four consecutive bytes; values: 16
     // bytes apart
-    auto put = [&](int k, float4 v) {
+    if (lane < nq) {
+      const int k = 4 * lane;
       if (!is_v) {
-        *reinterpret_cast<uint32_t*>(slab + i8_key_offset(pos, k, p.r)) = pack(v);
+        *reinterpret_cast<uint32_t*>(slab + i8_key_offset(pos, k, p.r)) = pack(v0);
       } else {
-        const float e[4] = {v.x, v.y, v.z, v.w};
+        const float e[4] = {v0.x, v0.y, v0.z, v0.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           slab[i8_value_offset(pos, k + i, p.r)] = static_cast<int8_t>(static_cast<uint8_t>(code(e[i])));
       }
-    };
-    if (lane < nq) put(4 * lane, v0);
-    if (lane == 0) sc[row] = scale;
+    }
   }
+  if (lane == 0) sc[row] = scale;
 }
 
 template <typename T, bool kQuant>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(Tiling<kQuant>::kThreads) void append_kernel(AppendParams p) {
+  using Tl = Tiling<kQuant>;
+  constexpr int kThreads = Tl::kThreads, kCols = Tl::kCols, kChunks = Tl::kChunks;
+  constexpr int kRowGroups = Tl::kRowGroups, kRowsPerThread = Tl::kRowsPerThread;
+  constexpr int kBatchChunk = Tl::kBatchChunk, kXPer = Tl::kXPer, kReaders = Tl::kReaders;
   const int width = p.G * p.r;                 // columns of one matrix
   const int tid = threadIdx.x;
-  const int cc = tid % 16, rg = tid / 16;      // 8-column chunk, row group
+  const int cc = tid % kChunks, rg = tid / kChunks;    // 8-column chunk, row group
   const int cb0 = blockIdx.x * kCols;
   const int col0 = cb0 + 8 * cc;               // in [0, 2*width)
   const int slice = blockIdx.y, nslices = gridDim.y;
@@ -214,9 +223,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   const T* x = static_cast<const T*>(p.x);
   const size_t prow = 2 * static_cast<size_t>(width);   // floats per (slice, sequence)
 
-  // all of this thread's A rows (rg + 16 i) first, 16 bytes each, with no
-  // branch around the loads: rows past the slice read its last row and
-  // columns past the block read column 0 (finite values; the matching x
+  // all of this thread's A rows (rg + kRowGroups i) first, 16 bytes each,
+  // with no branch around the loads: rows past the slice read its last row
+  // and columns past the block read column 0 (finite values; the matching x
   // entries are 0 and the results for such columns are never stored)
   Raw8<T> a[kRowsPerThread];
   const int ca = active ? c : 0;
@@ -225,36 +234,34 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
     const int row = min(rg + kRowGroups * i, rows - 1);
     a[i].load(A + static_cast<size_t>(i0 + row) * width + ca);
   }
-  // x entries of the first sequence chunk: four per thread, issued right
-  // after the A loads so both are in flight together
-  constexpr int kPer = kBatchChunk * kRows / kThreads;
-  float xv[kPer];
-  auto load_x = [&](int b0, int nb) {
+  // x entries of a sequence chunk (kXPer per thread), issued right after the
+  // A loads so both are in flight together
+  static_assert(kXPer * kThreads == kBatchChunk * kRows, "whole x entries per thread");
+  float xv[kXPer];
+  auto load_x = [&](int b0) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kXPer; ++u) {
       const int e = tid + u * kThreads, bb = e / kRows, i = e % kRows;
-      const int bc = min(bb, nb - 1), ic = min(i, rows - 1);
-      xv[u] = load_f32(x, static_cast<size_t>(b0 + bc) * p.dm + i0 + ic);
+      const int bc = min(b0 + bb, p.B - 1), ic = min(i, rows - 1);
+      xv[u] = load_f32(x, static_cast<size_t>(bc) * p.dm + i0 + ic);
     }
   };
-  load_x(0, min(kBatchChunk, p.B));
+  load_x(0);
   __shared__ float xs[kBatchChunk][kRows];
-  __shared__ float4 red[kRowGroups][kBatchChunk][kCols / 4];
+  __shared__ float4 red[kRowGroups][kBatchChunk][2 * kChunks];
   __shared__ int is_last;
-  const int fb = tid / 32, fq = tid % 32;      // reader: sequence in chunk, slot
-  const int fcol = cb0 + col_of_slot(fq);
+  const int fb = tid / (2 * kChunks), fq = tid % (2 * kChunks);   // reader: sequence, slot
+  const int fcol = cb0 + Tl::col_of_slot(fq);
   for (int b0 = 0; b0 < p.B; b0 += kBatchChunk) {
     const int nb = min(kBatchChunk, p.B - b0);
     __syncthreads();
-    {
-      if (b0 > 0) load_x(b0, nb);
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int e = tid + u * kThreads, bb = e / kRows, i = e % kRows;
-        xs[bb][i] = bb < nb && i < rows ? xv[u] : 0.f;
-      }
+    for (int u = 0; u < kXPer; ++u) {
+      const int e = tid + u * kThreads, bb = e / kRows, i = e % kRows;
+      xs[bb][i] = bb < nb && i < rows ? xv[u] : 0.f;
     }
     __syncthreads();
+    if (b0 + kBatchChunk < p.B) load_x(b0 + kBatchChunk);
 #pragma unroll
     for (int bb = 0; bb < kBatchChunk; ++bb) {
       float acc[8];
@@ -262,25 +269,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < kRowsPerThread; ++i) {
-        const float xv = xs[bb][rg + kRowGroups * i];
+        const float xr = xs[bb][rg + kRowGroups * i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv, a[i][e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xr, a[i][e], acc[e]);
       }
       red[rg][bb][cc] = float4{acc[0], acc[1], acc[2], acc[3]};
-      red[rg][bb][cc + 16] = float4{acc[4], acc[5], acc[6], acc[7]};
+      red[rg][bb][cc + kChunks] = float4{acc[4], acc[5], acc[6], acc[7]};
     }
     __syncthreads();
-    // row groups added in order; one 16-byte partial per thread
-    float4 s = red[0][fb][fq];
+    // row groups added in order; one 16-byte partial per reading thread
+    if (fb < nb) {
+      float4 s = red[0][fb][fq];
 #pragma unroll
-    for (int k = 1; k < kRowGroups; ++k) {
-      const float4 v = red[k][fb][fq];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    if (fb < nb && fcol < 2 * width) {
-      float* dst = p.part + (static_cast<size_t>(slice) * p.B + b0 + fb) * prow + fcol;
-      store_coherent2(dst, s.x, s.y);
-      store_coherent2(dst + 2, s.z, s.w);
+      for (int k = 1; k < kRowGroups; ++k) {
+        const float4 v = red[k][fb][fq];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+      if (fcol < 2 * width) {
+        float* dst = p.part + (static_cast<size_t>(slice) * p.B + b0 + fb) * prow + fcol;
+        store_coherent2(dst, s.x, s.y);
+        store_coherent2(dst + 2, s.z, s.w);
+      }
     }
   }
 
@@ -295,14 +304,19 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  if (fcol < 2 * width) {
-    const size_t sstride = static_cast<size_t>(p.B) * prow;
-    for (int b = fb; b < p.B; b += kThreads / 32) {
-      const int pos = p.pos[b];
-      if (pos < 0 || pos >= p.L) continue;
+  // the finished rows of kReaders sequences at a time (quantised caches:
+  // staged in LDS, then quantised one wave per (sequence, row segment))
+  __shared__ float4 rowbuf[kQuant ? kReaders : 1][2 * kChunks];
+  const int j0 = cb0 / p.r;                                   // first row segment
+  const int nseg = kQuant ? (min(cb0 + kCols, 2 * width) - cb0) / p.r : 0;   // r divides 256
+  const size_t sstride = static_cast<size_t>(p.B) * prow;
+  for (int bq = 0; bq < p.B; bq += kReaders) {
+    const int b = bq + fb;
+    const int pos = b < p.B ? p.pos[b] : -1;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (b < p.B && fcol < 2 * width && pos >= 0 && pos < p.L) {
       const float* src = p.part + static_cast<size_t>(b) * prow + fcol;
       // up to 32 slices (d_model 4096) in flight at once, then added in order
-      float4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int s0 = 0; s0 < nslices; s0 += 32) {
         float4 v[32];
 #pragma unroll
@@ -315,11 +329,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
           }
         }
       }
-      if constexpr (kQuant) {
-        float* dst = p.rows + static_cast<size_t>(b) * prow + fcol;
-        store_coherent2(dst, acc.x, acc.y);
-        store_coherent2(dst + 2, acc.z, acc.w);
-      } else {
+      if constexpr (!kQuant) {
         const float r4[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -332,71 +342,59 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
         }
       }
     }
+    if constexpr (kQuant) {
+      rowbuf[fb][(fcol - cb0) / 4] = acc;
+      __syncthreads();
+      const int wave = tid / 64, lane = tid % 64;
+      for (int task = wave; task < kReaders * nseg; task += kThreads / 64) {
+        const int bb = task / nseg, sg = task % nseg, bs = bq + bb;
+        if (bs >= p.B) continue;
+        const int ps = p.pos[bs];
+        if (ps < 0 || ps >= p.L) continue;
+        const float4 v0 = lane < p.r / 4 ? rowbuf[bb][(sg * p.r) / 4 + lane] : float4{0.f, 0.f, 0.f, 0.f};
+        quantize_row(p, v0, j0 + sg, bs, ps, lane);
+      }
+      __syncthreads();
+    }
   }
   if (tid == 0) __hip_atomic_store(&p.counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (kQuant) {
-    // second hand-off: row segments j = column / r (matrix j / G, group j % G)
-    // overlapping this block; the rows are complete at device scope before
-    // the segment counters count this block
-    __shared__ int seg_last[kCols + 1];
-    const int j0 = cb0 / p.r, j1 = (min(cb0 + kCols, 2 * width) - 1) / p.r;
-    wait_stores_complete();
-    __syncthreads();
-    for (int j = j0 + tid; j <= j1; j += kThreads) {
-      const int blocks = ((j + 1) * p.r - 1) / kCols - (j * p.r) / kCols + 1;
-      seg_last[j - j0] = __hip_atomic_fetch_add(&p.seg_counters[j], 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT) == blocks - 1;
-    }
-    __syncthreads();
-    bool any = false;
-    for (int j = j0; j <= j1; ++j) any |= seg_last[j - j0] != 0;
-    if (!any) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int j = j0; j <= j1; ++j) {
-      if (!seg_last[j - j0]) continue;
-      quantize_segment(p, j, tid / 64, tid % 64);
-      if (tid == 0)
-        __hip_atomic_store(&p.seg_counters[j], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 }
 
 size_t align_counters(size_t n) {
   return (n * sizeof(int32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
 }
-// counter area: one per column block, then (int8 cache) one per row segment
-size_t counter_bytes(int G, int r, bool quant) {
-  const size_t blocks = (2 * static_cast<size_t>(G) * r + kCols - 1) / kCols;
-  return align_counters(blocks) + (quant ? align_counters(2 * static_cast<size_t>(G)) : 0);
+// counter area: one per column block (of the narrower form)
+size_t counter_bytes(int G, int r) {
+  return align_counters((2 * static_cast<size_t>(G) * r + kMinCols - 1) / kMinCols);
 }
 
 }  // namespace
 
-size_t append_workspace_bytes(int B, int dm, int G, int r, bool quant) {
+size_t append_workspace_bytes(int B, int dm, int G, int r) {
   const size_t nks = (dm + kRows - 1) / kRows;
   const size_t row = 2 * size_t(G) * r * sizeof(float);
-  return counter_bytes(G, r, quant) + nks * B * row + (quant ? B * row : 0);
+  return counter_bytes(G, r) + nks * B * row;
 }
 
 void append_bind_workspace(AppendParams& p, void* workspace) {
   char* w = static_cast<char*>(workspace);
-  const size_t blocks = (2 * static_cast<size_t>(p.G) * p.r + kCols - 1) / kCols;
   p.counters = reinterpret_cast<int32_t*>(w);
-  p.seg_counters = p.quant ? reinterpret_cast<int32_t*>(w + align_counters(blocks)) : nullptr;
-  p.part = reinterpret_cast<float*>(w + counter_bytes(p.G, p.r, p.quant != 0));
-  const size_t nks = (p.dm + kRows - 1) / kRows;
-  p.rows = p.quant ? p.part + nks * p.B * 2 * size_t(p.G) * p.r : nullptr;
+  p.part = reinterpret_cast<float*>(w + counter_bytes(p.G, p.r));
 }
 
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
   const int cols = 2 * p.G * p.r;
-  const dim3 grid((cols + kCols - 1) / kCols, (p.dm + kRows - 1) / kRows);
+  const int rows = (p.dm + kRows - 1) / kRows;
   if (p.quant) {
-    if (dtype == 0) append_kernel<float, true><<<grid, kThreads, 0, st>>>(p);
-    else append_kernel<uint16_t, true><<<grid, kThreads, 0, st>>>(p);
+    using Tl = Tiling<true>;
+    const dim3 grid((cols + Tl::kCols - 1) / Tl::kCols, rows);
+    if (dtype == 0) append_kernel<float, true><<<grid, Tl::kThreads, 0, st>>>(p);
+    else append_kernel<uint16_t, true><<<grid, Tl::kThreads, 0, st>>>(p);
   } else {
-    if (dtype == 0) append_kernel<float, false><<<grid, kThreads, 0, st>>>(p);
-    else append_kernel<uint16_t, false><<<grid, kThreads, 0, st>>>(p);
+    using Tl = Tiling<false>;
+    const dim3 grid((cols + Tl::kCols - 1) / Tl::kCols, rows);
+    if (dtype == 0) append_kernel<float, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    else append_kernel<uint16_t, false><<<grid, Tl::kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }

@@ -47,16 +47,14 @@ struct AppendParams {
   void* h_k;          // [B, G, L, r]
   void* h_v;
   const int32_t* pos; // [B]
-  int32_t* counters;  // one arrival counter per 128-column block; zero between calls
+  int32_t* counters;  // one arrival counter per column block; zero between calls
   float* part;        // [ceil(dm/128), B, 2*G*r] fp32 row-slice partial sums
   int32_t B, dm, G, r, L;
-  // int8 cache (h_k, h_v int8 codes): per-row scales and the second hand-off
+  // quantised caches (h_k, h_v codes): per-row scales
   int32_t quant;      // 0: dtype cache; 8 or 4: quantised cache of that width
   int32_t hadamard;   // 1: rows rotated by the Hadamard matrix before quantising
   float* s_k;         // [B, G, L]
   float* s_v;
-  int32_t* seg_counters;  // one per (matrix, group) row segment; zero between calls
-  float* rows;        // [B, 2*G*r] fp32 finished latent rows
 };
 
 // Kernel variants of the context-split decode step.
@@ -85,8 +83,8 @@ int reconstruct_waves_per_wg(int r, int s);
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
-size_t append_workspace_bytes(int B, int dm, int G, int r, bool quant);
-// sets counters, part (and, with p.quant, seg_counters and rows)
+size_t append_workspace_bytes(int B, int dm, int G, int r);
+// sets counters and part
 void append_bind_workspace(AppendParams& p, void* workspace);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 

@@ -223,8 +223,8 @@ def test_append_validation(lib):
 @pytest.mark.parametrize("bits", [8, 4])
 def test_append_quant_validation(lib, bits):
     """The quantised cache write: the append checks, rank 64/128/256, NULL
-    scales, 4-byte aligned caches, and a workspace with a second counter area
-    and the finished rows (the same for both widths)."""
+    scales, 4-byte aligned caches, and the dtype append's workspace (the same
+    for both widths)."""
     fake = ctypes.c_void_p(0x1000)
     good = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
                          dtype=P.PALU_BF16)
@@ -256,9 +256,9 @@ def test_append_quant_validation(lib, bits):
         assert call(good, *ptrs) == P.PALU_ERR_NULL, i
     need = (P.palu_latent_append_i8_workspace if bits == 8
             else P.palu_latent_append_i4_workspace)(good)
-    # column-block counters (256 B), row-segment counters (256 B), the
-    # partials, then the finished fp32 rows [B, 2*G*r]
-    assert need == 256 + 256 + 32 * 8 * 1024 * 4 + 8 * 1024 * 4
+    # the same areas as the dtype append: column-block counters (256 B),
+    # then the partials
+    assert need == 256 + 32 * 8 * 1024 * 4
     assert call(good, *([True] * 9), nbytes=need - 1) == P.PALU_ERR_WORKSPACE
     odd = ctypes.c_void_p(0x1002)
     assert call(good, True, True, True, odd, True, True, True, True, True) == P.PALU_ERR_SHAPE
