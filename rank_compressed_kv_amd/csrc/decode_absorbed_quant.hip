@@ -52,6 +52,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // Llama-3-8B, 32K context); an int8 wave needs a whole SIMD's registers
 template <int kBits>
 constexpr int kWavesFor = kBits == 4 ? 8 : 4;
+constexpr float kV = 8.f;         // value weights' extra power of two (fp16 range: 2^8 kV kF)
 constexpr int kBlock = 32;       // tokens per cache block and per wave step
 constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
 
@@ -157,6 +158,9 @@ struct Block {
 template <int R, bool kShared, int kBits>
 __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_kernel(DecodeParams p) {
   constexpr int kWaves = kWavesFor<kBits>;
+  // every key and value product carries kF * 2^-24 (int4: 16 u against q~ / 16
+  // or 16 q~ against u; the subnormal codes' 2^-24)
+  constexpr float kF = kBits == 4 ? 16.f : 1.f;
   constexpr int kRowBytes = R * kBits / 8;               // bytes of a cached row
   const int nslice = (p.nq + 15) / 16;
   const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
 #pragma unroll
     for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
     if (lane == 0) sm.svmax[wave] = smax;
-    // one wave per head: q~ / 2^e with 2^e <= max |q~_h| < 2^(e+1), hi + lo
+    // one wave per head: q~ scaled by a power of two (below), hi + lo
 #pragma unroll
     for (int i = 0; i < kH; ++i) {
       const int hd = wave + kWaves * i;
@@ -282,14 +286,19 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
       for (int j = 0; j < R / 64; ++j) amax = fmaxf(amax, fabsf(qx[i][j]));
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+      // q~ / c with c = 2^(e-10), 2^e <= max |q~_h| < 2^(e+1): entries up to
+      // 2^11, so the lo parts of all but the smallest entries stay normal fp16
       const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
-      const float c = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
-      const float inv = 1.f / c;                     // exact: c is a power of two
+      const float c0 = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
+      const float boost = c0 >= 0x1p-100f ? 1024.f : 1.f;
+      const float c = c0 / boost;                    // exact: powers of two
+      const float inv = boost / c0;
       // int4: latents k % 8 in {2, 3, 6, 7} (k = lane + 64 j) meet operands
-      // scaled by 16, so their q~ is divided by 16 (exact)
-      const bool by16 = kBits == 4 && ((lane >> 1) & 1);
-      const float ks = by16 ? 0.0625f : 1.f;
-      float qsum = 0.f;                              // sum_k of what the products see
+      // scaled by 16, so the other latents' q~ is multiplied by 16 (exact):
+      // every product then carries kF = 16
+      const bool plain = kBits == 4 && !((lane >> 1) & 1);
+      const float ks = plain ? 16.f : 1.f;
+      float qsum = 0.f;                              // sum_k of q~_k / c
 #pragma unroll
       for (int j = 0; j < R / 64; ++j) {
         uint16_t hb, lb;
@@ -297,30 +306,33 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
         sm.q[0][hd][lane + 64 * j] = hb;
         sm.q[1][hd][lane + 64 * j] = lb;
         qsum += (static_cast<float>(__builtin_bit_cast(_Float16, hb)) +
-                 static_cast<float>(__builtin_bit_cast(_Float16, lb))) * (by16 ? 16.f : 1.f);
+                 static_cast<float>(__builtin_bit_cast(_Float16, lb))) * (plain ? 0.0625f : 1.f);
       }
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) qsum += __shfl_xor(qsum, o);
       if (lane == 0) {
         sm.qc[hd] = c;
-        sm.qbias[hd] = -(kBits == 8 ? 128.f : 8.f) * qsum * 0x1p-24f;
+        sm.qbias[hd] = -(kBits == 8 ? 128.f : 8.f) * qsum * (kF * 0x1p-24f);
       }
     }
   }
   barrier_lds();            // the first tiles stay in flight
   // scores are multiplied by qc * s_k, value weights by s_v / vref and the
   // partial sums by vref
-  const float qc = sm.qc[ln] * 0x1p24f;                 // the operands' 2^-24 too
+  const float qc = sm.qc[ln] * (0x1p24f / kF);          // the products' kF * 2^-24 too
   const float qb = sm.qbias[ln];
   float vref = sm.svmax[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) vref = fmaxf(vref, sm.svmax[w]);
   if (!(vref > 0.f && vref < INFINITY)) vref = 1.f;
   const float vinv = 1.f / vref;
-  // value weights of the tokens whose int4 operand elements carry 16 u (k-slot
-  // elements 2, 3, 6, 7: the lane's tokens i = 2, 3 of each half) divided by 16
-  const floatx4 vinvv = kBits == 4 ? floatx4{vinv, vinv, vinv * 0.0625f, vinv * 0.0625f}
-                                   : floatx4{vinv, vinv, vinv, vinv};
+  // value weights times kV (their fp16 lo parts stay normal longer: weights
+  // reach 2^8 kV kF <= 2^15), and for int4 those of the tokens whose operand
+  // elements carry u, not 16 u (k-slot elements 0, 1, 4, 5: the lane's tokens
+  // i = 0, 1 of each half) times 16, so every product carries kV kF
+  const float vw = vinv * kV;
+  const floatx4 vinvv = kBits == 4 ? floatx4{vw * 16.f, vw * 16.f, vw, vw}
+                                   : floatx4{vw, vw, vw, vw};
 
   State<R> st;
   st.m = -INFINITY;
@@ -487,7 +499,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  float uscale = vref * 0x1p24f;                       // the operands' 2^-24
+  float uscale = vref * (0x1p24f / (kF * kV));         // the products' factors
   if (p.hadamard) {
     // rotated cache: u = u'' H_r / r; latent 16 rb + 4 kb + i of the lane's
     // head: bits 0-1 in the vector, 2-3 in lane bits 4-5, the rest in rb
