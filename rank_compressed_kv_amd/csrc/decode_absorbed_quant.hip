@@ -129,12 +129,15 @@ __device__ __forceinline__ float bfly_lane(float x, int lane, int m) {
 // padded by 8 elements so the 16 heads' 16-byte reads spread over the banks
 template <int R, int kWaves>
 struct Smem {
-  uint16_t q[2][16][R + 8];
+  union {
+    uint16_t q[2][16][R + 8];
+    float urot[16][R + 4];   // merged value sums of a rotated cache (after the loop)
+  };
   float qc[16];              // power of two each head's q~ was divided by
   float qbias[16];           // -bias * sum_k q_k * 2^-24: the score accumulators' start
   float svmax[kWaves];       // each wave's largest value scale
-  float acc[kWaves / 2][4 * (R / 16)][64];   // softmax states (final merge)
-  float m[kWaves / 2][64], l[kWaves / 2][64];
+  float acc[kWaves][4 * (R / 16)][64];   // every wave's softmax state (final merge)
+  float m[kWaves][64], l[kWaves][64];
 };
 
 template <int R>
@@ -465,78 +468,73 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
     }
   }
 
-  // merge the waves' states in LDS, halving the number of live states each
-  // round: waves [h, 2h) publish, waves [0, h) fold in the state of wave + h;
-  // a side that saw no token has m = -inf and weight 0
+  // merge: every wave publishes its state, then after one barrier every
+  // thread combines one (head, lane group, row block) slice of all of them
+  // (a side that saw no token has m = -inf and weight 0) and writes it
 #pragma unroll
-  for (int h = kWaves / 2; h >= 1; h /= 2) {
-    __syncthreads();
-    if (wave >= h && wave < 2 * h) {
-      const int w = wave - h;
+  for (int rb = 0; rb < R / 16; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < R / 16; ++rb)
+    for (int i = 0; i < 4; ++i) sm.acc[wave][4 * rb + i][lane] = st.acc[rb][i];
+  sm.m[wave][lane] = st.m;
+  sm.l[wave][lane] = st.l;
+  __syncthreads();
+  const int th = threadIdx.x;
+  const int cln = th % 16, ckb = (th / 16) % 4, crq = th / 64;   // head, lane group, first row block
+  float M = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.acc[w][4 * rb + i][lane] = st.acc[rb][i];
-      sm.m[w][lane] = st.m;
-      sm.l[w][lane] = st.l;
-    }
-    __syncthreads();
-    if (wave < h) {
-      const float mo = sm.m[wave][lane];
-      const float M = fmaxf(st.m, mo);
-      const float a = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
-      const float c = mo == -INFINITY ? 0.f : exp2f(mo - M);
-      st.m = M;
-      st.l = st.l * a + sm.l[wave][lane] * c;
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][cln]);
+  float aw[kWaves];
 #pragma unroll
-      for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st.acc[rb][i] = st.acc[rb][i] * a + sm.acc[wave][4 * rb + i][lane] * c;
-    }
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = sm.m[w][cln];
+    aw[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
   }
-  if (wave > 0) return;
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
   float uscale = vref * (0x1p24f / (kF * kV));         // the products' factors
-  if (p.hadamard) {
-    // rotated cache: u = u'' H_r / r; latent 16 rb + 4 kb + i of the lane's
-    // head: bits 0-1 in the vector, 2-3 in lane bits 4-5, the rest in rb
-#pragma unroll
-    for (int rb = 0; rb < R / 16; ++rb) {
-      floatx4& a = st.acc[rb];
-      const float x0 = a[0] + a[1], x1 = a[0] - a[1], x2 = a[2] + a[3], x3 = a[2] - a[3];
-      a = floatx4{x0 + x2, x1 + x3, x0 - x2, x1 - x3};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = bfly_lane(a[e], lane, 16);
-        a[e] = bfly_lane(a[e], lane, 32);
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < R / 16; m *= 2)
-#pragma unroll
-      for (int rb = 0; rb < R / 16; ++rb)
-        if (!(rb & m)) {
-          const floatx4 a = st.acc[rb], c = st.acc[rb + m];
-          st.acc[rb] = a + c;
-          st.acc[rb + m] = a - c;
-        }
-    uscale *= 1.f / R;                                   // exact: R = 2^k
-  }
-  if (ln >= nqs) return;
-  const int head = g * p.nq + hq0 + ln;
+  const int head = g * p.nq + hq0 + cln;
   const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
-  if (kb == 0) {
-    p.part_ml[slot * 2] = st.m;
+  if (th < 16 && cln < nqs) {
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      l += aw[w] * ((sm.l[w][cln] + sm.l[w][16 + cln]) + (sm.l[w][32 + cln] + sm.l[w][48 + cln]));
+    p.part_ml[slot * 2] = M;
     p.part_ml[slot * 2 + 1] = l;
   }
-  float* u = p.part_u + slot * R;
+  // latents 16 rb + 4 ckb + i of head cln
+  for (int rb = crq; rb < R / 16; rb += kWaves) {
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb) {
-    const floatx4 v = st.acc[rb] * uscale;
-    *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) = float4{v[0], v[1], v[2], v[3]};
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(aw[w], sm.acc[w][4 * rb + i][16 * ckb + cln], v[i]);
+    if (p.hadamard) {
+      *reinterpret_cast<float4*>(&sm.urot[cln][16 * rb + 4 * ckb]) = float4{v[0], v[1], v[2], v[3]};
+    } else if (cln < nqs) {
+      v *= uscale;
+      *reinterpret_cast<float4*>(p.part_u + slot * R + 16 * rb + 4 * ckb) =
+          float4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  if (!p.hadamard) return;
+  // rotated cache: u = u'' H_r / r, one wave per head, latents 4 lane .. +3:
+  // butterflies over the two index bits inside the lane, then over lane bits
+  __syncthreads();
+  uscale *= 1.f / R;                                     // exact: R = 2^k
+  constexpr int nq4 = R / 4;                             // lanes holding latents
+  for (int hd = wave; hd < nqs; hd += kWaves) {
+    float4 v = lane < nq4 ? *reinterpret_cast<const float4*>(&sm.urot[hd][4 * lane])
+                          : float4{0.f, 0.f, 0.f, 0.f};
+    const float a0 = v.x + v.y, a1 = v.x - v.y, a2 = v.z + v.w, a3 = v.z - v.w;
+    v = float4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+    for (int m = 1; m < nq4; m *= 2)
+      v = float4{bfly_lane(v.x, lane, m), bfly_lane(v.y, lane, m), bfly_lane(v.z, lane, m),
+                 bfly_lane(v.w, lane, m)};
+    if (lane < nq4) {
+      const size_t sl = (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0 + hd) * p.n_split + split;
+      *reinterpret_cast<float4*>(p.part_u + sl * R + 4 * lane) =
+          float4{v.x * uscale, v.y * uscale, v.z * uscale, v.w * uscale};
+    }
   }
 }
 
