@@ -171,39 +171,12 @@ struct Smem {
       char kt[kWaves][kKTileBytes<R>];
       char vt[kWaves][kVTileBytes<R>];
     } t;
-    struct {                                         // softmax states (final merge)
-      float acc[kWaves / 2][4 * (R / 16)][64];
-      float m[kWaves / 2][64], l[kWaves / 2][64];
+    struct {                                         // every wave's softmax state
+      float acc[kWaves][4 * (R / 16)][64];
+      float m[kWaves][64], l[kWaves][64];
     } x;
   } u;
 };
-
-// st <- st (+) the state another wave published in slot w; a side that saw no
-// token has m = -inf and weight 0
-template <int R>
-__device__ __forceinline__ void combine(State<R>& st, const Smem<R>& sm, int w, int lane) {
-  const float mo = sm.u.x.m[w][lane];
-  const float M = fmaxf(st.m, mo);
-  const float a = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
-  const float c = mo == -INFINITY ? 0.f : exp2f(mo - M);
-  st.m = M;
-  st.l = st.l * a + sm.u.x.l[w][lane] * c;
-#pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st.acc[rb][i] = st.acc[rb][i] * a + sm.u.x.acc[w][4 * rb + i][lane] * c;
-}
-
-template <int R>
-__device__ __forceinline__ void publish(const State<R>& st, Smem<R>& sm, int w, int lane) {
-#pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.u.x.acc[w][4 * rb + i][lane] = st.acc[rb][i];
-  sm.u.x.m[w][lane] = st.m;
-  sm.u.x.l[w][lane] = st.l;
-}
 
 template <int R, bool kShared>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(DecodeParams p) {
@@ -309,36 +282,55 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
     }
   }
 
-  // merge the waves' states in LDS (the value tiles' space, after a barrier),
-  // halving the number of live states each round: waves [h, 2h) publish,
-  // waves [0, h) fold in the state of wave + h. [slot][value][lane] keeps
-  // consecutive lanes on consecutive banks.
+  // merge: after a barrier (the tiles' space is reused) every wave publishes
+  // its state, then after one more every thread combines one (head, lane
+  // group, row block) slice of all of them (a side that saw no token has m =
+  // -inf and weight 0) and writes it. [slot][value][lane] keeps consecutive
+  // lanes on consecutive banks.
+  __syncthreads();
 #pragma unroll
-  for (int h = kWaves / 2; h >= 1; h /= 2) {
-    __syncthreads();
-    if (wave >= h && wave < 2 * h) publish<R>(st, sm, wave - h, lane);
-    __syncthreads();
-    if (wave < h) combine<R>(st, sm, wave, lane);
+  for (int rb = 0; rb < R / 16; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.u.x.acc[wave][4 * rb + i][lane] = st.acc[rb][i];
+  sm.u.x.m[wave][lane] = st.m;
+  sm.u.x.l[wave][lane] = st.l;
+  __syncthreads();
+  const int th = threadIdx.x;
+  const int cln = th % 16, ckb = (th / 16) % 4, crq = th / 64;   // head, lane group, first row block
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.x.m[w][cln]);
+  float aw[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = sm.u.x.m[w][cln];
+    aw[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
   }
-  if (wave > 0) return;
-  const float M = st.m;
-  float l = st.l;
-
-  // head totals: sum the four lane groups' shares
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (ln >= nqs) return;
-  const int head = g * p.nq + hq0 + ln;
+  if (cln >= nqs) return;
+  const int head = g * p.nq + hq0 + cln;
   const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
-  if (kb == 0) {
+  if (th < 16) {
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      l += aw[w] * ((sm.u.x.l[w][cln] + sm.u.x.l[w][16 + cln]) +
+                    (sm.u.x.l[w][32 + cln] + sm.u.x.l[w][48 + cln]));
     p.part_ml[slot * 2] = M;
     p.part_ml[slot * 2 + 1] = l;
   }
+  // latents 16 rb + 4 ckb + i of head cln
   float* u = p.part_u + slot * R;
+  for (int rb = crq; rb < R / 16; rb += kWaves) {
+    float4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb)
-    *reinterpret_cast<float4*>(u + 16 * rb + 4 * kb) =
-        float4{st.acc[rb][0], st.acc[rb][1], st.acc[rb][2], st.acc[rb][3]};
+    for (int w = 0; w < kWaves; ++w) {
+      v.x = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 0][16 * ckb + cln], v.x);
+      v.y = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 1][16 * ckb + cln], v.y);
+      v.z = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 2][16 * ckb + cln], v.z);
+      v.w = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 3][16 * ckb + cln], v.w);
+    }
+    *reinterpret_cast<float4*>(u + 16 * rb + 4 * ckb) = v;
+  }
 }
 
 }  // namespace
