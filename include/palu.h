@@ -96,6 +96,10 @@ typedef struct palu_attn_desc {
   int32_t hadamard;     /* palu_decode_attn_i8 / _i4 only (0 elsewhere): 1 if the
                            quantised cache holds Hadamard-rotated rows (see
                            palu_latent_append_i8) */
+  int32_t prepared;     /* 0: the decode call forms its query-side operands itself;
+                           1: palu_decode_attn_prepare has formed them in this
+                           workspace (same descriptor otherwise, same q and b_k)
+                           and the call only reads them */
 } palu_attn_desc;
 
 /* Bytes of device workspace palu_decode_attn needs for this descriptor
@@ -130,6 +134,20 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              const void* h_v, const void* b_k, const void* b_v,
                              const int32_t* seq_lens, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* The query-side operands of a decode call, formed ahead of it: the absorbed
+ * queries q~ = q B_k[g][:, cols(j)]^T (ABSORBED; the clarification of W1: with
+ * no rotary embedding B_k moves onto the query), the scaled queries
+ * (FULL_RANK), or B_k transposed for the matrix-core reconstruct kernel
+ * (RECONSTRUCT), written into the call's workspace. They depend on q and b_k
+ * only, not on the cache, so a caller can run this on another stream while
+ * palu_latent_append writes the step's token, then make the decode call with
+ * desc->prepared = 1 on the same workspace (after that stream's work).
+ *   q [B, Hq, d], b_k [G, r, D_g] dtype (b_k may be NULL in FULL_RANK mode);
+ *   workspace as for palu_decode_attn (this call writes its query area).
+ * Errors: as palu_decode_attn's descriptor checks, NULL, WORKSPACE, DEVICE. */
+palu_status palu_decode_attn_prepare(const palu_attn_desc* desc, const void* q, const void* b_k,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* The int8 latent cache (per-token quantisation of the latents combined with
  * the low-rank cache, Palu author response to reviewer Fsn9 on W1/W2; "Avg.

@@ -24,7 +24,8 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_decode_attn_i8", "decode_attention_i8", "palu_decode_attn_i4",
+           "palu_decode_attn_prepare", "palu_decode_attn_i8", "decode_attention_i8",
+           "palu_decode_attn_i4",
            "decode_attention_i4", "palu_latent_append_workspace",
            "palu_latent_append_i4_workspace", "palu_latent_append_i4", "latent_append_i4",
            "palu_latent_append_i8_workspace", "palu_latent_append_i8", "latent_append_i8", "palu_latent_append", "palu_profile_begin",
@@ -37,7 +38,7 @@ PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-                    "palu_decode_attn_i8", "palu_decode_attn_i4",
+                    "palu_decode_attn_prepare", "palu_decode_attn_i8", "palu_decode_attn_i4",
                     "palu_latent_append_workspace", "palu_latent_append",
                     "palu_latent_append_i8_workspace", "palu_latent_append_i8",
                     "palu_latent_append_i4_workspace", "palu_latent_append_i4",
@@ -64,7 +65,8 @@ class AttnDesc(ctypes.Structure):
                 ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
-                ("latent_out", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
+                ("latent_out", ctypes.c_int32), ("hadamard", ctypes.c_int32),
+                ("prepared", ctypes.c_int32)]
 
 
 class AppendDesc(ctypes.Structure):
@@ -93,6 +95,7 @@ def library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
+    lib.palu_decode_attn_prepare.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, sz, vp]
     for fn in ("palu_decode_attn_i8", "palu_decode_attn_i4"):
         getattr(lib, fn).argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp, sz, vp]
@@ -201,6 +204,26 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         None if b_k is None else b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
         None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
+
+
+def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> None:
+    """Form the decode call's query-side operands (q~, scaled q or B_k^T) in the
+    workspace ahead of a call made with desc.prepared = 1."""
+    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    G, r = desc.n_groups, desc.rank
+    dt = _TORCH_DTYPE.get(desc.dtype)
+    if dt is None:
+        raise TypeError(f"unknown dtype code {desc.dtype}")
+    _need(q, "q", (B, Hq, d), dt)
+    if desc.mode != PALU_MODE_FULL_RANK or b_k is not None:
+        _need(b_k, "b_k", (G, r, (Hkv // G) * d), dt)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().palu_decode_attn_prepare(
+        ctypes.byref(desc), q.data_ptr(), None if b_k is None else b_k.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn_prepare")
 
 
 def _decode_quant(bits: int, desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
@@ -350,7 +373,8 @@ def palu_profile_end() -> Tuple[float, int]:
 def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_groups: int,
               rank: int, max_ctx: int, dtype: int, mode: str = "reconstruct",
               rope_theta: float = 0.0, scale: float = 0.0, split_tokens: int = 0,
-              latent_out: bool = False, hadamard: bool = False) -> AttnDesc:
+              latent_out: bool = False, hadamard: bool = False,
+              prepared: bool = False) -> AttnDesc:
     modes = {"reconstruct": PALU_MODE_RECONSTRUCT, "absorbed": PALU_MODE_ABSORBED,
              "full_rank": PALU_MODE_FULL_RANK}
     if mode not in modes:
@@ -358,7 +382,8 @@ def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_g
     return AttnDesc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                     n_groups=n_groups, rank=rank, max_ctx=max_ctx, dtype=dtype, mode=modes[mode],
                     split_tokens=split_tokens, scale=scale, rope_theta=rope_theta,
-                    latent_out=1 if latent_out else 0, hadamard=1 if hadamard else 0)
+                    latent_out=1 if latent_out else 0, hadamard=1 if hadamard else 0,
+                    prepared=1 if prepared else 0)
 
 
 def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: int,

@@ -71,6 +71,8 @@ palu_status validate_attn(const palu_attn_desc* d) {
     return fail(PALU_ERR_UNSUPPORTED, "unknown mode %d", d->mode);
   if (!(d->rope_theta >= 0.0) || std::isinf(d->rope_theta))
     return fail(PALU_ERR_UNSUPPORTED, "rope_theta must be finite and >= 0");
+  if (d->prepared != 0 && d->prepared != 1)
+    return fail(PALU_ERR_UNSUPPORTED, "prepared must be 0 or 1 (got %d)", d->prepared);
   if (d->mode == PALU_MODE_ABSORBED && d->rope_theta != 0.0)
     return fail(PALU_ERR_UNSUPPORTED,
                 "ABSORBED mode needs rope_theta == 0: a rotated key cannot absorb B_k into q");
@@ -216,6 +218,42 @@ palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
 
 namespace {
 
+// the launch parameters every decode call (and its prepare step) shares:
+// shapes, plan, workspace areas, scale, rotary frequencies
+DecodeParams call_params(const palu_attn_desc* desc, const Plan& pl, const WorkspaceLayout& wl,
+                         void* workspace) {
+  const bool full = desc->mode == PALU_MODE_FULL_RANK;
+  DecodeParams p = shape_params(desc);
+  char* ws = static_cast<char*>(workspace);
+  p.qt = reinterpret_cast<float*>(ws + wl.qt);
+  p.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+  p.part_u = reinterpret_cast<float*>(ws + wl.u);
+  p.bkt = ws + wl.bkt;
+  p.n_split = pl.n_split; p.split_tokens = pl.split_tokens;
+  const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
+  p.scale_log2 = float(scale * 1.4426950408889634);
+  p.rope = desc->rope_theta > 0.0 ? 1 : 0;
+  p.full_rank = full ? 1 : 0;
+  p.latent_out = !full && desc->latent_out != 0 ? 1 : 0;
+  p.hadamard = desc->hadamard;
+  for (int i = 0; i < p.d / 2; ++i)
+    p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
+  return p;
+}
+
+// the query-side operands of a call: q~ = q B_k^T (ABSORBED), q * scale
+// (FULL_RANK), B_k^T (RECONSTRUCT on the MFMA kernel)
+palu_status prepare_launch(const palu_attn_desc* desc, const DecodeParams& p, const Plan& pl,
+                           hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (desc->mode == PALU_MODE_FULL_RANK) e = launch_prescale_q(p, desc->dtype, s);
+  else if (desc->mode == PALU_MODE_ABSORBED) e = launch_absorb_q(p, desc->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
+  if (pl.kernel == SplitKernel::kReconstructMfma) e = launch_transpose_bk(p, desc->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
+  return PALU_OK;
+}
+
 // both decode entry points; s_k, s_v non-NULL selects int8 latents
 palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, const void* h_v,
                    const float* s_k, const float* s_v, int qbits, const void* b_k,
@@ -233,34 +271,18 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   if (workspace_bytes < wl.total)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
 
-  DecodeParams p = shape_params(desc);
+  DecodeParams p = call_params(desc, pl, wl, workspace);
   p.q = q; p.h_k = h_k; p.h_v = h_v; p.b_k = b_k; p.b_v = b_v;
   p.lens = seq_lens; p.out = out;
-  char* ws = static_cast<char*>(workspace);
-  p.qt = reinterpret_cast<float*>(ws + wl.qt);
-  p.part_ml = reinterpret_cast<float*>(ws + wl.ml);
-  p.part_u = reinterpret_cast<float*>(ws + wl.u);
-  p.bkt = ws + wl.bkt;
-  p.n_split = pl.n_split; p.split_tokens = pl.split_tokens;
-  const double scale = desc->scale > 0.f ? double(desc->scale) : 1.0 / std::sqrt(double(p.d));
-  p.scale_log2 = float(scale * 1.4426950408889634);
-  p.rope = desc->rope_theta > 0.0 ? 1 : 0;
-  p.full_rank = full ? 1 : 0;
-  p.latent_out = latent ? 1 : 0;
   p.qbits = qbits;
-  p.hadamard = desc->hadamard;
   p.s_k = s_k; p.s_v = s_v;
-  for (int i = 0; i < p.d / 2; ++i)
-    p.omega_rev[i] = p.rope ? std::pow(desc->rope_theta, -2.0 * i / p.d) / (2.0 * M_PI) : 0.0;
-
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int absorbed = desc->mode != PALU_MODE_RECONSTRUCT;   // scores against q~
   hipError_t e = hipSuccess;
-  if (full) e = launch_prescale_q(p, desc->dtype, s);
-  else if (absorbed) e = launch_absorb_q(p, desc->dtype, s);
-  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
-  if (pl.kernel == SplitKernel::kReconstructMfma) e = launch_transpose_bk(p, desc->dtype, s);
-  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
+  if (!desc->prepared) {
+    const palu_status ps = prepare_launch(desc, p, pl, s);
+    if (ps != PALU_OK) return ps;
+  }
 
   const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
   if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
@@ -320,6 +342,23 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
     return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
   return decode(desc, q, h_k, h_v, nullptr, nullptr, 0, b_k, b_v, seq_lens, out, workspace,
                 workspace_bytes, stream);
+}
+
+palu_status palu_decode_attn_prepare(const palu_attn_desc* desc, const void* q, const void* b_k,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  const bool full = desc->mode == PALU_MODE_FULL_RANK;
+  if (!q || (!full && !b_k) || !workspace)
+    return fail(PALU_ERR_NULL, "q, workspace and (except in FULL_RANK mode) b_k must be non-NULL");
+  const Plan pl = make_plan(desc);
+  const WorkspaceLayout wl = layout(desc, pl);
+  if (workspace_bytes < wl.total)
+    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
+  DecodeParams p = call_params(desc, pl, wl, workspace);
+  p.q = q; p.b_k = b_k;
+  st = prepare_launch(desc, p, pl, static_cast<hipStream_t>(stream));
+  return st == PALU_OK ? ok() : st;
 }
 
 palu_status palu_decode_attn_i8(const palu_attn_desc* desc, const void* q, const int8_t* h_k,

@@ -93,6 +93,34 @@ def test_full_rank_mode_needs_no_factors(lib):
                                 fake, 16, None) == P.PALU_ERR_WORKSPACE
 
 
+def test_prepare_validation(lib):
+    """The prepare step checks the descriptor (prepared must be 0 or 1), its
+    pointers (b_k may be NULL only in FULL_RANK mode) and the workspace before
+    launching anything."""
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc(prepared=True)
+    d.prepared = 2
+    assert lib.palu_decode_attn_prepare(ctypes.byref(d), fake, fake, fake, 1 << 40,
+                                        None) == P.PALU_ERR_UNSUPPORTED
+    assert lib.palu_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake,
+                                fake, 1 << 40, None) == P.PALU_ERR_UNSUPPORTED
+    d.prepared = 1
+    for mode, kw in (("absorbed", {}), ("reconstruct", dict(rope_theta=5e5))):
+        d = _desc(mode=mode, **kw)
+        assert lib.palu_decode_attn_prepare(ctypes.byref(d), None, fake, fake, 1 << 40,
+                                            None) == P.PALU_ERR_NULL
+        assert lib.palu_decode_attn_prepare(ctypes.byref(d), fake, None, fake, 1 << 40,
+                                            None) == P.PALU_ERR_NULL
+        assert lib.palu_decode_attn_prepare(ctypes.byref(d), fake, fake, None, 1 << 40,
+                                            None) == P.PALU_ERR_NULL
+        need = P.palu_decode_attn_workspace(d)
+        assert lib.palu_decode_attn_prepare(ctypes.byref(d), fake, fake, fake, need - 1,
+                                            None) == P.PALU_ERR_WORKSPACE
+    d = _desc(mode="full_rank", n_groups=8, rank=128)
+    assert lib.palu_decode_attn_prepare(ctypes.byref(d), fake, None, fake, 16,
+                                        None) == P.PALU_ERR_WORKSPACE
+
+
 def _quant(lib, bits, d, *ptrs, nbytes=1 << 40):
     fake = ctypes.c_void_p(0x1000)
     q, hk, hv, sk, sv, bk, bv, out, ws = [fake if p is True else p for p in ptrs]
