@@ -24,7 +24,9 @@ SMALL = {
 }
 
 APPEND = {
-    "r256_g2": W.CONFIGS[3].scaled(batch=4, max_ctx=64, ragged=None),       # a row spans 2 blocks
+    "r256_g2": W.CONFIGS[3].scaled(batch=4, max_ctx=64, ragged=None),       # a row is a block
+    "r256_b9": W.CONFIGS[3].scaled(batch=9, max_ctx=32, ragged=None, seed=83),   # two rounds of rows
+    "r128_b12": W.CONFIGS[4].scaled(batch=12, max_ctx=32, ragged=None, seed=84),
     "r256_g8": W.CONFIGS[2].scaled(batch=3, max_ctx=32, ragged=None),
     "r128": W.CONFIGS[4].scaled(max_ctx=64, ragged=None),
     "r64": W.CONFIGS[3].scaled(n_groups=4, rank=64, batch=2, max_ctx=32, seed=81),

@@ -138,7 +138,9 @@ def test_int8_matches_bf16_path_on_exact_cache():
 # ------------------------------------------------------ quantised cache write ---
 
 APPEND = {
-    "r256_g2": W.CONFIGS[3].scaled(batch=4, max_ctx=64, ragged=None),       # a row spans 2 blocks
+    "r256_g2": W.CONFIGS[3].scaled(batch=4, max_ctx=64, ragged=None),       # a row is a block
+    "r256_b9": W.CONFIGS[3].scaled(batch=9, max_ctx=32, ragged=None, seed=83),   # two rounds of rows
+    "r128_b12": W.CONFIGS[4].scaled(batch=12, max_ctx=32, ragged=None, seed=84),
     "r256_g8": W.CONFIGS[2].scaled(batch=3, max_ctx=32, ragged=None),
     "r128": W.CONFIGS[4].scaled(max_ctx=64, ragged=None),                   # one block per row
     "r64": W.CONFIGS[3].scaled(n_groups=4, rank=64, batch=2, max_ctx=32, seed=81),  # 2 per block
