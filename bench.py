@@ -154,6 +154,17 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     e1.record(stream)
     torch.cuda.synchronize()
     decode_ms = e0.elapsed_time(e1)
+    # timed loop 1c: each decode call between its own events, for the spread
+    # (mean, median, p10, p90 of single calls)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i, (a, b_) in enumerate(ev):
+        hk, hv = caches[i % n_copies]
+        a.record(stream)
+        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    calls_us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in ev])
     # timed loop 2: the same steps with HIP events recorded by the library
     # around the main kernel on its launch stream (the roofline figure); the
     # event packets add a few microseconds between kernels, so this loop does
@@ -166,7 +177,7 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
         torch.cuda.synchronize()
         kern_ms, kern_n = P.palu_profile_end()
     return dict(ms_per_step=total_ms / args.steps, kernel_ms=kern_ms / max(1, kern_n),
-                decode_ms=decode_ms / args.steps,
+                decode_ms=decode_ms / args.steps, calls_us=calls_us,
                 kernel=kname, n_split=n_split, split_tokens=split_tokens,
                 out=first_out.cpu().numpy())
 
@@ -303,11 +314,15 @@ def roofline(cfg, t, mode, res, lat_bytes, kern_gbs, traffic):
     kus = res["kernel_ms"] * 1e3
     rec = {"bound": "hbm", "achieved": _r(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": _r(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": res["kernel"],
-           "kernel_us": _r(kus, 2), "algorithmic_bytes": lat_bytes}
+           "kernel_us": _r(kus, 2), "algorithmic_bytes": lat_bytes,
+           # the estimated times of the pages' roofline table: bytes at peak HBM
+           # bandwidth (and, rebuilding keys, FLOPs at the dense MFMA peak)
+           "ideal_us_hbm": _r(lat_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
     if mode == "reconstruct":
         tokens = int(np.sum(t["lens"], dtype=np.int64))
         flops = 2.0 * tokens * cfg.n_groups * cfg.rank * cfg.group_dim
         rec["algorithmic_flops"] = flops
+        rec["ideal_us_mfma"] = _r(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 2)
         if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > lat_bytes / (HBM_PEAK_GBS * 1e9):
             tf = flops / (kus * 1e-6) / 1e12
             rec.update({"bound": "mfma", "achieved": _r(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -619,6 +634,11 @@ def main():
         "quantised_latents": quant,
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                       "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
+                      "decode_call_us_spread": {
+                          "mean": round(float(np.mean(r["calls_us"])), 2),
+                          "median": round(float(np.median(r["calls_us"])), 2),
+                          "p10": round(float(np.percentile(r["calls_us"], 10)), 2),
+                          "p90": round(float(np.percentile(r["calls_us"], 90)), 2)},
                       "kernel_us": _r(r["kernel_ms"] * 1e3, 2), "kernel": r["kernel"],
                       "latent_GBps_kernel": _r(lat_bytes / (r["kernel_ms"] * 1e-3) / 1e9, 1),
                       "sampled_parity_max_abs": parity[m][0],
@@ -629,6 +649,7 @@ def main():
         line["granularity_sweep"] = granularity_sweep(torch, P, W, cfg, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(O, cfg, t, args.mode, args.cpu_seconds)
+        line["gpu_over_cpu_baseline"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 
