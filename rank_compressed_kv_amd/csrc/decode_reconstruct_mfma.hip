@@ -385,12 +385,17 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
   barrier_lds();
   keys_scores(0);
   barrier_lds();
+  // With eight waves, each SIMD runs waves w and w + 4: the upper four take
+  // the keys of tile it+1 before the softmax of tile it (the two touch
+  // different buffers), so one wave's key MFMAs overlap the other's softmax.
+  const bool keys_first = kWaves >= 8 && wave >= kWaves / 2;
   auto iteration = [&](int it, u32v& k, u32v& v) {
+    if (keys_first && it + 1 < ntiles) keys_scores(it + 1);
     softmax_values(it);
     put((it + 2) % kNBuf, k, v);
     fetch(s0 + (it + 4) * kTile, k, v);
     if (it + 2 < ntiles) rope_next(it + 2);
-    if (it + 1 < ntiles) keys_scores(it + 1);
+    if (!keys_first && it + 1 < ntiles) keys_scores(it + 1);
     barrier_lds();
   };
   for (int it = 0; it < ntiles; it += 2) {
