@@ -3,11 +3,14 @@
 A step is one pass of the hot path over the whole batch of one layer: the
 latent append of the new token (h = x A into row len-1 of both caches),
 then decode attention over the len rows (query absorption when applicable,
-the context-split kernel, the split merge with the B_v up-projection), all on
-one stream. With --overlap the query-side operands (absorbed queries, or B_k
-transposed for the rebuilt keys), which do not depend on the cache, are formed
-on a second stream beside the append (palu_decode_attn_prepare); measured, the
-per-step fork and join cost more than they hide, so it is not the default.
+the context-split kernel, the split merge with the B_v up-projection), on one
+stream. By default (--step combined) the step's work before the decode call
+is one palu_latent_append_prepare call: the cache write, with the query
+absorption as extra workgroups of the same launch (the query-side operands
+do not depend on the cache); --step apart makes the append call and then a
+decode call that forms its own operands; --step overlap forms them on a
+second stream beside the append (palu_decode_attn_prepare), whose per-step
+fork and join measured more than they hide.
 
 Default workload: Llama-3-8B-shaped GQA (B=8, Hq=32, Hkv=8, d=128, 2 groups of
 4 KV heads at rank 256, 32768 tokens of context, bf16 latents), absorbed-key
@@ -59,8 +62,10 @@ def parse():
                     help="skip the second timed loop with events around the main kernel")
     ap.add_argument("--no-full-rank", action="store_true",
                     help="skip the uncompressed baseline (full bf16 K and V)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="form the query-side operands on a second stream beside the cache write")
+    ap.add_argument("--step", default="combined", choices=["combined", "apart", "overlap"],
+                    help="combined: palu_latent_append_prepare then the decode call; apart: "
+                         "the append call, then a decode call forming its own operands; "
+                         "overlap: the operands on a second stream beside the append")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the int8- and int4-latent absorbed steps")
     ap.add_argument("--sweep", action="store_true",
@@ -80,18 +85,15 @@ def dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-OVERLAP = False   # set by --overlap
+STEP = "combined"   # set by --step
 
 
-def overlap_setup(torch, P, desc):
-    """The prepared copy of a descriptor and the second stream of a step whose
-    query-side operands (palu_decode_attn_prepare) run beside the cache write;
-    (None, None) without --overlap."""
-    if not OVERLAP:
-        return None, None
+def step_setup(torch, P, desc):
+    """The prepared copy of a descriptor (decode calls after the query-side
+    operands were formed) and, for --step overlap, the second stream."""
     pdesc = P.AttnDesc.from_buffer_copy(desc)
     pdesc.prepared = 1
-    return pdesc, torch.cuda.Stream()
+    return pdesc, (torch.cuda.Stream() if STEP == "overlap" else None)
 
 
 def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
@@ -114,17 +116,23 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
     n_split, split_tokens, kname = P.palu_decode_attn_plan(desc)
     stream = torch.cuda.current_stream()
-    pdesc, side = overlap_setup(torch, P, desc)
+    pdesc, side = step_setup(torch, P, desc)
+    bkp = None if mode == "full_rank" else bk
 
     def step(i):
         hk, hv = caches[i % n_copies]
-        if side is None:
+        if STEP == "apart":
             P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, aws, stream)
             P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
             return
+        if STEP == "combined":
+            P.palu_latent_append_prepare(adesc, 0, x, ak, av, hk, hv, None, None, pos, aws,
+                                         desc, q, bkp, ws, stream)
+            P.palu_decode_attn(pdesc, q, hk, hv, bk, bv, lens, out, ws, stream)
+            return
         # the query-side operands on a second stream, under the cache write
         side.wait_stream(stream)
-        P.palu_decode_attn_prepare(pdesc, q, None if mode == "full_rank" else bk, ws, side)
+        P.palu_decode_attn_prepare(pdesc, q, bkp, ws, side)
         P.palu_latent_append(adesc, x, ak, av, hk, hv, pos, aws, stream)
         stream.wait_stream(side)
         P.palu_decode_attn(pdesc, q, hk, hv, bk, bv, lens, out, ws, stream)
@@ -213,7 +221,7 @@ def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
     aws = torch.zeros(append_ws(adesc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    pdesc, side = overlap_setup(torch, P, desc)
+    pdesc, side = step_setup(torch, P, desc)
 
     def decode(i):
         hk, hv, sk, sv = caches[i % n_copies]
@@ -221,9 +229,14 @@ def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
 
     def step(i):
         hk, hv, sk, sv = caches[i % n_copies]
-        if side is None:
+        if STEP == "apart":
             append_fn(adesc, x, ak, av, hk, hv, sk, sv, pos, aws, stream)
             decode(i)
+            return
+        if STEP == "combined":
+            P.palu_latent_append_prepare(adesc, bits, x, ak, av, hk, hv, sk, sv, pos, aws, desc,
+                                         q, bk, ws, stream)
+            decode_fn(pdesc, q, hk, hv, sk, sv, bk, bv, lens, out, ws, stream)
             return
         side.wait_stream(stream)
         P.palu_decode_attn_prepare(pdesc, q, bk, ws, side)
@@ -488,9 +501,9 @@ def load_traffic(kernel: str, args_suffix: str = ""):
 
 
 def main():
-    global OVERLAP
+    global STEP
     args = parse()
-    OVERLAP = args.overlap
+    STEP = args.step
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the library has no multi-GPU path); "
               f"got --gpus {args.gpus}", file=sys.stderr)
@@ -622,9 +635,12 @@ def main():
                                f"Hkv={cfg.n_kv_heads} d={cfg.head_dim} G={cfg.n_groups} "
                                f"r={cfg.rank} ctx={cfg.max_ctx}",
                    "global_batch": cfg.batch, "seq_len": cfg.max_ctx, "parallelism": "none (1 GPU)",
-                   "step": ("cache write, with the query-side operands formed on a second "
-                            "stream beside it, then the decode call" if OVERLAP
-                            else "cache write, then the decode call (one stream)"),
+                   "step": {"combined": "cache write with the query-side operands in the "
+                                        "same call (palu_latent_append_prepare), then the "
+                                        "decode call",
+                            "apart": "cache write, then the decode call (one stream)",
+                            "overlap": "cache write, with the query-side operands formed on a "
+                                       "second stream beside it, then the decode call"}[STEP],
                    "mode": args.mode, "n_split": main_res["n_split"],
                    "split_tokens": main_res["split_tokens"]},
         "latent_GBps": round(gbs_step, 1),

@@ -283,6 +283,32 @@ palu_status palu_latent_append_i4(const palu_append_desc* desc, const void* x, c
                                   float* s_v, const int32_t* pos, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* One decode step's work ahead of its decode call, in as few launches as it
+ * allows: the cache write that qbits selects (0: palu_latent_append, 8:
+ * palu_latent_append_i8, 4: palu_latent_append_i4) and
+ * palu_decode_attn_prepare for `attn`; the decode call then follows on the
+ * same stream with attn->prepared = 1 and the same workspace. The two parts
+ * are independent (the query-side operands read q and b_k, never the cache).
+ * When attn is ABSORBED with the append's dtype and head_dim / 8 is a power
+ * of two <= 32, the query absorption (the clarification of W1: B_k moves onto
+ * the query) runs as extra workgroups of the append's launch, beside the
+ * cache write, in one launch; otherwise the two are launched one after the
+ * other on `stream`. Either way the results are those of the two calls.
+ *   ad, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, append_ws, append_ws_bytes: as
+ *     for the append call qbits selects (s_k, s_v unused and may be NULL for
+ *     qbits 0; h_k, h_v are int8_t* / uint8_t* codes for qbits 8 / 4);
+ *   attn, q, b_k, workspace, workspace_bytes: as for palu_decode_attn_prepare
+ *     (attn->prepared is not read).
+ * Errors: those of the two calls, checked before anything is launched;
+ * UNSUPPORTED for qbits other than 0, 8 and 4. */
+palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits, const void* x,
+                                       const void* a_k, const void* a_v, void* h_k, void* h_v,
+                                       float* s_k, float* s_v, const int32_t* pos,
+                                       void* append_ws, size_t append_ws_bytes,
+                                       const palu_attn_desc* attn, const void* q,
+                                       const void* b_k, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Optional timing of the main decode kernel (the context-split kernel) with HIP
  * events on the stream it is launched on. palu_profile_begin(n) arms n records
  * (events are created here, once); each later palu_decode_attn call records one

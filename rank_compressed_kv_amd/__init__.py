@@ -24,7 +24,8 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
-           "palu_decode_attn_prepare", "palu_decode_attn_i8", "decode_attention_i8",
+           "palu_decode_attn_prepare", "palu_latent_append_prepare", "palu_decode_attn_i8",
+           "decode_attention_i8",
            "palu_decode_attn_i4",
            "decode_attention_i4", "palu_latent_append_workspace",
            "palu_latent_append_i4_workspace", "palu_latent_append_i4", "latent_append_i4",
@@ -42,7 +43,7 @@ EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu
                     "palu_latent_append_workspace", "palu_latent_append",
                     "palu_latent_append_i8_workspace", "palu_latent_append_i8",
                     "palu_latent_append_i4_workspace", "palu_latent_append_i4",
-                    "palu_profile_begin", "palu_profile_end",
+                    "palu_latent_append_prepare", "palu_profile_begin", "palu_profile_end",
                     "palu_status_string", "palu_last_error")
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +108,9 @@ def library() -> ctypes.CDLL:
             ctypes.POINTER(AppendDesc), ctypes.POINTER(sz)]
         getattr(lib, f"palu_latent_append_{b}").argtypes = [
             ctypes.POINTER(AppendDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.palu_latent_append_prepare.argtypes = [
+        ctypes.POINTER(AppendDesc), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+        ctypes.POINTER(AttnDesc), vp, vp, vp, sz, vp]
     lib.palu_profile_begin.argtypes = [ctypes.c_int32]
     lib.palu_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), i32p]
     for fn in EXPORTED_SYMBOLS:
@@ -206,9 +210,8 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
 
 
-def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> None:
-    """Form the decode call's query-side operands (q~, scaled q or B_k^T) in the
-    workspace ahead of a call made with desc.prepared = 1."""
+def _prepare_checks(desc: AttnDesc, q, b_k, workspace) -> int:
+    """Shapes and dtypes of a prepare step's tensors; the workspace's bytes."""
     palu_decode_attn_plan(desc)          # the library validates the descriptor first
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r = desc.n_groups, desc.rank
@@ -220,7 +223,13 @@ def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> 
         _need(b_k, "b_k", (G, r, (Hkv // G) * d), dt)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    return workspace.numel() * workspace.element_size()
+
+
+def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> None:
+    """Form the decode call's query-side operands (q~, scaled q or B_k^T) in the
+    workspace ahead of a call made with desc.prepared = 1."""
+    nbytes = _prepare_checks(desc, q, b_k, workspace)
     _check(library().palu_decode_attn_prepare(
         ctypes.byref(desc), q.data_ptr(), None if b_k is None else b_k.data_ptr(),
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn_prepare")
@@ -283,24 +292,29 @@ def palu_latent_append_workspace(desc: AppendDesc) -> int:
 
 def palu_latent_append(desc: AppendDesc, x, a_k, a_v, h_k, h_v, pos, workspace,
                        stream=None) -> None:
-    palu_latent_append_workspace(desc)   # the library validates the descriptor first
-    B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
-    dt = _TORCH_DTYPE.get(desc.dtype)
-    if dt is None:
-        raise TypeError(f"unknown dtype code {desc.dtype}")
-    _need(x, "x", (B, dm), dt)
-    _need(a_k, "a_k", (dm, G * r), dt)
-    _need(a_v, "a_v", (dm, G * r), dt)
-    _need(h_k, "h_k", (B, G, L, r), dt)
-    _need(h_v, "h_v", (B, G, L, r), dt)
-    _need(pos, "pos", (B,), torch.int32)
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _append_checks(0, desc, x, a_k, a_v, h_k, h_v, None, None, pos, workspace)
     _check(library().palu_latent_append(
         ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),
         h_v.data_ptr(), pos.data_ptr(), workspace.data_ptr(), nbytes, _stream(stream)),
         "palu_latent_append")
+
+
+def palu_latent_append_prepare(adesc: AppendDesc, qbits: int, x, a_k, a_v, h_k, h_v, s_k, s_v,
+                               pos, append_ws, desc: AttnDesc, q, b_k, workspace,
+                               stream=None) -> None:
+    """The cache write qbits selects (0, 8, 4) and the decode call's query-side
+    operands in one call (one launch when the absorption can ride in the
+    append's); the decode call follows with desc.prepared = 1."""
+    if qbits not in (0, 8, 4):
+        raise ValueError(f"qbits must be 0, 8 or 4 (got {qbits})")
+    abytes = _append_checks(qbits, adesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, append_ws)
+    nbytes = _prepare_checks(desc, q, b_k, workspace)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(library().palu_latent_append_prepare(
+        ctypes.byref(adesc), qbits, x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(),
+        h_k.data_ptr(), h_v.data_ptr(), ptr(s_k), ptr(s_v), pos.data_ptr(),
+        append_ws.data_ptr(), abytes, ctypes.byref(desc), q.data_ptr(), ptr(b_k),
+        workspace.data_ptr(), nbytes, _stream(stream)), "palu_latent_append_prepare")
 
 
 def palu_latent_append_i8_workspace(desc: AppendDesc) -> int:
@@ -317,27 +331,39 @@ def palu_latent_append_i4_workspace(desc: AppendDesc) -> int:
     return int(n.value)
 
 
-def _append_quant(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
-                  workspace, stream) -> None:
+def _append_checks(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
+                   workspace) -> int:
+    """Shapes and dtypes of an append's tensors (bits 0: dtype cache, 8 / 4:
+    int8 / int4 codes with scales); the workspace's bytes."""
     # the library validates the descriptor first
-    (palu_latent_append_i8_workspace if bits == 8 else palu_latent_append_i4_workspace)(desc)
+    {0: palu_latent_append_workspace, 8: palu_latent_append_i8_workspace,
+     4: palu_latent_append_i4_workspace}[bits](desc)
     B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
     dt = _TORCH_DTYPE.get(desc.dtype)
     if dt is None:
         raise TypeError(f"unknown dtype code {desc.dtype}")
-    cache = (B, G, L, r) if bits == 8 else (B, G, L, r // 2)
-    ctype = torch.int8 if bits == 8 else torch.uint8
     _need(x, "x", (B, dm), dt)
     _need(a_k, "a_k", (dm, G * r), dt)
     _need(a_v, "a_v", (dm, G * r), dt)
-    _need(h_k, "h_k", cache, ctype)
-    _need(h_v, "h_v", cache, ctype)
-    _need(s_k, "s_k", (B, G, L), torch.float32)
-    _need(s_v, "s_v", (B, G, L), torch.float32)
+    if bits == 0:
+        _need(h_k, "h_k", (B, G, L, r), dt)
+        _need(h_v, "h_v", (B, G, L, r), dt)
+    else:
+        cache = (B, G, L, r) if bits == 8 else (B, G, L, r // 2)
+        ctype = torch.int8 if bits == 8 else torch.uint8
+        _need(h_k, "h_k", cache, ctype)
+        _need(h_v, "h_v", cache, ctype)
+        _need(s_k, "s_k", (B, G, L), torch.float32)
+        _need(s_v, "s_v", (B, G, L), torch.float32)
     _need(pos, "pos", (B,), torch.int32)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    return workspace.numel() * workspace.element_size()
+
+
+def _append_quant(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
+                  workspace, stream) -> None:
+    nbytes = _append_checks(bits, desc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace)
     name = f"palu_latent_append_i{bits}"
     _check(getattr(library(), name)(
         ctypes.byref(desc), x.data_ptr(), a_k.data_ptr(), a_v.data_ptr(), h_k.data_ptr(),

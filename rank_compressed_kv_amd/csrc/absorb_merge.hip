@@ -16,6 +16,7 @@
 //   values are never rebuilt, B_v acts after the weighted sum).
 #include <math.h>
 
+#include "absorb_device.h"
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -25,7 +26,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWarps = kThreads / 64;
 constexpr int kAbsRows = 64;        // rows of r per absorb workgroup (general form)
-constexpr int kHeadChunk = 8;       // query heads absorbed per pass
 
 // General form (any even d <= 256): thread = (row, quarter of d).
 template <typename T, bool kVec8>
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
   const int k = blockIdx.z * kAbsRows + kq;
   const int dq = (p.d + 3) / 4;                        // columns per quarter
   const int c0 = qtr * dq, c1 = min(p.d, c0 + dq);
-  __shared__ float qs[kHeadChunk][2 * kMaxHalfDim];
+  __shared__ float qs[kAbsHeadChunk][2 * kMaxHalfDim];
   const T* row = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg +
                  static_cast<size_t>(min(k, p.r - 1)) * p.Dg + jl * p.d;
   // the quarter-row of B_k: at most 64 columns, loaded at once
@@ -53,20 +53,20 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 64; ++e) v[e] = c0 + e < c1 ? load_f32(row, c0 + e) : 0.f;
   }
-  for (int h0 = 0; h0 < p.gqa; h0 += kHeadChunk) {
-    const int nh = min(kHeadChunk, p.gqa - h0);
+  for (int h0 = 0; h0 < p.gqa; h0 += kAbsHeadChunk) {
+    const int nh = min(kAbsHeadChunk, p.gqa - h0);
     const int head0 = j * p.gqa + h0;
     __syncthreads();
-    for (int e = tid; e < kHeadChunk * p.d; e += kThreads) {
+    for (int e = tid; e < kAbsHeadChunk * p.d; e += kThreads) {
       const int hh = e / p.d, c = e % p.d;
       qs[hh][c] = hh < nh ? load_f32(static_cast<const T*>(p.q),
                                      (static_cast<size_t>(b) * p.Hq + head0 + hh) * p.d + c)
                           : 0.f;
     }
     __syncthreads();
-    float acc[kHeadChunk];
+    float acc[kAbsHeadChunk];
 #pragma unroll
-    for (int hh = 0; hh < kHeadChunk; ++hh) {
+    for (int hh = 0; hh < kAbsHeadChunk; ++hh) {
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < 64; ++e)
@@ -81,43 +81,12 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
   }
 }
 
-// Fast form when d/8 is a power of two <= 32: thread = (row k, 8-column
-// chunk); one 16-byte load of B_k per thread, the chunks of a row are added
-// with lane shuffles. Workgroup (KV head, sequence, 256*8/d rows of r).
+// Fast form when d/8 is a power of two <= 32 (absorb_rows): workgroup (KV
+// head, sequence, 256*8/d rows of r).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void absorb_q_vec_kernel(DecodeParams p) {
-  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int g = j / p.s, jl = j % p.s;
-  const int ncc = p.d / 8, rows = kThreads / ncc;
-  const int cc = tid % ncc, kr = tid / ncc;
-  const int k = blockIdx.z * rows + kr;
-  const T* row = static_cast<const T*>(p.b_k) + static_cast<size_t>(g) * p.r * p.Dg +
-                 static_cast<size_t>(min(k, p.r - 1)) * p.Dg + jl * p.d;
-  float v[8];
-  load8_f32(row + 8 * cc, v);
-  __shared__ float qs[kHeadChunk][2 * kMaxHalfDim];
-  for (int h0 = 0; h0 < p.gqa; h0 += kHeadChunk) {
-    const int nh = min(kHeadChunk, p.gqa - h0);
-    const int head0 = j * p.gqa + h0;
-    __syncthreads();
-    for (int e = tid; e < nh * p.d; e += kThreads) {
-      const int hh = e / p.d, c = e % p.d;
-      qs[hh][c] = load_f32(static_cast<const T*>(p.q),
-                           (static_cast<size_t>(b) * p.Hq + head0 + hh) * p.d + c);
-    }
-    __syncthreads();
-    for (int hh = 0; hh < nh; ++hh) {
-      const float4 q0 = *reinterpret_cast<const float4*>(&qs[hh][8 * cc]);
-      const float4 q1 = *reinterpret_cast<const float4*>(&qs[hh][8 * cc + 4]);
-      float a = q0.x * v[0];
-      a = fmaf(q0.y, v[1], a); a = fmaf(q0.z, v[2], a); a = fmaf(q0.w, v[3], a);
-      a = fmaf(q1.x, v[4], a); a = fmaf(q1.y, v[5], a); a = fmaf(q1.z, v[6], a);
-      a = fmaf(q1.w, v[7], a);
-      for (int off = 1; off < ncc; off <<= 1) a += __shfl_xor(a, off);
-      if (cc == 0 && k < p.r)
-        p.qt[(static_cast<size_t>(b) * p.Hq + head0 + hh) * p.r + k] = a * p.scale_log2;
-    }
-  }
+  __shared__ float qs[kAbsHeadChunk][2 * kMaxHalfDim];
+  absorb_rows<T, kThreads>(absorb_args(p), blockIdx.x, blockIdx.y, blockIdx.z, qs);
 }
 
 // q~ = q (the uncompressed baseline: keys are the cached rows themselves),
@@ -434,9 +403,8 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
-  const int ncc = p.d / 8;
-  if (p.d % 8 == 0 && ncc <= 32 && (ncc & (ncc - 1)) == 0) {
-    const int rows = kThreads / ncc;
+  if (absorb_carriable(absorb_args(p))) {
+    const int rows = kThreads / (p.d / 8);
     const dim3 grid(p.Hkv, p.B, (p.r + rows - 1) / rows);
     if (dtype == 0) absorb_q_vec_kernel<float><<<grid, kThreads, 0, st>>>(p);
     else absorb_q_vec_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);

@@ -409,10 +409,25 @@ palu_status validate_append_quant(const palu_append_desc* d, int bits) {
   return PALU_OK;
 }
 
-// every append entry point; qbits 8 / 4: int8 / int4 cache with scales, 0: dtype
-palu_status append(const palu_append_desc* d, int qbits, const void* x, const void* a_k,
-                   const void* a_v, void* h_k, void* h_v, float* s_k, float* s_v,
-                   const int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {
+// the checks of the append entry point qbits selects (0: dtype cache, 8 / 4:
+// int8 / int4 cache with scales)
+palu_status validate_append_call(const palu_append_desc* d, int qbits, const float* s_k,
+                                 const float* s_v) {
+  if (qbits != 0 && qbits != 8 && qbits != 4)
+    return fail(PALU_ERR_UNSUPPORTED, "qbits must be 0, 8 or 4 (got %d)", qbits);
+  palu_status st = qbits ? validate_append_quant(d, qbits) : validate_append(d);
+  if (st != PALU_OK) return st;
+  if (!qbits && d->hadamard)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
+  if (qbits && (!s_k || !s_v)) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
+  return PALU_OK;
+}
+
+// the launch parameters of an append (pointers and workspace checked)
+palu_status append_params(const palu_append_desc* d, int qbits, const void* x, const void* a_k,
+                          const void* a_v, void* h_k, void* h_v, float* s_k, float* s_v,
+                          const int32_t* pos, void* workspace, size_t workspace_bytes,
+                          AppendParams& p) {
   const bool quant = qbits != 0;
   if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
     return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
@@ -423,13 +438,24 @@ palu_status append(const palu_append_desc* d, int qbits, const void* x, const vo
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(PALU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  AppendParams p{};
+  p = AppendParams{};
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
   p.B = d->batch; p.dm = d->d_model; p.G = d->n_groups; p.r = d->rank; p.L = d->max_ctx;
   p.quant = qbits;
   p.hadamard = d->hadamard;
   p.s_k = s_k; p.s_v = s_v;
   append_bind_workspace(p, workspace);
+  return PALU_OK;
+}
+
+// every append entry point (descriptor already validated)
+palu_status append(const palu_append_desc* d, int qbits, const void* x, const void* a_k,
+                   const void* a_v, void* h_k, void* h_v, float* s_k, float* s_v,
+                   const int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {
+  AppendParams p;
+  const palu_status st = append_params(d, qbits, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
+                                       workspace, workspace_bytes, p);
+  if (st != PALU_OK) return st;
   hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   return ok();
@@ -449,10 +475,8 @@ palu_status palu_latent_append_workspace(const palu_append_desc* d, size_t* byte
 palu_status palu_latent_append(const palu_append_desc* d, const void* x, const void* a_k,
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  palu_status st = validate_append(d);
+  palu_status st = validate_append_call(d, 0, nullptr, nullptr);
   if (st != PALU_OK) return st;
-  if (d->hadamard)
-    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
   return append(d, 0, x, a_k, a_v, h_k, h_v, nullptr, nullptr, pos, workspace, workspace_bytes,
                 stream);
 }
@@ -469,9 +493,8 @@ palu_status palu_latent_append_i8(const palu_append_desc* d, const void* x, cons
                                   const void* a_v, int8_t* h_k, int8_t* h_v, float* s_k,
                                   float* s_v, const int32_t* pos, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  palu_status st = validate_append_quant(d, 8);
+  palu_status st = validate_append_call(d, 8, s_k, s_v);
   if (st != PALU_OK) return st;
-  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
   return append(d, 8, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
 }
 
@@ -487,10 +510,53 @@ palu_status palu_latent_append_i4(const palu_append_desc* d, const void* x, cons
                                   const void* a_v, uint8_t* h_k, uint8_t* h_v, float* s_k,
                                   float* s_v, const int32_t* pos, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  palu_status st = validate_append_quant(d, 4);
+  palu_status st = validate_append_call(d, 4, s_k, s_v);
   if (st != PALU_OK) return st;
-  if (!s_k || !s_v) return fail(PALU_ERR_NULL, "s_k and s_v must be non-NULL");
   return append(d, 4, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, workspace, workspace_bytes, stream);
+}
+
+palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits, const void* x,
+                                       const void* a_k, const void* a_v, void* h_k, void* h_v,
+                                       float* s_k, float* s_v, const int32_t* pos,
+                                       void* append_ws, size_t append_ws_bytes,
+                                       const palu_attn_desc* attn, const void* q,
+                                       const void* b_k, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  // every check of both calls before anything is launched
+  palu_status st = validate_append_call(ad, qbits, s_k, s_v);
+  if (st != PALU_OK) return st;
+  AppendParams ap;
+  st = append_params(ad, qbits, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, append_ws,
+                     append_ws_bytes, ap);
+  if (st != PALU_OK) return st;
+  st = validate_attn(attn);
+  if (st != PALU_OK) return st;
+  const bool full = attn->mode == PALU_MODE_FULL_RANK;
+  if (!q || (!full && !b_k) || !workspace)
+    return fail(PALU_ERR_NULL, "q, workspace and (except in FULL_RANK mode) b_k must be non-NULL");
+  const Plan pl = make_plan(attn);
+  const WorkspaceLayout wl = layout(attn, pl);
+  if (workspace_bytes < wl.total)
+    return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wl.total);
+  DecodeParams dp = call_params(attn, pl, wl, workspace);
+  dp.q = q; dp.b_k = b_k;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AbsorbArgs ab = absorb_args(dp);
+  if (attn->mode == PALU_MODE_ABSORBED && attn->dtype == ad->dtype && absorb_carriable(ab)) {
+    // the absorption rides in the append's launch: one workgroup per (KV
+    // head, sequence, slice of r rows)
+    ap.ab = ab;
+    const int rows = append_threads(qbits) / (ab.d / 8);
+    ap.ab.units = ab.Hkv * ab.B * ((ab.r + rows - 1) / rows);
+    const hipError_t e = launch_append(ap, ad->dtype, s);
+    if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  const hipError_t e = launch_append(ap, ad->dtype, s);
+  if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  st = prepare_launch(attn, dp, pl, s);
+  return st == PALU_OK ? ok() : st;
 }
 
 palu_status palu_profile_begin(int32_t max_records) {

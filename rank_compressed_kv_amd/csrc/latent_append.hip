@@ -27,6 +27,7 @@
 // With the Hadamard option (a quantisation-friendly enhancement the author
 // responses name, answer to Q2) each fp32 row is first rotated by Sylvester's
 // H_r, h'' = h H_r, which spreads an outlier latent over all r codes.
+#include "absorb_device.h"
 #include "device_util.h"
 #include "palu_internal.h"
 
@@ -202,18 +203,35 @@ __device__ void quantize_row(const AppendParams& p, float4 v0, int j, int b, int
   if (lane == 0) sc[row] = scale;
 }
 
-template <typename T, bool kQuant>
+// kFuse: the launch also carries the query absorption of the decode call that
+// follows, as workgroups past the last row slice (one absorb_rows unit each,
+// staged in this kernel's reduction buffer, which they do not otherwise use);
+// they share no data with the append's workgroups.
+template <typename T, bool kQuant, bool kFuse>
 __global__ __launch_bounds__(Tiling<kQuant>::kThreads) void append_kernel(AppendParams p) {
   using Tl = Tiling<kQuant>;
   constexpr int kThreads = Tl::kThreads, kCols = Tl::kCols, kChunks = Tl::kChunks;
   constexpr int kRowGroups = Tl::kRowGroups, kRowsPerThread = Tl::kRowsPerThread;
   constexpr int kBatchChunk = Tl::kBatchChunk, kXPer = Tl::kXPer, kReaders = Tl::kReaders;
+  __shared__ float4 red[kRowGroups][kBatchChunk][2 * kChunks];
+  if constexpr (kFuse) {
+    static_assert(sizeof(red) >= kAbsHeadChunk * 2 * kMaxHalfDim * sizeof(float),
+                  "the reduction buffer holds the absorption's query rows");
+    if (static_cast<int>(blockIdx.y) >= p.nslices) {
+      const int u = (blockIdx.y - p.nslices) * gridDim.x + blockIdx.x;
+      if (u >= p.ab.units) return;
+      absorb_rows<T, kThreads>(p.ab, u % p.ab.Hkv, (u / p.ab.Hkv) % p.ab.B,
+                               u / (p.ab.Hkv * p.ab.B),
+                               reinterpret_cast<float (*)[2 * kMaxHalfDim]>(&red[0][0][0]));
+      return;
+    }
+  }
   const int width = p.G * p.r;                 // columns of one matrix
   const int tid = threadIdx.x;
   const int cc = tid % kChunks, rg = tid / kChunks;    // 8-column chunk, row group
   const int cb0 = blockIdx.x * kCols;
   const int col0 = cb0 + 8 * cc;               // in [0, 2*width)
-  const int slice = blockIdx.y, nslices = gridDim.y;
+  const int slice = blockIdx.y, nslices = p.nslices;
   const int i0 = slice * kRows;
   const int rows = min(kRows, p.dm - i0);
   const bool active = col0 < 2 * width;
@@ -248,7 +266,6 @@ __global__ __launch_bounds__(Tiling<kQuant>::kThreads) void append_kernel(Append
   };
   load_x(0);
   __shared__ float xs[kBatchChunk][kRows];
-  __shared__ float4 red[kRowGroups][kBatchChunk][2 * kChunks];
   __shared__ int is_last;
   const int fb = tid / (2 * kChunks), fq = tid % (2 * kChunks);   // reader: sequence, slot
   const int fcol = cb0 + Tl::col_of_slot(fq);
@@ -377,6 +394,7 @@ size_t append_workspace_bytes(int B, int dm, int G, int r) {
 }
 
 void append_bind_workspace(AppendParams& p, void* workspace) {
+  p.nslices = (p.dm + kRows - 1) / kRows;
   char* w = static_cast<char*>(workspace);
   p.counters = reinterpret_cast<int32_t*>(w);
   p.part = reinterpret_cast<float*>(w + counter_bytes(p.G, p.r));
@@ -384,19 +402,33 @@ void append_bind_workspace(AppendParams& p, void* workspace) {
 
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
   const int cols = 2 * p.G * p.r;
-  const int rows = (p.dm + kRows - 1) / kRows;
+  const bool fuse = p.ab.units > 0;
   if (p.quant) {
     using Tl = Tiling<true>;
-    const dim3 grid((cols + Tl::kCols - 1) / Tl::kCols, rows);
-    if (dtype == 0) append_kernel<float, true><<<grid, Tl::kThreads, 0, st>>>(p);
-    else append_kernel<uint16_t, true><<<grid, Tl::kThreads, 0, st>>>(p);
+    const int bx = (cols + Tl::kCols - 1) / Tl::kCols;
+    const dim3 grid(bx, p.nslices + (fuse ? (p.ab.units + bx - 1) / bx : 0));
+    if (dtype == 0) {
+      if (fuse) append_kernel<float, true, true><<<grid, Tl::kThreads, 0, st>>>(p);
+      else append_kernel<float, true, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    } else {
+      if (fuse) append_kernel<uint16_t, true, true><<<grid, Tl::kThreads, 0, st>>>(p);
+      else append_kernel<uint16_t, true, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    }
   } else {
     using Tl = Tiling<false>;
-    const dim3 grid((cols + Tl::kCols - 1) / Tl::kCols, rows);
-    if (dtype == 0) append_kernel<float, false><<<grid, Tl::kThreads, 0, st>>>(p);
-    else append_kernel<uint16_t, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    const int bx = (cols + Tl::kCols - 1) / Tl::kCols;
+    const dim3 grid(bx, p.nslices + (fuse ? (p.ab.units + bx - 1) / bx : 0));
+    if (dtype == 0) {
+      if (fuse) append_kernel<float, false, true><<<grid, Tl::kThreads, 0, st>>>(p);
+      else append_kernel<float, false, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    } else {
+      if (fuse) append_kernel<uint16_t, false, true><<<grid, Tl::kThreads, 0, st>>>(p);
+      else append_kernel<uint16_t, false, false><<<grid, Tl::kThreads, 0, st>>>(p);
+    }
   }
   return hipGetLastError();
 }
+
+int append_threads(int quant) { return quant ? Tiling<true>::kThreads : Tiling<false>::kThreads; }
 
 }  // namespace palu

@@ -40,6 +40,19 @@ struct DecodeParams {
   double omega_rev[kMaxHalfDim];
 };
 
+// The query absorption's operands (absorbed-key mode): q~[b, j*gqa + h, k] =
+// scale_log2 * q[b, j*gqa + h] . B_k[g][k, jl*d .. jl*d + d) for KV head
+// j = g*s + jl. Shared by its own launch and the append launch that can
+// carry it as extra workgroups.
+struct AbsorbArgs {
+  const void* q;      // [B, Hq, d]
+  const void* b_k;    // [G, r, Dg]
+  float* qt;          // [B, Hq, r] fp32
+  int32_t B, Hq, Hkv, s, gqa, d, Dg, r;
+  float scale_log2;
+  int32_t units;      // workgroups of the carried form: Hkv * B * slices of r (0: none)
+};
+
 struct AppendParams {
   const void* x;      // [B, dm]
   const void* a_k;    // [dm, G*r]
@@ -55,6 +68,8 @@ struct AppendParams {
   int32_t hadamard;   // 1: rows rotated by the Hadamard matrix before quantising
   float* s_k;         // [B, G, L]
   float* s_v;
+  int32_t nslices;    // row slices of d_model (workgroup rows of the append proper)
+  AbsorbArgs ab;      // absorption carried by the launch (ab.units > 0)
 };
 
 // Kernel variants of the context-split decode step.
@@ -69,6 +84,22 @@ const char* split_kernel_name(SplitKernel k);
 
 // Launchers return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st);
+// the absorption's operands of a call; units = 0 (set by the carrying launch)
+__host__ __device__ inline AbsorbArgs absorb_args(const DecodeParams& p) {
+  AbsorbArgs a{};
+  a.q = p.q; a.b_k = p.b_k; a.qt = p.qt;
+  a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.s = p.s; a.gqa = p.gqa; a.d = p.d; a.Dg = p.Dg;
+  a.r = p.r;
+  a.scale_log2 = p.scale_log2;
+  a.units = 0;
+  return a;
+}
+// whether the absorption has the one-load-per-thread form (d / 8 a power of
+// two <= 32) that an append launch can carry
+inline bool absorb_carriable(const AbsorbArgs& a) {
+  const int ncc = a.d / 8;
+  return a.d % 8 == 0 && ncc <= 32 && (ncc & (ncc - 1)) == 0;
+}
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
@@ -84,8 +115,9 @@ hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st)
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 size_t append_workspace_bytes(int B, int dm, int G, int r);
-// sets counters and part
+// sets counters, part and nslices
 void append_bind_workspace(AppendParams& p, void* workspace);
+int append_threads(int quant);   // threads per append workgroup
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu

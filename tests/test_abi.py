@@ -248,6 +248,53 @@ def test_append_validation(lib):
                                   misaligned, need, None) == P.PALU_ERR_WORKSPACE
 
 
+def test_append_prepare_validation(lib):
+    """The combined step checks both calls' arguments before launching
+    anything: the append's (per qbits) and the prepare step's. Every call here
+    is rejected, so nothing is launched on the fake pointers."""
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    ad = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
+                       dtype=P.PALU_BF16)
+    d = _desc()
+
+    def call(qbits=0, ad_=ad, d_=d, a=None, b=None):
+        a = [fake] * 9 if a is None else a       # x, a_k, a_v, h_k, h_v, s_k, s_v, pos, ws
+        b = [fake] * 3 if b is None else b       # q, b_k, workspace
+        return lib.palu_latent_append_prepare(
+            None if ad_ is None else ctypes.byref(ad_), qbits, *a[:8], a[8], big,
+            None if d_ is None else ctypes.byref(d_), b[0], b[1], b[2], big, None)
+
+    assert call(qbits=3) == P.PALU_ERR_UNSUPPORTED
+    assert call(ad_=None) == P.PALU_ERR_NULL
+    assert call(d_=None) == P.PALU_ERR_NULL
+    for i in (0, 1, 2, 3, 4, 7, 8):              # every append pointer but the scales
+        a = [fake] * 9
+        a[i] = None
+        assert call(a=a) == P.PALU_ERR_NULL
+    for bits in (8, 4):
+        for i in (5, 6):                          # the scales, for a quantised cache
+            a = [fake] * 9
+            a[i] = None
+            assert call(qbits=bits, a=a) == P.PALU_ERR_NULL
+    for i in range(3):
+        b = [fake] * 3
+        b[i] = None
+        assert call(b=b) == P.PALU_ERR_NULL
+    bad = P.AppendDesc(**{**{f: getattr(ad, f) for f, _ in P.AppendDesc._fields_}, "hadamard": 1})
+    assert call(ad_=bad) == P.PALU_ERR_UNSUPPORTED   # a dtype cache has no Hadamard form
+    worse = _desc(head_dim=3)
+    assert call(d_=worse) == P.PALU_ERR_SHAPE
+    need = P.palu_decode_attn_workspace(d)
+    assert lib.palu_latent_append_prepare(
+        ctypes.byref(ad), 0, *([fake] * 8), fake, big, ctypes.byref(d), fake, fake, fake,
+        need - 1, None) == P.PALU_ERR_WORKSPACE
+    aneed = P.palu_latent_append_workspace(ad)
+    assert lib.palu_latent_append_prepare(
+        ctypes.byref(ad), 0, *([fake] * 8), fake, aneed - 1, ctypes.byref(d), fake, fake, fake,
+        big, None) == P.PALU_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 def test_append_quant_validation(lib, bits):
     """The quantised cache write: the append checks, rank 64/128/256, NULL
