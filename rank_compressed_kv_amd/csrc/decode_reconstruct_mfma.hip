@@ -121,10 +121,14 @@ template <int R, int kWaves>
 struct Smem {
   char k[kNBuf][kTile * kKStride<R>];
   char v[kNBuf][kVBytes<R>];
-  float4 spart[2][kWaves][64];   // partial scores of each wave (its lanes' float4), two tiles
+  // partial scores of each wave (its lanes' float4), two tiles; a wave's block
+  // is padded by 32 B so that the blocks of two KV heads' waves, read by one
+  // 8-lane group, fall on different LDS banks
+  float4 spart[2][kWaves][66];
   // cos, sin of t * omega_f for the 16 tokens t of a tile, f < 64, two tiles:
-  // rtab[buf][f / 4][t - tok0][f % 4] (a lane's four frequencies are 32 contiguous B)
-  float2 rtab[2][16][kTile][4];
+  // rtab[buf][f / 2][t - tok0][f % 2]: a lane's frequencies f, f + 1 are one
+  // 16-byte row, and the 16 tokens' rows are contiguous (conflict-free reads)
+  float2 rtab[2][32][kTile][2];
 };
 
 template <int R, int kP, int HW, bool kShared>
@@ -211,7 +215,7 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
 #pragma unroll
     for (int e = 0; e < kRE; ++e) {
       const int idx = tid + e * kThreads, f = idx >> 4;
-      sm.rtab[buf][f >> 2][idx & 15][f & 3] = float2{rc[e], rs[e]};
+      sm.rtab[buf][f >> 1][idx & 15][f & 1] = float2{rc[e], rs[e]};
     }
   };
   // the tables of tiles 0 and 1; the thread state then stands at tile 1
@@ -254,9 +258,10 @@ __global__ __launch_bounds__((Shape<R, kP, HW>::kThreads)) void split_reconstruc
     // rotate the pairs (f, f + 64): f = 16*cbs(i) + 4kb + e, token ln
 #pragma unroll
     for (int i = 0; i < kP; ++i) {
-      const float4* rt = reinterpret_cast<const float4*>(&sm.rtab[it & 1][4 * cbs(i) + kb][ln][0]);
-      const float4 r01 = rt[0];
-      const float4 r23 = rt[1];
+      // frequencies 16 cbs(i) + 4 kb + (0, 1) and (2, 3)
+      const int f2 = 2 * (4 * cbs(i) + kb);
+      const float4 r01 = *reinterpret_cast<const float4*>(&sm.rtab[it & 1][f2][ln][0]);
+      const float4 r23 = *reinterpret_cast<const float4*>(&sm.rtab[it & 1][f2 + 1][ln][0]);
       const float c4[4] = {r01.x, r01.z, r23.x, r23.z}, s4[4] = {r01.y, r01.w, r23.y, r23.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
