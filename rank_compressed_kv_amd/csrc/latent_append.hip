@@ -27,6 +27,11 @@
 // With the Hadamard option (a quantisation-friendly enhancement the author
 // responses name, answer to Q2) each fp32 row is first rotated by Sylvester's
 // H_r, h'' = h H_r, which spreads an outlier latent over all r codes.
+//
+// The launch can also carry the next decode call's query absorption
+// (q~ = q B_k^T, which reads neither the cache nor A): its workgroups come
+// after the append's in the grid, each running one absorb_rows unit, so the
+// two run side by side in one launch instead of one after the other.
 #include "absorb_device.h"
 #include "device_util.h"
 #include "palu_internal.h"
