@@ -73,3 +73,47 @@ def test_full_size_quantised_sampled(bits, rot):
         g_s.append(got[b, h])
         w_s.append(w)
     assert_close(np.array(g_s), np.array(w_s), what=f"full int{bits} rot={rot}")
+
+
+def test_full_size_step_sampled():
+    """The step the benchmark times, at config 3's full size: one
+    palu_latent_append_prepare call (the token's latents into row len-1 of
+    both caches, the query absorption in the same launch), then the decode
+    call with prepared = 1, in the library's own plan; sampled outputs
+    against the oracle on the cache after its own append of that token."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = W.CONFIGS[3]
+    t = W.generate(cfg, parts=("decode", "append"))
+    pairs = _pairs(cfg, t["lens"])
+    print(f"[full] step cfg3 pairs={pairs}", flush=True)
+    desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
+                       max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, mode="absorbed")
+    adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=P.PALU_BF16)
+    pdesc = P.AttnDesc.from_buffer_copy(desc)
+    pdesc.prepared = 1
+    pos = (t["lens"] - 1).astype(np.int32)
+    hk, hv = dev(t["h_k"]), dev(t["h_v"])
+    ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    aws = torch.zeros(P.palu_latent_append_workspace(adesc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    q, bk, bv, lens = dev(t["q"]), dev(t["b_k"]), dev(t["b_v"]), dev(t["lens"])
+    P.palu_latent_append_prepare(adesc, 0, dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv,
+                                 None, None, dev(pos), aws, desc, q, bk, ws)
+    P.palu_decode_attn(pdesc, q, hk, hv, bk, bv, lens, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # the oracle's own append of the token, then decode attention
+    caches = []
+    for cache, a in ((t["h_k"], t["a_k"]), (t["h_v"], t["a_v"])):
+        h64 = O.latent_project(t["x"], a).reshape(cfg.batch, cfg.n_groups, cfg.rank)
+        c = cache.copy()
+        for b, p in enumerate(pos):
+            c[b, :, int(p)] = O.append_rows_bf16(h64[b])
+        caches.append(c)
+    want = O.decode_attention(t["q"], caches[0], caches[1], t["b_k"], t["b_v"], t["lens"],
+                              rope_theta=0.0, select=pairs)
+    sel = tuple(np.array(pairs).T)
+    assert_close(got[sel], want[sel], what="full cfg3 step")
