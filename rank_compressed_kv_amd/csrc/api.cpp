@@ -542,21 +542,23 @@ palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits
   dp.q = q; dp.b_k = b_k;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const AbsorbArgs ab = absorb_args(dp);
-  if (attn->mode == PALU_MODE_ABSORBED && attn->dtype == ad->dtype && absorb_carriable(ab)) {
-    // the absorption rides in the append's launch: one workgroup per (KV
-    // head, sequence, slice of r rows)
-    ap.ab = ab;
+  // the absorption rides in the append's launch when it can: one extra
+  // workgroup per (KV head, sequence, slice of r rows)
+  AbsorbArgs ab = absorb_args(dp);
+  if (absorb_carriable(ab)) {
     const int rows = append_threads(qbits) / (ab.d / 8);
-    ap.ab.units = ab.Hkv * ab.B * ((ab.r + rows - 1) / rows);
-    const hipError_t e = launch_append(ap, ad->dtype, s);
-    if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
-    return ok();
+    ab.units = ab.Hkv * ab.B * ((ab.r + rows - 1) / rows);
   }
+  const bool carry = attn->mode == PALU_MODE_ABSORBED && attn->dtype == ad->dtype &&
+                     absorb_carriable(ab) && append_can_carry(ap, ab.units);
+  if (carry) ap.ab = ab;
   const hipError_t e = launch_append(ap, ad->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
-  st = prepare_launch(attn, dp, pl, s);
-  return st == PALU_OK ? ok() : st;
+  if (!carry) {
+    st = prepare_launch(attn, dp, pl, s);
+    if (st != PALU_OK) return st;
+  }
+  return ok();
 }
 
 palu_status palu_profile_begin(int32_t max_records) {

@@ -436,4 +436,10 @@ hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
 
 int append_threads(int quant) { return quant ? Tiling<true>::kThreads : Tiling<false>::kThreads; }
 
+bool append_can_carry(const AppendParams& p, long units) {
+  const int kc = p.quant ? Tiling<true>::kCols : Tiling<false>::kCols;
+  const long bx = (2L * p.G * p.r + kc - 1) / kc;
+  return units > 0 && p.nslices + (units + bx - 1) / bx <= 65535;
+}
+
 }  // namespace palu

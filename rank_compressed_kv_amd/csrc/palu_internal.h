@@ -118,6 +118,8 @@ size_t append_workspace_bytes(int B, int dm, int G, int r);
 // sets counters, part and nslices
 void append_bind_workspace(AppendParams& p, void* workspace);
 int append_threads(int quant);   // threads per append workgroup
+// whether an append launch can take `units` absorb workgroups (grid bound)
+bool append_can_carry(const AppendParams& p, long units);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu
