@@ -292,8 +292,9 @@ palu_status palu_latent_append_i4(const palu_append_desc* desc, const void* x, c
  * When attn is ABSORBED with the append's dtype and head_dim / 8 is a power
  * of two <= 32, the query absorption (the clarification of W1: B_k moves onto
  * the query) runs as extra workgroups of the append's launch, beside the
- * cache write, in one launch; otherwise the two are launched one after the
- * other on `stream`. Either way the results are those of the two calls.
+ * cache write, in one launch (unless those would exceed a launch grid's
+ * 65535 rows, at very large batch); otherwise the two are launched one after
+ * the other on `stream`. Either way the results are those of the two calls.
  *   ad, x, a_k, a_v, h_k, h_v, s_k, s_v, pos, append_ws, append_ws_bytes: as
  *     for the append call qbits selects (s_k, s_v unused and may be NULL for
  *     qbits 0; h_k, h_v are int8_t* / uint8_t* codes for qbits 8 / 4);
