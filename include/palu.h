@@ -30,7 +30,10 @@
  *   - Validation is done on the host before any HIP call; on an error nothing
  *     is launched and palu_last_error() gives a one-line reason (thread-local).
  *   - The library keeps no state between calls except that text and the
- *     optional profiling records below; calls are re-entrant.
+ *     optional profiling records below; calls are re-entrant (calls made
+ *     while profiling is armed claim distinct records), except
+ *     palu_profile_begin and palu_profile_end, which must not run while
+ *     other calls are in progress.
  *   - Conditions only the device can see (a length above max_ctx, an append
  *     position outside [0, max_ctx)) are not errors: lengths are clamped to
  *     [0, max_ctx] and out-of-range append rows are skipped.
@@ -301,7 +304,9 @@ palu_status palu_latent_append_i4(const palu_append_desc* desc, const void* x, c
  *   attn, q, b_k, workspace, workspace_bytes: as for palu_decode_attn_prepare
  *     (attn->prepared is not read).
  * Errors: those of the two calls, checked before anything is launched;
- * UNSUPPORTED for qbits other than 0, 8 and 4. */
+ * UNSUPPORTED for qbits other than 0, 8 and 4; WORKSPACE also when the byte
+ * ranges [append_ws, +append_ws_bytes) and [workspace, +workspace_bytes)
+ * overlap. */
 palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits, const void* x,
                                        const void* a_k, const void* a_v, void* h_k, void* h_v,
                                        float* s_k, float* s_v, const int32_t* pos,
@@ -312,14 +317,18 @@ palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits
 
 /* Optional timing of the main decode kernel (the context-split kernel) with HIP
  * events on the stream it is launched on. palu_profile_begin(n) arms n records
- * (events are created here, once); each later palu_decode_attn call records one
- * start/stop pair around that kernel until n are used. palu_profile_end waits
- * for the recorded events, returns the summed milliseconds and the count,
- * releases the events and disarms. Not thread-safe; for benchmarks. */
+ * (events are created here, once); each later palu_decode_attn call claims the
+ * next start/stop pair (one atomic increment, so concurrent calls never share
+ * a pair) and records it around that kernel, until n are used.
+ * palu_profile_end waits for the recorded events, returns the summed
+ * milliseconds and the count, releases the events and disarms. begin and end
+ * themselves must not overlap any other call; for benchmarks. */
 palu_status palu_profile_begin(int32_t max_records);
 palu_status palu_profile_end(double* total_ms, int32_t* count);
 
-const char* palu_status_string(palu_status status);
+/* A short text for a status code; any value is accepted (codes that are not
+ * a palu_status give "unknown status"). */
+const char* palu_status_string(int32_t status);
 const char* palu_last_error(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,11 @@ beyond what the definitions state):
 
 Readings where the pages are silent (each listed in the design notes):
   * frequencies omega_i = theta ** (-2 i / d), i in [0, d/2), and the pair
-    rotated together is (i, i + d/2) of a head's d channels;
+    rotated together is (i, i + d/2) of a head's d channels. No page fixes
+    the pairing (the interleaved pairs (2i, 2i+1) fit them equally well), so
+    apply_rope is parity unpinned as to the pairing: its pins fix the sign,
+    the frequency schedule and the rotation's properties, and both sides
+    share the pairing;
   * RoPE acts on reconstructed keys at positions 0..len-1; q arrives already
     position-encoded;
   * group g holds KV heads g*s .. g*s+s-1; KV head g*s+jl uses columns

@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdarg>
@@ -158,11 +160,30 @@ WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   return w;
 }
 
+// Profiling records: a call claims the next start/stop pair with one atomic
+// increment, so calls from several host threads never share a pair.
 struct Profiler {
   std::vector<hipEvent_t> start, stop;
-  int used = 0;
+  std::atomic<int> used{0};
   bool armed = false;
 } g_prof;
+
+// The device's largest grid extent in y (launches that carry extra
+// workgroup rows must stay within it); read once per device.
+long max_grid_y() {
+  static std::atomic<long> cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 65535;
+  if (dev < 64) {
+    const long c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess || v <= 0)
+    v = 65535;
+  if (dev < 64) cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 }  // namespace
 
@@ -181,7 +202,7 @@ using namespace palu;
 
 extern "C" {
 
-const char* palu_status_string(palu_status s) {
+const char* palu_status_string(int32_t s) {
   switch (s) {
     case PALU_OK: return "ok";
     case PALU_ERR_NULL: return "null pointer";
@@ -284,8 +305,12 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
     if (ps != PALU_OK) return ps;
   }
 
-  const bool timed = g_prof.armed && g_prof.used < int(g_prof.start.size());
-  if (timed) (void)hipEventRecord(g_prof.start[g_prof.used], s);
+  int rec = -1;
+  if (g_prof.armed) {
+    rec = g_prof.used.fetch_add(1, std::memory_order_relaxed);
+    if (rec >= int(g_prof.start.size())) rec = -1;
+  }
+  if (rec >= 0) (void)hipEventRecord(g_prof.start[rec], s);
   switch (pl.kernel) {
     case SplitKernel::kAbsorbedMfma:
       e = p.qbits ? launch_split_absorbed_quant(p, s) : launch_split_absorbed_mfma(p, s);
@@ -293,7 +318,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
-  if (timed) (void)hipEventRecord(g_prof.stop[g_prof.used++], s);
+  if (rec >= 0) (void)hipEventRecord(g_prof.stop[rec], s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
 
   e = launch_merge(p, desc->dtype, s);
@@ -541,17 +566,31 @@ palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits
   DecodeParams dp = call_params(attn, pl, wl, workspace);
   dp.q = q; dp.b_k = b_k;
 
+  // the two workspaces must not share a byte: in the carried launch the
+  // absorb workgroups write q~ while the append's write partials and arrival
+  // counters, and a counter left nonzero would make later appends skip rows
+  {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(append_ws), a1 = a0 + append_ws_bytes;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + workspace_bytes;
+    if (a0 < w1 && w0 < a1)
+      return fail(PALU_ERR_WORKSPACE, "the append workspace and the decode workspace overlap");
+  }
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the absorption rides in the append's launch when it can: one extra
   // workgroup per (KV head, sequence, slice of r rows)
   AbsorbArgs ab = absorb_args(dp);
+  long units = 0;
   if (absorb_carriable(ab)) {
-    const int rows = append_threads(qbits) / (ab.d / 8);
-    ab.units = ab.Hkv * ab.B * ((ab.r + rows - 1) / rows);
+    const long rows = append_threads(qbits) / (ab.d / 8);
+    units = long(ab.Hkv) * ab.B * ((ab.r + rows - 1) / rows);
   }
   const bool carry = attn->mode == PALU_MODE_ABSORBED && attn->dtype == ad->dtype &&
-                     absorb_carriable(ab) && append_can_carry(ap, ab.units);
-  if (carry) ap.ab = ab;
+                     absorb_carriable(ab) && append_can_carry(ap, units, max_grid_y());
+  if (carry) {
+    ab.units = int32_t(units);
+    ap.ab = ab;
+  }
   const hipError_t e = launch_append(ap, ad->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   if (!carry) {
@@ -574,7 +613,7 @@ palu_status palu_profile_begin(int32_t max_records) {
         hipEventCreateWithFlags(&g_prof.stop[i], hipEventDisableSystemFence) != hipSuccess)
       return fail(PALU_ERR_DEVICE, "hipEventCreate failed");
   }
-  g_prof.used = 0;
+  g_prof.used.store(0);
   g_prof.armed = true;
   return ok();
 }
@@ -583,7 +622,8 @@ palu_status palu_profile_end(double* total_ms, int32_t* count) {
   if (!g_prof.armed) return fail(PALU_ERR_UNSUPPORTED, "profiling not armed");
   double sum = 0.0;
   palu_status st = PALU_OK;
-  for (int i = 0; i < g_prof.used; ++i) {
+  const int used = std::min(g_prof.used.load(), int(g_prof.start.size()));
+  for (int i = 0; i < used; ++i) {
     float ms = 0.f;
     if (hipEventSynchronize(g_prof.stop[i]) != hipSuccess ||
         hipEventElapsedTime(&ms, g_prof.start[i], g_prof.stop[i]) != hipSuccess) {
@@ -593,12 +633,15 @@ palu_status palu_profile_end(double* total_ms, int32_t* count) {
     sum += ms;
   }
   if (total_ms) *total_ms = sum;
-  if (count) *count = g_prof.used;
+  if (count) *count = used;
   for (size_t i = 0; i < g_prof.start.size(); ++i) {
     if (g_prof.start[i]) (void)hipEventDestroy(g_prof.start[i]);
     if (g_prof.stop[i]) (void)hipEventDestroy(g_prof.stop[i]);
   }
-  g_prof = Profiler{};
+  g_prof.start.clear();
+  g_prof.stop.clear();
+  g_prof.used.store(0);
+  g_prof.armed = false;
   return st == PALU_OK ? ok() : st;
 }
 

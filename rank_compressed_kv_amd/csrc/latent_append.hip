@@ -66,20 +66,24 @@ struct Tiling {
 };
 
 // Hand-off of the partials between workgroups on different XCDs, whose L2
-// caches are not coherent with each other:
-//   writer: device-scope stores (written through past its L2), then
-//           s_waitcnt vmcnt(0) (acknowledged, i.e. performed at device scope)
-//           before the workgroup barrier and the counter increment, so no
-//           cache-wide L2 write-back is needed;
-//   reader: the last arriver's device-scope acquire fence invalidates its own
-//           caches, after which ordinary 16-byte loads see every partial.
+// caches are not coherent with each other, in release/acquire terms:
+//   writer: device-scope (agent) stores of the partials, then the workgroup
+//           barrier (every wave's stores happen before it), then one thread's
+//           counter increment with release semantics at agent scope, which
+//           makes everything that happened before it visible at agent scope
+//           before the increment is;
+//   reader: the last arriver's increment reads the final count; after the
+//           workgroup barrier every thread takes an agent-scope acquire fence
+//           (which drops its stale cached lines), so ordinary 16-byte loads
+//           see every partial.
+// The stores themselves are agent-scope atomics so that the release has no
+// dirty L2 lines of this data to write back.
 __device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
   const uint64_t bits = static_cast<uint64_t>(__float_as_uint(a)) |
                         (static_cast<uint64_t>(__float_as_uint(b)) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Byte offset of latent k of token t inside one (b, g) slab of the int8 cache.
 // The slab is a run of 32-token blocks of 32 r bytes each, ordered as the
@@ -315,12 +319,12 @@ __global__ __launch_bounds__(Tiling<kQuant>::kThreads) void append_kernel(Append
     }
   }
 
-  // arrival: every thread's partial stores are complete (device-coherent)
-  // before the workgroup is counted; the last one reads them coherently.
-  wait_stores_complete();
+  // arrival: the barrier orders every wave's partial stores before the
+  // counter increment, which releases them at agent scope; the last arriver
+  // acquires them.
   __syncthreads();
   if (tid == 0)
-    is_last = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1, __ATOMIC_RELAXED,
+    is_last = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1, __ATOMIC_ACQ_REL,
                                      __HIP_MEMORY_SCOPE_AGENT) == nslices - 1;
   __syncthreads();
   if (!is_last) return;
@@ -436,10 +440,10 @@ hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st) {
 
 int append_threads(int quant) { return quant ? Tiling<true>::kThreads : Tiling<false>::kThreads; }
 
-bool append_can_carry(const AppendParams& p, long units) {
+bool append_can_carry(const AppendParams& p, long units, long max_grid_y) {
   const int kc = p.quant ? Tiling<true>::kCols : Tiling<false>::kCols;
   const long bx = (2L * p.G * p.r + kc - 1) / kc;
-  return units > 0 && p.nslices + (units + bx - 1) / bx <= 65535;
+  return units > 0 && units <= 0x7fffffffL && p.nslices + (units + bx - 1) / bx <= max_grid_y;
 }
 
 }  // namespace palu

@@ -118,8 +118,9 @@ size_t append_workspace_bytes(int B, int dm, int G, int r);
 // sets counters, part and nslices
 void append_bind_workspace(AppendParams& p, void* workspace);
 int append_threads(int quant);   // threads per append workgroup
-// whether an append launch can take `units` absorb workgroups (grid bound)
-bool append_can_carry(const AppendParams& p, long units);
+// whether an append launch can take `units` absorb workgroups (grid rows
+// within the device's bound max_grid_y)
+bool append_can_carry(const AppendParams& p, long units, long max_grid_y);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
 }  // namespace palu

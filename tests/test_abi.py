@@ -293,6 +293,15 @@ def test_append_prepare_validation(lib):
     assert lib.palu_latent_append_prepare(
         ctypes.byref(ad), 0, *([fake] * 8), fake, aneed - 1, ctypes.byref(d), fake, fake, fake,
         big, None) == P.PALU_ERR_WORKSPACE
+    # the two workspaces may not share a byte (checked before any launch):
+    # the decode workspace starting inside the append's, or the append's
+    # starting inside the decode one's
+    a0 = 1 << 32
+    for w0 in (a0 + aneed - 256, a0 - need + 256, a0):
+        assert lib.palu_latent_append_prepare(
+            ctypes.byref(ad), 0, *([fake] * 8), ctypes.c_void_p(a0), aneed, ctypes.byref(d),
+            fake, fake, ctypes.c_void_p(w0), need, None) == P.PALU_ERR_WORKSPACE, hex(w0)
+    assert b"overlap" in lib.palu_last_error()
 
 
 @pytest.mark.parametrize("bits", [8, 4])

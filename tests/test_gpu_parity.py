@@ -193,7 +193,7 @@ def test_null_lens_means_full_capacity():
     assert_close(got, want, what="lens=NULL")
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_latent_append(idx):
     """h[b, g, pos[b]] = x[b] A: bf16 rows agree with the oracle's fp32-then-bf16
     rounding except where the exact value sits within the fp32 summation error

@@ -121,8 +121,10 @@ def test_step_matches_separate_calls(name):
 
 def test_step_against_oracle():
     """The bf16 absorbed step (one launch before the decode call) against the
-    oracle: decode attention over the cache the step wrote, whose new rows are
-    the oracle's own projection up to the last bit of bf16 rounding."""
+    oracle on inputs the oracle forms itself: its own cache write of the
+    token (x A, rounded to fp32 then to bf16) into row pos[b] of the seeded
+    caches, then decode attention over those caches. The GPU-written rows are
+    also held to the oracle's within bf16 rounding of the fp32 sum."""
     import torch
     import rank_compressed_kv_amd as P
     cfg, qbits, mode = CASES["bf16_absorbed"]
@@ -137,12 +139,16 @@ def test_step_against_oracle():
     _decode(P, 0, pdesc, ops, cache, out, ws)
     torch.cuda.synchronize()
     bits = lambda c: c.cpu().view(torch.int16).numpy().view(np.uint16)
-    hk, hv = bits(cache[0]), bits(cache[1])
-    # the written rows: the oracle's x A within bf16 rounding
     as_f = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    for h, a in ((hk, t["a_k"]), (hv, t["a_v"])):
-        want = O.latent_project(t["x"], a).reshape(cfg.batch, cfg.n_groups, cfg.rank)
+    oracle_caches = []
+    for h, seeded, a in ((bits(cache[0]), t["h_k"], t["a_k"]), (bits(cache[1]), t["h_v"], t["a_v"])):
+        h64 = O.latent_project(t["x"], a).reshape(cfg.batch, cfg.n_groups, cfg.rank)
         got = np.stack([as_f(h[b, :, int(p)]) for b, p in enumerate(pos)])
-        np.testing.assert_allclose(got, want, rtol=2.0 ** -7, atol=1e-6)
-    want = O.decode_attention(t["q"], hk, hv, t["b_k"], t["b_v"], lens, rope_theta=0.0)
+        np.testing.assert_allclose(got, h64, rtol=2.0 ** -7, atol=1e-6)
+        c = seeded.copy()
+        for b, p in enumerate(pos):
+            c[b, :, int(p)] = O.append_rows_bf16(h64[b])
+        oracle_caches.append(c)
+    want = O.decode_attention(t["q"], oracle_caches[0], oracle_caches[1], t["b_k"], t["b_v"],
+                              lens, rope_theta=0.0)
     assert_close(out.cpu().numpy().astype(np.float64), want, what="step vs oracle")

@@ -59,6 +59,25 @@ MUTANTS = {
                          "return keep.astype(np.uint16)"),
     "append_ties_up": ("append_rows_bf16", "(rest == 0x8000) & ((keep & np.uint64(1)) == 1)",
                        "(rest == 0x8000)"),
+    "bf16_widen_shift_8": ("to_f64", "<< np.uint32(16)", "<< np.uint32(8)"),
+    "bf16_widen_as_fp16": ("to_f64",
+                           "return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)",
+                           "return a.view(np.float16).astype(np.float64)"),
+    "bf16_widen_as_integer": ("to_f64",
+                              "return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)",
+                              "return a.astype(np.float64)"),
+    "append_i4_uses_i8_quantiser": ("append_rows_i4", "return quantize_rows_i4(",
+                                    "return quantize_rows_i8("),
+    "append_i8_uses_i4_quantiser": ("append_rows_i8", "return quantize_rows_i8(",
+                                    "return quantize_rows_i4("),
+    "append_i8_via_bf16": ("append_rows_i8",
+                           "np.asarray(h64, dtype=np.float64).astype(np.float32)",
+                           "(append_rows_bf16(h64).astype(np.uint32) << np.uint32(16)).view(np.float32)"),
+    "hadamard_i4_rotation_dropped": ("append_rows_i4_hadamard",
+                                     "quantize_rows_i4((h @ hadamard(h.shape[-1])).astype(np.float32))",
+                                     "quantize_rows_i4(h.astype(np.float32))"),
+    "hadamard_i4_uses_i8": ("append_rows_i4_hadamard", "return quantize_rows_i4(",
+                            "return quantize_rows_i8("),
 }
 
 PINS = [name for name in dir(P) if name.startswith("test_")]

@@ -571,3 +571,118 @@ def test_append_matches_projection():
     bits = O.append_rows_bf16(h)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.abs(back - h) <= np.abs(h) * 2.0 ** -8)
+
+
+# -------------------------------------------------- bf16 storage widening ---
+
+def test_to_f64_bf16_bit_patterns():
+    """A bf16 value is the fp32 number whose upper 16 bits are its bits.
+    Hand-derived: 0x3F80 is sign 0, exponent 127, mantissa 0 -> 1.0; 0xBF82 is
+    -(1 + 2/128) = -1.015625; 0x0001 is the smallest subnormal, 2^-126 * 2^-7
+    = 2^-133; 0x7F80 is +inf; 0x4049 is 2 * (1 + 73/128) = 3.140625; 0x8000 is
+    -0.0. Also a cross-check against torch's own bfloat16 -> float64 widening."""
+    bits = np.array([0x3F80, 0xBF82, 0x0001, 0x7F80, 0x4049, 0x8000], dtype=np.uint16)
+    want = [1.0, -1.015625, 2.0 ** -133, math.inf, 3.140625, -0.0]
+    got = O.to_f64(bits)
+    assert got.dtype == np.float64
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1.0, g) == math.copysign(1.0, w), (g, w)
+    rng = np.random.default_rng(50)
+    many = rng.integers(0, 2 ** 16, size=4096, dtype=np.uint16)
+    many = many[(many & 0x7F80) != 0x7F80]            # finite patterns only
+    ref = torch.from_numpy(many.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.to_f64(many), ref)
+
+
+def _bf16_bits(values):
+    """bf16 bits of values that are exactly representable in bf16: the upper
+    half of their fp32 encoding (struct packing, independent of the oracle)."""
+    import struct
+    out = []
+    for v in np.asarray(values, dtype=np.float64).ravel():
+        w = struct.unpack("<I", struct.pack("<f", float(v)))[0]
+        assert w & 0xFFFF == 0, v
+        out.append(w >> 16)
+    return np.array(out, dtype=np.uint16).reshape(np.shape(values))
+
+
+def test_brute_force_on_bf16_storage():
+    """The oracle fed bf16 bit patterns (every input of the bf16 workloads
+    reaches it so) gives the brute-force result of the values those bits
+    hold: inputs are multiples of 1/16 in [-4, 4), exact in bf16."""
+    Bsz, Hq, Hkv, d, G, r, L = 2, 4, 2, 8, 1, 4, 6
+    rng = np.random.default_rng(51)
+    draw = lambda *shape: rng.integers(-64, 64, size=shape) / 16.0
+    q, h_k, h_v = draw(Bsz, Hq, d), draw(Bsz, G, L, r), draw(Bsz, G, L, r)
+    b_k, b_v = draw(G, r, Hkv // G * d) / 4, draw(G, r, Hkv // G * d) / 4
+    lens = np.array([L, 3])
+    want = _brute(q.tolist(), h_k.tolist(), h_v.tolist(), b_k.tolist(), b_v.tolist(),
+                  lens.tolist(), 10000.0)
+    got = O.decode_attention(_bf16_bits(q), _bf16_bits(h_k), _bf16_bits(h_v), _bf16_bits(b_k),
+                             _bf16_bits(b_v), lens, rope_theta=10000.0)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------- quantised cache writes (rows) ---
+#
+# Per-token quantisation of the latents (Palu author response to reviewer
+# Fsn9, W1/W2; "Avg. Bits" with a scale shared by a group, answer to Q4). The
+# kernel's row is an fp32 sum, so the oracle rounds the exact row to fp32 once
+# and takes every decision on that fp32 row. The rows below hold elements whose
+# exact value and fp32 rounding fall on different sides of a rounding decision.
+
+def test_append_rows_i8_hand_row():
+    """Exact row [127 + 2^-40, 2.5 + 2^-30, 2.5078125, -63.5, 0.5 - 2^-40, -1.5,
+    0, 126.5] rounds to the fp32 row [127, 2.5, 2.5078125, -63.5, 0.5, -1.5, 0,
+    126.5] (the added terms are far below half an fp32 ulp). amax = 127, so
+    scale = 127/127 = 1 and the multiplier 127/127 = 1; codes are the
+    nearest-even integers of the fp32 row: [127, 2, 3, -64, 0, -2, 0, 126]. The
+    exact value 2.5 + 2^-30 would give 3, and 2.5078125 rounded to bf16 first
+    (a tie, to the even 2.5) would give 2."""
+    h = np.array([[127 + 2.0 ** -40, 2.5 + 2.0 ** -30, 2.5078125, -63.5, 0.5 - 2.0 ** -40,
+                   -1.5, 0.0, 126.5]])
+    codes, scales = O.append_rows_i8(h)
+    assert codes.dtype == np.int8
+    np.testing.assert_array_equal(codes[0], [127, 2, 3, -64, 0, -2, 0, 126])
+    assert scales.dtype == np.float32 and scales[0] == np.float32(1.0)
+    # the same row ten times larger: amax 1270 (exact in fp32), scale 10,
+    # multiplier fl(127/1270) = fl(0.1); every code is then one fp32 product
+    # away from the integer or tie it was before, computed here by hand
+    h10 = np.array([[1270.0, 25.0, 5.0, -635.0, 0.0, 12.5, -12.5, 1265.0]])
+    codes, scales = O.append_rows_i8(h10)
+    inv = np.float32(127.0) / np.float32(1270.0)                  # fl(0.1)
+    prods = [np.float32(v) * inv for v in h10[0]]
+    np.testing.assert_array_equal(codes[0], [int(np.rint(p)) for p in prods])
+    assert scales[0] == np.float32(1270.0) / np.float32(127.0)
+    assert list(codes[0][:4]) == [127, 2, 0, -64]
+
+
+def test_append_rows_i4_hand_row():
+    """int4: exact row [7 + 2^-40, 2.5 + 2^-30, -3.5, 1.5, 0.5 - 2^-40, 6.5, -7,
+    0.25] -> fp32 [7, 2.5, -3.5, 1.5, 0.5, 6.5, -7, 0.25]; amax 7, scale 7/7 =
+    1, multiplier 1; codes nearest-even: [7, 2, -4, 2, 0, 6, -7, 0] (15
+    levels). An int8 quantiser would give 127 for the first element."""
+    h = np.array([[7 + 2.0 ** -40, 2.5 + 2.0 ** -30, -3.5, 1.5, 0.5 - 2.0 ** -40, 6.5, -7.0,
+                   0.25]])
+    codes, scales = O.append_rows_i4(h)
+    np.testing.assert_array_equal(codes[0], [7, 2, -4, 2, 0, 6, -7, 0])
+    assert scales[0] == np.float32(1.0)
+    z_codes, z_scales = O.append_rows_i4(np.zeros((1, 8)))
+    assert np.all(z_codes == 0) and z_scales[0] == 0.0
+
+
+def test_hadamard_i4_quantisation_of_a_spike():
+    """Rotated int4 write of a row with one nonzero latent c at index k: h H_r
+    is c times row k of Sylvester's matrix (entries +-c), so every code is
+    +-7 with the sign of c H[k], the scale is |c|/7, and rotating the
+    dequantised row back gives the spike."""
+    r, k, c = 64, 9, np.float32(-3.0)
+    h = np.zeros((1, r))
+    h[0, k] = c
+    codes, scales = O.append_rows_i4_hadamard(h)
+    i, j = k, np.arange(r)
+    sign_row = (-1.0) ** np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    np.testing.assert_array_equal(codes[0], (7 * np.sign(c) * sign_row).astype(np.int8))
+    assert scales[0] == np.float32(3.0) / np.float32(7.0)
+    back = O.dequantize_rows_i8_hadamard(codes, scales)
+    np.testing.assert_allclose(back[0], h[0], atol=1e-6)
