@@ -138,6 +138,25 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
                              const int32_t* seq_lens, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* palu_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The call works in a scratch array the
+ * library owns on each GPU (32 MiB, a static device array: each GPU the library
+ * runs on holds its copy until the process ends) and allocates nothing.
+ *   desc, q, h_k, h_v, b_k, b_v, seq_lens, out, stream: as for palu_decode_attn,
+ *   on the current device (the stream, if not NULL, must belong to it).
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (several streams, several
+ * host threads) race and must be ordered by the caller.
+ * Errors: those of palu_decode_attn; WORKSPACE when the call needs more
+ * scratch than 32 MiB (palu_decode_attn_workspace gives the figure);
+ * UNSUPPORTED for desc->prepared = 1 (prepared operands live in a caller's
+ * workspace), hadamard, or a stream of another device; DEVICE when the
+ * scratch's address cannot be looked up. Nothing is launched on an error. */
+palu_status palu_decode_attn_noalloc(const palu_attn_desc* desc, const void* q, const void* h_k,
+                                     const void* h_v, const void* b_k, const void* b_v,
+                                     const int32_t* seq_lens, float* out, void* stream);
+
 /* The query-side operands of a decode call, formed ahead of it: the absorbed
  * queries q~ = q B_k[g][:, cols(j)]^T (ABSORBED; the clarification of W1: with
  * no rotary embedding B_k moves onto the query), the scaled queries

@@ -24,6 +24,7 @@ __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
            "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+           "palu_decode_attn_noalloc",
            "palu_decode_attn_prepare", "palu_latent_append_prepare", "palu_decode_attn_i8",
            "decode_attention_i8",
            "palu_decode_attn_i4",
@@ -39,6 +40,7 @@ PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
+                    "palu_decode_attn_noalloc",
                     "palu_decode_attn_prepare", "palu_decode_attn_i8", "palu_decode_attn_i4",
                     "palu_latent_append_workspace", "palu_latent_append",
                     "palu_latent_append_i8_workspace", "palu_latent_append_i8",
@@ -96,6 +98,8 @@ def library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.palu_decode_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
+    lib.palu_decode_attn_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp,
+                                             vp, vp]
     lib.palu_decode_attn_prepare.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, sz, vp]
     for fn in ("palu_decode_attn_i8", "palu_decode_attn_i4"):
         getattr(lib, fn).argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp,
@@ -178,9 +182,8 @@ def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
 _TORCH_DTYPE = {PALU_F32: torch.float32, PALU_BF16: torch.bfloat16}
 
 
-def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace,
-                     stream=None) -> None:
-    """Enqueue one decode step. All tensors are checked against desc first."""
+def _decode_checks(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out) -> None:
+    """Shapes, dtypes and devices of a decode call's tensors against desc."""
     palu_decode_attn_plan(desc)          # the library validates the descriptor first
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r, L = desc.n_groups, desc.rank, desc.max_ctx
@@ -200,6 +203,12 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
     _need(out, "out", (B, Hq, r if latent else d), torch.float32)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", (B,), torch.int32)
+
+
+def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, workspace,
+                     stream=None) -> None:
+    """Enqueue one decode step. All tensors are checked against desc first."""
+    _decode_checks(desc, q, h_k, h_v, b_k, b_v, seq_lens, out)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
@@ -208,6 +217,18 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
         None if b_k is None else b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
         None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
         workspace.data_ptr(), nbytes, _stream(stream)), "palu_decode_attn")
+
+
+def palu_decode_attn_noalloc(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out,
+                             stream=None) -> None:
+    """palu_decode_attn in the library's static scratch (no workspace; nothing
+    is allocated). Calls overlapping in time on one GPU race."""
+    _decode_checks(desc, q, h_k, h_v, b_k, b_v, seq_lens, out)
+    _check(library().palu_decode_attn_noalloc(
+        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(),
+        None if b_k is None else b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
+        None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(), _stream(stream)),
+        "palu_decode_attn_noalloc")
 
 
 def _prepare_checks(desc: AttnDesc, q, b_k, workspace) -> int:

@@ -275,14 +275,23 @@ palu_status prepare_launch(const palu_attn_desc* desc, const DecodeParams& p, co
   return PALU_OK;
 }
 
+// the operand pointers a decode call needs for its mode
+palu_status decode_pointers(const palu_attn_desc* desc, const void* q, const void* h_k,
+                            const void* h_v, const void* b_k, const void* b_v, const float* out) {
+  const bool full = desc->mode == PALU_MODE_FULL_RANK;
+  const bool latent = !full && desc->latent_out != 0;
+  if (!q || !h_k || !h_v || (!full && !b_k) || (!full && !latent && !b_v) || !out)
+    return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
+                               "must be non-NULL");
+  return PALU_OK;
+}
+
 // both decode entry points; s_k, s_v non-NULL selects int8 latents
 palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, const void* h_v,
                    const float* s_k, const float* s_v, int qbits, const void* b_k,
                    const void* b_v, const int32_t* seq_lens, float* out, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  const bool full = desc->mode == PALU_MODE_FULL_RANK;
-  const bool latent = !full && desc->latent_out != 0;
-  if (!q || !h_k || !h_v || (!full && !b_k) || (!full && !latent && !b_v) || !out || !workspace)
+  if (decode_pointers(desc, q, h_k, h_v, b_k, b_v, out) != PALU_OK || !workspace)
     return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
                                "must be non-NULL");
   const Plan pl = make_plan(desc);
@@ -367,6 +376,44 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const vo
     return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
   return decode(desc, q, h_k, h_v, nullptr, nullptr, 0, b_k, b_v, seq_lens, out, workspace,
                 workspace_bytes, stream);
+}
+
+palu_status palu_decode_attn_noalloc(const palu_attn_desc* desc, const void* q, const void* h_k,
+                                     const void* h_v, const void* b_k, const void* b_v,
+                                     const int32_t* seq_lens, float* out, void* stream) {
+  // every check on the host first, then the scratch's address (one lookup per
+  // device), then the ordinary call on it
+  palu_status st = validate_attn(desc);
+  if (st != PALU_OK) return st;
+  if (desc->hadamard)
+    return fail(PALU_ERR_UNSUPPORTED, "hadamard applies to the int8 and int4 caches only");
+  if (desc->prepared)
+    return fail(PALU_ERR_UNSUPPORTED,
+                "prepared = 1 needs a caller-owned workspace (use palu_decode_attn)");
+  st = decode_pointers(desc, q, h_k, h_v, b_k, b_v, out);
+  if (st != PALU_OK) return st;
+  const size_t need = layout(desc, make_plan(desc)).total;
+  if (need > kStaticScratchBytes)
+    return fail(PALU_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use palu_decode_attn with a workspace)", need, kStaticScratchBytes);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(PALU_ERR_DEVICE, "hipGetDevice failed");
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return fail(PALU_ERR_DEVICE, "hipStreamGetDevice failed");
+    if (sdev != dev)
+      return fail(PALU_ERR_UNSUPPORTED, "the stream belongs to device %d, the current device is "
+                                        "%d", sdev, dev);
+  }
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(dev, &ws);
+  if (e != hipSuccess)
+    return fail(PALU_ERR_DEVICE, "static scratch lookup: %s", hipGetErrorString(e));
+  return decode(desc, q, h_k, h_v, nullptr, nullptr, 0, b_k, b_v, seq_lens, out, ws,
+                kStaticScratchBytes, stream);
 }
 
 palu_status palu_decode_attn_prepare(const palu_attn_desc* desc, const void* q, const void* b_k,

@@ -123,4 +123,10 @@ int append_threads(int quant);   // threads per append workgroup
 bool append_can_carry(const AppendParams& p, long units, long max_grid_y);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
 
+// The library's static device scratch (palu_decode_attn_noalloc): its size,
+// and the device address of `device`'s copy (looked up once per device; the
+// device must be current).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(int device, void** ptr);
+
 }  // namespace palu

@@ -401,3 +401,30 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 32, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         P.palu_decode_attn(d, q, q, q, q, q, None, q, q)
+
+
+def test_noalloc_validation(lib):
+    """The entry point without a workspace checks everything on the host
+    first: the descriptor, the operand pointers, prepared / hadamard, and the
+    scratch the call needs against the static scratch's 32 MiB. Every call
+    here is rejected before any HIP call, so nothing is launched."""
+    fake = ctypes.c_void_p(0x1000)
+    ops = [fake] * 5 + [None, fake]          # q, h_k, h_v, b_k, b_v, seq_lens, out
+
+    def call(d, ops_=ops):
+        return lib.palu_decode_attn_noalloc(ctypes.byref(d), *ops_, None)
+
+    assert lib.palu_decode_attn_noalloc(None, *ops, None) == P.PALU_ERR_NULL
+    assert call(_desc(head_dim=127)) == P.PALU_ERR_SHAPE
+    for i in (0, 1, 2, 3, 4, 6):
+        o = list(ops)
+        o[i] = None
+        assert call(_desc(), o) == P.PALU_ERR_NULL, i
+    assert call(_desc(prepared=True)) == P.PALU_ERR_UNSUPPORTED
+    assert call(_desc(hadamard=True)) == P.PALU_ERR_UNSUPPORTED
+    # far beyond 32 MiB of split partials: rejected with the figure it needs
+    big = _desc(batch=256)
+    need = P.palu_decode_attn_workspace(big)
+    assert need > 32 << 20
+    assert call(big) == P.PALU_ERR_WORKSPACE
+    assert str(need).encode() in lib.palu_last_error()
