@@ -47,6 +47,7 @@ constexpr int kSplitQuantum = 64;    // split sizes are multiples of this many t
 constexpr int kTargetWorkgroups = 1024;
 constexpr int kAbsorbedWorkgroups = 256;   // one per CU on a 256-CU MI355X
 constexpr int kTargetWaves = 2048;         // reconstruct kernel: eight per CU
+constexpr int kWaveKernelWaves = 1024;     // one-wave-per-head kernel: four per CU
 
 palu_status validate_attn(const palu_attn_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
@@ -112,6 +113,8 @@ Plan make_plan(const palu_attn_desc* d) {
     pl.kernel = SplitKernel::kAbsorbedMfma;
   if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_mfma_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kReconstructMfma;
+  if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_wave_supported(sp, d->dtype))
+    pl.kernel = SplitKernel::kReconstructWave;
   int st = d->split_tokens;
   if (st == 0) {
     // Aim at a fixed number of (split, b, g) units: 256 for the generic
@@ -127,6 +130,13 @@ Plan make_plan(const palu_attn_desc* d) {
     if (pl.kernel == SplitKernel::kReconstructMfma) {
       slices = sp.s / reconstruct_heads_per_wg(sp.r, sp.s);
       wg_target = double(kTargetWaves) / reconstruct_waves_per_wg(sp.r, sp.s);
+    }
+    // one wave per KV head: aim at one wave per SIMD (1024 waves), i.e. one
+    // four-wave workgroup per CU
+    if (pl.kernel == SplitKernel::kReconstructWave) {
+      const int hw = reconstruct_wave_heads_per_wg(sp.s);
+      slices = sp.s / hw;
+      wg_target = double(kWaveKernelWaves) / hw;
     }
     const double want = double(d->max_ctx) * d->batch * d->n_groups * slices / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
@@ -153,9 +163,10 @@ WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   w.ml = w.qt + qt_bytes;
   w.u = w.ml + align256(heads * pl.n_split * 2 * 4);
   w.bkt = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
-  const size_t bkt_bytes = pl.kernel == SplitKernel::kReconstructMfma
-                               ? align256(size_t(d->n_kv_heads) * d->head_dim * d->rank * elem)
-                               : 0;
+  const bool bkt = pl.kernel == SplitKernel::kReconstructMfma ||
+                   pl.kernel == SplitKernel::kReconstructWave;
+  const size_t bkt_bytes =
+      bkt ? align256(size_t(d->n_kv_heads) * d->head_dim * d->rank * elem) : 0;
   w.total = w.bkt + bkt_bytes;
   return w;
 }
@@ -192,6 +203,7 @@ const char* split_kernel_name(SplitKernel k) {
     case SplitKernel::kGeneric: return "split_generic_kernel";
     case SplitKernel::kAbsorbedMfma: return "split_absorbed_mfma_kernel";
     case SplitKernel::kReconstructMfma: return "split_reconstruct_mfma_kernel";
+    case SplitKernel::kReconstructWave: return "split_reconstruct_wave_kernel";
   }
   return "?";
 }
@@ -270,7 +282,8 @@ palu_status prepare_launch(const palu_attn_desc* desc, const DecodeParams& p, co
   if (desc->mode == PALU_MODE_FULL_RANK) e = launch_prescale_q(p, desc->dtype, s);
   else if (desc->mode == PALU_MODE_ABSORBED) e = launch_absorb_q(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
-  if (pl.kernel == SplitKernel::kReconstructMfma) e = launch_transpose_bk(p, desc->dtype, s);
+  if (pl.kernel == SplitKernel::kReconstructMfma || pl.kernel == SplitKernel::kReconstructWave)
+    e = launch_transpose_bk(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
   return PALU_OK;
 }
@@ -325,6 +338,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
       e = p.qbits ? launch_split_absorbed_quant(p, s) : launch_split_absorbed_mfma(p, s);
       break;
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
+    case SplitKernel::kReconstructWave: e = launch_split_reconstruct_wave(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
   if (rec >= 0) (void)hipEventRecord(g_prof.stop[rec], s);

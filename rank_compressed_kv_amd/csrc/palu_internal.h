@@ -77,7 +77,9 @@ enum class SplitKernel {
   kGeneric = 0,        // VALU, any dtype/shape in range
   kAbsorbedMfma = 1,   // bf16, absorbed keys, r in {32, 64, 128, 256}
   kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
-                         // head, r in {128, 256, 512}
+                         // head, r in {32, ..., 512}: a KV head's columns split over waves
+  kReconstructWave = 3,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
+                         // head, r in {32, 64, 128, 256}: one wave per KV head
 };
 
 const char* split_kernel_name(SplitKernel k);
@@ -112,6 +114,9 @@ bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);
 int reconstruct_heads_per_wg(int r, int s);   // KV heads per workgroup (0: not served)
 int reconstruct_waves_per_wg(int r, int s);
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
+bool reconstruct_wave_supported(const DecodeParams& p, int dtype);
+int reconstruct_wave_heads_per_wg(int s);   // KV heads (waves) per workgroup
+hipError_t launch_split_reconstruct_wave(const DecodeParams& p, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 size_t append_workspace_bytes(int B, int dm, int G, int r);
