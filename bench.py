@@ -66,6 +66,10 @@ def parse():
                     help="combined: palu_latent_append_prepare then the decode call; apart: "
                          "the append call, then a decode call forming its own operands; "
                          "overlap: the operands on a second stream beside the append")
+    ap.add_argument("--a-layout", default="out_in", choices=["out_in", "in_out"],
+                    help="memory layout of the dtype-cache step's projections a_k, a_v: "
+                         "out_in = [G*r, d_model] (the nn.Linear weight layout, one-pass cache "
+                         "write), in_out = [d_model, G*r]; the quantised steps take in_out")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the int8- and int4-latent absorbed steps")
     ap.add_argument("--sweep", action="store_true",
@@ -102,6 +106,9 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     q, bk, bv = dev(torch, t["q"]), dev(torch, t["b_k"]), dev(torch, t["b_v"])
     lens = dev(torch, t["lens"])
     x, ak, av = dev(torch, t["x"]), dev(torch, t["a_k"]), dev(torch, t["a_v"])
+    a_layout = P.PALU_A_OUT_IN if args.a_layout == "out_in" else P.PALU_A_IN_OUT
+    if a_layout == P.PALU_A_OUT_IN:
+        ak, av = ak.t().contiguous(), av.t().contiguous()
     pos = (lens - 1).to(torch.int32).contiguous()
     hk0, hv0 = dev(torch, t["h_k"]), dev(torch, t["h_v"])
     caches = [(hk0, hv0)] + [(hk0.clone(), hv0.clone()) for _ in range(n_copies - 1)]
@@ -110,7 +117,8 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
                        max_ctx=cfg.max_ctx, dtype=P.PALU_BF16 if cfg.dtype == "bf16" else P.PALU_F32,
                        mode=mode, rope_theta=theta, split_tokens=args.split_tokens)
     adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
-                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=desc.dtype)
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=desc.dtype,
+                          a_layout=a_layout)
     ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
     aws = torch.zeros(P.palu_latent_append_workspace(adesc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
@@ -641,7 +649,9 @@ def main():
                                         "decode call",
                             "apart": "cache write, then the decode call (one stream)",
                             "overlap": "cache write, with the query-side operands formed on a "
-                                       "second stream beside it, then the decode call"}[STEP],
+                                       "second stream beside it, then the decode call"}[STEP]
+                           + ("; a_k, a_v stored [G*r, d_model]" if args.a_layout == "out_in"
+                              else "; a_k, a_v stored [d_model, G*r]"),
                    "mode": args.mode, "n_split": main_res["n_split"],
                    "split_tokens": main_res["split_tokens"]},
         "latent_GBps": round(gbs_step, 1),

@@ -231,6 +231,19 @@ palu_status palu_decode_attn_i4(const palu_attn_desc* desc, const void* q, const
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* How the append's projections a_k, a_v are laid out in memory. Either way
+ * the call computes h = x a with a of shape [d_model, G*r]. */
+typedef enum palu_a_layout {
+  /* a[d_model, G*r]: entry (i, c) at i * G*r + c, the product as written */
+  PALU_A_IN_OUT = 0,
+  /* a^T[G*r, d_model]: entry (i, c) at c * d_model + i, each latent's weights
+   * contiguous (a torch.nn.Linear weight, out_features x in_features). The
+   * dtype cache write then finishes each latent in one workgroup: one pass,
+   * no workspace (size 0; the workspace pointer may be NULL). Needs d_model
+   * % 8 == 0 (SHAPE); not offered for the int8 / int4 caches (UNSUPPORTED). */
+  PALU_A_OUT_IN = 1
+} palu_a_layout;
+
 typedef struct palu_append_desc {
   int32_t batch;     /* B >= 1                                                    */
   int32_t d_model;   /* width of x, 1..65536                                      */
@@ -241,27 +254,33 @@ typedef struct palu_append_desc {
                         the cache */
   int32_t hadamard;  /* palu_latent_append_i8 / _i4 only (0 elsewhere): 1 rotates each
                         row by the Hadamard matrix before quantising */
+  int32_t a_layout;  /* palu_a_layout of a_k and a_v; PALU_A_IN_OUT (0) in a
+                        zero-initialised descriptor */
 } palu_append_desc;
 
 /* Bytes of device workspace palu_latent_append needs for this descriptor:
  * arrival counters (one int32 per 128 columns of [a_k | a_v], padded to 256
- * bytes) followed by fp32 partial sums over slices of 128 rows of d_model. */
+ * bytes) followed by fp32 partial sums over slices of 128 rows of d_model;
+ * 0 with a_layout PALU_A_OUT_IN. */
 palu_status palu_latent_append_workspace(const palu_append_desc* desc, size_t* bytes);
 
 /* Cache write of one token per sequence (answer to Q2: h = x A):
  *   h_k[b, g, pos[b], :] = x[b] . a_k[:, g*r:(g+1)*r], likewise h_v with a_v.
- *   x [B, d_model]; a_k, a_v [d_model, G*r]; h_k, h_v [B, G, L_cap, r];
+ *   x [B, d_model]; a_k, a_v [d_model, G*r] (or transposed, see
+ *   palu_a_layout); h_k, h_v [B, G, L_cap, r]; x, a_k, a_v 16-byte aligned;
  *   pos [B] int32 on the device; workspace: 16-byte aligned device memory of
  *   at least the size reported by palu_latent_append_workspace whose counter
  *   area (its first bytes, see above) is zero before the first call, e.g.
  *   allocated zeroed; every call that completes leaves it zero again and
  *   overwrites the rest. Calls that share a workspace must not overlap in
- *   time (same stream, or ordered by events). Products are summed in fp32
- *   (per 128-row slice in a fixed order, then the slices in order); a bf16
+ *   time (same stream, or ordered by events). Products are summed in fp32 in
+ *   a fixed order (PALU_A_IN_OUT: per 128-row slice, then the slices in
+ *   order; PALU_A_OUT_IN: per thread over d_model chunks 2048 apart, then the
+ *   256 threads' sums in order), so results do not depend on timing; a bf16
  *   cache stores the sum rounded to the nearest bf16 (ties to even). Rows with
  *   pos outside [0, L_cap) are left untouched. Errors: NULL, SHAPE (also
- *   G*r > 65536 or G*r not a multiple of 8), UNSUPPORTED, WORKSPACE (too small
- *   or misaligned), DEVICE. */
+ *   G*r > 65536 or G*r not a multiple of 8), UNSUPPORTED (also an unknown
+ *   a_layout), WORKSPACE (too small or misaligned), DEVICE. */
 palu_status palu_latent_append(const palu_append_desc* desc, const void* x, const void* a_k,
                                const void* a_v, void* h_k, void* h_v, const int32_t* pos,
                                void* workspace, size_t workspace_bytes, void* stream);

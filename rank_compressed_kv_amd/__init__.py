@@ -10,7 +10,8 @@ calls raise; there is no fallback.
 Layouts (row-major): q [B, Hq, d]; h_k, h_v [B, G, L_cap, r] (int8 caches
 with row scales s_k, s_v [B, G, L_cap] float32); b_k, b_v
 [G, r, s*d]; seq_lens [B] int32; out [B, Hq, d] float32; x [B, d_model];
-a_k, a_v [d_model, G*r]; pos [B] int32.
+a_k, a_v [d_model, G*r] (or [G*r, d_model] with a_layout PALU_A_OUT_IN); pos
+[B] int32.
 """
 from __future__ import annotations
 
@@ -21,7 +22,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["PaluError", "AttnDesc", "AppendDesc", "PALU_F32", "PALU_BF16",
-           "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK", "library",
+           "PALU_MODE_RECONSTRUCT", "PALU_MODE_ABSORBED", "PALU_MODE_FULL_RANK",
+           "PALU_A_IN_OUT", "PALU_A_OUT_IN", "library",
            "library_path", "full_rank_attention",
            "palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
            "palu_decode_attn_noalloc",
@@ -38,6 +40,7 @@ PALU_OK, PALU_ERR_NULL, PALU_ERR_SHAPE, PALU_ERR_UNSUPPORTED, PALU_ERR_WORKSPACE
     PALU_ERR_DEVICE = range(6)
 PALU_F32, PALU_BF16 = 0, 1
 PALU_MODE_RECONSTRUCT, PALU_MODE_ABSORBED, PALU_MODE_FULL_RANK = 0, 1, 2
+PALU_A_IN_OUT, PALU_A_OUT_IN = 0, 1
 
 EXPORTED_SYMBOLS = ("palu_decode_attn_workspace", "palu_decode_attn_plan", "palu_decode_attn",
                     "palu_decode_attn_noalloc",
@@ -76,7 +79,7 @@ class AppendDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_groups", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("hadamard", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("a_layout", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -167,11 +170,13 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    # the happy path costs a few attribute reads: a decode step makes two
+    # calls, each checking up to nine tensors, and the checks run per call
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (got {t.device})")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -179,12 +184,34 @@ def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _desc_first(validate, desc, checks, *args):
+    """Run the tensor checks; when one fails, let the library judge the
+    descriptor first, so a bad descriptor is reported as the library's error
+    (PaluError) rather than as a tensor mismatch it implies."""
+    try:
+        return checks(*args)
+    except (TypeError, ValueError):
+        validate(desc)
+        raise
+
+
+def _workspace_bytes(workspace) -> int:
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.numel() * workspace.element_size()
+
+
 _TORCH_DTYPE = {PALU_F32: torch.float32, PALU_BF16: torch.bfloat16}
 
 
 def _decode_checks(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out) -> None:
     """Shapes, dtypes and devices of a decode call's tensors against desc."""
-    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    _desc_first(palu_decode_attn_plan, desc, _decode_tensor_checks, desc, q, h_k, h_v, b_k,
+                b_v, seq_lens, out)
+
+
+def _decode_tensor_checks(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out) -> None:
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r, L = desc.n_groups, desc.rank, desc.max_ctx
     dg = (Hkv // G) * d
@@ -209,9 +236,7 @@ def palu_decode_attn(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, out, works
                      stream=None) -> None:
     """Enqueue one decode step. All tensors are checked against desc first."""
     _decode_checks(desc, q, h_k, h_v, b_k, b_v, seq_lens, out)
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _workspace_bytes(workspace)
     _check(library().palu_decode_attn(
         ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(),
         None if b_k is None else b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
@@ -233,7 +258,11 @@ def palu_decode_attn_noalloc(desc: AttnDesc, q, h_k, h_v, b_k, b_v, seq_lens, ou
 
 def _prepare_checks(desc: AttnDesc, q, b_k, workspace) -> int:
     """Shapes and dtypes of a prepare step's tensors; the workspace's bytes."""
-    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    return _desc_first(palu_decode_attn_plan, desc, _prepare_tensor_checks, desc, q, b_k,
+                       workspace)
+
+
+def _prepare_tensor_checks(desc: AttnDesc, q, b_k, workspace) -> int:
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r = desc.n_groups, desc.rank
     dt = _TORCH_DTYPE.get(desc.dtype)
@@ -242,9 +271,7 @@ def _prepare_checks(desc: AttnDesc, q, b_k, workspace) -> int:
     _need(q, "q", (B, Hq, d), dt)
     if desc.mode != PALU_MODE_FULL_RANK or b_k is not None:
         _need(b_k, "b_k", (G, r, (Hkv // G) * d), dt)
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    return workspace.numel() * workspace.element_size()
+    return _workspace_bytes(workspace)
 
 
 def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> None:
@@ -258,7 +285,18 @@ def palu_decode_attn_prepare(desc: AttnDesc, q, b_k, workspace, stream=None) -> 
 
 def _decode_quant(bits: int, desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
                   workspace, stream) -> None:
-    palu_decode_attn_plan(desc)          # the library validates the descriptor first
+    nbytes = _desc_first(palu_decode_attn_plan, desc, _quant_tensor_checks, bits, desc, q, h_k,
+                         h_v, s_k, s_v, b_k, b_v, seq_lens, out, workspace)
+    name = f"palu_decode_attn_i{bits}"
+    _check(getattr(library(), name)(
+        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), s_k.data_ptr(),
+        s_v.data_ptr(), b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
+        None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream(stream)), name)
+
+
+def _quant_tensor_checks(bits: int, desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens,
+                         out, workspace) -> int:
     B, Hq, Hkv, d = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     G, r, L = desc.n_groups, desc.rank, desc.max_ctx
     dg = (Hkv // G) * d
@@ -279,15 +317,7 @@ def _decode_quant(bits: int, desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, se
     _need(out, "out", (B, Hq, r if latent else d), torch.float32)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", (B,), torch.int32)
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
-    name = f"palu_decode_attn_i{bits}"
-    _check(getattr(library(), name)(
-        ctypes.byref(desc), q.data_ptr(), h_k.data_ptr(), h_v.data_ptr(), s_k.data_ptr(),
-        s_v.data_ptr(), b_k.data_ptr(), None if b_v is None else b_v.data_ptr(),
-        None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
-        workspace.data_ptr(), nbytes, _stream(stream)), name)
+    return _workspace_bytes(workspace)
 
 
 def palu_decode_attn_i8(desc: AttnDesc, q, h_k, h_v, s_k, s_v, b_k, b_v, seq_lens, out,
@@ -356,16 +386,22 @@ def _append_checks(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v,
                    workspace) -> int:
     """Shapes and dtypes of an append's tensors (bits 0: dtype cache, 8 / 4:
     int8 / int4 codes with scales); the workspace's bytes."""
-    # the library validates the descriptor first
-    {0: palu_latent_append_workspace, 8: palu_latent_append_i8_workspace,
-     4: palu_latent_append_i4_workspace}[bits](desc)
+    validate = {0: palu_latent_append_workspace, 8: palu_latent_append_i8_workspace,
+                4: palu_latent_append_i4_workspace}[bits]
+    return _desc_first(validate, desc, _append_tensor_checks, bits, desc, x, a_k, a_v, h_k, h_v,
+                       s_k, s_v, pos, workspace)
+
+
+def _append_tensor_checks(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
+                          workspace) -> int:
     B, dm, G, r, L = desc.batch, desc.d_model, desc.n_groups, desc.rank, desc.max_ctx
     dt = _TORCH_DTYPE.get(desc.dtype)
     if dt is None:
         raise TypeError(f"unknown dtype code {desc.dtype}")
     _need(x, "x", (B, dm), dt)
-    _need(a_k, "a_k", (dm, G * r), dt)
-    _need(a_v, "a_v", (dm, G * r), dt)
+    a_shape = (G * r, dm) if desc.a_layout == PALU_A_OUT_IN else (dm, G * r)
+    _need(a_k, "a_k", a_shape, dt)
+    _need(a_v, "a_v", a_shape, dt)
     if bits == 0:
         _need(h_k, "h_k", (B, G, L, r), dt)
         _need(h_v, "h_v", (B, G, L, r), dt)
@@ -377,9 +413,7 @@ def _append_checks(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v,
         _need(s_k, "s_k", (B, G, L), torch.float32)
         _need(s_v, "s_v", (B, G, L), torch.float32)
     _need(pos, "pos", (B,), torch.int32)
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    return workspace.numel() * workspace.element_size()
+    return _workspace_bytes(workspace)
 
 
 def _append_quant(bits: int, desc: AppendDesc, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
@@ -434,9 +468,12 @@ def attn_desc(*, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_g
 
 
 def append_desc(*, batch: int, d_model: int, n_groups: int, rank: int, max_ctx: int,
-                dtype: int, hadamard: bool = False) -> AppendDesc:
+                dtype: int, hadamard: bool = False, a_layout: int = 0) -> AppendDesc:
+    """a_layout PALU_A_IN_OUT (0): a_k, a_v [d_model, G*r]; PALU_A_OUT_IN (1):
+    [G*r, d_model], the torch.nn.Linear weight layout."""
     return AppendDesc(batch=batch, d_model=d_model, n_groups=n_groups, rank=rank,
-                      max_ctx=max_ctx, dtype=dtype, hadamard=1 if hadamard else 0)
+                      max_ctx=max_ctx, dtype=dtype, hadamard=1 if hadamard else 0,
+                      a_layout=a_layout)
 
 
 def decode_attention(q, h_k, h_v, b_k, b_v, seq_lens=None, *, n_kv_heads: int,
@@ -518,11 +555,14 @@ def full_rank_attention(q, k, v, seq_lens=None, *, scale: float = 0.0, split_tok
     return out
 
 
-def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None) -> None:
-    """Allocates the workspace with torch when it is not given."""
+def latent_append(x, a_k, a_v, h_k, h_v, pos, workspace=None, stream=None, *,
+                  a_layout: int = 0) -> None:
+    """Allocates the workspace with torch when it is not given. a_layout
+    PALU_A_OUT_IN takes a_k, a_v as [G*r, d_model]."""
     B, dm = x.shape
     _, G, L, r = h_k.shape
-    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x))
+    desc = append_desc(batch=B, d_model=dm, n_groups=G, rank=r, max_ctx=L, dtype=_dt(x),
+                       a_layout=a_layout)
     if workspace is None:
         workspace = torch.zeros(palu_latent_append_workspace(desc), dtype=torch.uint8,
                                 device=x.device)

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(DecodeParams p) {
 }
 
 // Fast form when d/8 is a power of two <= 32 (absorb_rows): workgroup (KV
-// head, sequence, 256*8/d rows of r).
+// head, sequence, kAbsRowsPer*256*8/d rows of r).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void absorb_q_vec_kernel(DecodeParams p) {
   __shared__ float qs[kAbsHeadChunk][2 * kMaxHalfDim];
@@ -404,8 +404,7 @@ __global__ __launch_bounds__(kThreads) void merge_fast_kernel(DecodeParams p) {
 
 hipError_t launch_absorb_q(const DecodeParams& p, int dtype, hipStream_t st) {
   if (absorb_carriable(absorb_args(p))) {
-    const int rows = kThreads / (p.d / 8);
-    const dim3 grid(p.Hkv, p.B, (p.r + rows - 1) / rows);
+    const dim3 grid(p.Hkv, p.B, absorb_slices(absorb_args(p), kThreads));
     if (dtype == 0) absorb_q_vec_kernel<float><<<grid, kThreads, 0, st>>>(p);
     else absorb_q_vec_kernel<uint16_t><<<grid, kThreads, 0, st>>>(p);
     return hipGetLastError();

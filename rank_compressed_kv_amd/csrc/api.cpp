@@ -468,6 +468,10 @@ palu_status palu_decode_attn_i4(const palu_attn_desc* desc, const void* q, const
 }  // extern "C"
 
 namespace {
+hipError_t launch_append_any(const AppendParams& p, int dtype, hipStream_t st) {
+  return p.a_layout == PALU_A_OUT_IN ? launch_append_t(p, dtype, st) : launch_append(p, dtype, st);
+}
+
 palu_status validate_append(const palu_append_desc* d) {
   if (!d) return fail(PALU_ERR_NULL, "descriptor is NULL");
   if (d->batch < 1 || d->d_model < 1 || d->n_groups < 1 || d->rank < 1 || d->max_ctx < 1)
@@ -478,12 +482,26 @@ palu_status validate_append(const palu_append_desc* d) {
     return fail(PALU_ERR_SHAPE, "n_groups * rank must be a multiple of 8 and <= 65536");
   if (d->dtype != PALU_F32 && d->dtype != PALU_BF16)
     return fail(PALU_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->a_layout != PALU_A_IN_OUT && d->a_layout != PALU_A_OUT_IN)
+    return fail(PALU_ERR_UNSUPPORTED, "unknown a_layout %d", d->a_layout);
+  if (d->a_layout == PALU_A_OUT_IN && d->d_model % 8)
+    return fail(PALU_ERR_SHAPE, "a_layout PALU_A_OUT_IN needs d_model %% 8 == 0 (got %d)",
+                d->d_model);
   return PALU_OK;
+}
+
+// workspace bytes of a validated descriptor's append
+size_t append_need(const palu_append_desc* d) {
+  if (d->a_layout == PALU_A_OUT_IN) return 0;
+  return append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
 }
 
 palu_status validate_append_quant(const palu_append_desc* d, int bits) {
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
+  if (d->a_layout != PALU_A_IN_OUT)
+    return fail(PALU_ERR_UNSUPPORTED, "the int%d cache write takes a_layout PALU_A_IN_OUT only",
+                bits);
   if (d->rank != 64 && d->rank != 128 && d->rank != 256)
     return fail(PALU_ERR_UNSUPPORTED, "int%d cache needs rank 64, 128 or 256 (got %d)", bits,
                 d->rank);
@@ -515,14 +533,14 @@ palu_status append_params(const palu_append_desc* d, int qbits, const void* x, c
                           const int32_t* pos, void* workspace, size_t workspace_bytes,
                           AppendParams& p) {
   const bool quant = qbits != 0;
-  if (!x || !a_k || !a_v || !h_k || !h_v || !pos || !workspace)
+  const size_t need = append_need(d);
+  if (!x || !a_k || !a_v || !h_k || !h_v || !pos || (need && !workspace))
     return fail(PALU_ERR_NULL, "x, a_k, a_v, h_k, h_v, pos and workspace must be non-NULL");
   if (quant && (reinterpret_cast<uintptr_t>(h_k) % 4 || reinterpret_cast<uintptr_t>(h_v) % 4))
     return fail(PALU_ERR_SHAPE, "int%d caches must be 4-byte aligned", qbits);
-  const size_t need = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
   if (workspace_bytes < need)
     return fail(PALU_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+  if (need && reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(PALU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   p = AppendParams{};
   p.x = x; p.a_k = a_k; p.a_v = a_v; p.h_k = h_k; p.h_v = h_v; p.pos = pos;
@@ -530,7 +548,8 @@ palu_status append_params(const palu_append_desc* d, int qbits, const void* x, c
   p.quant = qbits;
   p.hadamard = d->hadamard;
   p.s_k = s_k; p.s_v = s_v;
-  append_bind_workspace(p, workspace);
+  p.a_layout = d->a_layout;
+  if (need) append_bind_workspace(p, workspace);
   return PALU_OK;
 }
 
@@ -542,7 +561,7 @@ palu_status append(const palu_append_desc* d, int qbits, const void* x, const vo
   const palu_status st = append_params(d, qbits, x, a_k, a_v, h_k, h_v, s_k, s_v, pos,
                                        workspace, workspace_bytes, p);
   if (st != PALU_OK) return st;
-  hipError_t e = launch_append(p, d->dtype, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_append_any(p, d->dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -554,7 +573,7 @@ palu_status palu_latent_append_workspace(const palu_append_desc* d, size_t* byte
   palu_status st = validate_append(d);
   if (st != PALU_OK) return st;
   if (!bytes) return fail(PALU_ERR_NULL, "bytes is NULL");
-  *bytes = append_workspace_bytes(d->batch, d->d_model, d->n_groups, d->rank);
+  *bytes = append_need(d);
   return ok();
 }
 
@@ -641,18 +660,20 @@ palu_status palu_latent_append_prepare(const palu_append_desc* ad, int32_t qbits
   // the absorption rides in the append's launch when it can: one extra
   // workgroup per (KV head, sequence, slice of r rows)
   AbsorbArgs ab = absorb_args(dp);
+  const bool cols = ap.a_layout == PALU_A_OUT_IN;
   long units = 0;
-  if (absorb_carriable(ab)) {
-    const long rows = append_threads(qbits) / (ab.d / 8);
-    units = long(ab.Hkv) * ab.B * ((ab.r + rows - 1) / rows);
-  }
+  if (absorb_carriable(ab))
+    units = long(ab.Hkv) * ab.B *
+            absorb_slices(ab, cols ? append_t_threads() : append_threads(qbits));
+  const bool fits = cols ? units > 0 && append_t_blocks(ap) + units <= 0x7fffffffL
+                         : append_can_carry(ap, units, max_grid_y());
   const bool carry = attn->mode == PALU_MODE_ABSORBED && attn->dtype == ad->dtype &&
-                     absorb_carriable(ab) && append_can_carry(ap, units, max_grid_y());
+                     absorb_carriable(ab) && fits;
   if (carry) {
     ab.units = int32_t(units);
     ap.ab = ab;
   }
-  const hipError_t e = launch_append(ap, ad->dtype, s);
+  const hipError_t e = launch_append_any(ap, ad->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   if (!carry) {
     st = prepare_launch(attn, dp, pl, s);

@@ -69,6 +69,7 @@ struct AppendParams {
   float* s_k;         // [B, G, L]
   float* s_v;
   int32_t nslices;    // row slices of d_model (workgroup rows of the append proper)
+  int32_t a_layout;   // 0: a [dm, G*r]; 1: a^T [G*r, dm] (one-pass kernel, no workspace)
   AbsorbArgs ab;      // absorption carried by the launch (ab.units > 0)
 };
 
@@ -102,6 +103,13 @@ inline bool absorb_carriable(const AbsorbArgs& a) {
   const int ncc = a.d / 8;
   return a.d % 8 == 0 && ncc <= 32 && (ncc & (ncc - 1)) == 0;
 }
+// rows of r each thread of that form absorbs, and its workgroups (slices of
+// r) per (KV head, sequence) at `threads` threads a workgroup
+constexpr int kAbsRowsPer = 4;
+inline int absorb_slices(const AbsorbArgs& a, int threads) {
+  const int rows = threads / (a.d / 8) * kAbsRowsPer;
+  return (a.r + rows - 1) / rows;
+}
 hipError_t launch_prescale_q(const DecodeParams& p, int dtype, hipStream_t st);   // q~ = q
 hipError_t launch_split_generic(const DecodeParams& p, int dtype, int absorbed, hipStream_t st);
 bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
@@ -127,6 +135,11 @@ int append_threads(int quant);   // threads per append workgroup
 // within the device's bound max_grid_y)
 bool append_can_carry(const AppendParams& p, long units, long max_grid_y);
 hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t st);
+// the one-pass form for a^T [G*r, dm] (dtype caches): its append workgroups
+// (the carried absorption's come after them) and threads per workgroup
+long append_t_blocks(const AppendParams& p);
+int append_t_threads();
+hipError_t launch_append_t(const AppendParams& p, int dtype, hipStream_t st);
 
 // The library's static device scratch (palu_decode_attn_noalloc): its size,
 // and the device address of `device`'s copy (looked up once per device; the

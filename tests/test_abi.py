@@ -248,6 +248,41 @@ def test_append_validation(lib):
                                   misaligned, need, None) == P.PALU_ERR_WORKSPACE
 
 
+def test_append_layout_validation(lib):
+    """a_layout: 0 or 1; the transposed projection needs d_model % 8 == 0 and
+    no workspace (size 0), and is not offered for the quantised caches. Every
+    call here is rejected, so nothing is launched on the fake pointers."""
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    cols = P.append_desc(batch=8, d_model=4096, n_groups=2, rank=256, max_ctx=32768,
+                         dtype=P.PALU_BF16, a_layout=P.PALU_A_OUT_IN)
+    assert P.palu_latent_append_workspace(cols) == 0
+    for kw, status in ((dict(a_layout=2), P.PALU_ERR_UNSUPPORTED),
+                       (dict(a_layout=-1), P.PALU_ERR_UNSUPPORTED),
+                       (dict(d_model=4100), P.PALU_ERR_SHAPE)):
+        d = P.AppendDesc(**{**{f: getattr(cols, f) for f, _ in P.AppendDesc._fields_}, **kw})
+        n = ctypes.c_size_t(0)
+        assert lib.palu_latent_append_workspace(ctypes.byref(d), ctypes.byref(n)) == status
+        assert lib.palu_latent_append(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
+                                      fake, big, None) == status
+    # the row-major form still accepts d_model 4100
+    rows = P.AppendDesc(**{**{f: getattr(cols, f) for f, _ in P.AppendDesc._fields_},
+                           "d_model": 4100, "a_layout": P.PALU_A_IN_OUT})
+    assert P.palu_latent_append_workspace(rows) > 0
+    for i in range(6):                            # x, a_k, a_v, h_k, h_v, pos
+        ptrs = [fake] * 6
+        ptrs[i] = None
+        assert lib.palu_latent_append(ctypes.byref(cols), *ptrs, None, 0,
+                                      None) == P.PALU_ERR_NULL
+    for bits in (8, 4):
+        n = ctypes.c_size_t(0)
+        assert getattr(lib, f"palu_latent_append_i{bits}_workspace")(
+            ctypes.byref(cols), ctypes.byref(n)) == P.PALU_ERR_UNSUPPORTED
+        assert getattr(lib, f"palu_latent_append_i{bits}")(
+            ctypes.byref(cols), fake, fake, fake, fake, fake, fake, fake, fake, fake, big,
+            None) == P.PALU_ERR_UNSUPPORTED
+
+
 def test_append_prepare_validation(lib):
     """The combined step checks both calls' arguments before launching
     anything: the append's (per qbits) and the prepare step's. Every call here

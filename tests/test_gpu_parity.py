@@ -198,14 +198,37 @@ def test_latent_append(idx):
     """h[b, g, pos[b]] = x[b] A: bf16 rows agree with the oracle's fp32-then-bf16
     rounding except where the exact value sits within the fp32 summation error
     of a rounding midpoint; rows other than pos[b] are untouched."""
+    base = W.CONFIGS[idx]
+    _check_append(base.scaled(batch=min(base.batch, 4), max_ctx=64, ragged=None), 0)
+
+
+# the transposed projection (one-pass kernel): every config, a batch that
+# takes two passes of 8 sequences, and d_model 3072 (a partial 2048-chunk slab)
+APPEND_COLS = {f"cfg{i}": W.CONFIGS[i].scaled(batch=min(W.CONFIGS[i].batch, 4), max_ctx=64,
+                                              ragged=None) for i in (1, 2, 3, 4, 5)}
+APPEND_COLS["b11"] = W.CONFIGS[3].scaled(batch=11, max_ctx=32, ragged=None, seed=61)
+APPEND_COLS["dm3072"] = W.CONFIGS[2].scaled(batch=3, max_ctx=32, ragged=None, n_q_heads=24,
+                                            n_kv_heads=24, n_groups=6, seed=62)
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_COLS))
+def test_latent_append_transposed_projection(name):
+    """The same write from a_k, a_v stored [G*r, d_model] (PALU_A_OUT_IN)."""
+    _check_append(APPEND_COLS[name], 1)
+
+
+def _check_append(cfg, a_layout):
     import torch
     import rank_compressed_kv_amd as P
-    base = W.CONFIGS[idx]
-    cfg = base.scaled(batch=min(base.batch, 4), max_ctx=64, ragged=None)
     t = W.generate(cfg, parts=("decode", "append"))
+    print(f"[append] B={cfg.batch} d_model={cfg.d_model} G={cfg.n_groups} r={cfg.rank} "
+          f"a_layout={a_layout}", flush=True)
     hk, hv = dev(t["h_k"]), dev(t["h_v"])
     before_k = hk.clone()
-    P.latent_append(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv, dev(t["pos"]))
+    ak, av = t["a_k"], t["a_v"]
+    if a_layout:
+        ak, av = np.ascontiguousarray(ak.T), np.ascontiguousarray(av.T)
+    P.latent_append(dev(t["x"]), dev(ak), dev(av), hk, hv, dev(t["pos"]), a_layout=a_layout)
     torch.cuda.synchronize()
     G, r = cfg.n_groups, cfg.rank
     for name, cache, a in (("k", hk, t["a_k"]), ("v", hv, t["a_v"])):
@@ -266,7 +289,8 @@ def test_append_workspace_reuse():
         assert int(ws[:256].count_nonzero()) == 0
 
 
-def test_append_out_of_range_rows_skipped():
+@pytest.mark.parametrize("a_layout", [0, 1])
+def test_append_out_of_range_rows_skipped(a_layout):
     import torch
     import rank_compressed_kv_amd as P
     cfg = W.CONFIGS[3].scaled(batch=2, max_ctx=16)
@@ -274,6 +298,9 @@ def test_append_out_of_range_rows_skipped():
     hk, hv = dev(t["h_k"]), dev(t["h_v"])
     before = (hk.clone(), hv.clone())
     pos = torch.tensor([-1, 16], dtype=torch.int32, device="cuda")
-    P.latent_append(dev(t["x"]), dev(t["a_k"]), dev(t["a_v"]), hk, hv, pos)
+    ak, av = dev(t["a_k"]), dev(t["a_v"])
+    if a_layout:
+        ak, av = ak.t().contiguous(), av.t().contiguous()
+    P.latent_append(dev(t["x"]), ak, av, hk, hv, pos, a_layout=a_layout)
     torch.cuda.synchronize()
     assert torch.equal(hk, before[0]) and torch.equal(hv, before[1])

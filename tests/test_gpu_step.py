@@ -36,10 +36,18 @@ CASES = {
                          "reconstruct"),
     "bf16_full_rank": (W.CONFIGS[3].scaled(batch=2, max_ctx=256, ragged=None, seed=98,
                                            n_groups=8, rank=128), 0, "full_rank"),
+    # the projection stored transposed [G*r, d_model]: the one-pass cache
+    # write, carrying the absorption or followed by the prepare launch
+    "bf16_absorbed_cols": (W.CONFIGS[3].scaled(batch=9, max_ctx=256, ragged=None, seed=99), 0,
+                           "absorbed", 1),
+    "f32_absorbed_cols": (W.CONFIGS[1].scaled(batch=2, max_ctx=256, ragged=None, seed=100), 0,
+                          "absorbed", 1),
+    "bf16_reconstruct_cols": (W.CONFIGS[3].scaled(batch=3, max_ctx=512, ragged=None, seed=101),
+                              0, "reconstruct", 1),
 }
 
 
-def _setup(cfg, qbits, mode):
+def _setup(cfg, qbits, mode, a_layout=0):
     import torch
     import rank_compressed_kv_amd as P
     parts = ("decode", "append") + (("i8",) if qbits == 8 else ("i4",) if qbits == 4 else ())
@@ -50,7 +58,7 @@ def _setup(cfg, qbits, mode):
                        head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
                        max_ctx=cfg.max_ctx, dtype=dt, mode=mode, rope_theta=theta)
     adesc = P.append_desc(batch=cfg.batch, d_model=cfg.d_model, n_groups=cfg.n_groups,
-                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=dt)
+                          rank=cfg.rank, max_ctx=cfg.max_ctx, dtype=dt, a_layout=a_layout)
     # the appended token is the last of each sequence's context
     pos = np.minimum(t["pos"], cfg.max_ctx - 1).astype(np.int32)
     lens = (pos + 1).astype(np.int32)
@@ -62,7 +70,10 @@ def _setup(cfg, qbits, mode):
                  dev(t["sk_i4"]), dev(t["sv_i4"])]
     else:
         cache = [dev(t["h_k"]), dev(t["h_v"]), None, None]
-    ops = dict(x=dev(t["x"]), a_k=dev(t["a_k"]), a_v=dev(t["a_v"]), pos=dev(pos),
+    ak, av = t["a_k"], t["a_v"]
+    if a_layout:
+        ak, av = np.ascontiguousarray(ak.T), np.ascontiguousarray(av.T)
+    ops = dict(x=dev(t["x"]), a_k=dev(ak), a_v=dev(av), pos=dev(pos),
                q=dev(t["q"]), b_k=dev(t["b_k"]), b_v=dev(t["b_v"]), lens=dev(lens))
     wsz = P.palu_decode_attn_workspace(desc)
     asz = P.palu_latent_append_workspace(adesc)
@@ -83,10 +94,12 @@ def _decode(P, qbits, desc, ops, cache, out, ws):
 def test_step_matches_separate_calls(name):
     import torch
     import rank_compressed_kv_amd as P
-    cfg, qbits, mode = CASES[name]
-    t, desc, adesc, cache0, ops, wsz, asz, fresh, pos, lens, theta = _setup(cfg, qbits, mode)
-    print(f"[step] {name} qbits={qbits} mode={mode} B={cfg.batch} pos={pos.tolist()}",
-          flush=True)
+    cfg, qbits, mode = CASES[name][:3]
+    a_layout = CASES[name][3] if len(CASES[name]) > 3 else 0
+    t, desc, adesc, cache0, ops, wsz, asz, fresh, pos, lens, theta = _setup(cfg, qbits, mode,
+                                                                             a_layout)
+    print(f"[step] {name} qbits={qbits} mode={mode} a_layout={a_layout} B={cfg.batch} "
+          f"pos={pos.tolist()}", flush=True)
     bk = None if mode == "full_rank" else ops["b_k"]
     shape = (cfg.batch, cfg.n_q_heads, cfg.head_dim)
 
