@@ -91,6 +91,35 @@ def dev(torch, a):
 
 STEP = "combined"   # set by --step
 
+_SPIN_CYCLES_PER_US = None
+
+
+def queue_behind_spin(torch, stream, us):
+    """Enqueue a GPU spin of about `us` microseconds on `stream` (torch's
+    sleep kernel, its clock rate measured once with events). A timed loop's
+    start event is recorded after it, so while the GPU spins the host queues
+    the loop's calls and the events time the GPU's back-to-back execution,
+    not the host's first submissions."""
+    global _SPIN_CYCLES_PER_US
+    if _SPIN_CYCLES_PER_US is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)                     # warm the kernel up
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_US = 2_000_000 / max(1.0, a.elapsed_time(b) * 1e3)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
+
+
+def host_us(fn, n):
+    """Host time of n calls of fn(i) (queued, not waited for), per call."""
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    return (time.perf_counter() - t0) / max(1, n) * 1e6
+
 
 def step_setup(torch, P, desc):
     """The prepared copy of a descriptor (decode calls after the query-side
@@ -147,14 +176,19 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
 
     # the first step's output is kept for the sampled parity check (the append
     # has written row len-1 of copy 0)
+    def decode(i):
+        hk, hv = caches[i % n_copies]
+        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+
     step(0)
     torch.cuda.synchronize()
     first_out = out.clone()
-    for i in range(args.warmup):
-        step(i + 1)
+    step_host = host_us(lambda i: step(i + 1), max(1, args.warmup))
     torch.cuda.synchronize()
-    # timed loop 1: the steps alone (the throughput figure)
+    # timed loop 1: the steps alone (the throughput figure), queued behind a
+    # spin long enough for the host to submit them all
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_behind_spin(torch, stream, 1.5 * args.steps * step_host + 500)
     e0.record(stream)
     for i in range(args.steps):
         step(i)
@@ -163,10 +197,12 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     total_ms = e0.elapsed_time(e1)
     # timed loop 1b: the decode call alone (no cache write), the quantity the
     # pages compare with the uncompressed baseline
+    call_host = host_us(decode, max(1, args.warmup))
+    torch.cuda.synchronize()
+    queue_behind_spin(torch, stream, 1.5 * args.steps * call_host + 500)
     e0.record(stream)
     for i in range(args.steps):
-        hk, hv = caches[i % n_copies]
-        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+        decode(i)
     e1.record(stream)
     torch.cuda.synchronize()
     decode_ms = e0.elapsed_time(e1)
@@ -194,6 +230,7 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
         kern_ms, kern_n = P.palu_profile_end()
     return dict(ms_per_step=total_ms / args.steps, kernel_ms=kern_ms / max(1, kern_n),
                 decode_ms=decode_ms / args.steps, calls_us=calls_us,
+                host_us_per_step=step_host, host_us_per_call=call_host,
                 kernel=kname, n_split=n_split, split_tokens=split_tokens,
                 out=first_out.cpu().numpy())
 
@@ -261,6 +298,9 @@ def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     res = {}
     for name, fn in (("step", step), ("decode", decode)):
+        h = host_us(fn, max(1, args.warmup))
+        torch.cuda.synchronize()
+        queue_behind_spin(torch, stream, 1.5 * args.steps * h + 500)
         e0.record(stream)
         for i in range(args.steps):
             fn(i)
@@ -303,10 +343,10 @@ def time_full_rank(torch, P, W, cfg, t, args):
     call(0)
     torch.cuda.synchronize()
     first = out.clone()
-    for i in range(args.warmup):
-        call(i + 1)
+    h = host_us(lambda i: call(i + 1), max(1, args.warmup))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_behind_spin(torch, stream, 1.5 * args.steps * h + 500)
     e0.record(stream)
     for i in range(args.steps):
         call(i)
@@ -379,12 +419,13 @@ def granularity_sweep(torch, P, W, cfg, args):
             out = torch.empty(c.batch, c.n_q_heads, c.head_dim, dtype=torch.float32, device="cuda")
             _, _, kname = P.palu_decode_attn_plan(desc)
             stream = torch.cuda.current_stream()
-            for _ in range(3):
-                P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+            h = host_us(lambda i: P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws,
+                                                     stream), 3)
             torch.cuda.synchronize()
             n = max(5, args.steps // 4)
             P.palu_profile_begin(n)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            queue_behind_spin(torch, stream, 1.5 * n * h + 500)
             e0.record(stream)
             for _ in range(n):
                 P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
@@ -659,8 +700,13 @@ def main():
         "roofline": roofline(cfg, t, args.mode, main_res, lat_bytes, kern_gbs, traffic),
         "full_rank_baseline": full,
         "quantised_latents": quant,
+        "timing": "each timed loop is queued behind a GPU spin recorded before its start "
+                  "event, so the events time back-to-back GPU execution; host_us_* is the "
+                  "binding's submission time per step or call",
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                       "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
+                      "host_us_per_step": round(r["host_us_per_step"], 1),
+                      "host_us_per_decode_call": round(r["host_us_per_call"], 1),
                       "decode_call_us_spread": {
                           "mean": round(float(np.mean(r["calls_us"])), 2),
                           "median": round(float(np.median(r["calls_us"])), 2),
