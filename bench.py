@@ -72,8 +72,14 @@ def parse():
                          "write), in_out = [d_model, G*r]; the quantised steps take in_out")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the int8- and int4-latent absorbed steps")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the head-grouping sweep (s = 1, 2, 4, 8 KV heads per "
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the HBM read-stream probe")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the rebuilt-key rows of the other workloads (2, 4, 5)")
+    ap.add_argument("--no-oracle-configs", action="store_true",
+                    help="skip timing the oracle per workload and key mode")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false",
+                    help="skip the head-grouping sweep (s = 1, 2, 4, 8 KV heads per "
                          "group at 75%% key compression) and add it to the JSON line")
     return ap.parse_args()
 
@@ -391,6 +397,140 @@ def roofline(cfg, t, mode, res, lat_bytes, kern_gbs, traffic):
     return rec
 
 
+def reconstruct_configs(torch, P, W, O, args, which=(2, 4, 5)):
+    """The rebuilt-key decode call at the other workloads' full sizes (MHA
+    Llama-2-7B, the 128K-token outlier context, the ragged J-LRD batch): call
+    time queued behind a spin, kernel time from the library's events, each
+    against its roofline, and two sampled (b, h) outputs against the oracle.
+    Caches are rotated over enough copies to defeat the Infinity Cache."""
+    rows = {}
+    for c in which:
+        cfg = W.CONFIGS[c]
+        t = W.generate(cfg, parts=("decode",))
+        lat_bytes = W.latent_bytes(cfg, t["lens"])
+        tokens = int(np.sum(t["lens"], dtype=np.int64))
+        flops = 2.0 * tokens * cfg.n_groups * cfg.rank * cfg.group_dim
+        n_copies = min(16, max(1, int(math.ceil(ROTATE_BYTES / lat_bytes))))
+        q, bk, bv, lens = (dev(torch, t[k]) for k in ("q", "b_k", "b_v", "lens"))
+        hk0, hv0 = dev(torch, t["h_k"]), dev(torch, t["h_v"])
+        caches = [(hk0, hv0)] + [(hk0.clone(), hv0.clone()) for _ in range(n_copies - 1)]
+        desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                           head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
+                           max_ctx=cfg.max_ctx, dtype=P.PALU_BF16, mode="reconstruct",
+                           rope_theta=cfg.rope_theta)
+        ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+        out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32,
+                          device="cuda")
+        n_split, split_tokens, kname = P.palu_decode_attn_plan(desc)
+        stream = torch.cuda.current_stream()
+
+        def call(i):
+            hk, hv = caches[i % n_copies]
+            P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
+
+        call(0)
+        torch.cuda.synchronize()
+        first = out.cpu().numpy()
+        n = max(5, args.steps // 2)
+        h = host_us(call, 3)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_behind_spin(torch, stream, 1.5 * n * h + 500)
+        e0.record(stream)
+        for i in range(n):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        call_us = e0.elapsed_time(e1) / n * 1e3
+        P.palu_profile_begin(n)
+        for i in range(n):
+            call(i)
+        torch.cuda.synchronize()
+        kms, kn = P.palu_profile_end()
+        kus = kms / max(1, kn) * 1e3
+        del caches, hk0, hv0
+        torch.cuda.empty_cache()
+        rng = np.random.default_rng(c)
+        pairs = [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_q_heads)))
+                 for _ in range(2)]
+        want = O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"],
+                                  rope_theta=cfg.rope_theta, select=pairs)
+        idx = tuple(np.array(pairs).T)
+        d = first.astype(np.float64)[idx] - want[idx]
+        tf = flops / (kus * 1e-6) / 1e12
+        gbs = lat_bytes / (kus * 1e-6) / 1e9
+        mfma_bound = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > lat_bytes / (HBM_PEAK_GBS * 1e9)
+        rows[f"cfg{c}"] = {
+            "workload": f"{cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} "
+                        f"d={cfg.head_dim} G={cfg.n_groups} r={cfg.rank} ctx={cfg.max_ctx}"
+                        + (" ragged" if cfg.ragged else ""),
+            "kernel": kname, "n_split": n_split, "split_tokens": split_tokens,
+            "us_per_decode_call": round(call_us, 2), "kernel_us": round(kus, 2),
+            "latent_bytes": lat_bytes, "rebuild_flops": flops,
+            "latent_GBps_kernel": round(gbs, 1), "rebuild_TFLOPs": round(tf, 1),
+            "roofline": {"bound": "mfma" if mfma_bound else "hbm",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS if mfma_bound
+                                       else gbs / HBM_PEAK_GBS, 4),
+                         "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)},
+            "sampled_parity_max_abs": float(np.abs(d).max()),
+            "sampled_parity_rel_l2": float(np.linalg.norm(d) / np.linalg.norm(want[idx]))}
+        print(f"[bench] cfg{c} reconstruct: {call_us:.1f} us/call, kernel {kname} {kus:.1f} us",
+              file=sys.stderr, flush=True)
+        del t
+    return rows
+
+
+def oracle_per_config(O, W, budget_s):
+    """The oracle timed on the host per (workload, key mode): one (b, head
+    group) pair at full context per configuration, scaled to a whole step;
+    plus the whole of the tiny workload with one BLAS thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threadpool_limits, cores = None, os.cpu_count() or 1
+    rows = {}
+    for c, cfg in W.CONFIGS.items():
+        # one sequence is enough: the oracle works pair by pair
+        small = cfg.scaled(batch=1)
+        t = W.generate(small, parts=("decode",))
+        hpg = cfg.n_q_heads // cfg.n_groups
+        for mode in cfg.modes:
+            theta = cfg.rope_theta if mode == "reconstruct" else 0.0
+            sel = [(0, i) for i in range(hpg)]
+            t0 = time.perf_counter()
+            O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"],
+                               rope_theta=theta, select=sel)
+            el = time.perf_counter() - t0
+            # a ragged workload's pairs cost in proportion to their length:
+            # scale the sampled pair to the mean length of the range
+            n0 = int(t["lens"][0])
+            mean_len = (cfg.ragged[0] + cfg.ragged[1]) / 2 if cfg.ragged else n0
+            pairs = cfg.batch * cfg.n_groups
+            per_step = el * pairs * mean_len / max(1, n0)
+            rows[f"cfg{c}_{mode}"] = {"s_per_pair": round(el, 4), "pair_len": n0,
+                                      "pairs_per_step": pairs,
+                                      "steps_per_s": round(1.0 / per_step, 6)}
+            if el > budget_s:
+                break
+    one = None
+    if threadpool_limits is not None:
+        cfg = W.CONFIGS[1]
+        t = W.generate(cfg)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for mode in cfg.modes:
+                O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"],
+                                   rope_theta=0.0)
+            el = time.perf_counter() - t0
+        one = {"cores": 1, "s_per_step_both_modes": round(el, 4),
+               "steps_per_s_per_mode": round(len(cfg.modes) / el, 2)}
+    return {"cores": int(cores), "kind": "oracle", "per_config": rows, "tiny_one_thread": one,
+            "what": "one (batch, head-group) pair at full context per workload and key mode, "
+                    "fp64 NumPy; steps/s = 1 / (seconds per pair x pairs per step)"}
+
+
 def granularity_sweep(torch, P, W, cfg, args):
     """Decode-call time per head grouping at 75% key compression (r = D_g / 4):
     M-LRD s = 1 ... J-LRD s = Hkv, same total latent bytes; key-rebuild FLOPs
@@ -448,6 +588,51 @@ def granularity_sweep(torch, P, W, cfg, args):
         del q, bk, bv, lens, hk, hv
         torch.cuda.empty_cache()
     return rows
+
+
+def read_stream_probe(torch):
+    """The HBM read rate a plain streaming kernel reaches here (libpalu_probe:
+    16-byte non-temporal loads, one contiguous chunk per workgroup): the best
+    of a few launch shapes over a 1 GiB buffer, ten launches each."""
+    import ctypes
+    path = os.path.join(ROOT, "rank_compressed_kv_amd", "libpalu_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.palu_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p]
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(65536, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (256, 512, 1024, 2048):
+        for threads in (256, 512):
+            for inflight in (4, 8, 16):
+                call = lambda: lib.palu_probe_read_stream(buf.data_ptr(), nbytes, out.data_ptr(),
+                                                          grid, threads, inflight,
+                                                          stream.cuda_stream)
+                if call() != 0:
+                    continue
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(10):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                gbs = 10 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if best is None or gbs > best["GBps"]:
+                    best = {"GBps": round(gbs, 1), "grid": grid, "threads": threads,
+                            "loads_in_flight_per_thread": inflight}
+    del buf, out
+    torch.cuda.empty_cache()
+    if best:
+        best["frac_of_published_peak"] = round(best["GBps"] / HBM_PEAK_GBS, 4)
+        best["what"] = ("1 GiB read once per launch with 16-byte non-temporal loads, "
+                        "best launch shape of 24")
+    return best
 
 
 def oracle_appended(O, cfg, t, caches, rot=False, bits=8):
@@ -718,8 +903,17 @@ def main():
                       "sampled_parity_rel_l2": parity[m][1]}
                   for m, r in results.items()},
     }
+    if not args.no_probe:
+        probe = read_stream_probe(torch)
+        if probe:
+            probe["main_kernel_frac_of_probe"] = round(kern_gbs / probe["GBps"], 4)
+        line["read_stream_probe"] = probe
+    if not args.no_configs:
+        line["reconstruct_other_workloads"] = reconstruct_configs(torch, P, W, O, args)
     if args.sweep:
         line["granularity_sweep"] = granularity_sweep(torch, P, W, cfg, args)
+    if not args.no_cpu_baseline and not args.no_oracle_configs:
+        line["oracle_per_workload"] = oracle_per_config(O, W, args.cpu_seconds)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(O, cfg, t, args.mode, args.cpu_seconds)
         line["gpu_over_cpu_baseline"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
