@@ -72,6 +72,10 @@ def parse():
                          "write), in_out = [d_model, G*r]; the quantised steps take in_out")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the int8- and int4-latent absorbed steps")
+    ap.add_argument("--profile-calls", type=int, default=0,
+                    help="profiling run: make this many decode calls of --config in --mode "
+                         "(default split plan, no cache rotation) and exit; for rocprofv3 "
+                         "counter passes")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM read-stream probe")
     ap.add_argument("--no-configs", action="store_true",
@@ -590,6 +594,29 @@ def granularity_sweep(torch, P, W, cfg, args):
     return rows
 
 
+def profile_calls(torch, P, W, cfg, args):
+    """The decode call of one workload, made --profile-calls times on one
+    cache (for counter passes: every call of the main kernel is the same
+    work); prints the plan."""
+    t = W.generate(cfg, parts=("decode",))
+    theta = cfg.rope_theta if args.mode == "reconstruct" else 0.0
+    q, bk, bv, lens = (dev(torch, t[k]) for k in ("q", "b_k", "b_v", "lens"))
+    hk, hv = dev(torch, t["h_k"]), dev(torch, t["h_v"])
+    desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
+                       max_ctx=cfg.max_ctx, dtype=P.PALU_BF16 if cfg.dtype == "bf16" else P.PALU_F32,
+                       mode=args.mode, rope_theta=theta, split_tokens=args.split_tokens)
+    ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    for _ in range(args.profile_calls):
+        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws)
+    torch.cuda.synchronize()
+    ns, st, kname = P.palu_decode_attn_plan(desc)
+    print(f"[profile] cfg{args.config} {cfg.name} {args.mode}: {args.profile_calls} calls of "
+          f"{kname}, n_split {ns}, split_tokens {st}, latent bytes "
+          f"{W.latent_bytes(cfg, t['lens'])}", flush=True)
+
+
 def read_stream_probe(torch):
     """The HBM read rate a plain streaming kernel reaches here (libpalu_probe:
     16-byte non-temporal loads, one contiguous chunk per workgroup): the best
@@ -753,6 +780,9 @@ def main():
     torch.cuda.set_device(0)
 
     cfg = W.CONFIGS[args.config]
+    if args.profile_calls:
+        profile_calls(torch, P, W, cfg, args)
+        return
     t = W.generate(cfg, parts=("decode", "append"))
     # the append writes row len-1, so the step attends over exactly len rows
     lat_bytes = W.latent_bytes(cfg, t["lens"])

@@ -115,6 +115,8 @@ Plan make_plan(const palu_attn_desc* d) {
     pl.kernel = SplitKernel::kReconstructMfma;
   if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_wave_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kReconstructWave;
+  if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_wide_supported(sp, d->dtype))
+    pl.kernel = SplitKernel::kReconstructWide;
   int st = d->split_tokens;
   if (st == 0) {
     // Aim at a fixed number of (split, b, g) units: 256 for the generic
@@ -137,6 +139,10 @@ Plan make_plan(const palu_attn_desc* d) {
       const int hw = reconstruct_wave_heads_per_wg(sp.s);
       slices = sp.s / hw;
       wg_target = double(kWaveKernelWaves) / hw;
+    }
+    if (pl.kernel == SplitKernel::kReconstructWide) {
+      slices = sp.s / 4;
+      wg_target = double(kWaveKernelWaves) / 4;
     }
     const double want = double(d->max_ctx) * d->batch * d->n_groups * slices / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
@@ -164,7 +170,8 @@ WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   w.u = w.ml + align256(heads * pl.n_split * 2 * 4);
   w.bkt = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
   const bool bkt = pl.kernel == SplitKernel::kReconstructMfma ||
-                   pl.kernel == SplitKernel::kReconstructWave;
+                   pl.kernel == SplitKernel::kReconstructWave ||
+                   pl.kernel == SplitKernel::kReconstructWide;
   const size_t bkt_bytes =
       bkt ? align256(size_t(d->n_kv_heads) * d->head_dim * d->rank * elem) : 0;
   w.total = w.bkt + bkt_bytes;
@@ -204,6 +211,7 @@ const char* split_kernel_name(SplitKernel k) {
     case SplitKernel::kAbsorbedMfma: return "split_absorbed_mfma_kernel";
     case SplitKernel::kReconstructMfma: return "split_reconstruct_mfma_kernel";
     case SplitKernel::kReconstructWave: return "split_reconstruct_wave_kernel";
+    case SplitKernel::kReconstructWide: return "split_reconstruct_wide_kernel";
   }
   return "?";
 }
@@ -282,7 +290,8 @@ palu_status prepare_launch(const palu_attn_desc* desc, const DecodeParams& p, co
   if (desc->mode == PALU_MODE_FULL_RANK) e = launch_prescale_q(p, desc->dtype, s);
   else if (desc->mode == PALU_MODE_ABSORBED) e = launch_absorb_q(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
-  if (pl.kernel == SplitKernel::kReconstructMfma || pl.kernel == SplitKernel::kReconstructWave)
+  if (pl.kernel == SplitKernel::kReconstructMfma || pl.kernel == SplitKernel::kReconstructWave ||
+      pl.kernel == SplitKernel::kReconstructWide)
     e = launch_transpose_bk(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
   return PALU_OK;
@@ -339,6 +348,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
       break;
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     case SplitKernel::kReconstructWave: e = launch_split_reconstruct_wave(p, s); break;
+    case SplitKernel::kReconstructWide: e = launch_split_reconstruct_wide(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
   if (rec >= 0) (void)hipEventRecord(g_prof.stop[rec], s);

@@ -53,118 +53,20 @@
 // ring of four LDS buffers; rows past the split's end are
 // clamped to its last valid row and masked. One workgroup barrier per tile
 // (LDS only, so the loads stay in flight across it).
-#include <math.h>
-
-#include <utility>
-
-#include "device_util.h"
-#include "palu_internal.h"
+#include "reconstruct_wave_util.h"
 
 namespace palu {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+using namespace wave;
 
-constexpr int kTile = 16;          // tokens per tile
-constexpr int kD = 128;            // head dim
 constexpr int kNBuf = 4;           // LDS tile buffers
-constexpr int kAnchor = 32;        // tiles between exact cos/sin evaluations
-constexpr float kLazy = 8.0f;      // log2 units: p <= 2^8 between rescales
-constexpr float kKeyScale = 1.0f / 256.0f;   // rebuilt keys enter fp16 times 2^-8
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, sizeof(r));
-  return r;
-}
-
-// a ~ hi + lo with hi = bf16(a) and lo = bf16(a - hi), both nearest-even, for a
-// pair of values: about 16 significant bits in two bf16 terms
-__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
-  const float ah = __uint_as_float(hi << 16), bh = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a - ah, b - bh}, bf16x2));
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, halfx2));
-}
-
-// max and sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
-// of a 16x16 MFMA result) with the gfx950 lane-swap moves: a swap of a
-// register with itself leaves each lane's own value in one result and its
-// partner's in the other, which is all a symmetric reduction needs
-__device__ __forceinline__ float max_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-// x + its value in lane l ^ 16 (lane groups 0 + 1 and 2 + 3)
-__device__ __forceinline__ float add_pair_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1, fully
-// expanded whatever the body's size (the slot schedule below relies on it).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Keeps a register value in an AGPR: an empty asm statement whose operand
-// must live there. Matrix-core instructions read their A and B operands from
-// AGPRs directly, so B_k^T (128 registers at rank 128) stays in the AGPRs and
-// the VGPRs are left to everything else; no instruction is emitted.
-__device__ __forceinline__ void hold_in_agpr(u32x4& v) { asm volatile("" : "+a"(v)); }
-
-// the transposing LDS read: see the header comment
-__device__ __forceinline__ short4v read_tr16(const char* p) {
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  return __builtin_bit_cast(short4v, v);
-}
-
-// K tile rows padded by 16 B (the 16 rows of an operand read start on
-// different banks); V tile rows padded by 32 B (the four rows of a 16-lane
-// transposing read cover all 32 banks)
-template <int R>
-constexpr int kKStride = 2 * R + 16;
-template <int R>
-constexpr int kVStride = 2 * R + 32;
 
 template <int R>
 struct Smem {
   char k[kNBuf][kTile * kKStride<R>];
   char v[kNBuf][kTile * kVStride<R>];
-  // 2^-8 (cos, sin) of t * omega_f for the 16 tokens t of a tile, f < 64, two
-  // tiles: rtab[buf][f / 2][t - tok0][f % 2]; a lane's frequencies f, f + 1 are
-  // one 16-byte row and the 16 tokens' rows are contiguous
-  float2 rtab[2][32][kTile][2];
-  // (cos, sin) of 16 * omega_f: the rotation of a frequency over one tile
-  float2 rstep[64];
-  // omega_f / (2 pi), for the exact evaluations
-  double orev[64];
+  RotTable rot;
   // q of each wave's query heads as the score MFMA's B operand (fp16), lane
   // order: qop[wave][m][lane]
   uint4 qop[4][4][64];
@@ -191,7 +93,6 @@ template <int R, int HW, bool kShared>
 __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(DecodeParams p) {
   constexpr int kThreads = 64 * HW;
   constexpr int kPieces = (2 * R + kThreads - 1) / kThreads;   // 16-B pieces per matrix
-  constexpr int kRE = 1024 / kThreads;                          // rotation-table entries
   constexpr int kC = R / 32;                                    // 32-latent key chunks
   constexpr int kRB = R / 16;                                   // 16-latent value blocks
   const int nslice = p.s / HW;
@@ -212,108 +113,17 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   __shared__ Smem<R> sm;
 
   // ---- operands held for the whole split -----------------------------------
-  // B_k^T as the key MFMA's A operand: lane (ln, kb) of block blk, chunk c
-  // holds column 16 blk + ln, latents 32 c + 8 kb .. +8
-  const uint16_t* Bt = static_cast<const uint16_t*>(p.bkt) +
-                       (static_cast<size_t>(g) * p.Dg + kvh * kD) * R;
+  // B_k^T as the key MFMA's A operand (column 16 blk + ln, latents 32 c + 8 kb
+  // .. +8 in lane (ln, kb) of block blk, chunk c), from the transposed copy
   u32x4 bt[8][kC];
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk)
-#pragma unroll
-    for (int c = 0; c < kC; ++c)
-      bt[blk][c] = *reinterpret_cast<const u32x4*>(Bt + static_cast<size_t>(16 * blk + ln) * R +
-                                                   32 * c + 8 * kb);
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk)
-#pragma unroll
-    for (int c = 0; c < kC; ++c) hold_in_agpr(bt[blk][c]);
-  // q as the score MFMA's B operand, fp16: lane (ln = query head, kb), MFMA m
-  // (block pair m, m + 4) holds columns 16 m + 4 kb + j and 16 (m + 4) + 4 kb + j,
-  // j < 4, scaled by a power of two that puts the head's largest |q| in
-  // [256, 512) (exact; the factor goes back into the head's score scale)
-  const bool qvalid = ln < gqa;
-  float hscale;                                          // log2-unit score factor of head ln
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           (static_cast<size_t>(b) * p.Hq + head0 + (qvalid ? ln : 0)) * kD;
-    uint2 qw[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      qw[2 * m] = *reinterpret_cast<const uint2*>(qrow + 16 * m + 4 * kb);
-      qw[2 * m + 1] = *reinterpret_cast<const uint2*>(qrow + 16 * (m + 4) + 4 * kb);
-    }
-    float qf[4][8];
-    float qmax = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint2 w = qw[2 * m + h];
-        const float v[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          qf[m][4 * h + j] = qvalid ? v[j] : 0.f;
-          qmax = fmaxf(qmax, fabsf(qf[m][4 * h + j]));
-        }
-      }
-    qmax = max_groups(qmax);
-    int ex = 0;
-    (void)frexpf(qmax, &ex);                             // qmax = mant * 2^ex, mant in [0.5, 1)
-    const float qs = qmax > 0.f ? ldexpf(1.f, 9 - ex) : 1.f;
-    hscale = p.scale_log2 * (qmax > 0.f ? ldexpf(1.f, ex - 1) : 256.f);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = pack_f16x2(qf[m][2 * j] * qs, qf[m][2 * j + 1] * qs);
-      sm.qop[wave][m][lane] = uint4{u[0], u[1], u[2], u[3]};
-    }
-  }
+  load_bkt<kC>(bt, static_cast<const uint16_t*>(p.bkt) + (static_cast<size_t>(g) * p.Dg + kvh * kD) * R,
+               R, 0, ln, kb);
+  const float hscale = q_operand(p, b, head0, gqa, ln, kb, lane, sm.qop[wave]);
 
-  // rotation table: thread entry e is (token gt = idx % 16, frequency
-  // f = idx / 16) with idx = tid + e * kThreads. Every kAnchor tiles the
-  // entries are evaluated from the angle; in between a tile's entry is the
-  // previous tile's entry (read back from the table) times the 16-position
-  // step of its frequency, one exact complex product. The table holds
-  // 2^-8 (cos, sin); without rotary embedding, (2^-8, 0).
-  // Entry e of a thread has frequency f = tid / 16 + e * kThreads / 16 and
-  // token tid % 16, so its slot is one per-thread offset plus e times a
-  // constant stride (entries kThreads apart are kThreads / 32 rows of
-  // rtab[.][f / 2] apart).
-  const bool rope = p.rope != 0;
-  if (tid < 64) {
-    float c = 1.f, sn = 0.f;
-    if (rope) rope_cos_sin(p.omega_rev[tid], kTile, c, sn);
-    sm.rstep[tid] = float2{c, sn};
-    sm.orev[tid] = p.omega_rev[tid];
-  }
+  // the rotation table (shared by the waves; filled by all threads)
+  Rot<kThreads> rot(sm.rot, tid, p.rope != 0);
+  rot.init(p, tid);
   barrier_lds();                                         // rstep and orev before any use
-  const int f0 = tid >> 4, gt = tid & 15;
-  constexpr int kFStep = kThreads / 16;                 // frequency step between entries
-  auto rslot = [&](int buf) { return &sm.rtab[buf][f0 >> 1][gt][f0 & 1]; };
-  constexpr int kSlotStep = (kFStep / 2) * kTile * 2;   // float2 elements between entries
-  auto rope_exact = [&](int tok0, int buf) {
-    float2* dst = rslot(buf);
-#pragma unroll
-    for (int e = 0; e < kRE; ++e) {
-      float c = 1.f, sn = 0.f;
-      if (rope) rope_cos_sin(sm.orev[f0 + e * kFStep], tok0 + gt, c, sn);
-      dst[e * kSlotStep] = float2{c * kKeyScale, sn * kKeyScale};
-    }
-  };
-  // the recurrence step of the table of tile nt into buffer nt & 1 from tile
-  // nt - 1's (buffer (nt - 1) & 1, read-only meanwhile: nothing rewrites it
-  // before the next barrier); tiles at anchors are then overwritten exactly
-  auto rope_step = [&](int nt) {
-    float2* dst = rslot(nt & 1);
-    const float2* src = rslot((nt - 1) & 1);
-#pragma unroll
-    for (int e = 0; e < kRE; ++e) {
-      const float2 o = src[e * kSlotStep];
-      const float2 st = sm.rstep[f0 + e * kFStep];
-      dst[e * kSlotStep] = float2{o.x * st.x - o.y * st.y, o.y * st.x + o.x * st.y};
-    }
-  };
 
   // ---- softmax state of query head ln (lanes ln >= gqa carry a zero query
   // and are never written out)
@@ -450,7 +260,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   put(1, stg[0][0], stg[0][1]);
 #pragma unroll
   for (int i = 0; i < kStages; ++i) fetch(s0 + (2 + i) * kTile, stg[i][0], stg[i][1]);
-  rope_exact(s0, 0);
+  rot.exact(s0, 0);
   barrier_lds();
   floatx4 kx[8], ky[8];
   keys(0, kx);
@@ -474,8 +284,8 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
     float mx = 0.f;
     auto rows = [&](int blk) {
-      rt[blk][0] = *reinterpret_cast<const float4*>(&sm.rtab[it & 1][8 * blk + 2 * kb][ln][0]);
-      rt[blk][1] = *reinterpret_cast<const float4*>(&sm.rtab[it & 1][8 * blk + 2 * kb + 1][ln][0]);
+      rt[blk][0] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb][ln][0]);
+      rt[blk][1] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb + 1][ln][0]);
     };
     auto rotate = [&](int blk, int i) {                 // pair (f, f + 64), f = 16 blk + 4 kb + i
       const float4 r = rt[blk][i / 2];
@@ -525,7 +335,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
                        pack_f16x2(cur[m + 4][0], cur[m + 4][1]),
                        pack_f16x2(cur[m + 4][2], cur[m + 4][3])};
       } else if constexpr (w == kRope) {
-        rope_step(it + 1);
+        rot.step(it + 1);
       } else if constexpr (w >= kScore0 && w < kScore0 + 4) {   // S[token 4 kb + i][head ln]
         constexpr int m = w - kScore0;
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a16[m]),
@@ -558,7 +368,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
       static_for<w1 - w0>([&](auto J) { item(std::integral_constant<int, kOrder[w0 + J]>{}); });
       __builtin_amdgcn_sched_barrier(0);
     });
-    if ((it + 1) % kAnchor == 0) rope_exact(s0 + (it + 1) * kTile, (it + 1) & 1);
+    if ((it + 1) % kAnchor == 0) rot.exact(s0 + (it + 1) * kTile, (it + 1) & 1);
     sc_prev = sc;
     mx_prev = mx;
     barrier_lds();
