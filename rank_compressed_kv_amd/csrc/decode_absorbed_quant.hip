@@ -17,10 +17,14 @@
 //     16x16x32 for the scores (16 tokens x 16 heads over 32 latents) and for
 //     the values (r x 16 heads over 32 tokens);
 //   - a block's key scales multiply its scores, its value scales fold into the
-//     weights (p_t s_t; the running sum l keeps p_t). q~ (hi + lo in fp16) is
-//     divided per head by a power of two near its largest entry and the value
-//     scales by the split's largest one, so fp16 operands stay in range
-//     whatever the magnitudes; both are undone in fp32.
+//     weights (p_t s_t; the running sum l keeps p_t). q~ is divided per head
+//     by a power of two near its largest entry and the value scales by the
+//     split's largest one, so fp16 operands stay in range whatever the
+//     magnitudes; both are undone in fp32. q~ and the weights are each
+//     rounded once to fp16 (11 significant bits; relative error 2^-12 per
+//     entry, averaging out over the 256 latents of a score and the tokens of
+//     a sum): the codes carry at most 8 bits, and the bf16 kernel's two-term
+//     operands would double the MFMAs of a kernel that is not HBM-bound.
 // One workgroup owns one (batch, group, context split) and 16 query heads;
 // its waves (four for int8, eight for int4) take the split's 32-token
 // blocks round-robin and combine
@@ -56,12 +60,6 @@ constexpr float kV = 8.f;         // value weights' extra power of two (fp16 ran
 constexpr int kBlock = 32;       // tokens per cache block and per wave step
 constexpr float kLazy = 8.0f;    // log2 units: p <= 2^8 between rescales
 
-// x ~ hi + lo in two fp16 (nearest even each): the MFMA operand bits
-__device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
-  const _Float16 h = static_cast<_Float16>(x);
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x - static_cast<float>(h)));
-}
 
 // Codes enter the matrix cores as fp16 subnormals: the fp16 with bits 0x00uu
 // is u * 2^-24 exactly, so a byte or a nibble moved into the low bits of a
@@ -130,7 +128,7 @@ __device__ __forceinline__ float bfly_lane(float x, int lane, int m) {
 template <int R, int kWaves>
 struct Smem {
   union {
-    uint16_t q[2][16][R + 8];
+    uint16_t q[16][R + 8];
     float urot[16][R + 4];   // merged value sums of a rotated cache (after the loop)
   };
   float qc[16];              // power of two each head's q~ was divided by
@@ -258,7 +256,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
 #pragma unroll
     for (int o = 32; o >= 1; o /= 2) smax = fmaxf(smax, __shfl_xor(smax, o));
     if (lane == 0) sm.svmax[wave] = smax;
-    // one wave per head: q~ scaled by a power of two (below), hi + lo
+    // one wave per head: q~ scaled by a power of two (below), fp16
 #pragma unroll
     for (int i = 0; i < kH; ++i) {
       const int hd = wave + kWaves * i;
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
       // q~ / c with c = 2^(e-10), 2^e <= max |q~_h| < 2^(e+1): entries up to
-      // 2^11, so the lo parts of all but the smallest entries stay normal fp16
+      // 2^11, so all but the smallest entries stay normal fp16
       const uint32_t eb = __float_as_uint(amax) & 0x7F800000u;
       const float c0 = (eb == 0u || eb == 0x7F800000u) ? 1.f : __uint_as_float(eb);
       const float boost = c0 >= 0x1p-100f ? 1024.f : 1.f;
@@ -304,12 +302,9 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
       float qsum = 0.f;                              // sum_k of q~_k / c
 #pragma unroll
       for (int j = 0; j < R / 64; ++j) {
-        uint16_t hb, lb;
-        split_f16(qx[i][j] * inv * ks, hb, lb);
-        sm.q[0][hd][lane + 64 * j] = hb;
-        sm.q[1][hd][lane + 64 * j] = lb;
-        qsum += (static_cast<float>(__builtin_bit_cast(_Float16, hb)) +
-                 static_cast<float>(__builtin_bit_cast(_Float16, lb))) * (plain ? 0.0625f : 1.f);
+        const _Float16 h = static_cast<_Float16>(qx[i][j] * inv * ks);   // nearest even
+        sm.q[hd][lane + 64 * j] = __builtin_bit_cast(uint16_t, h);
+        qsum += static_cast<float>(h) * (plain ? 0.0625f : 1.f);
       }
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) qsum += __shfl_xor(qsum, o);
@@ -329,7 +324,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
   for (int w = 1; w < kWaves; ++w) vref = fmaxf(vref, sm.svmax[w]);
   if (!(vref > 0.f && vref < INFINITY)) vref = 1.f;
   const float vinv = 1.f / vref;
-  // value weights times kV (their fp16 lo parts stay normal longer: weights
+  // value weights times kV (small weights stay normal fp16 longer: weights
   // reach 2^8 kV kF <= 2^15), and for int4 those of the tokens whose operand
   // elements carry u, not 16 u (k-slot elements 0, 1, 4, 5: the lane's tokens
   // i = 0, 1 of each half) times 16, so every product carries kV kF
@@ -352,13 +347,12 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
     // the reads inside)
     asm volatile("" ::: "memory");
     // scores of the two 16-token halves: S^T[16 tok x 16 heads] of half h
-    // (q~ hi and lo parts in separate accumulators: four independent chains)
-    floatx4 shi[2] = {{qb, qb, qb, qb}, {qb, qb, qb, qb}};
-    floatx4 slo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // (even and odd chunks in separate accumulators: four independent chains)
+    floatx4 se[2] = {{qb, qb, qb, qb}, {qb, qb, qb, qb}};
+    floatx4 so[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int c = 0; c < R / 32; ++c) {
-      const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[0][ln][32 * c + 8 * kb]);
-      const uint4 ql = *reinterpret_cast<const uint4*>(&sm.q[1][ln][32 * c + 8 * kb]);
+      const uint4 qh = *reinterpret_cast<const uint4*>(&sm.q[ln][32 * c + 8 * kb]);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // key chunk c of half h: int8 word h*R/64 + c/2, bytes 8*(c%2) .. +8;
@@ -370,13 +364,13 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
         } else {
           a = key_operand4(x.k[h * (R / 32) + c]);
         }
-        shi[h] = mfma(a, qh, shi[h]);
-        slo[h] = mfma(a, ql, slo[h]);
+        if (c % 2 == 0) se[h] = mfma(a, qh, se[h]);
+        else so[h] = mfma(a, qh, so[h]);
       }
     }
     // scores in units of qc * 2^-24 (qc the head's power-of-two divisor),
     // bias already out: that factor is applied in the exponent
-    floatx4 sc[2] = {(shi[0] + slo[0]) * x.sk0, (shi[1] + slo[1]) * x.sk1};
+    floatx4 sc[2] = {(se[0] + so[0]) * x.sk0, (se[1] + so[1]) * x.sk1};
     floatx4 sv[2] = {x.sv0 * vinvv, x.sv1 * vinvv};
     if constexpr (decltype(masked)::value) {
 #pragma unroll
@@ -404,8 +398,8 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
     }
     // P^T operand: k-slot 8*kb + j is token 4*kb + j (j < 4) or 16 + 4*kb + j - 4
     // weights (v_exp_f32: arguments <= kLazy, results below 2^-126 flush to
-    // 0, far under the fp16 operands' resolution), each as hi + lo fp16
-    uint32_t ph[4], pl[4];
+    // 0, far under the fp16 operands' resolution), rounded once to fp16
+    uint32_t ph[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -413,19 +407,14 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
         const float pe0 = __builtin_amdgcn_exp2f(fmaf(qc, sc[h][i], -st.m));
         const float pe1 = __builtin_amdgcn_exp2f(fmaf(qc, sc[h][i + 1], -st.m));
         st.l += pe0 + pe1;
-        const float x0 = pe0 * sv[h][i], x1 = pe1 * sv[h][i + 1];
-        const half2v hi = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
-        const half2v lo = {static_cast<_Float16>(x0 - static_cast<float>(hi[0])),
-                           static_cast<_Float16>(x1 - static_cast<float>(hi[1]))};
-        ph[2 * h + i / 2] = __builtin_bit_cast(uint32_t, hi);
-        pl[2 * h + i / 2] = __builtin_bit_cast(uint32_t, lo);
+        const half2v w = {static_cast<_Float16>(pe0 * sv[h][i]),
+                          static_cast<_Float16>(pe1 * sv[h][i + 1])};
+        ph[2 * h + i / 2] = __builtin_bit_cast(uint32_t, w);
       }
     const uint4 bh = {ph[0], ph[1], ph[2], ph[3]};
-    const uint4 bl = {pl[0], pl[1], pl[2], pl[3]};
     // values: U^T[16 rb .. +16, heads] += H_v^T[., 32 tokens] P^T; latent rows
     // 16*rb + ln of the lane's eight tokens in word rb/2, bytes 8*(rb%2) .. +8
-    // (four row blocks at a time, hi parts first: an MFMA never waits on the
-    // one just before it)
+    // (four row blocks at a time)
     static_assert(R % 64 == 0, "row blocks come in fours");
 #pragma unroll
     for (int rb0 = 0; rb0 < R / 16; rb0 += 4) {
@@ -442,8 +431,6 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) st.acc[rb0 + u] = mfma(a[u], bh, st.acc[rb0 + u]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) st.acc[rb0 + u] = mfma(a[u], bl, st.acc[rb0 + u]);
     }
   };
   // the hot loops fetch unconditionally (a fetch under a branch made the

@@ -135,9 +135,12 @@ def test_int4_latent_output():
 @pytest.mark.parametrize("idx", [3, 64])
 def test_int4_matches_int8_on_the_same_codes(idx):
     """Codes in [-7, 7] are also int8 codes: the int8 decode on them (same
-    scales) computes the same attention; the two differ only in the rounding
-    of the score accumulators, whose bias term (128 or 8 times the sum of q~)
-    is taken back in fp32."""
+    scales, the same fp16 q~ and weights) computes the same attention; the two
+    differ only in the rounding of the fp32 score accumulators, which sum r
+    products q~_k (code_k + bias) with bias 128 or 8, the bias term being taken
+    back in fp32: with r = 256 and |code| <= 7 the int8 sums run about 20
+    times larger than the scores, so each score carries a relative rounding
+    error of order 20 * sqrt(r) * 2^-24 ~ 2e-5, and the outputs a few 1e-5."""
     import torch
     import rank_compressed_kv_amd as P
     cfg = SMALL[idx]
@@ -150,7 +153,7 @@ def test_int4_matches_int8_on_the_same_codes(idx):
     torch.cuda.synchronize()
     b = b.cpu().numpy().astype(np.float64)
     print(f"[int4 vs int8] cfg{idx} max|d|={np.max(np.abs(a - b)):.3e}", flush=True)
-    assert_close(a, b, max_abs=2e-4, rel_l2=2e-5, what="int4 vs int8")
+    assert_close(a, b, max_abs=2e-4, rel_l2=1e-4, what="int4 vs int8")
 
 
 @pytest.mark.parametrize("idx", [3, 4, 64])
