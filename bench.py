@@ -73,9 +73,15 @@ def parse():
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the int8- and int4-latent absorbed steps")
     ap.add_argument("--profile-calls", type=int, default=0,
-                    help="profiling run: make this many decode calls of --config in --mode "
+                    help="profiling run: copy 1 GiB on the device (the counters' "
+                         "calibration), make this many decode calls of --config in --mode "
                          "(default split plan, no cache rotation) and exit; for rocprofv3 "
                          "counter passes")
+    ap.add_argument("--profile-bits", type=int, default=0, choices=[0, 8, 4],
+                    help="with --profile-calls: the int8 (8) or int4 (4) latent cache "
+                         "(absorbed keys) instead of the dtype cache")
+    ap.add_argument("--profile-hadamard", action="store_true",
+                    help="with --profile-bits: a Hadamard-rotated cache")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM read-stream probe")
     ap.add_argument("--no-configs", action="store_true",
@@ -597,24 +603,43 @@ def granularity_sweep(torch, P, W, cfg, args):
 def profile_calls(torch, P, W, cfg, args):
     """The decode call of one workload, made --profile-calls times on one
     cache (for counter passes: every call of the main kernel is the same
-    work); prints the plan."""
-    t = W.generate(cfg, parts=("decode",))
-    theta = cfg.rope_theta if args.mode == "reconstruct" else 0.0
+    work), after a 1 GiB device copy that calibrates the HBM byte counters;
+    prints the plan."""
+    src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    torch.empty_like(src).copy_(src)
+    torch.cuda.synchronize()
+    del src
+    bits = args.profile_bits
+    mode = "absorbed" if bits else args.mode
+    t = W.generate(cfg, parts=("decode",) + ((f"i{bits}",) if bits else ()))
+    theta = cfg.rope_theta if mode == "reconstruct" else 0.0
     q, bk, bv, lens = (dev(torch, t[k]) for k in ("q", "b_k", "b_v", "lens"))
-    hk, hv = dev(torch, t["h_k"]), dev(torch, t["h_v"])
     desc = P.attn_desc(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                        head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank,
                        max_ctx=cfg.max_ctx, dtype=P.PALU_BF16 if cfg.dtype == "bf16" else P.PALU_F32,
-                       mode=args.mode, rope_theta=theta, split_tokens=args.split_tokens)
+                       mode=mode, rope_theta=theta, split_tokens=args.split_tokens,
+                       hadamard=bool(bits and args.profile_hadamard))
     ws = torch.empty(P.palu_decode_attn_workspace(desc), dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    if bits:
+        from rank_compressed_kv_amd.layout import pack_i4_cache, pack_i8_cache
+        pack = pack_i8_cache if bits == 8 else pack_i4_cache
+        sfx = "" if bits == 8 else "_i4"
+        hk, hv = dev(torch, pack(t[f"k_i{bits}"], "k")), dev(torch, pack(t[f"v_i{bits}"], "v"))
+        sk, sv = dev(torch, t["sk" + sfx]), dev(torch, t["sv" + sfx])
+        fn = P.palu_decode_attn_i8 if bits == 8 else P.palu_decode_attn_i4
+        call = lambda: fn(desc, q, hk, hv, sk, sv, bk, bv, lens, out, ws)
+    else:
+        hk, hv = dev(torch, t["h_k"]), dev(torch, t["h_v"])
+        call = lambda: P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws)
     for _ in range(args.profile_calls):
-        P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws)
+        call()
     torch.cuda.synchronize()
     ns, st, kname = P.palu_decode_attn_plan(desc)
-    print(f"[profile] cfg{args.config} {cfg.name} {args.mode}: {args.profile_calls} calls of "
-          f"{kname}, n_split {ns}, split_tokens {st}, latent bytes "
-          f"{W.latent_bytes(cfg, t['lens'])}", flush=True)
+    what = f"int{bits}{' hadamard' if args.profile_hadamard else ''}" if bits else cfg.dtype
+    print(f"[profile] cfg{args.config} {cfg.name} {mode} {what}: {args.profile_calls} calls, "
+          f"n_split {ns}, split_tokens {st}, latent bytes {W.latent_bytes(cfg, t['lens'])}",
+          flush=True)
 
 
 def read_stream_probe(torch):
@@ -735,13 +760,16 @@ def cpu_baseline(O, cfg, t, mode, budget_s):
                       f"fp64 NumPy, {el:.1f} s; steps/s = steps / seconds"}
 
 
-def load_traffic(kernel: str, args_suffix: str = ""):
+def load_traffic(kernel: str, args_suffix: str = "", label: str = ""):
     """HBM bytes (read + write) per launch of a kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a 1 GiB copy measured in
-    the same runs). The records are keyed by kernel name with template
-    arguments: the one whose name is `kernel` and whose arguments end with
-    args_suffix is taken. None when there is no single such record or when the
-    kernel's source has changed since the counters were taken."""
+    the same runs; rank_compressed_kv_amd.profiling writes the record). The
+    records are keyed by kernel name with template arguments: the one whose
+    name is `kernel`, whose arguments end with args_suffix and whose label
+    (the variant a pass ran, e.g. "hadamard"; none for the plain one) is
+    `label` is taken. None
+    when there is no single such record or when the kernel's sources have
+    changed since its counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -749,15 +777,18 @@ def load_traffic(kernel: str, args_suffix: str = ""):
     try:
         with open(path) as f:
             rec = json.load(f)
+        hits = [v for key, v in rec["kernels"].items()
+                for name, lab in [key.split(" | ") if " | " in key else (key, "")]
+                if name.split("<")[0] == kernel and name.endswith(args_suffix) and lab == label]
+        if len(hits) != 1 or not hits[0].get("sources"):
+            return None
         h = hashlib.sha256()
-        for rel in rec["sources"]:          # the kernel file and the headers it uses
+        for rel in hits[0]["sources"]:
             with open(os.path.join(ROOT, rel), "rb") as f:
                 h.update(f.read())
-        if h.hexdigest() != rec["sources_sha256"]:
+        if h.hexdigest() != hits[0]["sources_sha256"]:
             return None
-        hits = [v for name, v in rec["kernels"].items()
-                if name.split("<")[0] == kernel and name.endswith(args_suffix)]
-        return round(hits[0]["bytes"]) if len(hits) == 1 else None
+        return round(hits[0]["bytes"])
     except Exception:
         return None
 
@@ -869,8 +900,8 @@ def main():
                     "frac_hbm_kernel": _r(qbytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "step_speedup_vs_bf16": round(results["absorbed"]["ms_per_step"]
                                                   / ri["ms_per_step"], 3),
-                    "traffic": load_traffic("split_absorbed_int_kernel",
-                                            f", {bits}>") if not rot else None,
+                    "traffic": load_traffic("split_absorbed_int_kernel", f", {bits}>",
+                                            "hadamard" if rot else ""),
                     "sampled_parity_max_abs": dmax,
                     "sampled_parity_rel_l2": math.sqrt(num / den) if den > 0 else None}
                 print(f"[bench] int{bits} absorbed{' hadamard' if rot else ''}: "
