@@ -212,8 +212,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   // LDS copy of tile it+2 from the register stage (its buffer last held tile
   // it-2) and the request of tile it+3 into the stage, the rotation-table
   // reads, the 16 pair rotations, the four fp16 packs and score MFMAs, the
-  // scale, mask and running max. The next H_k chunk is read half a chunk
-  // ahead. Region 2: the rare rescale, tile it's softmax and values, the
+  // scale, mask and running max. H_k chunks are read two chunks ahead. Region 2: the rare rescale, tile it's softmax and values, the
   // rotation table of tile it+1 (its buffer last served tile it-1); the
   // barrier.
   constexpr int kSlots = 8 * kC;
@@ -224,8 +223,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     const int bf1 = next_buf(bf), bf2 = next_buf(bf1);   // tiles it+1, it+2
     const char* kt = sm.k[bf1] + ln * kKStride<R> + 16 * kb;
     const uint4* qo = &sm.qop[wave][0][lane];
-    u32x4 h[2];
+    // H_k chunks in a ring of three, each read two chunks (16 MFMAs) ahead
+    u32x4 h[3];
     h[0] = *reinterpret_cast<const u32x4*>(kt);
+    h[1] = *reinterpret_cast<const u32x4*>(kt + 64);
     float4 rt[4][2];
     uint4 a16[4];
     sc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -282,11 +283,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     };
     static_for<kSlots>([&](auto S) {
       constexpr int slot = S, c = slot / 8, blk = slot % 8;
-      if constexpr (blk == 4 && c + 1 < kC) h[(c + 1) & 1] = *reinterpret_cast<const u32x4*>(kt + 64 * (c + 1));
+      if constexpr (blk == 0 && c + 2 < kC) h[(c + 2) % 3] = *reinterpret_cast<const u32x4*>(kt + 64 * (c + 2));
       const floatx4 acc_in = c == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : nxt[blk];
       hold_in_agpr(bt[blk][c]);
       nxt[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bt[blk][c]),
-                                                         __builtin_bit_cast(bf16x8, h[c & 1]),
+                                                         __builtin_bit_cast(bf16x8, h[c % 3]),
                                                          acc_in, 0, 0, 0);
       constexpr int w0 = slot * kItems / kSlots, w1 = (slot + 1) * kItems / kSlots;
       static_for<w1 - w0>([&](auto J) { item(std::integral_constant<int, w0 + J>{}); });
