@@ -135,12 +135,7 @@ Plan make_plan(const palu_attn_desc* d) {
     }
     // one wave per KV head: aim at one wave per SIMD (1024 waves), i.e. one
     // four-wave workgroup per CU
-    if (pl.kernel == SplitKernel::kReconstructWave) {
-      const int hw = reconstruct_wave_heads_per_wg(sp.s);
-      slices = sp.s / hw;
-      wg_target = double(kWaveKernelWaves) / hw;
-    }
-    if (pl.kernel == SplitKernel::kReconstructWide) {
+    if (pl.kernel == SplitKernel::kReconstructWave || pl.kernel == SplitKernel::kReconstructWide) {
       slices = sp.s / 4;
       wg_target = double(kWaveKernelWaves) / 4;
     }

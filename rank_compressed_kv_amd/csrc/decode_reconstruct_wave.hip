@@ -10,10 +10,9 @@
 // weighted sum runs over h_v rows and B_v is applied in the merge pass.
 //
 // Shapes served: head_dim 128, at most four query heads per KV head, rank 32,
-// 64 or 128 (at rank 256 B_k^T alone fills the register file and the older
-// block-per-split kernel is faster). A workgroup owns one (batch, group, context split, slice of
-// HW KV heads) and has one wave per KV head of the slice (HW = 4 for groups of
-// four or more heads). Each wave keeps its KV head's whole B_k^T (128 columns x
+// 64 or 128, a multiple of four KV heads per group (rank 256 has a kernel of
+// its own). A workgroup owns one (batch, group, context split, slice of four
+// KV heads) and has one wave per KV head of the slice. Each wave keeps its KV head's whole B_k^T (128 columns x
 // r latents, from a transposed copy in the workspace) in registers for the
 // split, so a wave rebuilds, rotates and scores its head's keys on its own:
 // no partial scores cross waves, and each wave runs the online softmax of its
@@ -429,30 +428,22 @@ hipError_t launch_shape(const DecodeParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int R>
-hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
-  switch (reconstruct_wave_heads_per_wg(p.s)) {
-    case 4: return launch_shape<R, 4>(p, st);
-    case 2: return launch_shape<R, 2>(p, st);
-    case 1: return launch_shape<R, 1>(p, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 }  // namespace
 
-int reconstruct_wave_heads_per_wg(int s) { return s % 4 == 0 ? 4 : (s % 2 == 0 ? 2 : 1); }
-
+// Four KV heads a workgroup only: with fewer, the workgroup's few waves fill
+// the LDS ring and the rotation table alone, and the block-per-split kernel
+// is faster (rank 32 with one KV head a group: 481 against 191 us at the
+// Llama-3-8B shape).
 bool reconstruct_wave_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && p.d == kD && p.gqa <= 4 &&
+  return dtype == 1 && p.d == kD && p.gqa <= 4 && p.s % 4 == 0 &&
          (p.r == 32 || p.r == 64 || p.r == 128);
 }
 
 hipError_t launch_split_reconstruct_wave(const DecodeParams& p, hipStream_t st) {
   switch (p.r) {
-    case 32: return launch_rank<32>(p, st);
-    case 64: return launch_rank<64>(p, st);
-    case 128: return launch_rank<128>(p, st);
+    case 32: return launch_shape<32, 4>(p, st);
+    case 64: return launch_shape<64, 4>(p, st);
+    case 128: return launch_shape<128, 4>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

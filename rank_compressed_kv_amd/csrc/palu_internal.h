@@ -80,7 +80,8 @@ enum class SplitKernel {
   kReconstructMfma = 2,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
                          // head, r in {32, ..., 512}: a KV head's columns split over waves
   kReconstructWave = 3,  // bf16, rebuilt + rotated keys, d 128, <= 4 q heads per KV
-                         // head, r in {32, 64, 128}: one wave per KV head
+                         // head, r in {32, 64, 128}, KV heads per group a multiple
+                         // of 4: one wave per KV head
   kReconstructWide = 4,  // the same at r 256 (B_k^T in all of a wave's AGPRs), KV
                          // heads per group a multiple of 4
 };
@@ -125,7 +126,6 @@ int reconstruct_heads_per_wg(int r, int s);   // KV heads per workgroup (0: not 
 int reconstruct_waves_per_wg(int r, int s);
 hipError_t launch_transpose_bk(const DecodeParams& p, int dtype, hipStream_t st);
 bool reconstruct_wave_supported(const DecodeParams& p, int dtype);
-int reconstruct_wave_heads_per_wg(int s);   // KV heads (waves) per workgroup
 hipError_t launch_split_reconstruct_wave(const DecodeParams& p, hipStream_t st);
 bool reconstruct_wide_supported(const DecodeParams& p, int dtype);   // four KV heads a workgroup
 hipError_t launch_split_reconstruct_wide(const DecodeParams& p, hipStream_t st);

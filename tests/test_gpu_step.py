@@ -15,6 +15,10 @@ from tests.parity_util import assert_close, dev
 
 pytestmark = pytest.mark.gpu
 
+# one group of eight KV heads at rank 32, a short cache: many small sequences
+CARRY = W.CONFIGS[3].scaled(n_q_heads=8, n_kv_heads=8, n_groups=1, rank=32, max_ctx=64,
+                            ragged=None)
+
 CASES = {
     # the absorption carried by the append's launch
     "bf16_absorbed": (W.CONFIGS[3].scaled(batch=3, max_ctx=512, ragged=None, seed=90), 0,
@@ -44,6 +48,14 @@ CASES = {
                           "absorbed", 1),
     "bf16_reconstruct_cols": (W.CONFIGS[3].scaled(batch=3, max_ctx=512, ragged=None, seed=101),
                               0, "reconstruct", 1),
+    # the carried absorption's launch bound: with a_k, a_v [d_model, G*r] the
+    # absorb workgroups are further grid rows (d_model / 128 + Hkv * B rows at
+    # r = 32); 4096 sequences stay within the 65535 rows of a launch, 8192
+    # cross it and make two launches; the transposed form's one-dimensional
+    # grid carries both
+    "carry_bound_below": (CARRY.scaled(batch=4096, seed=102), 0, "absorbed"),
+    "carry_bound_above": (CARRY.scaled(batch=8192, seed=103), 0, "absorbed"),
+    "carry_bound_above_cols": (CARRY.scaled(batch=8192, seed=104), 0, "absorbed", 1),
 }
 
 
