@@ -31,9 +31,10 @@
 // the VALU only work at once when one wave's code interleaves them); the
 // softmax and values follow in their own block (at this rank the registers
 // do not allow them to be interleaved too).
-// Loads: 16-byte pieces of each tile go through one register stage into a
-// ring of four LDS buffers; rows past the split's end are clamped to its last
-// valid row and masked.
+// Loads: 16-byte pieces of each tile go through one of two register stages
+// (a tile is requested two iterations before its LDS copy) into a ring of
+// four LDS buffers; rows past the split's end are clamped to its last valid
+// row and masked.
 #include "reconstruct_wave_util.h"
 
 namespace palu {
@@ -162,18 +163,29 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   };
 
   // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
-  // the tile (byte 16*that in a row-major tile of 16 rows of 2R bytes). One
-  // tile waits in registers (vector types, so they stay in registers) and
-  // the two ahead of the one being consumed are in LDS.
+  // the tile (byte 16*that in a row-major tile of 16 rows of 2R bytes). Two
+  // tiles wait in registers (vector types, so they stay in registers; stage
+  // it & 1 holds tile it+2 at iteration it) and the two ahead of the one
+  // being consumed are in LDS.
   typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
+  // a piece's byte offset inside its tile's rows (the same for every tile, so
+  // a tile only moves the scalar base; the split's last tile clamps its rows)
+  uint32_t poff[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) poff[i] = 16u * static_cast<uint32_t>(tid + i * kThreads);
   auto fetch = [&](int tok0, u32v& k, u32v& v) {
+    const bool tail = tok0 + kTile > t1;
+    const size_t base = static_cast<size_t>(min(tok0, last)) * (2 * R);
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int pc = tid + i * kThreads;
-      const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
-      const size_t off = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R) + pcol;
-      const uint4 a = load_tile16<kShared>(Hk + off);
-      const uint4 c = load_tile16<kShared>(Hv + off);
+      uint32_t o = poff[i];
+      if (tail) {
+        asm volatile("" : "+v"(o));                      // keeps the clamp inside this rare branch
+        const int row = min(static_cast<int>(o / (2 * R)), last - min(tok0, last));
+        o = static_cast<uint32_t>(row * (2 * R)) + o % (2 * R);
+      }
+      const uint4 a = load_tile16<kShared>(Hk + base + o);
+      const uint4 c = load_tile16<kShared>(Hv + base + o);
       k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
       v[4 * i] = c.x; v[4 * i + 1] = c.y; v[4 * i + 2] = c.z; v[4 * i + 3] = c.w;
     }
@@ -190,14 +202,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     }
   };
 
-  // Prologue: tiles 0 and 1 into LDS, tile 2 in the register stage, the
-  // rotation table of tile 0, the keys of tile 0.
-  u32v stk, stv;
-  fetch(s0, stk, stv);
-  put(0, stk, stv);
-  fetch(s0 + kTile, stk, stv);
-  put(1, stk, stv);
-  fetch(s0 + 2 * kTile, stk, stv);
+  // Prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in the register stages,
+  // the rotation table of tile 0, the keys of tile 0.
+  u32v stk0, stv0, stk1, stv1;
+  fetch(s0, stk0, stv0);
+  put(0, stk0, stv0);
+  fetch(s0 + kTile, stk0, stv0);
+  put(1, stk0, stv0);
+  fetch(s0 + 2 * kTile, stk0, stv0);
+  __builtin_amdgcn_sched_barrier(0);                     // stage 0's loads are the older ones
+  fetch(s0 + 3 * kTile, stk1, stv1);
   rot.exact(s0, 0);
   barrier_lds();
   floatx4 kx[8], ky[8];
@@ -209,16 +223,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   // written as 8 kC slots in a fixed order (the compiler may not move code
   // across slots): slot (c, blk) issues the key MFMA of tile it+1's column
   // block blk and chunk c, then its share of the work items of tile it: the
-  // LDS copy of tile it+2 from the register stage (its buffer last held tile
-  // it-2) and the request of tile it+3 into the stage, the rotation-table
+  // LDS copy of tile it+2 from its register stage (its buffer last held tile
+  // it-2) and the request of tile it+4 into the stage, the rotation-table
   // reads, the 16 pair rotations, the four fp16 packs and score MFMAs, the
   // scale, mask and running max. H_k chunks are read two chunks ahead. Region 2: the rare rescale, tile it's softmax and values, the
   // rotation table of tile it+1 (its buffer last served tile it-1); the
   // barrier.
   constexpr int kSlots = 8 * kC;
   constexpr int kItems = 32;
-  auto region1 = [&](int it, int bf, floatx4 (&cur)[8], floatx4 (&nxt)[8], floatx4& sc,
-                     float& mx) {
+  auto region1 = [&](int it, int bf, floatx4 (&cur)[8], floatx4 (&nxt)[8], u32v& stk, u32v& stv,
+                     floatx4& sc, float& mx) {
     const int tok0 = s0 + it * kTile;
     const int bf1 = next_buf(bf), bf2 = next_buf(bf1);   // tiles it+1, it+2
     const char* kt = sm.k[bf1] + ln * kKStride<R> + 16 * kb;
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
       if constexpr (w == 0) {
         put(bf2, stk, stv);
       } else if constexpr (w == 1) {
-        fetch(s0 + (it + 3) * kTile, stk, stv);
+        fetch(s0 + (it + 4) * kTile, stk, stv);
       } else if constexpr (w == 2 || w == 3) {
         rows(w - 2);
       } else if constexpr (w < 8) {
@@ -294,10 +308,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto iteration = [&](int it, floatx4 (&cur)[8], floatx4 (&nxt)[8]) {
+  auto iteration = [&](int it, floatx4 (&cur)[8], floatx4 (&nxt)[8], u32v& stk, u32v& stv) {
     floatx4 sc;
     float mx;
-    region1(it, cb, cur, nxt, sc, mx);
+    region1(it, cb, cur, nxt, stk, stv, sc, mx);
     softmax_values(cb, sc, mx);
     cb = next_buf(cb);
     if (it + 1 < ntiles) {
@@ -306,11 +320,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     }
     barrier_lds();
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    iteration(it, kx, ky);
-    if (it + 1 >= ntiles) break;
-    iteration(it + 1, ky, kx);
+  // whole pairs in the loop (both halves every trip, so the compiler's wait
+  // counts see stage 0's loads as the older ones at the loop's head), an odd
+  // last tile after it
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    iteration(it, kx, ky, stk0, stv0);
+    iteration(it + 1, ky, kx, stk1, stv1);
   }
+  if (it < ntiles) iteration(it, kx, ky, stk0, stv0);
 
   // ---- partials of this wave's query heads: the remainder rows (kb = 1) are
   // added to the bf16 rows (kb = 0); the sum l over the four lane groups

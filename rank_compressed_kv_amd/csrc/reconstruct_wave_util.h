@@ -221,20 +221,30 @@ struct Rot {
   }
   // the table of tile nt into buffer nt & 1 from tile nt - 1's (buffer
   // (nt - 1) & 1, which nothing rewrites before the next barrier): every
-  // read first, then the products and writes
-  __device__ __forceinline__ void step(int nt) {
-    float2* dst = slot(nt & 1);
-    const float2* src = slot((nt - 1) & 1);
+  // read first (step_read), then the products and writes (step_write); the
+  // two halves may sit apart in a schedule
+  struct StepRegs {
     float2 o[kRE], st[kRE];
+  };
+  __device__ __forceinline__ void step_read(int nt, StepRegs& r) {
+    const float2* src = slot((nt - 1) & 1);
 #pragma unroll
     for (int e = 0; e < kRE; ++e) {
-      o[e] = src[e * kSlotStep];
-      st[e] = t.rstep[f0 + e * kFStep];
+      r.o[e] = src[e * kSlotStep];
+      r.st[e] = t.rstep[f0 + e * kFStep];
     }
+  }
+  __device__ __forceinline__ void step_write(int nt, const StepRegs& r) {
+    float2* dst = slot(nt & 1);
 #pragma unroll
     for (int e = 0; e < kRE; ++e)
-      dst[e * kSlotStep] = float2{o[e].x * st[e].x - o[e].y * st[e].y,
-                                  o[e].y * st[e].x + o[e].x * st[e].y};
+      dst[e * kSlotStep] = float2{r.o[e].x * r.st[e].x - r.o[e].y * r.st[e].y,
+                                  r.o[e].y * r.st[e].x + r.o[e].x * r.st[e].y};
+  }
+  __device__ __forceinline__ void step(int nt) {
+    StepRegs r;
+    step_read(nt, r);
+    step_write(nt, r);
   }
 };
 
