@@ -20,9 +20,12 @@ timing starts; several copies of the cache are rotated so that the 256 MB
 Infinity Cache cannot serve the latents.
 
 Prints ONE JSON line. Timing: W warm-up steps, then K steps between
-torch.cuda.synchronize() calls, timed with events on the launch stream. The
-main kernel is also timed alone with HIP events the library records around
-it (palu_profile_begin/end), which gives the roofline figure.
+torch.cuda.synchronize() calls, timed with events on the launch stream; each
+timed loop follows untimed calls of the same work (at least W, about 40 ms of
+GPU time: on this part the clocks take about 25 ms of continuous work to
+settle). The main kernel is also timed alone with HIP events the library
+records around it (palu_profile_begin/end), which gives the roofline
+figure.
 """
 from __future__ import annotations
 
@@ -107,26 +110,26 @@ def dev(torch, a):
 
 STEP = "combined"   # set by --step
 
-_SPIN_CYCLES_PER_US = None
+WARM_MS = 40.0   # GPU work enqueued ahead of each timed loop
 
 
-def queue_behind_spin(torch, stream, us):
-    """Enqueue a GPU spin of about `us` microseconds on `stream` (torch's
-    sleep kernel, its clock rate measured once with events). A timed loop's
-    start event is recorded after it, so while the GPU spins the host queues
-    the loop's calls and the events time the GPU's back-to-back execution,
-    not the host's first submissions."""
-    global _SPIN_CYCLES_PER_US
-    if _SPIN_CYCLES_PER_US is None:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(1000)                     # warm the kernel up
-        a.record()
-        torch.cuda._sleep(2_000_000)
-        b.record()
-        torch.cuda.synchronize()
-        _SPIN_CYCLES_PER_US = 2_000_000 / max(1.0, a.elapsed_time(b) * 1e3)
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
+def warm_ahead(torch, stream, fn, n_min):
+    """Enqueue untimed calls fn(i) on `stream` ahead of a timed loop, without
+    waiting for them: at least n_min and about WARM_MS of GPU time (the
+    per-call time is taken from three calls first). The GPU's clocks settle
+    while it runs them (on this part a kernel reaches its steady rate after
+    about 25 ms of continuous work), and meanwhile the host queues the timed
+    calls, so the timed loop's events see back-to-back GPU execution rather
+    than the host's first submissions."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(3):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    per_ms = max(1e-3, a.elapsed_time(b) / 3)
+    for i in range(int(min(4000, max(n_min, math.ceil(WARM_MS / per_ms))))):
+        fn(i)
 
 
 def host_us(fn, n):
@@ -201,10 +204,10 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     first_out = out.clone()
     step_host = host_us(lambda i: step(i + 1), max(1, args.warmup))
     torch.cuda.synchronize()
-    # timed loop 1: the steps alone (the throughput figure), queued behind a
-    # spin long enough for the host to submit them all
+    # timed loop 1: the steps alone (the throughput figure), behind the
+    # warm-up work
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    queue_behind_spin(torch, stream, 1.5 * args.steps * step_host + 500)
+    warm_ahead(torch, stream, step, args.warmup)
     e0.record(stream)
     for i in range(args.steps):
         step(i)
@@ -215,7 +218,7 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     # pages compare with the uncompressed baseline
     call_host = host_us(decode, max(1, args.warmup))
     torch.cuda.synchronize()
-    queue_behind_spin(torch, stream, 1.5 * args.steps * call_host + 500)
+    warm_ahead(torch, stream, decode, args.warmup)
     e0.record(stream)
     for i in range(args.steps):
         decode(i)
@@ -226,6 +229,7 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     # (mean, median, p10, p90 of single calls)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    warm_ahead(torch, stream, decode, args.warmup)
     for i, (a, b_) in enumerate(ev):
         hk, hv = caches[i % n_copies]
         a.record(stream)
@@ -239,6 +243,7 @@ def time_mode(torch, P, W, cfg, t, mode, args, n_copies):
     # not give the step rate
     kern_ms, kern_n = float("nan"), 0
     if not args.no_kernel_events:
+        warm_ahead(torch, stream, step, args.warmup)
         P.palu_profile_begin(args.steps)
         for i in range(args.steps):
             step(i)
@@ -314,9 +319,7 @@ def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     res = {}
     for name, fn in (("step", step), ("decode", decode)):
-        h = host_us(fn, max(1, args.warmup))
-        torch.cuda.synchronize()
-        queue_behind_spin(torch, stream, 1.5 * args.steps * h + 500)
+        warm_ahead(torch, stream, fn, args.warmup)
         e0.record(stream)
         for i in range(args.steps):
             fn(i)
@@ -325,6 +328,7 @@ def time_quant(torch, P, W, cfg, t, args, bits, rot=False):
         res[name] = e0.elapsed_time(e1) / args.steps
     kern_ms, kern_n = float("nan"), 0
     if not args.no_kernel_events:
+        warm_ahead(torch, stream, step, args.warmup)
         P.palu_profile_begin(args.steps)
         for i in range(args.steps):
             step(i)
@@ -359,16 +363,15 @@ def time_full_rank(torch, P, W, cfg, t, args):
     call(0)
     torch.cuda.synchronize()
     first = out.clone()
-    h = host_us(lambda i: call(i + 1), max(1, args.warmup))
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    queue_behind_spin(torch, stream, 1.5 * args.steps * h + 500)
+    warm_ahead(torch, stream, call, args.warmup)
     e0.record(stream)
     for i in range(args.steps):
         call(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    warm_ahead(torch, stream, call, args.warmup)
     P.palu_profile_begin(args.steps)
     for i in range(args.steps):
         call(i)
@@ -410,7 +413,7 @@ def roofline(cfg, t, mode, res, lat_bytes, kern_gbs, traffic):
 def reconstruct_configs(torch, P, W, O, args, which=(2, 4, 5)):
     """The rebuilt-key decode call at the other workloads' full sizes (MHA
     Llama-2-7B, the 128K-token outlier context, the ragged J-LRD batch): call
-    time queued behind a spin, kernel time from the library's events, each
+    time behind warm-up work, kernel time from the library's events, each
     against its roofline, and two sampled (b, h) outputs against the oracle.
     Caches are rotated over enough copies to defeat the Infinity Cache."""
     rows = {}
@@ -442,16 +445,15 @@ def reconstruct_configs(torch, P, W, O, args, which=(2, 4, 5)):
         torch.cuda.synchronize()
         first = out.cpu().numpy()
         n = max(5, args.steps // 2)
-        h = host_us(call, 3)
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        queue_behind_spin(torch, stream, 1.5 * n * h + 500)
+        warm_ahead(torch, stream, call, 3)
         e0.record(stream)
         for i in range(n):
             call(i)
         e1.record(stream)
         torch.cuda.synchronize()
         call_us = e0.elapsed_time(e1) / n * 1e3
+        warm_ahead(torch, stream, call, 3)
         P.palu_profile_begin(n)
         for i in range(n):
             call(i)
@@ -569,13 +571,11 @@ def granularity_sweep(torch, P, W, cfg, args):
             out = torch.empty(c.batch, c.n_q_heads, c.head_dim, dtype=torch.float32, device="cuda")
             _, _, kname = P.palu_decode_attn_plan(desc)
             stream = torch.cuda.current_stream()
-            h = host_us(lambda i: P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws,
-                                                     stream), 3)
-            torch.cuda.synchronize()
             n = max(5, args.steps // 4)
+            warm_ahead(torch, stream, lambda i: P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens,
+                                                                   out, ws, stream), 3)
             P.palu_profile_begin(n)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            queue_behind_spin(torch, stream, 1.5 * n * h + 500)
             e0.record(stream)
             for _ in range(n):
                 P.palu_decode_attn(desc, q, hk, hv, bk, bv, lens, out, ws, stream)
@@ -946,9 +946,12 @@ def main():
         "roofline": roofline(cfg, t, args.mode, main_res, lat_bytes, kern_gbs, traffic),
         "full_rank_baseline": full,
         "quantised_latents": quant,
-        "timing": "each timed loop is queued behind a GPU spin recorded before its start "
-                  "event, so the events time back-to-back GPU execution; host_us_* is the "
-                  "binding's submission time per step or call",
+        "timing": "each timed loop (and each kernel-event loop) follows untimed calls of "
+                  "the same work, at least W and about 40 ms of GPU time, enqueued without "
+                  "waiting: the clocks settle during them and the host queues the timed "
+                  "calls meanwhile, so the events time back-to-back GPU execution at the "
+                  "steady clock rate; host_us_* is the binding's submission time per step "
+                  "or call",
         "modes": {m: {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                       "us_per_decode_call": round(r["decode_ms"] * 1e3, 2),
                       "host_us_per_step": round(r["host_us_per_step"], 1),
