@@ -242,13 +242,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     h[0] = *reinterpret_cast<const u32x4*>(kt);
     h[1] = *reinterpret_cast<const u32x4*>(kt + 64);
     float4 rt[4][2];
-    uint4 a16[4];
+    uint4 a16[4], q16[4];
     sc = floatx4{0.f, 0.f, 0.f, 0.f};
     // items in order: 0 the LDS copy, 1 the request, then the table rows of
     // block b read one block ahead of its four pair rotations (2: rows 0,
     // 3: rows 1, 4-7: rotations 0, 8: rows 2, 9-12: rotations 1, 13: rows 3,
-    // 14-17: rotations 2, 18-21: rotations 3), 22-25 the packs, 26-29 the
-    // score MFMAs, 30 scale and mask, 31 the running max
+    // 14-17: rotations 2, 18-21: rotations 3 and the q operands of the score
+    // MFMAs), 22-25 the packs, 26-29 the score MFMAs, 30 scale and mask, 31
+    // the running max
     auto rows = [&](int blk) {
       rt[blk][0] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb][ln][0]);
       rt[blk][1] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb + 1][ln][0]);
@@ -278,6 +279,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
         rows(3);
       } else if constexpr (w < 22) {
         rotate(2 + (w - 14) / 4, (w - 14) % 4);
+        if constexpr (w >= 18) q16[w - 18] = qo[64 * (w - 18)];   // score MFMA w-18's q, early
       } else if constexpr (w < 26) {                     // fp16 A operand of score MFMA m
         constexpr int m = w - 22;
         a16[m] = uint4{pack_f16x2(cur[m][0], cur[m][1]), pack_f16x2(cur[m][2], cur[m][3]),
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
       } else if constexpr (w < 30) {                     // S[token 4 kb + i][head ln]
         constexpr int m = w - 26;
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a16[m]),
-                                                    __builtin_bit_cast(f16x8, qo[64 * m]), sc,
+                                                    __builtin_bit_cast(f16x8, q16[m]), sc,
                                                     0, 0, 0);
       } else if constexpr (w == 30) {                    // log2 units; past the split: masked
 #pragma unroll
