@@ -134,7 +134,7 @@ struct Smem {
   float qc[16];              // power of two each head's q~ was divided by
   float qbias[16];           // -bias * sum_k q_k * 2^-24: the score accumulators' start
   float svmax[kWaves];       // each wave's largest value scale
-  float acc[kWaves][4 * (R / 16)][64];   // every wave's softmax state (final merge)
+  floatx4 acc[kWaves][R / 16][64];   // every wave's value sums (final merge), 16 B a lane
   float m[kWaves][64], l[kWaves][64];
 };
 
@@ -459,9 +459,7 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
   // thread combines one (head, lane group, row block) slice of all of them
   // (a side that saw no token has m = -inf and weight 0) and writes it
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.acc[wave][4 * rb + i][lane] = st.acc[rb][i];
+  for (int rb = 0; rb < R / 16; ++rb) sm.acc[wave][rb][lane] = st.acc[rb];
   sm.m[wave][lane] = st.m;
   sm.l[wave][lane] = st.l;
   __syncthreads();
@@ -491,9 +489,11 @@ __global__ __launch_bounds__(64 * kWavesFor<kBits>, 1) void split_absorbed_int_k
   for (int rb = crq; rb < R / 16; rb += kWaves) {
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < kWaves; ++w) {
+      const floatx4 a = sm.acc[w][rb][16 * ckb + cln];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(aw[w], sm.acc[w][4 * rb + i][16 * ckb + cln], v[i]);
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(aw[w], a[i], v[i]);
+    }
     if (p.hadamard) {
       *reinterpret_cast<float4*>(&sm.urot[cln][16 * rb + 4 * ckb]) = float4{v[0], v[1], v[2], v[3]};
     } else if (cln < nqs) {
