@@ -119,7 +119,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     }
   };
 
-  // tile it's softmax and values, after the running max of its scores
+  // tile it's softmax and values, after the running max of its scores (sc:
+  // the raw scores, mx: their scaled maximum in log2 units)
   const bool rhi = ln < gqa;                             // P row ln: bf16 part of head ln
   const bool rlo = ln >= 4 && ln - 4 < gqa;              // P row ln: remainder of head ln - 4
   const int vrow = 4 * kb + (ln >> 2), vcol = 4 * (ln & 3);   // transposing-read source
@@ -139,14 +140,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[rb][i] *= ah[i];
     }
-    // weights 2^(s - m) <= 2^kLazy by the hardware exp2 (results below 2^-126
+    // weights 2^(s hscale - m) <= 2^kLazy by the hardware exp2 (results below 2^-126
     // flush to zero, which a weight of that size is anyway); masked tokens
     // (s = -inf) give 0. The P operand: rows 0..3 bf16(p) of head ln, rows
     // 4..7 the remainders of head ln - 4 (moved four lanes up inside each
     // 16-lane row)
     floatx4 pv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], hscale, -m_run));
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     uint32_t h0, h1, lo0, lo1;
     split_bf16x2(pv[0], pv[1], h0, lo0);
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   // LDS copy of tile it+2 from its register stage (its buffer last held tile
   // it-2) and the request of tile it+4 into the stage, the rotation-table
   // reads, the 16 pair rotations, the four fp16 packs and score MFMAs, the
-  // scale, mask and running max. H_k chunks are read two chunks ahead. Region 2: the rare rescale, tile it's softmax and values, the
+  // last tile's mask and the running max. H_k chunks are read two chunks
+  // ahead. Region 2: the rare rescale, tile it's softmax and values, the
   // rotation table of tile it+1 (its buffer last served tile it-1); the
   // barrier.
   constexpr int kSlots = 8 * kC;
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     // block b read one block ahead of its four pair rotations (2: rows 0,
     // 3: rows 1, 4-7: rotations 0, 8: rows 2, 9-12: rotations 1, 13: rows 3,
     // 14-17: rotations 2, 18-21: rotations 3 and the q operands of the score
-    // MFMAs), 22-25 the packs, 26-29 the score MFMAs, 30 scale and mask, 31
-    // the running max
+    // MFMAs), 22-25 the packs, 26-29 the score MFMAs, 30 the mask of the
+    // split's last tile, 31 the running max
     auto rows = [&](int blk) {
       rt[blk][0] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb][ln][0]);
       rt[blk][1] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * blk + 2 * kb + 1][ln][0]);
@@ -290,11 +292,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a16[m]),
                                                     __builtin_bit_cast(f16x8, q16[m]), sc,
                                                     0, 0, 0);
-      } else if constexpr (w == 30) {                    // log2 units; past the split: masked
+      } else if constexpr (w == 30) {                    // the split's last tile: its tail masked
+        if (tok0 + kTile > t1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] * hscale : -INFINITY;
-      } else {
-        mx = max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+          for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] : -INFINITY;
+        }
+      } else {                                           // in log2 units (hscale > 0)
+        mx = hscale * max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       }
     };
     static_for<kSlots>([&](auto S) {
