@@ -120,16 +120,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   };
 
   // tile it's softmax and values, after the running max of its scores (sc:
-  // the raw scores, mx: their scaled maximum in log2 units)
+  // the raw scores, mx: their scaled maximum in log2 units). Tiles go in
+  // pairs: the first's weights wait in registers (pv_pair) and one bf16 MFMA
+  // 16x16x32 per value block takes both tiles' 32 tokens (k slot 8 kb + j is
+  // token 4 kb + j of the first tile for j < 4, token 4 kb + j - 4 of the
+  // second for j >= 4: a lane's own weights and its transposing reads of the
+  // two V tiles); a tile without a partner (an odd count's last) takes the
+  // 16x16x16 form.
   const bool rhi = ln < gqa;                             // P row ln: bf16 part of head ln
   const bool rlo = ln >= 4 && ln - 4 < gqa;              // P row ln: remainder of head ln - 4
   const int vrow = 4 * kb + (ln >> 2), vcol = 4 * (ln & 3);   // transposing-read source
-  auto softmax_values = [&](int bf, floatx4 sc, float mx) {
+  floatx4 pv_pair = {0.f, 0.f, 0.f, 0.f};                // the pair's first tile's weights
+  // the P operand of four weights: rows 0..3 bf16(p) of head ln, rows 4..7 the
+  // remainders of head ln - 4 (moved four lanes up inside each 16-lane row)
+  auto p_operand = [&](floatx4 pv) {
+    uint32_t h0, h1, lo0, lo1;
+    split_bf16x2(pv[0], pv[1], h0, lo0);
+    split_bf16x2(pv[2], pv[3], h1, lo1);
+    const uint32_t lo0s = __builtin_amdgcn_update_dpp(0u, lo0, 0x114, 0xf, 0xf, true);
+    const uint32_t lo1s = __builtin_amdgcn_update_dpp(0u, lo1, 0x114, 0xf, 0xf, true);
+    const uint32_t a0 = rhi ? h0 : (rlo ? lo0s : 0u), a1 = rhi ? h1 : (rlo ? lo1s : 0u);
+    return __builtin_bit_cast(short4v, uint2{a0, a1});
+  };
+  // kMode: 0 a tile alone, 1 the first of a pair (weights kept), 2 the second
+  // (values of both; bfp: the first's buffer)
+  auto softmax_values = [&](int bf, int bfp, floatx4 sc, float mx, auto kMode) {
+    constexpr int mode = kMode;
     if (__any(mx > m_run + kLazy)) {                     // wave-uniform, rare
       const float mn = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
+      if constexpr (mode == 2) pv_pair *= alpha;         // this lane's head's factor
       // acc rows belong to heads 0..3: take each head's factor from its lane
       float ah[4];
 #pragma unroll
@@ -140,27 +162,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[rb][i] *= ah[i];
     }
-    // weights 2^(s hscale - m) <= 2^kLazy by the hardware exp2 (results below 2^-126
-    // flush to zero, which a weight of that size is anyway); masked tokens
-    // (s = -inf) give 0. The P operand: rows 0..3 bf16(p) of head ln, rows
-    // 4..7 the remainders of head ln - 4 (moved four lanes up inside each
-    // 16-lane row)
+    // weights 2^(s hscale - m) <= 2^kLazy by the hardware exp2 (results below
+    // 2^-126 flush to zero, which a weight of that size is anyway); masked
+    // tokens (s = -inf) give 0
     floatx4 pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], hscale, -m_run));
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    uint32_t h0, h1, lo0, lo1;
-    split_bf16x2(pv[0], pv[1], h0, lo0);
-    split_bf16x2(pv[2], pv[3], h1, lo1);
-    const uint32_t lo0s = __builtin_amdgcn_update_dpp(0u, lo0, 0x114, 0xf, 0xf, true);
-    const uint32_t lo1s = __builtin_amdgcn_update_dpp(0u, lo1, 0x114, 0xf, 0xf, true);
-    const uint32_t a0 = rhi ? h0 : (rlo ? lo0s : 0u), a1 = rhi ? h1 : (rlo ? lo1s : 0u);
-    const short4v pa = __builtin_bit_cast(short4v, uint2{a0, a1});
-    // U[row][16 rb + ln] += sum_t P[row][t] H_v[t][16 rb + ln]
-    const char* vb = sm.v[bf] + vrow * kVStride<R> + 2 * vcol;
+    if constexpr (mode == 1) {
+      pv_pair = pv;
+    } else if constexpr (mode == 0) {
+      // U[row][16 rb + ln] += sum_t P[row][t] H_v[t][16 rb + ln]
+      const short4v pa = p_operand(pv);
+      const char* vb = sm.v[bf] + vrow * kVStride<R> + 2 * vcol;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, read_tr16(vb + 32 * rb), acc[rb], 0, 0, 0);
+      for (int rb = 0; rb < kRB; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, read_tr16(vb + 32 * rb), acc[rb], 0, 0, 0);
+    } else {
+      const short8v pa = __builtin_shufflevector(p_operand(pv_pair), p_operand(pv), 0, 1, 2, 3, 4, 5, 6, 7);
+      const char* va = sm.v[bfp] + vrow * kVStride<R> + 2 * vcol;
+      const char* vb = sm.v[bf] + vrow * kVStride<R> + 2 * vcol;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const short8v hv = __builtin_shufflevector(read_tr16(va + 32 * rb), read_tr16(vb + 32 * rb),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                          __builtin_bit_cast(bf16x8, hv), acc[rb], 0, 0, 0);
+      }
+    }
   };
 
   // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
@@ -314,11 +343,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto iteration = [&](int it, floatx4 (&cur)[8], floatx4 (&nxt)[8], u32v& stk, u32v& stv) {
+  auto iteration = [&](int it, floatx4 (&cur)[8], floatx4 (&nxt)[8], u32v& stk, u32v& stv,
+                       auto kMode) {
     floatx4 sc;
     float mx;
     region1(it, cb, cur, nxt, stk, stv, sc, mx);
-    softmax_values(cb, sc, mx);
+    softmax_values(cb, cb == 0 ? kNBuf - 1 : cb - 1, sc, mx, kMode);
     cb = next_buf(cb);
     if (it + 1 < ntiles) {
       if ((it + 1) % kAnchor == 0) rot.exact(s0 + (it + 1) * kTile, (it + 1) & 1);
@@ -331,10 +361,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
   // last tile after it
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    iteration(it, kx, ky, stk0, stv0);
-    iteration(it + 1, ky, kx, stk1, stv1);
+    iteration(it, kx, ky, stk0, stv0, std::integral_constant<int, 1>{});
+    iteration(it + 1, ky, kx, stk1, stv1, std::integral_constant<int, 2>{});
   }
-  if (it < ntiles) iteration(it, kx, ky, stk0, stv0);
+  if (it < ntiles) iteration(it, kx, ky, stk0, stv0, std::integral_constant<int, 0>{});
 
   // ---- partials of this wave's query heads: the remainder rows (kb = 1) are
   // added to the bf16 rows (kb = 0); the sum l over the four lane groups

@@ -86,6 +86,33 @@ def test_length_edges_and_poisoned_tail(idx, mode):
         assert_close(got, want, what=f"edges cfg{idx}/{mode}/split{st}", **_tol(cfg))
 
 
+def bump_keys(hk, up, down):
+    """Key latents (bf16 bits) of tokens `up` times 16 and of tokens `down`
+    times -16: exponent + 4 (no overflow at these magnitudes), sign flipped."""
+    hk = hk.copy()
+    for rows, sign in ((up, 0), (down, 0x8000)):
+        f = hk[:, :, rows, :].astype(np.uint32)
+        f = np.where((f & 0x7F80) != 0, f + (4 << 7), f) ^ sign
+        hk[:, :, rows, :] = f.astype(np.uint16)
+    return hk
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_reconstruct_rescale_inside_tile_pair(idx):
+    """The rank-256 kernels take a pair of 16-token tiles' values in one MFMA,
+    the first tile's weights waiting for the second: tokens of second tiles
+    (16..31 of each 32) whose key latents are scaled by 16 and by -16 (exact in
+    bf16) raise the running max by far more than the lazy-rescale threshold, so
+    the kept weights are rescaled too; lengths leave odd and even tile counts."""
+    cfg = SMALL[idx].scaled(batch=3, max_ctx=420, ragged=None)
+    t = W.generate(cfg, lens=np.array([420, 405, 37]))
+    t = dict(t, h_k=bump_keys(t["h_k"], [17, 18, 19, 150, 389, 28], [20, 21, 22, 152, 400, 30]))
+    for st in (0, 64, 128):
+        print(f"[pair-rescale] cfg{idx} split={st}", flush=True)
+        got, theta = run_decode(cfg, t, "reconstruct", split_tokens=st)
+        assert_close(got, _oracle(cfg, t, theta), what=f"pair rescale cfg{idx} split={st}")
+
+
 # (KV heads per group s, rank r): the granularities at 75% key compression
 # (M-LRD s=1 r=32 ... J-LRD s=8 r=256) and rank 512 with 2, 4 and 8 heads
 GROUPINGS = [(1, 32), (2, 64), (4, 128), (8, 256), (1, 128), (2, 256), (2, 512), (4, 512),
