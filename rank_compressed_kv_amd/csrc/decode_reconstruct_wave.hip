@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
         for (int i = 0; i < 4; ++i) acc[rb][i] *= ah[i];
     }
   };
-  // the P operand of a tile's scores: weights 2^(s - m) <= 2^kLazy by the
+  // the P operand of a tile's raw scores: weights 2^(s hscale - m) <= 2^kLazy by the
   // hardware exp2 (results below 2^-126 flush to zero, which a weight of
   // that size is anyway; masked tokens, s = -inf, give 0); rows 0..3 bf16(p)
   // of head ln, rows 4..7 the remainders of head ln - 4 (moved four lanes up
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   auto p_operand = [&](floatx4 sc) {
     floatx4 pv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], hscale, -m_run));
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     uint32_t h0, h1, lo0, lo1;
     split_bf16x2(pv[0], pv[1], h0, lo0);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
     // MFMAs 0, 12 rows 2, 13-16 rotations 1, 17 reads 2, 18 MFMAs 1, 19 rows
     // 3, 20-23 rotations 2, 24 reads 3, 25 MFMAs 2, 26-29 rotations 3, 30
     // MFMAs 3, 31-34 packs, 35 table of tile it+1, 36-39 score MFMAs, 40
-    // scale and mask, 41 running max
+    // the mask of the split's last tile, 41 running max
     auto item = [&](auto W) {
       constexpr int w = W;
       if constexpr (w == kPut) {
@@ -340,12 +340,14 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a16[m]),
                                                     __builtin_bit_cast(f16x8, qo[64 * m]), sc,
                                                     0, 0, 0);
-      } else if constexpr (w == kMask) {                 // log2 units; past the split: masked
+      } else if constexpr (w == kMask) {                 // the split's last tile: its tail masked
+        if (tok0 + kTile > t1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] * hscale : -INFINITY;
-      } else {
+          for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] : -INFINITY;
+        }
+      } else {                                           // in log2 units (hscale > 0)
         static_assert(w == kMax, "unknown item");
-        mx = max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        mx = hscale * max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       }
     };
     // one key MFMA: column block blk, chunk c of tile it+1 (the next H_k
