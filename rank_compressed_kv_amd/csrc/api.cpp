@@ -117,6 +117,8 @@ Plan make_plan(const palu_attn_desc* d) {
     pl.kernel = SplitKernel::kReconstructWave;
   if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_wide_supported(sp, d->dtype))
     pl.kernel = SplitKernel::kReconstructWide;
+  if (d->mode == PALU_MODE_RECONSTRUCT && reconstruct_quarter_supported(sp, d->dtype))
+    pl.kernel = SplitKernel::kReconstructQuarter;
   int st = d->split_tokens;
   if (st == 0) {
     // Aim at a fixed number of (split, b, g) units: 256 for the generic
@@ -138,6 +140,16 @@ Plan make_plan(const palu_attn_desc* d) {
     if (pl.kernel == SplitKernel::kReconstructWave || pl.kernel == SplitKernel::kReconstructWide) {
       slices = sp.s / 4;
       wg_target = double(kWaveKernelWaves) / 4;
+    }
+    // four waves per KV head (column quarters), eight-wave workgroups, one
+    // per CU: aim at eight rounds of workgroups. A workgroup's split runs
+    // for about 100 us at 1024 tokens, so with ragged lengths (short
+    // sequences leave their late splits empty) a single round would end on a
+    // long tail; eight rounds keep it to a few percent and cost about 7% when
+    // every sequence is full length (more workgroup set-ups)
+    if (pl.kernel == SplitKernel::kReconstructQuarter) {
+      slices = sp.s / 2;
+      wg_target = double(kWaveKernelWaves) * 2;
     }
     const double want = double(d->max_ctx) * d->batch * d->n_groups * slices / wg_target;
     st = int(std::ceil(want / kSplitQuantum)) * kSplitQuantum;
@@ -166,7 +178,8 @@ WorkspaceLayout layout(const palu_attn_desc* d, const Plan& pl) {
   w.bkt = w.u + align256(heads * pl.n_split * size_t(d->rank) * 4);
   const bool bkt = pl.kernel == SplitKernel::kReconstructMfma ||
                    pl.kernel == SplitKernel::kReconstructWave ||
-                   pl.kernel == SplitKernel::kReconstructWide;
+                   pl.kernel == SplitKernel::kReconstructWide ||
+                   pl.kernel == SplitKernel::kReconstructQuarter;
   const size_t bkt_bytes =
       bkt ? align256(size_t(d->n_kv_heads) * d->head_dim * d->rank * elem) : 0;
   w.total = w.bkt + bkt_bytes;
@@ -207,6 +220,7 @@ const char* split_kernel_name(SplitKernel k) {
     case SplitKernel::kReconstructMfma: return "split_reconstruct_mfma_kernel";
     case SplitKernel::kReconstructWave: return "split_reconstruct_wave_kernel";
     case SplitKernel::kReconstructWide: return "split_reconstruct_wide_kernel";
+    case SplitKernel::kReconstructQuarter: return "split_reconstruct_quarter_kernel";
   }
   return "?";
 }
@@ -286,7 +300,7 @@ palu_status prepare_launch(const palu_attn_desc* desc, const DecodeParams& p, co
   else if (desc->mode == PALU_MODE_ABSORBED) e = launch_absorb_q(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "absorb_q launch: %s", hipGetErrorString(e));
   if (pl.kernel == SplitKernel::kReconstructMfma || pl.kernel == SplitKernel::kReconstructWave ||
-      pl.kernel == SplitKernel::kReconstructWide)
+      pl.kernel == SplitKernel::kReconstructWide || pl.kernel == SplitKernel::kReconstructQuarter)
     e = launch_transpose_bk(p, desc->dtype, s);
   if (e != hipSuccess) return fail(PALU_ERR_DEVICE, "transpose launch: %s", hipGetErrorString(e));
   return PALU_OK;
@@ -344,6 +358,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
     case SplitKernel::kReconstructMfma: e = launch_split_reconstruct_mfma(p, s); break;
     case SplitKernel::kReconstructWave: e = launch_split_reconstruct_wave(p, s); break;
     case SplitKernel::kReconstructWide: e = launch_split_reconstruct_wide(p, s); break;
+    case SplitKernel::kReconstructQuarter: e = launch_split_reconstruct_quarter(p, s); break;
     default: e = launch_split_generic(p, desc->dtype, absorbed, s); break;
   }
   if (rec >= 0) (void)hipEventRecord(g_prof.stop[rec], s);

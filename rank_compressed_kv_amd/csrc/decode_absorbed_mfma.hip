@@ -60,10 +60,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 }
 
 // q~ in LDS as the score MFMA's B operand: [hi|lo][head][k] bf16; rows padded
-// by 8 elements so the 16 heads' 16-byte reads spread over the banks.
+// by 16 elements (32 bytes: a row stride of 32 mod 64 bytes keeps the 16
+// heads' 16-byte reads free of bank conflicts on gfx950).
 template <int R>
 struct QTile {
-  static constexpr int kStride = R + 8;
+  static constexpr int kStride = R + 16;
   uint16_t v[2][16][kStride];
 };
 
@@ -77,10 +78,10 @@ __device__ __forceinline__ int vtile_off(int row, int cb) {
 }
 template <int R>
 constexpr int kVTileBytes = kTile * R * 2 + 3 * 32;
-// key tile rows padded by 16 bytes: the 16 rows of an operand read start on
-// different banks
+// key tile rows padded by 32 bytes (a row stride of 32 mod 64 bytes keeps the
+// 16 rows of an operand read free of bank conflicts on gfx950)
 template <int R>
-constexpr int kKStride = 2 * R + 16;
+constexpr int kKStride = 2 * R + 32;
 template <int R>
 constexpr int kKTileBytes = kTile * kKStride<R>;
 

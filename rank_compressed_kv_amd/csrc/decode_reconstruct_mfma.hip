@@ -94,9 +94,10 @@ __device__ __forceinline__ float lane_xor(float x, int addr) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
 }
 
-// K tile: rows padded by 16 B so the 16 rows of an operand read hit distinct banks
+// K tile: rows padded by 32 B (a row stride of 32 mod 64 bytes keeps the 16
+// rows of an operand read free of bank conflicts on gfx950)
 template <int R>
-constexpr int kKStride = 2 * R + 16;
+constexpr int kKStride = 2 * R + 32;
 // V tile: groups of four rows offset by 32 B (conflict-free column gathers)
 template <int R>
 __device__ __forceinline__ int vtile_off(int row, int cb) {

@@ -77,6 +77,56 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
 
   __shared__ Smem sm;
 
+  const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
+  const char* Hk = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.h_k) + row0 * R);
+  const char* Hv = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.h_v) + row0 * R);
+  const int ntiles = (t1 - s0 + kTile - 1) / kTile;
+
+  // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
+  // the tile (byte 16*that in a row-major tile of 16 rows of 2R bytes). Two
+  // tiles wait in registers (vector types, so they stay in registers; stage
+  // it & 1 holds tile it+2 at iteration it) and the two ahead of the one
+  // being consumed are in LDS. The first two tiles are requested before
+  // anything else, so their latency overlaps the B_k^T loads and the set-up.
+  typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
+  // a piece's byte offset inside its tile's rows (the same for every tile, so
+  // a tile only moves the scalar base; the split's last tile clamps its rows)
+  uint32_t poff[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) poff[i] = 16u * static_cast<uint32_t>(tid + i * kThreads);
+  auto fetch = [&](int tok0, u32v& k, u32v& v) {
+    const bool tail = tok0 + kTile > t1;
+    const size_t base = static_cast<size_t>(min(tok0, last)) * (2 * R);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      uint32_t o = poff[i];
+      if (tail) {
+        asm volatile("" : "+v"(o));                      // keeps the clamp inside this rare branch
+        const int row = min(static_cast<int>(o / (2 * R)), last - min(tok0, last));
+        o = static_cast<uint32_t>(row * (2 * R)) + o % (2 * R);
+      }
+      const uint4 a = load_tile16<kShared>(Hk + base + o);
+      const uint4 c = load_tile16<kShared>(Hv + base + o);
+      k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
+      v[4 * i] = c.x; v[4 * i + 1] = c.y; v[4 * i + 2] = c.z; v[4 * i + 3] = c.w;
+    }
+  };
+  auto put = [&](int buf, const u32v& k, const u32v& v) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int pc = tid + i * kThreads;
+      const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
+      *reinterpret_cast<uint4*>(sm.k[buf] + prow * kKStride<R> + pcol) =
+          uint4{k[4 * i], k[4 * i + 1], k[4 * i + 2], k[4 * i + 3]};
+      *reinterpret_cast<uint4*>(sm.v[buf] + prow * kVStride<R> + pcol) =
+          uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    }
+  };
+
+  u32v stk0, stv0, stk1, stv1;
+  fetch(s0, stk0, stv0);
+  fetch(s0 + kTile, stk1, stv1);
+
   u32x4 bt[8][kC];
   load_bkt<kC>(bt, static_cast<const uint16_t*>(p.bkt) + (static_cast<size_t>(g) * p.Dg + kvh * kD) * R,
                R, 0, ln, kb);
@@ -94,10 +144,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
-  const char* Hk = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.h_k) + row0 * R);
-  const char* Hv = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.h_v) + row0 * R);
-  const int ntiles = (t1 - s0 + kTile - 1) / kTile;
   // the ring's next buffer (the buffer of tile it is carried through the
   // loop rather than computed as it % kNBuf, which keeps the LDS addresses
   // one register plus an immediate offset)
@@ -192,53 +238,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_reconstruct_wide_kernel(
     }
   };
 
-  // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
-  // the tile (byte 16*that in a row-major tile of 16 rows of 2R bytes). Two
-  // tiles wait in registers (vector types, so they stay in registers; stage
-  // it & 1 holds tile it+2 at iteration it) and the two ahead of the one
-  // being consumed are in LDS.
-  typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
-  // a piece's byte offset inside its tile's rows (the same for every tile, so
-  // a tile only moves the scalar base; the split's last tile clamps its rows)
-  uint32_t poff[kPieces];
-#pragma unroll
-  for (int i = 0; i < kPieces; ++i) poff[i] = 16u * static_cast<uint32_t>(tid + i * kThreads);
-  auto fetch = [&](int tok0, u32v& k, u32v& v) {
-    const bool tail = tok0 + kTile > t1;
-    const size_t base = static_cast<size_t>(min(tok0, last)) * (2 * R);
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      uint32_t o = poff[i];
-      if (tail) {
-        asm volatile("" : "+v"(o));                      // keeps the clamp inside this rare branch
-        const int row = min(static_cast<int>(o / (2 * R)), last - min(tok0, last));
-        o = static_cast<uint32_t>(row * (2 * R)) + o % (2 * R);
-      }
-      const uint4 a = load_tile16<kShared>(Hk + base + o);
-      const uint4 c = load_tile16<kShared>(Hv + base + o);
-      k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
-      v[4 * i] = c.x; v[4 * i + 1] = c.y; v[4 * i + 2] = c.z; v[4 * i + 3] = c.w;
-    }
-  };
-  auto put = [&](int buf, const u32v& k, const u32v& v) {
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int pc = tid + i * kThreads;
-      const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
-      *reinterpret_cast<uint4*>(sm.k[buf] + prow * kKStride<R> + pcol) =
-          uint4{k[4 * i], k[4 * i + 1], k[4 * i + 2], k[4 * i + 3]};
-      *reinterpret_cast<uint4*>(sm.v[buf] + prow * kVStride<R> + pcol) =
-          uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-    }
-  };
-
   // Prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in the register stages,
   // the rotation table of tile 0, the keys of tile 0.
-  u32v stk0, stv0, stk1, stv1;
-  fetch(s0, stk0, stv0);
   put(0, stk0, stv0);
-  fetch(s0 + kTile, stk0, stv0);
-  put(1, stk0, stv0);
+  put(1, stk1, stv1);
   fetch(s0 + 2 * kTile, stk0, stv0);
   __builtin_amdgcn_sched_barrier(0);                     // stage 0's loads are the older ones
   fetch(s0 + 3 * kTile, stk1, stv1);

@@ -94,27 +94,40 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int L) {
 }
 
 // Which (context split, batch, group, head slice) a workgroup of a
-// context-split kernel owns. With one head slice, blockIdx is (split, g, b).
-// With several, the launch is one-dimensional: units u = split + n_split*(g +
-// G*b) are padded to a multiple of 8 and the nslice workgroups of unit u get
-// linear ids 8 apart, which puts them on the same XCD (workgroups are dealt
-// to the 8 XCDs round-robin) at about the same time, so the latent tiles they
-// all read are shared through that XCD's L2.
+// context-split kernel owns. Units u = split + n_split*(g + G*b) are dealt to
+// the 8 XCDs (workgroups go to the XCDs round-robin in linear id order) with
+// a rotation: XCD c's workgroup in block a of eight units takes unit 8a + ((c
+// - a) mod 8). Without it XCD c would always get the splits u = c (mod 8),
+// i.e. the same split indices of every sequence whenever n_split is a
+// multiple of 8 (or divides 8); with ragged lengths the late splits are empty
+// for short sequences and whole XCDs would sit idle. With one head slice,
+// blockIdx is (x, y, z) over (n_split, G, B) and the rotation covers the whole
+// blocks only (a partial last block keeps its order). With several, the
+// launch is one-dimensional: the units are padded to a multiple of 8 and the
+// nslice workgroups of a unit get linear ids 8 apart, which puts them on the
+// same XCD at about the same time, so the latent tiles they all read are
+// shared through that XCD's L2.
 struct SplitUnit {
   int split, g, b, hs;
   bool live;
 };
 __device__ __forceinline__ SplitUnit split_unit(int n_split, int G, int B, int nslice) {
   SplitUnit u{};
+  const int units = n_split * G * B;
+  int unit;
   if (nslice == 1) {
-    u.split = blockIdx.x; u.g = blockIdx.y; u.b = blockIdx.z; u.hs = 0; u.live = true;
-    return u;
+    const int k = blockIdx.x + n_split * (blockIdx.y + G * blockIdx.z);
+    const int a = k >> 3;
+    unit = 8 * a + 8 <= units ? 8 * a + ((k - a) & 7) : k;
+    u.hs = 0;
+  } else {
+    const int id = blockIdx.x;
+    const int lo = id & 7, hi = id >> 3;
+    u.hs = hi % nslice;
+    const int a = hi / nslice;
+    unit = 8 * a + ((lo - a) & 7);
   }
-  const int id = blockIdx.x;
-  const int lo = id & 7, hi = id >> 3;
-  u.hs = hi % nslice;
-  const int unit = (hi / nslice) * 8 + lo;
-  u.live = unit < n_split * G * B;
+  u.live = unit < units;
   u.split = unit % n_split;
   const int rest = unit / n_split;
   u.g = rest % G;

@@ -84,6 +84,8 @@ enum class SplitKernel {
                          // of 4: one wave per KV head
   kReconstructWide = 4,  // the same at r 256 (B_k^T in all of a wave's AGPRs), KV
                          // heads per group a multiple of 4
+  kReconstructQuarter = 5,  // the same at r 512: four waves per KV head, each with a
+                            // quarter of its columns' B_k^T; KV heads per group even
 };
 
 const char* split_kernel_name(SplitKernel k);
@@ -129,6 +131,8 @@ bool reconstruct_wave_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_reconstruct_wave(const DecodeParams& p, hipStream_t st);
 bool reconstruct_wide_supported(const DecodeParams& p, int dtype);   // four KV heads a workgroup
 hipError_t launch_split_reconstruct_wide(const DecodeParams& p, hipStream_t st);
+bool reconstruct_quarter_supported(const DecodeParams& p, int dtype);   // two KV heads a workgroup
+hipError_t launch_split_reconstruct_quarter(const DecodeParams& p, hipStream_t st);
 hipError_t launch_split_reconstruct_mfma(const DecodeParams& p, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t st);
 size_t append_workspace_bytes(int B, int dm, int G, int r);

@@ -43,6 +43,8 @@ KERNEL_SOURCES = {
                                       "device_util.h"],
     "split_reconstruct_wide_kernel": ["decode_reconstruct_wide.hip", "reconstruct_wave_util.h",
                                       "device_util.h"],
+    "split_reconstruct_quarter_kernel": ["decode_reconstruct_quarter.hip", "reconstruct_wave_util.h",
+                                      "device_util.h"],
     "split_reconstruct_mfma_kernel": ["decode_reconstruct_mfma.hip", "device_util.h"],
 }
 

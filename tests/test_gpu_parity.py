@@ -97,13 +97,16 @@ def bump_keys(hk, up, down):
     return hk
 
 
-@pytest.mark.parametrize("idx", [2, 3])
+@pytest.mark.parametrize("idx", [2, 3, 5])
 def test_reconstruct_rescale_inside_tile_pair(idx):
     """The rank-256 kernels take a pair of 16-token tiles' values in one MFMA,
     the first tile's weights waiting for the second: tokens of second tiles
     (16..31 of each 32) whose key latents are scaled by 16 and by -16 (exact in
     bf16) raise the running max by far more than the lazy-rescale threshold, so
-    the kept weights are rescaled too; lengths leave odd and even tile counts."""
+    the kept weights are rescaled too; lengths leave odd and even tile counts.
+    At rank 512 (four waves per KV head, each with a quarter of the columns)
+    the same jumps check that the four waves, which add the partial scores in
+    one order, take the same rescale decisions."""
     cfg = SMALL[idx].scaled(batch=3, max_ctx=420, ragged=None)
     t = W.generate(cfg, lens=np.array([420, 405, 37]))
     t = dict(t, h_k=bump_keys(t["h_k"], [17, 18, 19, 150, 389, 28], [20, 21, 22, 152, 400, 30]))
