@@ -29,16 +29,21 @@
 //            barrier) and every quarter adds them in the same order, so the
 //            four waves of a head hold the same scores and softmax state;
 //   softmax  online, base 2, lazy rescale;
-//   values   its latent quarter: U[rows x 128] += P[rows x 16 tok] H_v[16 tok
-//            x 128], bf16 MFMA 16x16x16 with P hi in rows 0..3 and lo in rows
-//            4..7, the H_v operand read from the LDS tile with the
-//            transposing read.
+//   values   its latent quarter: U[rows x 128] += P[rows x tok] H_v[tok x
+//            128] with P hi in rows 0..3 and lo in rows 4..7, the H_v operand
+//            read from the LDS tile with the transposing read; two consecutive
+//            tiles share one bf16 MFMA 16x16x32 per 16-latent block (k slot
+//            8 kb + j is token 4 kb + j of the first tile for j < 4 and of
+//            the second for j >= 4), the first tile's weights waiting in
+//            registers and rescaled with the state if the second raises the
+//            max; an odd count's last tile takes the 16x16x16 form.
 // The next tile's key MFMAs are interleaved slot by slot with this tile's
 // rotations, pack and score MFMA; the two waves on a SIMD fill each other's
 // gaps (the softmax's dependent chain, LDS and exp latencies).
-// Loads: 16-byte pieces of each tile go through a register stage into a ring
-// of three LDS buffers; rows past the split's end are clamped to its last
-// valid row and masked.
+// Loads: 16-byte pieces of each tile go through a register stage into LDS
+// rings of three K and four V buffers (a pair's first V tile stays while the
+// tile after the pair's second is copied in); rows past the split's end are
+// clamped to its last valid row and masked.
 #include "reconstruct_wave_util.h"
 
 namespace palu {
@@ -53,15 +58,19 @@ constexpr int kParts = 4;          // waves (column quarters) per KV head
 constexpr int kWaves = kParts * kHeads;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVB = R / kParts / 16;   // 16-latent value blocks per wave
-constexpr int kNBuf = 3;           // LDS tile buffers
+constexpr int kNBuf = 3;           // LDS K tile buffers
+constexpr int kVBuf = 4;           // LDS V tile buffers
 
 struct Smem {
   char k[kNBuf][kTile * kKStride<R>];
-  char v[kNBuf][kTile * kVStride<R>];
-  uint4 qop[kWaves][4][64];        // each wave's q operand: qop[wave][m][lane]
+  char v[kVBuf][kTile * kVStride<R>];
+  uint4 qop[kWaves][64];           // each wave's score q operand (block pair qc)
   RotTable rot;
   floatx4 sp[kWaves][64];          // partial scores of the current tile
 };
+// the q operands of all four block pairs are built in V buffers 2 and 3
+// (first written by the loop, after the prologue's barriers)
+static_assert(2 * kTile * kVStride<R> >= kWaves * 4 * 64 * 16, "q operand staging fits");
 static_assert(sizeof(Smem) <= 160 * 1024, "fits the LDS of a CU");
 
 template <bool kShared>
@@ -121,14 +130,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
       v[4 * i] = c.x; v[4 * i + 1] = c.y; v[4 * i + 2] = c.z; v[4 * i + 3] = c.w;
     }
   };
-  auto put = [&](int buf, const u32v& k, const u32v& v) {
+  auto put = [&](int kbuf, int vbuf, const u32v& k, const u32v& v) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int pc = tid + i * kThreads;
       const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
-      *reinterpret_cast<uint4*>(sm.k[buf] + prow * kKStride<R> + pcol) =
+      *reinterpret_cast<uint4*>(sm.k[kbuf] + prow * kKStride<R> + pcol) =
           uint4{k[4 * i], k[4 * i + 1], k[4 * i + 2], k[4 * i + 3]};
-      *reinterpret_cast<uint4*>(sm.v[buf] + prow * kVStride<R> + pcol) =
+      *reinterpret_cast<uint4*>(sm.v[vbuf] + prow * kVStride<R> + pcol) =
           uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
     }
   };
@@ -153,7 +162,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
 #pragma unroll
       for (int c = 0; c < kC; ++c) hold_in_agpr(bt[lb][c]);
   }
-  const float hscale = q_operand(p, b, head0, gqa, ln, kb, lane, sm.qop[wave]);
+  float hscale;
+  {
+    uint4 (*qall)[64] = reinterpret_cast<uint4 (*)[64]>(sm.v[2]) + 4 * wave;
+    hscale = q_operand(p, b, head0, gqa, ln, kb, lane, qall);
+    sm.qop[wave][lane] = qall[qc][lane];                 // this wave's own rows: no barrier needed
+  }
   Rot<kThreads> rot(sm.rot, tid, p.rope != 0);
   rot.init(p, tid);
   barrier_lds();                                         // rstep and orev before any use
@@ -167,9 +181,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
 #pragma unroll
   for (int rb = 0; rb < kVB; ++rb) acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // the ring's next buffer (the buffer of tile it is carried through the
+  // the rings' next buffers (the buffers of tile it are carried through the
   // loop, which keeps the LDS addresses one register plus an immediate offset)
   auto next_buf = [](int bf) { return bf + 1 == kNBuf ? 0 : bf + 1; };
+  auto next_vbuf = [](int bf) { return bf + 1 == kVBuf ? 0 : bf + 1; };
 
   // keys of the tile in buffer bf: kk[lb] = K^T of column block qc + 4 lb
   auto keys = [&](int bf, floatx4 (&kk)[2]) {
@@ -191,12 +206,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
   const bool rhi = ln < gqa;                             // P row ln: bf16 part of head ln
   const bool rlo = ln >= 4 && ln - 4 < gqa;              // P row ln: remainder of head ln - 4
   const int vrow = 4 * kb + (ln >> 2), vcol = 4 * (ln & 3);   // transposing-read source
-  auto softmax_values = [&](int bf, floatx4 sc, float mx) {
+  // kMode: 0 a tile alone, 1 the first of a pair (weights kept in pv_pair),
+  // 2 the second (values of both; bfp: the first's V buffer)
+  floatx4 pv_pair;
+  auto softmax_values = [&](int bf, int bfp, floatx4 sc, float mx, auto kMode) {
+    constexpr int mode = kMode;
     if (__any(mx > m_run + kLazy)) {                     // wave-uniform, rare
       const float mn = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
+      if constexpr (mode == 2) pv_pair *= alpha;         // this lane's head's factor
       // acc rows belong to heads 0..3: take each head's factor from its lane
       float ah[4];
 #pragma unroll
@@ -216,30 +236,47 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], hscale, -m_run));
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    uint32_t h0, h1, lo0, lo1;
-    split_bf16x2(pv[0], pv[1], h0, lo0);
-    split_bf16x2(pv[2], pv[3], h1, lo1);
-    const uint32_t lo0s = __builtin_amdgcn_update_dpp(0u, lo0, 0x114, 0xf, 0xf, true);
-    const uint32_t lo1s = __builtin_amdgcn_update_dpp(0u, lo1, 0x114, 0xf, 0xf, true);
-    const uint32_t a0 = rhi ? h0 : (rlo ? lo0s : 0u), a1 = rhi ? h1 : (rlo ? lo1s : 0u);
-    const short4v pa = __builtin_bit_cast(short4v, uint2{a0, a1});
+    auto p_operand = [&](floatx4 w) {
+      uint32_t h0, h1, lo0, lo1;
+      split_bf16x2(w[0], w[1], h0, lo0);
+      split_bf16x2(w[2], w[3], h1, lo1);
+      const uint32_t lo0s = __builtin_amdgcn_update_dpp(0u, lo0, 0x114, 0xf, 0xf, true);
+      const uint32_t lo1s = __builtin_amdgcn_update_dpp(0u, lo1, 0x114, 0xf, 0xf, true);
+      const uint32_t a0 = rhi ? h0 : (rlo ? lo0s : 0u), a1 = rhi ? h1 : (rlo ? lo1s : 0u);
+      return __builtin_bit_cast(short4v, uint2{a0, a1});
+    };
     // U[row][128 qc + 16 rb + ln] += sum_t P[row][t] H_v[t][128 qc + 16 rb + ln]
     const char* vb = sm.v[bf] + vrow * kVStride<R> + 2 * vcol + (R / 2) * qc;
+    if constexpr (mode == 1) {
+      pv_pair = pv;
+    } else if constexpr (mode == 0) {
+      const short4v pa = p_operand(pv);
 #pragma unroll
-    for (int rb = 0; rb < kVB; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, read_tr16(vb + 32 * rb), acc[rb], 0, 0, 0);
+      for (int rb = 0; rb < kVB; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, read_tr16(vb + 32 * rb), acc[rb], 0, 0, 0);
+    } else {
+      const short8v pa = __builtin_shufflevector(p_operand(pv_pair), p_operand(pv), 0, 1, 2, 3, 4, 5, 6, 7);
+      const char* va = sm.v[bfp] + vrow * kVStride<R> + 2 * vcol + (R / 2) * qc;
+#pragma unroll
+      for (int rb = 0; rb < kVB; ++rb) {
+        const short8v hv = __builtin_shufflevector(read_tr16(va + 32 * rb), read_tr16(vb + 32 * rb),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                          __builtin_bit_cast(bf16x8, hv), acc[rb], 0, 0, 0);
+      }
+    }
   };
 
   // Prologue: tiles 0 and 1 into LDS, tile 2 in the register stage, the
   // rotation table of tile 0, the keys of tile 0.
-  put(0, stk, stv);
-  put(1, st1k, st1v);
+  put(0, 0, stk, stv);
+  put(1, 1, st1k, st1v);
   fetch(s0 + 2 * kTile, stk, stv);
   rot.exact(s0, 0);
   barrier_lds();
   floatx4 kx[2], ky[2];
   keys(0, kx);
-  int cb = 0;                                            // buffer of tile it
+  int cb = 0, cvb = 0;                                   // K and V buffers of tile it
 
   // Iteration it (after the barrier that made tiles it and it+1 and tile
   // it's rotation table visible). Region 1 is one straight run of code
@@ -247,16 +284,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
   // across slots): slot (c, lb) issues the key MFMA of tile it+1's block
   // qc + 4 lb and chunk c (H_k chunks read two chunks ahead), then its share
   // of the work items of tile it: the LDS copy of tile it+2 from the register
-  // stage (its buffer last held tile it-1) and the request of tile it+3 into
-  // the stage, the rotation-table rows of the wave's block pair, its four
-  // pair rotations, the fp16 pack and the partial score MFMA (its q
-  // operand read a few items earlier). Then the partial scores meet in LDS (a barrier), the last tile's mask, the running
-  // max, the rare rescale, tile it's softmax and values, the rotation table of
-  // tile it+1 (its buffer last served tile it-1); the barrier.
+  // stage (its K buffer last held tile it-1, its V buffer tile it-2) and the
+  // request of tile it+3 into the stage, the rotation-table rows of the
+  // wave's block pair, its four pair rotations, the fp16 pack and the partial
+  // score MFMA (its q operand read a few items earlier). Then the partial
+  // scores meet in LDS (a barrier), the last tile's mask, the running max, the
+  // rare rescale, tile it's softmax and values (of the pair it ends), the
+  // rotation table of tile it+1 (its buffer last served tile it-1); the
+  // barrier.
   constexpr int kSlots = 2 * kC;
   enum : int { kPut = 0, kFetch, kRows, kRot0, kQ = kRot0 + 2, kRot2, kPack = kRot2 + 2, kScore, kN };
-  auto region1 = [&](int it, int bf, floatx4 (&cur)[2], floatx4 (&nxt)[2], floatx4& sc) {
+  auto region1 = [&](int it, int bf, int vbf, floatx4 (&cur)[2], floatx4 (&nxt)[2], floatx4& sc) {
     const int bf1 = next_buf(bf), bf2 = next_buf(bf1);   // tiles it+1, it+2
+    const int vbf2 = next_vbuf(next_vbuf(vbf));          // V of tile it+2
     const char* kt = sm.k[bf1] + ln * kKStride<R> + 16 * kb;
     // H_k chunks in a ring of three, each read two chunks (4 MFMAs) ahead
     u32x4 h[3];
@@ -268,14 +308,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
     auto item = [&](auto W) {
       constexpr int w = W;
       if constexpr (w == kPut) {
-        put(bf2, stk, stv);
+        put(bf2, vbf2, stk, stv);
       } else if constexpr (w == kFetch) {
         fetch(s0 + (it + 3) * kTile, stk, stv);
       } else if constexpr (w == kRows) {                 // frequencies 16 qc + 4 kb + 0..3
         rt[0] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * qc + 2 * kb][ln][0]);
         rt[1] = *reinterpret_cast<const float4*>(&sm.rot.rtab[it & 1][8 * qc + 2 * kb + 1][ln][0]);
       } else if constexpr (w == kQ) {                    // q of the score MFMA of block pair qc
-        q16 = sm.qop[wave][qc][lane];
+        q16 = sm.qop[wave][lane];
       } else if constexpr ((w >= kRot0 && w < kRot0 + 2) || (w >= kRot2 && w < kRot2 + 2)) {
         constexpr int i = w < kQ ? w - kRot0 : w - kRot2 + 2;   // pair (f, f + 64), f = 16 qc + 4 kb + i
         const float4 r = rt[i / 2];
@@ -305,9 +345,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto iteration = [&](int it, floatx4 (&cur)[2], floatx4 (&nxt)[2]) {
+  auto iteration = [&](int it, floatx4 (&cur)[2], floatx4 (&nxt)[2], auto kMode) {
     floatx4 sc;
-    region1(it, cb, cur, nxt, sc);
+    region1(it, cb, cvb, cur, nxt, sc);
     // the four quarters' partial scores of tile it meet in LDS (sp is free:
     // its last readers passed the end-of-iteration barrier), added in quarter
     // order by every wave of the head
@@ -326,8 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
       for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] : -INFINITY;
     }
     const float mx = hscale * max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    softmax_values(cb, sc, mx);
+    softmax_values(cvb, cvb == 0 ? kVBuf - 1 : cvb - 1, sc, mx, kMode);
     cb = next_buf(cb);
+    cvb = next_vbuf(cvb);
     if (it + 1 < ntiles) {
       if ((it + 1) % kAnchor == 0) rot.exact(s0 + (it + 1) * kTile, (it + 1) & 1);
       else rot.step(it + 1);
@@ -336,10 +377,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
   };
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    iteration(it, kx, ky);
-    iteration(it + 1, ky, kx);
+    iteration(it, kx, ky, std::integral_constant<int, 1>{});
+    iteration(it + 1, ky, kx, std::integral_constant<int, 2>{});
   }
-  if (it < ntiles) iteration(it, kx, ky);
+  if (it < ntiles) iteration(it, kx, ky, std::integral_constant<int, 0>{});
 
   // ---- partials of this wave's query heads (latent quarter qc): the
   // remainder rows (kb = 1) are added to the bf16 rows (kb = 0); the sum l over
