@@ -129,7 +129,7 @@ Plan make_plan(const palu_attn_desc* d) {
                                                           : double(kAbsorbedWorkgroups);
     // the reconstruct MFMA kernel launches one workgroup per slice of KV heads,
     // and aims at about 2048 waves on the chip whatever its workgroup size
-    int slices = 1;
+    double slices = 1;
     if (pl.kernel == SplitKernel::kAbsorbedMfma) slices = absorbed_head_slices(sp.nq);
     if (pl.kernel == SplitKernel::kReconstructMfma) {
       slices = sp.s / reconstruct_heads_per_wg(sp.r, sp.s);
@@ -137,9 +137,15 @@ Plan make_plan(const palu_attn_desc* d) {
     }
     // one wave per KV head: aim at one wave per SIMD (1024 waves), i.e. one
     // four-wave workgroup per CU
+    // (groups of one or two KV heads share a workgroup: s / 4 of one a group)
     if (pl.kernel == SplitKernel::kReconstructWave || pl.kernel == SplitKernel::kReconstructWide) {
-      slices = sp.s / 4;
+      slices = sp.s / 4.0;
       wg_target = double(kWaveKernelWaves) / 4;
+      // groups of one or two KV heads at rank 32 (and two at rank 64): two
+      // workgroups fit a CU (registers and LDS), so aim at two rounds of
+      // CUs (measured at the Llama-3-8B shape: one KV head a group, rank 32,
+      // 101 -> 79 us; two, rank 64, 121 -> 87 us; four rounds were slower)
+      if (sp.s < 4 && (sp.r == 32 || (sp.r == 64 && sp.s == 2))) wg_target *= 2;
     }
     // four waves per KV head (column quarters), eight-wave workgroups, one
     // per CU: aim at eight rounds of workgroups. A workgroup's split runs

@@ -10,15 +10,19 @@
 // weighted sum runs over h_v rows and B_v is applied in the merge pass.
 //
 // Shapes served: head_dim 128, at most four query heads per KV head, rank 32,
-// 64 or 128, a multiple of four KV heads per group (rank 256 has a kernel of
-// its own). A workgroup owns one (batch, group, context split, slice of four
-// KV heads) and has one wave per KV head of the slice. Each wave keeps its KV head's whole B_k^T (128 columns x
-// r latents, from a transposed copy in the workspace) in registers for the
-// split, so a wave rebuilds, rotates and scores its head's keys on its own:
-// no partial scores cross waves, and each wave runs the online softmax of its
-// own query heads only. The waves share the latent tiles (read from HBM once
-// per workgroup into LDS) and the rotation table; their softmax states never
-// meet (each wave writes its heads' split partials itself).
+// 64 or 128, and either a multiple of four KV heads per group or groups of
+// one or two KV heads (rank 256 has a kernel of its own). A workgroup has
+// four waves, one per KV head, and owns one context split of one batch row
+// for four consecutive KV heads: a slice of one group, or four (two) whole
+// groups of one (two) KV heads, each group with its own latent tile. Each
+// wave keeps its KV head's whole B_k^T (128 columns x r latents, from a
+// transposed copy in the workspace) in registers for the split, so a wave
+// rebuilds, rotates and scores its head's keys on its own: no partial scores
+// cross waves, and each wave runs the online softmax of its own query heads
+// only. The waves of a group share its latent tiles (read from HBM once per
+// workgroup into LDS, loaded by those waves); all four share the rotation
+// table (same tokens); their softmax states never meet (each wave writes its
+// heads' split partials itself).
 // Per 16-token tile, wave of KV head j:
 //   keys     K^T[16 cols x 16 tok] = B_k^T[cols x r] * H_k^T[r x tok] for the 8
 //            column blocks, bf16 MFMA 16x16x32, H_k from the tile in LDS. Lane
@@ -61,10 +65,18 @@ using namespace wave;
 
 constexpr int kNBuf = 4;           // LDS tile buffers
 
-template <int R>
+// K tile row stride: 32 mod 64 bytes keeps the operand reads free of bank
+// conflicts; the four-group rank-32 form takes 16 mod 64 (one key chunk a
+// tile, so its few reads may conflict) to stay within half the LDS, which
+// lets two of its workgroups share a CU
+template <int R, int NG>
+constexpr int kKS = NG == 4 && R == 32 ? 2 * R + 16 : kKStride<R>;
+
+// NG: latent tiles a workgroup streams at once (one per head group it covers)
+template <int R, int NG>
 struct Smem {
-  char k[kNBuf][kTile * kKStride<R>];
-  char v[kNBuf][kTile * kVStride<R>];
+  char k[kNBuf][NG][kTile * kKS<R, NG>];
+  char v[kNBuf][NG][kTile * kVStride<R>];
   RotTable rot;
   // q of each wave's query heads as the score MFMA's B operand (fp16), lane
   // order: qop[wave][m][lane]
@@ -88,17 +100,26 @@ constexpr int kOrder[] = {
 template <int N>
 constexpr int count_of(const int (&)[N]) { return N; }
 
-template <int R, int HW, bool kShared>
-__global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(DecodeParams p) {
+template <int R, int HW, int NG, bool kShared>
+__global__ __launch_bounds__(64 * HW, NG > 1 ? 2 : 1) void split_reconstruct_wave_kernel(DecodeParams p) {
   constexpr int kThreads = 64 * HW;
-  constexpr int kPieces = (2 * R + kThreads - 1) / kThreads;   // 16-B pieces per matrix
+  constexpr int kWS = HW / NG;                                  // waves (KV heads) sharing a tile
+  constexpr int kST = 64 * kWS;                                 // threads that load a tile
+  constexpr int kPieces = (2 * R + kST - 1) / kST;              // 16-B pieces per matrix
   constexpr int kC = R / 32;                                    // 32-latent key chunks
   constexpr int kRB = R / 16;                                   // 16-latent value blocks
-  const int nslice = p.s / HW;
-  const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
+  static_assert(HW % NG == 0, "whole groups per workgroup");
+  // NG = 1: the HW KV heads are a slice of one group; NG > 1: groups of
+  // HW / NG KV heads, NG consecutive groups a workgroup (units over (split,
+  // group block, batch))
+  const int nslice = NG > 1 ? 1 : p.s / HW;
+  const SplitUnit un = split_unit(p.n_split, p.G / NG, p.B, nslice);
   if (!un.live) return;
-  const int split = un.split, g = un.g, b = un.b, hs = un.hs;
+  const int split = un.split, b = un.b, hs = un.hs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gs = NG > 1 ? wave / kWS : 0;               // this wave's tile slot
+  const int g = un.g * NG + gs;                          // its group
+  const int stid = tid - gs * kST;                       // its thread's index among the slot's loaders
   const int ln = lane & 15, kb = lane >> 4;
   const int n = clamp_len(p.lens, b, p.L);
   const int s0 = split * p.split_tokens;
@@ -106,10 +127,10 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   const int t1 = min(n, s0 + p.split_tokens);
   const int last = t1 - 1;
   const int gqa = p.gqa;                                 // query heads per KV head (<= 4)
-  const int kvh = hs * HW + wave;                        // this wave's KV head in the group
+  const int kvh = NG > 1 ? wave % kWS : hs * HW + wave;  // this wave's KV head in its group
   const int head0 = g * p.nq + kvh * gqa;                // its first query head
 
-  __shared__ Smem<R> sm;
+  __shared__ Smem<R, NG> sm;
 
   // ---- operands held for the whole split -----------------------------------
   // B_k^T as the key MFMA's A operand (column 16 blk + ln, latents 32 c + 8 kb
@@ -140,12 +161,12 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
 
   // keys of tile it (K tile in LDS): kk[blk] = K^T of column block blk
   auto keys = [&](int it, floatx4 (&kk)[8]) {
-    const char* kt = sm.k[it % kNBuf];
+    const char* kt = sm.k[it % kNBuf][gs];
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) kk[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
-      const bf16x8 h = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
+      const bf16x8 h = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKS<R, NG> + 2 * (32 * c + 8 * kb)));
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk)
         kk[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bt[blk][c]), h,
@@ -199,18 +220,18 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   // blocks in four groups
   auto vgroup = [](int g, int& b0, int& b1) { b0 = g * kRB / 4; b1 = (g + 1) * kRB / 4; };
 
-  // Loads: thread piece i (< kPieces) is the 16-byte piece tid + i*kThreads of
+  // Loads: thread piece i (< kPieces) is the 16-byte piece stid + i*kST of
   // the tile (byte 16*that in a row-major tile of 16 rows), if below 2R. Two
   // tiles wait in registers (stages a and b, vector types so they stay in
   // registers) and two ahead of the one being consumed are in LDS.
   typedef uint32_t u32v __attribute__((ext_vector_type(4 * kPieces)));
   // (the piece guard is a compile-time true when the threads divide the tile,
   // so the loads and copies add no branch to the iteration's straight run)
-  constexpr bool kWhole = (2 * R) % kThreads == 0;
+  constexpr bool kWhole = (2 * R) % kST == 0;
   auto fetch = [&](int tok0, u32v& k, u32v& v) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int pc = tid + i * kThreads;
+      const int pc = stid + i * kST;
       if (kWhole || pc < 2 * R) {
         const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
         const size_t row = static_cast<size_t>(min(tok0 + prow, last)) * (2 * R) + pcol;
@@ -224,12 +245,12 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   auto put = [&](int buf, const u32v& k, const u32v& v) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int pc = tid + i * kThreads;
+      const int pc = stid + i * kST;
       if (kWhole || pc < 2 * R) {
         const int prow = (pc * 16) / (2 * R), pcol = (pc * 16) % (2 * R);
-        *reinterpret_cast<uint4*>(sm.k[buf] + prow * kKStride<R> + pcol) =
+        *reinterpret_cast<uint4*>(sm.k[buf][gs] + prow * kKS<R, NG> + pcol) =
             uint4{k[4 * i], k[4 * i + 1], k[4 * i + 2], k[4 * i + 3]};
-        *reinterpret_cast<uint4*>(sm.v[buf] + prow * kVStride<R> + pcol) =
+        *reinterpret_cast<uint4*>(sm.v[buf][gs] + prow * kVStride<R> + pcol) =
             uint4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
       }
     }
@@ -271,8 +292,8 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
     constexpr bool vals = kVals;                          // tile it-1 exists
     if constexpr (vals) rescale(mx_prev);
     const int tok0 = s0 + it * kTile;
-    const char* kt = sm.k[(it + 1) % kNBuf] + ln * kKStride<R> + 16 * kb;
-    const char* vb = sm.v[(it + kNBuf - 1) % kNBuf] + vrow * kVStride<R> + 2 * vcol;
+    const char* kt = sm.k[(it + 1) % kNBuf][gs] + ln * kKS<R, NG> + 16 * kb;
+    const char* vb = sm.v[(it + kNBuf - 1) % kNBuf][gs] + vrow * kVStride<R> + 2 * vcol;
     const uint4* qo = &sm.qop[wave][0][lane];
     u32x4 h[2];
     h[0] = *reinterpret_cast<const u32x4*>(kt);
@@ -384,7 +405,7 @@ __global__ __launch_bounds__(64 * HW, 1) void split_reconstruct_wave_kernel(Deco
   {
     rescale(mx_prev);
     const short4v pa = p_operand(sc_prev);
-    const char* vb = sm.v[(ntiles - 1) % kNBuf] + vrow * kVStride<R> + 2 * vcol;
+    const char* vb = sm.v[(ntiles - 1) % kNBuf][gs] + vrow * kVStride<R> + 2 * vcol;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, read_tr16(vb + 32 * rb), acc[rb], 0, 0, 0);
@@ -420,28 +441,60 @@ hipError_t launch_shape(const DecodeParams& p, hipStream_t st) {
   const int nslice = p.s / HW;
   if (nslice == 1) {
     const dim3 grid(p.n_split, p.G, p.B);
-    split_reconstruct_wave_kernel<R, HW, false><<<grid, 64 * HW, 0, st>>>(p);
+    split_reconstruct_wave_kernel<R, HW, 1, false><<<grid, 64 * HW, 0, st>>>(p);
   } else {
     const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
     if (ids == 0) return hipErrorInvalidValue;
-    split_reconstruct_wave_kernel<R, HW, true>
+    split_reconstruct_wave_kernel<R, HW, 1, true>
         <<<dim3(static_cast<unsigned>(ids)), 64 * HW, 0, st>>>(p);
   }
   return hipGetLastError();
 }
 
+// groups of one or two KV heads: NG = 4 / s groups a four-wave workgroup
+template <int R, int NG>
+hipError_t launch_groups(const DecodeParams& p, hipStream_t st) {
+  if (p.G % NG != 0) return hipErrorInvalidValue;
+  const dim3 grid(p.n_split, p.G / NG, p.B);
+  split_reconstruct_wave_kernel<R, 4, NG, false><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// Four KV heads a workgroup only: with fewer, the workgroup's few waves fill
-// the LDS ring and the rotation table alone, and the block-per-split kernel
-// is faster (rank 32 with one KV head a group: 481 against 191 us at the
-// Llama-3-8B shape).
+// Four waves (KV heads) a workgroup always: with fewer, the workgroup's few
+// waves fill the LDS ring and the rotation table alone, and the
+// block-per-split kernel is faster (rank 32 with one KV head a workgroup: 481
+// against 191 us at the Llama-3-8B shape). Groups of fewer than four KV
+// heads therefore share a workgroup: four consecutive KV heads of four (or
+// two) groups, each group's tile loaded by its own waves into its own ring.
 bool reconstruct_wave_supported(const DecodeParams& p, int dtype) {
-  return dtype == 1 && p.d == kD && p.gqa <= 4 && p.s % 4 == 0 &&
-         (p.r == 32 || p.r == 64 || p.r == 128);
+  if (dtype != 1 || p.d != kD || p.gqa > 4) return false;
+  if (p.s % 4 == 0) return p.r == 32 || p.r == 64 || p.r == 128;
+  // one or two KV heads a group: four consecutive KV heads (of four or two
+  // groups) a workgroup, one latent tile per group (the four tiles of rank
+  // 128 would not fit the LDS)
+  if ((p.s == 1 || p.s == 2) && p.Hkv % 4 == 0)
+    return p.r == 32 || p.r == 64 || (p.r == 128 && p.s == 2);
+  return false;
 }
 
 hipError_t launch_split_reconstruct_wave(const DecodeParams& p, hipStream_t st) {
+  if (p.s == 1) {
+    switch (p.r) {
+      case 32: return launch_groups<32, 4>(p, st);
+      case 64: return launch_groups<64, 4>(p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.s == 2) {
+    switch (p.r) {
+      case 32: return launch_groups<32, 2>(p, st);
+      case 64: return launch_groups<64, 2>(p, st);
+      case 128: return launch_groups<128, 2>(p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.r) {
     case 32: return launch_shape<32, 4>(p, st);
     case 64: return launch_shape<64, 4>(p, st);

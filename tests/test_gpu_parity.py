@@ -119,7 +119,7 @@ def test_reconstruct_rescale_inside_tile_pair(idx):
 # (KV heads per group s, rank r): the granularities at 75% key compression
 # (M-LRD s=1 r=32 ... J-LRD s=8 r=256) and rank 512 with 2, 4 and 8 heads
 GROUPINGS = [(1, 32), (2, 64), (4, 128), (8, 256), (1, 128), (2, 256), (2, 512), (4, 512),
-             (8, 512)]
+             (8, 512), (1, 64), (2, 32), (2, 128)]
 
 
 @pytest.mark.parametrize("s,r", GROUPINGS)
@@ -134,6 +134,22 @@ def test_reconstruct_head_groupings(s, r):
         got, theta = run_decode(cfg, t, "reconstruct", split_tokens=st)
         assert theta > 0
         assert_close(got, _oracle(cfg, t, theta), what=f"s={s} r={r} split={st}")
+
+
+@pytest.mark.parametrize("s,r,hq", [(1, 32, 8), (2, 64, 16), (1, 64, 24)])
+def test_reconstruct_groups_in_one_workgroup(s, r, hq):
+    """Groups of one or two KV heads whose four consecutive KV heads share a
+    workgroup (each group's tile in its own LDS ring), with one, two and
+    three query heads per KV head, ragged lengths and a NaN-poisoned tail."""
+    cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r, batch=3, max_ctx=530, n_q_heads=hq,
+                              seed=70 + s)
+    t = W.generate(cfg, lens=np.array([530, 301, 17]))
+    hk, hv = W.poison_tail(t["h_k"], t["lens"]), W.poison_tail(t["h_v"], t["lens"])
+    print(f"[groups] s={s} r={r} hq={hq}", flush=True)
+    for st in (0, 64):
+        got, theta = run_decode(cfg, t, "reconstruct", split_tokens=st, h_k=hk, h_v=hv)
+        assert theta > 0
+        assert_close(got, _oracle(cfg, t, theta), what=f"groups s={s} r={r} hq={hq} split={st}")
 
 
 @pytest.mark.parametrize("s,r", [(1, 32), (2, 64), (4, 128), (8, 256)])
