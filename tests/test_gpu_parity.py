@@ -140,10 +140,11 @@ def test_reconstruct_head_groupings(s, r):
 def test_reconstruct_groups_in_one_workgroup(s, r, hq):
     """Groups of one or two KV heads whose four consecutive KV heads share a
     workgroup (each group's tile in its own LDS ring), with one, two and
-    three query heads per KV head, ragged lengths and a NaN-poisoned tail."""
-    cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r, batch=3, max_ctx=530, n_q_heads=hq,
+    three query heads per KV head, ragged lengths (one of them 0) and a
+    NaN-poisoned tail."""
+    cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r, batch=4, max_ctx=530, n_q_heads=hq,
                               seed=70 + s)
-    t = W.generate(cfg, lens=np.array([530, 301, 17]))
+    t = W.generate(cfg, lens=np.array([530, 301, 0, 17]))
     hk, hv = W.poison_tail(t["h_k"], t["lens"]), W.poison_tail(t["h_v"], t["lens"])
     print(f"[groups] s={s} r={r} hq={hq}", flush=True)
     for st in (0, 64):
