@@ -85,6 +85,10 @@ def parse():
                          "(absorbed keys) instead of the dtype cache")
     ap.add_argument("--profile-hadamard", action="store_true",
                     help="with --profile-bits: a Hadamard-rotated cache")
+    ap.add_argument("--profile-groups", type=int, default=0, choices=[0, 1, 2, 4, 8],
+                    help="with --profile-calls: the head-grouping sweep's workload with "
+                         "this many KV heads per group (the --config shape at 75%% key "
+                         "compression) instead of --config itself")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM read-stream probe")
     ap.add_argument("--no-configs", action="store_true",
@@ -551,7 +555,7 @@ def granularity_sweep(torch, P, W, cfg, args):
     for s in (1, 2, 4, 8):
         if cfg.n_kv_heads % s:
             continue
-        c = cfg.scaled(n_groups=cfg.n_kv_heads // s, rank=s * cfg.head_dim // 4, seed=60 + s)
+        c = sweep_config(cfg, s)
         t = W.generate(c)
         lat_bytes = W.latent_bytes(c, t["lens"])
         tokens = int(np.sum(t["lens"], dtype=np.int64))
@@ -598,6 +602,12 @@ def granularity_sweep(torch, P, W, cfg, args):
         del q, bk, bv, lens, hk, hv
         torch.cuda.empty_cache()
     return rows
+
+
+def sweep_config(cfg, s):
+    """The head-grouping sweep's workload: cfg's shape with s KV heads a group
+    and rank s * d / 4 (75% key compression at every grouping)."""
+    return cfg.scaled(n_groups=cfg.n_kv_heads // s, rank=s * cfg.head_dim // 4, seed=60 + s)
 
 
 def profile_calls(torch, P, W, cfg, args):
@@ -812,6 +822,8 @@ def main():
 
     cfg = W.CONFIGS[args.config]
     if args.profile_calls:
+        if args.profile_groups:
+            cfg = sweep_config(cfg, args.profile_groups)
         profile_calls(torch, P, W, cfg, args)
         return
     t = W.generate(cfg, parts=("decode", "append"))
