@@ -164,7 +164,11 @@ palu_status palu_decode_attn_noalloc(const palu_attn_desc* desc, const void* q, 
  * (RECONSTRUCT), written into the call's workspace. They depend on q and b_k
  * only, not on the cache, so a caller can run this on another stream while
  * palu_latent_append writes the step's token, then make the decode call with
- * desc->prepared = 1 on the same workspace (after that stream's work).
+ * desc->prepared = 1 on the same workspace (after that stream's work). In
+ * RECONSTRUCT mode the prepared operand is B_k transposed alone: it depends on
+ * b_k only and decode calls read it without writing it, so one prepare serves
+ * every later prepared call with the same descriptor, b_k and workspace (B_k
+ * is a weight: the transpose can be formed once, not per decode step).
  *   q [B, Hq, d], b_k [G, r, D_g] dtype (b_k may be NULL in FULL_RANK mode);
  *   workspace as for palu_decode_attn (this call writes its query area).
  * Errors: as palu_decode_attn's descriptor checks, NULL, WORKSPACE, DEVICE. */

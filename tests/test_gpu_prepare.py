@@ -64,3 +64,35 @@ def test_prepared_call_is_the_same_call(kind):
     torch.cuda.synchronize()
     assert torch.isfinite(out1).all()
     assert torch.equal(out1, out2), kind
+
+
+@pytest.mark.parametrize("rank", [256, 128])
+def test_reconstruct_prepare_once_serves_later_calls(rank):
+    """In RECONSTRUCT mode the prepared operand is B_k transposed alone: one
+    palu_decode_attn_prepare serves every later prepared call with the same
+    b_k and workspace (new queries and caches each call), each output equal to
+    the ordinary call's."""
+    import torch
+    import rank_compressed_kv_amd as P
+    cfg = W.CONFIGS[3].scaled(batch=2, max_ctx=1504, rank=rank)
+    base = W.generate(cfg)
+    bk, bv = dev(base["b_k"]), dev(base["b_v"])
+    kw = dict(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+              head_dim=cfg.head_dim, n_groups=cfg.n_groups, rank=cfg.rank, max_ctx=cfg.max_ctx,
+              dtype=P.PALU_BF16, mode="reconstruct", rope_theta=cfg.rope_theta)
+    plain, prep = P.attn_desc(**kw), P.attn_desc(**kw, prepared=True)
+    nws = P.palu_decode_attn_workspace(plain)
+    ws1 = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    P.palu_decode_attn_prepare(prep, dev(base["q"]), bk, ws2)
+    for call in range(3):
+        t = W.generate(cfg, seed=900 + call)
+        q, hk, hv, lens = dev(t["q"]), dev(t["h_k"]), dev(t["h_v"]), dev(t["lens"])
+        out1 = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32,
+                           device="cuda")
+        out2 = torch.empty_like(out1)
+        P.palu_decode_attn(plain, q, hk, hv, bk, bv, lens, out1, ws1)
+        P.palu_decode_attn(prep, q, hk, hv, bk, bv, lens, out2, ws2)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out1).all()
+        assert torch.equal(out1, out2), (rank, call)
