@@ -483,6 +483,8 @@ def reconstruct_configs(torch, P, W, O, args, which=(2, 4, 5)):
             "kernel": kname, "n_split": n_split, "split_tokens": split_tokens,
             "us_per_decode_call": round(call_us, 2), "kernel_us": round(kus, 2),
             "latent_bytes": lat_bytes, "rebuild_flops": flops,
+            "ideal_us_hbm": round(lat_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+            "ideal_us_mfma": round(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
             "latent_GBps_kernel": round(gbs, 1), "rebuild_TFLOPs": round(tf, 1),
             "roofline": {"bound": "mfma" if mfma_bound else "hbm",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS if mfma_bound
@@ -565,7 +567,9 @@ def granularity_sweep(torch, P, W, cfg, args):
         del t
         row = {"s": s, "groups": c.n_groups, "rank": c.rank, "latent_bytes": lat_bytes,
                "rebuild_gflop": round(flops / 1e9, 2),
-               "rebuild_flop_per_byte": round(flops / lat_bytes, 1)}
+               "rebuild_flop_per_byte": round(flops / lat_bytes, 1),
+               "ideal_us_hbm": round(lat_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+               "ideal_us_mfma_rebuild": round(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 2)}
         for mode in ("absorbed", "reconstruct"):
             theta = c.rope_theta if mode == "reconstruct" else 0.0
             desc = P.attn_desc(batch=c.batch, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
