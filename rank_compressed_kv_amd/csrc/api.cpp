@@ -130,7 +130,7 @@ Plan make_plan(const palu_attn_desc* d) {
     // the reconstruct MFMA kernel launches one workgroup per slice of KV heads,
     // and aims at about 2048 waves on the chip whatever its workgroup size
     double slices = 1;
-    if (pl.kernel == SplitKernel::kAbsorbedMfma) slices = absorbed_head_slices(sp.nq);
+    if (pl.kernel == SplitKernel::kAbsorbedMfma) slices = absorbed_mfma_slices(sp.nq);
     if (pl.kernel == SplitKernel::kReconstructMfma) {
       slices = sp.s / reconstruct_heads_per_wg(sp.r, sp.s);
       wg_target = double(kTargetWaves) / reconstruct_waves_per_wg(sp.r, sp.s);

@@ -164,9 +164,97 @@ __device__ __forceinline__ void softmax_values(State<R>& st, floatx4 s, const ch
   }
 }
 
+// Two blocks of 16 query heads from the same tile (groups of 17..32 heads):
+// each K chunk read from LDS feeds both blocks' score MFMAs, and each value
+// gather both blocks' value MFMAs, so a latent byte is read once per
+// workgroup for all its heads.
 template <int R>
+__device__ __forceinline__ void scores2(const char* kt, const QTile<R>* qs, int tok0, int t1,
+                                        int lane, floatx4 (&s)[2]) {
+  const int ln = lane & 15, kb = lane >> 4;
+  floatx4 acc4[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc4[hb][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < R / 32; ++c) {
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt + ln * kKStride<R> + 2 * (32 * c + 8 * kb)));
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const bf16x8 qh = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[hb].v[0][ln][32 * c + 8 * kb]));
+      const bf16x8 ql = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[hb].v[1][ln][32 * c + 8 * kb]));
+      acc4[hb][2 * (c & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh, acc4[hb][2 * (c & 1)], 0, 0, 0);
+      acc4[hb][2 * (c & 1) + 1] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql, acc4[hb][2 * (c & 1) + 1], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    s[hb] = (acc4[hb][0] + acc4[hb][2]) + (acc4[hb][1] + acc4[hb][3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (tok0 + 4 * kb + i >= t1) s[hb][i] = -INFINITY;
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void softmax_values2(State<R> (&st)[2], const floatx4 (&s)[2],
+                                                const char* vt, int lane) {
+  const int ln = lane & 15, kb = lane >> 4;
+  short4v ph[2], pl[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float mx = fmaxf(fmaxf(s[hb][0], s[hb][1]), fmaxf(s[hb][2], s[hb][3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > st[hb].m + kLazy)) {
+      const float mn = fmaxf(st[hb].m, mx);
+      const float alpha = exp2f(st[hb].m - mn);
+      st[hb].m = mn;
+      st[hb].l *= alpha;
+#pragma unroll
+      for (int rb = 0; rb < R / 16; ++rb) st[hb].acc[rb] *= alpha;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = exp2f(s[hb][e] - st[hb].m);
+      st[hb].l += p;
+      const float hi = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
+      ph[hb][e] = static_cast<short>(__float_as_uint(hi) >> 16);
+      pl[hb][e] = static_cast<short>(f32_to_bf16_rne(p - hi));
+    }
+  }
+  constexpr int kU = R / 16 < 4 ? R / 16 : 4;
+  const char* vb = vt + vtile_off<R>(4 * kb, 2 * ln);
+#pragma unroll
+  for (int rb0 = 0; rb0 < R / 16; rb0 += kU) {
+    short4v a[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[u][e] = *reinterpret_cast<const short*>(vb + e * (2 * R) + 32 * (rb0 + u));
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        st[hb].acc[rb0 + u] =
+            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[u], ph[hb], st[hb].acc[rb0 + u], 0, 0, 0);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        st[hb].acc[rb0 + u] =
+            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[u], pl[hb], st[hb].acc[rb0 + u], 0, 0, 0);
+  }
+}
+
+// NHB: blocks of 16 query heads a workgroup serves (one, or two for groups of
+// more than 16 heads)
+template <int R, int NHB>
 struct Smem {
-  QTile<R> q;
+  QTile<R> q[NHB];
   union {
     struct {                                         // per-wave tiles (streaming)
       char kt[kWaves][kKTileBytes<R>];
@@ -179,16 +267,20 @@ struct Smem {
   } u;
 };
 
-template <int R, bool kShared>
+template <int R, int NHB, bool kShared>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(DecodeParams p) {
-  // query heads of a group beyond 16 go to further head slices (workgroups
-  // that read the same latents, shared through one XCD's L2)
-  const int nslice = (p.nq + 15) / 16;
+  // a workgroup serves NHB blocks of 16 query heads; heads of a group beyond
+  // them go to further head slices (workgroups that read the same latents,
+  // shared through one XCD's L2)
+  constexpr int kHS = 16 * NHB;
+  const int nslice = (p.nq + kHS - 1) / kHS;
   const SplitUnit un = split_unit(p.n_split, p.G, p.B, nslice);
   if (!un.live) return;
   const int split = un.split, g = un.g, b = un.b;
-  const int hq0 = un.hs * 16;                            // first query head of the slice
-  const int nqs = min(16, p.nq - hq0);                   // its query heads
+  const int hq0 = un.hs * kHS;                           // first query head of the slice
+  int nqs[NHB];                                          // query heads of each block (<= 0: none)
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) nqs[hb] = min(16, p.nq - hq0 - 16 * hb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, kb = lane >> 4;
   const int n = clamp_len(p.lens, b, p.L);
@@ -197,7 +289,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   const int t1 = min(n, s0 + p.split_tokens);
   const int last = t1 - 1;
 
-  __shared__ Smem<R> sm;
+  __shared__ Smem<R, NHB> sm;
   const size_t row0 = (static_cast<size_t>(b) * p.G + g) * p.L;
   const uint16_t* Hk = static_cast<const uint16_t*>(p.h_k) + row0 * R;
   const uint16_t* Hv = static_cast<const uint16_t*>(p.h_v) + row0 * R;
@@ -237,28 +329,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   {
     constexpr int kQ = 16 * R / (64 * kWaves);
     const float* qrow = p.qt + (static_cast<size_t>(b) * p.Hq + g * p.nq + hq0) * R;
-    float qx[kQ];
+    float qx[NHB][kQ];
 #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-      const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
-      qx[u] = qrow[min(hd, nqs - 1) * R + k];
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int nh = nqs[hb];                            // a block without heads reads nothing
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+        const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
+        if constexpr (NHB == 1) qx[hb][u] = qrow[min(hd, nh - 1) * R + k];   // nh >= 1
+        else qx[hb][u] = nh > 0 ? qrow[(16 * hb + min(hd, nh - 1)) * R + k] : 0.f;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kQ; ++u) {
-      const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
-      const float x = hd < nqs ? qx[u] : 0.f;
-      const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
-      sm.q.v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
-      sm.q.v[1][hd][k] = f32_to_bf16_rne(x - hi);
-    }
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+        const int e = threadIdx.x + u * 64 * kWaves, hd = e / R, k = e % R;
+        const float x = hd < nqs[hb] ? qx[hb][u] : 0.f;
+        const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+        sm.q[hb].v[0][hd][k] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
+        sm.q[hb].v[1][hd][k] = f32_to_bf16_rne(x - hi);
+      }
   }
   barrier_lds();            // the first tiles stay in flight
 
-  State<R> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  State<R> st[NHB];
 #pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb) st.acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < NHB; ++hb) {
+    st[hb].m = -INFINITY;
+    st[hb].l = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < R / 16; ++rb) st[hb].acc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (mine > 0) {
     char* kt = sm.u.t.kt[wave];
@@ -278,8 +380,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
     for (int j = 0; j < mine; ++j) {
       stage(ka, va);
       fetch(ka, va, first + step * (j + 1));
-      const floatx4 s = scores<R>(kt, sm.q, first + step * j, t1, lane);
-      softmax_values<R>(st, s, vt, lane);
+      if constexpr (NHB == 1) {
+        const floatx4 s = scores<R>(kt, sm.q[0], first + step * j, t1, lane);
+        softmax_values<R>(st[0], s, vt, lane);
+      } else {
+        floatx4 s[2];
+        scores2<R>(kt, sm.q, first + step * j, t1, lane, s);
+        softmax_values2<R>(st, s, vt, lane);
+      }
     }
   }
 
@@ -287,50 +395,60 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_absorbed_mfma_kernel(Dec
   // its state, then after one more every thread combines one (head, lane
   // group, row block) slice of all of them (a side that saw no token has m =
   // -inf and weight 0) and writes it. [slot][value][lane] keeps consecutive
-  // lanes on consecutive banks.
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < R / 16; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.u.x.acc[wave][4 * rb + i][lane] = st.acc[rb][i];
-  sm.u.x.m[wave][lane] = st.m;
-  sm.u.x.l[wave][lane] = st.l;
-  __syncthreads();
+  // lanes on consecutive banks. Head blocks go one after the other through
+  // the same space.
   const int th = threadIdx.x;
   const int cln = th % 16, ckb = (th / 16) % 4, crq = th / 64;   // head, lane group, first row block
-  float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.x.m[w][cln]);
-  float aw[kWaves];
+  for (int hb = 0; hb < NHB; ++hb) {
+    __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm.u.x.m[w][cln];
-    aw[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
-  }
-  if (cln >= nqs) return;
-  const int head = g * p.nq + hq0 + cln;
-  const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
-  if (th < 16) {
-    float l = 0.f;
+    for (int rb = 0; rb < R / 16; ++rb)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      l += aw[w] * ((sm.u.x.l[w][cln] + sm.u.x.l[w][16 + cln]) +
-                    (sm.u.x.l[w][32 + cln] + sm.u.x.l[w][48 + cln]));
-    p.part_ml[slot * 2] = M;
-    p.part_ml[slot * 2 + 1] = l;
-  }
-  // latents 16 rb + 4 ckb + i of head cln
-  float* u = p.part_u + slot * R;
-  for (int rb = crq; rb < R / 16; rb += kWaves) {
-    float4 v = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) sm.u.x.acc[wave][4 * rb + i][lane] = st[hb].acc[rb][i];
+    sm.u.x.m[wave][lane] = st[hb].m;
+    sm.u.x.l[wave][lane] = st[hb].l;
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.x.m[w][cln]);
+    float aw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      v.x = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 0][16 * ckb + cln], v.x);
-      v.y = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 1][16 * ckb + cln], v.y);
-      v.z = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 2][16 * ckb + cln], v.z);
-      v.w = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 3][16 * ckb + cln], v.w);
+      const float mw = sm.u.x.m[w][cln];
+      aw[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
     }
-    *reinterpret_cast<float4*>(u + 16 * rb + 4 * ckb) = v;
+    if constexpr (NHB == 1) {
+      if (cln >= nqs[0]) return;
+    } else {
+      if (cln >= nqs[hb]) continue;                      // the next block's barriers follow
+    }
+    {
+      const int head = g * p.nq + hq0 + 16 * hb + cln;
+      const size_t slot = (static_cast<size_t>(b) * p.Hq + head) * p.n_split + split;
+      if (th < 16) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          l += aw[w] * ((sm.u.x.l[w][cln] + sm.u.x.l[w][16 + cln]) +
+                        (sm.u.x.l[w][32 + cln] + sm.u.x.l[w][48 + cln]));
+        p.part_ml[slot * 2] = M;
+        p.part_ml[slot * 2 + 1] = l;
+      }
+      // latents 16 rb + 4 ckb + i of head cln
+      float* u = p.part_u + slot * R;
+      for (int rb = crq; rb < R / 16; rb += kWaves) {
+        float4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          v.x = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 0][16 * ckb + cln], v.x);
+          v.y = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 1][16 * ckb + cln], v.y);
+          v.z = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 2][16 * ckb + cln], v.z);
+          v.w = fmaf(aw[w], sm.u.x.acc[w][4 * rb + 3][16 * ckb + cln], v.w);
+        }
+        *reinterpret_cast<float4*>(u + 16 * rb + 4 * ckb) = v;
+      }
+    }
   }
 }
 
@@ -342,18 +460,26 @@ bool absorbed_mfma_supported(const DecodeParams& p, int dtype) {
 
 int absorbed_head_slices(int nq) { return (nq + 15) / 16; }
 
-template <int R>
-hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
-  const int nslice = absorbed_head_slices(p.nq);
+int absorbed_mfma_slices(int nq) { return nq > 16 ? (nq + 31) / 32 : 1; }
+
+template <int R, int NHB>
+hipError_t launch_blocks(const DecodeParams& p, hipStream_t st) {
+  const int nslice = (p.nq + 16 * NHB - 1) / (16 * NHB);
   if (nslice == 1) {
-    split_absorbed_mfma_kernel<R, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
+    split_absorbed_mfma_kernel<R, NHB, false><<<dim3(p.n_split, p.G, p.B), 64 * kWaves, 0, st>>>(p);
   } else {
     const long ids = split_unit_ids(p.n_split, p.G, p.B, nslice);
     if (ids == 0) return hipErrorInvalidValue;
-    split_absorbed_mfma_kernel<R, true>
+    split_absorbed_mfma_kernel<R, NHB, true>
         <<<dim3(static_cast<unsigned>(ids)), 64 * kWaves, 0, st>>>(p);
   }
   return hipGetLastError();
+}
+
+// groups of more than 16 query heads: two head blocks a workgroup
+template <int R>
+hipError_t launch_rank(const DecodeParams& p, hipStream_t st) {
+  return p.nq > 16 ? launch_blocks<R, 2>(p, st) : launch_blocks<R, 1>(p, st);
 }
 
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st) {

@@ -122,6 +122,9 @@ bool absorbed_mfma_supported(const DecodeParams& p, int dtype);
 bool absorbed_quant_supported(const DecodeParams& p, int dtype);
 hipError_t launch_split_absorbed_quant(const DecodeParams& p, hipStream_t st);
 int absorbed_head_slices(int nq);   // workgroups per (split, b, g): 16 query heads each
+// the bf16 absorbed kernel's workgroups per (split, b, g): 16 query heads, or
+// 32 (two head blocks) each when a group has more than 16
+int absorbed_mfma_slices(int nq);
 hipError_t launch_split_absorbed_mfma(const DecodeParams& p, hipStream_t st);
 bool reconstruct_mfma_supported(const DecodeParams& p, int dtype);
 int reconstruct_heads_per_wg(int r, int s);   // KV heads per workgroup (0: not served)

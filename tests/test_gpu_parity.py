@@ -153,6 +153,23 @@ def test_reconstruct_groups_in_one_workgroup(s, r, hq):
         assert_close(got, _oracle(cfg, t, theta), what=f"groups s={s} r={r} hq={hq} split={st}")
 
 
+@pytest.mark.parametrize("hq,r", [(24, 128), (40, 256), (64, 64), (32, 256)])
+def test_absorbed_many_query_heads_per_group(hq, r):
+    """Absorbed keys with more than 16 query heads a group (two head blocks a
+    workgroup): 24 heads (a partial second block), 40 (a second slice whose
+    second block is empty), 64 (two full slices), 32; ragged lengths (one
+    0), a NaN-poisoned tail and several split sizes."""
+    cfg = W.CONFIGS[3].scaled(n_q_heads=hq, n_kv_heads=8, n_groups=1, rank=r, batch=3,
+                              max_ctx=600, seed=80 + hq)
+    t = W.generate(cfg, lens=np.array([600, 0, 233]))
+    hk, hv = W.poison_tail(t["h_k"], t["lens"]), W.poison_tail(t["h_v"], t["lens"])
+    print(f"[many-heads] hq={hq} r={r}", flush=True)
+    for st in (0, 64, 192):
+        got, _ = run_decode(cfg, t, "absorbed", split_tokens=st, h_k=hk, h_v=hv)
+        assert np.all(got[1] == 0.0)
+        assert_close(got, _oracle(cfg, t, 0.0), what=f"absorbed hq={hq} r={r} split={st}")
+
+
 @pytest.mark.parametrize("s,r", [(1, 32), (2, 64), (4, 128), (8, 256)])
 def test_absorbed_head_groupings(s, r):
     """Absorbed keys for every head grouping at 75% compression: ranks 32-256 on
