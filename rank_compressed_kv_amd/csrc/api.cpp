@@ -105,7 +105,11 @@ DecodeParams shape_params(const palu_attn_desc* d) {
   return p;
 }
 
-Plan make_plan(const palu_attn_desc* d) {
+// qbits: the int8 / int4 cache calls, whose kernel takes 16 query heads a
+// workgroup whatever the group size (the bf16 kernel takes 32 in groups of
+// more than 16): their plan has as many workgroups per split as that kernel
+// launches, and never more splits than the bf16 plan the workspace is sized for
+Plan make_plan(const palu_attn_desc* d, int qbits = 0) {
   Plan pl{};
   const DecodeParams sp = shape_params(d);
   pl.kernel = SplitKernel::kGeneric;
@@ -130,7 +134,8 @@ Plan make_plan(const palu_attn_desc* d) {
     // the reconstruct MFMA kernel launches one workgroup per slice of KV heads,
     // and aims at about 2048 waves on the chip whatever its workgroup size
     double slices = 1;
-    if (pl.kernel == SplitKernel::kAbsorbedMfma) slices = absorbed_mfma_slices(sp.nq);
+    if (pl.kernel == SplitKernel::kAbsorbedMfma)
+      slices = qbits ? absorbed_head_slices(sp.nq) : absorbed_mfma_slices(sp.nq);
     if (pl.kernel == SplitKernel::kReconstructMfma) {
       slices = sp.s / reconstruct_heads_per_wg(sp.r, sp.s);
       wg_target = double(kTargetWaves) / reconstruct_waves_per_wg(sp.r, sp.s);
@@ -331,7 +336,7 @@ palu_status decode(const palu_attn_desc* desc, const void* q, const void* h_k, c
   if (decode_pointers(desc, q, h_k, h_v, b_k, b_v, out) != PALU_OK || !workspace)
     return fail(PALU_ERR_NULL, "q, h_k, h_v, out, workspace and (as the mode needs) b_k, b_v "
                                "must be non-NULL");
-  const Plan pl = make_plan(desc);
+  const Plan pl = make_plan(desc, qbits);
   if (qbits && pl.kernel != SplitKernel::kAbsorbedMfma)
     return fail(PALU_ERR_UNSUPPORTED, "quantised latents need the absorbed MFMA kernel");
   const WorkspaceLayout wl = layout(desc, pl);

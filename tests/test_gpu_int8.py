@@ -20,6 +20,7 @@ SMALL = {
     64: W.CONFIGS[3].scaled(n_groups=4, rank=64, batch=2, max_ctx=704, seed=71),   # r 64
     48: W.CONFIGS[3].scaled(n_kv_heads=24, n_q_heads=48, n_groups=4, rank=128, batch=1,
                             max_ctx=896, seed=72),            # 12 q heads: a partial head slice
+    32: W.CONFIGS[3].scaled(n_groups=1, rank=256, batch=2, max_ctx=704, seed=73),   # 32 q heads a group
 }
 
 
