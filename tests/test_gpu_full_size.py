@@ -45,21 +45,23 @@ def test_full_size_sampled(idx, mode):
     assert_close(got[sel], want[sel], what=f"full cfg{idx}/{mode}", **_tol(cfg))
 
 
+@pytest.mark.parametrize("mode", ["reconstruct", "absorbed"])
 @pytest.mark.parametrize("s,r", [(1, 32), (2, 64), (4, 128), (8, 256)])
-def test_full_size_head_groupings_sampled(s, r):
+def test_full_size_head_groupings_sampled(s, r, mode):
     """The head-grouping sweep the benchmark times (the Llama-3-8B shape at
-    75% key compression, 32K context, rebuilt and rotated keys), one KV head
-    a group (M-LRD) to all eight (J-LRD), in the library's own plan."""
+    75% key compression, 32K context; rebuilt and rotated keys, or absorbed
+    keys: 32 query heads a group at s = 8), one KV head a group (M-LRD) to
+    all eight (J-LRD), in the library's own plan."""
     cfg = W.CONFIGS[3].scaled(n_groups=8 // s, rank=r)
     t = W.generate(cfg)
     pairs = _pairs(cfg, t["lens"])
-    print(f"[full] grouping s={s} r={r} pairs={pairs}", flush=True)
-    got, theta = run_decode(cfg, t, "reconstruct")
-    assert theta > 0
+    print(f"[full] grouping s={s} r={r} {mode} pairs={pairs}", flush=True)
+    got, theta = run_decode(cfg, t, mode)
+    assert (theta > 0) == (mode == "reconstruct")
     want = O.decode_attention(t["q"], t["h_k"], t["h_v"], t["b_k"], t["b_v"], t["lens"],
                               rope_theta=theta, select=pairs)
     sel = tuple(np.array(pairs).T)
-    assert_close(got[sel], want[sel], what=f"full grouping s={s} r={r}")
+    assert_close(got[sel], want[sel], what=f"full grouping s={s} r={r} {mode}")
 
 
 @pytest.mark.parametrize("bits", [8, 4])
