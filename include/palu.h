@@ -110,7 +110,10 @@ typedef struct palu_attn_desc {
 palu_status palu_decode_attn_workspace(const palu_attn_desc* desc, size_t* bytes);
 
 /* Launch plan for this descriptor: number of context splits, tokens per split
- * and the name of the main kernel (a static string). Any output may be NULL. */
+ * and the name of the main kernel (a static string). Any output may be NULL.
+ * The int8 / int4 decode calls take 16 query heads a workgroup; for groups of
+ * more than 16 query heads they use fewer splits than reported here (never
+ * more, so palu_decode_attn_workspace covers them). */
 palu_status palu_decode_attn_plan(const palu_attn_desc* desc, int32_t* n_split,
                                   int32_t* split_tokens, const char** kernel);
 
