@@ -25,10 +25,12 @@
 //   scores   the partial S[tok x q heads] over its 32 columns by one fp16
 //            MFMA 16x16x32 from the rotated keys rounded once to fp16 and q
 //            in fp16 after a per-head power-of-two scale (q held in
-//            registers); the four quarters' partial scores meet in LDS (one
-//            barrier) and every quarter adds them in the same order, so the
-//            four waves of a head hold the same scores and softmax state;
-//   softmax  online, base 2, lazy rescale;
+//            registers); the four quarters' partial scores meet in LDS on
+//            the tile's barrier and every quarter adds them in the same
+//            order, so the four waves of a head hold the same scores and
+//            softmax state;
+//   softmax  online, base 2, lazy rescale, one iteration after the scores
+//            (they are whole only after the barrier);
 //   values   its latent quarter: U[rows x 128] += P[rows x tok] H_v[tok x
 //            128] with P hi in rows 0..3 and lo in rows 4..7, the H_v operand
 //            read from the LDS tile with the transposing read; two consecutive
@@ -41,9 +43,10 @@
 // rotations, pack and score MFMA; the two waves on a SIMD fill each other's
 // gaps (the softmax's dependent chain, LDS and exp latencies).
 // Loads: 16-byte pieces of each tile go through a register stage into LDS
-// rings of three K and four V buffers (a pair's first V tile stays while the
-// tile after the pair's second is copied in); rows past the split's end are
-// clamped to its last valid row and masked.
+// rings of two K and five V buffers (a tile's values run an iteration after
+// its scores, and a pair's first V tile stays until the pair's second is
+// summed); rows past the split's end are clamped to its last valid row and
+// masked. One barrier per tile.
 #include "reconstruct_wave_util.h"
 
 namespace palu {
@@ -58,15 +61,15 @@ constexpr int kParts = 4;          // waves (column quarters) per KV head
 constexpr int kWaves = kParts * kHeads;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVB = R / kParts / 16;   // 16-latent value blocks per wave
-constexpr int kNBuf = 3;           // LDS K tile buffers
-constexpr int kVBuf = 4;           // LDS V tile buffers
+constexpr int kNBuf = 2;           // LDS K tile buffers
+constexpr int kVBuf = 5;           // LDS V tile buffers (a tile's values run an iteration late)
 
 struct Smem {
   char k[kNBuf][kTile * kKStride<R>];
   char v[kVBuf][kTile * kVStride<R>];
   uint4 qop[kWaves][64];           // each wave's score q operand (block pair qc)
   RotTable rot;
-  floatx4 sp[kWaves][64];          // partial scores of the current tile
+  floatx4 sp[2][kWaves][64];       // partial scores, by tile parity
 };
 // the q operands of all four block pairs are built in V buffers 2 and 3
 // (first written by the loop, after the prologue's barriers)
@@ -276,7 +279,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
   barrier_lds();
   floatx4 kx[2], ky[2];
   keys(0, kx);
+  barrier_lds();                                         // tile 0's K buffer takes tile 2 next
   int cb = 0, cvb = 0;                                   // K and V buffers of tile it
+  int pvb = 0;                                           // V buffer of tile it-1
 
   // Iteration it (after the barrier that made tiles it and it+1 and tile
   // it's rotation table visible). Region 1 is one straight run of code
@@ -284,14 +289,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
   // across slots): slot (c, lb) issues the key MFMA of tile it+1's block
   // qc + 4 lb and chunk c (H_k chunks read two chunks ahead), then its share
   // of the work items of tile it: the LDS copy of tile it+2 from the register
-  // stage (its K buffer last held tile it-1, its V buffer tile it-2) and the
-  // request of tile it+3 into the stage, the rotation-table rows of the
-  // wave's block pair, its four pair rotations, the fp16 pack and the partial
-  // score MFMA (its q operand read a few items earlier). Then the partial
-  // scores meet in LDS (a barrier), the last tile's mask, the running max, the
-  // rare rescale, tile it's softmax and values (of the pair it ends), the
-  // rotation table of tile it+1 (its buffer last served tile it-1); the
-  // barrier.
+  // stage (its K buffer last held tile it, whose keys were formed before the
+  // last barrier; its V buffer tile it-3) and the request of tile it+3 into
+  // the stage, the rotation-table rows of the wave's block pair, its four
+  // pair rotations, the fp16 pack and the partial score MFMA (its q operand
+  // read a few items earlier). Then tile it-1's softmax and values (its
+  // partial scores in LDS since the last barrier), tile it's partial scores
+  // into LDS, the rotation table of tile it+1 (its buffer last served tile
+  // it-1); the barrier.
   constexpr int kSlots = 2 * kC;
   enum : int { kPut = 0, kFetch, kRows, kRot0, kQ = kRot0 + 2, kRot2, kPack = kRot2 + 2, kScore, kN };
   auto region1 = [&](int it, int bf, int vbf, floatx4 (&cur)[2], floatx4 (&nxt)[2], floatx4& sc) {
@@ -345,28 +350,36 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto iteration = [&](int it, floatx4 (&cur)[2], floatx4 (&nxt)[2], auto kMode) {
-    floatx4 sc;
-    region1(it, cb, cvb, cur, nxt, sc);
-    // the four quarters' partial scores of tile it meet in LDS (sp is free:
-    // its last readers passed the end-of-iteration barrier), added in quarter
-    // order by every wave of the head
-    sm.sp[wave][lane] = sc;
-    barrier_lds();
-    sc = sm.sp[jh][lane];
+  // tile pt's softmax and values, one iteration after its scores: the four
+  // quarters' partial scores (in LDS since the barrier that ended tile pt's
+  // iteration) added in quarter order by every wave of the head, the mask of
+  // the split's last tile, the running max
+  auto softmax_of = [&](int pt, int vbuf, auto kMode) {
+    floatx4 sc = sm.sp[pt & 1][jh][lane];
 #pragma unroll
     for (int c = 1; c < kParts; ++c) {
-      const floatx4 o = sm.sp[jh + kHeads * c][lane];
+      const floatx4 o = sm.sp[pt & 1][jh + kHeads * c][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] += o[i];
     }
-    const int tok0 = s0 + it * kTile;
+    const int tok0 = s0 + pt * kTile;
     if (tok0 + kTile > t1) {                             // the split's last tile: its tail masked
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = tok0 + 4 * kb + i < t1 ? sc[i] : -INFINITY;
     }
     const float mx = hscale * max_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    softmax_values(cvb, cvb == 0 ? kVBuf - 1 : cvb - 1, sc, mx, kMode);
+    softmax_values(vbuf, vbuf == 0 ? kVBuf - 1 : vbuf - 1, sc, mx, kMode);
+  };
+  // Iteration it: region 1, then tile it-1's softmax and values (kPrev: its
+  // mode; none in the first iteration), tile it's partial scores into LDS,
+  // the rotation table of tile it+1, the barrier.
+  auto iteration = [&](int it, floatx4 (&cur)[2], floatx4 (&nxt)[2], auto kPrev) {
+    constexpr int prev = kPrev;                          // -1: no tile it-1
+    floatx4 sc;
+    region1(it, cb, cvb, cur, nxt, sc);
+    if constexpr (prev >= 0) softmax_of(it - 1, pvb, std::integral_constant<int, prev>{});
+    sm.sp[it & 1][wave][lane] = sc;
+    pvb = cvb;
     cb = next_buf(cb);
     cvb = next_vbuf(cvb);
     if (it + 1 < ntiles) {
@@ -375,12 +388,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_reconstruct_quarter_kernel(
     }
     barrier_lds();
   };
-  int it = 0;
+  // tiles go in pairs (even, odd): an even tile's softmax keeps its weights
+  // (mode 1), the odd one's takes both tiles' values (mode 2); an even last
+  // tile stands alone (mode 0)
+  iteration(0, kx, ky, std::integral_constant<int, -1>{});
+  int it = 1;
   for (; it + 1 < ntiles; it += 2) {
-    iteration(it, kx, ky, std::integral_constant<int, 1>{});
-    iteration(it + 1, ky, kx, std::integral_constant<int, 2>{});
+    iteration(it, ky, kx, std::integral_constant<int, 1>{});
+    iteration(it + 1, kx, ky, std::integral_constant<int, 2>{});
   }
-  if (it < ntiles) iteration(it, kx, ky, std::integral_constant<int, 0>{});
+  if (it < ntiles) iteration(it, ky, kx, std::integral_constant<int, 1>{});
+  if ((ntiles - 1) % 2) softmax_of(ntiles - 1, pvb, std::integral_constant<int, 2>{});
+  else softmax_of(ntiles - 1, pvb, std::integral_constant<int, 0>{});
 
   // ---- partials of this wave's query heads (latent quarter qc): the
   // remainder rows (kb = 1) are added to the bf16 rows (kb = 0); the sum l over
